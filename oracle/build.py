@@ -1,0 +1,26 @@
+"""Build the CPU oracle (plain C, gcc) into oracle/liboracle.so.
+
+Test infrastructure: only the tests, the smoke check and the benchmark's CPU
+baseline load the result.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "moe_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

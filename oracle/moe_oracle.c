@@ -1,0 +1,613 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the W4A16 MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+ * Python binding) may include, link, load or call this file; only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg do.  It shares no code
+ * with the HIP path: its fp16 codec, quantiser, blob reader, router, sort,
+ * FFN, combine and residency-policy simulator are all written here from the
+ * pages and the readings recorded in the design notes.
+ *
+ * Sources (web pages):
+ *  [HR] Horizon RunMap, "Prévia Técnica" (horizonrunmap.com/pt):
+ *       "02 / A solução" and "03 / Arquitetura" (router picks experts; the
+ *       expert kernel combines compact INT4 weights and FP16 scales with FP16
+ *       activations and hands the result back to the model), "08 /
+ *       Comportamento do modelo" (W4: INT4 expert weights with FP16 scales;
+ *       A16: FP16 activations; FP32 accumulation with explicit roundings),
+ *       "03 / Arquitetura, resident-qpacked-cache-v1" (slot cache contract).
+ *  [ST] Hamidun News, "Desenvolvedor do Strata cria mapa ao vivo de 24 576
+ *       especialistas MoE em uma GTX 1070", section "Como 125 bilhões de
+ *       parâmetros cabem em 8 GB" (decayed access counter, LRU/LFU cache).
+ *  [LH] lucashiago.com.br local-inference explainer, step 1 formula
+ *       (bytes = P x bits / 8, per-block scale overhead).
+ *
+ * Where the pages are silent (softmax form, tie-break, SwiGLU, group size,
+ * quantiser rounding, nibble order, logit summation order, eviction
+ * constants) the code follows the readings listed in the design notes; each
+ * such point is marked READING below.
+ *
+ * Precision: everything is fp64 except (a) the router logits, which are
+ * defined by a pinned fp32 summation order so that a GPU can reproduce them
+ * bit for bit, and (b) the quantiser, whose codes are decided in fp32 like
+ * the GPU quantiser.  Only the final layer output is rounded to fp16 (RNE).
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off moe_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ENOMEM (-3)
+
+/* ------------------------------------------------------------------ fp16 */
+
+/* IEEE binary16 -> double, exact. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 31;
+    int man = h & 1023;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);                 /* subnormal or zero */
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + man), ex - 25);    /* (1 + m/1024) 2^(ex-15) */
+    return sign ? -v : v;
+}
+
+/* double -> IEEE binary16, round to nearest, ties to even. */
+uint16_t oracle_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7e00;
+    if (a >= 65520.0)                 /* halfway between 65504 and 2^16 -> even = inf */
+        return sign | 0x7c00;
+    int q_exp;                        /* value = r * 2^q_exp with integer r */
+    if (a >= ldexp(1.0, -14)) {
+        int e;
+        frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+        q_exp = e - 11;               /* 10 fraction bits below the leading one */
+    } else {
+        q_exp = -24;                  /* subnormal quantum */
+    }
+    double r = nearbyint(ldexp(a, -q_exp));   /* exact scaling, then RNE */
+    if (q_exp == -24)                 /* r in [0, 1024]; 1024 encodes 2^-14 */
+        return sign | (uint16_t)r;
+    if (r >= 2048.0) {                /* mantissa overflow: next binade */
+        r = 1024.0;
+        q_exp += 1;
+    }
+    int ex = q_exp + 25;
+    if (ex >= 31)
+        return sign | 0x7c00;
+    return sign | (uint16_t)(ex << 10) | (uint16_t)((int)r - 1024);
+}
+
+/* ----------------------------------------------------- expert blob format */
+
+/*
+ * Canonical expert blob ([HR] "02 / A solução": compact weights and FP16
+ * scales kept in separate formats).  Six sections, each starting on a 256-byte
+ * boundary:
+ *   gate_q [I][H/2], up_q [I][H/2], down_q [H][I/2]        (u8, two codes/byte)
+ *   gate_s [I][H/g], up_s [I][H/g], down_s [H][I/g]        (fp16 scales)
+ * Rows are [out][in] with the input dimension contiguous.  Byte b of a row
+ * holds element 2b in its low nibble and element 2b+1 in its high nibble, as
+ * u = q + 8 (READING: symmetric codes q in [-7, 7], no zero point).
+ */
+static int64_t al256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+int oracle_blob_layout(int H, int I, int g, int64_t off[6], int64_t *total)
+{
+    if (H <= 0 || I <= 0 || g <= 0 || H % g || I % g || H % 2 || I % 2)
+        return OR_EINVAL;
+    int64_t sz[6];
+    sz[0] = (int64_t)I * H / 2;
+    sz[1] = (int64_t)I * H / 2;
+    sz[2] = (int64_t)H * I / 2;
+    sz[3] = (int64_t)I * (H / g) * 2;
+    sz[4] = (int64_t)I * (H / g) * 2;
+    sz[5] = (int64_t)H * (I / g) * 2;
+    int64_t o = 0;
+    for (int i = 0; i < 6; i++) {
+        off[i] = o;
+        o = al256(o + sz[i]);
+    }
+    *total = o;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------- quantiser */
+
+/*
+ * Group-wise symmetric INT4 quantisation of a [rows][K] fp32 matrix, groups of
+ * g consecutive elements along K ([HR] "08": expert weights INT4 with FP16
+ * scales; [LH] step 1: every block carries its own scale).
+ * READING: s = fp16_rne(amax / 7) with amax/7 computed in fp32;
+ *          q = clamp(rne(w / s), -7, 7) with w / s computed in fp32;
+ *          q = 0 when s == 0.
+ * Codes are decided in fp32 so a GPU quantiser can make the same decision.
+ */
+int oracle_quantize_rows(const float *w, int rows, int K, int g,
+                         uint8_t *q, uint16_t *s)
+{
+    if (!w || !q || !s || rows < 0 || K <= 0 || g <= 0 || K % g || K % 2)
+        return OR_EINVAL;
+    int ng = K / g;
+    for (int r = 0; r < rows; r++) {
+        const float *wr = w + (int64_t)r * K;
+        uint8_t *qr = q + (int64_t)r * (K / 2);
+        memset(qr, 0, (size_t)(K / 2));
+        for (int G = 0; G < ng; G++) {
+            float amax = 0.0f;
+            for (int i = 0; i < g; i++) {
+                float a = fabsf(wr[G * g + i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float sf = amax / 7.0f;
+            uint16_t sh = oracle_f64_to_f16((double)sf);
+            s[(int64_t)r * ng + G] = sh;
+            float sv = (float)oracle_f16_to_f64(sh);
+            for (int i = 0; i < g; i++) {
+                int c = G * g + i;
+                int qi = 0;
+                if (sv != 0.0f) {
+                    float t = wr[c] / sv;
+                    double rr = nearbyint((double)t);
+                    if (rr > 7.0) rr = 7.0;
+                    if (rr < -7.0) rr = -7.0;
+                    qi = (int)rr;
+                }
+                uint8_t u = (uint8_t)(qi + 8);
+                if (c & 1)
+                    qr[c / 2] |= (uint8_t)(u << 4);
+                else
+                    qr[c / 2] |= u;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Quantise one expert's three projections into a canonical blob. */
+int oracle_pack_expert(const float *wg, const float *wu, const float *wd,
+                       int H, int I, int g, uint8_t *blob)
+{
+    int64_t off[6], total;
+    int rc = oracle_blob_layout(H, I, g, off, &total);
+    if (rc) return rc;
+    memset(blob, 0, (size_t)total);
+    rc = oracle_quantize_rows(wg, I, H, g, blob + off[0], (uint16_t *)(blob + off[3]));
+    if (rc) return rc;
+    rc = oracle_quantize_rows(wu, I, H, g, blob + off[1], (uint16_t *)(blob + off[4]));
+    if (rc) return rc;
+    return oracle_quantize_rows(wd, H, I, g, blob + off[2], (uint16_t *)(blob + off[5]));
+}
+
+/* Dequantised element (r, c) of a [rows][K] section: q * s, exact in fp64. */
+static double deq(const uint8_t *qs, const uint16_t *ss, int K, int g, int r, int c)
+{
+    uint8_t b = qs[(int64_t)r * (K / 2) + c / 2];
+    int u = (c & 1) ? (b >> 4) : (b & 15);
+    return (double)(u - 8) * oracle_f16_to_f64(ss[(int64_t)r * (K / g) + c / g]);
+}
+
+/* Dequantise a whole [rows][K] section to fp64 (tests use it as a pin). */
+int oracle_dequant_rows(const uint8_t *q, const uint16_t *s, int rows, int K, int g,
+                        double *out)
+{
+    if (!q || !s || !out || K % g || K % 2)
+        return OR_EINVAL;
+    for (int r = 0; r < rows; r++)
+        for (int c = 0; c < K; c++)
+            out[(int64_t)r * K + c] = deq(q, s, K, g, r, c);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- router */
+
+/*
+ * Router logit l[t,e] = sum_h x[t,h] * Wr[e,h] in fp32, in a pinned order
+ * (READING; the pages only say accumulation is FP32 with explicit roundings,
+ * [HR] "08"): H is cut into chunks of 8 elements; chunk c is added, element
+ * by element in increasing h, into partial number (c mod 64), chunks taken in
+ * increasing c; the 64 partials are then combined by an xor butterfly with
+ * strides 32, 16, 8, 4, 2, 1 (a_j <- a_j + a_{j xor s}).  fp16 x fp16
+ * products are exact in fp32, so this order fixes every rounding.
+ */
+static float logit_pinned(const uint16_t *x, const uint16_t *w, int H)
+{
+    float part[64], nxt[64];
+    for (int j = 0; j < 64; j++)
+        part[j] = 0.0f;
+    for (int c = 0; c < H / 8; c++) {
+        int lane = c % 64;
+        for (int i = 0; i < 8; i++) {
+            int h = c * 8 + i;
+            float prod = (float)oracle_f16_to_f64(x[h]) * (float)oracle_f16_to_f64(w[h]);
+            part[lane] = part[lane] + prod;
+        }
+    }
+    for (int st = 32; st >= 1; st >>= 1) {
+        for (int j = 0; j < 64; j++)
+            nxt[j] = part[j] + part[j ^ st];
+        memcpy(part, nxt, sizeof part);
+    }
+    return part[0];
+}
+
+/*
+ * Routing ([HR] "03 / Arquitetura": the router chooses which experts work on
+ * this token).  READING: logits over all E experts (plus an optional fp32
+ * per-expert bias added after the dot product); the top-k are the k largest
+ * logits, ties going to the lower expert index, stored in that order;
+ * weights are softmax over all E logits (fp64) taken at the chosen experts,
+ * not renormalised unless `renorm` is set.
+ * Outputs: idx[T][k] int32, w[T][k] fp32, optionally logits[T][E] fp32.
+ */
+int oracle_route(const uint16_t *x, const uint16_t *wr, const float *bias,
+                 int T, int H, int E, int k, int renorm,
+                 int32_t *idx, float *w, float *logits)
+{
+    if (!x || !wr || !idx || !w || T < 0 || H <= 0 || H % 8 || E <= 0 || k <= 0 || k > E)
+        return OR_EINVAL;
+    float *l = malloc(sizeof(float) * (size_t)E);
+    double *p = malloc(sizeof(double) * (size_t)E);
+    char *taken = malloc((size_t)E);
+    if (!l || !p || !taken) {
+        free(l); free(p); free(taken);
+        return OR_ENOMEM;
+    }
+    for (int t = 0; t < T; t++) {
+        for (int e = 0; e < E; e++) {
+            float v = logit_pinned(x + (int64_t)t * H, wr + (int64_t)e * H, H);
+            if (bias)
+                v = v + bias[e];
+            l[e] = v;
+            if (logits)
+                logits[(int64_t)t * E + e] = v;
+        }
+        /* top-k by (logit descending, index ascending) */
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || l[e] > l[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[(int64_t)t * k + j] = best;
+        }
+        /* softmax over all E, fp64 */
+        double m = l[0];
+        for (int e = 1; e < E; e++)
+            if (l[e] > m) m = l[e];
+        double den = 0.0;
+        for (int e = 0; e < E; e++) {
+            p[e] = exp((double)l[e] - m);
+            den += p[e];
+        }
+        double sel = 0.0;
+        for (int j = 0; j < k; j++)
+            sel += p[idx[(int64_t)t * k + j]] / den;
+        for (int j = 0; j < k; j++) {
+            double pj = p[idx[(int64_t)t * k + j]] / den;
+            if (renorm)
+                pj = pj / sel;
+            w[(int64_t)t * k + j] = (float)pj;
+        }
+    }
+    free(l); free(p); free(taken);
+    return OR_OK;
+}
+
+/* ----------------------------------------------------------- permutation */
+
+/*
+ * Token-to-expert grouping (the pages' "experts computed in groups", [HR]
+ * "04 / Resultados", Grouped executor).  READING: stable counting sort of
+ * the flat index f = t*k + j by expert idx[f]:
+ *   counts[e], offsets[E+1] (exclusive scan, offsets[E] = T*k),
+ *   perm[p] = f for sorted position p (f ascending inside each expert),
+ *   inv_perm[f] = p.
+ */
+int oracle_permute(const int32_t *idx, int T, int k, int E,
+                   int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm)
+{
+    if (!idx || !counts || !offsets || !perm || !inv_perm || T < 0 || k <= 0 || E <= 0)
+        return OR_EINVAL;
+    int n = T * k;
+    for (int e = 0; e < E; e++)
+        counts[e] = 0;
+    for (int f = 0; f < n; f++) {
+        if (idx[f] < 0 || idx[f] >= E)
+            return OR_EINVAL;
+        counts[idx[f]]++;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; e++)
+        offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = malloc(sizeof(int32_t) * (size_t)E);
+    if (!fill)
+        return OR_ENOMEM;
+    for (int e = 0; e < E; e++)
+        fill[e] = offsets[e];
+    for (int f = 0; f < n; f++) {
+        int p = fill[idx[f]]++;
+        perm[p] = f;
+        inv_perm[f] = p;
+    }
+    free(fill);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------ expert FFN */
+
+static double silu(double a) { return a / (1.0 + exp(-a)); }
+
+/*
+ * Routed expert FFN straight from the compact weights ([HR] "03": the kernel
+ * reads compact weights and scales, uses the FP16 activations and never keeps
+ * an expanded expert; here each element is decoded on use).  READING: SwiGLU,
+ *   h = silu(Wg x) * (Wu x),  y = Wd h,  W = q * s,  all in fp64.
+ * Sorted row p (offsets[e] <= p < offsets[e+1]) belongs to expert e and to
+ * token t = perm[p] / k.  `rows` (length nrows) selects sorted rows to
+ * compute; NULL means all T*k rows.  y is [nrows][H] fp64.
+ */
+int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
+                      const uint8_t *const *blobs, int T, int H, int I, int E, int k, int g,
+                      const int32_t *rows, int nrows, double *y)
+{
+    int64_t off[6], total;
+    if (!x || !perm || !offsets || !blobs || !y || k <= 0)
+        return OR_EINVAL;
+    if (oracle_blob_layout(H, I, g, off, &total))
+        return OR_EINVAL;
+    int n = T * k;
+    if (!rows)
+        nrows = n;
+    double *xv = malloc(sizeof(double) * (size_t)H);
+    double *hv = malloc(sizeof(double) * (size_t)I);
+    if (!xv || !hv) {
+        free(xv); free(hv);
+        return OR_ENOMEM;
+    }
+    for (int r = 0; r < nrows; r++) {
+        int p = rows ? rows[r] : r;
+        if (p < 0 || p >= n) {
+            free(xv); free(hv);
+            return OR_EINVAL;
+        }
+        int e = 0;
+        while (e < E && !(offsets[e] <= p && p < offsets[e + 1]))
+            e++;
+        if (e == E || !blobs[e]) {
+            free(xv); free(hv);
+            return OR_EINVAL;
+        }
+        const uint8_t *b = blobs[e];
+        const uint8_t *gq = b + off[0], *uq = b + off[1], *dq = b + off[2];
+        const uint16_t *gs = (const uint16_t *)(b + off[3]);
+        const uint16_t *us = (const uint16_t *)(b + off[4]);
+        const uint16_t *ds = (const uint16_t *)(b + off[5]);
+        int t = perm[p] / k;
+        for (int c = 0; c < H; c++)
+            xv[c] = oracle_f16_to_f64(x[(int64_t)t * H + c]);
+        for (int i = 0; i < I; i++) {
+            double a = 0.0, u = 0.0;
+            for (int c = 0; c < H; c++) {
+                a += deq(gq, gs, H, g, i, c) * xv[c];
+                u += deq(uq, us, H, g, i, c) * xv[c];
+            }
+            hv[i] = silu(a) * u;
+        }
+        for (int o = 0; o < H; o++) {
+            double acc = 0.0;
+            for (int i = 0; i < I; i++)
+                acc += deq(dq, ds, I, g, o, i) * hv[i];
+            y[(int64_t)r * H + o] = acc;
+        }
+    }
+    free(xv); free(hv);
+    return OR_OK;
+}
+
+/*
+ * Shared (non-routed) expert in FP16 weights ([HR] "03": the non-routed part
+ * stays outside the INT4 compression, in FP16).  READING: the same SwiGLU FFN,
+ * weights wg, wu [Is][H] and wd [H][Is] fp16 row-major, evaluated in fp64 for
+ * the tokens in `toks` (NULL = all T).  s is [ntoks][H] fp64.
+ */
+int oracle_shared_ffn(const uint16_t *x, const uint16_t *wg, const uint16_t *wu,
+                      const uint16_t *wd, int T, int H, int Is,
+                      const int32_t *toks, int ntoks, double *s)
+{
+    if (!x || !wg || !wu || !wd || !s || H <= 0 || Is <= 0)
+        return OR_EINVAL;
+    if (!toks)
+        ntoks = T;
+    double *xv = malloc(sizeof(double) * (size_t)H);
+    double *hv = malloc(sizeof(double) * (size_t)Is);
+    if (!xv || !hv) {
+        free(xv); free(hv);
+        return OR_ENOMEM;
+    }
+    for (int r = 0; r < ntoks; r++) {
+        int t = toks ? toks[r] : r;
+        for (int c = 0; c < H; c++)
+            xv[c] = oracle_f16_to_f64(x[(int64_t)t * H + c]);
+        for (int i = 0; i < Is; i++) {
+            double a = 0.0, u = 0.0;
+            for (int c = 0; c < H; c++) {
+                a += oracle_f16_to_f64(wg[(int64_t)i * H + c]) * xv[c];
+                u += oracle_f16_to_f64(wu[(int64_t)i * H + c]) * xv[c];
+            }
+            hv[i] = silu(a) * u;
+        }
+        for (int o = 0; o < H; o++) {
+            double acc = 0.0;
+            for (int i = 0; i < Is; i++)
+                acc += oracle_f16_to_f64(wd[(int64_t)o * Is + i]) * hv[i];
+            s[(int64_t)r * H + o] = acc;
+        }
+    }
+    free(xv); free(hv);
+    return OR_OK;
+}
+
+/* --------------------------------------------------------------- combine */
+
+/*
+ * Router-weighted combine ([HR] "03": the expert results go back to the rest
+ * of the model weighted by the router).  READING:
+ *   out[t] = fp16_rne( residual[t] + sum_j w[t,j] * y[inv_perm[t*k+j]] + s[t] )
+ * evaluated in fp64; residual (fp16) and s (fp64) are optional (NULL).
+ * y is indexed by sorted row: [T*k][H].  out_f64 (optional) gets the value
+ * before the final rounding.
+ */
+int oracle_combine(const double *y, const int32_t *inv_perm, const float *w,
+                   const double *shared, const uint16_t *residual,
+                   int T, int H, int k, uint16_t *out, double *out_f64)
+{
+    if (!y || !inv_perm || !w || !out || T < 0 || H <= 0 || k <= 0)
+        return OR_EINVAL;
+    for (int t = 0; t < T; t++) {
+        for (int o = 0; o < H; o++) {
+            double acc = residual ? oracle_f16_to_f64(residual[(int64_t)t * H + o]) : 0.0;
+            for (int j = 0; j < k; j++) {
+                int p = inv_perm[(int64_t)t * k + j];
+                acc += (double)w[(int64_t)t * k + j] * y[(int64_t)p * H + o];
+            }
+            if (shared)
+                acc += shared[(int64_t)t * H + o];
+            out[(int64_t)t * H + o] = oracle_f64_to_f16(acc);
+            if (out_f64)
+                out_f64[(int64_t)t * H + o] = acc;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------- residency simulator */
+
+/*
+ * Replays a routing trace through the expert-slot cache policy.
+ * [HR] "03 / Arquitetura" (resident-qpacked-cache-v1): capacity is fixed
+ * before requests; misses are copied into spare slots while readers keep the
+ * previous generation; evicted copies are dropped (never written back).
+ * [ST] "Como 125 bilhões...": eviction by an access counter whose old hits
+ * decay (an LRU/LFU hybrid).
+ * READING of the policy, per routed event (layer l, k distinct experts R):
+ *   1. decay every counter of layer l: c <- c - (c >> shift)
+ *      (shift < 0: no decay, i.e. LFU);
+ *   2. c[e] += 65536 for e in R;
+ *   3. hits (R resident) are touched in ascending expert id, each taking the
+ *      next value of a global use clock;
+ *   4. misses are handled in ascending expert id: the victim is the resident
+ *      expert not in R with the lowest (counter, last use, id); the miss takes
+ *      its place and the next clock value.
+ * Initial placement per layer is experts 0..C-1 with last-use values ordered
+ * by id (expert 0 oldest).  shift = 0 is plain LRU.
+ * Outputs per event: hits, misses, the missed experts and the victims in the
+ * order handled (-1 padded to k).
+ */
+int oracle_pool_sim(int L, int E, int C, int shift, int k,
+                    const int32_t *ev_layer, const int32_t *ev_ids, int n_ev,
+                    int32_t *ev_hits, int32_t *ev_misses,
+                    int32_t *miss_list, int32_t *evict_list)
+{
+    if (L <= 0 || E <= 0 || C < k || C > E || k <= 0 || !ev_layer || !ev_ids)
+        return OR_EINVAL;
+    size_t n = (size_t)L * E;
+    char *res = calloc(n, 1);
+    int64_t *cnt = calloc(n, sizeof(int64_t));
+    int64_t *last = calloc(n, sizeof(int64_t));
+    char *inR = calloc((size_t)E, 1);
+    if (!res || !cnt || !last || !inR) {
+        free(res); free(cnt); free(last); free(inR);
+        return OR_ENOMEM;
+    }
+    for (int l = 0; l < L; l++)
+        for (int e = 0; e < C; e++) {
+            res[(size_t)l * E + e] = 1;
+            last[(size_t)l * E + e] = (int64_t)e - C;
+        }
+    int64_t clock = 0;
+    int rc = OR_OK;
+    for (int i = 0; i < n_ev; i++) {
+        int l = ev_layer[i];
+        const int32_t *R = ev_ids + (int64_t)i * k;
+        if (l < 0 || l >= L) { rc = OR_EINVAL; break; }
+        char *rl = res + (size_t)l * E;
+        int64_t *cl = cnt + (size_t)l * E, *tl = last + (size_t)l * E;
+        memset(inR, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            if (R[j] < 0 || R[j] >= E || inR[R[j]]) { rc = OR_EINVAL; break; }
+            inR[R[j]] = 1;
+        }
+        if (rc) break;
+        if (shift >= 0)
+            for (int e = 0; e < E; e++)
+                cl[e] -= cl[e] >> shift;
+        for (int e = 0; e < E; e++)
+            if (inR[e])
+                cl[e] += 65536;
+        int hits = 0, misses = 0;
+        for (int e = 0; e < E; e++)
+            if (inR[e] && rl[e]) {
+                tl[e] = ++clock;
+                hits++;
+            }
+        for (int e = 0; e < E; e++) {
+            if (!inR[e] || rl[e])
+                continue;
+            int v = -1;
+            for (int c = 0; c < E; c++) {
+                if (!rl[c] || inR[c])
+                    continue;
+                if (v < 0 || cl[c] < cl[v] || (cl[c] == cl[v] && tl[c] < tl[v]) ||
+                    (cl[c] == cl[v] && tl[c] == tl[v] && c < v))
+                    v = c;
+            }
+            rl[v] = 0;
+            rl[e] = 1;
+            tl[e] = ++clock;
+            if (miss_list) miss_list[(int64_t)i * k + misses] = e;
+            if (evict_list) evict_list[(int64_t)i * k + misses] = v;
+            misses++;
+        }
+        for (int j = misses; j < k; j++) {
+            if (miss_list) miss_list[(int64_t)i * k + j] = -1;
+            if (evict_list) evict_list[(int64_t)i * k + j] = -1;
+        }
+        if (ev_hits) ev_hits[i] = hits;
+        if (ev_misses) ev_misses[i] = misses;
+    }
+    free(res); free(cnt); free(last); free(inR);
+    return rc;
+}
+
+/* ------------------------------------------------ array helpers (tests) */
+
+void oracle_f16_to_f64_n(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f16_to_f64(in[i]);
+}
+
+void oracle_f64_to_f16_n(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f64_to_f16(in[i]);
+}
