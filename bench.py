@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 MoE hot path on one MI355X.
+
+Default workload (decode): 16 stacked OLMoE-shaped MoE layers (hidden 2048,
+64 experts, top-8, SwiGLU intermediate 1024, INT4 group 128 with fp16
+scales, all experts resident in HBM), one token per step, fresh x0 ~ N(0,1)
+per step, x_{l+1} = fp16(x_l + MoE_l(x_l)).  A step is route -> permute ->
+routed expert FFN -> combine for all 16 layers.  Prints one JSON line.
+
+    python bench.py [--steps 128] [--warmup 16] [--workload decode|batched]
+                    [--graph/--no-graph] [--no-cpu-baseline]
+
+The batched workload times single OLMoE-shaped layers at T = 64, 512, 4096
+(grouped INT4 -> LDS -> FP16 MFMA path) and reports MFMA utilisation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA, TFLOP/s
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def build_layers(cfg, layers, dev, torch, M):
+    """Device-resident layers: weights drawn by moe_inputs (numpy), quantised
+    and prepacked by the library's kernels."""
+    import moe_inputs as MI
+    from int4_weight_only_router_amd.layer import MoELayer, blob_table
+    _, total = M.moe_blob_layout(cfg.H, cfg.I, cfg.g)
+    out = []
+    for l in range(layers):
+        t0 = time.time()
+        blobs = torch.empty((cfg.E, total), dtype=torch.uint8, device=dev)
+        for b0 in range(0, cfg.E, 32):
+            ids = list(range(b0, min(cfg.E, b0 + 32)))
+            n = len(ids)
+            wg = torch.empty((n, cfg.I, cfg.H), dtype=torch.float32, device=dev)
+            wu = torch.empty((n, cfg.I, cfg.H), dtype=torch.float32, device=dev)
+            wd = torch.empty((n, cfg.H, cfg.I), dtype=torch.float32, device=dev)
+            for i, (e, (g_, u_, d_)) in enumerate(MI.gen_experts(cfg, l, ids)):
+                wg[i].copy_(torch.from_numpy(g_))
+                wu[i].copy_(torch.from_numpy(u_))
+                wd[i].copy_(torch.from_numpy(d_))
+            canon = torch.empty((n, total), dtype=torch.uint8, device=dev)
+            M.moe_quantize_experts(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, canon)
+            M.moe_prepack_experts(canon, n, cfg.H, cfg.I, cfg.g, blobs[b0:b0 + n])
+            del wg, wu, wd, canon
+        router = torch.from_numpy(MI.gen_router(cfg, l)).to(dev)
+        b = MI.zipf_bias(cfg, l)
+        bias = None if b is None else torch.from_numpy(b).to(dev)
+        lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, router, blob_table(blobs), bias,
+                       device=dev)
+        lay._blobs = blobs
+        out.append(lay)
+        torch.cuda.synchronize()
+        log("layer %d ready (%.1fs)" % (l, time.time() - t0))
+    return out, total
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def cpu_baseline_decode(cfg, layers, steps):
+    """The oracle (plain C, one thread) on `steps` decode steps of the same
+    16-layer chain; weight generation and oracle packing of the routed
+    experts happen outside the timer."""
+    import numpy as np
+    import moe_inputs as MI
+    import oracle as O
+    routers = [MI.gen_router(cfg, l) for l in range(layers)]
+    cache = {}
+    busy = 0.0
+    for s in range(steps):
+        x = MI.gen_x(cfg, 1, step=s)
+        for l in range(layers):
+            t0 = time.perf_counter()
+            idx, w, _ = O.route(x, routers[l], None, cfg.k)
+            counts, offsets, perm, inv = O.permute(idx, cfg.E)
+            busy += time.perf_counter() - t0
+            need = [e for e in np.unique(idx) if (l, int(e)) not in cache]
+            for e, wts in MI.gen_experts(cfg, l, need):
+                cache[(l, int(e))] = O.pack_expert(*wts, cfg.g)
+            blobs = [cache.get((l, e)) for e in range(cfg.E)]
+            t0 = time.perf_counter()
+            y = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g)
+            out, _ = O.combine(y, inv, w, None, x)
+            busy += time.perf_counter() - t0
+            x = out
+    return steps / busy, busy
+
+
+# ------------------------------------------------------------------ decode
+
+def run_decode(args, torch, M):
+    import numpy as np
+    import moe_inputs as MI
+    cfg = MI.OLMOE_DECODE
+    dev = "cuda:0"
+    L = cfg.layers
+    lays, blob_bytes = build_layers(cfg, L, dev, torch, M)
+    K, W = args.steps, args.warmup
+    xs = torch.from_numpy(np.concatenate([MI.gen_x(cfg, 1, step=s) for s in range(K + W)])).to(dev)
+    bufs = lays[0].buffers(1)
+    assert bufs.regime == M.MOE_REGIME_DECODE
+    act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        x = xs[s:s + 1]
+        for l, lay in enumerate(lays):
+            out = act[l & 1]
+            if ev is not None:
+                ev[l][0].record(stream)
+            lay.route_permute(x, bufs)
+            if ev is not None:
+                ev[l][1].record(stream)
+            lay.experts(x, bufs)
+            if ev is not None:
+                ev[l][2].record(stream)
+            lay.combine(bufs, residual=x, out=out)
+            if ev is not None:
+                ev[l][3].record(stream)
+            x = out
+        return x
+
+    log("warmup %d steps" % W)
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        # one captured step reading x0 from a fixed buffer; its input is
+        # refreshed by a device copy inside the same graph
+        xin = torch.empty((1, cfg.H), dtype=torch.float16, device=dev)
+        sel = torch.zeros(1, dtype=torch.int64, device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            xin.copy_(xs.index_select(0, sel))
+            x = xin
+            for l, lay in enumerate(lays):
+                out = act[l & 1]
+                lay.route_permute(x, bufs)
+                lay.experts(x, bufs)
+                lay.combine(bufs, residual=x, out=out)
+                x = out
+        graph = (g, sel)
+        for s in range(3):
+            sel.fill_(s)
+            g.replay()
+        torch.cuda.synchronize()
+
+    log("timed %d steps (graph=%s)" % (K, bool(graph)))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph:
+        g, sel = graph
+        for s in range(W, W + K):
+            sel.fill_(s)
+            g.replay()
+    else:
+        for s in range(W, W + K):
+            step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-kernel durations with events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+    ffn_ms, route_ms, comb_ms = [], [], []
+    for s in range(W, W + K):
+        step(s, ev)
+        torch.cuda.synchronize()
+        for l in range(L):
+            route_ms.append(ev[l][0].elapsed_time(ev[l][1]))
+            ffn_ms.append(ev[l][1].elapsed_time(ev[l][2]))
+            comb_ms.append(ev[l][2].elapsed_time(ev[l][3]))
+    ffn_avg = float(np.mean(ffn_ms))
+    counts = bufs.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    ffn_bytes = touched * blob_bytes + cfg.H * 2          # INT4 + scales of routed experts, x
+    achieved = ffn_bytes / (ffn_avg * 1e-3) / 1e9
+    ms_step = elapsed * 1e3 / K
+    res = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (batched), W4A16",
+        "value": round(K / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4-weights/f16-activations/f32-accumulate",
+        "data": "synthetic (seeded numpy draws: x ~ N(0,1), router ~ N(0,0.02), experts "
+                "~ N(0,0.02) quantised INT4 g128)",
+        "config": {"workload": "olmoe_decode: 16 MoE layers H=2048 E=64 top-8 I=1024 g=128, "
+                               "1 token/step, all experts resident",
+                   "layers": L, "tokens_per_step": 1, "graph": bool(graph)},
+        "layer_tokens_per_s": round(K * L / elapsed, 1),
+        "per_layer_us": {"route+permute": round(float(np.mean(route_ms)) * 1e3, 2),
+                         "expert_ffn": round(ffn_avg * 1e3, 2),
+                         "combine": round(float(np.mean(comb_ms)) * 1e3, 2)},
+        "roofline": {"kernel": "ffn_decode_kernel (moe_expert_ffn_w4a16, DECODE)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "alg_bytes_per_launch": ffn_bytes,
+                     "avg_launch_us": round(ffn_avg * 1e3, 3)},
+    }
+    if args.cpu_baseline:
+        log("cpu baseline (oracle, 1 thread)")
+        sps, busy = cpu_baseline_decode(cfg, L, args.cpu_steps)
+        res["cpu_baseline"] = {"value": round(sps, 4), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "%d decode steps x 16 layers (route, permute, fp64 "
+                                         "expert FFN, combine; %.1f s of CPU work)"
+                                         % (args.cpu_steps, busy)}
+    return res
+
+
+# ----------------------------------------------------------------- batched
+
+def run_batched(args, torch, M):
+    import numpy as np
+    import moe_inputs as MI
+    cfg = MI.OLMOE_BATCHED
+    dev = "cuda:0"
+    lays, blob_bytes = build_layers(cfg, 1, dev, torch, M)
+    lay = lays[0]
+    lines = []
+    for T in cfg.T:
+        x = torch.from_numpy(MI.gen_x(cfg, T)).to(dev)
+        b = lay.buffers(T)
+        for _ in range(args.warmup):
+            lay.forward(x, b)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ffn, tot = [], []
+        for _ in range(args.steps):
+            lay.route_permute(x, b)
+            e0.record()
+            lay.experts(x, b)
+            e1.record()
+            lay.combine(b)
+            e2.record()
+            torch.cuda.synchronize()
+            ffn.append(e0.elapsed_time(e1))
+            tot.append(e1.elapsed_time(e2))
+        ffn_ms = float(np.median(ffn))
+        flops = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I
+        counts = b.counts.cpu().numpy()
+        touched = int((counts > 0).sum())
+        tflops = flops / (ffn_ms * 1e-3) / 1e12
+        gbs = touched * blob_bytes / (ffn_ms * 1e-3) / 1e9
+        lines.append({"T": T, "expert_ffn_us": round(ffn_ms * 1e3, 1),
+                      "tflops": round(tflops, 1), "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                      "weight_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        log(str(lines[-1]))
+    return {"workload": "olmoe_batched", "results": lines}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", choices=["decode", "batched"], default="decode")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=True)
+    ap.add_argument("--no-graph", dest="graph", action="store_false")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path is built for one MI355X and no "
+              "multi-GPU path exists in this build (see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_weight_only_router_amd as M
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    M.lib()
+    if args.workload == "decode":
+        res = run_decode(args, torch, M)
+    else:
+        res = run_batched(args, torch, M)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,306 @@
+/*
+ * moe_w4a16.h -- C ABI of libmoe_w4a16.so, the MI355X (gfx950) hot path of a
+ * sparsely-activated Mixture-of-Experts layer with INT4 weight-only routed
+ * experts and FP16 activations (W4A16).
+ *
+ * Sources.  The pages describe the method, not an API:
+ *  - Horizon RunMap, "Prévia Técnica" (horizonrunmap.com/pt):
+ *    "02 / A solução", "03 / Arquitetura" -- the router chooses experts; own
+ *    kernels combine compact INT4 weights and FP16 scales with FP16
+ *    activations and hand the result back to the model, never keeping an
+ *    expanded expert; non-routed parts stay FP16; the optional slot cache
+ *    (resident-qpacked-cache-v1) with an immutable host source, temporary
+ *    slots, generation publish and consumer retirement.
+ *    "08 / Comportamento do modelo" -- W4 = INT4 expert weights with FP16
+ *    scales, A16 = FP16 activations, FP32 accumulation stages with explicit
+ *    roundings.
+ *  - Hamidun News, "Desenvolvedor do Strata cria mapa ao vivo de 24 576
+ *    especialistas MoE em uma GTX 1070", "Como 125 bilhões de parâmetros
+ *    cabem em 8 GB" -- hot experts resident, the rest loaded on demand,
+ *    eviction by an access counter with decay.
+ * Where the pages are silent (softmax form, tie-break, SwiGLU, group size,
+ * quantiser rounding, logit summation order, eviction constants) the
+ * functions follow fixed readings stated next to each declaration.
+ *
+ * Conventions
+ *  - Every function returns MOE_OK (0) or a negative MOE_E* code; a
+ *    thread-local message is available from moe_last_error().  No exception
+ *    crosses the ABI.
+ *  - Shapes and pointers are validated on the host before anything is
+ *    launched; on error nothing is launched and outputs are untouched.
+ *  - "device" pointers are HIP device memory (hipMalloc / torch CUDA
+ *    tensors) of the current device; "host" pointers are CPU memory.
+ *  - The caller allocates and owns every activation, weight, output and
+ *    workspace; compute calls never allocate.  The slot pool owns its HBM
+ *    slots, tables, side stream and events (allocated once at creation).
+ *  - Compute calls are asynchronous on the caller's stream and do not
+ *    synchronise with the host.  Inputs must be finite (not checked).
+ *  - Layouts are row-major; fp16 is IEEE binary16; int32 indices.
+ *
+ * Kernel envelope (MOE_EUNSUPPORTED outside it): H in {256, 512, 1024, 2048};
+ * I a multiple of 64 (up to 8192); group g in {32, 64, 128} dividing
+ * H and I; E <= 1024; k <= 16 and k <= E; T*k < 2^31.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ codes */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* null pointer, bad size, k > E, g does not divide H/I ... */
+    MOE_EUNSUPPORTED = -2,  /* valid but outside the kernel envelope */
+    MOE_ENOMEM = -3,        /* workspace too small, or pool allocation failed */
+    MOE_EHIP = -4,          /* a HIP runtime call failed (message has the hipError_t) */
+    MOE_ECAPACITY = -5,     /* the slot pool rejects the profile or the routed set */
+    MOE_ESTATE = -6         /* slot pool used out of order */
+};
+
+enum { MOE_RENORM = 1u };                       /* moe_route flag */
+enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2 };
+enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ------------------------------------------------------- expert blob */
+/*
+ * Canonical expert blob (Horizon RunMap "02 / A solução": compact weights
+ * and FP16 scales in separate formats; lucashiago.com.br explainer step 1:
+ * every block of weights carries its scale).  Six sections, each 256-byte
+ * aligned:  gate_q[I][H/2], up_q[I][H/2], down_q[H][I/2]  (u8: element 2b in
+ * the low nibble of byte b, element 2b+1 in the high nibble, stored as
+ * u = q + 8 with q in [-7, 7]) then gate_s[I][H/g], up_s[I][H/g],
+ * down_s[H][I/g] (fp16 scales, one per group of g along the input dim).
+ * W = q * s.  offsets[6] get the section offsets, *total_bytes the blob size.
+ * Host-only, no GPU needed.  MOE_EINVAL on bad sizes.
+ */
+int moe_blob_layout(int H, int I, int group, int64_t offsets[6], int64_t *total_bytes);
+
+/*
+ * Quantise n experts to canonical blobs on the device (symmetric group-wise
+ * INT4; reading: s = fp16_rne(fp32(amax/7)), q = clamp(rne(fp32(w/s)), -7, 7),
+ * q = 0 when s = 0).
+ *   wg, wu: device fp32 [n][I][H]; wd: device fp32 [n][H][I] (row-major)
+ *   blobs:  device, n consecutive blobs of total_bytes each (output)
+ * Offline step (load time), not part of the per-token path.
+ */
+int moe_quantize_experts(const float *wg, const float *wu, const float *wd,
+                         int n, int H, int I, int group, void *blobs, hipStream_t stream);
+
+/*
+ * Byte bijection from canonical blobs to the device layout the kernels read
+ * (same size; never expands to fp16).  Applied once at load, to resident
+ * weights and to the pinned source of the slot pool.
+ *   src: device, n canonical blobs; dst: device, n blobs (must not overlap src)
+ * Device layout: gate and up rows fused into 64-row blocks (32 gate rows then
+ * the 32 up rows of the same intermediate indices), down in 64-row blocks;
+ * inside a block, 32-element input chunks of all 64 rows are contiguous
+ * (16 bytes per row, nibbles interleaved for in-register conversion);
+ * scales in [block][group][64 rows] order.
+ */
+int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *dst,
+                        hipStream_t stream);
+
+/* Inverse of moe_prepack_experts (for inspection and tests). */
+int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *dst,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------ router */
+/*
+ * Router softmax + top-k (Horizon RunMap "03 / Arquitetura": the router
+ * selects the experts of each token; routing stays outside INT4, "08").
+ *   x_f16:        device fp16 [T][H] activations
+ *   w_router_f16: device fp16 [E][H]
+ *   logit_bias:   device fp32 [E] added to every logit after the dot product,
+ *                 or NULL
+ *   flags:        MOE_RENORM renormalises the k weights to sum to one
+ *   topk_idx:     device int32 [T][k] (output), experts by (logit desc,
+ *                 index asc) -- ties go to the lower expert index
+ *   topk_w:       device fp32 [T][k] (output), softmax over all E logits at
+ *                 the chosen experts
+ * Logits are fp32 in a fixed summation order (chunks of 8 elements of H go
+ * to partial (chunk mod 64) in increasing order, partials combined by an xor
+ * butterfly 32,16,8,4,2,1), so the indices are reproducible bit for bit.
+ * T = 0 is a no-op.
+ */
+int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bias,
+              int T, int H, int E, int k, unsigned flags,
+              int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/* ------------------------------------------------------- permutation */
+/*
+ * Token-to-expert grouping (the pages' grouped executor computes experts in
+ * groups, Horizon RunMap "04 / Resultados").  Stable counting sort of the
+ * flat index f = t*k + j by expert topk_idx[f]:
+ *   counts   device int32 [E]     tokens routed to each expert
+ *   offsets  device int32 [E+1]   exclusive scan of counts, offsets[E] = T*k
+ *   perm     device int32 [T*k]   sorted position -> f (f ascending per expert)
+ *   inv_perm device int32 [T*k]   f -> sorted position
+ * ws: device scratch of at least moe_permute_workspace_bytes(T, k, E) bytes
+ * (contents need no initialisation).  Bit-exact: one correct answer.
+ */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+int moe_permute(const int32_t *topk_idx, int T, int k, int E,
+                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ routed expert FFN */
+/*
+ * What moe_expert_ffn_w4a16 will do for a shape: the resolved regime (AUTO
+ * picks DECODE while T*k/E is small, else BATCHED), the dtype and number of
+ * slices of y, and the workspace it needs.  Host-only.
+ *   DECODE : y is fp32 [slices][T*k][H], partial sums over intermediate
+ *            slices of 32 (slices = I/32); moe_combine adds the slices.
+ *   BATCHED: y is fp16 [1][T*k][H].
+ */
+int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
+                        int *resolved_regime, int *y_dtype, int *y_slices,
+                        size_t *ws_bytes);
+
+/*
+ * Routed-expert SwiGLU FFN computed directly from INT4 weights
+ * (Horizon RunMap "03 / Arquitetura" and "08": the kernel reads compact
+ * weights and FP16 scales, converts what it needs during the computation,
+ * uses FP16 activations and FP32 accumulation, and never keeps an expanded
+ * expert).  For each sorted row p of expert e and token t = perm[p] / k:
+ *   h = silu(Wg[e] x_t) * (Wu[e] x_t),   y_p = Wd[e] h,   W = q * s.
+ *   x_f16          device fp16 [T][H]
+ *   perm, offsets  device, from moe_permute
+ *   d_expert_blobs device array of E device pointers to prepacked blobs
+ *                  (moe_prepack_experts); an entry may be NULL only for an
+ *                  expert no token routes to
+ *   y              device output, layout from moe_expert_ffn_plan; y_dtype
+ *                  and y_slices must equal the plan's (MOE_EINVAL otherwise)
+ *   ws             device scratch of the plan's size (may be NULL if 0)
+ * Rounding: DECODE converts h to fp16 before the down projection; BATCHED
+ * stores h and y as fp16.  Everything else accumulates in fp32.
+ */
+int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *offsets,
+                         const void *const *d_expert_blobs,
+                         int T, int H, int I, int E, int k, int group, int regime,
+                         void *y, int y_dtype, int y_slices,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ shared FP16 expert */
+/*
+ * Separate FP16 non-routed expert (Horizon RunMap "03": parts outside the
+ * routed experts stay FP16).  SwiGLU FFN applied to every token:
+ *   s_t = Wd (silu(Wg x_t) * (Wu x_t)),
+ *   wg, wu: device fp16 [Is][H];  wd: device fp16 [H][Is]  (row-major)
+ *   out_f32: device fp32 [T][H]
+ * h is rounded to fp16 between the projections; fp32 accumulation.
+ */
+size_t moe_shared_ffn_workspace_bytes(int T, int H, int Is);
+int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const void *wd,
+                       int T, int H, int Is, float *out_f32,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ combine */
+/*
+ * Router-weighted combine (Horizon RunMap "03": results go back to the rest
+ * of the model).  For each token t and column c:
+ *   out[t,c] = fp16_rne( r + sum_j w[t,j] * Y(inv_perm[t*k+j], c) + s[t,c] )
+ * where Y(p,c) is y[p,c] (y_dtype F16, y_slices 1) or the sum over slices of
+ * y[slice][p][c] (F32) taken in slice order, r = residual[t,c] or 0, s the
+ * shared-expert output or 0.  fp32 sum in the order: experts j = 0..k-1
+ * (each the slice sum), shared, residual; one final rounding.
+ *   y            device, from moe_expert_ffn_w4a16
+ *   inv_perm     device int32 [T*k];  topk_w device fp32 [T][k]
+ *   shared_f32   device fp32 [T][H] or NULL
+ *   residual_f16 device fp16 [T][H] or NULL (may alias out_f16)
+ *   out_f16      device fp16 [T][H]
+ */
+int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                const float *topk_w, const float *shared_f32, const void *residual_f16,
+                int T, int H, int k, void *out_f16, hipStream_t stream);
+
+/* ------------------------------------------------- expert slot pool */
+/*
+ * Partial residency (Horizon RunMap "03 / Arquitetura",
+ * resident-qpacked-cache-v1; "07 / De volta à oficina": hit, miss, discard):
+ * the complete INT4 source stays immutable in pinned host memory; each layer
+ * owns C resident slots plus S spare slots in HBM; a miss is copied into a
+ * spare slot on a side stream while readers keep the previous generation;
+ * once the routed group's copies complete, a new complete generation of the
+ * layer's expert table is published; an evicted slot is reused only after
+ * the kernels that read it have retired.  Capacity is fixed at creation.
+ * Eviction (Strata, decayed access counter; reading): per routed event of a
+ * layer, every counter of the layer decays c <- c - (c >> decay_shift)
+ * (decay_shift < 0: no decay), routed experts add 65536, hits then misses
+ * are touched in ascending id on a use clock, and each miss (ascending id)
+ * evicts the resident non-routed expert with the lowest (counter, last use,
+ * id).  decay_shift = 0 is plain LRU.  Initial placement: experts 0..C-1.
+ */
+typedef struct moe_pool *moe_pool_t;
+
+typedef struct {
+    int layers;            /* L */
+    int experts;           /* E per layer */
+    int topk;              /* k */
+    int capacity;          /* C resident slots per layer, k <= C <= E */
+    int spares;            /* S spare slots per layer, S >= k */
+    int decay_shift;       /* counter decay; < 0 disables decay */
+    int64_t expert_bytes;  /* bytes of one prepacked blob */
+} moe_pool_config;
+
+typedef struct {
+    int64_t hits, misses, evictions, h2d_bytes, generation;
+} moe_pool_stats_t;
+
+/*
+ * pinned_src: host array of L*E host pointers (index l*E + e), each a blob
+ * in device layout inside pinned host memory (hipHostMalloc); read-only.
+ * Allocates L*(C+S) slots and 2*L tables of E device pointers on the
+ * current device, a side stream and events, and uploads the initial
+ * placement (synchronously).  MOE_ECAPACITY if C < k, C > E, S < k, or the
+ * slots do not fit in free device memory; MOE_EINVAL on bad arguments.
+ */
+int moe_pool_create(const moe_pool_config *cfg, const void *const *pinned_src,
+                    moe_pool_t *out);
+
+/*
+ * Make the distinct experts among host_ids[0..n) (the layer's routed ids,
+ * copied to the host) resident and publish the layer's next generation.
+ * Misses are copied H2D on the side stream into spare slots (waiting for the
+ * retirement of earlier readers of those slots); the compute stream is made
+ * to wait for the copies and the table update.  *d_table_out receives the
+ * device array of E blob pointers to pass to moe_expert_ffn_w4a16 on
+ * `compute` (NULL for non-resident experts).  `step` (may be NULL) gets this
+ * call's counters (hits/misses/evictions/h2d_bytes; generation = new one).
+ * MOE_ECAPACITY if the routed set has more misses than spares or more
+ * distinct experts than C; MOE_ESTATE if the layer's previous generation was
+ * not retired.  On any error the previous generation and all counters are
+ * unchanged.
+ */
+int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
+                     hipStream_t compute, const void *const **d_table_out,
+                     moe_pool_stats_t *step);
+
+/* Record that every kernel enqueued on `compute` so far that reads the
+ * layer's current generation has been issued; slots evicted by it become
+ * reusable once those kernels finish.  MOE_ESTATE if nothing to retire. */
+int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute);
+
+/* Cumulative counters since creation or the last reset. */
+int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out);
+
+/* Waits for all pool work, restores the initial placement, clears counters. */
+int moe_pool_reset(moe_pool_t pool);
+
+/* Waits for all pool work and frees everything.  NULL is a no-op. */
+int moe_pool_destroy(moe_pool_t pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

@@ -1,0 +1,233 @@
+"""ctypes marshalling for libmoe_w4a16.so (see include/moe_w4a16.h)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+from . import build as _build
+
+__all__ = [
+    "MoEError", "lib", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOMEM", "MOE_EHIP",
+    "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
+    "MOE_REGIME_BATCHED", "MOE_DTYPE_F16", "MOE_DTYPE_F32", "EXPORTS",
+    "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
+    "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
+    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
+    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
+    "moe_pool_prepare", "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
+    "moe_pool_destroy",
+]
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_ESTATE = \
+    0, -1, -2, -3, -4, -5, -6
+MOE_RENORM = 1
+MOE_REGIME_AUTO, MOE_REGIME_DECODE, MOE_REGIME_BATCHED = 0, 1, 2
+MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
+
+# every symbol include/moe_w4a16.h declares
+EXPORTS = [
+    "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
+    "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
+    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
+    "moe_shared_ffn_f16", "moe_combine", "moe_pool_create", "moe_pool_prepare",
+    "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("moe error %d: %s" % (code, msg))
+        self.code = code
+
+
+class PoolConfig(C.Structure):
+    _fields_ = [("layers", C.c_int), ("experts", C.c_int), ("topk", C.c_int),
+                ("capacity", C.c_int), ("spares", C.c_int), ("decay_shift", C.c_int),
+                ("expert_bytes", C.c_int64)]
+
+
+class PoolStats(C.Structure):
+    _fields_ = [("hits", C.c_int64), ("misses", C.c_int64), ("evictions", C.c_int64),
+                ("h2d_bytes", C.c_int64), ("generation", C.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+
+
+def _declare(L):
+    sig = {
+        "moe_last_error": (C.c_char_p, []),
+        "moe_blob_layout": (i32, [i32, i32, i32, vp, vp]),
+        "moe_quantize_experts": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
+        "moe_prepack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
+        "moe_unpack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
+        "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp]),
+        "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_expert_ffn_plan": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "moe_expert_ffn_w4a16": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                       vp, i32, i32, vp, sz, vp]),
+        "moe_shared_ffn_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_shared_ffn_f16": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]),
+        "moe_combine": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_pool_create": (i32, [C.POINTER(PoolConfig), vp, C.POINTER(vp)]),
+        "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
+        "moe_pool_retire": (i32, [vp, i32, vp]),
+        "moe_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
+        "moe_pool_reset": (i32, [vp]),
+        "moe_pool_destroy": (i32, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def lib(path: str | None = None):
+    """Load (building in-tree first if absent) libmoe_w4a16.so."""
+    global _lib
+    if _lib is None:
+        path = path or _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        _lib = C.CDLL(path)
+        _declare(_lib)
+    return _lib
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc):
+    if rc != 0:
+        raise MoEError(rc, moe_last_error())
+    return rc
+
+
+def _p(t):
+    """Device/host pointer of a tensor (or an int address); None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- entries
+
+def moe_blob_layout(H, I, group):
+    off = (C.c_int64 * 6)()
+    tot = C.c_int64()
+    _check(lib().moe_blob_layout(H, I, group, off, C.byref(tot)))
+    return list(off), tot.value
+
+
+def moe_quantize_experts(wg, wu, wd, n, H, I, group, blobs, stream=None):
+    return _check(lib().moe_quantize_experts(_p(wg), _p(wu), _p(wd), n, H, I, group, _p(blobs),
+                                             _s(stream)))
+
+
+def moe_prepack_experts(src, n, H, I, group, dst, stream=None):
+    return _check(lib().moe_prepack_experts(_p(src), n, H, I, group, _p(dst), _s(stream)))
+
+
+def moe_unpack_experts(src, n, H, I, group, dst, stream=None):
+    return _check(lib().moe_unpack_experts(_p(src), n, H, I, group, _p(dst), _s(stream)))
+
+
+def moe_route(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk_w, stream=None):
+    return _check(lib().moe_route(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, flags,
+                                  _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def moe_permute_workspace_bytes(T, k, E):
+    return lib().moe_permute_workspace_bytes(T, k, E)
+
+
+def moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws=None, ws_bytes=0,
+                stream=None):
+    return _check(lib().moe_permute(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(perm),
+                                    _p(inv_perm), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_expert_ffn_plan(T, H, I, E, k, group, regime=MOE_REGIME_AUTO):
+    """Returns (resolved_regime, y_dtype, y_slices, ws_bytes)."""
+    r, dt, sl, ws = C.c_int(), C.c_int(), C.c_int(), C.c_size_t()
+    _check(lib().moe_expert_ffn_plan(T, H, I, E, k, group, regime, C.byref(r), C.byref(dt),
+                                     C.byref(sl), C.byref(ws)))
+    return r.value, dt.value, sl.value, ws.value
+
+
+def moe_expert_ffn_w4a16(x, perm, offsets, d_expert_blobs, T, H, I, E, k, group, regime, y,
+                         y_dtype, y_slices, ws=None, ws_bytes=0, stream=None):
+    return _check(lib().moe_expert_ffn_w4a16(
+        _p(x), _p(perm), _p(offsets), _p(d_expert_blobs), T, H, I, E, k, group, regime, _p(y),
+        y_dtype, y_slices, _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_shared_ffn_workspace_bytes(T, H, Is):
+    return lib().moe_shared_ffn_workspace_bytes(T, H, Is)
+
+
+def moe_shared_ffn_f16(x, wg, wu, wd, T, H, Is, out_f32, ws=None, ws_bytes=0, stream=None):
+    return _check(lib().moe_shared_ffn_f16(_p(x), _p(wg), _p(wu), _p(wd), T, H, Is, _p(out_f32),
+                                           _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, residual_f16, T, H, k,
+                out_f16, stream=None):
+    return _check(lib().moe_combine(_p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w),
+                                    _p(shared_f32), _p(residual_f16), T, H, k, _p(out_f16),
+                                    _s(stream)))
+
+
+def moe_pool_create(cfg: PoolConfig, pinned_src_ptrs):
+    """pinned_src_ptrs: sequence of L*E host addresses (ints)."""
+    arr = (C.c_void_p * len(pinned_src_ptrs))(*pinned_src_ptrs)
+    h = C.c_void_p()
+    _check(lib().moe_pool_create(C.byref(cfg), C.cast(arr, C.c_void_p), C.byref(h)))
+    return h
+
+
+def moe_pool_prepare(pool, layer, host_ids, n, compute=None):
+    """host_ids: host address (int) or a numpy int32 array.  Returns
+    (device table address, PoolStats of this step)."""
+    if hasattr(host_ids, "ctypes"):
+        host_ids = host_ids.ctypes.data
+    tab = C.c_void_p()
+    st = PoolStats()
+    _check(lib().moe_pool_prepare(pool, layer, host_ids, n, _s(compute), C.byref(tab),
+                                  C.byref(st)))
+    return tab.value, st
+
+
+def moe_pool_retire(pool, layer, compute=None):
+    return _check(lib().moe_pool_retire(pool, layer, _s(compute)))
+
+
+def moe_pool_stats(pool):
+    st = PoolStats()
+    _check(lib().moe_pool_stats(pool, C.byref(st)))
+    return st
+
+
+def moe_pool_reset(pool):
+    return _check(lib().moe_pool_reset(pool))
+
+
+def moe_pool_destroy(pool):
+    return _check(lib().moe_pool_destroy(pool))

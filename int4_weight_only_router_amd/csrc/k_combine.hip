@@ -1,0 +1,116 @@
+// k_combine.hip -- router-weighted combine (K6).
+//
+// Horizon RunMap "03 / Arquitetura": the experts' results return to the rest
+// of the model, weighted by the router.  For token t, column c:
+//   out = fp16_rne( sum_j w[t,j] * Y_j + s[t,c] + r[t,c] ),
+//   Y_j = sum over slices of y[slice][inv_perm[t*k+j]][c] (slice order),
+// summed in fp32 in exactly that order (j ascending, then shared, then
+// residual), so repeated runs give identical bits.
+#include "moe_common.h"
+
+namespace moe {
+
+// Decode partials: fp32 y [S][T*k][H].  Block = 16 expert slots x 16 columns;
+// thread (j, c) sums the S slices of its (expert, column) sequentially, then
+// the j = 0 threads fold the k weighted values in order.
+__global__ __launch_bounds__(256) void combine_slices_kernel(
+    const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
+    const float *__restrict__ w, const float *__restrict__ shared, const f16 *residual, int T,
+    int H, int k, f16 *out)
+{
+    __shared__ float part[16][17];
+    const int cc = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int t = blockIdx.y;
+    const int c = blockIdx.x * 16 + cc;
+    const size_t ntk = (size_t)T * k;
+    if (j < k && c < H) {
+        const size_t p = (size_t)inv_perm[(size_t)t * k + j];
+        const float *src = y + p * H + c;
+        float v = 0.0f;
+        for (int s = 0; s < S; ++s)
+            v += src[(size_t)s * ntk * H];
+        part[j][cc] = w[(size_t)t * k + j] * v;
+    }
+    __syncthreads();
+    if (j == 0 && c < H) {
+        float acc = 0.0f;
+        for (int jj = 0; jj < k; ++jj)
+            acc += part[jj][cc];
+        if (shared)
+            acc += shared[(size_t)t * H + c];
+        if (residual)
+            acc += (float)residual[(size_t)t * H + c];
+        out[(size_t)t * H + c] = (f16)acc;
+    }
+}
+
+// One slice (fp16 or fp32 y [T*k][H]): thread per (token, 8 columns).
+template <typename YT>
+__global__ __launch_bounds__(256) void combine_rows_kernel(
+    const YT *__restrict__ y, const int32_t *__restrict__ inv_perm, const float *__restrict__ w,
+    const float *__restrict__ shared, const f16 *residual, int T, int H, int k, f16 *out)
+{
+    const int per_row = H / 8;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)T * per_row)
+        return;
+    const int t = (int)(i / per_row);
+    const int c0 = (int)(i % per_row) * 8;
+    float acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        acc[m] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const size_t p = (size_t)inv_perm[(size_t)t * k + j];
+        const float wj = w[(size_t)t * k + j];
+        const YT *src = y + p * H + c0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m] += wj * (float)src[m];
+    }
+    if (shared) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m] += shared[(size_t)t * H + c0 + m];
+    }
+    if (residual) {
+        const half8_t r = *reinterpret_cast<const half8_t *>(residual + (size_t)t * H + c0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m] += (float)r[m];
+    }
+    half8_t o;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        o[m] = (f16)acc[m];
+    *reinterpret_cast<half8_t *>(out + (size_t)t * H + c0) = o;
+}
+
+int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, const float *w,
+                   const float *shared, const void *residual, int T, int H, int k, void *out,
+                   hipStream_t s)
+{
+    if (T == 0)
+        return MOE_OK;
+    const f16 *res = static_cast<const f16 *>(residual);
+    f16 *o = static_cast<f16 *>(out);
+    if (y_dtype == MOE_DTYPE_F32 && S > 1) {
+        dim3 grid((H + 15) / 16, T);
+        hipLaunchKernelGGL(combine_slices_kernel, grid, dim3(256), 0, s,
+                           static_cast<const float *>(y), S, inv_perm, w, shared, res, T, H, k, o);
+        MOE_LAUNCH_CHECK("combine_slices_kernel");
+        return MOE_OK;
+    }
+    const size_t n = (size_t)T * (H / 8);
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (y_dtype == MOE_DTYPE_F32)
+        hipLaunchKernelGGL(combine_rows_kernel<float>, grid, dim3(256), 0, s,
+                           static_cast<const float *>(y), inv_perm, w, shared, res, T, H, k, o);
+    else
+        hipLaunchKernelGGL(combine_rows_kernel<f16>, grid, dim3(256), 0, s,
+                           static_cast<const f16 *>(y), inv_perm, w, shared, res, T, H, k, o);
+    MOE_LAUNCH_CHECK("combine_rows_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,294 @@
+// k_ffn_decode.hip -- decode-regime routed expert FFN straight from INT4
+// weights (K3), and the FP16 GEMV pair of the shared expert at small T.
+//
+// Horizon RunMap "03 / Arquitetura" and "08 / Comportamento do modelo": the
+// expert kernel reads compact INT4 weights and FP16 scales, converts the
+// values it needs during the computation (here: in registers), multiplies
+// with FP16 activations and accumulates in FP32; no expanded copy of an
+// expert ever exists.  SwiGLU h = silu(Wg x) * (Wu x), y = Wd h.
+//
+// Decode kernel layout.  One workgroup per (intermediate slice of 32, active
+// expert).  In the device layout a slice is one fused 64-row block (32 gate
+// rows + the 32 up rows of the same intermediate indices) whose 32-element
+// input chunks are 1 KB contiguous runs: a wave reads one run with one 16-byte
+// load per lane, lane = weight row, and every lane dots its 32 nibbles with
+// the same 32 activations (broadcast from LDS).  No cross-lane reduction is
+// needed along K.  The waves split K, their partial sums meet in LDS, SwiGLU
+// is applied, and the 32 fp16 h values then multiply the slice's 32-column
+// strip of the down projection (one 1 KB run per 64 output rows).  Each
+// workgroup writes an fp32 partial y for its slice; moe_combine adds the
+// slices in order.  All weight loads of a workgroup are issued before any
+// arithmetic, so a workgroup keeps its whole ~96 KB in flight.
+#include "moe_common.h"
+
+namespace moe {
+
+// Finds the a-th expert (in id order) with at least one routed row; -1 if none.
+__device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ offsets, int E,
+                                                 int a, int lane)
+{
+    int seen = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const bool act = e < E && offsets[e + 1] > offsets[e];
+        const uint64_t m = __ballot(act);
+        const int n = __popcll(m);
+        if (seen + n > a) {
+            const int r = a - seen;
+            const int rank = __popcll(m & ((1ull << lane) - 1ull));
+            const uint64_t hit = __ballot(act && rank == r);
+            return e0 + (__ffsll((long long)hit) - 1);
+        }
+        seen += n;
+    }
+    return -1;
+}
+
+template <int H, int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
+    const f16 *__restrict__ x, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs, int I, int E,
+    int k, int g, int ntk, int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds,
+    float *__restrict__ y)
+{
+    constexpr int NK = H / 32;                 // input chunks of gate/up rows
+    constexpr int CPW = NK / NW;               // chunks per wave
+    constexpr int NRB = H / 64;                // 64-row blocks of the down projection
+    constexpr int RBW = (NRB + NW - 1) / NW;   // down blocks per wave
+    static_assert(NK % NW == 0, "H/32 must be a multiple of the wave count");
+
+    __shared__ __align__(16) f16 xs[H];
+    __shared__ float red[NW * 64];
+    __shared__ __align__(16) f16 hs[32];
+    __shared__ int s_e;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slice = blockIdx.x;
+
+    if (wave == 0) {
+        int e = nth_active_expert(offsets, E, blockIdx.y, lane);
+        if (lane == 0)
+            s_e = e;
+    }
+    __syncthreads();
+    const int e = s_e;
+    if (e < 0)
+        return;
+    const int p0 = offsets[e], p1 = offsets[e + 1];
+    const uint8_t *blob = blobs[e];
+    const int IC = I / 32;                     // input chunks of the down rows
+
+    // ---- issue every weight load of this workgroup up front
+    const uint4_t *guq = reinterpret_cast<const uint4_t *>(blob + off_guq) +
+                         ((size_t)slice * NK + (size_t)wave * CPW) * 64 + lane;
+    uint4_t wq[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+        wq[i] = guq[(size_t)i * 64];
+    const uint4_t *dqb = reinterpret_cast<const uint4_t *>(blob + off_dq);
+    uint4_t dq[RBW];
+#pragma unroll
+    for (int r = 0; r < RBW; ++r) {
+        const int rb = wave * RBW + r;
+        dq[r] = (rb < NRB) ? dqb[((size_t)rb * IC + slice) * 64 + lane] : uint4_t{0u, 0u, 0u, 0u};
+    }
+    const uint16_t *gus = reinterpret_cast<const uint16_t *>(blob + off_gus);
+    const uint16_t *dsc = reinterpret_cast<const uint16_t *>(blob + off_ds);
+    const int HG = H / g, IG = I / g;
+    float sgu[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int c = wave * CPW + i;
+        sgu[i] = h2f(gus[((size_t)slice * HG + (c * 32) / g) * 64 + lane]);
+    }
+    float sd[RBW];
+#pragma unroll
+    for (int r = 0; r < RBW; ++r) {
+        const int rb = wave * RBW + r;
+        sd[r] = (rb < NRB) ? h2f(dsc[((size_t)rb * IG + (slice * 32) / g) * 64 + lane]) : 0.0f;
+    }
+
+    for (int p = p0; p < p1; ++p) {
+        const int t = perm[p] / k;
+        {
+            const uint4_t *src = reinterpret_cast<const uint4_t *>(x + (size_t)t * H);
+            uint4_t *dst = reinterpret_cast<uint4_t *>(xs);
+            for (int i = threadIdx.x; i < H / 8; i += NW * 64)
+                dst[i] = src[i];
+        }
+        __syncthreads();
+
+        // gate/up rows (lane = row of the fused block), K split over waves
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int c = wave * CPW + i;
+            const half2_t *xc = reinterpret_cast<const half2_t *>(xs + c * 32);
+            half2_t q[16];
+            nib8_to_h2x4(wq[i].x, q + 0);
+            nib8_to_h2x4(wq[i].y, q + 4);
+            nib8_to_h2x4(wq[i].z, q + 8);
+            nib8_to_h2x4(wq[i].w, q + 12);
+            float d = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                d = dot2(q[m], xc[m], d);
+            acc = fmaf(d, sgu[i], acc);
+        }
+        red[wave * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                v += red[w * 64 + lane];
+            const float up = __shfl(v, (lane + 32) & 63, 64);
+            if (lane < 32) {
+                const float hv = v / (1.0f + expf(-v)) * up;
+                hs[lane] = (f16)hv;
+            }
+        }
+        __syncthreads();
+
+        // down strip: lane = output row, 32 h values from LDS
+        const half2_t *hh = reinterpret_cast<const half2_t *>(hs);
+        float *yrow = y + ((size_t)slice * ntk + p) * H;
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) {
+            const int rb = wave * RBW + r;
+            if (rb < NRB) {
+                half2_t q[16];
+                nib8_to_h2x4(dq[r].x, q + 0);
+                nib8_to_h2x4(dq[r].y, q + 4);
+                nib8_to_h2x4(dq[r].z, q + 8);
+                nib8_to_h2x4(dq[r].w, q + 12);
+                float d = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    d = dot2(q[m], hh[m], d);
+                yrow[rb * 64 + lane] = d * sd[r];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int H>
+static void launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
+                            const int32_t *offsets, const uint8_t *const *blobs, int I, int E,
+                            int k, int g, int ntk, const DevLayout &L, float *y)
+{
+    constexpr int NW = (H >= 1024) ? 8 : 4;
+    hipLaunchKernelGGL((ffn_decode_kernel<H, NW>), grid, dim3(NW * 64), 0, s, x, perm, offsets,
+                       blobs, I, E, k, g, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y);
+}
+
+int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
+                      const void *const *blobs, int T, int H, int I, int E, int k, int g,
+                      float *y, hipStream_t s)
+{
+    const int ntk = T * k;
+    if (ntk == 0)
+        return MOE_OK;
+    const DevLayout L = dev_layout(H, I, g);
+    dim3 grid(I / 32, (unsigned)min(E, ntk));
+    const f16 *xh = static_cast<const f16 *>(x);
+    const uint8_t *const *b = reinterpret_cast<const uint8_t *const *>(blobs);
+    switch (H) {
+    case 256: launch_decode_h<256>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
+    case 512: launch_decode_h<512>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
+    case 1024: launch_decode_h<1024>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
+    case 2048: launch_decode_h<2048>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
+    default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
+    }
+    MOE_LAUNCH_CHECK("ffn_decode_kernel");
+    return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------
+// FP16 GEMV pair for the shared expert at small T (weights row-major fp16,
+// the layout the caller hands over).  One wave per output row, lanes along K
+// with 16-byte loads, xor-butterfly reduction.
+//   swiglu=1: h[t][r] = fp16(silu(Wg[r].x_t) * (Wu[r].x_t)), r < R
+//   swiglu=0: out[t][r] = W[r].in_t (fp32), r < R
+constexpr int GEMV_WAVES = 4;
+
+template <int T_MAX>
+__global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
+    const f16 *__restrict__ in, const f16 *__restrict__ wa, const f16 *__restrict__ wb, int T,
+    int R, int K, int swiglu, f16 *__restrict__ hout, float *__restrict__ fout)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
+    if (r >= R)
+        return;
+    const int nch = K / 8;
+    const uint4_t *ra = reinterpret_cast<const uint4_t *>(wa + (size_t)r * K);
+    const uint4_t *rb = swiglu ? reinterpret_cast<const uint4_t *>(wb + (size_t)r * K) : nullptr;
+    float aa[T_MAX], bb[T_MAX];
+#pragma unroll
+    for (int t = 0; t < T_MAX; ++t) {
+        aa[t] = 0.0f;
+        bb[t] = 0.0f;
+    }
+    for (int c = lane; c < nch; c += 64) {
+        const half8_t va = __builtin_bit_cast(half8_t, ra[c]);
+        half8_t vb = {};
+        if (swiglu)
+            vb = __builtin_bit_cast(half8_t, rb[c]);
+#pragma unroll
+        for (int t = 0; t < T_MAX; ++t) {
+            if (t < T) {
+                const half8_t xv = __builtin_bit_cast(
+                    half8_t, reinterpret_cast<const uint4_t *>(in + (size_t)t * K)[c]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    half2_t xp = {xv[2 * m], xv[2 * m + 1]};
+                    half2_t ap = {va[2 * m], va[2 * m + 1]};
+                    aa[t] = dot2(ap, xp, aa[t]);
+                    if (swiglu) {
+                        half2_t bp = {vb[2 * m], vb[2 * m + 1]};
+                        bb[t] = dot2(bp, xp, bb[t]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T_MAX; ++t) {
+        if (t >= T)
+            break;
+        float a = aa[t], b = bb[t];
+#pragma unroll
+        for (int st = 32; st >= 1; st >>= 1) {
+            a += __shfl_xor(a, st, 64);
+            if (swiglu)
+                b += __shfl_xor(b, st, 64);
+        }
+        if (lane == 0) {
+            if (swiglu)
+                hout[(size_t)t * R + r] = (f16)(a / (1.0f + expf(-a)) * b);
+            else
+                fout[(size_t)t * R + r] = a;
+        }
+    }
+}
+
+int launch_shared_gemv(const void *x, const void *wg, const void *wu, const void *wd, int T,
+                       int H, int Is, float *out, void *ws, hipStream_t s)
+{
+    f16 *h = static_cast<f16 *>(ws);   // [T][Is]
+    dim3 b(GEMV_WAVES * 64);
+    hipLaunchKernelGGL(gemv_f16_kernel<4>, dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
+                       (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, 1, h,
+                       (float *)nullptr);
+    MOE_LAUNCH_CHECK("gemv_f16_kernel(gate/up)");
+    hipLaunchKernelGGL(gemv_f16_kernel<4>, dim3((H + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
+                       (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is, 0,
+                       (f16 *)nullptr, out);
+    MOE_LAUNCH_CHECK("gemv_f16_kernel(down)");
+    return MOE_OK;
+}
+
+}  // namespace moe

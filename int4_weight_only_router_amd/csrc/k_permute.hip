@@ -1,0 +1,204 @@
+// k_permute.hip -- token-to-expert grouping (K2).
+//
+// The pages' grouped executor computes the compact experts in groups
+// (Horizon RunMap, "04 / Resultados"); this kernel produces that grouping:
+// a stable counting sort of the flat index f = t*k + j by expert.
+//   counts[E], offsets[E+1] (exclusive scan), perm[p] = f, inv_perm[f] = p,
+// with f ascending inside each expert.  Integer work, one correct answer.
+//
+// Stability without atomics in the scatter: the flat range is cut into
+// chunks of CH elements in order; chunk b's elements of expert e start at
+// offsets[e] + (elements of e in chunks < b).  Inside a chunk one wave walks
+// the elements 64 at a time; a lane's rank among equal keys of earlier lanes
+// comes from a readlane sweep, and a per-expert running counter in LDS
+// advances by the group's multiplicity (LDS max of the new end positions).
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int PERM_CH = 512;     // elements per chunk in the multi-block path
+constexpr int PERM_SMALL = 512;  // up to this many elements: one wave does everything
+
+// Stable scatter of elements [f0, f1) by one wave, running counters in cnt[].
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ idx, int f0, int f1,
+                                             int E, int *cnt, int32_t *__restrict__ perm,
+                                             int32_t *__restrict__ inv_perm, int lane)
+{
+    for (int base = f0; base < f1; base += 64) {
+        const int f = base + lane;
+        int key = (f < f1) ? idx[f] : -1;
+        if ((unsigned)key >= (unsigned)E)   // out-of-range ids are skipped, never scattered
+            key = -1;
+        const bool valid = key >= 0;
+        int rank = 0;
+        const int nval = min(64, f1 - base);
+        for (int i = 0; i < nval; ++i) {
+            int ki = __builtin_amdgcn_readlane(key, i);
+            rank += (ki == key && i < lane) ? 1 : 0;
+        }
+        int pos = 0;
+        if (valid)
+            pos = cnt[key] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            atomicMax(&cnt[key], pos + 1);
+            perm[pos] = f;
+            inv_perm[f] = pos;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Whole sort in one wave (small T*k).
+__global__ __launch_bounds__(64) void permute_small_kernel(
+    const int32_t *__restrict__ idx, int n, int E, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
+{
+    extern __shared__ int cnt[];   // [E]
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64)
+        cnt[e] = 0;
+    __syncthreads();
+    for (int f = lane; f < n; f += 64)
+        if ((unsigned)idx[f] < (unsigned)E)
+            atomicAdd(&cnt[idx[f]], 1);
+    __syncthreads();
+    // exclusive scan over E in segments of per = ceil(E/64) experts per lane
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int seg = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E)
+            seg += cnt[e0 + i];
+    int incl = seg;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+        int o = __shfl_up(incl, st, 64);
+        if (lane >= st)
+            incl += o;
+    }
+    int run = incl - seg;
+    __syncthreads();
+    for (int i = 0; i < per; ++i) {
+        int e = e0 + i;
+        if (e < E) {
+            int c = cnt[e];
+            counts[e] = c;
+            offsets[e] = run;
+            cnt[e] = run;        // becomes the running write position
+            run += c;
+        }
+    }
+    if (lane == 63)
+        offsets[E] = run;
+    __syncthreads();
+    wave_scatter(idx, 0, n, E, cnt, perm, inv_perm, lane);
+}
+
+// Phase 1: per-chunk histograms hist[b][E].
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t *__restrict__ idx, int n,
+                                                           int E, int32_t *__restrict__ hist)
+{
+    extern __shared__ int h[];
+    const int b = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        h[e] = 0;
+    __syncthreads();
+    const int f0 = b * PERM_CH, f1 = min(n, f0 + PERM_CH);
+    for (int f = f0 + threadIdx.x; f < f1; f += blockDim.x)
+        if ((unsigned)idx[f] < (unsigned)E)
+            atomicAdd(&h[idx[f]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hist[(size_t)b * E + e] = h[e];
+}
+
+// Phase 2: counts, offsets and per-chunk bases (one block, thread per expert).
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    const int32_t *__restrict__ hist, int nb, int E, int n, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ base)
+{
+    __shared__ int wsum[16];
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E)
+        for (int b = 0; b < nb; ++b)
+            c += hist[(size_t)b * E + e];
+    // block exclusive scan of c over e
+    const int lane = e & 63, w = e >> 6;
+    int incl = c;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+        int o = __shfl_up(incl, st, 64);
+        if (lane >= st)
+            incl += o;
+    }
+    if (lane == 63)
+        wsum[w] = incl;
+    __syncthreads();
+    int pre = 0;
+    for (int i = 0; i < w; ++i)
+        pre += wsum[i];
+    const int off = pre + incl - c;
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+        int run = off;
+        for (int b = 0; b < nb; ++b) {
+            base[(size_t)b * E + e] = run;
+            run += hist[(size_t)b * E + e];
+        }
+    }
+    if (e == 0)
+        offsets[E] = n;
+}
+
+// Phase 3: stable scatter, one wave per chunk.
+__global__ __launch_bounds__(64) void permute_scatter_kernel(
+    const int32_t *__restrict__ idx, int n, int E, const int32_t *__restrict__ base,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
+{
+    extern __shared__ int cnt[];
+    const int b = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 64)
+        cnt[e] = base[(size_t)b * E + e];
+    __syncthreads();
+    const int f0 = b * PERM_CH, f1 = min(n, f0 + PERM_CH);
+    wave_scatter(idx, f0, f1, E, cnt, perm, inv_perm, threadIdx.x);
+}
+
+size_t permute_ws_bytes(int T, int k, int E)
+{
+    const int64_t n = (int64_t)T * k;
+    if (n <= PERM_SMALL)
+        return 0;
+    const int64_t nb = (n + PERM_CH - 1) / PERM_CH;
+    return (size_t)(2 * nb * E * sizeof(int32_t));
+}
+
+int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
+                   int32_t *perm, int32_t *inv_perm, void *ws, hipStream_t s)
+{
+    const int n = T * k;
+    if (n <= PERM_SMALL) {
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), E * sizeof(int), s, idx, n,
+                           E, counts, offsets, perm, inv_perm);
+        MOE_LAUNCH_CHECK("permute_small_kernel");
+        return MOE_OK;
+    }
+    const int nb = (n + PERM_CH - 1) / PERM_CH;
+    int32_t *hist = static_cast<int32_t *>(ws);
+    int32_t *base = hist + (size_t)nb * E;
+    hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(256), E * sizeof(int), s, idx, n, E,
+                       hist);
+    MOE_LAUNCH_CHECK("permute_hist_kernel");
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, E, n, counts,
+                       offsets, base);
+    MOE_LAUNCH_CHECK("permute_scan_kernel");
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(64), E * sizeof(int), s, idx, n, E,
+                       base, perm, inv_perm);
+    MOE_LAUNCH_CHECK("permute_scatter_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,189 @@
+// k_quant.hip -- load-time INT4 quantisation and the canonical <-> device
+// layout bijection of expert blobs.
+//
+// Horizon RunMap "08 / Comportamento do modelo": routed expert weights are
+// stored as INT4 with FP16 scales; lucashiago.com.br explainer, step 1: each
+// block of weights carries its scale.  Reading: symmetric groups of g along
+// the input dimension, s = fp16_rne(amax / 7) with amax / 7 in fp32,
+// q = clamp(rne(w / s), -7, 7) with w / s in fp32, q = 0 when s = 0; stored as
+// u = q + 8, element 2b in the low nibble of byte b.
+#include "moe_common.h"
+
+namespace moe {
+
+// One thread per 32-element chunk of a row; a group of g spans g/32 adjacent
+// threads of one wave, which share the group maximum through lane shuffles.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const float *__restrict__ w, int64_t w_stride, int rows, int K, int g,
+    uint8_t *__restrict__ blobs, int64_t blob_stride, int64_t off_q, int64_t off_s)
+{
+    const int n = blockIdx.y;
+    const int nch = K / 32;
+    const int64_t cid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool valid = cid < (int64_t)rows * nch;
+    const int row = valid ? (int)(cid / nch) : 0;
+    const int c = valid ? (int)(cid % nch) : 0;
+    const float *src = w + n * w_stride + (int64_t)row * K + c * 32;
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float4_t f = valid ? *reinterpret_cast<const float4_t *>(src + 4 * i)
+                           : float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            v[4 * i + m] = f[m];
+            amax = fmaxf(amax, fabsf(f[m]));
+        }
+    }
+    const int span = g / 32;   // 1, 2 or 4 threads per group
+    for (int st = 1; st < span; st <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, st, 64));
+    if (!valid)
+        return;
+    const f16 sh = (f16)(amax / 7.0f);
+    const float sv = (float)sh;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        int q = 0;
+        if (sv != 0.0f) {
+            float r = rintf(v[i] / sv);
+            r = fminf(fmaxf(r, -7.0f), 7.0f);
+            q = (int)r;
+        }
+        const uint32_t u = (uint32_t)(q + 8);
+        words[i >> 3] |= u << (4 * (i & 7));   // canonical: element i at bits 4i of the chunk
+    }
+    uint8_t *blob = blobs + n * blob_stride;
+    *reinterpret_cast<uint4_t *>(blob + off_q + (int64_t)row * (K / 2) + c * 16) =
+        uint4_t{words[0], words[1], words[2], words[3]};
+    if ((c * 32) % g == 0)
+        reinterpret_cast<f16 *>(blob + off_s)[(int64_t)row * (K / g) + (c * 32) / g] = sh;
+}
+
+__device__ __forceinline__ uint32_t canon_to_dev(uint32_t cw)
+{
+    uint32_t d = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        d |= ((cw >> (8 * i)) & 0xFu) << (4 * i);
+        d |= ((cw >> (8 * i + 4)) & 0xFu) << (16 + 4 * i);
+    }
+    return d;
+}
+
+__device__ __forceinline__ uint32_t dev_to_canon(uint32_t dw)
+{
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c |= ((dw >> (4 * i)) & 0xFu) << (8 * i);
+        c |= ((dw >> (16 + 4 * i)) & 0xFu) << (8 * i + 4);
+    }
+    return c;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4_t *p, int64_t n16)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = uint4_t{0u, 0u, 0u, 0u};
+}
+
+// Item ranges: [0,nguq) fused gate/up 16-byte chunks, then down chunks, then
+// fused gate/up scales, then down scales.  dir = 0: canonical -> device.
+__global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict__ src,
+                                                      uint8_t *__restrict__ dst, int H, int I,
+                                                      int g, int64_t stride, CanonLayout C,
+                                                      DevLayout D, int dir)
+{
+    const int n = blockIdx.y;
+    const int NKH = H / 32, NKI = I / 32, HG = H / g, IG = I / g;
+    const int64_t nguq = (int64_t)(I / 32) * NKH * 64;
+    const int64_t ndq = (int64_t)(H / 64) * NKI * 64;
+    const int64_t ngus = (int64_t)(I / 32) * HG * 64;
+    const int64_t nds = (int64_t)(H / 64) * IG * 64;
+    const uint8_t *s = src + n * stride;
+    uint8_t *d = dst + n * stride;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nguq + ndq + ngus + nds;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t devoff, canoff;
+        int kind;   // 0 = 16-byte nibble chunk, 1 = 2-byte scale
+        if (i < nguq) {
+            const int64_t b = i / (NKH * 64), c = (i / 64) % NKH, r = i % 64;
+            const int64_t row = 32 * b + (r & 31);
+            devoff = D.gu_q + i * 16;
+            canoff = (r < 32 ? C.gate_q : C.up_q) + row * (H / 2) + c * 16;
+            kind = 0;
+        } else if (i < nguq + ndq) {
+            const int64_t j = i - nguq;
+            const int64_t b = j / (NKI * 64), c = (j / 64) % NKI, r = j % 64;
+            devoff = D.d_q + j * 16;
+            canoff = C.down_q + (64 * b + r) * (I / 2) + c * 16;
+            kind = 0;
+        } else if (i < nguq + ndq + ngus) {
+            const int64_t j = i - nguq - ndq;
+            const int64_t b = j / (HG * 64), G = (j / 64) % HG, r = j % 64;
+            devoff = D.gu_s + j * 2;
+            canoff = (r < 32 ? C.gate_s : C.up_s) + ((32 * b + (r & 31)) * HG + G) * 2;
+            kind = 1;
+        } else {
+            const int64_t j = i - nguq - ndq - ngus;
+            const int64_t b = j / (IG * 64), G = (j / 64) % IG, r = j % 64;
+            devoff = D.d_s + j * 2;
+            canoff = C.down_s + ((64 * b + r) * IG + G) * 2;
+            kind = 1;
+        }
+        if (kind == 0) {
+            const uint4_t v = *reinterpret_cast<const uint4_t *>(s + (dir == 0 ? canoff : devoff));
+            uint4_t o;
+            if (dir == 0)
+                o = uint4_t{canon_to_dev(v.x), canon_to_dev(v.y), canon_to_dev(v.z),
+                            canon_to_dev(v.w)};
+            else
+                o = uint4_t{dev_to_canon(v.x), dev_to_canon(v.y), dev_to_canon(v.z),
+                            dev_to_canon(v.w)};
+            *reinterpret_cast<uint4_t *>(d + (dir == 0 ? devoff : canoff)) = o;
+        } else {
+            *reinterpret_cast<uint16_t *>(d + (dir == 0 ? devoff : canoff)) =
+                *reinterpret_cast<const uint16_t *>(s + (dir == 0 ? canoff : devoff));
+        }
+    }
+}
+
+int launch_quantize(const float *wg, const float *wu, const float *wd, int n, int H, int I, int g,
+                    void *blobs, hipStream_t s)
+{
+    const CanonLayout C = canon_layout(H, I, g);
+    uint8_t *b = static_cast<uint8_t *>(blobs);
+    hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, s, (uint4_t *)b,
+                       (int64_t)n * C.total / 16);
+    MOE_LAUNCH_CHECK("zero_kernel");
+    struct P { const float *w; int rows, K; int64_t q, sc; } ps[3] = {
+        {wg, I, H, C.gate_q, C.gate_s}, {wu, I, H, C.up_q, C.up_s}, {wd, H, I, C.down_q, C.down_s}};
+    for (const P &p : ps) {
+        const int64_t chunks = (int64_t)p.rows * (p.K / 32);
+        dim3 grid((unsigned)((chunks + 255) / 256), n);
+        hipLaunchKernelGGL(quantize_rows_kernel, grid, dim3(256), 0, s, p.w,
+                           (int64_t)p.rows * p.K, p.rows, p.K, g, b, C.total, p.q, p.sc);
+        MOE_LAUNCH_CHECK("quantize_rows_kernel");
+    }
+    return MOE_OK;
+}
+
+int launch_prepack(const void *src, int n, int H, int I, int g, void *dst, int dir, hipStream_t s)
+{
+    const CanonLayout C = canon_layout(H, I, g);
+    const DevLayout D = dev_layout(H, I, g);
+    hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, s, (uint4_t *)dst,
+                       (int64_t)n * C.total / 16);
+    MOE_LAUNCH_CHECK("zero_kernel");
+    hipLaunchKernelGGL(prepack_kernel, dim3(512, n), dim3(256), 0, s,
+                       static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), H, I, g,
+                       C.total, C, D, dir);
+    MOE_LAUNCH_CHECK("prepack_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe

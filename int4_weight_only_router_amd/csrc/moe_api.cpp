@@ -1,0 +1,299 @@
+// moe_api.cpp -- the C ABI of libmoe_w4a16: argument validation, regime
+// choice and dispatch to the HIP kernels.  Nothing here computes on the host.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "moe_common.h"
+
+namespace moe {
+
+static thread_local std::string g_err;
+
+int set_error(int code, const char *fmt, ...)
+{
+    char buf[768];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+void clear_error() { g_err.clear(); }
+
+// kernels (defined in the .hip files)
+int launch_route(const void *, const void *, const float *, int, int, int, int, unsigned,
+                 int32_t *, float *, hipStream_t);
+size_t permute_ws_bytes(int T, int k, int E);
+int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
+                   void *, hipStream_t);
+int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *, int,
+                      int, int, int, int, int, float *, hipStream_t);
+size_t ffn_batched_ws_bytes(int T, int I, int k);
+int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
+                       int, int, int, int, int, void *, void *, hipStream_t);
+int launch_shared_gemv(const void *, const void *, const void *, const void *, int, int, int,
+                       float *, void *, hipStream_t);
+int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
+                          float *, void *, hipStream_t);
+int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
+                   const void *, int, int, int, void *, hipStream_t);
+int launch_quantize(const float *, const float *, const float *, int, int, int, int, void *,
+                    hipStream_t);
+int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
+
+constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
+constexpr int SHARED_GEMV_MAX_T = 4;  // shared expert: GEMV up to this many tokens
+
+static int check_expert_shape(const char *fn, int H, int I, int g)
+{
+    if (H <= 0 || I <= 0 || g <= 0)
+        return set_error(MOE_EINVAL, "%s: non-positive size (H=%d I=%d g=%d)", fn, H, I, g);
+    if (g % 32 || H % g || I % g)
+        return set_error(MOE_EINVAL, "%s: group %d must be a multiple of 32 dividing H=%d, I=%d",
+                         fn, g, H, I);
+    if (!h_supported(H) || I % 64 || I > 8192 || (g != 32 && g != 64 && g != 128))
+        return set_error(MOE_EUNSUPPORTED,
+                         "%s: outside the kernel envelope (H in {256, 512, 1024, 2048}, "
+                         "I %% 64 == 0 and <= 8192, g in {32,64,128}); got H=%d I=%d g=%d",
+                         fn, H, I, g);
+    return MOE_OK;
+}
+
+static int check_route_shape(const char *fn, int T, int E, int k)
+{
+    if (T < 0 || E <= 0 || k <= 0 || k > E)
+        return set_error(MOE_EINVAL, "%s: need T >= 0, E > 0, 0 < k <= E (T=%d E=%d k=%d)", fn,
+                         T, E, k);
+    if (E > 1024 || k > 16)
+        return set_error(MOE_EUNSUPPORTED, "%s: E <= 1024 and k <= 16 required (E=%d k=%d)", fn,
+                         E, k);
+    if ((int64_t)T * k >= (int64_t)1 << 31)
+        return set_error(MOE_EUNSUPPORTED, "%s: T*k too large", fn);
+    return MOE_OK;
+}
+
+static int resolve_regime(int T, int regime)
+{
+    if (regime == MOE_REGIME_AUTO)
+        return T <= DECODE_MAX_T ? MOE_REGIME_DECODE : MOE_REGIME_BATCHED;
+    return regime;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+int moe_blob_layout(int H, int I, int group, int64_t offsets[6], int64_t *total_bytes)
+{
+    clear_error();
+    if (!offsets || !total_bytes || H <= 0 || I <= 0 || group <= 0 || H % group || I % group ||
+        H % 2 || I % 2)
+        return set_error(MOE_EINVAL, "moe_blob_layout: bad arguments (H=%d I=%d g=%d)", H, I,
+                         group);
+    const CanonLayout L = canon_layout(H, I, group);
+    offsets[0] = L.gate_q;
+    offsets[1] = L.up_q;
+    offsets[2] = L.down_q;
+    offsets[3] = L.gate_s;
+    offsets[4] = L.up_s;
+    offsets[5] = L.down_s;
+    *total_bytes = L.total;
+    return MOE_OK;
+}
+
+int moe_quantize_experts(const float *wg, const float *wu, const float *wd, int n, int H, int I,
+                         int group, void *blobs, hipStream_t stream)
+{
+    clear_error();
+    if (!wg || !wu || !wd || !blobs || n < 0)
+        return set_error(MOE_EINVAL, "moe_quantize_experts: null pointer or n < 0");
+    int rc = check_expert_shape("moe_quantize_experts", H, I, group);
+    if (rc || n == 0)
+        return rc;
+    return launch_quantize(wg, wu, wd, n, H, I, group, blobs, stream);
+}
+
+static int prepack_common(const char *fn, const void *src, int n, int H, int I, int group,
+                          void *dst, int dir, hipStream_t stream)
+{
+    clear_error();
+    if (!src || !dst || n < 0)
+        return set_error(MOE_EINVAL, "%s: null pointer or n < 0", fn);
+    int rc = check_expert_shape(fn, H, I, group);
+    if (rc || n == 0)
+        return rc;
+    const int64_t tot = canon_layout(H, I, group).total * (int64_t)n;
+    const char *a = static_cast<const char *>(src), *b = static_cast<const char *>(dst);
+    if (a < b + tot && b < a + tot)
+        return set_error(MOE_EINVAL, "%s: src and dst overlap", fn);
+    return launch_prepack(src, n, H, I, group, dst, dir, stream);
+}
+
+int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *dst,
+                        hipStream_t stream)
+{
+    return prepack_common("moe_prepack_experts", src, n, H, I, group, dst, 0, stream);
+}
+
+int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *dst,
+                       hipStream_t stream)
+{
+    return prepack_common("moe_unpack_experts", src, n, H, I, group, dst, 1, stream);
+}
+
+int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T, int H,
+              int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_route_shape("moe_route", T, E, k);
+    if (rc)
+        return rc;
+    if (T > 0 && (!x_f16 || !w_router_f16 || !topk_idx || !topk_w))
+        return set_error(MOE_EINVAL, "moe_route: null pointer");
+    if (H <= 0 || H % 8)
+        return set_error(MOE_EINVAL, "moe_route: H=%d must be a positive multiple of 8", H);
+    if (H > 8192)
+        return set_error(MOE_EUNSUPPORTED, "moe_route: H=%d > 8192", H);
+    if (flags & ~(unsigned)MOE_RENORM)
+        return set_error(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
+    return launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
+                        stream);
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E)
+{
+    if (T < 0 || k <= 0 || E <= 0)
+        return 0;
+    return permute_ws_bytes(T, k, E);
+}
+
+int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
+                int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_route_shape("moe_permute", T, E, k);
+    if (rc)
+        return rc;
+    if (!counts || !offsets || (T > 0 && (!topk_idx || !perm || !inv_perm)))
+        return set_error(MOE_EINVAL, "moe_permute: null pointer");
+    const size_t need = permute_ws_bytes(T, k, E);
+    if (need && (!ws || ws_bytes < need))
+        return set_error(MOE_ENOMEM, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
+    return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws, stream);
+}
+
+int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
+                        int *resolved_regime, int *y_dtype, int *y_slices, size_t *ws_bytes)
+{
+    clear_error();
+    int rc = check_route_shape("moe_expert_ffn_plan", T, E, k);
+    if (rc)
+        return rc;
+    rc = check_expert_shape("moe_expert_ffn_plan", H, I, group);
+    if (rc)
+        return rc;
+    if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_BATCHED)
+        return set_error(MOE_EINVAL, "moe_expert_ffn_plan: bad regime %d", regime);
+    const int r = resolve_regime(T, regime);
+    if (resolved_regime)
+        *resolved_regime = r;
+    if (y_dtype)
+        *y_dtype = (r == MOE_REGIME_DECODE) ? MOE_DTYPE_F32 : MOE_DTYPE_F16;
+    if (y_slices)
+        *y_slices = (r == MOE_REGIME_DECODE) ? I / 32 : 1;
+    if (ws_bytes)
+        *ws_bytes = (r == MOE_REGIME_DECODE) ? 0 : ffn_batched_ws_bytes(T, I, k);
+    return MOE_OK;
+}
+
+int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *offsets,
+                         const void *const *d_expert_blobs, int T, int H, int I, int E, int k,
+                         int group, int regime, void *y, int y_dtype, int y_slices, void *ws,
+                         size_t ws_bytes, hipStream_t stream)
+{
+    int r = 0, dt = 0, sl = 0;
+    size_t need = 0;
+    int rc = moe_expert_ffn_plan(T, H, I, E, k, group, regime, &r, &dt, &sl, &need);
+    if (rc)
+        return rc;
+    if (y_dtype != dt || y_slices != sl)
+        return set_error(MOE_EINVAL,
+                         "moe_expert_ffn_w4a16: y must be dtype %d with %d slices for this "
+                         "regime (got dtype %d, %d slices)",
+                         dt, sl, y_dtype, y_slices);
+    if (T == 0)
+        return MOE_OK;
+    if (!x_f16 || !perm || !offsets || !d_expert_blobs || !y)
+        return set_error(MOE_EINVAL, "moe_expert_ffn_w4a16: null pointer");
+    if (need && (!ws || ws_bytes < need))
+        return set_error(MOE_ENOMEM, "moe_expert_ffn_w4a16: workspace %zu < %zu bytes", ws_bytes,
+                         need);
+    if (r == MOE_REGIME_DECODE)
+        return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group,
+                                 static_cast<float *>(y), stream);
+    return launch_ffn_batched(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
+                              stream);
+}
+
+size_t moe_shared_ffn_workspace_bytes(int T, int H, int Is)
+{
+    (void)H;
+    if (T <= 0 || Is <= 0)
+        return 0;
+    return (size_t)al256((int64_t)T * Is * 2);
+}
+
+int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const void *wd, int T,
+                       int H, int Is, float *out_f32, void *ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    clear_error();
+    if (T < 0 || H <= 0 || Is <= 0)
+        return set_error(MOE_EINVAL, "moe_shared_ffn_f16: bad sizes T=%d H=%d Is=%d", T, H, Is);
+    if (!h_supported(H) || Is % 64 || Is > 8192)
+        return set_error(MOE_EUNSUPPORTED,
+                         "moe_shared_ffn_f16: outside the envelope (H=%d, Is=%d)", H, Is);
+    if (T == 0)
+        return MOE_OK;
+    if (!x_f16 || !wg || !wu || !wd || !out_f32)
+        return set_error(MOE_EINVAL, "moe_shared_ffn_f16: null pointer");
+    const size_t need = moe_shared_ffn_workspace_bytes(T, H, Is);
+    if (!ws || ws_bytes < need)
+        return set_error(MOE_ENOMEM, "moe_shared_ffn_f16: workspace %zu < %zu bytes", ws_bytes,
+                         need);
+    if (T <= SHARED_GEMV_MAX_T)
+        return launch_shared_gemv(x_f16, wg, wu, wd, T, H, Is, out_f32, ws, stream);
+    return launch_shared_batched(x_f16, wg, wu, wd, T, H, Is, out_f32, ws, stream);
+}
+
+int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                const float *topk_w, const float *shared_f32, const void *residual_f16, int T,
+                int H, int k, void *out_f16, hipStream_t stream)
+{
+    clear_error();
+    if (T < 0 || H <= 0 || k <= 0 || k > 16 || y_slices <= 0)
+        return set_error(MOE_EINVAL, "moe_combine: bad sizes T=%d H=%d k=%d slices=%d", T, H, k,
+                         y_slices);
+    if (y_dtype != MOE_DTYPE_F16 && y_dtype != MOE_DTYPE_F32)
+        return set_error(MOE_EINVAL, "moe_combine: bad y dtype %d", y_dtype);
+    if (y_dtype == MOE_DTYPE_F16 && y_slices != 1)
+        return set_error(MOE_EINVAL, "moe_combine: fp16 y has exactly one slice");
+    if (H % 8)
+        return set_error(MOE_EUNSUPPORTED, "moe_combine: H=%d must be a multiple of 8", H);
+    if (T == 0)
+        return MOE_OK;
+    if (!y || !inv_perm || !topk_w || !out_f16)
+        return set_error(MOE_EINVAL, "moe_combine: null pointer");
+    return launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, residual_f16, T, H,
+                          k, out_f16, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// moe_common.h -- internal helpers of libmoe_w4a16 (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ errors (host)
+
+int set_error(int code, const char *fmt, ...);   // stores a thread-local message
+void clear_error();
+
+#define MOE_HIP_TRY(expr)                                                        \
+    do {                                                                         \
+        hipError_t _e = (expr);                                                  \
+        if (_e != hipSuccess)                                                    \
+            return ::moe::set_error(MOE_EHIP, "%s failed: %s (%d)", #expr,        \
+                                    hipGetErrorString(_e), (int)_e);             \
+    } while (0)
+
+// Launch check: a bad launch configuration is reported by hipGetLastError.
+#define MOE_LAUNCH_CHECK(what)                                                   \
+    do {                                                                         \
+        hipError_t _e = hipGetLastError();                                       \
+        if (_e != hipSuccess)                                                    \
+            return ::moe::set_error(MOE_EHIP, "launch of %s failed: %s (%d)",     \
+                                    what, hipGetErrorString(_e), (int)_e);       \
+    } while (0)
+
+inline int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Canonical blob section offsets (format documented in moe_w4a16.h).
+struct CanonLayout {
+    int64_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+};
+inline CanonLayout canon_layout(int H, int I, int g) {
+    CanonLayout L;
+    int64_t o = 0;
+    L.gate_q = o; o = al256(o + int64_t(I) * H / 2);
+    L.up_q = o;   o = al256(o + int64_t(I) * H / 2);
+    L.down_q = o; o = al256(o + int64_t(H) * I / 2);
+    L.gate_s = o; o = al256(o + int64_t(I) * (H / g) * 2);
+    L.up_s = o;   o = al256(o + int64_t(I) * (H / g) * 2);
+    L.down_s = o; o = al256(o + int64_t(H) * (I / g) * 2);
+    L.total = o;
+    return L;
+}
+
+// Device (prepacked) layout inside a blob of the same total size:
+//   gu_q : fused gate/up INT4, I/32 blocks x (H/32 chunks) x 64 rows x 16 B
+//   d_q  : down INT4, H/64 blocks x (I/32 chunks) x 64 rows x 16 B
+//   gu_s : fused gate/up scales, I/32 blocks x (H/g) x 64 rows fp16
+//   d_s  : down scales, H/64 blocks x (I/g) x 64 rows fp16
+struct DevLayout {
+    int64_t gu_q, d_q, gu_s, d_s, end;
+};
+inline DevLayout dev_layout(int H, int I, int g) {
+    DevLayout L;
+    int64_t o = 0;
+    L.gu_q = o; o = al256(o + int64_t(I) * H);
+    L.d_q = o;  o = al256(o + int64_t(H) * I / 2);
+    L.gu_s = o; o = al256(o + int64_t(2) * I * (H / g) * 2);
+    L.d_s = o;  o = o + int64_t(H) * (I / g) * 2;
+    L.end = o;
+    return L;
+}
+
+// Shape envelope shared by the expert kernels.
+inline bool h_supported(int H) {
+    return H == 256 || H == 512 || H == 1024 || H == 2048;
+}
+
+// ------------------------------------------------------------- device side
+
+typedef _Float16 f16;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+
+// Four packed nibble pairs of one dword -> four fp16 pairs (q0,q1) .. (q6,q7)
+// with q = u - 8.  Dword layout (device format): element 2i in bits [4i,4i+4),
+// element 2i+1 in bits [16+4i, 16+4i+4), i = 0..3.  OR-ing a nibble into the
+// mantissa of 1024.0 (0x6400) gives 1024 + u exactly; a nibble at bits 4..7
+// gives 1024 + 16u.  Both decode exactly to u - 8.
+__device__ __forceinline__ void nib8_to_h2x4(uint32_t w, half2_t out[4]) {
+    const uint32_t M = 0x64006400u;
+    uint32_t a = (w & 0x000F000Fu) | M;
+    uint32_t b = (w & 0x00F000F0u) | M;
+    uint32_t w8 = w >> 8;
+    uint32_t c = (w8 & 0x000F000Fu) | M;
+    uint32_t d = (w8 & 0x00F000F0u) | M;
+    const half2_t k1032 = {(f16)-1032.0f, (f16)-1032.0f};
+    const half2_t s16 = {(f16)0.0625f, (f16)0.0625f};
+    const half2_t k72 = {(f16)-72.0f, (f16)-72.0f};
+    out[0] = __builtin_bit_cast(half2_t, a) + k1032;
+    out[1] = __builtin_bit_cast(half2_t, b) * s16 + k72;
+    out[2] = __builtin_bit_cast(half2_t, c) + k1032;
+    out[3] = __builtin_bit_cast(half2_t, d) * s16 + k72;
+}
+
+__device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+    return (float)__builtin_bit_cast(f16, bits);
+}
+
+}  // namespace moe

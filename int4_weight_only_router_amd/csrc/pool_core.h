@@ -1,0 +1,252 @@
+// pool_core.h -- expert slot pool for partial residency: policy, slot
+// bookkeeping and the generation protocol, independent of how bytes move.
+//
+// Horizon RunMap "03 / Arquitetura" (resident-qpacked-cache-v1) and "07 / De
+// volta à oficina": the complete compact source stays immutable in host RAM;
+// a missing expert is copied through pinned memory into a temporary GPU slot
+// while readers keep the previous generation; once the routed group's copies
+// complete, a new complete generation is published; a discarded copy is
+// dropped without write-back and its slot is reused only after its
+// consumers retire; capacity is fixed before requests and a profile with too
+// few spares is rejected; a failure before publication keeps the previous
+// generation.  Strata article ("Como 125 bilhões..."): eviction by an access
+// counter whose old hits decay.  Constants are a reading: decay
+// c <- c - (c >> shift) per routed event of the layer, +65536 per routed
+// expert, hits then misses touched in ascending id on a use clock, victim =
+// resident non-routed expert with lowest (counter, last use, id).
+//
+// The Backend provides: init(), slot_ptr(l, s), wait_retired(l),
+// copy(l, dst, src, n), upload_table(l, buf, entries) -> device table ptr,
+// publish(l, compute), retire(l, compute), sync(), destroy().
+#pragma once
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+int set_error(int code, const char *fmt, ...);
+
+template <class Backend>
+class SlotPool {
+  public:
+    moe_pool_config cfg{};
+    std::vector<const void *> src;   // [L*E] pinned host blobs
+    Backend be;
+
+    struct Layer {
+        std::vector<int64_t> cnt, last;  // per expert
+        std::vector<int> slot_of;        // expert -> slot or -1
+        std::vector<int> expert_in;      // slot -> expert or -1
+        int cur_buf = 0;
+        bool prepared = false;
+        const void *const *table = nullptr;
+    };
+    std::vector<Layer> layers;
+    int64_t clock = 0;
+    moe_pool_stats_t tot{};
+
+    int nslots() const { return cfg.capacity + cfg.spares; }
+
+    int create(const moe_pool_config &c, const void *const *pinned_src)
+    {
+        cfg = c;
+        if (c.layers <= 0 || c.experts <= 0 || c.topk <= 0 || c.expert_bytes <= 0 || !pinned_src)
+            return set_error(MOE_EINVAL, "moe_pool_create: bad configuration");
+        if (c.capacity < c.topk || c.capacity > c.experts || c.spares < c.topk)
+            return set_error(MOE_ECAPACITY,
+                             "moe_pool_create: profile rejected (C=%d, S=%d, k=%d, E=%d): need "
+                             "k <= C <= E and S >= k",
+                             c.capacity, c.spares, c.topk, c.experts);
+        if (c.expert_bytes % 256)
+            return set_error(MOE_EINVAL, "moe_pool_create: expert_bytes must be a multiple of 256");
+        src.assign(pinned_src, pinned_src + (size_t)c.layers * c.experts);
+        for (const void *p : src)
+            if (!p)
+                return set_error(MOE_EINVAL, "moe_pool_create: null source blob");
+        int rc = be.init(cfg);
+        if (rc)
+            return rc;
+        return place_initial();
+    }
+
+    int place_initial()
+    {
+        layers.assign(cfg.layers, Layer{});
+        clock = 0;
+        tot = moe_pool_stats_t{};
+        for (int l = 0; l < cfg.layers; ++l) {
+            Layer &L = layers[l];
+            L.cnt.assign(cfg.experts, 0);
+            L.last.assign(cfg.experts, 0);
+            L.slot_of.assign(cfg.experts, -1);
+            L.expert_in.assign(nslots(), -1);
+            for (int e = 0; e < cfg.capacity; ++e) {
+                L.slot_of[e] = e;
+                L.expert_in[e] = e;
+                L.last[e] = (int64_t)e - cfg.capacity;
+                int rc = be.copy(l, be.slot_ptr(l, e), src[(size_t)l * cfg.experts + e],
+                                 (size_t)cfg.expert_bytes);
+                if (rc)
+                    return rc;
+            }
+            std::vector<const void *> tab(cfg.experts, nullptr);
+            for (int e = 0; e < cfg.experts; ++e)
+                if (L.slot_of[e] >= 0)
+                    tab[e] = be.slot_ptr(l, L.slot_of[e]);
+            L.cur_buf = 0;
+            int rc = be.upload_table(l, 0, tab.data(), &L.table);
+            if (rc)
+                return rc;
+        }
+        return be.sync();
+    }
+
+    int prepare(int l, const int32_t *ids, int n, hipStream_t compute,
+                const void *const **table_out, moe_pool_stats_t *step)
+    {
+        if (l < 0 || l >= cfg.layers || n < 0 || (n > 0 && !ids) || !table_out)
+            return set_error(MOE_EINVAL, "moe_pool_prepare: bad arguments");
+        Layer &L0 = layers[l];
+        if (L0.prepared)
+            return set_error(MOE_ESTATE,
+                             "moe_pool_prepare: layer %d generation not retired", l);
+        const int E = cfg.experts;
+        std::vector<char> inR(E, 0);
+        int nR = 0;
+        for (int i = 0; i < n; ++i) {
+            if (ids[i] < 0 || ids[i] >= E)
+                return set_error(MOE_EINVAL, "moe_pool_prepare: expert id %d out of range",
+                                 ids[i]);
+            if (!inR[ids[i]]) {
+                inR[ids[i]] = 1;
+                ++nR;
+            }
+        }
+        if (nR > cfg.capacity)
+            return set_error(MOE_ECAPACITY,
+                             "moe_pool_prepare: %d distinct experts exceed capacity %d", nR,
+                             cfg.capacity);
+        // policy on a copy of the layer state
+        Layer L = L0;
+        int64_t clk = clock;
+        if (cfg.decay_shift >= 0)
+            for (int e = 0; e < E; ++e)
+                L.cnt[e] -= L.cnt[e] >> cfg.decay_shift;
+        for (int e = 0; e < E; ++e)
+            if (inR[e])
+                L.cnt[e] += 65536;
+        int hits = 0;
+        std::vector<int> misses, victims;
+        for (int e = 0; e < E; ++e)
+            if (inR[e] && L.slot_of[e] >= 0) {
+                L.last[e] = ++clk;
+                ++hits;
+            }
+        for (int e = 0; e < E; ++e)
+            if (inR[e] && L.slot_of[e] < 0)
+                misses.push_back(e);
+        std::vector<int> spares;
+        for (int s = 0; s < nslots(); ++s)
+            if (L.expert_in[s] < 0)
+                spares.push_back(s);
+        if ((int)misses.size() > (int)spares.size())
+            return set_error(MOE_ECAPACITY, "moe_pool_prepare: %d misses exceed %d spare slots",
+                             (int)misses.size(), (int)spares.size());
+        std::vector<int> fill_slot, victim_slot;
+        for (size_t i = 0; i < misses.size(); ++i) {
+            const int m = misses[i];
+            int v = -1;
+            for (int c = 0; c < E; ++c) {
+                if (L.slot_of[c] < 0 || inR[c])
+                    continue;
+                if (v < 0 || L.cnt[c] < L.cnt[v] || (L.cnt[c] == L.cnt[v] && L.last[c] < L.last[v]) ||
+                    (L.cnt[c] == L.cnt[v] && L.last[c] == L.last[v] && c < v))
+                    v = c;
+            }
+            const int sp = spares[i];
+            victims.push_back(v);
+            victim_slot.push_back(L.slot_of[v]);
+            fill_slot.push_back(sp);
+            // the victim leaves the table now; its slot stays occupied (not a
+            // spare) until this generation is published and retired
+            L.slot_of[v] = -1;
+            L.expert_in[sp] = m;
+            L.slot_of[m] = sp;
+            L.last[m] = ++clk;
+        }
+        // copies of the misses into spare slots (side stream, after earlier
+        // readers of those slots retired); table of the new generation
+        int rc = be.wait_retired(l);
+        if (rc)
+            return rc;
+        for (size_t i = 0; i < misses.size(); ++i) {
+            rc = be.copy(l, be.slot_ptr(l, fill_slot[i]), src[(size_t)l * E + misses[i]],
+                         (size_t)cfg.expert_bytes);
+            if (rc)
+                return rc;   // nothing published: previous generation and counters intact
+        }
+        std::vector<const void *> tab(E, nullptr);
+        for (int e = 0; e < E; ++e)
+            if (L.slot_of[e] >= 0)
+                tab[e] = be.slot_ptr(l, L.slot_of[e]);
+        const int nbuf = L.cur_buf ^ 1;
+        const void *const *dtab = nullptr;
+        rc = be.upload_table(l, nbuf, tab.data(), &dtab);
+        if (rc)
+            return rc;
+        rc = be.publish(l, compute);
+        if (rc)
+            return rc;
+        // commit: the victims' slots become spares (reusable after retirement)
+        for (int vs : victim_slot)
+            L.expert_in[vs] = -1;
+        L.cur_buf = nbuf;
+        L.table = dtab;
+        L.prepared = true;
+        L0 = std::move(L);
+        clock = clk;
+        moe_pool_stats_t st{};
+        st.hits = hits;
+        st.misses = (int64_t)misses.size();
+        st.evictions = (int64_t)victims.size();
+        st.h2d_bytes = st.misses * cfg.expert_bytes;
+        tot.hits += st.hits;
+        tot.misses += st.misses;
+        tot.evictions += st.evictions;
+        tot.h2d_bytes += st.h2d_bytes;
+        tot.generation += 1;
+        st.generation = tot.generation;
+        if (step)
+            *step = st;
+        *table_out = dtab;
+        return MOE_OK;
+    }
+
+    int retire(int l, hipStream_t compute)
+    {
+        if (l < 0 || l >= cfg.layers)
+            return set_error(MOE_EINVAL, "moe_pool_retire: bad layer %d", l);
+        if (!layers[l].prepared)
+            return set_error(MOE_ESTATE, "moe_pool_retire: layer %d has nothing to retire", l);
+        int rc = be.retire(l, compute);
+        if (rc)
+            return rc;
+        layers[l].prepared = false;
+        return MOE_OK;
+    }
+
+    int reset()
+    {
+        int rc = be.sync();
+        if (rc)
+            return rc;
+        return place_initial();
+    }
+};
+
+}  // namespace moe

@@ -1,0 +1,189 @@
+// pool_hip.cpp -- HIP backend of the expert slot pool and its C ABI.
+// Slots live in HBM; misses are hipMemcpyAsync H2D from the pinned source on
+// a side stream; the compute stream waits on an event recorded after the
+// copies and the table upload; a per-layer retirement event recorded on the
+// compute stream guards reuse of evicted slots and of the older table buffer.
+#include <hip/hip_runtime.h>
+
+#include "moe_common.h"
+#include "pool_core.h"
+
+namespace moe {
+
+struct HipPoolBackend {
+    moe_pool_config cfg{};
+    int nslots = 0;
+    uint8_t *slots = nullptr;            // [L][C+S][bytes]
+    const void **tables = nullptr;       // device [L][2][E]
+    const void **staging = nullptr;      // pinned host [L][2][E]
+    hipStream_t side = nullptr;
+    std::vector<hipEvent_t> retire_ev, copies_ev, upload_ev;
+    std::vector<char> retired, uploaded;
+
+    int init(const moe_pool_config &c)
+    {
+        cfg = c;
+        nslots = c.capacity + c.spares;
+        const size_t slot_bytes = (size_t)c.layers * nslots * (size_t)c.expert_bytes;
+        const size_t tab_bytes = (size_t)c.layers * 2 * c.experts * sizeof(void *);
+        size_t freeb = 0, totalb = 0;
+        MOE_HIP_TRY(hipMemGetInfo(&freeb, &totalb));
+        if (slot_bytes + tab_bytes + (64u << 20) > freeb)
+            return set_error(MOE_ECAPACITY,
+                             "moe_pool_create: %zu slot bytes do not fit in %zu free bytes",
+                             slot_bytes, freeb);
+        MOE_HIP_TRY(hipMalloc(&slots, slot_bytes));
+        MOE_HIP_TRY(hipMalloc(&tables, tab_bytes));
+        MOE_HIP_TRY(hipHostMalloc((void **)&staging, tab_bytes, hipHostMallocDefault));
+        MOE_HIP_TRY(hipStreamCreateWithFlags(&side, hipStreamNonBlocking));
+        retire_ev.assign(c.layers, nullptr);
+        copies_ev.assign(c.layers, nullptr);
+        upload_ev.assign((size_t)c.layers * 2, nullptr);
+        retired.assign(c.layers, 0);
+        uploaded.assign((size_t)c.layers * 2, 0);
+        for (auto *v : {&retire_ev, &copies_ev, &upload_ev})
+            for (auto &ev : *v)
+                MOE_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        return MOE_OK;
+    }
+    void *slot_ptr(int l, int s) { return slots + ((size_t)l * nslots + s) * cfg.expert_bytes; }
+    int wait_retired(int l)
+    {
+        if (retired[l])
+            MOE_HIP_TRY(hipStreamWaitEvent(side, retire_ev[l], 0));
+        return MOE_OK;
+    }
+    int copy(int, void *dst, const void *src, size_t n)
+    {
+        MOE_HIP_TRY(hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, side));
+        return MOE_OK;
+    }
+    int upload_table(int l, int buf, const void *const *entries, const void *const **dtab)
+    {
+        const size_t i = (size_t)l * 2 + buf;
+        const void **st = staging + i * cfg.experts;
+        if (uploaded[i])
+            MOE_HIP_TRY(hipEventSynchronize(upload_ev[i]));
+        for (int e = 0; e < cfg.experts; ++e)
+            st[e] = entries[e];
+        const void **dt = tables + i * cfg.experts;
+        MOE_HIP_TRY(hipMemcpyAsync((void *)dt, (const void *)st, cfg.experts * sizeof(void *),
+                                   hipMemcpyHostToDevice, side));
+        MOE_HIP_TRY(hipEventRecord(upload_ev[i], side));
+        uploaded[i] = 1;
+        *dtab = dt;
+        return MOE_OK;
+    }
+    int publish(int l, hipStream_t compute)
+    {
+        MOE_HIP_TRY(hipEventRecord(copies_ev[l], side));
+        MOE_HIP_TRY(hipStreamWaitEvent(compute, copies_ev[l], 0));
+        return MOE_OK;
+    }
+    int retire(int l, hipStream_t compute)
+    {
+        MOE_HIP_TRY(hipEventRecord(retire_ev[l], compute));
+        retired[l] = 1;
+        return MOE_OK;
+    }
+    int sync()
+    {
+        MOE_HIP_TRY(hipDeviceSynchronize());
+        std::fill(retired.begin(), retired.end(), 0);
+        return MOE_OK;
+    }
+    void destroy()
+    {
+        if (side)
+            (void)hipStreamSynchronize(side);
+        (void)hipDeviceSynchronize();
+        for (auto *v : {&retire_ev, &copies_ev, &upload_ev})
+            for (auto &ev : *v)
+                if (ev)
+                    (void)hipEventDestroy(ev);
+        if (side)
+            (void)hipStreamDestroy(side);
+        if (staging)
+            (void)hipHostFree(staging);
+        if (tables)
+            (void)hipFree(tables);
+        if (slots)
+            (void)hipFree(slots);
+        side = nullptr;
+        staging = nullptr;
+        tables = nullptr;
+        slots = nullptr;
+    }
+};
+
+}  // namespace moe
+
+struct moe_pool {
+    moe::SlotPool<moe::HipPoolBackend> p;
+};
+
+extern "C" {
+
+int moe_pool_create(const moe_pool_config *cfg, const void *const *pinned_src, moe_pool_t *out)
+{
+    moe::clear_error();
+    if (!cfg || !out)
+        return moe::set_error(MOE_EINVAL, "moe_pool_create: null argument");
+    moe_pool *pool = new (std::nothrow) moe_pool();
+    if (!pool)
+        return moe::set_error(MOE_ENOMEM, "moe_pool_create: out of host memory");
+    int rc = pool->p.create(*cfg, pinned_src);
+    if (rc) {
+        pool->p.be.destroy();
+        delete pool;
+        return rc;
+    }
+    *out = pool;
+    return MOE_OK;
+}
+
+int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
+                     hipStream_t compute, const void *const **d_table_out, moe_pool_stats_t *step)
+{
+    moe::clear_error();
+    if (!pool)
+        return moe::set_error(MOE_EINVAL, "moe_pool_prepare: null pool");
+    return pool->p.prepare(layer, host_ids, n, compute, d_table_out, step);
+}
+
+int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute)
+{
+    moe::clear_error();
+    if (!pool)
+        return moe::set_error(MOE_EINVAL, "moe_pool_retire: null pool");
+    return pool->p.retire(layer, compute);
+}
+
+int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out)
+{
+    moe::clear_error();
+    if (!pool || !out)
+        return moe::set_error(MOE_EINVAL, "moe_pool_stats: null argument");
+    *out = pool->p.tot;
+    return MOE_OK;
+}
+
+int moe_pool_reset(moe_pool_t pool)
+{
+    moe::clear_error();
+    if (!pool)
+        return moe::set_error(MOE_EINVAL, "moe_pool_reset: null pool");
+    return pool->p.reset();
+}
+
+int moe_pool_destroy(moe_pool_t pool)
+{
+    moe::clear_error();
+    if (!pool)
+        return MOE_OK;
+    pool->p.be.destroy();
+    delete pool;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+"""Plumbing around the C ABI: device buffers (torch) and the call sequence of
+one MoE layer -- route, permute, routed expert FFN, optional shared expert,
+combine.  No arithmetic happens here; every step is a libmoe_w4a16 call on
+the given stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi as A
+
+
+def load_experts(weights, H, I, group, device="cuda", stream=None):
+    """Quantise and prepack experts on the device.
+
+    weights: iterable of (wg [I,H], wu [I,H], wd [H,I]) float32 arrays
+    (numpy or torch).  Returns a uint8 device tensor [n, blob_bytes] in the
+    device layout.  Quantisation and prepacking run in the library's kernels.
+    """
+    weights = list(weights)
+    n = len(weights)
+    _, total = A.moe_blob_layout(H, I, group)
+    dev = torch.empty((n, total), dtype=torch.uint8, device=device)
+    canon = torch.empty((n, total), dtype=torch.uint8, device=device)
+    wg = torch.empty((n, I, H), dtype=torch.float32, device=device)
+    wu = torch.empty((n, I, H), dtype=torch.float32, device=device)
+    wd = torch.empty((n, H, I), dtype=torch.float32, device=device)
+    for e, (g_, u_, d_) in enumerate(weights):
+        wg[e].copy_(torch.as_tensor(g_))
+        wu[e].copy_(torch.as_tensor(u_))
+        wd[e].copy_(torch.as_tensor(d_))
+    A.moe_quantize_experts(wg, wu, wd, n, H, I, group, canon, stream)
+    A.moe_prepack_experts(canon, n, H, I, group, dev, stream)
+    return dev, canon
+
+
+def blob_table(blobs: torch.Tensor) -> torch.Tensor:
+    """Device array of per-expert blob addresses for a [E, bytes] tensor."""
+    E, nbytes = blobs.shape
+    base = blobs.data_ptr()
+    return torch.tensor([base + e * nbytes for e in range(E)], dtype=torch.int64,
+                        device=blobs.device)
+
+
+@dataclass
+class LayerBuffers:
+    T: int
+    regime: int
+    y_dtype: int
+    y_slices: int
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    inv_perm: torch.Tensor
+    perm_ws: torch.Tensor | None
+    y: torch.Tensor
+    ffn_ws: torch.Tensor | None
+    shared_out: torch.Tensor | None
+    shared_ws: torch.Tensor | None
+    out: torch.Tensor
+
+
+class MoELayer:
+    """One W4A16 MoE layer resident on the device."""
+
+    def __init__(self, H, I, E, k, group, router, table, bias=None, shared=None,
+                 renorm=False, device="cuda"):
+        self.H, self.I, self.E, self.k, self.g = H, I, E, k, group
+        self.router = router            # fp16 [E, H] device
+        self.table = table              # int64 [E] device (blob addresses)
+        self.bias = bias                # fp32 [E] device or None
+        self.shared = shared            # (wg, wu, wd) fp16 device or None
+        self.flags = A.MOE_RENORM if renorm else 0
+        self.device = device
+
+    def buffers(self, T, regime=A.MOE_REGIME_AUTO) -> LayerBuffers:
+        d = self.device
+        r, ydt, ysl, ffn_ws = A.moe_expert_ffn_plan(T, self.H, self.I, self.E, self.k, self.g,
+                                                    regime)
+        pws = A.moe_permute_workspace_bytes(T, self.k, self.E)
+        n = T * self.k
+        ytype = torch.float32 if ydt == A.MOE_DTYPE_F32 else torch.float16
+        sh_out = sh_ws = None
+        if self.shared is not None:
+            Is = self.shared[0].shape[0]
+            sh_out = torch.empty((T, self.H), dtype=torch.float32, device=d)
+            sh_ws = torch.empty(max(1, A.moe_shared_ffn_workspace_bytes(T, self.H, Is)),
+                                dtype=torch.uint8, device=d)
+        return LayerBuffers(
+            T=T, regime=r, y_dtype=ydt, y_slices=ysl,
+            topk_idx=torch.empty((T, self.k), dtype=torch.int32, device=d),
+            topk_w=torch.empty((T, self.k), dtype=torch.float32, device=d),
+            counts=torch.empty(self.E, dtype=torch.int32, device=d),
+            offsets=torch.empty(self.E + 1, dtype=torch.int32, device=d),
+            perm=torch.empty(max(n, 1), dtype=torch.int32, device=d),
+            inv_perm=torch.empty(max(n, 1), dtype=torch.int32, device=d),
+            perm_ws=torch.empty(pws, dtype=torch.uint8, device=d) if pws else None,
+            y=torch.empty((ysl, max(n, 1), self.H), dtype=ytype, device=d),
+            ffn_ws=torch.empty(ffn_ws, dtype=torch.uint8, device=d) if ffn_ws else None,
+            shared_out=sh_out, shared_ws=sh_ws,
+            out=torch.empty((T, self.H), dtype=torch.float16, device=d),
+        )
+
+    def route_permute(self, x, b: LayerBuffers, stream=None):
+        T = b.T
+        A.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.flags,
+                    b.topk_idx, b.topk_w, stream)
+        A.moe_permute(b.topk_idx, T, self.k, self.E, b.counts, b.offsets, b.perm, b.inv_perm,
+                      b.perm_ws, 0 if b.perm_ws is None else b.perm_ws.numel(), stream)
+
+    def experts(self, x, b: LayerBuffers, table=None, stream=None):
+        A.moe_expert_ffn_w4a16(x, b.perm, b.offsets, self.table if table is None else table,
+                               b.T, self.H, self.I, self.E, self.k, self.g, b.regime, b.y,
+                               b.y_dtype, b.y_slices, b.ffn_ws,
+                               0 if b.ffn_ws is None else b.ffn_ws.numel(), stream)
+        if self.shared is not None:
+            wg, wu, wd = self.shared
+            A.moe_shared_ffn_f16(x, wg, wu, wd, b.T, self.H, wg.shape[0], b.shared_out,
+                                 b.shared_ws, b.shared_ws.numel(), stream)
+
+    def combine(self, b: LayerBuffers, residual=None, out=None, stream=None):
+        out = b.out if out is None else out
+        A.moe_combine(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, b.shared_out, residual,
+                      b.T, self.H, self.k, out, stream)
+        return out
+
+    def forward(self, x, b: LayerBuffers, residual=None, out=None, stream=None):
+        self.route_permute(x, b, stream)
+        self.experts(x, b, stream=stream)
+        return self.combine(b, residual, out, stream)

@@ -61,6 +61,21 @@ double oracle_f16_to_f64(uint16_t h)
     return sign ? -v : v;
 }
 
+/* Decode table of all 65536 fp16 values (filled once from the function
+ * above; lookups return exactly the same doubles). */
+static double f16tab[65536];
+static int f16tab_ready = 0;
+
+static double H2D(uint16_t h)
+{
+    if (!f16tab_ready) {
+        for (int i = 0; i < 65536; i++)
+            f16tab[i] = oracle_f16_to_f64((uint16_t)i);
+        f16tab_ready = 1;
+    }
+    return f16tab[h];
+}
+
 /* double -> IEEE binary16, round to nearest, ties to even. */
 uint16_t oracle_f64_to_f16(double v)
 {
@@ -198,7 +213,7 @@ static double deq(const uint8_t *qs, const uint16_t *ss, int K, int g, int r, in
 {
     uint8_t b = qs[(int64_t)r * (K / 2) + c / 2];
     int u = (c & 1) ? (b >> 4) : (b & 15);
-    return (double)(u - 8) * oracle_f16_to_f64(ss[(int64_t)r * (K / g) + c / g]);
+    return (double)(u - 8) * H2D(ss[(int64_t)r * (K / g) + c / g]);
 }
 
 /* Dequantise a whole [rows][K] section to fp64 (tests use it as a pin). */
@@ -224,7 +239,7 @@ int oracle_dequant_rows(const uint8_t *q, const uint16_t *s, int rows, int K, in
  * strides 32, 16, 8, 4, 2, 1 (a_j <- a_j + a_{j xor s}).  fp16 x fp16
  * products are exact in fp32, so this order fixes every rounding.
  */
-static float logit_pinned(const uint16_t *x, const uint16_t *w, int H)
+static float logit_pinned(const float *x, const float *w, int H)
 {
     float part[64], nxt[64];
     for (int j = 0; j < 64; j++)
@@ -233,7 +248,7 @@ static float logit_pinned(const uint16_t *x, const uint16_t *w, int H)
         int lane = c % 64;
         for (int i = 0; i < 8; i++) {
             int h = c * 8 + i;
-            float prod = (float)oracle_f16_to_f64(x[h]) * (float)oracle_f16_to_f64(w[h]);
+            float prod = x[h] * w[h];
             part[lane] = part[lane] + prod;
         }
     }
@@ -263,13 +278,19 @@ int oracle_route(const uint16_t *x, const uint16_t *wr, const float *bias,
     float *l = malloc(sizeof(float) * (size_t)E);
     double *p = malloc(sizeof(double) * (size_t)E);
     char *taken = malloc((size_t)E);
-    if (!l || !p || !taken) {
-        free(l); free(p); free(taken);
+    float *wf = malloc(sizeof(float) * (size_t)E * H);   /* fp16 values, exact in fp32 */
+    float *xf = malloc(sizeof(float) * (size_t)H);
+    if (!l || !p || !taken || !wf || !xf) {
+        free(l); free(p); free(taken); free(wf); free(xf);
         return OR_ENOMEM;
     }
+    for (int64_t i = 0; i < (int64_t)E * H; i++)
+        wf[i] = (float)H2D(wr[i]);
     for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++)
+            xf[h] = (float)H2D(x[(int64_t)t * H + h]);
         for (int e = 0; e < E; e++) {
-            float v = logit_pinned(x + (int64_t)t * H, wr + (int64_t)e * H, H);
+            float v = logit_pinned(xf, wf + (int64_t)e * H, H);
             if (bias)
                 v = v + bias[e];
             l[e] = v;
@@ -308,7 +329,7 @@ int oracle_route(const uint16_t *x, const uint16_t *wr, const float *bias,
             w[(int64_t)t * k + j] = (float)pj;
         }
     }
-    free(l); free(p); free(taken);
+    free(l); free(p); free(taken); free(wf); free(xf);
     return OR_OK;
 }
 
@@ -379,48 +400,67 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *off
         nrows = n;
     double *xv = malloc(sizeof(double) * (size_t)H);
     double *hv = malloc(sizeof(double) * (size_t)I);
-    if (!xv || !hv) {
-        free(xv); free(hv);
-        return OR_ENOMEM;
+    /* dequantised matrices of the expert in use (decoded once per expert) */
+    double *Wg = malloc(sizeof(double) * (size_t)I * H);
+    double *Wu = malloc(sizeof(double) * (size_t)I * H);
+    double *Wd = malloc(sizeof(double) * (size_t)H * I);
+    int rc = OR_OK, cur = -1;
+    if (!xv || !hv || !Wg || !Wu || !Wd) {
+        rc = OR_ENOMEM;
+        goto done;
     }
     for (int r = 0; r < nrows; r++) {
         int p = rows ? rows[r] : r;
         if (p < 0 || p >= n) {
-            free(xv); free(hv);
-            return OR_EINVAL;
+            rc = OR_EINVAL;
+            goto done;
         }
         int e = 0;
         while (e < E && !(offsets[e] <= p && p < offsets[e + 1]))
             e++;
         if (e == E || !blobs[e]) {
-            free(xv); free(hv);
-            return OR_EINVAL;
+            rc = OR_EINVAL;
+            goto done;
         }
-        const uint8_t *b = blobs[e];
-        const uint8_t *gq = b + off[0], *uq = b + off[1], *dq = b + off[2];
-        const uint16_t *gs = (const uint16_t *)(b + off[3]);
-        const uint16_t *us = (const uint16_t *)(b + off[4]);
-        const uint16_t *ds = (const uint16_t *)(b + off[5]);
+        if (e != cur) {
+            const uint8_t *b = blobs[e];
+            const uint8_t *gq = b + off[0], *uq = b + off[1], *dq = b + off[2];
+            const uint16_t *gs = (const uint16_t *)(b + off[3]);
+            const uint16_t *us = (const uint16_t *)(b + off[4]);
+            const uint16_t *ds = (const uint16_t *)(b + off[5]);
+            for (int i = 0; i < I; i++)
+                for (int c = 0; c < H; c++) {
+                    Wg[(int64_t)i * H + c] = deq(gq, gs, H, g, i, c);
+                    Wu[(int64_t)i * H + c] = deq(uq, us, H, g, i, c);
+                }
+            for (int o = 0; o < H; o++)
+                for (int i = 0; i < I; i++)
+                    Wd[(int64_t)o * I + i] = deq(dq, ds, I, g, o, i);
+            cur = e;
+        }
         int t = perm[p] / k;
         for (int c = 0; c < H; c++)
-            xv[c] = oracle_f16_to_f64(x[(int64_t)t * H + c]);
+            xv[c] = H2D(x[(int64_t)t * H + c]);
         for (int i = 0; i < I; i++) {
             double a = 0.0, u = 0.0;
+            const double *wg = Wg + (int64_t)i * H, *wu = Wu + (int64_t)i * H;
             for (int c = 0; c < H; c++) {
-                a += deq(gq, gs, H, g, i, c) * xv[c];
-                u += deq(uq, us, H, g, i, c) * xv[c];
+                a += wg[c] * xv[c];
+                u += wu[c] * xv[c];
             }
             hv[i] = silu(a) * u;
         }
         for (int o = 0; o < H; o++) {
             double acc = 0.0;
+            const double *wd = Wd + (int64_t)o * I;
             for (int i = 0; i < I; i++)
-                acc += deq(dq, ds, I, g, o, i) * hv[i];
+                acc += wd[i] * hv[i];
             y[(int64_t)r * H + o] = acc;
         }
     }
-    free(xv); free(hv);
-    return OR_OK;
+done:
+    free(xv); free(hv); free(Wg); free(Wu); free(Wd);
+    return rc;
 }
 
 /*
@@ -446,19 +486,19 @@ int oracle_shared_ffn(const uint16_t *x, const uint16_t *wg, const uint16_t *wu,
     for (int r = 0; r < ntoks; r++) {
         int t = toks ? toks[r] : r;
         for (int c = 0; c < H; c++)
-            xv[c] = oracle_f16_to_f64(x[(int64_t)t * H + c]);
+            xv[c] = H2D(x[(int64_t)t * H + c]);
         for (int i = 0; i < Is; i++) {
             double a = 0.0, u = 0.0;
             for (int c = 0; c < H; c++) {
-                a += oracle_f16_to_f64(wg[(int64_t)i * H + c]) * xv[c];
-                u += oracle_f16_to_f64(wu[(int64_t)i * H + c]) * xv[c];
+                a += H2D(wg[(int64_t)i * H + c]) * xv[c];
+                u += H2D(wu[(int64_t)i * H + c]) * xv[c];
             }
             hv[i] = silu(a) * u;
         }
         for (int o = 0; o < H; o++) {
             double acc = 0.0;
             for (int i = 0; i < Is; i++)
-                acc += oracle_f16_to_f64(wd[(int64_t)o * Is + i]) * hv[i];
+                acc += H2D(wd[(int64_t)o * Is + i]) * hv[i];
             s[(int64_t)r * H + o] = acc;
         }
     }
@@ -484,7 +524,7 @@ int oracle_combine(const double *y, const int32_t *inv_perm, const float *w,
         return OR_EINVAL;
     for (int t = 0; t < T; t++) {
         for (int o = 0; o < H; o++) {
-            double acc = residual ? oracle_f16_to_f64(residual[(int64_t)t * H + o]) : 0.0;
+            double acc = residual ? H2D(residual[(int64_t)t * H + o]) : 0.0;
             for (int j = 0; j < k; j++) {
                 int p = inv_perm[(int64_t)t * k + j];
                 acc += (double)w[(int64_t)t * k + j] * y[(int64_t)p * H + o];

@@ -1,0 +1,127 @@
+"""Helpers of the GPU tests: device layers built from the seeded inputs
+(quantised and prepacked by the library's own kernels), oracle blobs built
+from the same draws by the oracle's own quantiser, tolerance checks, and a
+progress line on the real stderr before each GPU step."""
+import sys
+
+import numpy as np
+import torch
+
+import int4_weight_only_router_amd as M
+from int4_weight_only_router_amd.layer import MoELayer, blob_table
+import moe_inputs as MI
+import oracle as O
+
+DEV = "cuda:0"
+ATOL = 2e-2      # max |delta| on outputs
+RTOL_L2 = 1e-2   # relative L2 on outputs
+WTOL = 1e-5      # routing weights
+
+
+def say(msg):
+    sys.__stderr__.write("[gpu] %s\n" % msg)
+    sys.__stderr__.flush()
+
+
+def f16(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def device_experts(cfg, layer, experts=None, batch=32):
+    """Prepacked device blobs [E, bytes] of a layer; canonical blobs too."""
+    experts = list(range(cfg.E)) if experts is None else list(experts)
+    _, total = M.moe_blob_layout(cfg.H, cfg.I, cfg.g)
+    dev = torch.empty((cfg.E, total), dtype=torch.uint8, device=DEV)
+    canon = torch.empty((cfg.E, total), dtype=torch.uint8, device=DEV)
+    for b0 in range(0, len(experts), batch):
+        ids = experts[b0:b0 + batch]
+        n = len(ids)
+        wg = torch.empty((n, cfg.I, cfg.H), dtype=torch.float32, device=DEV)
+        wu = torch.empty((n, cfg.I, cfg.H), dtype=torch.float32, device=DEV)
+        wd = torch.empty((n, cfg.H, cfg.I), dtype=torch.float32, device=DEV)
+        for i, (e, (g_, u_, d_)) in enumerate(MI.gen_experts(cfg, layer, ids)):
+            wg[i].copy_(torch.from_numpy(g_))
+            wu[i].copy_(torch.from_numpy(u_))
+            wd[i].copy_(torch.from_numpy(d_))
+        cb = torch.empty((n, total), dtype=torch.uint8, device=DEV)
+        db = torch.empty((n, total), dtype=torch.uint8, device=DEV)
+        M.moe_quantize_experts(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, cb)
+        M.moe_prepack_experts(cb, n, cfg.H, cfg.I, cfg.g, db)
+        idx = torch.tensor(ids, device=DEV)
+        dev[idx] = db
+        canon[idx] = cb
+        del wg, wu, wd
+    torch.cuda.synchronize()
+    return dev, canon
+
+
+class OracleBlobs:
+    """Lazily packed oracle blobs of one layer (same draws, oracle quantiser)."""
+
+    def __init__(self, cfg, layer):
+        self.cfg, self.layer, self.cache = cfg, layer, {}
+
+    def get(self, experts):
+        c = self.cfg
+        need = [e for e in sorted(set(int(e) for e in experts)) if e not in self.cache]
+        for e, w in MI.gen_experts(c, self.layer, need):
+            self.cache[e] = O.pack_expert(*w, c.g)
+        return [self.cache.get(e) for e in range(c.E)]
+
+
+_EXPERT_CACHE = {}
+
+
+def cached_experts(cfg, layer):
+    key = (cfg.cid, cfg.H, cfg.E, cfg.I, cfg.g, layer)
+    if key not in _EXPERT_CACHE:
+        if len(_EXPERT_CACHE) >= 3:
+            _EXPERT_CACHE.pop(next(iter(_EXPERT_CACHE)))
+        say("build experts cfg=%s layer=%d" % (cfg.name, layer))
+        _EXPERT_CACHE[key] = device_experts(cfg, layer)[0]
+    return _EXPERT_CACHE[key]
+
+
+def make_layer(cfg, layer=0, shared=True):
+    dev = cached_experts(cfg, layer)
+    router = f16(MI.gen_router(cfg, layer))
+    b = MI.zipf_bias(cfg, layer)
+    bias = None if b is None else torch.from_numpy(b).to(DEV)
+    sh = None
+    if shared and cfg.Is:
+        sh = tuple(f16(w) for w in MI.gen_shared(cfg))
+    lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, router, blob_table(dev), bias, sh,
+                   device=DEV)
+    lay._blobs = dev            # keep the storage alive
+    return lay
+
+
+def check_close(got, ref, what, atol=ATOL, rtol_l2=RTOL_L2):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    d = np.abs(got - ref)
+    mx = float(d.max()) if d.size else 0.0
+    l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert mx <= atol and l2 <= rtol_l2, "%s: max|d|=%.3g (<= %g), relL2=%.3g (<= %g)" % (
+        what, mx, atol, l2, rtol_l2)
+    return mx, l2
+
+
+def sample_rows(offsets, n_per_expert=2, max_rows=64, seed=0):
+    """Sorted rows to check: first and last row of each non-empty expert bucket
+    (tile edges), plus seeded random rows, capped."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    E = len(offsets) - 1
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            rows.add(a)
+            rows.add(b - 1)
+            for r in rng.integers(a, b, n_per_expert):
+                rows.add(int(r))
+    rows = sorted(rows)
+    if len(rows) > max_rows:
+        rows = sorted(rng.choice(rows, max_rows, replace=False).tolist())
+    return np.array(rows, np.int32)

@@ -1,0 +1,401 @@
+"""GPU parity: every entry point of libmoe_w4a16 against the CPU oracle on
+the same seeded inputs.  Integer results (quantised codes, routing indices,
+counts, offsets, permutations) must match bit for bit; floating results
+within max|d| <= 2e-2 and relative L2 <= 1e-2 (routing weights within 1e-5).
+At full sizes the oracle checks sampled rows/tokens, always including the
+first and last row of every expert bucket (tile edges)."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_router_amd as M
+from int4_weight_only_router_amd.layer import MoELayer, blob_table
+import moe_inputs as MI
+import oracle as O
+from tests.gpu_util import (DEV, WTOL, OracleBlobs, check_close, device_experts, f16,
+                            make_layer, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ------------------------------------------------------------- quantiser
+
+@pytest.mark.parametrize("cfg", [MI.TINY, MI.OLMOE_DECODE, MI.E512], ids=lambda c: c.name)
+def test_quantize_bit_exact(cfg):
+    say("quantize %s" % cfg.name)
+    _, canon = device_experts(cfg, 0, experts=[0, 1, cfg.E - 1])
+    ob = OracleBlobs(cfg, 0).get([0, 1, cfg.E - 1])
+    for e in (0, 1, cfg.E - 1):
+        assert np.array_equal(_np(canon[e]), ob[e]), "expert %d blob differs" % e
+
+
+def _numpy_prepack(canon, H, I, g):
+    """Independent rendering of the documented device layout (format only)."""
+    gq, uq, dq, gs, us, ds = O.blob_sections(canon, H, I, g)
+    out = np.zeros_like(canon)
+
+    def relayout(chunk):   # 16 canonical bytes -> 16 device bytes
+        w = chunk.view(np.uint32)
+        o = np.zeros(4, np.uint32)
+        for i in range(4):
+            o |= ((w >> (8 * i)) & 0xF) << (4 * i)
+            o |= ((w >> (8 * i + 4)) & 0xF) << (16 + 4 * i)
+        return o.view(np.uint8)
+
+    o = 0
+    for b in range(I // 32):
+        for c in range(H // 32):
+            for r in range(64):
+                src = (gq if r < 32 else uq)[32 * b + (r & 31), 16 * c:16 * c + 16]
+                out[o:o + 16] = relayout(src)
+                o += 16
+    o = -(-o // 256) * 256
+    for b in range(H // 64):
+        for c in range(I // 32):
+            for r in range(64):
+                out[o:o + 16] = relayout(dq[64 * b + r, 16 * c:16 * c + 16])
+                o += 16
+    o = -(-o // 256) * 256
+    v = out[o:].view(np.uint16)
+    j = 0
+    for b in range(I // 32):
+        for G in range(H // g):
+            for r in range(64):
+                v[j] = (gs if r < 32 else us)[32 * b + (r & 31), G]
+                j += 1
+    o2 = -(-(o + 2 * j) // 256) * 256
+    v = out[o2:].view(np.uint16)
+    j = 0
+    for b in range(H // 64):
+        for G in range(I // g):
+            for r in range(64):
+                v[j] = ds[64 * b + r, G]
+                j += 1
+    return out
+
+
+def test_prepack_layout_and_round_trip():
+    cfg = MI.TINY
+    say("prepack round trip")
+    dev, canon = device_experts(cfg, 0, experts=[0, 3])
+    for e in (0, 3):
+        ref = _numpy_prepack(_np(canon[e]), cfg.H, cfg.I, cfg.g)
+        assert np.array_equal(_np(dev[e]), ref)
+    back = torch.empty_like(dev)
+    M.moe_unpack_experts(dev, cfg.E, cfg.H, cfg.I, cfg.g, back)
+    torch.cuda.synchronize()
+    for e in (0, 3):
+        assert np.array_equal(_np(back[e]), _np(canon[e]))
+
+
+# ---------------------------------------------------------------- router
+
+def _route_gpu(x, wr, bias, T, H, E, k, flags=0):
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    M.moe_route(x, wr, bias, T, H, E, k, flags, idx, w)
+    torch.cuda.synchronize()
+    return _np(idx), _np(w)
+
+
+@pytest.mark.parametrize("cfg,T,renorm", [
+    (MI.TINY, 16, False), (MI.TINY, 16, True), (MI.OLMOE_DECODE, 1, False),
+    (MI.OLMOE_DECODE, 64, False), (MI.OLMOE_DECODE, 512, False),
+    (MI.OLMOE_DECODE, 4096, False), (MI.E512, 1, False), (MI.E512, 256, False),
+    (MI.E512, 4096, False), (MI.OLMOE_DECODE, 67, False)],
+    ids=lambda v: getattr(v, "name", str(v)))
+def test_route_bit_exact(cfg, T, renorm):
+    say("route %s T=%d renorm=%d" % (cfg.name, T, renorm))
+    x = MI.gen_x(cfg, T)
+    wr = MI.gen_router(cfg)
+    b = MI.zipf_bias(cfg)
+    idx, w = _route_gpu(f16(x), f16(wr), None if b is None else torch.from_numpy(b).to(DEV),
+                        T, cfg.H, cfg.E, cfg.k, M.MOE_RENORM if renorm else 0)
+    toks = np.arange(T) if T <= 512 else np.random.default_rng(T).choice(T, 256, replace=False)
+    oi, ow, _ = O.route(x[toks], wr, b, cfg.k, renorm)
+    assert np.array_equal(idx[toks], oi)
+    assert np.max(np.abs(w[toks] - ow)) <= WTOL
+
+
+def test_route_ties_go_to_lower_index():
+    cfg = MI.OLMOE_DECODE
+    say("route ties")
+    T = 8
+    x = MI.gen_x(cfg, T)
+    x[0] = 0.0                                  # all logits equal -> experts 0..k-1
+    wr = MI.gen_router(cfg)
+    wr[40] = wr[3]                              # duplicated rows -> exact ties
+    wr[17] = wr[3]
+    wr[63] = wr[9]
+    idx, w = _route_gpu(f16(x), f16(wr), None, T, cfg.H, cfg.E, cfg.k)
+    oi, ow, _ = O.route(x, wr, None, cfg.k)
+    assert np.array_equal(idx, oi)
+    assert np.array_equal(idx[0], np.arange(cfg.k))
+    assert np.max(np.abs(w - ow)) <= WTOL
+
+
+# ----------------------------------------------------------- permutation
+
+def _permute_gpu(idx_np, E):
+    T, k = idx_np.shape
+    n = T * k
+    idx = torch.from_numpy(idx_np).to(DEV)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((max(n, 1),), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((max(n, 1),), -7, dtype=torch.int32, device=DEV)
+    wsb = M.moe_permute_workspace_bytes(T, k, E)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    M.moe_permute(idx, T, k, E, counts, offsets, perm, inv, ws, wsb)
+    torch.cuda.synchronize()
+    return _np(counts), _np(offsets), _np(perm)[:n], _np(inv)[:n]
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(1, 8, 64, 0), (16, 2, 8, 0), (64, 8, 64, 0),
+                                        (512, 8, 64, 0), (513, 8, 64, 0), (4096, 8, 64, 0),
+                                        (4096, 10, 512, 1.1), (300, 16, 1024, 1.0),
+                                        (1, 1, 1, 0), (0, 8, 64, 0)])
+def test_permute_bit_exact(T, k, E, skew):
+    say("permute T=%d k=%d E=%d" % (T, k, E))
+    rng = np.random.default_rng(T * 7 + E)
+    p = None
+    if skew:
+        p = np.arange(1, E + 1, dtype=np.float64) ** -skew
+        p /= p.sum()
+    idx = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(T)],
+                   dtype=np.int32).reshape(T, k)
+    got = _permute_gpu(idx, E)
+    ref = O.permute(idx, E)
+    for a, b_, name in zip(got, ref, ("counts", "offsets", "perm", "inv_perm")):
+        assert np.array_equal(a, b_), name
+
+
+def test_permute_hot_expert():
+    """Every token routes to expert 5 (one bucket with T rows)."""
+    say("permute hot expert")
+    T, k, E = 4096, 8, 64
+    rng = np.random.default_rng(1)
+    idx = np.stack([np.concatenate([[5], rng.choice(np.delete(np.arange(E), 5), k - 1,
+                                                    replace=False)]) for _ in range(T)])
+    idx = idx.astype(np.int32)
+    got = _permute_gpu(idx, E)
+    ref = O.permute(idx, E)
+    for a, b_ in zip(got, ref):
+        assert np.array_equal(a, b_)
+
+
+# ------------------------------------------------------------ expert FFN
+
+def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
+    lay = make_layer(cfg, layer, shared=False)
+    x = MI.gen_x(cfg, T)
+    b = lay.buffers(T, regime)
+    say("ffn %s T=%d regime=%d" % (cfg.name, T, b.regime))
+    xd = f16(x)
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    torch.cuda.synchronize()
+    bias = MI.zipf_bias(cfg, layer)
+    oi, ow, _ = O.route(x, MI.gen_router(cfg, layer), bias, cfg.k)
+    assert np.array_equal(_np(b.topk_idx), oi)
+    counts, offsets, perm, inv = O.permute(oi, cfg.E)
+    assert np.array_equal(_np(b.offsets), offsets) and np.array_equal(_np(b.perm), perm[:T * cfg.k])
+    rows = sample_rows(offsets, max_rows=max_rows) if T * cfg.k > max_rows else \
+        np.arange(T * cfg.k, dtype=np.int32)
+    used = np.unique(oi)
+    blobs = OracleBlobs(cfg, layer).get(used)
+    y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
+    y = _np(b.y).astype(np.float64)
+    y_rows = y.sum(axis=0)[rows] if b.y_dtype == M.MOE_DTYPE_F32 else y[0][rows]
+    return check_close(y_rows, y_ref, "y %s T=%d" % (cfg.name, T))
+
+
+@pytest.mark.parametrize("cfg,T,regime", [
+    (MI.TINY, 16, M.MOE_REGIME_DECODE), (MI.TINY, 16, M.MOE_REGIME_BATCHED),
+    (MI.TINY, 1, M.MOE_REGIME_AUTO), (MI.TINY, 300, M.MOE_REGIME_BATCHED),
+    (MI.OLMOE_DECODE, 1, M.MOE_REGIME_AUTO), (MI.OLMOE_DECODE, 3, M.MOE_REGIME_AUTO),
+    (MI.OLMOE_DECODE, 64, M.MOE_REGIME_BATCHED), (MI.OLMOE_DECODE, 512, M.MOE_REGIME_BATCHED),
+    (MI.OLMOE_DECODE, 4096, M.MOE_REGIME_BATCHED), (MI.E512, 1, M.MOE_REGIME_AUTO),
+    (MI.E512, 256, M.MOE_REGIME_BATCHED), (MI.E512, 4096, M.MOE_REGIME_BATCHED)],
+    ids=lambda v: getattr(v, "name", str(v)))
+def test_expert_ffn(cfg, T, regime):
+    _ffn_case(cfg, T, regime)
+
+
+# -------------------------------------------------------- shared expert
+
+@pytest.mark.parametrize("T", [1, 3, 256, 4096])
+def test_shared_ffn(T):
+    cfg = MI.E512
+    say("shared T=%d" % T)
+    wg, wu, wd = MI.gen_shared(cfg)
+    x = MI.gen_x(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)
+    wsb = M.moe_shared_ffn_workspace_bytes(T, cfg.H, cfg.Is)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    M.moe_shared_ffn_f16(f16(x), f16(wg), f16(wu), f16(wd), T, cfg.H, cfg.Is, out, ws, wsb)
+    torch.cuda.synchronize()
+    toks = np.arange(T) if T <= 16 else np.sort(
+        np.random.default_rng(T).choice(T, 24, replace=False))
+    ref = O.shared_ffn(x, wg, wu, wd, toks=toks)
+    check_close(_np(out)[toks], ref, "shared T=%d" % T)
+
+
+# --------------------------------------------------------------- combine
+
+def _assert_combine_close(got, ref16, ref64, absum, nterms):
+    """The GPU sums n terms in fp32, the oracle in fp64: they differ by at most
+    the recursive-summation bound gamma_n * sum|terms| (Higham), and each is
+    then rounded once to fp16, adding at most one fp16 ulp between them."""
+    u = 2.0 ** -24
+    bound = nterms * u / (1 - nterms * u) * absum
+    ulp = np.spacing(np.abs(ref16)).astype(np.float64)
+    err = np.abs(got - ref16.astype(np.float64))
+    r = err / (ulp + bound)
+    i = np.unravel_index(np.argmax(r), r.shape)
+    assert r[i] <= 1.0, "worst at %s: got %r ref16 %r ref64 %r (ulp %g, bound %g)" % (
+        i, got[i], float(ref16[i]), ref64[i], ulp[i], bound[i])
+
+
+@pytest.mark.parametrize("S,dt,shared,res", [(32, M.MOE_DTYPE_F32, False, True),
+                                             (16, M.MOE_DTYPE_F32, True, False),
+                                             (1, M.MOE_DTYPE_F16, True, True),
+                                             (1, M.MOE_DTYPE_F32, False, False)])
+def test_combine(S, dt, shared, res):
+    say("combine S=%d dt=%d" % (S, dt))
+    rng = np.random.default_rng(S + dt)
+    T, k, H = 37, 8, 512
+    ys = (rng.standard_normal((S, T * k, H)) * (0.05 if S > 1 else 0.3)).astype(
+        np.float32 if dt == M.MOE_DTYPE_F32 else np.float16)
+    inv = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32) if shared else None
+    r = rng.standard_normal((T, H)).astype(np.float16) if res else None
+    out = torch.empty((T, H), dtype=torch.float16, device=DEV)
+    M.moe_combine(torch.from_numpy(ys).to(DEV), dt, S, torch.from_numpy(inv).to(DEV),
+                  torch.from_numpy(w).to(DEV), None if sh is None else torch.from_numpy(sh).to(DEV),
+                  None if r is None else f16(r), T, H, k, out)
+    torch.cuda.synchronize()
+    yo = ys.astype(np.float64).sum(axis=0)
+    ref, ref64 = O.combine(yo, inv, w, None if sh is None else sh.astype(np.float64), r)
+    got = _np(out).astype(np.float64)
+    yabs = np.abs(ys.astype(np.float64)).sum(axis=0)
+    absum = sum(w[:, j:j + 1].astype(np.float64) * yabs[inv[np.arange(T) * k + j]]
+                for j in range(k))
+    if sh is not None:
+        absum = absum + np.abs(sh)
+    if r is not None:
+        absum = absum + np.abs(r.astype(np.float64))
+    _assert_combine_close(got, ref, ref64, absum, S * k + 2)
+
+
+def test_combine_in_place_residual():
+    say("combine in place")
+    rng = np.random.default_rng(3)
+    T, k, H = 5, 2, 256
+    ys = rng.standard_normal((1, T * k, H)).astype(np.float16)
+    inv = np.arange(T * k, dtype=np.int32)
+    w = np.full((T, k), 0.5, np.float32)
+    r = rng.standard_normal((T, H)).astype(np.float16)
+    buf = f16(r)
+    M.moe_combine(torch.from_numpy(ys).to(DEV), M.MOE_DTYPE_F16, 1,
+                  torch.from_numpy(inv).to(DEV), torch.from_numpy(w).to(DEV), None, buf, T, H, k,
+                  buf)
+    torch.cuda.synchronize()
+    ref, ref64 = O.combine(ys[0].astype(np.float64), inv, w, None, r)
+    absum = np.abs(r.astype(np.float64)) + 0.5 * np.abs(ys[0].astype(np.float64)).reshape(
+        T, k, H).sum(axis=1)
+    _assert_combine_close(_np(buf).astype(np.float64), ref, ref64, absum, k + 1)
+
+
+# ---------------------------------------------------------- whole layer
+
+def _oracle_tokens(cfg, x, toks, layer=0, residual=None, shared=True):
+    """Oracle layer output for selected tokens (routing, FFN, combine)."""
+    xs = x[toks]
+    wr = MI.gen_router(cfg, layer)
+    bias = MI.zipf_bias(cfg, layer)
+    idx, _, _ = O.route(xs, wr, bias, cfg.k)
+    blobs = OracleBlobs(cfg, layer).get(np.unique(idx))
+    sh = MI.gen_shared(cfg) if (shared and cfg.Is) else None
+    res = None if residual is None else residual[toks]
+    return O.moe_layer(xs, wr, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, bias=bias,
+                       shared=sh, residual=res)
+
+
+@pytest.mark.parametrize("cfg,T", [(MI.TINY, 16), (MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 64),
+                                   (MI.OLMOE_DECODE, 512), (MI.OLMOE_DECODE, 4096),
+                                   (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_end_to_end(cfg, T):
+    lay = make_layer(cfg, 0)
+    x = MI.gen_x(cfg, T)
+    res = MI.gen_residual(cfg, T) if cfg.residual else None
+    b = lay.buffers(T)
+    say("layer %s T=%d regime=%d" % (cfg.name, T, b.regime))
+    out = lay.forward(f16(x), b, None if res is None else f16(res))
+    torch.cuda.synchronize()
+    toks = np.arange(T) if T <= 16 else np.sort(
+        np.random.default_rng(T).choice(T, 12, replace=False))
+    ref = _oracle_tokens(cfg, x, toks, residual=res)
+    assert np.array_equal(_np(b.topk_idx)[toks], ref["idx"])
+    check_close(_np(out)[toks].astype(np.float64), ref["out_f64"], "out %s T=%d" % (cfg.name, T))
+    # determinism: a second run gives the same bits
+    out2 = lay.forward(f16(x), lay.buffers(T), None if res is None else f16(res))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_single_expert_top1_hot_path():
+    """E = 1, k = 1 with a ragged T: one bucket of T rows, weight exactly 1."""
+    cfg = MI.MoEConfig(90, "e1k1", H=256, E=1, k=1, I=128, g=64)
+    lay = make_layer(cfg, 0, shared=False)
+    for T, regime in [(1, M.MOE_REGIME_DECODE), (300, M.MOE_REGIME_BATCHED),
+                      (5, M.MOE_REGIME_DECODE)]:
+        say("e1k1 T=%d" % T)
+        x = MI.gen_x(cfg, T)
+        b = lay.buffers(T, regime)
+        out = lay.forward(f16(x), b)
+        torch.cuda.synchronize()
+        assert np.all(_np(b.topk_w) == 1.0)
+        ref = _oracle_tokens(cfg, x, np.arange(T), shared=False)
+        check_close(_np(out).astype(np.float64), ref["out_f64"], "e1k1 T=%d" % T)
+
+
+def test_hot_expert_many_tiles():
+    """A large bias sends every token to expert 5: one bucket of 4096 rows."""
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0, shared=False)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[5] = 100.0
+    lay.bias = torch.from_numpy(bias).to(DEV)
+    T = 4096
+    x = MI.gen_x(cfg, T)
+    b = lay.buffers(T)
+    say("hot expert T=%d" % T)
+    xd = f16(x)
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    torch.cuda.synchronize()
+    oi, _, _ = O.route(x, MI.gen_router(cfg), bias, cfg.k)
+    assert np.array_equal(_np(b.topk_idx), oi)
+    counts, offsets, perm, _ = O.permute(oi, cfg.E)
+    assert counts[5] == T
+    rows = np.array([offsets[5], offsets[5] + 127, offsets[5] + 128, offsets[5] + 2049,
+                     offsets[6] - 1], np.int32)
+    y_ref = O.expert_ffn(x, perm, offsets, OracleBlobs(cfg, 0).get([5]), cfg.H, cfg.I, cfg.E,
+                         cfg.k, cfg.g, rows=rows)
+    check_close(_np(b.y)[0][rows].astype(np.float64), y_ref, "hot expert y")
+
+
+def test_zero_tokens_is_noop():
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0, shared=False)
+    b = lay.buffers(0)
+    lay.forward(f16(np.zeros((0, cfg.H), np.float16)), b)
+    torch.cuda.synchronize()
+    assert np.all(_np(b.offsets) == 0) and np.all(_np(b.counts) == 0)
