@@ -153,6 +153,25 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                 void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * moe_route followed by moe_permute, with the same arguments and results
+ * (same passages and readings).  For T <= 8 both run in one launch: the
+ * logits are spread over many workgroups, and the workgroup that finishes
+ * last (an atomic ticket in ws; no workgroup ever waits for another) does the
+ * top-k, the softmax and the stable sort -- the decode path's one launch
+ * instead of two.  For larger T it issues the two separate launches.
+ * ws: device scratch of moe_route_permute_workspace_bytes(T, k, E) bytes.  It
+ * must be zero-filled before its first use by this function; every completed
+ * call leaves it reusable (the ticket back at zero).  Calls that share one
+ * workspace must not run concurrently.
+ */
+size_t moe_route_permute_workspace_bytes(int T, int k, int E);
+int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias,
+                      int T, int H, int E, int k, unsigned flags,
+                      int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets,
+                      int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* ------------------------------------------------ routed expert FFN */
 /*
  * What moe_expert_ffn_w4a16 will do for a shape: the resolved regime (AUTO

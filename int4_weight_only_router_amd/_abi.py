@@ -12,8 +12,9 @@ __all__ = [
     "MOE_REGIME_BATCHED", "MOE_DTYPE_F16", "MOE_DTYPE_F32", "EXPORTS",
     "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
+    "moe_route_permute_workspace_bytes", "moe_route_permute", "moe_expert_ffn_plan",
+    "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes", "moe_shared_ffn_f16",
+    "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
     "moe_pool_prepare", "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
 ]
@@ -28,8 +29,9 @@ MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
 EXPORTS = [
     "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "moe_pool_create", "moe_pool_prepare",
+    "moe_route_permute_workspace_bytes", "moe_route_permute", "moe_expert_ffn_plan",
+    "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes", "moe_shared_ffn_f16",
+    "moe_combine", "moe_pool_create", "moe_pool_prepare",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
 ]
 
@@ -68,6 +70,9 @@ def _declare(L):
         "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp]),
         "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_route_permute_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_route_permute": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp, vp,
+                                    vp, vp, vp, sz, vp]),
         "moe_expert_ffn_plan": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
         "moe_expert_ffn_w4a16": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        vp, i32, i32, vp, sz, vp]),
@@ -162,6 +167,18 @@ def moe_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws=None, ws_
                 stream=None):
     return _check(lib().moe_permute(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(perm),
                                     _p(inv_perm), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_route_permute_workspace_bytes(T, k, E):
+    return lib().moe_route_permute_workspace_bytes(T, k, E)
+
+
+def moe_route_permute(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk_w, counts,
+                      offsets, perm, inv_perm, ws=None, ws_bytes=0, stream=None):
+    return _check(lib().moe_route_permute(_p(x), _p(w_router), _p(logit_bias), T, H, E, k,
+                                          flags, _p(topk_idx), _p(topk_w), _p(counts),
+                                          _p(offsets), _p(perm), _p(inv_perm), _p(ws), ws_bytes,
+                                          _s(stream)))
 
 
 def moe_expert_ffn_plan(T, H, I, E, k, group, regime=MOE_REGIME_AUTO):

@@ -26,9 +26,20 @@ __global__ __launch_bounds__(256) void combine_slices_kernel(
     if (j < k && c < H) {
         const size_t p = (size_t)inv_perm[(size_t)t * k + j];
         const float *src = y + p * H + c;
+        const size_t stride = ntk * H;
         float v = 0.0f;
-        for (int s = 0; s < S; ++s)
-            v += src[(size_t)s * ntk * H];
+        // issue a batch of slice loads before summing them (in slice order)
+        constexpr int SB = 32;
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            float vb[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i)
+                vb[i] = (s0 + i < S) ? src[(size_t)(s0 + i) * stride] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < SB; ++i)
+                if (s0 + i < S)
+                    v += vb[i];
+        }
         part[j][cc] = w[(size_t)t * k + j] * v;
     }
     __syncthreads();

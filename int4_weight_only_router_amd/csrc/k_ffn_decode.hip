@@ -23,25 +23,86 @@
 
 namespace moe {
 
-// Finds the a-th expert (in id order) with at least one routed row; -1 if none.
-__device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ offsets, int E,
-                                                 int a, int lane)
+// Finds the a-th expert (in id order) with at least one routed row; -1 if
+// none.  The blob pointers are fetched in the same sweep as the offsets, so
+// the expert's weight address is known one memory round trip after entry.
+__device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ offsets,
+                                                 const uint8_t *const *__restrict__ blobs, int E,
+                                                 int a, int lane, const uint8_t **blob_out)
 {
     int seen = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        const bool act = e < E && offsets[e + 1] > offsets[e];
+        const bool inb = e < E;
+        const int o0 = inb ? offsets[e] : 0;
+        const int o1 = inb ? offsets[e + 1] : 0;
+        const uint8_t *bp = inb ? blobs[e] : nullptr;
+        const bool act = o1 > o0;
         const uint64_t m = __ballot(act);
         const int n = __popcll(m);
         if (seen + n > a) {
             const int r = a - seen;
             const int rank = __popcll(m & ((1ull << lane) - 1ull));
             const uint64_t hit = __ballot(act && rank == r);
-            return e0 + (__ffsll((long long)hit) - 1);
+            const int src = __ffsll((long long)hit) - 1;
+            *blob_out = reinterpret_cast<const uint8_t *>(
+                __shfl(reinterpret_cast<long long>(bp), src, 64));
+            return e0 + src;
         }
         seen += n;
     }
     return -1;
+}
+
+constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are staged at entry
+
+// The dot products take the weights as "magic" fp16 values without decoding
+// them: OR-ing a nibble into the mantissa of 1024.0 gives v = 1024 + u (low
+// field of a half, bits 0..3) or v = 1024 + 16u (high field, bits 4..7).  With
+// the activation pair of a high field pre-divided by 16 (exact: a power of
+// two), v * x' = 1024 x + u x or 64 x + u x, and the chunk sum of
+// (u - 8) x = q x follows by starting the accumulator at
+// -1032 * (sum of x over low-field pairs) - 72 * (sum over high-field pairs).
+// That constant depends only on the activations, so it is computed once per
+// token and chunk.  Pair p of a 32-element chunk is a high-field pair iff p is
+// odd (device nibble layout).  The fp32 running sums stay within a few
+// thousand, so rounding is ~1e-7 relative to them: far inside the budget.
+__device__ __forceinline__ float dot_chunk(uint4_t w, const half2_t *xp, float d)
+{
+    const uint32_t M = 0x64006400u;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t v = ws[j], v8 = ws[j] >> 8;
+        d = dot2(__builtin_bit_cast(half2_t, (v & 0x000F000Fu) | M), xp[4 * j + 0], d);
+        d = dot2(__builtin_bit_cast(half2_t, (v & 0x00F000F0u) | M), xp[4 * j + 1], d);
+        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x000F000Fu) | M), xp[4 * j + 2], d);
+        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x00F000F0u) | M), xp[4 * j + 3], d);
+    }
+    return d;
+}
+
+// Prepares one 32-element chunk of activations: pairs with odd index divided
+// by 16, and the chunk's correction constant.
+__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr)
+{
+    float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const half8_t v = *reinterpret_cast<const half8_t *>(src + 8 * q);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f16 a = v[2 * m], b = v[2 * m + 1];
+            if (m & 1) {
+                shi += (float)a + (float)b;
+                dst[4 * q + m] = half2_t{a * (f16)0.0625f, b * (f16)0.0625f};
+            } else {
+                slo += (float)a + (float)b;
+                dst[4 * q + m] = half2_t{a, b};
+            }
+        }
+    }
+    *corr = -1032.0f * slo - 72.0f * shi;
 }
 
 template <int H, int NW>
@@ -57,26 +118,42 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     constexpr int RBW = (NRB + NW - 1) / NW;   // down blocks per wave
     static_assert(NK % NW == 0, "H/32 must be a multiple of the wave count");
 
-    __shared__ __align__(16) f16 xs[H];
+    __shared__ __align__(16) half2_t xp[DECODE_XPRE][H / 2];   // prepared activations
+    __shared__ float xc[DECODE_XPRE][NK];                     // their chunk constants
     __shared__ float red[NW * 64];
-    __shared__ __align__(16) f16 hs[32];
+    __shared__ __align__(16) half2_t hp[16];                  // prepared h chunk
+    __shared__ float hcorr;
     __shared__ int s_e;
+    __shared__ const uint8_t *s_blob;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int slice = blockIdx.x;
+    const int T = ntk / k;
+    const bool xpre = T <= DECODE_XPRE;
 
+    // activations of the whole (small) batch are prepared while the expert
+    // is looked up: thread -> (token, chunk)
+    if (xpre) {
+        for (int i = threadIdx.x; i < T * NK; i += NW * 64) {
+            const int t = i / NK, c = i % NK;
+            prep_chunk(x + (size_t)t * H + c * 32, &xp[t][c * 16], &xc[t][c]);
+        }
+    }
     if (wave == 0) {
-        int e = nth_active_expert(offsets, E, blockIdx.y, lane);
-        if (lane == 0)
+        const uint8_t *bp = nullptr;
+        int e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &bp);
+        if (lane == 0) {
             s_e = e;
+            s_blob = bp;
+        }
     }
     __syncthreads();
     const int e = s_e;
     if (e < 0)
         return;
     const int p0 = offsets[e], p1 = offsets[e + 1];
-    const uint8_t *blob = blobs[e];
+    const uint8_t *blob = s_blob;
     const int IC = I / 32;                     // input chunks of the down rows
 
     // ---- issue every weight load of this workgroup up front
@@ -111,29 +188,20 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
     for (int p = p0; p < p1; ++p) {
         const int t = perm[p] / k;
-        {
-            const uint4_t *src = reinterpret_cast<const uint4_t *>(x + (size_t)t * H);
-            uint4_t *dst = reinterpret_cast<uint4_t *>(xs);
-            for (int i = threadIdx.x; i < H / 8; i += NW * 64)
-                dst[i] = src[i];
+        int slot = t;
+        if (!xpre) {
+            slot = 0;
+            for (int c = threadIdx.x; c < NK; c += NW * 64)
+                prep_chunk(x + (size_t)t * H + c * 32, &xp[0][c * 16], &xc[0][c]);
+            __syncthreads();
         }
-        __syncthreads();
 
         // gate/up rows (lane = row of the fused block), K split over waves
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int c = wave * CPW + i;
-            const half2_t *xc = reinterpret_cast<const half2_t *>(xs + c * 32);
-            half2_t q[16];
-            nib8_to_h2x4(wq[i].x, q + 0);
-            nib8_to_h2x4(wq[i].y, q + 4);
-            nib8_to_h2x4(wq[i].z, q + 8);
-            nib8_to_h2x4(wq[i].w, q + 12);
-            float d = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m)
-                d = dot2(q[m], xc[m], d);
+            const float d = dot_chunk(wq[i], &xp[slot][c * 16], xc[slot][c]);
             acc = fmaf(d, sgu[i], acc);
         }
         red[wave * 64 + lane] = acc;
@@ -144,31 +212,30 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
             for (int w = 0; w < NW; ++w)
                 v += red[w * 64 + lane];
             const float up = __shfl(v, (lane + 32) & 63, 64);
+            // h for intermediate index lane (lanes < 32), rounded to fp16
+            const f16 hq = (f16)(v / (1.0f + expf(-v)) * up);
+            const bool odd = (lane >> 1) & 1;
+            float cc = 0.0f;
             if (lane < 32) {
-                const float hv = v / (1.0f + expf(-v)) * up;
-                hs[lane] = (f16)hv;
+                reinterpret_cast<f16 *>(hp)[lane] = odd ? hq * (f16)0.0625f : hq;
+                cc = (odd ? -72.0f : -1032.0f) * (float)hq;
             }
+#pragma unroll
+            for (int st = 16; st >= 1; st >>= 1)
+                cc += __shfl_xor(cc, st, 64);
+            if (lane == 0)
+                hcorr = cc;
         }
         __syncthreads();
 
-        // down strip: lane = output row, 32 h values from LDS
-        const half2_t *hh = reinterpret_cast<const half2_t *>(hs);
+        // down strip: lane = output row, the 32 prepared h values from LDS
         float *yrow = y + ((size_t)slice * ntk + p) * H;
+        const float hc = hcorr;
 #pragma unroll
         for (int r = 0; r < RBW; ++r) {
             const int rb = wave * RBW + r;
-            if (rb < NRB) {
-                half2_t q[16];
-                nib8_to_h2x4(dq[r].x, q + 0);
-                nib8_to_h2x4(dq[r].y, q + 4);
-                nib8_to_h2x4(dq[r].z, q + 8);
-                nib8_to_h2x4(dq[r].w, q + 12);
-                float d = 0.0f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    d = dot2(q[m], hh[m], d);
-                yrow[rb * 64 + lane] = d * sd[r];
-            }
+            if (rb < NRB)
+                yrow[rb * 64 + lane] = dot_chunk(dq[r], hp, hc) * sd[r];
         }
         __syncthreads();
     }

@@ -12,42 +12,12 @@
 // the elements 64 at a time; a lane's rank among equal keys of earlier lanes
 // comes from a readlane sweep, and a per-expert running counter in LDS
 // advances by the group's multiplicity (LDS max of the new end positions).
-#include "moe_common.h"
+#include "k_sort_common.h"
 
 namespace moe {
 
 constexpr int PERM_CH = 512;     // elements per chunk in the multi-block path
 constexpr int PERM_SMALL = 512;  // up to this many elements: one wave does everything
-
-// Stable scatter of elements [f0, f1) by one wave, running counters in cnt[].
-__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ idx, int f0, int f1,
-                                             int E, int *cnt, int32_t *__restrict__ perm,
-                                             int32_t *__restrict__ inv_perm, int lane)
-{
-    for (int base = f0; base < f1; base += 64) {
-        const int f = base + lane;
-        int key = (f < f1) ? idx[f] : -1;
-        if ((unsigned)key >= (unsigned)E)   // out-of-range ids are skipped, never scattered
-            key = -1;
-        const bool valid = key >= 0;
-        int rank = 0;
-        const int nval = min(64, f1 - base);
-        for (int i = 0; i < nval; ++i) {
-            int ki = __builtin_amdgcn_readlane(key, i);
-            rank += (ki == key && i < lane) ? 1 : 0;
-        }
-        int pos = 0;
-        if (valid)
-            pos = cnt[key] + rank;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            atomicMax(&cnt[key], pos + 1);
-            perm[pos] = f;
-            inv_perm[f] = pos;
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-}
 
 // Whole sort in one wave (small T*k).
 __global__ __launch_bounds__(64) void permute_small_kernel(
@@ -55,44 +25,8 @@ __global__ __launch_bounds__(64) void permute_small_kernel(
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
 {
     extern __shared__ int cnt[];   // [E]
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64)
-        cnt[e] = 0;
-    __syncthreads();
-    for (int f = lane; f < n; f += 64)
-        if ((unsigned)idx[f] < (unsigned)E)
-            atomicAdd(&cnt[idx[f]], 1);
-    __syncthreads();
-    // exclusive scan over E in segments of per = ceil(E/64) experts per lane
-    const int per = (E + 63) / 64;
-    const int e0 = lane * per;
-    int seg = 0;
-    for (int i = 0; i < per; ++i)
-        if (e0 + i < E)
-            seg += cnt[e0 + i];
-    int incl = seg;
-#pragma unroll
-    for (int st = 1; st < 64; st <<= 1) {
-        int o = __shfl_up(incl, st, 64);
-        if (lane >= st)
-            incl += o;
-    }
-    int run = incl - seg;
-    __syncthreads();
-    for (int i = 0; i < per; ++i) {
-        int e = e0 + i;
-        if (e < E) {
-            int c = cnt[e];
-            counts[e] = c;
-            offsets[e] = run;
-            cnt[e] = run;        // becomes the running write position
-            run += c;
-        }
-    }
-    if (lane == 63)
-        offsets[E] = run;
-    __syncthreads();
-    wave_scatter(idx, 0, n, E, cnt, perm, inv_perm, lane);
+    wave_count_scan(idx, n, E, cnt, counts, offsets, threadIdx.x);
+    wave_scatter(idx, 0, n, E, cnt, perm, inv_perm, threadIdx.x);
 }
 
 // Phase 1: per-chunk histograms hist[b][E].

@@ -1,4 +1,5 @@
-// k_route.hip -- router logits, softmax and top-k (K1).
+// k_route.hip -- router logits, softmax and top-k (K1), optionally fused with
+// the token-to-expert permutation for batches that fit one workgroup.
 //
 // Horizon RunMap, "03 / Arquitetura": the router selects the experts that
 // work on each token; "08 / Comportamento do modelo": routing stays outside
@@ -15,61 +16,79 @@
 //  * Top-k by (logit desc, expert asc); softmax over all E logits taken at the
 //    chosen experts; optional renormalisation over the k chosen.
 //
-// Work split: a workgroup of 4 waves owns TT tokens (x tile staged in LDS);
-// wave w computes experts w, w+4, ... for all TT tokens, so each router
-// chunk loaded from global memory is reused TT times.
-#include "moe_common.h"
+// Work split: a workgroup owns TT tokens (x tile in LDS); wave w computes
+// experts w, w+NW, ... for all TT tokens, each router chunk loaded from
+// global memory once per workgroup and reused TT times.  A wave issues the
+// loads of its next expert before the arithmetic of the current one, so at
+// decode sizes the router costs about two memory round trips, not one per
+// expert.
+#include "k_sort_common.h"
 
 namespace moe {
 
-constexpr int ROUTE_WAVES = 4;
-
-template <int TT>
-__global__ __launch_bounds__(ROUTE_WAVES * 64) void route_kernel(
+template <int H, int TT, int NW>
+__global__ __launch_bounds__(NW * 64) void route_kernel(
     const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
-    int T, int H, int E, int k, unsigned flags, int32_t *__restrict__ idx_out,
-    float *__restrict__ w_out)
+    int T, int E, int k, unsigned flags, int32_t *__restrict__ idx_out, float *__restrict__ w_out)
 {
+    constexpr int NCH = H / 8;                // 8-element chunks of a row
+    constexpr int NCL = (NCH + 63) / 64;      // chunks per lane
     extern __shared__ __align__(16) unsigned char smem[];
-    f16 *xs = reinterpret_cast<f16 *>(smem);                                  // [TT][H]
+    const int nb = (E + 63) / 64;
+    f16 *xs = reinterpret_cast<f16 *>(smem);                                    // [TT][H]
     float *lg = reinterpret_cast<float *>(smem + (size_t)TT * H * sizeof(f16));  // [TT][E]
+    Cand *cand = reinterpret_cast<Cand *>(lg + (size_t)TT * E);                  // [NW][nb*16]
+    Cand *sel = cand + (size_t)NW * nb * 16;                                     // [NW][16]
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * TT;
     const int nt = min(TT, T - t0);
 
-    // x tile -> LDS (16-byte pieces); rows past T are zero
     {
-        const int per_row = H / 8;
+        constexpr int per_row = H / 8;
         const uint4_t *src = reinterpret_cast<const uint4_t *>(x);
         uint4_t *dst = reinterpret_cast<uint4_t *>(xs);
-        for (int i = threadIdx.x; i < TT * per_row; i += blockDim.x) {
-            int r = i / per_row;
+        for (int i = threadIdx.x; i < TT * per_row; i += NW * 64) {
+            const int r = i / per_row;
             uint4_t v = {0u, 0u, 0u, 0u};
             if (r < nt)
                 v = src[(size_t)(t0 + r) * per_row + (i % per_row)];
             dst[i] = v;
         }
     }
+
+    uint4_t cur[NCL], nxt[NCL];
+    auto load = [&](int e, uint4_t *dst) {
+        const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
+#pragma unroll
+        for (int m = 0; m < NCL; ++m) {
+            const int c = lane + 64 * m;
+            dst[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    load(wave, cur);
     __syncthreads();
 
-    const int nchunk = H / 8;
-    for (int e = wave; e < E; e += ROUTE_WAVES) {
+    for (int e = wave; e < E; e += NW) {
+        load(e + NW, nxt);
         float acc[TT];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
             acc[tt] = 0.0f;
-        const uint4_t *wrow = reinterpret_cast<const uint4_t *>(wr + (size_t)e * H);
-        for (int c = lane; c < nchunk; c += 64) {
-            uint4_t wv = wrow[c];
-            half8_t wh = __builtin_bit_cast(half8_t, wv);
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                half8_t xh = *reinterpret_cast<const half8_t *>(xs + (size_t)tt * H + c * 8);
+        for (int m = 0; m < NCL; ++m) {
+            const int c = lane + 64 * m;
+            if (c < NCH) {
+                const half8_t wh = __builtin_bit_cast(half8_t, cur[m]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[tt] = acc[tt] + (float)xh[i] * (float)wh[i];
+                for (int tt = 0; tt < TT; ++tt) {
+                    const half8_t xh =
+                        *reinterpret_cast<const half8_t *>(xs + (size_t)tt * H + c * 8);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc[tt] = acc[tt] + (float)xh[i] * (float)wh[i];
+                }
             }
         }
         const float b = bias ? bias[e] : 0.0f;
@@ -84,68 +103,274 @@ __global__ __launch_bounds__(ROUTE_WAVES * 64) void route_kernel(
             if (lane == 0)
                 lg[tt * E + e] = a;
         }
+#pragma unroll
+        for (int m = 0; m < NCL; ++m)
+            cur[m] = nxt[m];
     }
     __syncthreads();
 
-    // top-k + softmax: wave w handles tokens w, w+4, ...
-    for (int tt = wave; tt < nt; tt += ROUTE_WAVES) {
+    // top-k + softmax: wave w handles tokens w, w+NW, ... (rank-based top-k)
+    Cand *wc = cand + (size_t)wave * nb * 16;
+    Cand *st = sel + wave * 16;
+    for (int tt = wave; tt < nt; tt += NW) {
         const float *l = lg + tt * E;
-        // each lane scans its experts e = lane + 64 m; "taken" bits per lane
-        uint32_t taken = 0u;   // bit m set when expert lane+64m chosen (E <= 2048)
-        float vsel[16];
-        int esel[16];
-        for (int j = 0; j < k; ++j) {
-            float bv = 0.0f;
-            int be = 0x7fffffff;
-            for (int m = 0, e = lane; e < E; ++m, e += 64) {
-                if (taken & (1u << m))
-                    continue;
-                float v = l[e];
-                if (be == 0x7fffffff || v > bv) {   // ascending e: ties keep lower index
-                    bv = v;
-                    be = e;
-                }
-            }
-            // wave argmax with lower-index tie-break
-#pragma unroll
-            for (int st = 32; st >= 1; st >>= 1) {
-                float ov = __shfl_xor(bv, st, 64);
-                int oe = __shfl_xor(be, st, 64);
-                bool take = (oe != 0x7fffffff) &&
-                            (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-                if (take) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be & 63) == lane)
-                taken |= 1u << (be >> 6);
-            vsel[j] = bv;
-            esel[j] = be;
-        }
-        // softmax over all E (fp32), max = best logit
-        const float m = vsel[0];
+        for (int b = 0; b < nb; ++b)
+            block_topk(l, E, k, b, lane, wc + b * k);
+        __builtin_amdgcn_wave_barrier();
+        merge_topk(wc, nb * k, k, lane, st);
+        __builtin_amdgcn_wave_barrier();
+        const float m = st[0].v;
         float part = 0.0f;
         for (int e = lane; e < E; e += 64)
             part += expf(l[e] - m);
 #pragma unroll
-        for (int st = 32; st >= 1; st >>= 1)
-            part += __shfl_xor(part, st, 64);
-        const float den = part;
-        float wsum = 0.0f;
-        for (int j = 0; j < k; ++j)
-            wsum += expf(vsel[j] - m) / den;
-        if (lane == 0) {
+        for (int sh = 32; sh >= 1; sh >>= 1)
+            part += __shfl_xor(part, sh, 64);
+        float p = 0.0f;
+        if (lane < k)
+            p = expf(st[lane].v - m) / part;
+        if (flags & MOE_RENORM) {
+            float ws = p;
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1)
+                ws += __shfl_xor(ws, sh, 64);
+            p = p / ws;
+        }
+        if (lane < k) {
             const size_t t = (size_t)(t0 + tt);
-            for (int j = 0; j < k; ++j) {
-                float p = expf(vsel[j] - m) / den;
-                if (flags & MOE_RENORM)
-                    p = p / wsum;
-                idx_out[t * k + j] = esel[j];
-                w_out[t * k + j] = p;
+            idx_out[t * k + lane] = st[lane].e;
+            w_out[t * k + lane] = p;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Small batches (T <= 8) spread over many workgroups.  Workgroup g computes
+// the logits of experts 4g..4g+3 (one wave each, every router load issued at
+// once) for all T tokens and stores them to the workspace with agent-scope
+// (write-through) stores; once they are acknowledged, one thread takes a
+// ticket from an atomic counter.  The workgroup holding the last ticket reads
+// every logit back with agent-scope loads and does the top-k, the softmax
+// and, when FUSE, the stable sort, then returns the counter to zero.  No
+// cache-wide fence is needed because all shared data moves through the
+// coherent path, and no workgroup ever waits for another.
+constexpr int RSPLIT_EPW = 4;
+
+template <int H, int TT, bool FUSE>
+__global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
+    const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
+    int T, int E, int k, unsigned flags, unsigned *ticket, float *ws_logits,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
+{
+    constexpr int NCH = H / 8;
+    constexpr int NCL = (NCH + 63) / 64;
+    extern __shared__ __align__(16) unsigned char smem[];
+    f16 *xs = reinterpret_cast<f16 *>(smem);   // [TT][H]; reused by the last group
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * RSPLIT_EPW + wave;
+
+    uint4_t wv[NCL];
+    {
+        const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
+#pragma unroll
+        for (int m = 0; m < NCL; ++m) {
+            const int c = lane + 64 * m;
+            wv[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
+        }
+        const uint4_t *src = reinterpret_cast<const uint4_t *>(x);
+        uint4_t *dst = reinterpret_cast<uint4_t *>(xs);
+        for (int i = threadIdx.x; i < T * (H / 8); i += RSPLIT_EPW * 64)
+            dst[i] = src[i];
+    }
+    __syncthreads();
+    if (e < E) {
+        float acc[TT];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+            acc[tt] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NCL; ++m) {
+            const int c = lane + 64 * m;
+            if (c < NCH) {
+                const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    if (tt < T) {
+                        const half8_t xh =
+                            *reinterpret_cast<const half8_t *>(xs + (size_t)tt * H + c * 8);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            acc[tt] = acc[tt] + (float)xh[i] * (float)wh[i];
+                    }
+                }
+            }
+        }
+        const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            float a = acc[tt];
+#pragma unroll
+            for (int st = 32; st >= 1; st >>= 1)
+                a = a + __shfl_xor(a, st, 64);
+            if (bias)
+                a = a + b;
+            if (lane == 0 && tt < T)
+                __hip_atomic_store(ws_logits + tt * E + e, a, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's logit stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+
+    const int nb = (E + 63) / 64;
+    float *lg = reinterpret_cast<float *>(smem);                      // [T][E]
+    Cand *cand = reinterpret_cast<Cand *>(lg + (size_t)TT * E);       // [T][nb][k]
+    Cand *sel = cand + (size_t)TT * nb * 16;                          // [T][16]
+    int *sidx = reinterpret_cast<int *>(sel + TT * 16);               // [T*k]
+    int *cnt = sidx + TT * 16;                                        // [E]
+    for (int i = threadIdx.x; i < T * E; i += RSPLIT_EPW * 64)
+        lg[i] = __hip_atomic_load(ws_logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+
+    // local top-k of every (token, 64-expert block), spread over the waves
+    for (int tb = wave; tb < T * nb; tb += RSPLIT_EPW) {
+        const int tt = tb / nb, b = tb % nb;
+        block_topk(lg + tt * E, E, k, b, lane, cand + ((size_t)tt * nb + b) * k);
+    }
+    __syncthreads();
+    // merge, softmax and outputs: one wave per token
+    for (int tt = wave; tt < T; tt += RSPLIT_EPW) {
+        Cand *st = sel + tt * 16;
+        merge_topk(cand + (size_t)tt * nb * k, nb * k, k, lane, st);
+        __builtin_amdgcn_wave_barrier();
+        const float m = st[0].v;
+        float part = 0.0f;
+        for (int ee = lane; ee < E; ee += 64)
+            part += expf(lg[tt * E + ee] - m);
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1)
+            part += __shfl_xor(part, sh, 64);
+        const float den = part;
+        float p = 0.0f;
+        if (lane < k)
+            p = expf(st[lane].v - m) / den;
+        if (flags & MOE_RENORM) {
+            float ws = p;
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1)
+                ws += __shfl_xor(ws, sh, 64);
+            p = p / ws;
+        }
+        if (lane < k) {
+            idx_out[(size_t)tt * k + lane] = st[lane].e;
+            w_out[(size_t)tt * k + lane] = p;
+            if (FUSE)
+                sidx[tt * k + lane] = st[lane].e;
+        }
+    }
+    if (FUSE) {
+        __syncthreads();
+        if (wave == 0) {
+            const int n = T * k;
+            if (E <= 128) {
+                wave_small_sort(sidx, n, E, counts, offsets, perm, inv_perm, lane);
+            } else {
+                wave_count_scan(sidx, n, E, cnt, counts, offsets, lane);
+                wave_stable_positions(sidx, n, perm, inv_perm, lane);
             }
         }
     }
+}
+
+size_t route_split_ws_bytes(int T, int E) { return 256 + (size_t)T * E * sizeof(float); }
+
+// T <= 8; ws: zero-filled ticket (first 256 bytes) + T*E logits.
+template <int H>
+static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, int T, int E,
+                                int k, unsigned flags, int32_t *idx, float *w, int32_t *counts,
+                                int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
+                                hipStream_t s)
+{
+    unsigned *ticket = static_cast<unsigned *>(ws);
+    float *lg = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
+    const dim3 grid((E + RSPLIT_EPW - 1) / RSPLIT_EPW), block(RSPLIT_EPW * 64);
+    const size_t nb = (E + 63) / 64;
+    const size_t xb = (size_t)8 * H * sizeof(f16);
+    const size_t lb = (size_t)8 * E * sizeof(float) + (size_t)8 * nb * 16 * sizeof(Cand) +
+                      (size_t)8 * 16 * sizeof(Cand) + (size_t)(8 * 16 + E) * sizeof(int);
+    const size_t lds = xb > lb ? xb : lb;
+#define MOE_RSPLIT(TT)                                                                          \
+    hipLaunchKernelGGL((route_split_kernel<H, TT, true>), grid, block, lds, s, x, wr, bias, T,  \
+                       E, k, flags, ticket, lg, idx, w, counts, offsets, perm, inv_perm)
+    if (T <= 1) MOE_RSPLIT(1);
+    else if (T <= 2) MOE_RSPLIT(2);
+    else if (T <= 4) MOE_RSPLIT(4);
+    else MOE_RSPLIT(8);
+#undef MOE_RSPLIT
+    MOE_LAUNCH_CHECK("route_split_kernel");
+    return MOE_OK;
+}
+
+int launch_route_split(const void *x, const void *wr, const float *bias, int T, int H, int E,
+                       int k, unsigned flags, int32_t *idx, float *w, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
+                       hipStream_t s)
+{
+    const f16 *xh = static_cast<const f16 *>(x), *wh = static_cast<const f16 *>(wr);
+    switch (H) {
+    case 256: return launch_route_split_h<256>(xh, wh, bias, T, E, k, flags, idx, w, counts,
+                                               offsets, perm, inv_perm, ws, s);
+    case 512: return launch_route_split_h<512>(xh, wh, bias, T, E, k, flags, idx, w, counts,
+                                               offsets, perm, inv_perm, ws, s);
+    case 1024: return launch_route_split_h<1024>(xh, wh, bias, T, E, k, flags, idx, w, counts,
+                                                 offsets, perm, inv_perm, ws, s);
+    case 2048: return launch_route_split_h<2048>(xh, wh, bias, T, E, k, flags, idx, w, counts,
+                                                 offsets, perm, inv_perm, ws, s);
+    default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
+    }
+}
+
+template <int H>
+static int launch_route_h(const f16 *x, const f16 *wr, const float *bias, int T, int E, int k,
+                          unsigned flags, int32_t *idx, float *w, hipStream_t s)
+{
+    const size_t nb = (E + 63) / 64;
+    const size_t per_tok = (size_t)H * sizeof(f16) + (size_t)E * sizeof(float);
+    auto lds_for = [&](int TT, int NW) {
+        return (size_t)TT * per_tok + (size_t)NW * (nb * 16 + 16) * sizeof(Cand);
+    };
+#define MOE_ROUTE_LAUNCH(TT, NW)                                                                 \
+    hipLaunchKernelGGL((route_kernel<H, TT, NW>), dim3((T + TT - 1) / TT), dim3(NW * 64),        \
+                       lds_for(TT, NW), s, x, wr, bias, T, E, k, flags, idx, w)
+    if (T <= 8) {
+        // one workgroup of 16 waves
+        if (T <= 1) MOE_ROUTE_LAUNCH(1, 16);
+        else if (T <= 2) MOE_ROUTE_LAUNCH(2, 16);
+        else if (T <= 4) MOE_ROUTE_LAUNCH(4, 16);
+        else MOE_ROUTE_LAUNCH(8, 16);
+    } else {
+        // token tiles of 8 (fewer if the tile would exceed 64 KB of LDS)
+        if (lds_for(8, 4) <= 65536) MOE_ROUTE_LAUNCH(8, 4);
+        else if (lds_for(4, 4) <= 65536) MOE_ROUTE_LAUNCH(4, 4);
+        else MOE_ROUTE_LAUNCH(2, 4);
+    }
+#undef MOE_ROUTE_LAUNCH
+    MOE_LAUNCH_CHECK("route_kernel");
+    return MOE_OK;
 }
 
 int launch_route(const void *x, const void *wr, const float *bias, int T, int H, int E, int k,
@@ -153,27 +378,14 @@ int launch_route(const void *x, const void *wr, const float *bias, int T, int H,
 {
     if (T == 0)
         return MOE_OK;
-    // tokens per workgroup: 8 for large T, fewer if the tile would exceed the
-    // default 64 KB of dynamic LDS
-    const size_t per_tok = (size_t)H * sizeof(f16) + (size_t)E * sizeof(float);
-    int TT = (T >= 64) ? 8 : 1;
-    while (TT > 1 && TT * per_tok > 65536)
-        TT >>= 1;
-    const size_t lds = TT * per_tok;
-    dim3 grid((T + TT - 1) / TT), block(ROUTE_WAVES * 64);
     const f16 *xh = static_cast<const f16 *>(x), *wh = static_cast<const f16 *>(wr);
-    switch (TT) {
-    case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, lds, s, xh, wh, bias, T, H, E, k,
-                               flags, idx, w); break;
-    case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, lds, s, xh, wh, bias, T, H, E, k,
-                               flags, idx, w); break;
-    case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, lds, s, xh, wh, bias, T, H, E, k,
-                               flags, idx, w); break;
-    default: hipLaunchKernelGGL(route_kernel<1>, grid, block, lds, s, xh, wh, bias, T, H, E, k,
-                                flags, idx, w); break;
+    switch (H) {
+    case 256: return launch_route_h<256>(xh, wh, bias, T, E, k, flags, idx, w, s);
+    case 512: return launch_route_h<512>(xh, wh, bias, T, E, k, flags, idx, w, s);
+    case 1024: return launch_route_h<1024>(xh, wh, bias, T, E, k, flags, idx, w, s);
+    case 2048: return launch_route_h<2048>(xh, wh, bias, T, E, k, flags, idx, w, s);
+    default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
     }
-    MOE_LAUNCH_CHECK("route_kernel");
-    return MOE_OK;
 }
 
 }  // namespace moe

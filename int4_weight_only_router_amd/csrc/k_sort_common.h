@@ -1,0 +1,192 @@
+// k_sort_common.h -- device helpers shared by the permutation kernels.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+// Stable scatter of flat elements [f0, f1) by one wave.  cnt[e] holds the
+// next free sorted position of expert e; a lane's rank among earlier lanes
+// with the same key comes from a readlane sweep, and the counter advances by
+// the group's multiplicity (LDS max of the new end positions).  Out-of-range
+// ids are skipped.
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ idx, int f0, int f1,
+                                             int E, int *cnt, int32_t *__restrict__ perm,
+                                             int32_t *__restrict__ inv_perm, int lane)
+{
+    for (int base = f0; base < f1; base += 64) {
+        const int f = base + lane;
+        int key = (f < f1) ? idx[f] : -1;
+        if ((unsigned)key >= (unsigned)E)
+            key = -1;
+        const bool valid = key >= 0;
+        int rank = 0;
+        const int nval = min(64, f1 - base);
+        for (int i = 0; i < nval; ++i) {
+            int ki = __builtin_amdgcn_readlane(key, i);
+            rank += (ki == key && i < lane) ? 1 : 0;
+        }
+        int pos = 0;
+        if (valid)
+            pos = cnt[key] + rank;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            atomicMax(&cnt[key], pos + 1);
+            perm[pos] = f;
+            inv_perm[f] = pos;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Counts, offsets and running positions of n flat elements by one wave
+// (histogram in LDS cnt[E], exclusive scan); afterwards cnt[e] = offsets[e].
+__device__ __forceinline__ void wave_count_scan(const int32_t *__restrict__ idx, int n, int E,
+                                                int *cnt, int32_t *__restrict__ counts,
+                                                int32_t *__restrict__ offsets, int lane)
+{
+    for (int e = lane; e < E; e += 64)
+        cnt[e] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int f = lane; f < n; f += 64)
+        if ((unsigned)idx[f] < (unsigned)E)
+            atomicAdd(&cnt[idx[f]], 1);
+    __builtin_amdgcn_wave_barrier();
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int seg = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E)
+            seg += cnt[e0 + i];
+    int incl = seg;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+        int o = __shfl_up(incl, st, 64);
+        if (lane >= st)
+            incl += o;
+    }
+    int run = incl - seg;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < per; ++i) {
+        int e = e0 + i;
+        if (e < E) {
+            int c = cnt[e];
+            counts[e] = c;
+            offsets[e] = run;
+            cnt[e] = run;
+            run += c;
+        }
+    }
+    if (lane == 63)
+        offsets[E] = run;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Selection order of the router: a ranks before b iff its logit is larger,
+// or equal with a lower expert index (a strict total order).
+__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb)
+{
+    return va > vb || (va == vb && ea < eb);
+}
+
+struct Cand {
+    float v;
+    int e;   // -1: empty slot
+};
+
+// Local top-k of one block of 64 experts of a token, by one wave: lane i
+// holds expert 64b+i, its rank inside the block is the number of block
+// members that rank before it (broadcast reads of the block from LDS, fully
+// unrolled), and ranks below k land in cand[0..k).  Slots past the block's
+// size are marked empty.  l must be 16-byte aligned when E % 4 == 0.
+__device__ __forceinline__ void block_topk(const float *l, int E, int k, int b, int lane,
+                                           Cand *cand)
+{
+    const int e0 = 64 * b;
+    const int e = e0 + lane;
+    const int nvalid = min(64, E - e0);
+    const bool valid = lane < nvalid;
+    const float v = valid ? l[e] : 0.0f;
+    int rank = 0;
+    if (nvalid == 64 && (E & 3) == 0) {
+#pragma unroll
+        for (int j = 0; j < 64; j += 4) {
+            const float4_t q = *reinterpret_cast<const float4_t *>(l + e0 + j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rank += ranks_before(q[i], e0 + j + i, v, e) ? 1 : 0;
+        }
+    } else {
+        for (int j = 0; j < nvalid; ++j)
+            rank += ranks_before(l[e0 + j], e0 + j, v, e) ? 1 : 0;
+    }
+    if (valid && rank < k)
+        cand[rank] = Cand{v, e};
+    if (!valid && lane < k)
+        cand[lane] = Cand{0.0f, -1};
+}
+
+// Global top-k of one token from its C block candidates, by one wave.
+// Writes the chosen (logit, expert) in order to sel[0..k).
+__device__ __forceinline__ void merge_topk(const Cand *cand, int C, int k, int lane, Cand *sel)
+{
+    for (int c = lane; c < C; c += 64) {
+        const Cand me = cand[c];
+        int rank = 0;
+        int j = 0;
+        for (; j + 8 <= C; j += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const Cand o = cand[j + i];
+                rank += (o.e >= 0 && ranks_before(o.v, o.e, me.v, me.e)) ? 1 : 0;
+            }
+        }
+        for (; j < C; ++j) {
+            const Cand o = cand[j];
+            rank += (o.e >= 0 && ranks_before(o.v, o.e, me.v, me.e)) ? 1 : 0;
+        }
+        if (me.e >= 0 && rank < k)
+            sel[rank] = me;
+    }
+}
+
+// Stable sorted position of each of n keys (flat order f) by one wave:
+// pos(f) = #{g : key_g < key_f} + #{g < f : key_g == key_f}.
+__device__ __forceinline__ void wave_stable_positions(const int *keys, int n, int32_t *perm,
+                                                      int32_t *inv_perm, int lane)
+{
+    for (int f = lane; f < n; f += 64) {
+        const int key = keys[f];
+        int pos = 0;
+        for (int g = 0; g < n; ++g) {
+            const int kg = keys[g];
+            pos += (kg < key || (kg == key && g < f)) ? 1 : 0;
+        }
+        perm[pos] = f;
+        inv_perm[f] = pos;
+    }
+}
+
+// Counting sort of n small keys (n <= 128) by one wave, without atomics:
+// counts[e] = #{g : key_g == e}, offsets[e] = #{g : key_g < e}, positions as
+// in wave_stable_positions.
+__device__ __forceinline__ void wave_small_sort(const int *keys, int n, int E,
+                                                int32_t *counts, int32_t *offsets,
+                                                int32_t *perm, int32_t *inv_perm, int lane)
+{
+    for (int e = lane; e < E; e += 64) {
+        int lt = 0, eq = 0;
+        for (int g = 0; g < n; ++g) {
+            const int kg = keys[g];
+            lt += kg < e ? 1 : 0;
+            eq += kg == e ? 1 : 0;
+        }
+        offsets[e] = lt;
+        counts[e] = eq;
+    }
+    if (lane == 0)
+        offsets[E] = n;
+    wave_stable_positions(keys, n, perm, inv_perm, lane);
+}
+
+}  // namespace moe

@@ -28,6 +28,10 @@ void clear_error() { g_err.clear(); }
 int launch_route(const void *, const void *, const float *, int, int, int, int, unsigned,
                  int32_t *, float *, hipStream_t);
 size_t permute_ws_bytes(int T, int k, int E);
+size_t route_split_ws_bytes(int T, int E);
+int launch_route_split(const void *, const void *, const float *, int, int, int, int, unsigned,
+                       int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *, void *,
+                       hipStream_t);
 int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
                    void *, hipStream_t);
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *, int,
@@ -46,6 +50,7 @@ int launch_quantize(const float *, const float *, const float *, int, int, int, 
 int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
+constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
 constexpr int SHARED_GEMV_MAX_T = 4;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
@@ -149,23 +154,69 @@ int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *ds
     return prepack_common("moe_unpack_experts", src, n, H, I, group, dst, 1, stream);
 }
 
+static int check_route_args(const char *fn, const void *x_f16, const void *w_router_f16, int T,
+                            int H, int E, int k, unsigned flags, const int32_t *topk_idx,
+                            const float *topk_w)
+{
+    int rc = check_route_shape(fn, T, E, k);
+    if (rc)
+        return rc;
+    if (T > 0 && (!x_f16 || !w_router_f16 || !topk_idx || !topk_w))
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    if (H <= 0 || H % 8)
+        return set_error(MOE_EINVAL, "%s: H=%d must be a positive multiple of 8", fn, H);
+    if (!h_supported(H))
+        return set_error(MOE_EUNSUPPORTED, "%s: H=%d not in {256, 512, 1024, 2048}", fn, H);
+    if (flags & ~(unsigned)MOE_RENORM)
+        return set_error(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    return MOE_OK;
+}
+
 int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T, int H,
               int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w, hipStream_t stream)
 {
     clear_error();
-    int rc = check_route_shape("moe_route", T, E, k);
+    int rc = check_route_args("moe_route", x_f16, w_router_f16, T, H, E, k, flags, topk_idx,
+                              topk_w);
     if (rc)
         return rc;
-    if (T > 0 && (!x_f16 || !w_router_f16 || !topk_idx || !topk_w))
-        return set_error(MOE_EINVAL, "moe_route: null pointer");
-    if (H <= 0 || H % 8)
-        return set_error(MOE_EINVAL, "moe_route: H=%d must be a positive multiple of 8", H);
-    if (H > 8192)
-        return set_error(MOE_EUNSUPPORTED, "moe_route: H=%d > 8192", H);
-    if (flags & ~(unsigned)MOE_RENORM)
-        return set_error(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
     return launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
                         stream);
+}
+
+size_t moe_route_permute_workspace_bytes(int T, int k, int E)
+{
+    if (T < 0 || k <= 0 || E <= 0)
+        return 0;
+    if (T > 0 && T <= ROUTE_FUSED_MAX_T)
+        return route_split_ws_bytes(T, E);
+    return permute_ws_bytes(T, k, E);
+}
+
+int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T,
+                      int H, int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w,
+                      int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_route_args("moe_route_permute", x_f16, w_router_f16, T, H, E, k, flags,
+                              topk_idx, topk_w);
+    if (rc)
+        return rc;
+    if (!counts || !offsets || (T > 0 && (!perm || !inv_perm)))
+        return set_error(MOE_EINVAL, "moe_route_permute: null pointer");
+    const size_t need = moe_route_permute_workspace_bytes(T, k, E);
+    if (need && (!ws || ws_bytes < need))
+        return set_error(MOE_ENOMEM, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes,
+                         need);
+    if (T > 0 && T <= ROUTE_FUSED_MAX_T)
+        return launch_route_split(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
+                                  topk_w, counts, offsets, perm, inv_perm, ws, stream);
+    rc = launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
+                      stream);
+    if (rc)
+        return rc;
+    return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws, stream);
 }
 
 size_t moe_permute_workspace_bytes(int T, int k, int E)

@@ -81,7 +81,10 @@ class MoELayer:
         d = self.device
         r, ydt, ysl, ffn_ws = A.moe_expert_ffn_plan(T, self.H, self.I, self.E, self.k, self.g,
                                                     regime)
-        pws = A.moe_permute_workspace_bytes(T, self.k, self.E)
+        # route/permute scratch; zero-filled once (the fused router keeps an
+        # atomic ticket in it)
+        pws = max(A.moe_permute_workspace_bytes(T, self.k, self.E),
+                  A.moe_route_permute_workspace_bytes(T, self.k, self.E))
         n = T * self.k
         ytype = torch.float32 if ydt == A.MOE_DTYPE_F32 else torch.float16
         sh_out = sh_ws = None
@@ -98,19 +101,25 @@ class MoELayer:
             offsets=torch.empty(self.E + 1, dtype=torch.int32, device=d),
             perm=torch.empty(max(n, 1), dtype=torch.int32, device=d),
             inv_perm=torch.empty(max(n, 1), dtype=torch.int32, device=d),
-            perm_ws=torch.empty(pws, dtype=torch.uint8, device=d) if pws else None,
+            perm_ws=torch.zeros(pws, dtype=torch.uint8, device=d) if pws else None,
             y=torch.empty((ysl, max(n, 1), self.H), dtype=ytype, device=d),
             ffn_ws=torch.empty(ffn_ws, dtype=torch.uint8, device=d) if ffn_ws else None,
             shared_out=sh_out, shared_ws=sh_ws,
             out=torch.empty((T, self.H), dtype=torch.float16, device=d),
         )
 
-    def route_permute(self, x, b: LayerBuffers, stream=None):
+    def route_permute(self, x, b: LayerBuffers, stream=None, fused=True):
         T = b.T
+        nws = 0 if b.perm_ws is None else b.perm_ws.numel()
+        if fused:
+            A.moe_route_permute(x, self.router, self.bias, T, self.H, self.E, self.k,
+                                self.flags, b.topk_idx, b.topk_w, b.counts, b.offsets, b.perm,
+                                b.inv_perm, b.perm_ws, nws, stream)
+            return
         A.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.flags,
                     b.topk_idx, b.topk_w, stream)
         A.moe_permute(b.topk_idx, T, self.k, self.E, b.counts, b.offsets, b.perm, b.inv_perm,
-                      b.perm_ws, 0 if b.perm_ws is None else b.perm_ws.numel(), stream)
+                      b.perm_ws, nws, stream)
 
     def experts(self, x, b: LayerBuffers, table=None, stream=None):
         A.moe_expert_ffn_w4a16(x, b.perm, b.offsets, self.table if table is None else table,

@@ -121,6 +121,38 @@ def test_route_bit_exact(cfg, T, renorm):
     assert np.max(np.abs(w[toks] - ow)) <= WTOL
 
 
+@pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 3),
+                                   (MI.OLMOE_DECODE, 8), (MI.OLMOE_DECODE, 9), (MI.E512, 1),
+                                   (MI.E512, 5), (MI.TINY, 16), (MI.E512, 70)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_route_permute_fused_bit_exact(cfg, T):
+    say("route_permute %s T=%d" % (cfg.name, T))
+    x = MI.gen_x(cfg, T, step=7)
+    wr = MI.gen_router(cfg)
+    b = MI.zipf_bias(cfg)
+    n = T * cfg.k
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device=DEV)
+    counts = torch.full((cfg.E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((cfg.E + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    wsb = M.moe_route_permute_workspace_bytes(T, cfg.k, cfg.E)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    for rep in range(2):   # the workspace is reusable: the second call must agree
+      M.moe_route_permute(f16(x), f16(wr), None if b is None else torch.from_numpy(b).to(DEV),
+                          T, cfg.H, cfg.E, cfg.k, 0, idx, w, counts, offsets, perm, inv, ws, wsb)
+      torch.cuda.synchronize()
+      oi, ow, _ = O.route(x, wr, b, cfg.k)
+      assert np.array_equal(_np(idx), oi)
+      assert np.max(np.abs(_np(w) - ow)) <= WTOL
+      for got, ref, name in zip((counts, offsets, perm, inv), O.permute(oi, cfg.E),
+                                ("counts", "offsets", "perm", "inv_perm")):
+          assert np.array_equal(_np(got), ref), name
+      if T <= 8:
+          assert int(_np(ws[:4].view(torch.int32))[0]) == 0   # ticket back at zero
+
+
 def test_route_ties_go_to_lower_index():
     cfg = MI.OLMOE_DECODE
     say("route ties")
