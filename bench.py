@@ -102,6 +102,39 @@ def cpu_baseline_decode(cfg, layers, steps):
 
 # ------------------------------------------------------------------ decode
 
+def _graph_time(torch, fn, reps):
+    """Average duration of one call of fn (a sequence of launches on the
+    current stream), captured once in a graph and replayed `reps` times
+    between two events: launches run back to back, as in the timed loop."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _profile_traffic(kernel_src, key):
+    """HBM bytes per launch measured by rocprofv3 counters and recorded under
+    profiles/, if the kernel source has not changed since (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+        src = open(os.path.join(ROOT, kernel_src), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def run_decode(args, torch, M):
     import numpy as np
     import moe_inputs as MI
@@ -111,50 +144,34 @@ def run_decode(args, torch, M):
     lays, blob_bytes = build_layers(cfg, L, dev, torch, M)
     K, W = args.steps, args.warmup
     xs = torch.from_numpy(np.concatenate([MI.gen_x(cfg, 1, step=s) for s in range(K + W)])).to(dev)
-    bufs = lays[0].buffers(1)
-    assert bufs.regime == M.MOE_REGIME_DECODE
+    bufs = [lay.buffers(1) for lay in lays]
+    assert bufs[0].regime == M.MOE_REGIME_DECODE
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
-    stream = torch.cuda.current_stream()
 
-    def step(s, ev=None):
-        x = xs[s:s + 1]
+    def step_from(x):
         for l, lay in enumerate(lays):
             out = act[l & 1]
-            if ev is not None:
-                ev[l][0].record(stream)
-            lay.route_permute(x, bufs)
-            if ev is not None:
-                ev[l][1].record(stream)
-            lay.experts(x, bufs)
-            if ev is not None:
-                ev[l][2].record(stream)
-            lay.combine(bufs, residual=x, out=out)
-            if ev is not None:
-                ev[l][3].record(stream)
+            lay.route_permute(x, bufs[l])
+            lay.experts(x, bufs[l])
+            lay.combine(bufs[l], residual=x, out=out)
             x = out
         return x
 
     log("warmup %d steps" % W)
     for s in range(W):
-        step(s)
+        step_from(xs[s:s + 1])
     torch.cuda.synchronize()
 
     graph = None
     if args.graph:
-        # one captured step reading x0 from a fixed buffer; its input is
-        # refreshed by a device copy inside the same graph
+        # one captured step reading x0 from a fixed buffer, refreshed by a
+        # device copy inside the same graph
         xin = torch.empty((1, cfg.H), dtype=torch.float16, device=dev)
         sel = torch.zeros(1, dtype=torch.int64, device=dev)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             xin.copy_(xs.index_select(0, sel))
-            x = xin
-            for l, lay in enumerate(lays):
-                out = act[l & 1]
-                lay.route_permute(x, bufs)
-                lay.experts(x, bufs)
-                lay.combine(bufs, residual=x, out=out)
-                x = out
+            step_from(xin)
         graph = (g, sel)
         for s in range(3):
             sel.fill_(s)
@@ -171,26 +188,27 @@ def run_decode(args, torch, M):
             g.replay()
     else:
         for s in range(W, W + K):
-            step(s)
+            step_from(xs[s:s + 1])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # per-kernel durations with events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
-    ffn_ms, route_ms, comb_ms = [], [], []
-    for s in range(W, W + K):
-        step(s, ev)
-        torch.cuda.synchronize()
-        for l in range(L):
-            route_ms.append(ev[l][0].elapsed_time(ev[l][1]))
-            ffn_ms.append(ev[l][1].elapsed_time(ev[l][2]))
-            comb_ms.append(ev[l][2].elapsed_time(ev[l][3]))
-    ffn_avg = float(np.mean(ffn_ms))
-    counts = bufs.counts.cpu().numpy()
-    touched = int((counts > 0).sum())
-    ffn_bytes = touched * blob_bytes + cfg.H * 2          # INT4 + scales of routed experts, x
-    achieved = ffn_bytes / (ffn_avg * 1e-3) / 1e9
+    # per-kernel launch durations (HIP events on the launch stream): each
+    # layer's kernel once per replay, all 16 layers in turn (415 MB of
+    # expert weights per pass, more than the 256 MB Infinity Cache)
+    reps = max(4, K // 8)
+    x0 = xs[0:1]
+    t_route = _graph_time(torch, lambda: [lay.route_permute(x0, bufs[l])
+                                          for l, lay in enumerate(lays)], reps) / L
+    t_ffn = _graph_time(torch, lambda: [lay.experts(x0, bufs[l])
+                                        for l, lay in enumerate(lays)], reps) / L
+    t_comb = _graph_time(torch, lambda: [lay.combine(bufs[l], residual=x0, out=act[0])
+                                         for l, lay in enumerate(lays)], reps) / L
+    touched = [int((b.counts.cpu().numpy() > 0).sum()) for b in bufs]
+    ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
+    achieved = ffn_bytes / (t_ffn * 1e-3) / 1e9
     ms_step = elapsed * 1e3 / K
+    traffic = _profile_traffic("int4_weight_only_router_amd/csrc/k_ffn_decode.hip",
+                               "ffn_decode_kernel olmoe_decode")
     res = {
         "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (batched), W4A16",
         "value": round(K / elapsed, 2),
@@ -205,15 +223,15 @@ def run_decode(args, torch, M):
                                "1 token/step, all experts resident",
                    "layers": L, "tokens_per_step": 1, "graph": bool(graph)},
         "layer_tokens_per_s": round(K * L / elapsed, 1),
-        "per_layer_us": {"route+permute": round(float(np.mean(route_ms)) * 1e3, 2),
-                         "expert_ffn": round(ffn_avg * 1e3, 2),
-                         "combine": round(float(np.mean(comb_ms)) * 1e3, 2)},
+        "per_layer_us": {"route+permute": round(t_route * 1e3, 2),
+                         "expert_ffn": round(t_ffn * 1e3, 2),
+                         "combine": round(t_comb * 1e3, 2)},
         "roofline": {"kernel": "ffn_decode_kernel (moe_expert_ffn_w4a16, DECODE)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
                      "alg_bytes_per_launch": ffn_bytes,
-                     "avg_launch_us": round(ffn_avg * 1e3, 3)},
+                     "avg_launch_us": round(t_ffn * 1e3, 3)},
     }
     if args.cpu_baseline:
         log("cpu baseline (oracle, 1 thread)")
@@ -267,12 +285,35 @@ def run_batched(args, torch, M):
     return {"workload": "olmoe_batched", "results": lines}
 
 
+def run_copy(args, torch, M):
+    """A plain device-to-device copy of known size: the reference for scaling
+    the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(args.steps):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    return {"workload": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+            "median_ms": round(med, 4), "GBs_read_plus_write": round(2 * nbytes / med / 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", choices=["decode", "batched"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "batched", "copy"], default="decode")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
@@ -290,8 +331,10 @@ def main():
     M.lib()
     if args.workload == "decode":
         res = run_decode(args, torch, M)
-    else:
+    elif args.workload == "batched":
         res = run_batched(args, torch, M)
+    else:
+        res = run_copy(args, torch, M)
     print(json.dumps(res), flush=True)
 
 
