@@ -7,11 +7,15 @@ scales, all experts resident in HBM), one token per step, fresh x0 ~ N(0,1)
 per step, x_{l+1} = fp16(x_l + MoE_l(x_l)).  A step is route -> permute ->
 routed expert FFN -> combine for all 16 layers.  Prints one JSON line.
 
-    python bench.py [--steps 128] [--warmup 16] [--workload decode|batched]
-                    [--graph/--no-graph] [--no-cpu-baseline]
+    python bench.py [--steps 128] [--warmup 16] [--graph/--no-graph]
+                    [--no-cpu-baseline] [--workload decode|batched|partial|copy]
 
-The batched workload times single OLMoE-shaped layers at T = 64, 512, 4096
-(grouped INT4 -> LDS -> FP16 MFMA path) and reports MFMA utilisation.
+Other workloads (one JSON line each, not the headline):
+  batched  single OLMoE-shaped layers at T = 64, 512, 4096 (grouped INT4 ->
+           LDS -> FP16 MFMA path): MFMA and HBM fractions.
+  partial  16 layers with 30 of 64 experts per layer in an HBM slot pool and
+           the INT4 source in pinned host memory: tokens/s and H2D GiB.
+  copy     a 1 GiB device copy, the reference for HBM byte counters.
 """
 from __future__ import annotations
 
@@ -285,6 +289,116 @@ def run_batched(args, torch, M):
     return {"workload": "olmoe_batched", "results": lines}
 
 
+def run_partial(args, torch, M):
+    """Partial residency: 16 OLMoE-shaped layers, C of 64 experts per layer
+    resident in HBM slots (+ S spares), the full INT4 source in pinned host
+    memory; per token and layer: route (GPU) -> routed ids to the host ->
+    moe_pool_prepare (misses copied H2D on a side stream) -> expert FFN
+    through the published table -> retire -> combine.  Protocol: `blocks`
+    fresh pools, each a 64-token warmup then `prompts` x `tokens` tokens."""
+    import numpy as np
+    import moe_inputs as MI
+    import oracle as O
+    cfg = MI.PARTIAL
+    dev = "cuda:0"
+    L = cfg.layers
+    lays, blob_bytes = build_layers(cfg, L, dev, torch, M)
+    src = torch.empty((L, cfg.E, blob_bytes), dtype=torch.uint8, pin_memory=True)
+    for l, lay in enumerate(lays):
+        src[l].copy_(lay._blobs)
+        lay._blobs = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ptrs = [src[l, e].data_ptr() for l in range(L) for e in range(cfg.E)]
+    pc = M.PoolConfig(layers=L, experts=cfg.E, topk=cfg.k, capacity=cfg.capacity,
+                      spares=cfg.spares, decay_shift=args.decay_shift, expert_bytes=blob_bytes)
+    pool = M.moe_pool_create(pc, ptrs)
+    bufs = [lay.buffers(1) for lay in lays]
+    act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
+    host_ids = torch.empty(cfg.k, dtype=torch.int32, pin_memory=True)
+    ev = torch.cuda.Event()
+    stream = torch.cuda.current_stream()
+    trace_layers, trace_ids = [], []
+
+    def token(x0, record):
+        x = x0
+        misses = 0
+        for l, lay in enumerate(lays):
+            b = bufs[l]
+            lay.route_permute(x, b)
+            host_ids.copy_(b.topk_idx.view(-1), non_blocking=True)
+            ev.record(stream)
+            ev.synchronize()
+            ids = host_ids.numpy()
+            tab, st = M.moe_pool_prepare(pool, l, ids, cfg.k, stream)
+            misses += st.misses
+            if record:
+                trace_layers.append(l)
+                trace_ids.append(ids.copy())
+            lay.experts(x, b, table=tab)
+            M.moe_pool_retire(pool, l, stream)
+            out = act[l & 1]
+            lay.combine(b, residual=x, out=out)
+            x = out
+        return misses
+
+    blocks = []
+    try:
+        for blk in range(args.blocks):
+            M.moe_pool_reset(pool)
+            for i in range(cfg.warmup_tokens):
+                token(torch.from_numpy(MI.gen_prompt_token(cfg, -1, i)).to(dev), blk == 0)
+            torch.cuda.synchronize()
+            base = M.moe_pool_stats(pool)
+            x0s = [[torch.from_numpy(MI.gen_prompt_token(cfg, p, i)).to(dev)
+                    for i in range(args.tokens)] for p in range(args.prompts)]
+            busy = 0.0
+            ntok = 0
+            for p in range(args.prompts):
+                token(x0s[p][0], blk == 0)            # first token: outside the rate
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(1, args.tokens):
+                    token(x0s[p][i], blk == 0)
+                torch.cuda.synchronize()
+                busy += time.perf_counter() - t0
+                ntok += args.tokens - 1
+            st = M.moe_pool_stats(pool)
+            blocks.append({"tokens_per_s": ntok / busy,
+                           "h2d_bytes": st.h2d_bytes - base.h2d_bytes,
+                           "hits": st.hits - base.hits, "misses": st.misses - base.misses})
+            log("block %d: %.1f tokens/s, %.2f GiB H2D" % (
+                blk, blocks[-1]["tokens_per_s"], blocks[-1]["h2d_bytes"] / 2 ** 30))
+    finally:
+        M.moe_pool_destroy(pool)
+    # the policy replayed by the oracle's simulator on the recorded first
+    # block (warmup included) gives the same misses
+    tl = np.array(trace_layers, np.int32)
+    ti = np.array(trace_ids, np.int32)
+    _, sim_m, _, _ = O.pool_sim(L, cfg.E, cfg.capacity, args.decay_shift, cfg.k, tl, ti)
+    nw = cfg.warmup_tokens * L
+    sim_measured = int(sim_m[nw:].sum())
+    rates = [b["tokens_per_s"] for b in blocks]
+    tot_tok = args.blocks * args.prompts * (args.tokens - 1)
+    tot_time = sum(args.prompts * (args.tokens - 1) / r for r in rates)
+    h2d = sum(b["h2d_bytes"] for b in blocks)
+    hits = sum(b["hits"] for b in blocks)
+    misses = sum(b["misses"] for b in blocks)
+    return {
+        "workload": "olmoe_partial: 16 layers, %d of 64 experts resident + %d spares per layer, "
+                    "Zipf(1.0) router bias, %d blocks x (64 warmup + %d prompts x %d tokens)"
+                    % (cfg.capacity, cfg.spares, args.blocks, args.prompts, args.tokens),
+        "decode_tokens_per_s_pooled": round(tot_tok / tot_time, 2),
+        "block_tokens_per_s": [round(r, 2) for r in rates],
+        "block_spread": round((max(rates) - min(rates)) / max(rates), 4),
+        "h2d_GiB_measured": round(h2d / 2 ** 30, 3),
+        "hit_rate": round(hits / max(1, hits + misses), 4),
+        "misses_per_token": round(misses / (args.blocks * args.prompts * args.tokens), 3),
+        "simulator_misses_block0": sim_measured, "pool_misses_block0": blocks[0]["misses"],
+        "decay_shift": args.decay_shift,
+    }
+
+
 def run_copy(args, torch, M):
     """A plain device-to-device copy of known size: the reference for scaling
     the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
@@ -313,7 +427,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", choices=["decode", "batched", "copy"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "batched", "partial", "copy"],
+                    default="decode")
+    ap.add_argument("--blocks", type=int, default=3)
+    ap.add_argument("--prompts", type=int, default=12)
+    ap.add_argument("--tokens", type=int, default=128)
+    ap.add_argument("--decay-shift", type=int, default=3)
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
@@ -333,6 +452,8 @@ def main():
         res = run_decode(args, torch, M)
     elif args.workload == "batched":
         res = run_batched(args, torch, M)
+    elif args.workload == "partial":
+        res = run_partial(args, torch, M)
     else:
         res = run_copy(args, torch, M)
     print(json.dumps(res), flush=True)

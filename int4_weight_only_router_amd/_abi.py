@@ -93,9 +93,17 @@ def _declare(L):
 
 
 def lib(path: str | None = None):
-    """Load (building in-tree first if absent) libmoe_w4a16.so."""
+    """Load (building in-tree first if absent) libmoe_w4a16.so.
+
+    torch is imported first: its wheel carries its own HIP runtime under the
+    same soname, and loading torch first makes this library bind to that one
+    copy instead of pulling in a second runtime."""
     global _lib
     if _lib is None:
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         path = path or _build.LIB
         if not os.path.exists(path):
             _build.build()
