@@ -8,11 +8,13 @@ per step, x_{l+1} = fp16(x_l + MoE_l(x_l)).  A step is route -> permute ->
 routed expert FFN -> combine for all 16 layers.  Prints one JSON line.
 
     python bench.py [--steps 128] [--warmup 16] [--graph/--no-graph]
-                    [--no-cpu-baseline] [--workload decode|batched|partial|copy]
+                    [--no-cpu-baseline] [--workload decode|batched|e512|partial|copy] [--T ...]
 
 Other workloads (one JSON line each, not the headline):
-  batched  single OLMoE-shaped layers at T = 64, 512, 4096 (grouped INT4 ->
-           LDS -> FP16 MFMA path): MFMA and HBM fractions.
+  batched  single OLMoE-shaped layers at T = 64, 512, 4096 (grouped INT4
+           FP16-MFMA path): per-call times, MFMA and HBM fractions.
+  e512     single 512-expert layers (top-10, I = 512, FP16 shared expert with
+           I_s = 512, Zipf(1.1) router bias) at T = 1, 256, 4096.
   partial  16 layers with 30 of 64 experts per layer in an HBM slot pool and
            the INT4 source in pinned host memory: tokens/s and H2D GiB.
   copy     a 1 GiB device copy, the reference for HBM byte counters.
@@ -250,43 +252,74 @@ def run_decode(args, torch, M):
 
 # ----------------------------------------------------------------- batched
 
-def run_batched(args, torch, M):
+def run_batched(args, torch, M, cfg):
+    """Single layers of `cfg` at each batch size: median per-call times of
+    route+permute, routed expert FFN, shared expert and combine (HIP events
+    around each call on the current stream), with the MFMA fraction of the
+    routed FFN (routed FLOPs only) and the HBM fraction of the whole layer
+    (algorithmic bytes: touched expert blobs, router, shared weights, x, out)."""
     import numpy as np
     import moe_inputs as MI
-    cfg = MI.OLMOE_BATCHED
     dev = "cuda:0"
     lays, blob_bytes = build_layers(cfg, 1, dev, torch, M)
     lay = lays[0]
+    if cfg.Is:
+        lay.shared = tuple(torch.from_numpy(w).to(dev) for w in MI.gen_shared(cfg))
+    Ts = [int(t) for t in args.T.split(",")] if args.T else list(cfg.T)
     lines = []
-    for T in cfg.T:
+    for T in Ts:
         x = torch.from_numpy(MI.gen_x(cfg, T)).to(dev)
         b = lay.buffers(T)
         for _ in range(args.warmup):
             lay.forward(x, b)
         torch.cuda.synchronize()
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        ffn, tot = [], []
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        parts = {"route_permute": [], "expert_ffn": [], "shared": [], "combine": [], "layer": []}
+        ffn_ws = 0 if b.ffn_ws is None else b.ffn_ws.numel()
         for _ in range(args.steps):
+            ev[0].record()
             lay.route_permute(x, b)
-            e0.record()
-            lay.experts(x, b)
-            e1.record()
+            ev[1].record()
+            M.moe_expert_ffn_w4a16(x, b.perm, b.offsets, lay.table, T, cfg.H, cfg.I, cfg.E,
+                                   cfg.k, cfg.g, b.regime, b.y, b.y_dtype, b.y_slices, b.ffn_ws,
+                                   ffn_ws)
+            ev[2].record()
+            if lay.shared is not None:
+                wg, wu, wd = lay.shared
+                M.moe_shared_ffn_f16(x, wg, wu, wd, T, cfg.H, cfg.Is, b.shared_out, b.shared_ws,
+                                     b.shared_ws.numel())
+            ev[3].record()
             lay.combine(b)
-            e2.record()
+            ev[4].record()
             torch.cuda.synchronize()
-            ffn.append(e0.elapsed_time(e1))
-            tot.append(e1.elapsed_time(e2))
-        ffn_ms = float(np.median(ffn))
-        flops = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I
+            parts["route_permute"].append(ev[0].elapsed_time(ev[1]))
+            parts["expert_ffn"].append(ev[1].elapsed_time(ev[2]))
+            parts["shared"].append(ev[2].elapsed_time(ev[3]))
+            parts["combine"].append(ev[3].elapsed_time(ev[4]))
+            parts["layer"].append(ev[0].elapsed_time(ev[4]))
+        us = {k: float(np.median(v)) * 1e3 for k, v in parts.items()}
         counts = b.counts.cpu().numpy()
         touched = int((counts > 0).sum())
-        tflops = flops / (ffn_ms * 1e-3) / 1e12
-        gbs = touched * blob_bytes / (ffn_ms * 1e-3) / 1e9
-        lines.append({"T": T, "expert_ffn_us": round(ffn_ms * 1e3, 1),
-                      "tflops": round(tflops, 1), "mfma_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                      "weight_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-        log(str(lines[-1]))
-    return {"workload": "olmoe_batched", "results": lines}
+        f_routed = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I
+        f_shared = 2.0 * T * 3 * cfg.H * cfg.Is
+        f_router = 2.0 * T * cfg.E * cfg.H
+        b_alg = (touched * blob_bytes + cfg.E * cfg.H * 2 + 3 * cfg.H * cfg.Is * 2
+                 + 2 * T * cfg.H * 2)
+        tf = f_routed / (us["expert_ffn"] * 1e-6) / 1e12
+        line = {"T": T, "experts_touched": touched, "max_rows_per_expert": int(counts.max()),
+                "us": {k: round(v, 1) for k, v in us.items()},
+                "routed_tflops": round(tf, 1), "routed_mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                "layer_tflops": round((f_routed + f_shared + f_router) / (us["layer"] * 1e-6) / 1e12, 1),
+                "layer_alg_GB": round(b_alg / 1e9, 4),
+                "layer_hbm_frac": round(b_alg / (us["layer"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if cfg.Is:
+            tfs = f_shared / (us["shared"] * 1e-6) / 1e12
+            line["shared_tflops"] = round(tfs, 1)
+        lines.append(line)
+        log(str(line))
+    return {"workload": cfg.name, "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                                             "g": cfg.g, "Is": cfg.Is, "zipf_s": cfg.zipf_s},
+            "results": lines}
 
 
 def run_partial(args, torch, M):
@@ -427,8 +460,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", choices=["decode", "batched", "partial", "copy"],
+    ap.add_argument("--workload", choices=["decode", "batched", "e512", "partial", "copy"],
                     default="decode")
+    ap.add_argument("--T", default="", help="batched/e512: comma-separated batch sizes")
     ap.add_argument("--blocks", type=int, default=3)
     ap.add_argument("--prompts", type=int, default=12)
     ap.add_argument("--tokens", type=int, default=128)
@@ -450,8 +484,10 @@ def main():
     M.lib()
     if args.workload == "decode":
         res = run_decode(args, torch, M)
-    elif args.workload == "batched":
-        res = run_batched(args, torch, M)
+    elif args.workload in ("batched", "e512"):
+        import moe_inputs as MI
+        res = run_batched(args, torch, M, MI.OLMOE_BATCHED if args.workload == "batched"
+                          else MI.E512)
     elif args.workload == "partial":
         res = run_partial(args, torch, M)
     else:

@@ -104,7 +104,9 @@ int moe_quantize_experts(const float *wg, const float *wu, const float *wd,
  * Device layout: gate and up rows fused into 64-row blocks (32 gate rows then
  * the 32 up rows of the same intermediate indices), down in 64-row blocks;
  * inside a block, 32-element input chunks of all 64 rows are contiguous
- * (16 bytes per row, nibbles interleaved for in-register conversion);
+ * (16 bytes per row: four dwords holding elements 0-7, 16-23, 8-15, 24-31,
+ * each with element 2i at bits 4i and element 2i+1 at bits 16+4i, so that
+ * a nibble pair converts in registers with one mask);
  * scales in [block][group][64 rows] order.
  */
 int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *dst,
@@ -127,14 +129,20 @@ int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *ds
  *                 index asc) -- ties go to the lower expert index
  *   topk_w:       device fp32 [T][k] (output), softmax over all E logits at
  *                 the chosen experts
+ *   ws:           device scratch of moe_route_workspace_bytes(T, E) bytes
+ *                 (0 for T <= 8, where ws may be NULL; above that it holds the
+ *                 T x E fp32 logits between the logit and top-k launches;
+ *                 contents need no initialisation); MOE_ENOMEM if too small
  * Logits are fp32 in a fixed summation order (chunks of 8 elements of H go
  * to partial (chunk mod 64) in increasing order, partials combined by an xor
  * butterfly 32,16,8,4,2,1), so the indices are reproducible bit for bit.
  * T = 0 is a no-op.
  */
+size_t moe_route_workspace_bytes(int T, int E);
 int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bias,
               int T, int H, int E, int k, unsigned flags,
-              int32_t *topk_idx, float *topk_w, hipStream_t stream);
+              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              hipStream_t stream);
 
 /* ------------------------------------------------------- permutation */
 /*
@@ -159,7 +167,8 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
  * logits are spread over many workgroups, and the workgroup that finishes
  * last (an atomic ticket in ws; no workgroup ever waits for another) does the
  * top-k, the softmax and the stable sort -- the decode path's one launch
- * instead of two.  For larger T it issues the two separate launches.
+ * instead of two.  For larger T it runs moe_route's launches (logits into ws,
+ * then top-k) followed by moe_permute's, on the same ws.
  * ws: device scratch of moe_route_permute_workspace_bytes(T, k, E) bytes.  It
  * must be zero-filled before its first use by this function; every completed
  * call leaves it reusable (the ticket back at zero).  Calls that share one

@@ -11,10 +11,10 @@ __all__ = [
     "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
     "MOE_REGIME_BATCHED", "MOE_DTYPE_F16", "MOE_DTYPE_F32", "EXPORTS",
     "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
-    "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_route_permute_workspace_bytes", "moe_route_permute", "moe_expert_ffn_plan",
-    "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes", "moe_shared_ffn_f16",
-    "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
+    "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
+    "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
+    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
+    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
     "moe_pool_prepare", "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
 ]
@@ -28,10 +28,10 @@ MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
 # every symbol include/moe_w4a16.h declares
 EXPORTS = [
     "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
-    "moe_unpack_experts", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_route_permute_workspace_bytes", "moe_route_permute", "moe_expert_ffn_plan",
-    "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes", "moe_shared_ffn_f16",
-    "moe_combine", "moe_pool_create", "moe_pool_prepare",
+    "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
+    "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
+    "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
+    "moe_shared_ffn_f16", "moe_combine", "moe_pool_create", "moe_pool_prepare",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
 ]
 
@@ -67,7 +67,8 @@ def _declare(L):
         "moe_quantize_experts": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_prepack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
         "moe_unpack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
-        "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp]),
+        "moe_route_workspace_bytes": (sz, [i32, i32]),
+        "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp, sz, vp]),
         "moe_permute_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "moe_route_permute_workspace_bytes": (sz, [i32, i32, i32]),
@@ -162,9 +163,14 @@ def moe_unpack_experts(src, n, H, I, group, dst, stream=None):
     return _check(lib().moe_unpack_experts(_p(src), n, H, I, group, _p(dst), _s(stream)))
 
 
-def moe_route(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk_w, stream=None):
+def moe_route_workspace_bytes(T, E):
+    return lib().moe_route_workspace_bytes(T, E)
+
+
+def moe_route(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk_w, ws=None, ws_bytes=0,
+              stream=None):
     return _check(lib().moe_route(_p(x), _p(w_router), _p(logit_bias), T, H, E, k, flags,
-                                  _p(topk_idx), _p(topk_w), _s(stream)))
+                                  _p(topk_idx), _p(topk_w), _p(ws), ws_bytes, _s(stream)))
 
 
 def moe_permute_workspace_bytes(T, k, E):

@@ -70,7 +70,8 @@ constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are stage
 __device__ __forceinline__ float dot_chunk(uint4_t w, const half2_t *xp, float d)
 {
     const uint32_t M = 0x64006400u;
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // device chunk words hold elements 0-7, 16-23, 8-15, 24-31 in that order
+    const uint32_t ws[4] = {w.x, w.z, w.y, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t v = ws[j], v8 = ws[j] >> 8;

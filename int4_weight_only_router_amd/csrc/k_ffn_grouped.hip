@@ -5,15 +5,25 @@
 // compact experts computed in groups) and "08": compact INT4 weights with FP16
 // scales are converted inside the kernel, FP16 activations, FP32 accumulation.
 // With many tokens per expert the expert FFN is a dense contraction, so it
-// runs on the matrix cores: each K-step an INT4 tile of the weights is read
-// from HBM (16-byte loads of the device layout), converted in registers to
-// fp16 (q * s, one rounding), and written to LDS; the gathered activation rows
-// are staged in LDS beside it; four waves multiply 64x64 sub-tiles with
-// v_mfma_f32_32x32x16_f16.  The expanded tile lives only in LDS.
+// runs on the matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// Work list: (expert, 128-row tile of that expert's sorted rows) x (128
-// output columns).  The grid's y extent is an upper bound on the number of
-// row tiles; each workgroup finds its (expert, tile) from the offsets.
+// Work item: (row tile of 32*MF sorted rows of one expert) x (256 output
+// columns = four 64-row blocks of the weight matrix).  The workgroup's four
+// waves share the activation tile, staged in LDS 64 K at a time (double
+// buffered); wave w owns weight block 4*nt + w and computes its 32*MF x 64
+// output tile.  The weights never pass through LDS: in the device layout the
+// 8 nibbles one MFMA lane needs for one 16-K step (8 consecutive K of one
+// weight row) sit in one dword, and bytes 0-7 / 8-15 of a 16-byte chunk word
+// are the two lane halves' K slices for two consecutive steps, so a lane
+// fetches its B operand with one 8-byte load per 32-K chunk and converts it
+// in registers to fp16(q*s) (one rounding).  Loads of step k+1 (activations
+// and weights) are in flight while step k computes.
+//
+// Scheduling: the grid is persistent (as many workgroups as fit at once).
+// Workgroups are dealt to the 8 XCDs round-robin by id, so workgroup i works
+// for XCD i mod 8, and each XCD takes a contiguous range of row tiles with all
+// their column tiles: the row tile's activations and an expert's weight
+// blocks are then re-read from that XCD's L2 instead of from HBM.
 //
 // Modes
 //  GATEUP_W4 : A = x rows gathered through perm (token = perm[p] / k),
@@ -27,31 +37,56 @@ namespace moe {
 
 enum { GM_GATEUP_W4 = 0, GM_DOWN_W4 = 1, GM_GATEUP_F16 = 2, GM_DOWN_F16 = 3 };
 
-constexpr int BM = 128, BN = 128, BK = 64, KPAD = 8, LDK = BK + KPAD;
-constexpr int GEMM_THREADS = 256;
-constexpr size_t GEMM_LDS = (size_t)2 * (BM + BN) * LDK * sizeof(_Float16) + BM * sizeof(int);
+constexpr int GT = 256;       // threads per workgroup (4 waves)
+constexpr int BK = 64;        // K per pipeline step
+constexpr int LDK = BK + 8;   // LDS row stride in halfs (+8 spreads rows over banks)
+constexpr int NXCD = 8;       // XCDs of the part; workgroup i runs on XCD i mod 8
+
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
     const _Float16 *A;           // activations: x [T][K] or h [rows][K]
     const int32_t *perm;         // GATEUP_W4
-    const int32_t *offsets;      // W4 modes: [E+1]
+    const int32_t *offsets;      // W4 modes: [E+1]; null for the shared expert
     const uint8_t *const *blobs; // W4 modes
     int64_t off_q, off_s;        // W4: section offsets inside a blob
     const _Float16 *W0, *W1;     // F16 modes: gate/up or down (row-major)
     int k;                       // top-k (token = perm[p] / k)
     int E;                       // experts (1 for the shared expert)
     int rows;                    // total sorted rows (T*k) or tokens (T)
-    int K;                       // reduction length
-    int NW;                      // W4: 64-row blocks of B per expert matrix (unused for F16)
+    int K;                       // reduction length (multiple of 64)
+    int nblk;                    // 64-row blocks of B (output columns / 64, or I/32 fused)
     int g;                       // group size (W4)
     int ldo;                     // leading dim of the output (I for h, H for y/out)
     void *out;
 };
 
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
-                                          int target, int lane, int &e_out, int &p0, int &p1)
+// Row tiles of BM rows over all experts (offsets) or one implicit expert.
+__device__ __forceinline__ int count_row_tiles(const int32_t *__restrict__ offsets, int E,
+                                               int rows, int BM, int lane)
 {
-    if (offsets == nullptr) {   // single implicit expert covering all rows
+    if (offsets == nullptr)
+        return (rows + BM - 1) / BM;
+    int tot = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        int nt = 0;
+        if (e < E)
+            nt = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+#pragma unroll
+        for (int st = 32; st >= 1; st >>= 1)
+            nt += __shfl_xor(nt, st, 64);
+        tot += nt;
+    }
+    return tot;
+}
+
+// Expert and row range of row tile `target` (tiles numbered expert by expert).
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
+                                          int BM, int target, int lane, int &e_out, int &p0,
+                                          int &p1)
+{
+    if (offsets == nullptr) {
         const int nt = (rows + BM - 1) / BM;
         if (target >= nt)
             return false;
@@ -96,231 +131,601 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     return false;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(GEMM_THREADS) void grouped_gemm_kernel(GemmArgs a)
+// One dword of 8 nibbles (device order) times its group scale -> the 8 fp16
+// B-operand values of one lane for one 16-K step, fp16(q * s) exactly.  OR-ing
+// a nibble into the mantissa of 1024.0 gives 1024 + u (bits 0..3 of a half)
+// or 1024 + 16u (bits 4..7); subtracting 1032, or scaling by 1/16 and
+// subtracting 72, gives q = u - 8 exactly.  `magic` holds 0x64006400 in a
+// register so that mask-and-insert is one v_and_or_b32.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, uint32_t magic)
 {
-    extern __shared__ __align__(16) unsigned char smem[];
-    _Float16 *As = reinterpret_cast<_Float16 *>(smem);                 // [2][BM][LDK]
-    _Float16 *Bs = As + 2 * BM * LDK;                                  // [2][BN][LDK]
-    int *srow = reinterpret_cast<int *>(Bs + 2 * BN * LDK);            // [BM]
-    __shared__ int s_e, s_p0, s_p1;
+    const uint32_t w8 = w >> 8;
+    const half2_t k1032 = {(f16)-1032.0f, (f16)-1032.0f};
+    const half2_t s16 = {(f16)0.0625f, (f16)0.0625f};
+    const half2_t k72 = {(f16)-72.0f, (f16)-72.0f};
+    half2_t q[4];
+    q[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | magic) + k1032;
+    q[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | magic) * s16 + k72;
+    q[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | magic) + k1032;
+    q[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | magic) * s16 + k72;
+    half8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t v = q[i] * s2;
+        r[2 * i] = v[0];
+        r[2 * i + 1] = v[1];
+    }
+    return r;
+}
+
+// Loads through the global address space (plain pointers derived from a
+// loaded blob address would otherwise become flat loads, which the hardware
+// also counts against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T ldg(const T *p)
+{
+    typedef const __attribute__((address_space(1))) T gT;
+    return *(gT *)(p);
+}
+
+// ----------------------------------------------------------------------------
+// FP16 GEMM of the shared expert (GATEUP_F16, DOWN_F16): one implicit expert
+// over all T rows.  Four waves; the row tile of activations (32*MF rows x
+// 64 K) is staged in LDS (double buffered) and shared, wave w owns 64 weight
+// rows (block 4*nt + w: 32 gate + 32 up rows, or 64 down rows) whose 16-byte
+// K slices go straight from memory into the MFMA B operand.  Loads of step
+// k+1 are in flight while step k computes.
+template <int MODE, int MF>
+__global__ __launch_bounds__(GT) void f16_gemm_kernel(GemmArgs a)
+{
+    static_assert(MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16, "FP16 modes only");
+    constexpr bool GATEUP = MODE == GM_GATEUP_F16;
+    constexpr int BM = 32 * MF;
+    static_assert(BM * (BK / 8) == GT * MF, "activation staging assumes 256 threads");
+
+    __shared__ __align__(16) _Float16 As[2][BM * LDK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nb = blockIdx.x;   // output column tile (128 columns)
+    const int col = lane & 31;    // B column (weight row) of this lane inside a 32-wide fragment
+    const int half = lane >> 5;   // which 8-wide K slice of a 16-K step this lane feeds
 
-    if (wave == 0) {
-        int e = -1, p0 = 0, p1 = 0;
-        const bool ok = find_tile((MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) ? a.offsets
-                                                                               : nullptr,
-                                  a.E, a.rows, blockIdx.y, lane, e, p0, p1);
-        if (lane == 0) {
-            s_e = ok ? e : -1;
-            s_p0 = p0;
-            s_p1 = p1;
-        }
-    }
-    __syncthreads();
-    const int e = s_e;
-    if (e < 0)
-        return;
-    const int p0 = s_p0, mrows = s_p1 - s_p0;
-    for (int i = tid; i < BM; i += GEMM_THREADS) {
-        int src = -1;
-        if (i < mrows) {
-            const int p = p0 + i;
-            src = (MODE == GM_GATEUP_W4) ? a.perm[p] / a.k : p;
-        }
-        srow[i] = src;
-    }
-    __syncthreads();
-
+    const int R = (a.rows + BM - 1) / BM;
+    const int NT = (a.nblk + 3) / 4;
+    const int xcd = blockIdx.x % NXCD;
+    const int G = gridDim.x / NXCD;
+    const int r_lo = (int)((int64_t)R * xcd / NXCD);
+    const int r_hi = (int)((int64_t)R * (xcd + 1) / NXCD);
+    const int nitems = (r_hi - r_lo) * NT;
     const int K = a.K;
     const int nk = K / BK;
 
-    // ---- B source for this workgroup
-    const uint8_t *blob = nullptr;
-    if (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4)
-        blob = a.blobs[e];
+    for (int it = (int)blockIdx.x / NXCD; it < nitems; it += G) {
+        const int rt = r_lo + it / NT;
+        const int nt = it % NT;
+        const int p0 = rt * BM, mrows = min(BM, a.rows - p0);
+        __syncthreads();   // the previous item's LDS readers are done
 
-    // A staging: 4 x 16 B per thread; B staging: 1 x 16 B (W4) or 4 x 16 B (F16)
-    uint4_t ra[4];
-    uint4_t rb[4];
-    float rsc = 0.0f;
-
-    auto load_stage = [&](int kt) {
-        const int k0 = kt * BK;
+        // activation rows staged by this thread: row r = (tid + 256 i) / 8,
+        // 16-byte piece ks = tid % 8.  Rows past the tile's end re-read its
+        // first row: they only feed output rows that are never stored.
+        const _Float16 *arow[MF];
+        const int ks = tid & 7;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sgi = tid + GEMM_THREADS * i;   // 0..1023
-            const int r = sgi >> 3, ks = sgi & 7;
-            const int src = srow[r];
-            if (src >= 0)
-                ra[i] = *reinterpret_cast<const uint4_t *>(a.A + (size_t)src * K + k0 + ks * 8);
-            else
-                ra[i] = uint4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < MF; ++i) {
+            const int r = (tid + GT * i) >> 3;
+            arow[i] = a.A + (size_t)(p0 + (r < mrows ? r : 0)) * K + ks * 8;
         }
-        if (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
-            const int blk = tid >> 7, ch = (tid >> 6) & 1, row = tid & 63;
-            const int bidx = nb * 2 + blk;           // 64-row block within the expert matrix
-            const int kc = (k0 >> 5) + ch;           // 32-element chunk
-            const uint4_t *q = reinterpret_cast<const uint4_t *>(blob + a.off_q);
-            rb[0] = q[((size_t)bidx * (K / 32) + kc) * 64 + row];
-            const uint16_t *sc = reinterpret_cast<const uint16_t *>(blob + a.off_s);
-            rsc = h2f(sc[((size_t)bidx * (K / a.g) + (kc * 32) / a.g) * 64 + row]);
+
+        // this wave's weight rows (a wave past the last block computes on the
+        // last block and stores nothing)
+        const int blk = nt * 4 + wave;
+        const bool wact = blk < a.nblk;
+        const int bb = wact ? blk : a.nblk - 1;
+        const _Float16 *wr0, *wr1;
+        if constexpr (GATEUP) {
+            wr0 = a.W0 + (size_t)(bb * 32 + col) * K + 8 * half;
+            wr1 = a.W1 + (size_t)(bb * 32 + col) * K + 8 * half;
         } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sgi = tid + GEMM_THREADS * i;
-                const int n = sgi >> 3, ks = sgi & 7;   // GEMM column n of this tile
-                const _Float16 *wrow;
-                if (MODE == GM_GATEUP_F16) {
-                    const int blk = n >> 6, rr = n & 63;
-                    const int irow = (nb * 2 + blk) * 32 + (rr & 31);
-                    wrow = ((rr < 32) ? a.W0 : a.W1) + (size_t)irow * K;
-                } else {
-                    wrow = a.W0 + (size_t)(nb * BN + n) * K;
-                }
-                rb[i] = *reinterpret_cast<const uint4_t *>(wrow + k0 + ks * 8);
-            }
+            wr0 = a.W0 + (size_t)(bb * 64 + col) * K + 8 * half;
+            wr1 = a.W0 + (size_t)(bb * 64 + 32 + col) * K + 8 * half;
         }
-    };
 
-    auto store_stage = [&](int buf) {
-        _Float16 *as = As + buf * BM * LDK;
-        _Float16 *bs = Bs + buf * BN * LDK;
+        uint4_t ra[MF];
+        auto load_a = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sgi = tid + GEMM_THREADS * i;
-            const int r = sgi >> 3, ks = sgi & 7;
-            *reinterpret_cast<uint4_t *>(as + r * LDK + ks * 8) = ra[i];
-        }
-        if (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
-            const int blk = tid >> 7, ch = (tid >> 6) & 1, row = tid & 63;
-            const half2_t s2 = {(_Float16)rsc, (_Float16)rsc};
-            half2_t q[16];
-            nib8_to_h2x4(rb[0].x, q + 0);
-            nib8_to_h2x4(rb[0].y, q + 4);
-            nib8_to_h2x4(rb[0].z, q + 8);
-            nib8_to_h2x4(rb[0].w, q + 12);
+            for (int i = 0; i < MF; ++i)
+                ra[i] = ldg(reinterpret_cast<const uint4_t *>(arow[i] + kt * BK));
+        };
+        auto store_a = [&](int buf) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-                q[m] = q[m] * s2;
-            uint4_t *dst = reinterpret_cast<uint4_t *>(bs + (blk * 64 + row) * LDK + ch * 32);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint4_t v;
-                v.x = __builtin_bit_cast(uint32_t, q[4 * j + 0]);
-                v.y = __builtin_bit_cast(uint32_t, q[4 * j + 1]);
-                v.z = __builtin_bit_cast(uint32_t, q[4 * j + 2]);
-                v.w = __builtin_bit_cast(uint32_t, q[4 * j + 3]);
-                dst[j] = v;
+            for (int i = 0; i < MF; ++i) {
+                const int r = (tid + GT * i) >> 3;
+                *reinterpret_cast<uint4_t *>(&As[buf][r * LDK + ks * 8]) = ra[i];
             }
-        } else {
+        };
+        half8_t bc[2][4], bn[2][4];   // [fragment][16-K step]
+        auto load_b = [&](int kt, half8_t (&b)[2][4]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sgi = tid + GEMM_THREADS * i;
-                const int n = sgi >> 3, ks = sgi & 7;
-                *reinterpret_cast<uint4_t *>(bs + n * LDK + ks * 8) = rb[i];
+            for (int s = 0; s < 4; ++s) {
+                b[0][s] = ldg(reinterpret_cast<const half8_t *>(wr0 + kt * BK + 16 * s));
+                b[1][s] = ldg(reinterpret_cast<const half8_t *>(wr1 + kt * BK + 16 * s));
             }
-        }
-    };
+        };
 
-    const int wm = wave & 1, wn = wave >> 1;
-    float16_t acc[2][2];
+        float16_t acc[MF][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int m = 0; m < MF; ++m)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.0f;
+                for (int r = 0; r < 16; ++r)
+                    acc[m][n][r] = 0.0f;
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk)
-            load_stage(kt + 1);
-        const _Float16 *as = As + cur * BM * LDK;
-        const _Float16 *bs = Bs + cur * BN * LDK;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int kof = kk * 16 + (lane >> 5) * 8;
-            half8_t af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const half8_t *>(
-                    as + (wm * 64 + i * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const half8_t *>(
-                    bs + (wn * 64 + j * 32 + (lane & 31)) * LDK + kof);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j],
-                                                                      0, 0, 0);
-        }
-        if (kt + 1 < nk)
-            store_stage(cur ^ 1);
+        load_a(0);
+        load_b(0, bc);
+        store_a(0);
         __syncthreads();
-    }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) {
+                load_a(kt + 1);
+                load_b(kt + 1, bn);
+            }
+            const _Float16 *as = As[cur];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                half8_t af[MF];
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+                    af[m] = *reinterpret_cast<const half8_t *>(as + (m * 32 + col) * LDK + s * 16 +
+                                                               half * 8);
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], bc[n][s],
+                                                                          acc[m][n], 0, 0, 0);
+            }
+            if (more)
+                store_a(cur ^ 1);
+            __syncthreads();
+            if (more) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        bc[n][s] = bn[n][s];
+            }
+        }
 
-    // ---- epilogue.  32x32 accumulator layout: value r of lane l is
-    // row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
-    const int col = lane & 31;
+        // epilogue.  32x32 accumulator layout: value r of lane l is
+        // row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+        if (wact) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+            for (int m = 0; m < MF; ++m) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m >= mrows)
-                continue;
-            const size_t p = (size_t)(p0 + m);
-            if (MODE == GM_GATEUP_W4 || MODE == GM_GATEUP_F16) {
-                const float gv = acc[i][0][r], uv = acc[i][1][r];
-                const float hv = gv / (1.0f + expf(-gv)) * uv;
-                const int icol = (nb * 2 + wn) * 32 + col;
-                static_cast<_Float16 *>(a.out)[p * a.ldo + icol] = (_Float16)hv;
-            } else {
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (row >= mrows)
+                        continue;
+                    const size_t p = (size_t)(p0 + row);
+                    if constexpr (GATEUP) {
+                        const float gv = acc[m][0][r], uv = acc[m][1][r];
+                        const float hv = gv / (1.0f + expf(-gv)) * uv;
+                        static_cast<_Float16 *>(a.out)[p * a.ldo + blk * 32 + col] = (_Float16)hv;
+                    } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int ocol = nb * BN + wn * 64 + j * 32 + col;
-                    if (MODE == GM_DOWN_W4)
-                        static_cast<_Float16 *>(a.out)[p * a.ldo + ocol] = (_Float16)acc[i][j][r];
-                    else
-                        static_cast<float *>(a.out)[p * a.ldo + ocol] = acc[i][j][r];
+                        for (int n = 0; n < 2; ++n)
+                            static_cast<float *>(a.out)[p * a.ldo + blk * 64 + n * 32 + col] =
+                                acc[m][n][r];
+                    }
                 }
             }
         }
     }
 }
 
-template <int MODE>
-static int launch_mode(dim3 grid, hipStream_t s, const GemmArgs &a)
+// ----------------------------------------------------------------------------
+// INT4 grouped GEMM with a 4-stage global->LDS pipeline (GATEUP_W4, DOWN_W4).
+//
+// Work item: (row tile of 32*MF sorted rows of one expert) x (512 output
+// columns = eight 64-row weight blocks).  A workgroup has eight waves, two
+// per SIMD, so one wave's dequantisation, LDS reads and load issue overlap
+// the other's MFMAs; wave w owns weight block 8*nt + w and computes a
+// 32*MF x 64 output tile (MF x 2 fragments): each dequantised weight
+// fragment feeds MF MFMAs, each activation fragment two.
+//
+// Every operand of a 64-K step travels HBM -> LDS by the CU's direct-to-LDS
+// loads (global_load_lds: each lane's bytes land at the wave's LDS base +
+// lane * size), so nothing in flight occupies registers.  Per step and wave:
+// 4*MF rows of the activation tile (8 rows of 128 B per 64-lane load), the
+// wave's two 1 KB weight chunk runs (64 rows x 16 B) and one 4-byte load of
+// the two chunks' group scales (64 rows x fp16 each).  The count is the same
+// every step, so "step k has landed" is an exact vmcnt; a plain s_barrier
+// then publishes it (a fence would wait for every outstanding load).
+//
+// Inside a step the four 16-K sub-steps are software pipelined: operands of
+// sub-step s+1 (activation fragments from LDS, weights dequantised in
+// registers) are fetched while the MFMAs of s run.  Before the last sub-step
+// the wave holds every operand of the step, so the barrier that opens the
+// next step sits there; the stage just finished is then refilled with step
+// k+4.
+//
+// Activation stage layout: row r at r*128 B, its 16-byte piece j at slot
+// j ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 8 or 16 rows one LDS pass of
+// ds_read_b128 touches then hit distinct banks.
+constexpr int W4_NS = 4;     // pipeline stages
+constexpr int W4_WAVES = 8;  // waves per workgroup
+constexpr int W4_T = W4_WAVES * 64;
+
+template <int MF>
+struct W4Stage {
+    static constexpr int A = 32 * MF * 128;          // activation tile
+    static constexpr int B = W4_WAVES * 2 * 1024;    // per wave: 2 chunk runs
+    static constexpr int S = W4_WAVES * 256;         // per wave: [2 chunks][64 rows] fp16
+    static constexpr int BYTES = A + B + S;
+};
+
+template <int MF>
+constexpr size_t w4_lds_bytes() { return (size_t)W4_NS * W4Stage<MF>::BYTES; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void *g, unsigned char *l)
 {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, unsigned char *l)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
+}
+
+// Waits until at most N vector-memory instructions of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int PER>
+__device__ __forceinline__ void wait_steps(int younger)   // younger in 0..3
+{
+    if (younger >= 3)
+        wait_vm<3 * PER>();
+    else if (younger == 2)
+        wait_vm<2 * PER>();
+    else if (younger == 1)
+        wait_vm<PER>();
+    else
+        wait_vm<0>();
+}
+// Workgroup barrier after this wave's LDS reads have completed (no fence:
+// outstanding direct-to-LDS loads of later stages stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// SiLU(g) * u with the hardware exp2 / reciprocal (about 1 ulp each in fp32;
+// the result is rounded to fp16).
+__device__ __forceinline__ float swiglu_fast(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+template <int MODE, int MF>
+__global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
+{
+    static_assert(MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4, "INT4 modes only");
+    constexpr bool GATEUP = MODE == GM_GATEUP_W4;
+    constexpr int BM = 32 * MF;
+    constexpr int RPW = BM / W4_WAVES;        // activation rows loaded per wave (4*MF)
+    constexpr int NA = (RPW + 7) / 8;         // their 64-lane loads (lanes 8 per row)
+    constexpr int PER = NA + 3;               // direct-to-LDS loads per step and wave
+    using St = W4Stage<MF>;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_tiles, s_e, s_p0, s_p1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int fcol = (col & 7) ^ ((col >> 3) & 1);   // swizzle of rows m*32 + col
+    const int gshift = __builtin_ctz((unsigned)a.g);
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+    if (wave == 0) {
+        const int R = count_row_tiles(a.offsets, a.E, a.rows, BM, lane);
+        if (lane == 0)
+            s_tiles = R;
+    }
+    __syncthreads();
+    const int R = s_tiles;
+    const int NT = (a.nblk + W4_WAVES - 1) / W4_WAVES;
+    const int xcd = blockIdx.x % NXCD;
+    const int G = gridDim.x / NXCD;
+    const int r_lo = (int)((int64_t)R * xcd / NXCD);
+    const int r_hi = (int)((int64_t)R * (xcd + 1) / NXCD);
+    const int nitems = (r_hi - r_lo) * NT;
+    const int K = a.K;
+    const int nk = K / BK;
+
+    for (int it = (int)blockIdx.x / NXCD; it < nitems; it += G) {
+        const int rt = r_lo + it / NT;
+        const int nt = it % NT;
+        if (wave == 0) {
+            int e = -1, p0 = 0, p1 = 0;
+            const bool ok = find_tile(a.offsets, a.E, a.rows, BM, rt, lane, e, p0, p1);
+            if (lane == 0) {
+                s_e = ok ? e : -1;
+                s_p0 = p0;
+                s_p1 = p1;
+            }
+        }
+        __syncthreads();
+        const int e = s_e;
+        const int p0 = s_p0, mrows = s_p1 - s_p0;
+        __syncthreads();   // every wave has the tile and is done with the last item's stages
+        if (e < 0)
+            break;
+
+        // activation sources of this lane: load i covers rows wave*RPW + 8i ..+7
+        // (lane -> row lane >> 3, slot lane & 7 holding logical piece slot ^ f(row));
+        // with RPW = 4 only lanes 0-31 load.  Rows past the tile's end re-read
+        // its first row (their outputs are dropped).
+        const _Float16 *asrc[NA];
+        const bool aload = (RPW >= 8) || lane < 8 * RPW;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int r = wave * RPW + 8 * i + (lane >> 3);
+            const int fr = (r & 7) ^ ((r >> 3) & 1);
+            const int j = (lane & 7) ^ fr;
+            const int p = p0 + (r < mrows ? r : 0);
+            const int src = GATEUP ? ldg(a.perm + min(p, a.rows - 1)) / a.k : p;
+            asrc[i] = a.A + (size_t)src * K + j * 8;
+        }
+        // this wave's weight block (a wave past the last block works on the
+        // last one and stores nothing)
+        const int blk = nt * W4_WAVES + wave;
+        const int bb = min(blk, a.nblk - 1);
+        const uint8_t *blob = ldg(a.blobs + e);
+        const uint8_t *qsrc = blob + a.off_q + ((size_t)bb * (K / 32) * 64 + lane) * 16;
+        const uint8_t *ssrc = blob + a.off_s + ((size_t)bb * (K >> gshift) * 64 + col * 2) * 2;
+
+        auto issue = [&](int kt) {
+            unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
+            if (aload) {
+#pragma unroll
+                for (int i = 0; i < NA; ++i)
+                    dma16(asrc[i] + kt * BK, st + (wave * RPW + 8 * i) * 128);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dma16(qsrc + (size_t)(2 * kt + c) * 1024, st + St::A + wave * 2048 + c * 1024);
+            // lanes 0-31: chunk 2kt's group, rows 2l, 2l+1; lanes 32-63: chunk 2kt+1's
+            const int grp = ((2 * kt + half) * 32) >> gshift;
+            dma4(ssrc + (size_t)grp * 128, st + St::A + St::B + wave * 256);
+        };
+
+        // weight words and scales of one step: fragment n = rows n*32 + col
+        struct StepW {
+            uint2_t q[2][2];
+            f16 s[2][2];
+        };
+        auto read_w = [&](int kt, StepW &w) {
+            const unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
+            const unsigned char *bq = st + St::A + wave * 2048;
+            const unsigned char *sq = st + St::A + St::B + wave * 256;
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    w.q[n][c] = *reinterpret_cast<const uint2_t *>(bq + c * 1024 +
+                                                                   (n * 32 + col) * 16 + half * 8);
+                    w.s[n][c] = *reinterpret_cast<const f16 *>(sq + c * 128 + (n * 32 + col) * 2);
+                }
+        };
+        auto fetch = [&](int kt, int s, const StepW &w, half8_t *a_, half8_t *b_) {
+            const unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                a_[m] = *reinterpret_cast<const half8_t *>(
+                    st + (m * 32 + col) * 128 + (((2 * s + half) ^ fcol) << 4));
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const uint2_t q = w.q[n][s >> 1];
+                const f16 c = w.s[n][s >> 1];
+                b_[n] = dequant8((s & 1) ? q.y : q.x, half2_t{c, c}, magic);
+            }
+        };
+
+        float16_t acc[MF][2];
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[m][n][r] = 0.0f;
+
+        const int pre = min(W4_NS, nk);
+        for (int kt = 0; kt < pre; ++kt)
+            issue(kt);
+        wait_steps<PER>(pre - 1);
+        lds_barrier();
+        StepW wc, wn;
+        half8_t af[2][MF], bf[2][2];
+        read_w(0, wc);
+        fetch(0, 0, wc, af[0], bf[0]);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool next = kt + 1 < nk;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s == 3 && next) {
+                    // every operand of step kt is in registers: open step kt+1
+                    wait_steps<PER>(min(2, nk - 2 - kt));
+                    lds_barrier();
+                    if (kt + W4_NS < nk)
+                        issue(kt + W4_NS);   // refills the stage of step kt
+                }
+                // weights as the 32-row operand: acc[m][n] holds C^T, so a lane
+                // owns one token row and 4 consecutive output columns per
+                // group of 4 values
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            bf[s & 1][n], af[s & 1][m], acc[m][n], 0, 0, 0);
+                if (s < 3) {
+                    fetch(kt, s + 1, wc, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                } else if (next) {
+                    read_w(kt + 1, wn);
+                    fetch(kt + 1, 0, wn, af[0], bf[0]);
+                }
+            }
+            if (next)
+                wc = wn;
+        }
+
+        // ---- epilogue.  acc[m][n] = (weight rows) x (tokens): value r of
+        // lane l is output column 8*(r/4) + 4*(l/32) + (r%4) of fragment n and
+        // token row m*32 + l%32, so r = 4j..4j+3 are 4 consecutive columns
+        // (one 8-byte store).
+        if (blk < a.nblk) {
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                const int row = m * 32 + col;
+                if (row >= mrows)
+                    continue;
+                const size_t p = (size_t)(p0 + row);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c0 = 8 * j + 4 * half;
+                    half4_t v;
+                    if constexpr (GATEUP) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            v[i] = (_Float16)swiglu_fast(acc[m][0][4 * j + i], acc[m][1][4 * j + i]);
+                        *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) + p * a.ldo +
+                                                     blk * 32 + c0) = v;
+                    } else {
+#pragma unroll
+                        for (int f = 0; f < 2; ++f) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                v[i] = (_Float16)acc[m][f][4 * j + i];
+                            *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) +
+                                                         p * a.ldo + blk * 64 + f * 32 + c0) = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+static int num_cus()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// Upper bound on row tiles: every non-empty expert adds at most one partial tile.
+static int64_t tile_bound(int rows, int E, int BM)
+{
+    return ((int64_t)rows + BM - 1) / BM + (E > 1 ? std::min<int64_t>(E, rows) : 0);
+}
+
+// Row-tile height: tall tiles when experts hold many rows (more MFMA work per
+// activation and weight byte), shorter ones when the tall tiles would leave
+// CUs idle or mostly pad.
+static int pick_mf(int rows, int E, int nblk)
+{
+    const int NT = (nblk + W4_WAVES - 1) / W4_WAVES;
+    const int64_t avg = rows / std::max(1, std::min(E, rows));
+    int mf = avg >= 192 ? 4 : (avg >= 48 ? 2 : 1);
+    while (mf > 1 && (((int64_t)rows + 32 * mf - 1) / (32 * mf)) * NT < num_cus())
+        mf /= 2;
+    return mf;
+}
+
+// Row-tile height of the FP16 shared-expert GEMM: the tallest that still
+// gives every CU about two workgroups.
+static int pick_f16_mf(int rows, int nblk)
+{
+    const int NT = (nblk + 3) / 4;
+    int mf = 4;
+    while (mf > 1 && (((int64_t)rows + 32 * mf - 1) / (32 * mf)) * NT < 2 * num_cus())
+        mf /= 2;
+    return mf;
+}
+
+template <int MODE, int MF>
+static int launch_mf(hipStream_t s, const GemmArgs &a)
+{
+    const int64_t items = (((int64_t)a.rows + 32 * MF - 1) / (32 * MF)) * ((a.nblk + 3) / 4);
+    int64_t grid = std::min<int64_t>(items, (int64_t)2 * num_cus());
+    grid = std::max<int64_t>(NXCD, (grid + NXCD - 1) / NXCD * NXCD);
+    hipLaunchKernelGGL((f16_gemm_kernel<MODE, MF>), dim3((unsigned)grid), dim3(GT), 0, s, a);
+    MOE_LAUNCH_CHECK("f16_gemm_kernel");
+    return MOE_OK;
+}
+
+template <int MODE, int MF>
+static int launch_w4(hipStream_t s, const GemmArgs &a)
+{
+    constexpr size_t lds = w4_lds_bytes<MF>();
     static bool attr_set = false;   // raising the LDS limit is idempotent
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void *)grouped_gemm_kernel<MODE>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)GEMM_LDS);
+        hipError_t err = hipFuncSetAttribute((const void *)w4_gemm_kernel<MODE, MF>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess)
             return set_error(MOE_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
         attr_set = true;
     }
-    hipLaunchKernelGGL(grouped_gemm_kernel<MODE>, grid, dim3(GEMM_THREADS), GEMM_LDS, s, a);
-    MOE_LAUNCH_CHECK("grouped_gemm_kernel");
+    // one workgroup per CU (its LDS and eight waves fill it)
+    const int64_t items = tile_bound(a.rows, a.E, 32 * MF) * ((a.nblk + W4_WAVES - 1) / W4_WAVES);
+    int64_t grid = std::min<int64_t>(items, num_cus());
+    grid = std::max<int64_t>(NXCD, (grid + NXCD - 1) / NXCD * NXCD);
+    hipLaunchKernelGGL((w4_gemm_kernel<MODE, MF>), dim3((unsigned)grid), dim3(W4_T), lds, s, a);
+    MOE_LAUNCH_CHECK("w4_gemm_kernel");
     return MOE_OK;
 }
 
-static unsigned tile_bound(int rows, int E)
+template <int MODE>
+static int launch_mode(hipStream_t s, const GemmArgs &a)
 {
-    const int64_t nt = ((int64_t)rows + BM - 1) / BM + (E > 1 ? std::min<int64_t>(E, rows) : 0);
-    return (unsigned)std::max<int64_t>(nt, 1);
+    if constexpr (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
+        switch (pick_mf(a.rows, a.E, a.nblk)) {
+        case 4: return launch_w4<MODE, 4>(s, a);
+        case 2: return launch_w4<MODE, 2>(s, a);
+        default: return launch_w4<MODE, 1>(s, a);
+        }
+    } else {
+        switch (pick_f16_mf(a.rows, a.nblk)) {
+        case 4: return launch_mf<MODE, 4>(s, a);
+        case 2: return launch_mf<MODE, 2>(s, a);
+        default: return launch_mf<MODE, 1>(s, a);
+        }
+    }
 }
 
 size_t ffn_batched_ws_bytes(int T, int I, int k)
@@ -345,24 +750,26 @@ int launch_ffn_batched(const void *x, const int32_t *perm, const int32_t *offset
     a.E = E;
     a.rows = rows;
     a.g = g;
-    // gate/up: GEMM N = 2I (fused blocks), K = H, out h [rows][I]
+    // gate/up: fused 64-row blocks (I/32 of them), K = H, out h [rows][I]
     a.A = static_cast<const _Float16 *>(x);
     a.off_q = L.gu_q;
     a.off_s = L.gu_s;
     a.K = H;
+    a.nblk = I / 32;
     a.ldo = I;
     a.out = h;
-    int rc = launch_mode<GM_GATEUP_W4>(dim3(I / 64, tile_bound(rows, E)), s, a);
+    int rc = launch_mode<GM_GATEUP_W4>(s, a);
     if (rc)
         return rc;
-    // down: GEMM N = H, K = I, out y [rows][H] fp16
+    // down: H/64 blocks, K = I, out y [rows][H] fp16
     a.A = h;
     a.off_q = L.d_q;
     a.off_s = L.d_s;
     a.K = I;
+    a.nblk = H / 64;
     a.ldo = H;
     a.out = y;
-    return launch_mode<GM_DOWN_W4>(dim3(H / 128, tile_bound(rows, E)), s, a);
+    return launch_mode<GM_DOWN_W4>(s, a);
 }
 
 int launch_shared_batched(const void *x, const void *wg, const void *wu, const void *wd, int T,
@@ -378,18 +785,20 @@ int launch_shared_batched(const void *x, const void *wg, const void *wu, const v
     a.W0 = static_cast<const _Float16 *>(wg);
     a.W1 = static_cast<const _Float16 *>(wu);
     a.K = H;
+    a.nblk = Is / 32;
     a.ldo = Is;
     a.out = h;
-    int rc = launch_mode<GM_GATEUP_F16>(dim3(Is / 64, tile_bound(T, 1)), s, a);
+    int rc = launch_mode<GM_GATEUP_F16>(s, a);
     if (rc)
         return rc;
     a.A = h;
     a.W0 = static_cast<const _Float16 *>(wd);
     a.W1 = nullptr;
     a.K = Is;
+    a.nblk = H / 64;
     a.ldo = H;
     a.out = out;
-    return launch_mode<GM_DOWN_F16>(dim3(H / 128, tile_bound(T, 1)), s, a);
+    return launch_mode<GM_DOWN_F16>(s, a);
 }
 
 }  // namespace moe

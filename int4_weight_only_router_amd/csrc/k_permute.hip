@@ -10,8 +10,8 @@
 // chunks of CH elements in order; chunk b's elements of expert e start at
 // offsets[e] + (elements of e in chunks < b).  Inside a chunk one wave walks
 // the elements 64 at a time; a lane's rank among equal keys of earlier lanes
-// comes from a readlane sweep, and a per-expert running counter in LDS
-// advances by the group's multiplicity (LDS max of the new end positions).
+// comes from ballots over the key bits, and a per-expert running counter in
+// LDS advances by the group's multiplicity.
 #include "k_sort_common.h"
 
 namespace moe {
@@ -39,9 +39,17 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t *__rest
         h[e] = 0;
     __syncthreads();
     const int f0 = b * PERM_CH, f1 = min(n, f0 + PERM_CH);
-    for (int f = f0 + threadIdx.x; f < f1; f += blockDim.x)
-        if ((unsigned)idx[f] < (unsigned)E)
-            atomicAdd(&h[idx[f]], 1);
+    static_assert(PERM_CH % 256 == 0, "whole rounds of 256 threads");
+    int keys[PERM_CH / 256];
+#pragma unroll
+    for (int i = 0; i < PERM_CH / 256; ++i) {
+        const int f = f0 + threadIdx.x + 256 * i;
+        keys[i] = (f < f1) ? idx[f] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < PERM_CH / 256; ++i)
+        if ((unsigned)keys[i] < (unsigned)E)
+            atomicAdd(&h[keys[i]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
         hist[(size_t)b * E + e] = h[e];
@@ -55,9 +63,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     __shared__ int wsum[16];
     const int e = threadIdx.x;
     int c = 0;
-    if (e < E)
-        for (int b = 0; b < nb; ++b)
+    if (e < E) {
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {   // eight loads in flight per round
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = hist[(size_t)(b + i) * E + e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                c += v[i];
+        }
+        for (; b < nb; ++b)
             c += hist[(size_t)b * E + e];
+    }
     // block exclusive scan of c over e
     const int lane = e & 63, w = e >> 6;
     int incl = c;
@@ -78,7 +97,19 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
         counts[e] = c;
         offsets[e] = off;
         int run = off;
-        for (int b = 0; b < nb; ++b) {
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = hist[(size_t)(b + i) * E + e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                base[(size_t)(b + i) * E + e] = run;
+                run += v[i];
+            }
+        }
+        for (; b < nb; ++b) {
             base[(size_t)b * E + e] = run;
             run += hist[(size_t)b * E + e];
         }

@@ -93,6 +93,9 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4_t *p, int64_t n16)
 
 // Item ranges: [0,nguq) fused gate/up 16-byte chunks, then down chunks, then
 // fused gate/up scales, then down scales.  dir = 0: canonical -> device.
+// Inside a device chunk word the four dwords hold elements 0-7, 16-23, 8-15,
+// 24-31 of the chunk: bytes 0-7 are then the K-half one MFMA lane group needs
+// for two consecutive 16-K steps, bytes 8-15 the other half.
 __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict__ src,
                                                       uint8_t *__restrict__ dst, int H, int I,
                                                       int g, int64_t stride, CanonLayout C,
@@ -136,13 +139,14 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict_
             kind = 1;
         }
         if (kind == 0) {
+            // dwords 1 and 2 trade places (the swap is its own inverse)
             const uint4_t v = *reinterpret_cast<const uint4_t *>(s + (dir == 0 ? canoff : devoff));
             uint4_t o;
             if (dir == 0)
-                o = uint4_t{canon_to_dev(v.x), canon_to_dev(v.y), canon_to_dev(v.z),
+                o = uint4_t{canon_to_dev(v.x), canon_to_dev(v.z), canon_to_dev(v.y),
                             canon_to_dev(v.w)};
             else
-                o = uint4_t{dev_to_canon(v.x), dev_to_canon(v.y), dev_to_canon(v.z),
+                o = uint4_t{dev_to_canon(v.x), dev_to_canon(v.z), dev_to_canon(v.y),
                             dev_to_canon(v.w)};
             *reinterpret_cast<uint4_t *>(d + (dir == 0 ? devoff : canoff)) = o;
         } else {

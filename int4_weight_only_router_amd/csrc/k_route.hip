@@ -16,12 +16,11 @@
 //  * Top-k by (logit desc, expert asc); softmax over all E logits taken at the
 //    chosen experts; optional renormalisation over the k chosen.
 //
-// Work split: a workgroup owns TT tokens (x tile in LDS); wave w computes
-// experts w, w+NW, ... for all TT tokens, each router chunk loaded from
-// global memory once per workgroup and reused TT times.  A wave issues the
-// loads of its next expert before the arithmetic of the current one, so at
-// decode sizes the router costs about two memory round trips, not one per
-// expert.
+// route_kernel (T <= 8, one workgroup): the TT tokens are staged in LDS;
+// wave w computes experts w, w+NW, ... for all TT tokens, each router chunk
+// loaded from global memory once and reused TT times.  A wave issues the
+// loads of its next expert before the arithmetic of the current one.  Larger
+// batches use route_logits_kernel + route_topk_kernel below.
 #include "k_sort_common.h"
 
 namespace moe {
@@ -143,6 +142,172 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
         }
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+// Batches above 8 tokens: logits and top-k in two launches.
+//
+// route_logits_kernel: each wave computes an 8-token x 8-expert tile of
+// logits.  Lane j owns partial j of all 64 logits (chunks c = j, j+64, ...,
+// elements in order, acc = fma(x, w, acc) with exact fp16 products), reading
+// its 16-byte slices of the 8 activation rows and the 8 router rows straight
+// from memory (consecutive lanes read consecutive 16-byte slices of a row).
+// The 64 x 64 partials then go through LDS so that lane l holds the 64
+// partials of logit l and folds them in registers in the butterfly's order
+// (a_j + a_(j+32), then +16, ... +1): the same additions, operand for operand,
+// as the cross-lane butterfly, at one add per partial instead of a shuffle.
+constexpr int RL_WAVES = 4;   // waves per workgroup, 8 experts each
+
+template <int H>
+__global__ __launch_bounds__(RL_WAVES * 64) void route_logits_kernel(
+    const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
+    int T, int E, float *__restrict__ logits)
+{
+    constexpr int NCH = H / 8;                // 8-element chunks of a row
+    constexpr int NCL = (NCH + 63) / 64;      // chunks per lane
+    constexpr int RS = 68;                    // LDS row stride (floats) of the transposition
+    __shared__ __align__(16) float tr[RL_WAVES][64 * RS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 8;
+    const int e0 = (blockIdx.y * RL_WAVES + wave) * 8;
+
+    float acc[8][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[t][i] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCL; ++m) {
+        const int c = lane + 64 * m;
+        if (c < NCH) {
+            half8_t xv[8], wv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int tt = min(t0 + t, T - 1);   // rows past T compute garbage, never stored
+                xv[t] = *reinterpret_cast<const half8_t *>(x + (size_t)tt * H + c * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int ee = min(e0 + i, E - 1);
+                wv[i] = *reinterpret_cast<const half8_t *>(wr + (size_t)ee * H + c * 8);
+            }
+#pragma unroll
+            for (int el = 0; el < 8; ++el)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc[t][i] = __builtin_fmaf((float)xv[t][el], (float)wv[i][el], acc[t][i]);
+        }
+    }
+    float *trw = tr[wave];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            trw[(t * 8 + i) * RS + lane] = acc[t][i];
+    __builtin_amdgcn_wave_barrier();
+    float a[64];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const float4_t v = *reinterpret_cast<const float4_t *>(trw + lane * RS + 4 * q);
+        a[4 * q] = v[0];
+        a[4 * q + 1] = v[1];
+        a[4 * q + 2] = v[2];
+        a[4 * q + 3] = v[3];
+    }
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1)
+#pragma unroll
+        for (int j = 0; j < step; ++j)
+            a[j] = a[j] + a[j + step];
+    const int t = t0 + (lane >> 3), e = e0 + (lane & 7);
+    if (t < T && e < E) {
+        float l = a[0];
+        if (bias)
+            l = l + bias[e];
+        logits[(size_t)t * E + e] = l;
+    }
+}
+
+// route_topk_kernel: one wave per token over its E logits (rank-based top-k
+// in 64-expert blocks, merge, softmax over all E in fp32, optional renorm).
+constexpr int RT_WAVES = 4;
+
+__global__ __launch_bounds__(RT_WAVES * 64) void route_topk_kernel(
+    const float *__restrict__ logits, int T, int E, int k, unsigned flags,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nb = (E + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // per wave: the token's logits (E floats, 16-byte aligned), then candidates
+    const size_t lbytes = ((size_t)E * sizeof(float) + 15) & ~(size_t)15;
+    float *l = reinterpret_cast<float *>(smem + (size_t)wave * (lbytes + (nb * 16 + 16) * sizeof(Cand)));
+    Cand *wc = reinterpret_cast<Cand *>(reinterpret_cast<unsigned char *>(l) + lbytes);
+    Cand *st = wc + nb * 16;
+    const int t = blockIdx.x * RT_WAVES + wave;
+    if (t >= T)
+        return;
+    const float *lg = logits + (size_t)t * E;
+    for (int e = lane; e < E; e += 64)   // every load of the row in flight at once
+        l[e] = lg[e];
+    __builtin_amdgcn_wave_barrier();
+    for (int b = 0; b < nb; ++b)
+        block_topk(l, E, k, b, lane, wc + b * k);
+    __builtin_amdgcn_wave_barrier();
+    merge_topk(wc, nb * k, k, lane, st);
+    __builtin_amdgcn_wave_barrier();
+    const float m = st[0].v;
+    float part = 0.0f;
+    for (int e = lane; e < E; e += 64)
+        part += expf(l[e] - m);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1)
+        part += __shfl_xor(part, sh, 64);
+    float p = 0.0f;
+    if (lane < k)
+        p = expf(st[lane].v - m) / part;
+    if (flags & MOE_RENORM) {
+        float ws = p;
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1)
+            ws += __shfl_xor(ws, sh, 64);
+        p = p / ws;
+    }
+    if (lane < k) {
+        idx_out[(size_t)t * k + lane] = st[lane].e;
+        w_out[(size_t)t * k + lane] = p;
+    }
+}
+
+size_t route_batched_ws_bytes(int T, int E) { return (size_t)al256((int64_t)T * E * 4); }
+
+// T > 8: logits into ws (T*E fp32), then top-k.
+int launch_route_batched(const void *x, const void *wr, const float *bias, int T, int H, int E,
+                         int k, unsigned flags, int32_t *idx, float *w, void *ws, hipStream_t s)
+{
+    float *lg = static_cast<float *>(ws);
+    const f16 *xh = static_cast<const f16 *>(x), *wh = static_cast<const f16 *>(wr);
+    const dim3 grid((T + 7) / 8, (E + 8 * RL_WAVES - 1) / (8 * RL_WAVES)), block(RL_WAVES * 64);
+    switch (H) {
+    case 256: hipLaunchKernelGGL(route_logits_kernel<256>, grid, block, 0, s, xh, wh, bias, T, E, lg); break;
+    case 512: hipLaunchKernelGGL(route_logits_kernel<512>, grid, block, 0, s, xh, wh, bias, T, E, lg); break;
+    case 1024: hipLaunchKernelGGL(route_logits_kernel<1024>, grid, block, 0, s, xh, wh, bias, T, E, lg); break;
+    case 2048: hipLaunchKernelGGL(route_logits_kernel<2048>, grid, block, 0, s, xh, wh, bias, T, E, lg); break;
+    default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
+    }
+    MOE_LAUNCH_CHECK("route_logits_kernel");
+    const size_t nb = (E + 63) / 64;
+    const size_t lds = (size_t)RT_WAVES * ((((size_t)E * sizeof(float) + 15) & ~(size_t)15) +
+                                           (nb * 16 + 16) * sizeof(Cand));
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + RT_WAVES - 1) / RT_WAVES),
+                       dim3(RT_WAVES * 64), lds, s, lg, T, E, k, flags, idx, w);
+    MOE_LAUNCH_CHECK("route_topk_kernel");
+    return MOE_OK;
 }
 
 // Small batches (T <= 8) spread over many workgroups.  Workgroup g computes
@@ -356,18 +521,11 @@ static int launch_route_h(const f16 *x, const f16 *wr, const float *bias, int T,
 #define MOE_ROUTE_LAUNCH(TT, NW)                                                                 \
     hipLaunchKernelGGL((route_kernel<H, TT, NW>), dim3((T + TT - 1) / TT), dim3(NW * 64),        \
                        lds_for(TT, NW), s, x, wr, bias, T, E, k, flags, idx, w)
-    if (T <= 8) {
-        // one workgroup of 16 waves
-        if (T <= 1) MOE_ROUTE_LAUNCH(1, 16);
-        else if (T <= 2) MOE_ROUTE_LAUNCH(2, 16);
-        else if (T <= 4) MOE_ROUTE_LAUNCH(4, 16);
-        else MOE_ROUTE_LAUNCH(8, 16);
-    } else {
-        // token tiles of 8 (fewer if the tile would exceed 64 KB of LDS)
-        if (lds_for(8, 4) <= 65536) MOE_ROUTE_LAUNCH(8, 4);
-        else if (lds_for(4, 4) <= 65536) MOE_ROUTE_LAUNCH(4, 4);
-        else MOE_ROUTE_LAUNCH(2, 4);
-    }
+    // T <= 8 (larger batches take launch_route_batched): one workgroup of 16 waves
+    if (T <= 1) MOE_ROUTE_LAUNCH(1, 16);
+    else if (T <= 2) MOE_ROUTE_LAUNCH(2, 16);
+    else if (T <= 4) MOE_ROUTE_LAUNCH(4, 16);
+    else MOE_ROUTE_LAUNCH(8, 16);
 #undef MOE_ROUTE_LAUNCH
     MOE_LAUNCH_CHECK("route_kernel");
     return MOE_OK;

@@ -5,37 +5,54 @@
 
 namespace moe {
 
-// Stable scatter of flat elements [f0, f1) by one wave.  cnt[e] holds the
-// next free sorted position of expert e; a lane's rank among earlier lanes
-// with the same key comes from a readlane sweep, and the counter advances by
-// the group's multiplicity (LDS max of the new end positions).  Out-of-range
-// ids are skipped.
+// Stable scatter of flat elements [f0, f1) by one wave (f1 - f0 <= 64 *
+// WS_GROUPS per call; callers loop).  cnt[e] holds the next free sorted
+// position of expert e.  All keys of the range are loaded first (one memory
+// round trip, not one per group).  Per group of 64 elements, a lane's peers
+// (lanes holding the same key) come from one ballot per key bit; its rank is
+// the number of peers in lower lanes, and the lowest peer advances cnt[key]
+// by the group's multiplicity.  Out-of-range ids are skipped.
+constexpr int WS_GROUPS = 8;
+
 __device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ idx, int f0, int f1,
                                              int E, int *cnt, int32_t *__restrict__ perm,
                                              int32_t *__restrict__ inv_perm, int lane)
 {
-    for (int base = f0; base < f1; base += 64) {
-        const int f = base + lane;
-        int key = (f < f1) ? idx[f] : -1;
-        if ((unsigned)key >= (unsigned)E)
-            key = -1;
-        const bool valid = key >= 0;
-        int rank = 0;
-        const int nval = min(64, f1 - base);
-        for (int i = 0; i < nval; ++i) {
-            int ki = __builtin_amdgcn_readlane(key, i);
-            rank += (ki == key && i < lane) ? 1 : 0;
+    const int kbits = 32 - __builtin_clz((unsigned)max(E - 1, 1));
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base0 = f0; base0 < f1; base0 += 64 * WS_GROUPS) {
+        int keys[WS_GROUPS];
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g) {
+            const int f = base0 + 64 * g + lane;
+            keys[g] = (f < f1) ? idx[f] : -1;
         }
-        int pos = 0;
-        if (valid)
-            pos = cnt[key] + rank;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            atomicMax(&cnt[key], pos + 1);
-            perm[pos] = f;
-            inv_perm[f] = pos;
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g) {
+            const int f = base0 + 64 * g + lane;
+            const int key = keys[g];
+            const bool valid = (unsigned)key < (unsigned)E;
+            uint64_t peers = __ballot(valid);
+            if (peers == 0)
+                continue;   // uniform: nothing left in this group
+            for (int b = 0; b < kbits; ++b) {
+                const bool bit = (key >> b) & 1;
+                const uint64_t m = __ballot(bit);
+                peers &= bit ? m : ~m;
+            }
+            const int rank = __popcll(peers & below);
+            int pos = 0;
+            if (valid)
+                pos = cnt[key] + rank;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                if (rank == 0)
+                    cnt[key] = pos + __popcll(peers);
+                perm[pos] = f;
+                inv_perm[f] = pos;
+            }
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -48,9 +65,18 @@ __device__ __forceinline__ void wave_count_scan(const int32_t *__restrict__ idx,
     for (int e = lane; e < E; e += 64)
         cnt[e] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int f = lane; f < n; f += 64)
-        if ((unsigned)idx[f] < (unsigned)E)
-            atomicAdd(&cnt[idx[f]], 1);
+    for (int f0 = 0; f0 < n; f0 += 64 * WS_GROUPS) {   // keys loaded a batch at a time
+        int keys[WS_GROUPS];
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g) {
+            const int f = f0 + 64 * g + lane;
+            keys[g] = (f < n) ? idx[f] : -1;
+        }
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g)
+            if ((unsigned)keys[g] < (unsigned)E)
+                atomicAdd(&cnt[keys[g]], 1);
+    }
     __builtin_amdgcn_wave_barrier();
     const int per = (E + 63) / 64;
     const int e0 = lane * per;

@@ -29,6 +29,9 @@ int launch_route(const void *, const void *, const float *, int, int, int, int, 
                  int32_t *, float *, hipStream_t);
 size_t permute_ws_bytes(int T, int k, int E);
 size_t route_split_ws_bytes(int T, int E);
+size_t route_batched_ws_bytes(int T, int E);
+int launch_route_batched(const void *, const void *, const float *, int, int, int, int, unsigned,
+                         int32_t *, float *, void *, hipStream_t);
 int launch_route_split(const void *, const void *, const float *, int, int, int, int, unsigned,
                        int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *, void *,
                        hipStream_t);
@@ -51,6 +54,7 @@ int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
 constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
+constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
 constexpr int SHARED_GEMV_MAX_T = 4;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
@@ -172,16 +176,30 @@ static int check_route_args(const char *fn, const void *x_f16, const void *w_rou
     return MOE_OK;
 }
 
+size_t moe_route_workspace_bytes(int T, int E)
+{
+    if (T <= ROUTE_SMALL_MAX_T || E <= 0)
+        return 0;
+    return route_batched_ws_bytes(T, E);
+}
+
 int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T, int H,
-              int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w, hipStream_t stream)
+              int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w, void *ws,
+              size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
     int rc = check_route_args("moe_route", x_f16, w_router_f16, T, H, E, k, flags, topk_idx,
                               topk_w);
     if (rc)
         return rc;
-    return launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
-                        stream);
+    if (T <= ROUTE_SMALL_MAX_T)
+        return launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
+                            stream);
+    const size_t need = moe_route_workspace_bytes(T, E);
+    if (!ws || ws_bytes < need)
+        return set_error(MOE_ENOMEM, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
+    return launch_route_batched(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
+                                topk_w, ws, stream);
 }
 
 size_t moe_route_permute_workspace_bytes(int T, int k, int E)
@@ -190,7 +208,8 @@ size_t moe_route_permute_workspace_bytes(int T, int k, int E)
         return 0;
     if (T > 0 && T <= ROUTE_FUSED_MAX_T)
         return route_split_ws_bytes(T, E);
-    return permute_ws_bytes(T, k, E);
+    // logits of the batched router, then the permutation's scratch
+    return route_batched_ws_bytes(T, E) + permute_ws_bytes(T, k, E);
 }
 
 int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T,
@@ -212,11 +231,15 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
     if (T > 0 && T <= ROUTE_FUSED_MAX_T)
         return launch_route_split(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
                                   topk_w, counts, offsets, perm, inv_perm, ws, stream);
-    rc = launch_route(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
-                      stream);
-    if (rc)
-        return rc;
-    return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, ws, stream);
+    void *pws = nullptr;
+    if (T > 0) {
+        rc = launch_route_batched(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
+                                  topk_w, ws, stream);
+        if (rc)
+            return rc;
+        pws = static_cast<char *>(ws) + route_batched_ws_bytes(T, E);
+    }
+    return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, pws, stream);
 }
 
 size_t moe_permute_workspace_bytes(int T, int k, int E)

@@ -117,7 +117,7 @@ class MoELayer:
                                 b.inv_perm, b.perm_ws, nws, stream)
             return
         A.moe_route(x, self.router, self.bias, T, self.H, self.E, self.k, self.flags,
-                    b.topk_idx, b.topk_w, stream)
+                    b.topk_idx, b.topk_w, b.perm_ws, nws, stream)
         A.moe_permute(b.topk_idx, T, self.k, self.E, b.counts, b.offsets, b.perm, b.inv_perm,
                       b.perm_ws, nws, stream)
 

@@ -72,6 +72,9 @@ def test_compute_calls_reject_before_launch():
         M.moe_route(1, 1, None, 4, 2048, 8, 2, 4, 1, 1, stream=0)   # unknown flag
     assert ei.value.code == M.MOE_EINVAL
     with pytest.raises(M.MoEError) as ei:
+        M.moe_route(1, 1, None, 100, 2048, 64, 8, 0, 1, 1, None, 0, stream=0)  # no logit ws
+    assert ei.value.code == M.MOE_ENOMEM
+    with pytest.raises(M.MoEError) as ei:
         M.moe_permute(1, 10000, 8, 64, 1, 1, 1, 1, None, 0, stream=0)  # workspace missing
     assert ei.value.code == M.MOE_ENOMEM
     with pytest.raises(M.MoEError) as ei:   # y dtype does not match the plan
@@ -100,3 +103,13 @@ def test_pool_create_rejects_bad_profiles():
     with pytest.raises(M.MoEError) as ei:
         M.moe_pool_create(cfg, [1] * 8)
     assert ei.value.code == M.MOE_ECAPACITY
+
+
+def test_route_workspace_sizes():
+    # one-workgroup router up to 8 tokens needs no scratch; above, T x E fp32 logits
+    assert M.moe_route_workspace_bytes(8, 512) == 0
+    assert M.moe_route_workspace_bytes(9, 64) >= 9 * 64 * 4
+    assert M.moe_route_workspace_bytes(4096, 512) == 4096 * 512 * 4
+    # route + permute above 8 tokens: logits, then the permutation's scratch
+    assert (M.moe_route_permute_workspace_bytes(4096, 8, 64)
+            >= M.moe_route_workspace_bytes(4096, 64) + M.moe_permute_workspace_bytes(4096, 8, 64))

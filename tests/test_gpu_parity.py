@@ -17,6 +17,10 @@ from tests.gpu_util import (DEV, WTOL, OracleBlobs, check_close, device_experts,
 
 pytestmark = pytest.mark.gpu
 
+# group size 32 and an intermediate size (192) that leaves the last 256-column
+# tile of the fused gate/up matrix half empty
+G32 = MI.MoEConfig(91, "g32_i192", H=512, E=16, k=4, I=192, g=32)
+
 
 def _np(t):
     return t.detach().cpu().numpy()
@@ -44,7 +48,7 @@ def _numpy_prepack(canon, H, I, g):
         for i in range(4):
             o |= ((w >> (8 * i)) & 0xF) << (4 * i)
             o |= ((w >> (8 * i + 4)) & 0xF) << (16 + 4 * i)
-        return o.view(np.uint8)
+        return o[[0, 2, 1, 3]].view(np.uint8)   # elements 0-7, 16-23, 8-15, 24-31
 
     o = 0
     for b in range(I // 32):
@@ -97,7 +101,9 @@ def test_prepack_layout_and_round_trip():
 def _route_gpu(x, wr, bias, T, H, E, k, flags=0):
     idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, k), dtype=torch.float32, device=DEV)
-    M.moe_route(x, wr, bias, T, H, E, k, flags, idx, w)
+    wsb = M.moe_route_workspace_bytes(T, E)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    M.moe_route(x, wr, bias, T, H, E, k, flags, idx, w, ws, wsb)
     torch.cuda.synchronize()
     return _np(idx), _np(w)
 
@@ -252,7 +258,9 @@ def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
     (MI.OLMOE_DECODE, 1, M.MOE_REGIME_AUTO), (MI.OLMOE_DECODE, 3, M.MOE_REGIME_AUTO),
     (MI.OLMOE_DECODE, 64, M.MOE_REGIME_BATCHED), (MI.OLMOE_DECODE, 512, M.MOE_REGIME_BATCHED),
     (MI.OLMOE_DECODE, 4096, M.MOE_REGIME_BATCHED), (MI.E512, 1, M.MOE_REGIME_AUTO),
-    (MI.E512, 256, M.MOE_REGIME_BATCHED), (MI.E512, 4096, M.MOE_REGIME_BATCHED)],
+    (MI.E512, 256, M.MOE_REGIME_BATCHED), (MI.E512, 4096, M.MOE_REGIME_BATCHED),
+    (G32, 3, M.MOE_REGIME_DECODE), (G32, 300, M.MOE_REGIME_BATCHED),
+    (G32, 8192, M.MOE_REGIME_BATCHED)],
     ids=lambda v: getattr(v, "name", str(v)))
 def test_expert_ffn(cfg, T, regime):
     _ffn_case(cfg, T, regime)
@@ -361,7 +369,7 @@ def _oracle_tokens(cfg, x, toks, layer=0, residual=None, shared=True):
 
 @pytest.mark.parametrize("cfg,T", [(MI.TINY, 16), (MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 64),
                                    (MI.OLMOE_DECODE, 512), (MI.OLMOE_DECODE, 4096),
-                                   (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096)],
+                                   (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096), (G32, 300)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_end_to_end(cfg, T):
     lay = make_layer(cfg, 0)
