@@ -108,15 +108,11 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
     }
     __syncthreads();
 
-    // top-k + softmax: wave w handles tokens w, w+NW, ... (rank-based top-k)
-    Cand *wc = cand + (size_t)wave * nb * 16;
+    // top-k + softmax: wave w handles tokens w, w+NW, ...
     Cand *st = sel + wave * 16;
     for (int tt = wave; tt < nt; tt += NW) {
         const float *l = lg + tt * E;
-        for (int b = 0; b < nb; ++b)
-            block_topk(l, E, k, b, lane, wc + b * k);
-        __builtin_amdgcn_wave_barrier();
-        merge_topk(wc, nb * k, k, lane, st);
+        wave_topk(l, E, k, lane, st, cand + (size_t)wave * nb * 16);
         __builtin_amdgcn_wave_barrier();
         const float m = st[0].v;
         float part = 0.0f;
@@ -256,10 +252,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_topk_kernel(
     for (int e = lane; e < E; e += 64)   // every load of the row in flight at once
         l[e] = lg[e];
     __builtin_amdgcn_wave_barrier();
-    for (int b = 0; b < nb; ++b)
-        block_topk(l, E, k, b, lane, wc + b * k);
-    __builtin_amdgcn_wave_barrier();
-    merge_topk(wc, nb * k, k, lane, st);
+    wave_topk(l, E, k, lane, st, wc);
     __builtin_amdgcn_wave_barrier();
     const float m = st[0].v;
     float part = 0.0f;
@@ -411,16 +404,10 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
 
-    // local top-k of every (token, 64-expert block), spread over the waves
-    for (int tb = wave; tb < T * nb; tb += RSPLIT_EPW) {
-        const int tt = tb / nb, b = tb % nb;
-        block_topk(lg + tt * E, E, k, b, lane, cand + ((size_t)tt * nb + b) * k);
-    }
-    __syncthreads();
-    // merge, softmax and outputs: one wave per token
+    // top-k, softmax and outputs: one wave per token
     for (int tt = wave; tt < T; tt += RSPLIT_EPW) {
         Cand *st = sel + tt * 16;
-        merge_topk(cand + (size_t)tt * nb * k, nb * k, k, lane, st);
+        wave_topk(lg + tt * E, E, k, lane, st, cand + (size_t)tt * nb * 16);
         __builtin_amdgcn_wave_barrier();
         const float m = st[0].v;
         float part = 0.0f;

@@ -120,6 +120,51 @@ struct Cand {
     int e;   // -1: empty slot
 };
 
+// Top-k of one token's E logits by one wave (E <= 64*NV): lane l holds
+// experts l, l+64, ...; k rounds, each taking the best remaining pair by
+// (logit desc, index asc) -- a per-lane scan, then an xor-butterfly
+// reduction under the same strict order, so every lane agrees -- and
+// removing it from its owner lane.  sel[0..k) receives the pairs in order.
+template <int NV>
+__device__ __forceinline__ void wave_topk_nv(const float *l, int E, int k, int lane, Cand *sel)
+{
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = (e < E) ? l[e] : 0.0f;
+    }
+    unsigned live = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        live |= (lane + 64 * i < E) ? (1u << i) : 0u;
+    for (int j = 0; j < k; ++j) {
+        float bv = 0.0f;
+        int be = -1;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + 64 * i;
+            if (((live >> i) & 1u) && (be < 0 || ranks_before(v[i], e, bv, be))) {
+                bv = v[i];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
+            if (oe >= 0 && (be < 0 || ranks_before(ov, oe, bv, be))) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if (lane == 0)
+            sel[j] = Cand{bv, be};
+        if ((be & 63) == lane)
+            live &= ~(1u << (be >> 6));
+    }
+}
+
 // Local top-k of one block of 64 experts of a token, by one wave: lane i
 // holds expert 64b+i, its rank inside the block is the number of block
 // members that rank before it (broadcast reads of the block from LDS, fully
@@ -173,6 +218,27 @@ __device__ __forceinline__ void merge_topk(const Cand *cand, int C, int k, int l
         }
         if (me.e >= 0 && rank < k)
             sel[rank] = me;
+    }
+}
+
+// Top-k of one token's E logits (E <= 1024) by one wave into sel[0..k).
+// Up to two 64-expert blocks: rank-based (no dependent cross-lane chain;
+// scratch holds the blocks' nb*k candidates); above: k argmax rounds.
+__device__ __forceinline__ void wave_topk(const float *l, int E, int k, int lane, Cand *sel,
+                                          Cand *scratch)
+{
+    const int nb = (E + 63) >> 6;
+    if (nb <= 2) {
+        for (int b = 0; b < nb; ++b)
+            block_topk(l, E, k, b, lane, scratch + b * k);
+        __builtin_amdgcn_wave_barrier();
+        merge_topk(scratch, nb * k, k, lane, sel);
+    } else if (nb <= 4) {
+        wave_topk_nv<4>(l, E, k, lane, sel);
+    } else if (nb <= 8) {
+        wave_topk_nv<8>(l, E, k, lane, sel);
+    } else {
+        wave_topk_nv<16>(l, E, k, lane, sel);
     }
 }
 
