@@ -325,9 +325,10 @@ def run_batched(args, torch, M, cfg):
 def run_partial(args, torch, M):
     """Partial residency: 16 OLMoE-shaped layers, C of 64 experts per layer
     resident in HBM slots (+ S spares), the full INT4 source in pinned host
-    memory; per token and layer: route (GPU) -> routed ids to the host ->
-    moe_pool_prepare (misses copied H2D on a side stream) -> expert FFN
-    through the published table -> retire -> combine.  Protocol: `blocks`
+    memory; per token and layer one moe_pool_layer_forward call: route (GPU)
+    -> routed ids to the host -> prepare (misses copied H2D on a side stream)
+    -> expert FFN through the published table -> retire -> combine.
+    Protocol: `blocks`
     fresh pools, each a 64-token warmup then `prompts` x `tokens` tokens."""
     import numpy as np
     import moe_inputs as MI
@@ -349,29 +350,25 @@ def run_partial(args, torch, M):
     bufs = [lay.buffers(1) for lay in lays]
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
     host_ids = torch.empty(cfg.k, dtype=torch.int32, pin_memory=True)
-    ev = torch.cuda.Event()
+    largs = [lay.pool_args(b, host_ids) for lay, b in zip(lays, bufs)]
     stream = torch.cuda.current_stream()
+    step = M.PoolStats()
     trace_layers, trace_ids = [], []
 
     def token(x0, record):
-        x = x0
+        # one native call per layer: route, ids to the host, prepare (misses
+        # copied), expert FFN through the published table, retire, combine
+        x = x0.data_ptr()
         misses = 0
-        for l, lay in enumerate(lays):
-            b = bufs[l]
-            lay.route_permute(x, b)
-            host_ids.copy_(b.topk_idx.view(-1), non_blocking=True)
-            ev.record(stream)
-            ev.synchronize()
-            ids = host_ids.numpy()
-            tab, st = M.moe_pool_prepare(pool, l, ids, cfg.k, stream)
-            misses += st.misses
+        for l in range(L):
+            a = largs[l]
+            out = act[l & 1].data_ptr()
+            a.x_f16, a.residual_f16, a.out_f16 = x, x, out
+            M.moe_pool_layer_forward(pool, l, a, stream, step)
+            misses += step.misses
             if record:
                 trace_layers.append(l)
-                trace_ids.append(ids.copy())
-            lay.experts(x, b, table=tab)
-            M.moe_pool_retire(pool, l, stream)
-            out = act[l & 1]
-            lay.combine(b, residual=x, out=out)
+                trace_ids.append(host_ids.numpy().copy())
             x = out
         return misses
 

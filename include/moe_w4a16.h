@@ -300,7 +300,9 @@ int moe_pool_create(const moe_pool_config *cfg, const void *const *pinned_src,
  * copied to the host) resident and publish the layer's next generation.
  * Misses are copied H2D on the side stream into spare slots (waiting for the
  * retirement of earlier readers of those slots); the compute stream is made
- * to wait for the copies and the table update.  *d_table_out receives the
+ * to wait for the copies and the table update (a call whose experts are all
+ * resident republishes the current table: nothing copied, nothing awaited).
+ * *d_table_out receives the
  * device array of E blob pointers to pass to moe_expert_ffn_w4a16 on
  * `compute` (NULL for non-resident experts).  `step` (may be NULL) gets this
  * call's counters (hits/misses/evictions/h2d_bytes; generation = new one).
@@ -317,6 +319,45 @@ int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
  * layer's current generation has been issued; slots evicted by it become
  * reusable once those kernels finish.  MOE_ESTATE if nothing to retire. */
 int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute);
+
+/*
+ * One pooled MoE layer for a small batch -- the decode loop of a partially
+ * resident model -- in one host call, with the same readings as the calls it
+ * chains: moe_route_permute on `stream`; the T*k routed ids copied into
+ * host_ids (pinned host memory) and waited for (this call blocks the calling
+ * thread until they arrive); moe_pool_prepare on this layer; the routed
+ * expert FFN (moe_expert_ffn_w4a16 with the published table and `regime`);
+ * moe_pool_retire; moe_combine into out_f16.  E is the pool's expert count.
+ * Every buffer is the caller's, sized as for those calls (route_ws:
+ * moe_route_permute_workspace_bytes, zero-filled before its first use;
+ * y / ffn_ws: moe_expert_ffn_plan).  Errors are those of the chained calls;
+ * the first one stops the chain (a failure in prepare leaves the layer's
+ * previous generation published).
+ */
+typedef struct {
+    const void *x_f16;          /* device fp16 [T][H] */
+    const void *w_router_f16;   /* device fp16 [E][H] */
+    const float *logit_bias;    /* device fp32 [E] or NULL */
+    int T, H, I, k, group;
+    unsigned flags;             /* MOE_RENORM or 0 */
+    int32_t *topk_idx;          /* device [T][k] */
+    float *topk_w;              /* device [T][k] */
+    int32_t *counts, *offsets, *perm, *inv_perm;   /* device, as moe_permute */
+    void *route_ws;
+    size_t route_ws_bytes;
+    int regime;                 /* MOE_REGIME_* */
+    void *y;
+    int y_dtype, y_slices;
+    void *ffn_ws;
+    size_t ffn_ws_bytes;
+    const float *shared_f32;    /* device fp32 [T][H] or NULL */
+    const void *residual_f16;   /* device fp16 [T][H] or NULL */
+    void *out_f16;              /* device fp16 [T][H] */
+    int32_t *host_ids;          /* pinned host int32 [T*k] */
+} moe_pool_layer_args;
+
+int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args *args,
+                           hipStream_t stream, moe_pool_stats_t *step);
 
 /* Cumulative counters since creation or the last reset. */
 int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out);

@@ -14,8 +14,9 @@ __all__ = [
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "moe_pool_create",
-    "moe_pool_prepare", "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
+    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "PoolLayerArgs",
+    "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_retire",
+    "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
 ]
 
@@ -32,6 +33,7 @@ EXPORTS = [
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_pool_create", "moe_pool_prepare",
+    "moe_pool_layer_forward",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
 ]
 
@@ -54,6 +56,20 @@ class PoolStats(C.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class PoolLayerArgs(C.Structure):
+    """moe_pool_layer_args: device pointers as ints, host_ids a pinned host address."""
+    _fields_ = [("x_f16", C.c_void_p), ("w_router_f16", C.c_void_p), ("logit_bias", C.c_void_p),
+                ("T", C.c_int), ("H", C.c_int), ("I", C.c_int), ("k", C.c_int),
+                ("group", C.c_int), ("flags", C.c_uint),
+                ("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("counts", C.c_void_p),
+                ("offsets", C.c_void_p), ("perm", C.c_void_p), ("inv_perm", C.c_void_p),
+                ("route_ws", C.c_void_p), ("route_ws_bytes", C.c_size_t),
+                ("regime", C.c_int), ("y", C.c_void_p), ("y_dtype", C.c_int),
+                ("y_slices", C.c_int), ("ffn_ws", C.c_void_p), ("ffn_ws_bytes", C.c_size_t),
+                ("shared_f32", C.c_void_p), ("residual_f16", C.c_void_p),
+                ("out_f16", C.c_void_p), ("host_ids", C.c_void_p)]
 
 
 _lib = None
@@ -82,6 +98,8 @@ def _declare(L):
         "moe_combine": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "moe_pool_create": (i32, [C.POINTER(PoolConfig), vp, C.POINTER(vp)]),
         "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
+        "moe_pool_layer_forward": (i32, [vp, i32, C.POINTER(PoolLayerArgs), vp,
+                                         C.POINTER(PoolStats)]),
         "moe_pool_retire": (i32, [vp, i32, vp]),
         "moe_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
         "moe_pool_reset": (i32, [vp]),
@@ -244,6 +262,14 @@ def moe_pool_prepare(pool, layer, host_ids, n, compute=None):
     _check(lib().moe_pool_prepare(pool, layer, host_ids, n, _s(compute), C.byref(tab),
                                   C.byref(st)))
     return tab.value, st
+
+
+def moe_pool_layer_forward(pool, layer, args: PoolLayerArgs, stream=None, step=None):
+    """Runs one pooled layer (see PoolLayerArgs); returns this step's PoolStats
+    (`step`, if given, is filled and returned)."""
+    st = PoolStats() if step is None else step
+    _check(lib().moe_pool_layer_forward(pool, layer, C.byref(args), _s(stream), C.byref(st)))
+    return st
 
 
 def moe_pool_retire(pool, layer, compute=None):

@@ -179,33 +179,37 @@ class SlotPool {
             L.slot_of[m] = sp;
             L.last[m] = ++clk;
         }
-        // copies of the misses into spare slots (side stream, after earlier
-        // readers of those slots retired); table of the new generation
-        int rc = be.wait_retired(l);
-        if (rc)
-            return rc;
-        for (size_t i = 0; i < misses.size(); ++i) {
-            rc = be.copy(l, be.slot_ptr(l, fill_slot[i]), src[(size_t)l * E + misses[i]],
-                         (size_t)cfg.expert_bytes);
+        const void *const *dtab = L0.table;
+        if (!misses.empty()) {
+            // copies of the misses into spare slots (side stream, after earlier
+            // readers of those slots retired); table of the new generation
+            int rc = be.wait_retired(l);
             if (rc)
-                return rc;   // nothing published: previous generation and counters intact
+                return rc;
+            for (size_t i = 0; i < misses.size(); ++i) {
+                rc = be.copy(l, be.slot_ptr(l, fill_slot[i]), src[(size_t)l * E + misses[i]],
+                             (size_t)cfg.expert_bytes);
+                if (rc)
+                    return rc;   // nothing published: previous generation and counters intact
+            }
+            std::vector<const void *> tab(E, nullptr);
+            for (int e = 0; e < E; ++e)
+                if (L.slot_of[e] >= 0)
+                    tab[e] = be.slot_ptr(l, L.slot_of[e]);
+            const int nbuf = L.cur_buf ^ 1;
+            rc = be.upload_table(l, nbuf, tab.data(), &dtab);
+            if (rc)
+                return rc;
+            rc = be.publish(l, compute);
+            if (rc)
+                return rc;
+            L.cur_buf = nbuf;
         }
-        std::vector<const void *> tab(E, nullptr);
-        for (int e = 0; e < E; ++e)
-            if (L.slot_of[e] >= 0)
-                tab[e] = be.slot_ptr(l, L.slot_of[e]);
-        const int nbuf = L.cur_buf ^ 1;
-        const void *const *dtab = nullptr;
-        rc = be.upload_table(l, nbuf, tab.data(), &dtab);
-        if (rc)
-            return rc;
-        rc = be.publish(l, compute);
-        if (rc)
-            return rc;
+        // (all hits: the new generation holds the same experts in the same
+        // slots, so the published table is the current one, unchanged)
         // commit: the victims' slots become spares (reusable after retirement)
         for (int vs : victim_slot)
             L.expert_in[vs] = -1;
-        L.cur_buf = nbuf;
         L.table = dtab;
         L.prepared = true;
         L0 = std::move(L);

@@ -18,6 +18,7 @@ struct HipPoolBackend {
     const void **staging = nullptr;      // pinned host [L][2][E]
     hipStream_t side = nullptr;
     std::vector<hipEvent_t> retire_ev, copies_ev, upload_ev;
+    hipEvent_t ids_ev = nullptr;         // routed ids on the host (moe_pool_layer_forward)
     std::vector<char> retired, uploaded;
 
     int init(const moe_pool_config &c)
@@ -44,6 +45,7 @@ struct HipPoolBackend {
         for (auto *v : {&retire_ev, &copies_ev, &upload_ev})
             for (auto &ev : *v)
                 MOE_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        MOE_HIP_TRY(hipEventCreateWithFlags(&ids_ev, hipEventDisableTiming));
         return MOE_OK;
     }
     void *slot_ptr(int l, int s) { return slots + ((size_t)l * nslots + s) * cfg.expert_bytes; }
@@ -101,6 +103,9 @@ struct HipPoolBackend {
             for (auto &ev : *v)
                 if (ev)
                     (void)hipEventDestroy(ev);
+        if (ids_ev)
+            (void)hipEventDestroy(ids_ev);
+        ids_ev = nullptr;
         if (side)
             (void)hipStreamDestroy(side);
         if (staging)
@@ -149,6 +154,49 @@ int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
     if (!pool)
         return moe::set_error(MOE_EINVAL, "moe_pool_prepare: null pool");
     return pool->p.prepare(layer, host_ids, n, compute, d_table_out, step);
+}
+
+int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args *a,
+                           hipStream_t stream, moe_pool_stats_t *step)
+{
+    moe::clear_error();
+    if (!pool || !a || !a->host_ids)
+        return moe::set_error(MOE_EINVAL, "moe_pool_layer_forward: null argument");
+    auto &P = pool->p;
+    if (layer < 0 || layer >= P.cfg.layers)
+        return moe::set_error(MOE_EINVAL, "moe_pool_layer_forward: bad layer %d", layer);
+    const int E = P.cfg.experts;
+    const int n = a->T * a->k;
+    int rc = moe_route_permute(a->x_f16, a->w_router_f16, a->logit_bias, a->T, a->H, E, a->k,
+                               a->flags, a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm,
+                               a->inv_perm, a->route_ws, a->route_ws_bytes, stream);
+    if (rc)
+        return rc;
+    if (n > 0) {
+        hipError_t err = hipMemcpyAsync(a->host_ids, a->topk_idx, (size_t)n * sizeof(int32_t),
+                                        hipMemcpyDeviceToHost, stream);
+        if (err == hipSuccess)
+            err = hipEventRecord(P.be.ids_ev, stream);
+        if (err == hipSuccess)
+            err = hipEventSynchronize(P.be.ids_ev);
+        if (err != hipSuccess)
+            return moe::set_error(MOE_EHIP, "moe_pool_layer_forward: routed ids: %s",
+                                  hipGetErrorString(err));
+    }
+    const void *const *table = nullptr;
+    rc = P.prepare(layer, a->host_ids, n, stream, &table, step);
+    if (rc)
+        return rc;
+    rc = moe_expert_ffn_w4a16(a->x_f16, a->perm, a->offsets, table, a->T, a->H, a->I, E, a->k,
+                              a->group, a->regime, a->y, a->y_dtype, a->y_slices, a->ffn_ws,
+                              a->ffn_ws_bytes, stream);
+    const int rr = P.retire(layer, stream);   // the generation is released even on failure
+    if (rc)
+        return rc;
+    if (rr)
+        return rr;
+    return moe_combine(a->y, a->y_dtype, a->y_slices, a->inv_perm, a->topk_w, a->shared_f32,
+                       a->residual_f16, a->T, a->H, a->k, a->out_f16, stream);
 }
 
 int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute)

@@ -137,6 +137,23 @@ class MoELayer:
                       b.T, self.H, self.k, out, stream)
         return out
 
+    def pool_args(self, b: LayerBuffers, host_ids):
+        """PoolLayerArgs for moe_pool_layer_forward with this layer's weights and
+        b's buffers; x_f16 / residual_f16 / out_f16 are set per call."""
+        if self.shared is not None:
+            raise ValueError("pooled layers carry no shared expert")
+        z = lambda t: 0 if t is None else t.data_ptr()
+        a = A.PoolLayerArgs()
+        a.w_router_f16, a.logit_bias = z(self.router), z(self.bias)
+        a.T, a.H, a.I, a.k, a.group, a.flags = b.T, self.H, self.I, self.k, self.g, self.flags
+        a.topk_idx, a.topk_w, a.counts = z(b.topk_idx), z(b.topk_w), z(b.counts)
+        a.offsets, a.perm, a.inv_perm = z(b.offsets), z(b.perm), z(b.inv_perm)
+        a.route_ws, a.route_ws_bytes = z(b.perm_ws), 0 if b.perm_ws is None else b.perm_ws.numel()
+        a.regime, a.y, a.y_dtype, a.y_slices = b.regime, z(b.y), b.y_dtype, b.y_slices
+        a.ffn_ws, a.ffn_ws_bytes = z(b.ffn_ws), 0 if b.ffn_ws is None else b.ffn_ws.numel()
+        a.host_ids = host_ids.data_ptr()
+        return a
+
     def forward(self, x, b: LayerBuffers, residual=None, out=None, stream=None):
         self.route_permute(x, b, stream)
         self.experts(x, b, stream=stream)

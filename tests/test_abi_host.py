@@ -113,3 +113,11 @@ def test_route_workspace_sizes():
     # route + permute above 8 tokens: logits, then the permutation's scratch
     assert (M.moe_route_permute_workspace_bytes(4096, 8, 64)
             >= M.moe_route_workspace_bytes(4096, 64) + M.moe_permute_workspace_bytes(4096, 8, 64))
+
+
+def test_pool_layer_forward_rejects_null_arguments():
+    # validation happens on the host before anything is launched
+    args = M.PoolLayerArgs()
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_pool_layer_forward(None, 0, args, stream=0)
+    assert ei.value.code == M.MOE_EINVAL

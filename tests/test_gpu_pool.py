@@ -141,3 +141,46 @@ def test_pooled_decode_equals_resident_decode():
         assert M.moe_pool_stats(pool).h2d_bytes == misses * total
     finally:
         M.moe_pool_destroy(pool)
+
+
+def test_native_pooled_layer_equals_resident_decode():
+    """moe_pool_layer_forward (route, ids to the host, prepare, FFN, retire,
+    combine in one call) gives the bits of the resident decode, and its
+    counters match the pool's cumulative ones."""
+    cfg = MI.PARTIAL
+    L, steps = 3, 6
+    say("native pooled layer L=%d steps=%d" % (L, steps))
+    src, devs, total = _pinned_source(cfg, L)
+    pool = _make_pool(src, cfg, L, cfg.capacity, cfg.spares, 3, total)
+    lays = []
+    for l in range(L):
+        b = MI.zipf_bias(cfg, l)
+        lays.append(MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, f16(MI.gen_router(cfg, l)),
+                             blob_table(devs[l]), torch.from_numpy(b).to(DEV), device=DEV))
+    bref = [lay.buffers(1) for lay in lays]
+    bpool = [lay.buffers(1) for lay in lays]
+    host_ids = torch.empty(cfg.k, dtype=torch.int32, pin_memory=True)
+    args = [lay.pool_args(b, host_ids) for lay, b in zip(lays, bpool)]
+    stream = torch.cuda.current_stream()
+    misses = 0
+    try:
+        for s in range(steps):
+            x0 = f16(MI.gen_prompt_token(cfg, 1, s))
+            xr, xp = x0, x0
+            for l, lay in enumerate(lays):
+                outr = lay.forward(xr, bref[l], residual=xr, out=torch.empty_like(xr))
+                outp = torch.empty_like(xp)
+                a = args[l]
+                a.x_f16, a.residual_f16, a.out_f16 = xp.data_ptr(), xp.data_ptr(), outp.data_ptr()
+                st = M.moe_pool_layer_forward(pool, l, a, stream)
+                misses += st.misses
+                assert np.array_equal(host_ids.numpy(), bpool[l].topk_idx.cpu().numpy().ravel())
+                torch.cuda.synchronize()
+                assert torch.equal(bpool[l].topk_idx, bref[l].topk_idx)
+                assert torch.equal(outp.view(torch.int16), outr.view(torch.int16)), (s, l)
+                xr, xp = outr, outp
+        assert misses > 0
+        tot = M.moe_pool_stats(pool)
+        assert tot.misses == misses and tot.h2d_bytes == misses * total
+    finally:
+        M.moe_pool_destroy(pool)

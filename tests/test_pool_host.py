@@ -104,10 +104,12 @@ def test_pool_matches_simulator_and_tables_are_complete(L, shift):
         for e, ptr in enumerate(t):
             if ptr is not None:
                 assert np.array_equal(P.slot_bytes(ptr), P.src[l, e])
-        # the previous generation's table is untouched by this prepare
+        # the previous generation's table is untouched by this prepare; a
+        # generation with misses gets a table of its own, an all-hit one
+        # republishes the current table (same experts, same slots)
         if int(l) in prev:
             old_addr, old_entries = prev[int(l)]
-            assert old_addr != tab
+            assert (old_addr != tab) == (misses[i] > 0)
             assert P.table(old_addr) == old_entries
         # evicted experts are gone from the new table
         for v in el[i]:
