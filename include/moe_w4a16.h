@@ -205,7 +205,9 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
  *   perm, offsets  device, from moe_permute
  *   d_expert_blobs device array of E device pointers to prepacked blobs
  *                  (moe_prepack_experts); an entry may be NULL only for an
- *                  expert no token routes to
+ *                  expert no token routes to, except in the DECODE regime,
+ *                  where a routed expert with a NULL entry is skipped (its y
+ *                  rows are left unwritten for another launch to fill)
  *   y              device output, layout from moe_expert_ffn_plan; y_dtype
  *                  and y_slices must equal the plan's (MOE_EINVAL otherwise)
  *   ws             device scratch of the plan's size (may be NULL if 0)
@@ -328,6 +330,10 @@ int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute);
  * thread until they arrive); moe_pool_prepare on this layer; the routed
  * expert FFN (moe_expert_ffn_w4a16 with the published table and `regime`);
  * moe_pool_retire; moe_combine into out_f16.  E is the pool's expert count.
+ * When the routed set has both hits and misses and the decode kernel runs,
+ * the hits are computed first, on the previous generation's table (where
+ * every hit already sits in its slot and no miss appears), while the misses
+ * are copied; a second launch on the new table then computes the misses.
  * Every buffer is the caller's, sized as for those calls (route_ws:
  * moe_route_permute_workspace_bytes, zero-filled before its first use;
  * y / ffn_ws: moe_expert_ffn_plan).  Errors are those of the chained calls;

@@ -109,9 +109,9 @@ __device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *
 template <int H, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs, int I, int E,
-    int k, int g, int ntk, int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds,
-    float *__restrict__ y)
+    const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
+    const uint8_t *const *__restrict__ skip, int I, int E, int k, int g, int ntk,
+    int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, float *__restrict__ y)
 {
     constexpr int NK = H / 32;                 // input chunks of gate/up rows
     constexpr int CPW = NK / NW;               // chunks per wave
@@ -144,6 +144,10 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     if (wave == 0) {
         const uint8_t *bp = nullptr;
         int e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &bp);
+        // an expert without weights in the table, or one that `skip` lists
+        // (done by an earlier launch), is left to another launch
+        if (e >= 0 && (bp == nullptr || (skip != nullptr && skip[e] != nullptr)))
+            e = -1;
         if (lane == 0) {
             s_e = e;
             s_blob = bp;
@@ -244,17 +248,21 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
 template <int H>
 static void launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
-                            const int32_t *offsets, const uint8_t *const *blobs, int I, int E,
-                            int k, int g, int ntk, const DevLayout &L, float *y)
+                            const int32_t *offsets, const uint8_t *const *blobs,
+                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
+                            const DevLayout &L, float *y)
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
     hipLaunchKernelGGL((ffn_decode_kernel<H, NW>), grid, dim3(NW * 64), 0, s, x, perm, offsets,
-                       blobs, I, E, k, g, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y);
+                       blobs, skip, I, E, k, g, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y);
 }
 
+// skip (may be null): a device table of E pointers; experts with a non-null
+// entry there are not computed (an earlier launch did them).  Experts with a
+// null entry in `blobs` are not computed either.
 int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
-                      const void *const *blobs, int T, int H, int I, int E, int k, int g,
-                      float *y, hipStream_t s)
+                      const void *const *blobs, const void *const *skip, int T, int H, int I,
+                      int E, int k, int g, float *y, hipStream_t s)
 {
     const int ntk = T * k;
     if (ntk == 0)
@@ -263,11 +271,12 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
     dim3 grid(I / 32, (unsigned)min(E, ntk));
     const f16 *xh = static_cast<const f16 *>(x);
     const uint8_t *const *b = reinterpret_cast<const uint8_t *const *>(blobs);
+    const uint8_t *const *sk = reinterpret_cast<const uint8_t *const *>(skip);
     switch (H) {
-    case 256: launch_decode_h<256>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
-    case 512: launch_decode_h<512>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
-    case 1024: launch_decode_h<1024>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
-    case 2048: launch_decode_h<2048>(grid, s, xh, perm, offsets, b, I, E, k, g, ntk, L, y); break;
+    case 256: launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 512: launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 1024: launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 2048: launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
     MOE_LAUNCH_CHECK("ffn_decode_kernel");

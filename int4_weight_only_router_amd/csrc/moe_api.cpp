@@ -37,8 +37,8 @@ int launch_route_split(const void *, const void *, const float *, int, int, int,
                        hipStream_t);
 int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
                    void *, hipStream_t);
-int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *, int,
-                      int, int, int, int, int, float *, hipStream_t);
+int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
+                      const void *const *, int, int, int, int, int, int, float *, hipStream_t);
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
                        int, int, int, int, int, void *, void *, hipStream_t);
@@ -311,7 +311,8 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
         return set_error(MOE_ENOMEM, "moe_expert_ffn_w4a16: workspace %zu < %zu bytes", ws_bytes,
                          need);
     if (r == MOE_REGIME_DECODE)
-        return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group,
+        return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
+                                 group,
                                  static_cast<float *>(y), stream);
     return launch_ffn_batched(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
                               stream);

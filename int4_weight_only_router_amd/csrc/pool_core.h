@@ -44,6 +44,7 @@ class SlotPool {
         std::vector<int> expert_in;      // slot -> expert or -1
         int cur_buf = 0;
         bool prepared = false;
+        bool publish_pending = false;   // prepared with the compute-stream wait deferred
         const void *const *table = nullptr;
     };
     std::vector<Layer> layers;
@@ -106,8 +107,12 @@ class SlotPool {
         return be.sync();
     }
 
+    // defer_publish: the compute stream is not yet made to wait for the
+    // copies; the caller enqueues work that reads only the previous
+    // generation's experts first, then calls publish().
     int prepare(int l, const int32_t *ids, int n, hipStream_t compute,
-                const void *const **table_out, moe_pool_stats_t *step)
+                const void *const **table_out, moe_pool_stats_t *step,
+                bool defer_publish = false)
     {
         if (l < 0 || l >= cfg.layers || n < 0 || (n > 0 && !ids) || !table_out)
             return set_error(MOE_EINVAL, "moe_pool_prepare: bad arguments");
@@ -200,9 +205,12 @@ class SlotPool {
             rc = be.upload_table(l, nbuf, tab.data(), &dtab);
             if (rc)
                 return rc;
-            rc = be.publish(l, compute);
-            if (rc)
-                return rc;
+            if (!defer_publish) {
+                rc = be.publish(l, compute);
+                if (rc)
+                    return rc;
+            }
+            L.publish_pending = defer_publish;
             L.cur_buf = nbuf;
         }
         // (all hits: the new generation holds the same experts in the same
@@ -231,13 +239,29 @@ class SlotPool {
         return MOE_OK;
     }
 
+    // Makes `compute` wait for the copies of a deferred prepare (no-op otherwise).
+    int publish(int l, hipStream_t compute)
+    {
+        Layer &L = layers[l];
+        if (!L.publish_pending)
+            return MOE_OK;
+        int rc = be.publish(l, compute);
+        if (rc)
+            return rc;
+        L.publish_pending = false;
+        return MOE_OK;
+    }
+
     int retire(int l, hipStream_t compute)
     {
         if (l < 0 || l >= cfg.layers)
             return set_error(MOE_EINVAL, "moe_pool_retire: bad layer %d", l);
         if (!layers[l].prepared)
             return set_error(MOE_ESTATE, "moe_pool_retire: layer %d has nothing to retire", l);
-        int rc = be.retire(l, compute);
+        int rc = publish(l, compute);   // a deferred publish never outlives its generation
+        if (rc)
+            return rc;
+        rc = be.retire(l, compute);
         if (rc)
             return rc;
         layers[l].prepared = false;

@@ -123,6 +123,11 @@ struct HipPoolBackend {
 
 }  // namespace moe
 
+namespace moe {
+int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
+                      const void *const *, int, int, int, int, int, int, float *, hipStream_t);
+}
+
 struct moe_pool {
     moe::SlotPool<moe::HipPoolBackend> p;
 };
@@ -183,13 +188,40 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
             return moe::set_error(MOE_EHIP, "moe_pool_layer_forward: routed ids: %s",
                                   hipGetErrorString(err));
     }
+    // Hits first: every routed expert that was already resident is in the
+    // previous generation's table (same slot), a missed one is not, so the
+    // decode FFN of the hits runs on that table while the misses are being
+    // copied; after the copies, a second launch on the new table computes
+    // only the experts the previous one lacked.
+    const void *const *old_table = P.layers[layer].table;
     const void *const *table = nullptr;
-    rc = P.prepare(layer, a->host_ids, n, stream, &table, step);
+    moe_pool_stats_t st{};
+    rc = P.prepare(layer, a->host_ids, n, stream, &table, &st, /*defer_publish=*/true);
     if (rc)
         return rc;
-    rc = moe_expert_ffn_w4a16(a->x_f16, a->perm, a->offsets, table, a->T, a->H, a->I, E, a->k,
-                              a->group, a->regime, a->y, a->y_dtype, a->y_slices, a->ffn_ws,
-                              a->ffn_ws_bytes, stream);
+    if (step)
+        *step = st;
+    int resolved = 0;
+    rc = moe_expert_ffn_plan(a->T, a->H, a->I, E, a->k, a->group, a->regime, &resolved, nullptr,
+                             nullptr, nullptr);
+    const bool split = !rc && st.misses > 0 && st.hits > 0 && resolved == MOE_REGIME_DECODE;
+    if (split) {
+        rc = moe_expert_ffn_w4a16(a->x_f16, a->perm, a->offsets, old_table, a->T, a->H, a->I, E,
+                                  a->k, a->group, a->regime, a->y, a->y_dtype, a->y_slices,
+                                  a->ffn_ws, a->ffn_ws_bytes, stream);
+        if (!rc)
+            rc = P.publish(layer, stream);
+        if (!rc)
+            rc = moe::launch_ffn_decode(a->x_f16, a->perm, a->offsets, table, old_table, a->T,
+                                        a->H, a->I, E, a->k, a->group,
+                                        static_cast<float *>(a->y), stream);
+    } else if (!rc) {
+        rc = P.publish(layer, stream);
+        if (!rc)
+            rc = moe_expert_ffn_w4a16(a->x_f16, a->perm, a->offsets, table, a->T, a->H, a->I, E,
+                                      a->k, a->group, a->regime, a->y, a->y_dtype, a->y_slices,
+                                      a->ffn_ws, a->ffn_ws_bytes, stream);
+    }
     const int rr = P.retire(layer, stream);   // the generation is released even on failure
     if (rc)
         return rc;
