@@ -23,7 +23,10 @@
 // Workgroups are dealt to the 8 XCDs round-robin by id, so workgroup i works
 // for XCD i mod 8, and each XCD takes a contiguous range of row tiles with all
 // their column tiles: the row tile's activations and an expert's weight
-// blocks are then re-read from that XCD's L2 instead of from HBM.
+// blocks are then re-read from that XCD's L2 instead of from HBM.  A
+// workgroup first lists its items (expert, rows, source rows, blob) in LDS,
+// then runs them as one stream of K-steps, so the loads of the next item
+// start while the current one finishes and stores its results.
 //
 // Modes
 //  GATEUP_W4 : A = x rows gathered through perm (token = perm[p] / k),
@@ -60,76 +63,6 @@ struct GemmArgs {
     int ldo;                     // leading dim of the output (I for h, H for y/out)
     void *out;
 };
-
-// Row tiles of BM rows over all experts (offsets) or one implicit expert.
-__device__ __forceinline__ int count_row_tiles(const int32_t *__restrict__ offsets, int E,
-                                               int rows, int BM, int lane)
-{
-    if (offsets == nullptr)
-        return (rows + BM - 1) / BM;
-    int tot = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        int nt = 0;
-        if (e < E)
-            nt = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-#pragma unroll
-        for (int st = 32; st >= 1; st >>= 1)
-            nt += __shfl_xor(nt, st, 64);
-        tot += nt;
-    }
-    return tot;
-}
-
-// Expert and row range of row tile `target` (tiles numbered expert by expert).
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int rows,
-                                          int BM, int target, int lane, int &e_out, int &p0,
-                                          int &p1)
-{
-    if (offsets == nullptr) {
-        const int nt = (rows + BM - 1) / BM;
-        if (target >= nt)
-            return false;
-        e_out = 0;
-        p0 = target * BM;
-        p1 = min(rows, p0 + BM);
-        return true;
-    }
-    int seen = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        int c = 0, o = 0;
-        if (e < E) {
-            o = offsets[e];
-            c = offsets[e + 1] - o;
-        }
-        const int nt = (c + BM - 1) / BM;
-        int incl = nt;
-#pragma unroll
-        for (int st = 1; st < 64; st <<= 1) {
-            int v = __shfl_up(incl, st, 64);
-            if (lane >= st)
-                incl += v;
-        }
-        const int total = __shfl(incl, 63, 64);
-        if (seen + total > target) {
-            const int excl = incl - nt;
-            const bool mine = (seen + excl <= target) && (target < seen + incl);
-            const uint64_t m = __ballot(mine);
-            const int src = __ffsll((long long)m) - 1;
-            const int te = __shfl(e, src, 64);
-            const int to = __shfl(o, src, 64);
-            const int tc = __shfl(c, src, 64);
-            const int tx = __shfl(excl, src, 64);
-            e_out = te;
-            p0 = to + (target - seen - tx) * BM;
-            p1 = min(to + tc, p0 + BM);
-            return true;
-        }
-        seen += total;
-    }
-    return false;
-}
 
 // One dword of 8 nibbles (device order) times its group scale -> the 8 fp16
 // B-operand values of one lane for one 16-K step, fp16(q * s) exactly.  OR-ing
@@ -417,6 +350,20 @@ __device__ __forceinline__ float swiglu_fast(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// Per-workgroup item record (LDS): expert, row range, column tile, blob.
+struct W4Item {
+    int e, p0, p1, nt;
+    const uint8_t *blob;
+};
+constexpr int W4_MAXI = 16;   // items listed per batch
+
+template <int MF>
+constexpr size_t w4_lds_total()
+{
+    return w4_lds_bytes<MF>() + (size_t)W4_MAXI * sizeof(W4Item) +
+           (size_t)W4_MAXI * 32 * MF * sizeof(int);
+}
+
 template <int MODE, int MF>
 __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
 {
@@ -429,7 +376,13 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
     using St = W4Stage<MF>;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_tiles, s_e, s_p0, s_p1;
+    W4Item *items = reinterpret_cast<W4Item *>(smem + (size_t)W4_NS * St::BYTES);   // [MAXI]
+    int *srcs = reinterpret_cast<int *>(items + W4_MAXI);                            // [MAXI][BM]
+    // expert offsets and first row tile of each expert; built in the stage
+    // memory before any load targets it
+    int *s_off = reinterpret_cast<int *>(smem);       // [E+1]
+    int *s_ts = s_off + (a.E + 1);                    // [E+1]
+    __shared__ int s_wsum[W4_WAVES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -438,80 +391,144 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
     const int half = lane >> 5;
     const int fcol = (col & 7) ^ ((col >> 3) & 1);   // swizzle of rows m*32 + col
     const int gshift = __builtin_ctz((unsigned)a.g);
+    const int E = a.E;
+    const int K = a.K;
+    const int nk = K / BK;
+    const int NT = (a.nblk + W4_WAVES - 1) / W4_WAVES;
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-    if (wave == 0) {
-        const int R = count_row_tiles(a.offsets, a.E, a.rows, BM, lane);
-        if (lane == 0)
-            s_tiles = R;
-    }
-    __syncthreads();
-    const int R = s_tiles;
-    const int NT = (a.nblk + W4_WAVES - 1) / W4_WAVES;
+    // row tiles per expert and their exclusive scan (E <= 2 * W4_T)
+    auto build_tiles = [&]() {
+        const int e0 = 2 * tid;
+        int c[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                const int o = a.offsets[e];
+                s_off[e] = o;
+                c[i] = (a.offsets[e + 1] - o + BM - 1) / BM;
+            }
+        }
+        if (tid == 0)
+            s_off[E] = a.offsets[E];
+        const int t = c[0] + c[1];
+        int incl = t;
+#pragma unroll
+        for (int st = 1; st < 64; st <<= 1) {
+            const int v = __shfl_up(incl, st, 64);
+            if (lane >= st)
+                incl += v;
+        }
+        if (lane == 63)
+            s_wsum[wave] = incl;
+        __syncthreads();
+        int pre = 0;
+        for (int w = 0; w < wave; ++w)
+            pre += s_wsum[w];
+        const int excl = pre + incl - t;
+        if (e0 < E)
+            s_ts[e0] = excl;
+        if (e0 + 1 < E)
+            s_ts[e0 + 1] = excl + c[0];
+        if (tid == W4_T - 1)
+            s_ts[E] = pre + incl;
+        __syncthreads();
+    };
+
+    build_tiles();
+    const int R = s_ts[E];
     const int xcd = blockIdx.x % NXCD;
     const int G = gridDim.x / NXCD;
     const int r_lo = (int)((int64_t)R * xcd / NXCD);
     const int r_hi = (int)((int64_t)R * (xcd + 1) / NXCD);
     const int nitems = (r_hi - r_lo) * NT;
-    const int K = a.K;
-    const int nk = K / BK;
+    const int it0 = (int)blockIdx.x / NXCD;
+    const int nmine = it0 < nitems ? (nitems - it0 + G - 1) / G : 0;
 
-    for (int it = (int)blockIdx.x / NXCD; it < nitems; it += G) {
-        const int rt = r_lo + it / NT;
-        const int nt = it % NT;
-        if (wave == 0) {
-            int e = -1, p0 = 0, p1 = 0;
-            const bool ok = find_tile(a.offsets, a.E, a.rows, BM, rt, lane, e, p0, p1);
-            if (lane == 0) {
-                s_e = ok ? e : -1;
-                s_p0 = p0;
-                s_p1 = p1;
+    for (int j0 = 0; j0 < nmine; j0 += W4_MAXI) {
+        const int nb = min(W4_MAXI, nmine - j0);
+        if (j0 > 0)
+            build_tiles();   // the stages of the previous batch overwrote the table
+        // ---- this batch's items: expert by binary search over the first
+        // row tiles, row range, column tile, blob; then every item's source
+        // rows.  All of it is read before the first load into the stages,
+        // so the in-order load counter never makes a wait drain prefetches.
+        if (tid < nb) {
+            const int it = it0 + (j0 + tid) * G;
+            const int rt = r_lo + it / NT;
+            int lo = 0, hi = E - 1;   // largest e with s_ts[e] <= rt
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_ts[mid] <= rt)
+                    lo = mid;
+                else
+                    hi = mid - 1;
             }
+            W4Item r;
+            r.e = lo;
+            r.p0 = s_off[lo] + (rt - s_ts[lo]) * BM;
+            r.p1 = min(s_off[lo + 1], r.p0 + BM);
+            r.nt = it % NT;
+            r.blob = ldg(a.blobs + lo);
+            items[tid] = r;
         }
         __syncthreads();
-        const int e = s_e;
-        const int p0 = s_p0, mrows = s_p1 - s_p0;
-        __syncthreads();   // every wave has the tile and is done with the last item's stages
-        if (e < 0)
-            break;
-
-        // activation sources of this lane: load i covers rows wave*RPW + 8i ..+7
-        // (lane -> row lane >> 3, slot lane & 7 holding logical piece slot ^ f(row));
-        // with RPW = 4 only lanes 0-31 load.  Rows past the tile's end re-read
-        // its first row (their outputs are dropped).
-        const _Float16 *asrc[NA];
-        const bool aload = (RPW >= 8) || lane < 8 * RPW;
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int r = wave * RPW + 8 * i + (lane >> 3);
-            const int fr = (r & 7) ^ ((r >> 3) & 1);
-            const int j = (lane & 7) ^ fr;
-            const int p = p0 + (r < mrows ? r : 0);
-            const int src = GATEUP ? ldg(a.perm + min(p, a.rows - 1)) / a.k : p;
-            asrc[i] = a.A + (size_t)src * K + j * 8;
+        for (int i = tid; i < nb * BM; i += W4_T) {
+            const int q = i / BM, r = i - q * BM;
+            const int p0 = items[q].p0, mrows = items[q].p1 - p0;
+            const int p = p0 + (r < mrows ? r : 0);   // rows past the tile re-read its first row
+            srcs[i] = GATEUP ? ldg(a.perm + p) / a.k : p;
         }
-        // this wave's weight block (a wave past the last block works on the
-        // last one and stores nothing)
-        const int blk = nt * W4_WAVES + wave;
-        const int bb = min(blk, a.nblk - 1);
-        const uint8_t *blob = ldg(a.blobs + e);
-        const uint8_t *qsrc = blob + a.off_q + ((size_t)bb * (K / 32) * 64 + lane) * 16;
-        const uint8_t *ssrc = blob + a.off_s + ((size_t)bb * (K >> gshift) * 64 + col * 2) * 2;
+        __syncthreads();
 
-        auto issue = [&](int kt) {
-            unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
-            if (aload) {
+        // ---- the batch's steps as one stream: step g = item g / nk, K-step
+        // g % nk, stage g % W4_NS; loads run W4_NS - 1 steps ahead, across
+        // item boundaries
+        const int total = nb * nk;
+        int iq = 0, ikt = 0;   // next step to load
+        // sources of the item being loaded (refreshed when loading moves on
+        // to the next item): this lane's activation rows, weight chunk runs
+        // and scale rows
+        const _Float16 *asrc[NA];
+        uint64_t qbase = 0, sbase = 0;   // wave-uniform (scalar registers)
+        auto item_sources = [&]() {
 #pragma unroll
-                for (int i = 0; i < NA; ++i)
-                    dma16(asrc[i] + kt * BK, st + (wave * RPW + 8 * i) * 128);
+            for (int i = 0; i < NA; ++i) {
+                const int r = min(wave * RPW + 8 * i + (lane >> 3), BM - 1);
+                const int fr = (r & 7) ^ ((r >> 3) & 1);
+                const int jp = (lane & 7) ^ fr;
+                asrc[i] = a.A + (size_t)srcs[iq * BM + r] * K + jp * 8;
             }
+            const int nt = __builtin_amdgcn_readfirstlane(items[iq].nt);
+            const uint64_t blob = reinterpret_cast<uint64_t>(items[iq].blob);
+            const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(blob >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)blob);
+            const int bb = min(nt * W4_WAVES + wave, a.nblk - 1);
+            qbase = ub + a.off_q + (uint64_t)bb * (K / 32) * 64 * 16;
+            sbase = ub + a.off_s + (uint64_t)bb * (K >> gshift) * 64 * 2;
+        };
+        item_sources();
+        auto issue_next = [&]() {
+            unsigned char *st = smem + (size_t)((iq * nk + ikt) % W4_NS) * St::BYTES;
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-                dma16(qsrc + (size_t)(2 * kt + c) * 1024, st + St::A + wave * 2048 + c * 1024);
+            for (int i = 0; i < NA; ++i)
+                if (8 * RPW - 64 * i >= 64 || lane < 8 * RPW - 64 * i)
+                    dma16(asrc[i] + ikt * BK, st + (wave * RPW + 8 * i) * 128);
+            const uint8_t *q = reinterpret_cast<const uint8_t *>(qbase) +
+                               (size_t)(2 * ikt) * 1024 + lane * 16;
+            dma16(q, st + St::A + wave * 2048);
+            dma16(q + 1024, st + St::A + wave * 2048 + 1024);
             // lanes 0-31: chunk 2kt's group, rows 2l, 2l+1; lanes 32-63: chunk 2kt+1's
-            const int grp = ((2 * kt + half) * 32) >> gshift;
-            dma4(ssrc + (size_t)grp * 128, st + St::A + St::B + wave * 256);
+            const int grp = ((2 * ikt + half) * 32) >> gshift;
+            dma4(reinterpret_cast<const uint8_t *>(sbase) + (size_t)grp * 128 + col * 4,
+                 st + St::A + St::B + wave * 256);
+            if (++ikt == nk) {
+                ikt = 0;
+                if (++iq < nb)
+                    item_sources();
+            }
         };
 
         // weight words and scales of one step: fragment n = rows n*32 + col
@@ -519,8 +536,8 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
             uint2_t q[2][2];
             f16 s[2][2];
         };
-        auto read_w = [&](int kt, StepW &w) {
-            const unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
+        auto read_w = [&](int g, StepW &w) {
+            const unsigned char *st = smem + (size_t)(g % W4_NS) * St::BYTES;
             const unsigned char *bq = st + St::A + wave * 2048;
             const unsigned char *sq = st + St::A + St::B + wave * 256;
 #pragma unroll
@@ -532,8 +549,8 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
                     w.s[n][c] = *reinterpret_cast<const f16 *>(sq + c * 128 + (n * 32 + col) * 2);
                 }
         };
-        auto fetch = [&](int kt, int s, const StepW &w, half8_t *a_, half8_t *b_) {
-            const unsigned char *st = smem + (size_t)(kt % W4_NS) * St::BYTES;
+        auto fetch = [&](int g, int s, const StepW &w, half8_t *a_, half8_t *b_) {
+            const unsigned char *st = smem + (size_t)(g % W4_NS) * St::BYTES;
 #pragma unroll
             for (int m = 0; m < MF; ++m)
                 a_[m] = *reinterpret_cast<const half8_t *>(
@@ -555,9 +572,9 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
                 for (int r = 0; r < 16; ++r)
                     acc[m][n][r] = 0.0f;
 
-        const int pre = min(W4_NS, nk);
-        for (int kt = 0; kt < pre; ++kt)
-            issue(kt);
+        const int pre = min(W4_NS, total);
+        for (int i = 0; i < pre; ++i)
+            issue_next();
         wait_steps<PER>(pre - 1);
         lds_barrier();
         StepW wc, wn;
@@ -565,16 +582,15 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
         read_w(0, wc);
         fetch(0, 0, wc, af[0], bf[0]);
 
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool next = kt + 1 < nk;
+        int cq = 0, ckt = 0;   // item and K-step being computed
+        for (int g = 0; g < total; ++g) {
+            const bool next = g + 1 < total;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s == 3 && next) {
-                    // every operand of step kt is in registers: open step kt+1
-                    wait_steps<PER>(min(2, nk - 2 - kt));
+                    // every operand of step g is in registers: open step g+1
+                    wait_steps<PER>(min(2, total - 2 - g));
                     lds_barrier();
-                    if (kt + W4_NS < nk)
-                        issue(kt + W4_NS);   // refills the stage of step kt
                 }
                 // weights as the 32-row operand: acc[m][n] holds C^T, so a lane
                 // owns one token row and 4 consecutive output columns per
@@ -586,50 +602,69 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
                         acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                             bf[s & 1][n], af[s & 1][m], acc[m][n], 0, 0, 0);
                 if (s < 3) {
-                    fetch(kt, s + 1, wc, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                    fetch(g, s + 1, wc, af[(s + 1) & 1], bf[(s + 1) & 1]);
                 } else if (next) {
-                    read_w(kt + 1, wn);
-                    fetch(kt + 1, 0, wn, af[0], bf[0]);
+                    read_w(g + 1, wn);
+                    fetch(g + 1, 0, wn, af[0], bf[0]);
+                    if (g + W4_NS < total)
+                        issue_next();   // refills the stage of step g (read by no one now)
                 }
             }
             if (next)
                 wc = wn;
-        }
+            if (++ckt < nk)
+                continue;
 
-        // ---- epilogue.  acc[m][n] = (weight rows) x (tokens): value r of
-        // lane l is output column 8*(r/4) + 4*(l/32) + (r%4) of fragment n and
-        // token row m*32 + l%32, so r = 4j..4j+3 are 4 consecutive columns
-        // (one 8-byte store).
-        if (blk < a.nblk) {
+            // ---- epilogue of item cq (the next item's first steps are already
+            // loading).  acc[m][n] = (weight rows) x (tokens): value r of lane l
+            // is output column 8*(r/4) + 4*(l/32) + (r%4) of fragment n and
+            // token row m*32 + l%32, so r = 4j..4j+3 are 4 consecutive columns
+            // (one 8-byte store).
+            const W4Item itm = items[cq];
+            const int blk = itm.nt * W4_WAVES + wave;
+            if (blk < a.nblk) {
+                const int mrows = itm.p1 - itm.p0;
 #pragma unroll
-            for (int m = 0; m < MF; ++m) {
-                const int row = m * 32 + col;
-                if (row >= mrows)
-                    continue;
-                const size_t p = (size_t)(p0 + row);
+                for (int m = 0; m < MF; ++m) {
+                    const int row = m * 32 + col;
+                    if (row >= mrows)
+                        continue;
+                    const size_t p = (size_t)(itm.p0 + row);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c0 = 8 * j + 4 * half;
-                    half4_t v;
-                    if constexpr (GATEUP) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            v[i] = (_Float16)swiglu_fast(acc[m][0][4 * j + i], acc[m][1][4 * j + i]);
-                        *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) + p * a.ldo +
-                                                     blk * 32 + c0) = v;
-                    } else {
-#pragma unroll
-                        for (int f = 0; f < 2; ++f) {
+                    for (int j = 0; j < 4; ++j) {
+                        const int c0 = 8 * j + 4 * half;
+                        half4_t v;
+                        if constexpr (GATEUP) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                v[i] = (_Float16)acc[m][f][4 * j + i];
+                                v[i] = (_Float16)swiglu_fast(acc[m][0][4 * j + i],
+                                                             acc[m][1][4 * j + i]);
                             *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) +
-                                                         p * a.ldo + blk * 64 + f * 32 + c0) = v;
+                                                         p * a.ldo + blk * 32 + c0) = v;
+                        } else {
+#pragma unroll
+                            for (int f = 0; f < 2; ++f) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    v[i] = (_Float16)acc[m][f][4 * j + i];
+                                *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) +
+                                                             p * a.ldo + blk * 64 + f * 32 + c0) = v;
+                            }
                         }
                     }
                 }
             }
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[m][n][r] = 0.0f;
+            ckt = 0;
+            ++cq;
         }
+        __syncthreads();   // stages and item lists are free for the next batch
     }
 }
 
@@ -692,7 +727,8 @@ static int launch_mf(hipStream_t s, const GemmArgs &a)
 template <int MODE, int MF>
 static int launch_w4(hipStream_t s, const GemmArgs &a)
 {
-    constexpr size_t lds = w4_lds_bytes<MF>();
+    constexpr size_t lds = w4_lds_total<MF>();
+    static_assert(w4_lds_total<MF>() <= 160 * 1024, "LDS of one workgroup");
     static bool attr_set = false;   // raising the LDS limit is idempotent
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void *)w4_gemm_kernel<MODE, MF>,
