@@ -65,7 +65,7 @@ enum {
 };
 
 enum { MOE_RENORM = 1u };                       /* moe_route flag */
-enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2 };
+enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2, MOE_REGIME_SMALL = 3 };
 enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
 
 /* Thread-local text of the last error on this thread ("" if none). */
@@ -183,12 +183,17 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
 
 /* ------------------------------------------------ routed expert FFN */
 /*
- * What moe_expert_ffn_w4a16 will do for a shape: the resolved regime (AUTO
- * picks DECODE while T*k/E is small, else BATCHED), the dtype and number of
- * slices of y, and the workspace it needs.  Host-only.
- *   DECODE : y is fp32 [slices][T*k][H], partial sums over intermediate
- *            slices of 32 (slices = I/32); moe_combine adds the slices.
- *   BATCHED: y is fp16 [1][T*k][H].
+ * What moe_expert_ffn_w4a16 will do for a shape: the resolved regime, the
+ * dtype and number of slices of y, and the workspace it needs.  Host-only.
+ * AUTO picks DECODE for T <= 4 tokens, SMALL for T <= 32, else BATCHED.
+ *   DECODE : one launch, rows of an expert one after another on the vector
+ *            ALUs.  y is fp32 [slices][T*k][H], partial sums over
+ *            intermediate slices of 32 (slices = I/32); moe_combine adds them.
+ *   SMALL  : T <= 32 (Horizon RunMap "10 / Próximas perguntas": concurrent
+ *            use).  Each expert's weights are streamed once and its <= T rows
+ *            multiplied on the matrix cores; gate/up then down, h in ws.
+ *            T > 32 is MOE_EUNSUPPORTED.  y is fp16 [1][T*k][H].
+ *   BATCHED: tiled grouped GEMM, any T.  y is fp16 [1][T*k][H].
  */
 int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
                         int *resolved_regime, int *y_dtype, int *y_slices,
@@ -211,8 +216,9 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
  *   y              device output, layout from moe_expert_ffn_plan; y_dtype
  *                  and y_slices must equal the plan's (MOE_EINVAL otherwise)
  *   ws             device scratch of the plan's size (may be NULL if 0)
- * Rounding: DECODE converts h to fp16 before the down projection; BATCHED
- * stores h and y as fp16.  Everything else accumulates in fp32.
+ * Rounding: DECODE converts h to fp16 before the down projection; SMALL and
+ * BATCHED convert the weights to fp16(q * s) and store h and y as fp16.
+ * Everything else accumulates in fp32.
  */
 int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *offsets,
                          const void *const *d_expert_blobs,

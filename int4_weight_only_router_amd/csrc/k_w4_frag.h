@@ -1,0 +1,57 @@
+// k_w4_frag.h -- MFMA operand helpers shared by the INT4 expert GEMMs:
+// weight-word dequantisation into fp16 B fragments, global-address-space
+// loads and the SwiGLU epilogue.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
+
+// One dword of 8 nibbles (device order) times its group scale -> the 8 fp16
+// B-operand values of one lane for one 16-K step, fp16(q * s) exactly.  OR-ing
+// a nibble into the mantissa of 1024.0 gives 1024 + u (bits 0..3 of a half)
+// or 1024 + 16u (bits 4..7); subtracting 1032, or scaling by 1/16 and
+// subtracting 72, gives q = u - 8 exactly.  `magic` holds 0x64006400 in a
+// register so that mask-and-insert is one v_and_or_b32.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, uint32_t magic)
+{
+    const uint32_t w8 = w >> 8;
+    const half2_t k1032 = {(f16)-1032.0f, (f16)-1032.0f};
+    const half2_t s16 = {(f16)0.0625f, (f16)0.0625f};
+    const half2_t k72 = {(f16)-72.0f, (f16)-72.0f};
+    half2_t q[4];
+    q[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | magic) + k1032;
+    q[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | magic) * s16 + k72;
+    q[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | magic) + k1032;
+    q[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | magic) * s16 + k72;
+    half8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t v = q[i] * s2;
+        r[2 * i] = v[0];
+        r[2 * i + 1] = v[1];
+    }
+    return r;
+}
+
+// Loads through the global address space (plain pointers derived from a
+// loaded blob address would otherwise become flat loads, which the hardware
+// also counts against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T ldg(const T *p)
+{
+    typedef const __attribute__((address_space(1))) T gT;
+    return *(gT *)(p);
+}
+
+// SiLU(g) * u with the hardware exp2 / reciprocal (about 1 ulp each in fp32;
+// the result is rounded to fp16).
+__device__ __forceinline__ float swiglu_fast(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+}  // namespace moe

@@ -42,6 +42,9 @@ int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
                        int, int, int, int, int, void *, void *, hipStream_t);
+bool ffn_small_fits(int T, int H, int I);
+int launch_ffn_small(const void *, const int32_t *, const int32_t *, const void *const *, int, int,
+                     int, int, int, int, void *, void *, hipStream_t);
 int launch_shared_gemv(const void *, const void *, const void *, const void *, int, int, int,
                        float *, void *, hipStream_t);
 int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
@@ -53,6 +56,7 @@ int launch_quantize(const float *, const float *, const float *, int, int, int, 
 int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
+constexpr int SMALL_MAX_T = 32;       // AUTO: small-batch kernel up to this many tokens
 constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
 constexpr int SHARED_GEMV_MAX_T = 4;  // shared expert: GEMV up to this many tokens
@@ -85,10 +89,15 @@ static int check_route_shape(const char *fn, int T, int E, int k)
     return MOE_OK;
 }
 
-static int resolve_regime(int T, int regime)
+static int resolve_regime(int T, int H, int I, int regime)
 {
-    if (regime == MOE_REGIME_AUTO)
-        return T <= DECODE_MAX_T ? MOE_REGIME_DECODE : MOE_REGIME_BATCHED;
+    if (regime == MOE_REGIME_AUTO) {
+        if (T <= DECODE_MAX_T)
+            return MOE_REGIME_DECODE;
+        if (T <= SMALL_MAX_T && ffn_small_fits(T, H, I))
+            return MOE_REGIME_SMALL;
+        return MOE_REGIME_BATCHED;
+    }
     return regime;
 }
 
@@ -274,9 +283,12 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
     rc = check_expert_shape("moe_expert_ffn_plan", H, I, group);
     if (rc)
         return rc;
-    if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_BATCHED)
+    if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_SMALL)
         return set_error(MOE_EINVAL, "moe_expert_ffn_plan: bad regime %d", regime);
-    const int r = resolve_regime(T, regime);
+    const int r = resolve_regime(T, H, I, regime);
+    if (r == MOE_REGIME_SMALL && !ffn_small_fits(T, H, I))
+        return set_error(MOE_EUNSUPPORTED,
+                         "moe_expert_ffn_plan: small-batch regime takes T <= 32 (T=%d)", T);
     if (resolved_regime)
         *resolved_regime = r;
     if (y_dtype)
@@ -314,6 +326,9 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
         return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
                                  group,
                                  static_cast<float *>(y), stream);
+    if (r == MOE_REGIME_SMALL)
+        return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
+                                stream);
     return launch_ffn_batched(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
                               stream);
 }

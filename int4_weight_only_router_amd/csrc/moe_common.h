@@ -88,27 +88,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
-// Four packed nibble pairs of one dword -> four fp16 pairs (q0,q1) .. (q6,q7)
-// with q = u - 8.  Dword layout (device format): element 2i in bits [4i,4i+4),
-// element 2i+1 in bits [16+4i, 16+4i+4), i = 0..3.  OR-ing a nibble into the
-// mantissa of 1024.0 (0x6400) gives 1024 + u exactly; a nibble at bits 4..7
-// gives 1024 + 16u.  Both decode exactly to u - 8.
-__device__ __forceinline__ void nib8_to_h2x4(uint32_t w, half2_t out[4]) {
-    const uint32_t M = 0x64006400u;
-    uint32_t a = (w & 0x000F000Fu) | M;
-    uint32_t b = (w & 0x00F000F0u) | M;
-    uint32_t w8 = w >> 8;
-    uint32_t c = (w8 & 0x000F000Fu) | M;
-    uint32_t d = (w8 & 0x00F000F0u) | M;
-    const half2_t k1032 = {(f16)-1032.0f, (f16)-1032.0f};
-    const half2_t s16 = {(f16)0.0625f, (f16)0.0625f};
-    const half2_t k72 = {(f16)-72.0f, (f16)-72.0f};
-    out[0] = __builtin_bit_cast(half2_t, a) + k1032;
-    out[1] = __builtin_bit_cast(half2_t, b) * s16 + k72;
-    out[2] = __builtin_bit_cast(half2_t, c) + k1032;
-    out[3] = __builtin_bit_cast(half2_t, d) * s16 + k72;
-}
-
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }

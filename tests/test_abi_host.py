@@ -44,6 +44,17 @@ def test_plan_regimes():
     assert ws >= 4096 * 8 * 1024 * 2
     r, *_ = M.moe_expert_ffn_plan(1, 2048, 1024, 64, 8, 128, M.MOE_REGIME_BATCHED)
     assert r == M.MOE_REGIME_BATCHED
+    # small batch: fp16 y, h in the workspace
+    r, dt, sl, ws = M.moe_expert_ffn_plan(8, 2048, 1024, 64, 8, 128)
+    assert (r, dt, sl) == (M.MOE_REGIME_SMALL, M.MOE_DTYPE_F16, 1)
+    assert ws >= 8 * 8 * 1024 * 2
+    assert M.moe_expert_ffn_plan(32, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_SMALL
+    assert M.moe_expert_ffn_plan(33, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_BATCHED
+    assert M.moe_expert_ffn_plan(1, 256, 512, 8, 2, 64, M.MOE_REGIME_SMALL)[0] == \
+        M.MOE_REGIME_SMALL
+    assert M.moe_expert_ffn_plan(32, 2048, 8192, 64, 8, 128)[0] == M.MOE_REGIME_SMALL
+    assert M.moe_expert_ffn_plan(4, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_DECODE
+    assert M.moe_expert_ffn_plan(5, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_SMALL
 
 
 @pytest.mark.parametrize("args,code", [
@@ -55,6 +66,8 @@ def test_plan_regimes():
     ((1, 2048, 1024, 2048, 8, 128), M.MOE_EUNSUPPORTED),  # E > 1024
     ((1, 2048, 1024, 64, 17, 128), M.MOE_EUNSUPPORTED),  # k > 16
     ((-1, 2048, 1024, 64, 8, 128), M.MOE_EINVAL),        # T < 0
+    ((1, 2048, 1024, 64, 8, 128, 4), M.MOE_EINVAL),      # unknown regime
+    ((33, 2048, 1024, 64, 8, 128, M.MOE_REGIME_SMALL), M.MOE_EUNSUPPORTED),   # T > 32
 ])
 def test_plan_rejections(args, code):
     with pytest.raises(M.MoEError) as ei:

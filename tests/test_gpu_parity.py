@@ -260,7 +260,15 @@ def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
     (MI.OLMOE_DECODE, 4096, M.MOE_REGIME_BATCHED), (MI.E512, 1, M.MOE_REGIME_AUTO),
     (MI.E512, 256, M.MOE_REGIME_BATCHED), (MI.E512, 4096, M.MOE_REGIME_BATCHED),
     (G32, 3, M.MOE_REGIME_DECODE), (G32, 300, M.MOE_REGIME_BATCHED),
-    (G32, 8192, M.MOE_REGIME_BATCHED)],
+    (G32, 8192, M.MOE_REGIME_BATCHED),
+    # small-batch kernel: K split over 1..8 waves (set by the active-expert
+    # estimate), ragged T, T = 32 (the largest), group sizes 32 and 128
+    (MI.TINY, 2, M.MOE_REGIME_SMALL), (MI.TINY, 16, M.MOE_REGIME_SMALL),
+    (MI.TINY, 32, M.MOE_REGIME_SMALL), (MI.OLMOE_DECODE, 2, M.MOE_REGIME_SMALL),
+    (MI.OLMOE_DECODE, 8, M.MOE_REGIME_AUTO), (MI.OLMOE_DECODE, 17, M.MOE_REGIME_SMALL),
+    (MI.OLMOE_DECODE, 32, M.MOE_REGIME_SMALL), (MI.E512, 5, M.MOE_REGIME_SMALL),
+    (MI.E512, 32, M.MOE_REGIME_SMALL), (G32, 3, M.MOE_REGIME_SMALL),
+    (G32, 32, M.MOE_REGIME_SMALL)],
     ids=lambda v: getattr(v, "name", str(v)))
 def test_expert_ffn(cfg, T, regime):
     _ffn_case(cfg, T, regime)
@@ -367,7 +375,8 @@ def _oracle_tokens(cfg, x, toks, layer=0, residual=None, shared=True):
                        shared=sh, residual=res)
 
 
-@pytest.mark.parametrize("cfg,T", [(MI.TINY, 16), (MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 64),
+@pytest.mark.parametrize("cfg,T", [(MI.TINY, 16), (MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 8),
+                                   (MI.E512, 16), (MI.OLMOE_DECODE, 64),
                                    (MI.OLMOE_DECODE, 512), (MI.OLMOE_DECODE, 4096),
                                    (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096), (G32, 300)],
                          ids=lambda v: getattr(v, "name", str(v)))
@@ -395,7 +404,8 @@ def test_single_expert_top1_hot_path():
     cfg = MI.MoEConfig(90, "e1k1", H=256, E=1, k=1, I=128, g=64)
     lay = make_layer(cfg, 0, shared=False)
     for T, regime in [(1, M.MOE_REGIME_DECODE), (300, M.MOE_REGIME_BATCHED),
-                      (5, M.MOE_REGIME_DECODE)]:
+                      (5, M.MOE_REGIME_DECODE), (7, M.MOE_REGIME_SMALL),
+                      (32, M.MOE_REGIME_SMALL)]:
         say("e1k1 T=%d" % T)
         x = MI.gen_x(cfg, T)
         b = lay.buffers(T, regime)
@@ -430,6 +440,60 @@ def test_hot_expert_many_tiles():
     y_ref = O.expert_ffn(x, perm, offsets, OracleBlobs(cfg, 0).get([5]), cfg.H, cfg.I, cfg.E,
                          cfg.k, cfg.g, rows=rows)
     check_close(_np(b.y)[0][rows].astype(np.float64), y_ref, "hot expert y")
+
+
+def test_hot_expert_small_batch():
+    """Every one of 32 tokens routes to expert 5: the small-batch kernel's
+    largest row count (32, one MFMA column operand) next to experts with one
+    or two rows."""
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0, shared=False)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[5] = 100.0
+    lay.bias = torch.from_numpy(bias).to(DEV)
+    T = 32
+    x = MI.gen_x(cfg, T)
+    b = lay.buffers(T, M.MOE_REGIME_SMALL)
+    say("hot expert small T=%d" % T)
+    xd = f16(x)
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    torch.cuda.synchronize()
+    oi, _, _ = O.route(x, MI.gen_router(cfg), bias, cfg.k)
+    assert np.array_equal(_np(b.topk_idx), oi)
+    counts, offsets, perm, _ = O.permute(oi, cfg.E)
+    assert counts[5] == T
+    rows = np.arange(T * cfg.k, dtype=np.int32)
+    y_ref = O.expert_ffn(x, perm, offsets, OracleBlobs(cfg, 0).get(np.unique(oi)), cfg.H, cfg.I,
+                         cfg.E, cfg.k, cfg.g, rows=rows)
+    check_close(_np(b.y)[0][rows].astype(np.float64), y_ref, "hot expert small y")
+
+
+def test_small_batch_idle_waves_and_parts():
+    """Small-batch kernel with 14 fused blocks dealt four to a workgroup (the
+    last workgroup has two idle waves), the rows staged in two parts of K
+    (32 rows of H = 1024), and 32 rows on each of the 16 routed experts."""
+    cfg = MI.MoEConfig(92, "h1024_i448_e160", H=1024, E=160, k=16, I=448, g=64)
+    lay = make_layer(cfg, 0, shared=False)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[:cfg.k] = 100.0
+    lay.bias = torch.from_numpy(bias).to(DEV)
+    T = 32
+    x = MI.gen_x(cfg, T)
+    b = lay.buffers(T, M.MOE_REGIME_SMALL)
+    say("small batch idle waves T=%d" % T)
+    xd = f16(x)
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    torch.cuda.synchronize()
+    oi, _, _ = O.route(x, MI.gen_router(cfg), bias, cfg.k)
+    assert np.array_equal(_np(b.topk_idx), oi)
+    counts, offsets, perm, _ = O.permute(oi, cfg.E)
+    assert np.all(counts[:cfg.k] == T)
+    rows = np.arange(T * cfg.k, dtype=np.int32)
+    y_ref = O.expert_ffn(x, perm, offsets, OracleBlobs(cfg, 0).get(range(cfg.k)), cfg.H, cfg.I,
+                         cfg.E, cfg.k, cfg.g, rows=rows)
+    check_close(_np(b.y)[0][rows].astype(np.float64), y_ref, "small batch idle waves y")
 
 
 def test_zero_tokens_is_noop():
