@@ -39,6 +39,9 @@ def log(msg):
     sys.stderr.flush()
 
 
+REGIMES = {"auto": 0, "decode": 1, "batched": 2, "small": 3}   # MOE_REGIME_* values
+
+
 def build_layers(cfg, layers, dev, torch, M):
     """Device-resident layers: weights drawn by moe_inputs (numpy), quantised
     and prepacked by the library's kernels."""
@@ -126,15 +129,26 @@ def _graph_time(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def _profile_traffic(kernel_src, key):
-    """HBM bytes per launch measured by rocprofv3 counters and recorded under
-    profiles/, if the kernel source has not changed since (else None)."""
+DECODE_KERNEL_SOURCES = ("int4_weight_only_router_amd/csrc/k_ffn_decode.hip",
+                         "int4_weight_only_router_amd/csrc/k_decode_frag.h")
+
+
+def sources_sha256(paths):
+    """sha256 over the concatenated bytes of the files a kernel is built from."""
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def _profile_traffic(kernel_srcs, key):
+    """HBM bytes per launch measured by rocprofv3 counters and recorded under
+    profiles/, if the kernel's sources have not changed since (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))[key]
-        src = open(os.path.join(ROOT, kernel_src), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        if sources_sha256(kernel_srcs) != rec["source_sha256"]:
             return None
         return int(rec["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -213,8 +227,7 @@ def run_decode(args, torch, M):
     ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
     achieved = ffn_bytes / (t_ffn * 1e-3) / 1e9
     ms_step = elapsed * 1e3 / K
-    traffic = _profile_traffic("int4_weight_only_router_amd/csrc/k_ffn_decode.hip",
-                               "ffn_decode_kernel olmoe_decode")
+    traffic = _profile_traffic(DECODE_KERNEL_SOURCES, "ffn_decode_kernel olmoe_decode")
     res = {
         "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (batched), W4A16",
         "value": round(K / elapsed, 2),
@@ -253,51 +266,67 @@ def run_decode(args, torch, M):
 # ----------------------------------------------------------------- batched
 
 def run_batched(args, torch, M, cfg):
-    """Single layers of `cfg` at each batch size: median per-call times of
-    route+permute, routed expert FFN, shared expert and combine (HIP events
-    around each call on the current stream), with the MFMA fraction of the
-    routed FFN (routed FLOPs only) and the HBM fraction of the whole layer
-    (algorithmic bytes: touched expert blobs, router, shared weights, x, out)."""
+    """Single layers of `cfg` at each batch size.  Each part of the layer
+    (route+permute, routed expert FFN, shared expert, combine) and the whole
+    layer is captured in a graph over NC >= 16 copies of the layer's weights at
+    distinct addresses (NC x layer bytes > 3x the 256 MB last-level cache, so
+    no copy is still cached when its turn comes) and replayed; the average
+    per call is reported.  With it: the MFMA fraction of the routed FFN
+    (routed FLOPs), its HBM fraction (touched expert blobs only: the bound at
+    small T) and the HBM fraction of the whole layer (algorithmic bytes:
+    touched expert blobs, router, shared weights, x, out)."""
     import numpy as np
     import moe_inputs as MI
+    from int4_weight_only_router_amd.layer import MoELayer, blob_table
     dev = "cuda:0"
     lays, blob_bytes = build_layers(cfg, 1, dev, torch, M)
-    lay = lays[0]
+    base = lays[0]
+    shared = None
     if cfg.Is:
-        lay.shared = tuple(torch.from_numpy(w).to(dev) for w in MI.gen_shared(cfg))
+        shared = tuple(torch.from_numpy(w).to(dev) for w in MI.gen_shared(cfg))
+    # at least 16 calls per captured graph, so that the replay's own launch
+    # cost is shared (and the touched weights of 16 small-T calls still
+    # exceed the last-level cache)
+    nc = max(16, -(-3 * 256 * 2 ** 20 // (cfg.E * blob_bytes)))
+    copies = [base]
+    for _ in range(nc - 1):
+        bl = base._blobs.clone()
+        lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, base.router, blob_table(bl), base.bias,
+                       shared, device=dev)
+        lay._blobs = bl
+        copies.append(lay)
+    base.shared = shared
     Ts = [int(t) for t in args.T.split(",")] if args.T else list(cfg.T)
+    reps = max(1, args.steps // nc)
     lines = []
     for T in Ts:
         x = torch.from_numpy(MI.gen_x(cfg, T)).to(dev)
-        b = lay.buffers(T)
-        for _ in range(args.warmup):
-            lay.forward(x, b)
+        bufs = [lay.buffers(T, REGIMES[args.regime]) for lay in copies]
+        for _ in range(max(1, args.warmup)):
+            for lay, b in zip(copies, bufs):
+                lay.forward(x, b)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        parts = {"route_permute": [], "expert_ffn": [], "shared": [], "combine": [], "layer": []}
-        ffn_ws = 0 if b.ffn_ws is None else b.ffn_ws.numel()
-        for _ in range(args.steps):
-            ev[0].record()
-            lay.route_permute(x, b)
-            ev[1].record()
+
+        def each(fn):
+            return lambda: [fn(lay, b) for lay, b in zip(copies, bufs)]
+
+        def ffn(lay, b):
             M.moe_expert_ffn_w4a16(x, b.perm, b.offsets, lay.table, T, cfg.H, cfg.I, cfg.E,
                                    cfg.k, cfg.g, b.regime, b.y, b.y_dtype, b.y_slices, b.ffn_ws,
-                                   ffn_ws)
-            ev[2].record()
-            if lay.shared is not None:
-                wg, wu, wd = lay.shared
-                M.moe_shared_ffn_f16(x, wg, wu, wd, T, cfg.H, cfg.Is, b.shared_out, b.shared_ws,
-                                     b.shared_ws.numel())
-            ev[3].record()
-            lay.combine(b)
-            ev[4].record()
-            torch.cuda.synchronize()
-            parts["route_permute"].append(ev[0].elapsed_time(ev[1]))
-            parts["expert_ffn"].append(ev[1].elapsed_time(ev[2]))
-            parts["shared"].append(ev[2].elapsed_time(ev[3]))
-            parts["combine"].append(ev[3].elapsed_time(ev[4]))
-            parts["layer"].append(ev[0].elapsed_time(ev[4]))
-        us = {k: float(np.median(v)) * 1e3 for k, v in parts.items()}
+                                   0 if b.ffn_ws is None else b.ffn_ws.numel())
+
+        def shr(lay, b):
+            wg, wu, wd = lay.shared
+            M.moe_shared_ffn_f16(x, wg, wu, wd, T, cfg.H, cfg.Is, b.shared_out, b.shared_ws,
+                                 b.shared_ws.numel())
+
+        parts = {"route_permute": each(lambda lay, b: lay.route_permute(x, b)),
+                 "expert_ffn": each(ffn), "combine": each(lambda lay, b: lay.combine(b)),
+                 "layer": each(lambda lay, b: lay.forward(x, b))}
+        if shared is not None:
+            parts["shared"] = each(shr)
+        us = {k: _graph_time(torch, fn, reps) * 1e3 / nc for k, fn in parts.items()}
+        b = bufs[0]
         counts = b.counts.cpu().numpy()
         touched = int((counts > 0).sum())
         f_routed = 2.0 * T * cfg.k * 3 * cfg.H * cfg.I
@@ -306,19 +335,23 @@ def run_batched(args, torch, M, cfg):
         b_alg = (touched * blob_bytes + cfg.E * cfg.H * 2 + 3 * cfg.H * cfg.Is * 2
                  + 2 * T * cfg.H * 2)
         tf = f_routed / (us["expert_ffn"] * 1e-6) / 1e12
-        line = {"T": T, "experts_touched": touched, "max_rows_per_expert": int(counts.max()),
+        ffn_bytes = touched * blob_bytes
+        line = {"T": T, "regime": {1: "decode", 2: "batched", 3: "small"}.get(b.regime, b.regime),
+                "experts_touched": touched, "max_rows_per_expert": int(counts.max()),
                 "us": {k: round(v, 1) for k, v in us.items()},
+                "expert_ffn_alg_GB": round(ffn_bytes / 1e9, 4),
+                "expert_ffn_hbm_frac": round(ffn_bytes / (us["expert_ffn"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "routed_tflops": round(tf, 1), "routed_mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                 "layer_tflops": round((f_routed + f_shared + f_router) / (us["layer"] * 1e-6) / 1e12, 1),
                 "layer_alg_GB": round(b_alg / 1e9, 4),
                 "layer_hbm_frac": round(b_alg / (us["layer"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         if cfg.Is:
-            tfs = f_shared / (us["shared"] * 1e-6) / 1e12
-            line["shared_tflops"] = round(tfs, 1)
+            line["shared_tflops"] = round(f_shared / (us["shared"] * 1e-6) / 1e12, 1)
         lines.append(line)
         log(str(line))
-    return {"workload": cfg.name, "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                                             "g": cfg.g, "Is": cfg.Is, "zipf_s": cfg.zipf_s},
+    return {"workload": cfg.name, "weight_copies": nc, "regime": args.regime,
+            "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I, "g": cfg.g, "Is": cfg.Is,
+                       "zipf_s": cfg.zipf_s},
             "results": lines}
 
 
@@ -460,6 +493,8 @@ def main():
     ap.add_argument("--workload", choices=["decode", "batched", "e512", "partial", "copy"],
                     default="decode")
     ap.add_argument("--T", default="", help="batched/e512: comma-separated batch sizes")
+    ap.add_argument("--regime", choices=sorted(REGIMES), default="auto",
+                    help="batched/e512: routed-FFN regime (auto: the library's choice)")
     ap.add_argument("--blocks", type=int, default=3)
     ap.add_argument("--prompts", type=int, default=12)
     ap.add_argument("--tokens", type=int, default=128)

@@ -1,5 +1,5 @@
 // k_ffn_decode.hip -- decode-regime routed expert FFN straight from INT4
-// weights (K3), and the FP16 GEMV pair of the shared expert at small T.
+// weights (K3).
 //
 // Horizon RunMap "03 / Arquitetura" and "08 / Comportamento do modelo": the
 // expert kernel reads compact INT4 weights and FP16 scales, converts the
@@ -19,7 +19,7 @@
 // workgroup writes an fp32 partial y for its slice; moe_combine adds the
 // slices in order.  All weight loads of a workgroup are issued before any
 // arithmetic, so a workgroup keeps its whole ~96 KB in flight.
-#include "moe_common.h"
+#include "k_decode_frag.h"
 
 namespace moe {
 
@@ -55,56 +55,6 @@ __device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ off
 }
 
 constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are staged at entry
-
-// The dot products take the weights as "magic" fp16 values without decoding
-// them: OR-ing a nibble into the mantissa of 1024.0 gives v = 1024 + u (low
-// field of a half, bits 0..3) or v = 1024 + 16u (high field, bits 4..7).  With
-// the activation pair of a high field pre-divided by 16 (exact: a power of
-// two), v * x' = 1024 x + u x or 64 x + u x, and the chunk sum of
-// (u - 8) x = q x follows by starting the accumulator at
-// -1032 * (sum of x over low-field pairs) - 72 * (sum over high-field pairs).
-// That constant depends only on the activations, so it is computed once per
-// token and chunk.  Pair p of a 32-element chunk is a high-field pair iff p is
-// odd (device nibble layout).  The fp32 running sums stay within a few
-// thousand, so rounding is ~1e-7 relative to them: far inside the budget.
-__device__ __forceinline__ float dot_chunk(uint4_t w, const half2_t *xp, float d)
-{
-    const uint32_t M = 0x64006400u;
-    // device chunk words hold elements 0-7, 16-23, 8-15, 24-31 in that order
-    const uint32_t ws[4] = {w.x, w.z, w.y, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t v = ws[j], v8 = ws[j] >> 8;
-        d = dot2(__builtin_bit_cast(half2_t, (v & 0x000F000Fu) | M), xp[4 * j + 0], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v & 0x00F000F0u) | M), xp[4 * j + 1], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x000F000Fu) | M), xp[4 * j + 2], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x00F000F0u) | M), xp[4 * j + 3], d);
-    }
-    return d;
-}
-
-// Prepares one 32-element chunk of activations: pairs with odd index divided
-// by 16, and the chunk's correction constant.
-__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr)
-{
-    float slo = 0.0f, shi = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const half8_t v = *reinterpret_cast<const half8_t *>(src + 8 * q);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f16 a = v[2 * m], b = v[2 * m + 1];
-            if (m & 1) {
-                shi += (float)a + (float)b;
-                dst[4 * q + m] = half2_t{a * (f16)0.0625f, b * (f16)0.0625f};
-            } else {
-                slo += (float)a + (float)b;
-                dst[4 * q + m] = half2_t{a, b};
-            }
-        }
-    }
-    *corr = -1032.0f * slo - 72.0f * shi;
-}
 
 template <int H, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
@@ -280,91 +230,6 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
     MOE_LAUNCH_CHECK("ffn_decode_kernel");
-    return MOE_OK;
-}
-
-// ----------------------------------------------------------------------------
-// FP16 GEMV pair for the shared expert at small T (weights row-major fp16,
-// the layout the caller hands over).  One wave per output row, lanes along K
-// with 16-byte loads, xor-butterfly reduction.
-//   swiglu=1: h[t][r] = fp16(silu(Wg[r].x_t) * (Wu[r].x_t)), r < R
-//   swiglu=0: out[t][r] = W[r].in_t (fp32), r < R
-constexpr int GEMV_WAVES = 4;
-
-template <int T_MAX>
-__global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
-    const f16 *__restrict__ in, const f16 *__restrict__ wa, const f16 *__restrict__ wb, int T,
-    int R, int K, int swiglu, f16 *__restrict__ hout, float *__restrict__ fout)
-{
-    const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
-    if (r >= R)
-        return;
-    const int nch = K / 8;
-    const uint4_t *ra = reinterpret_cast<const uint4_t *>(wa + (size_t)r * K);
-    const uint4_t *rb = swiglu ? reinterpret_cast<const uint4_t *>(wb + (size_t)r * K) : nullptr;
-    float aa[T_MAX], bb[T_MAX];
-#pragma unroll
-    for (int t = 0; t < T_MAX; ++t) {
-        aa[t] = 0.0f;
-        bb[t] = 0.0f;
-    }
-    for (int c = lane; c < nch; c += 64) {
-        const half8_t va = __builtin_bit_cast(half8_t, ra[c]);
-        half8_t vb = {};
-        if (swiglu)
-            vb = __builtin_bit_cast(half8_t, rb[c]);
-#pragma unroll
-        for (int t = 0; t < T_MAX; ++t) {
-            if (t < T) {
-                const half8_t xv = __builtin_bit_cast(
-                    half8_t, reinterpret_cast<const uint4_t *>(in + (size_t)t * K)[c]);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    half2_t xp = {xv[2 * m], xv[2 * m + 1]};
-                    half2_t ap = {va[2 * m], va[2 * m + 1]};
-                    aa[t] = dot2(ap, xp, aa[t]);
-                    if (swiglu) {
-                        half2_t bp = {vb[2 * m], vb[2 * m + 1]};
-                        bb[t] = dot2(bp, xp, bb[t]);
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < T_MAX; ++t) {
-        if (t >= T)
-            break;
-        float a = aa[t], b = bb[t];
-#pragma unroll
-        for (int st = 32; st >= 1; st >>= 1) {
-            a += __shfl_xor(a, st, 64);
-            if (swiglu)
-                b += __shfl_xor(b, st, 64);
-        }
-        if (lane == 0) {
-            if (swiglu)
-                hout[(size_t)t * R + r] = (f16)(a / (1.0f + expf(-a)) * b);
-            else
-                fout[(size_t)t * R + r] = a;
-        }
-    }
-}
-
-int launch_shared_gemv(const void *x, const void *wg, const void *wu, const void *wd, int T,
-                       int H, int Is, float *out, void *ws, hipStream_t s)
-{
-    f16 *h = static_cast<f16 *>(ws);   // [T][Is]
-    dim3 b(GEMV_WAVES * 64);
-    hipLaunchKernelGGL(gemv_f16_kernel<4>, dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
-                       (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, 1, h,
-                       (float *)nullptr);
-    MOE_LAUNCH_CHECK("gemv_f16_kernel(gate/up)");
-    hipLaunchKernelGGL(gemv_f16_kernel<4>, dim3((H + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
-                       (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is, 0,
-                       (f16 *)nullptr, out);
-    MOE_LAUNCH_CHECK("gemv_f16_kernel(down)");
     return MOE_OK;
 }
 

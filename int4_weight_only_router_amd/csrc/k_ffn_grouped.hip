@@ -87,15 +87,18 @@ __global__ __launch_bounds__(GT) void f16_gemm_kernel(GemmArgs a)
 
     const int R = (a.rows + BM - 1) / BM;
     const int NT = (a.nblk + 3) / 4;
+    // XCD-contiguous row ranges when every XCD gets a row tile; with fewer
+    // row tiles than XCDs, all workgroups share the items
+    const bool split = R >= NXCD;
     const int xcd = blockIdx.x % NXCD;
-    const int G = gridDim.x / NXCD;
-    const int r_lo = (int)((int64_t)R * xcd / NXCD);
-    const int r_hi = (int)((int64_t)R * (xcd + 1) / NXCD);
+    const int G = split ? (int)gridDim.x / NXCD : (int)gridDim.x;
+    const int r_lo = split ? (int)((int64_t)R * xcd / NXCD) : 0;
+    const int r_hi = split ? (int)((int64_t)R * (xcd + 1) / NXCD) : R;
     const int nitems = (r_hi - r_lo) * NT;
     const int K = a.K;
     const int nk = K / BK;
 
-    for (int it = (int)blockIdx.x / NXCD; it < nitems; it += G) {
+    for (int it = split ? (int)blockIdx.x / NXCD : (int)blockIdx.x; it < nitems; it += G) {
         const int rt = r_lo + it / NT;
         const int nt = it % NT;
         const int p0 = rt * BM, mrows = min(BM, a.rows - p0);

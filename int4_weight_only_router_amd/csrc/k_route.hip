@@ -86,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
                         *reinterpret_cast<const half8_t *>(xs + (size_t)tt * H + c * 8);
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        acc[tt] = acc[tt] + (float)xh[i] * (float)wh[i];
+                        acc[tt] = __builtin_fmaf((float)xh[i], (float)wh[i], acc[tt]);
                 }
             }
         }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
                             *reinterpret_cast<const half8_t *>(xs + (size_t)tt * H + c * 8);
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
-                            acc[tt] = acc[tt] + (float)xh[i] * (float)wh[i];
+                            acc[tt] = __builtin_fmaf((float)xh[i], (float)wh[i], acc[tt]);
                     }
                 }
             }

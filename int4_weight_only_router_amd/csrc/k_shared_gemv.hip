@@ -1,0 +1,112 @@
+// k_shared_gemv.hip -- the shared FP16 expert at small T: a GEMV pair
+// (gate/up + SwiGLU, then down) straight from the row-major fp16 weights.
+//
+// Horizon RunMap "03 / Arquitetura": the non-routed parts of the model stay
+// in FP16 outside the INT4 compression.
+#include "moe_common.h"
+
+namespace moe {
+
+// FP16 GEMV pair for the shared expert at small T (weights row-major fp16,
+// the layout the caller hands over).  One wave per output row, lanes along K
+// with 16-byte loads, every token's dot product from the same weight
+// registers, xor-butterfly reduction.
+//   swiglu=1: h[t][r] = fp16(silu(Wg[r].x_t) * (Wu[r].x_t)), r < R
+//   swiglu=0: out[t][r] = W[r].in_t (fp32), r < R
+constexpr int GEMV_WAVES = 4;
+
+template <int T_MAX>
+__global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
+    const f16 *__restrict__ in, const f16 *__restrict__ wa, const f16 *__restrict__ wb, int T,
+    int R, int K, int swiglu, f16 *__restrict__ hout, float *__restrict__ fout)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
+    if (r >= R)
+        return;
+    const int nch = K / 8;
+    const uint4_t *ra = reinterpret_cast<const uint4_t *>(wa + (size_t)r * K);
+    const uint4_t *rb = swiglu ? reinterpret_cast<const uint4_t *>(wb + (size_t)r * K) : nullptr;
+    float aa[T_MAX], bb[T_MAX];
+#pragma unroll
+    for (int t = 0; t < T_MAX; ++t) {
+        aa[t] = 0.0f;
+        bb[t] = 0.0f;
+    }
+    for (int c = lane; c < nch; c += 64) {
+        const half8_t va = __builtin_bit_cast(half8_t, ra[c]);
+        half8_t vb = {};
+        if (swiglu)
+            vb = __builtin_bit_cast(half8_t, rb[c]);
+#pragma unroll
+        for (int t = 0; t < T_MAX; ++t) {
+            if (t < T) {
+                const half8_t xv = __builtin_bit_cast(
+                    half8_t, reinterpret_cast<const uint4_t *>(in + (size_t)t * K)[c]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    half2_t xp = {xv[2 * m], xv[2 * m + 1]};
+                    half2_t ap = {va[2 * m], va[2 * m + 1]};
+                    aa[t] = dot2(ap, xp, aa[t]);
+                    if (swiglu) {
+                        half2_t bp = {vb[2 * m], vb[2 * m + 1]};
+                        bb[t] = dot2(bp, xp, bb[t]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T_MAX; ++t) {
+        if (t >= T)
+            continue;
+        float a = aa[t], b = bb[t];
+#pragma unroll
+        for (int st = 32; st >= 1; st >>= 1) {
+            a += __shfl_xor(a, st, 64);
+            if (swiglu)
+                b += __shfl_xor(b, st, 64);
+        }
+        if (lane == 0) {
+            if (swiglu)
+                hout[(size_t)t * R + r] = (f16)(a / (1.0f + expf(-a)) * b);
+            else
+                fout[(size_t)t * R + r] = a;
+        }
+    }
+}
+
+template <int T_MAX>
+static int launch_gemv_pair(const void *x, const void *wg, const void *wu, const void *wd, int T,
+                            int H, int Is, float *out, f16 *h, hipStream_t s)
+{
+    dim3 b(GEMV_WAVES * 64);
+    hipLaunchKernelGGL(gemv_f16_kernel<T_MAX>, dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
+                       (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, 1, h,
+                       (float *)nullptr);
+    MOE_LAUNCH_CHECK("gemv_f16_kernel(gate/up)");
+    hipLaunchKernelGGL(gemv_f16_kernel<T_MAX>, dim3((H + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
+                       (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is, 0,
+                       (f16 *)nullptr, out);
+    MOE_LAUNCH_CHECK("gemv_f16_kernel(down)");
+    return MOE_OK;
+}
+
+// T <= 32: a weight row is read once and dotted with every token's row
+// (accumulators for up to T_MAX tokens per lane).
+int launch_shared_gemv(const void *x, const void *wg, const void *wu, const void *wd, int T,
+                       int H, int Is, float *out, void *ws, hipStream_t s)
+{
+    f16 *h = static_cast<f16 *>(ws);   // [T][Is]
+    if (T <= 4)
+        return launch_gemv_pair<4>(x, wg, wu, wd, T, H, Is, out, h, s);
+    if (T <= 8)
+        return launch_gemv_pair<8>(x, wg, wu, wd, T, H, Is, out, h, s);
+    if (T <= 16)
+        return launch_gemv_pair<16>(x, wg, wu, wd, T, H, Is, out, h, s);
+    if (T <= 32)
+        return launch_gemv_pair<32>(x, wg, wu, wd, T, H, Is, out, h, s);
+    return set_error(MOE_EUNSUPPORTED, "shared GEMV: T=%d > 32", T);
+}
+
+}  // namespace moe

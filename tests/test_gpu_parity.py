@@ -159,6 +159,38 @@ def test_route_permute_fused_bit_exact(cfg, T):
           assert int(_np(ws[:4].view(torch.int32))[0]) == 0   # ticket back at zero
 
 
+@pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 5), (MI.E512, 1),
+                                   (MI.E512, 7), (MI.TINY, 16), (MI.OLMOE_DECODE, 64),
+                                   (MI.E512, 300)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_router_logits_pinned_order(cfg, T):
+    """The logits the router kernels leave in their workspace equal the
+    oracle's pinned-order fp32 logits bit for bit (chunk c of 8 elements into
+    partial c mod 64 by single-rounding FMAs, xor butterfly, then the bias)."""
+    say("logits %s T=%d" % (cfg.name, T))
+    x = MI.gen_x(cfg, T, step=11)
+    wr = MI.gen_router(cfg)
+    b = MI.zipf_bias(cfg)
+    n = T * cfg.k
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device=DEV)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(n, dtype=torch.int32, device=DEV)
+    inv = torch.empty(n, dtype=torch.int32, device=DEV)
+    wsb = M.moe_route_permute_workspace_bytes(T, cfg.k, cfg.E)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    M.moe_route_permute(f16(x), f16(wr), None if b is None else torch.from_numpy(b).to(DEV),
+                        T, cfg.H, cfg.E, cfg.k, 0, idx, w, counts, offsets, perm, inv, ws, wsb)
+    torch.cuda.synchronize()
+    # T <= 8: one fused launch, logits after a 256-byte ticket; else the
+    # logits kernel's T x E buffer at the start of the workspace
+    off = 256 if T <= 8 else 0
+    got = _np(ws[off:off + T * cfg.E * 4].view(torch.float32)).reshape(T, cfg.E)
+    _, _, ref = O.route(x, wr, b, cfg.k)
+    assert np.array_equal(got.view(np.int32), ref.view(np.int32))
+
+
 def test_route_ties_go_to_lower_index():
     cfg = MI.OLMOE_DECODE
     say("route ties")
@@ -276,7 +308,7 @@ def test_expert_ffn(cfg, T, regime):
 
 # -------------------------------------------------------- shared expert
 
-@pytest.mark.parametrize("T", [1, 3, 256, 4096])
+@pytest.mark.parametrize("T", [1, 3, 8, 17, 32, 33, 100, 256, 4096])
 def test_shared_ffn(T):
     cfg = MI.E512
     say("shared T=%d" % T)
@@ -287,7 +319,7 @@ def test_shared_ffn(T):
     ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
     M.moe_shared_ffn_f16(f16(x), f16(wg), f16(wu), f16(wd), T, cfg.H, cfg.Is, out, ws, wsb)
     torch.cuda.synchronize()
-    toks = np.arange(T) if T <= 16 else np.sort(
+    toks = np.arange(T) if T <= 32 else np.sort(
         np.random.default_rng(T).choice(T, 24, replace=False))
     ref = O.shared_ffn(x, wg, wu, wd, toks=toks)
     check_close(_np(out)[toks], ref, "shared T=%d" % T)
