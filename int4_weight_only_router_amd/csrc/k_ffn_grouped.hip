@@ -306,6 +306,120 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ----------------------------------------------------------------------------
+// FP16 GEMM of the shared expert at moderate T, when (row tiles) x (4-block
+// column tiles) would leave most CUs idle: one workgroup per (32-row tile,
+// 64-row weight block), its four waves splitting K.  Both operands come
+// straight from memory into the MFMA registers, 8 16-K steps in flight per
+// wave (the activation rows are a few MB at most and stay in L2; a weight
+// block is read once from HBM and then from the L2 of the XCD that holds all
+// its row tiles).  The waves' partial sums meet in LDS and are added in wave
+// order; the epilogue is the one of f16_gemm_kernel.
+constexpr int SK_D = 8;
+
+template <int MODE>
+__global__ __launch_bounds__(GT) void f16_splitk_kernel(GemmArgs a)
+{
+    static_assert(MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16, "FP16 modes only");
+    constexpr bool GATEUP = MODE == GM_GATEUP_F16;
+    __shared__ float red[3][2][16][64];   // partials of waves 1..3
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int R = (a.rows + 31) / 32;
+    const int id = blockIdx.x;
+    int blk, rt;
+    if (a.nblk % NXCD == 0) {   // every row tile of a block on one XCD (workgroup i -> XCD i % 8)
+        const int xcd = id % NXCD, li = id / NXCD;
+        blk = xcd + NXCD * (li / R);
+        rt = li % R;
+    } else {
+        blk = id / R;
+        rt = id % R;
+    }
+    const int p0 = rt * 32, mrows = min(32, a.rows - p0);
+    const int K = a.K, KW = K / 4;
+    const int k0 = wave * KW + 8 * half;
+    const int nst = KW / 16;
+    const _Float16 *arow = a.A + (size_t)(p0 + min(col, mrows - 1)) * K + k0;
+    const _Float16 *w0, *w1;
+    if constexpr (GATEUP) {
+        w0 = a.W0 + (size_t)(blk * 32 + col) * K + k0;
+        w1 = a.W1 + (size_t)(blk * 32 + col) * K + k0;
+    } else {
+        w0 = a.W0 + (size_t)(blk * 64 + col) * K + k0;
+        w1 = a.W0 + (size_t)(blk * 64 + 32 + col) * K + k0;
+    }
+    half8_t ra[SK_D], rb0[SK_D], rb1[SK_D];
+    auto load = [&](int i, int st) {   // unconditional: past the end re-reads the last step
+        ra[i] = ldg(reinterpret_cast<const half8_t *>(arow + 16 * st));
+        rb0[i] = ldg(reinterpret_cast<const half8_t *>(w0 + 16 * st));
+        rb1[i] = ldg(reinterpret_cast<const half8_t *>(w1 + 16 * st));
+    };
+#pragma unroll
+    for (int i = 0; i < SK_D; ++i)
+        load(i, min(i, nst - 1));
+    float16_t acc[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[n][r] = 0.0f;
+    int st = 0;
+    for (; st + SK_D < nst; st += SK_D) {
+#pragma unroll
+        for (int i = 0; i < SK_D; ++i) {
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[i], rb0[i], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[i], rb1[i], acc[1], 0, 0, 0);
+            load(i, min(st + SK_D + i, nst - 1));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SK_D; ++i) {
+        if (st + i < nst) {
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[i], rb0[i], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[i], rb1[i], acc[1], 0, 0, 0);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[wave - 1][n][r][lane] = acc[n][r];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[n][r] += red[w][n][r][lane];
+    // value r of lane l: token row 8*(r/4) + 4*(l/32) + (r%4), weight column l%32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row >= mrows)
+            continue;
+        const size_t p = (size_t)(p0 + row);
+        if constexpr (GATEUP) {
+            const float gv = acc[0][r], uv = acc[1][r];
+            const float hv = gv / (1.0f + expf(-gv)) * uv;
+            static_cast<_Float16 *>(a.out)[p * a.ldo + blk * 32 + col] = (_Float16)hv;
+        } else {
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                static_cast<float *>(a.out)[p * a.ldo + blk * 64 + n * 32 + col] = acc[n][r];
+        }
+    }
+}
+
 // Per-workgroup item record (LDS): expert, row range, column tile, blob.
 struct W4Item {
     int e, p0, p1, nt;
@@ -702,9 +816,19 @@ static int launch_w4(hipStream_t s, const GemmArgs &a)
     return MOE_OK;
 }
 
+constexpr int SPLITK_MAX_ROWS = 1024;   // shared expert: split-K kernel up to this many tokens
+
 template <int MODE>
 static int launch_mode(hipStream_t s, const GemmArgs &a)
 {
+    if constexpr (MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16) {
+        if (a.rows <= SPLITK_MAX_ROWS && a.K % 64 == 0) {
+            const int64_t grid = (int64_t)((a.rows + 31) / 32) * a.nblk;
+            hipLaunchKernelGGL((f16_splitk_kernel<MODE>), dim3((unsigned)grid), dim3(GT), 0, s, a);
+            MOE_LAUNCH_CHECK("f16_splitk_kernel");
+            return MOE_OK;
+        }
+    }
     if constexpr (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
         switch (pick_mf(a.rows, a.E, a.nblk)) {
         case 4: return launch_w4<MODE, 4>(s, a);

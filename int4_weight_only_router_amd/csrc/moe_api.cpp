@@ -59,7 +59,7 @@ constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tok
 constexpr int SMALL_MAX_T = 32;       // AUTO: small-batch kernel up to this many tokens
 constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
-constexpr int SHARED_GEMV_MAX_T = 32; // shared expert: GEMV up to this many tokens
+constexpr int SHARED_GEMV_MAX_T = 8;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
 {

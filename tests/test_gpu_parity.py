@@ -308,7 +308,7 @@ def test_expert_ffn(cfg, T, regime):
 
 # -------------------------------------------------------- shared expert
 
-@pytest.mark.parametrize("T", [1, 3, 8, 17, 32, 33, 100, 256, 4096])
+@pytest.mark.parametrize("T", [1, 3, 8, 17, 32, 33, 100, 256, 1024, 1025, 4096])
 def test_shared_ffn(T):
     cfg = MI.E512
     say("shared T=%d" % T)
