@@ -299,12 +299,8 @@ __device__ __forceinline__ void wait_steps(int younger)   // younger in 0..3
     else
         wait_vm<0>();
 }
-// Workgroup barrier after this wave's LDS reads have completed (no fence:
-// outstanding direct-to-LDS loads of later stages stay in flight).
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+// lds_barrier (moe_common.h) waits for this wave's LDS reads only: the
+// outstanding direct-to-LDS loads of later stages stay in flight.
 
 // ----------------------------------------------------------------------------
 // FP16 GEMM of the shared expert at moderate T, when (row tiles) x (4-block

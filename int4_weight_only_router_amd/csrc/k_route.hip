@@ -33,11 +33,11 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
     constexpr int NCH = H / 8;                // 8-element chunks of a row
     constexpr int NCL = (NCH + 63) / 64;      // chunks per lane
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nb = (E + 63) / 64;
     f16 *xs = reinterpret_cast<f16 *>(smem);                                    // [TT][H]
     float *lg = reinterpret_cast<float *>(smem + (size_t)TT * H * sizeof(f16));  // [TT][E]
-    Cand *cand = reinterpret_cast<Cand *>(lg + (size_t)TT * E);                  // [NW][nb*16]
-    Cand *sel = cand + (size_t)NW * nb * 16;                                     // [NW][16]
+    const size_t tsb = topk_scratch_bytes(E);
+    unsigned char *scr = smem + ((((size_t)TT * H * sizeof(f16) + (size_t)TT * E * sizeof(float)) + 15) & ~(size_t)15);   // [NW][tsb]
+    Cand *sel = reinterpret_cast<Cand *>(scr + (size_t)NW * tsb);               // [NW][16]
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
     Cand *st = sel + wave * 16;
     for (int tt = wave; tt < nt; tt += NW) {
         const float *l = lg + tt * E;
-        wave_topk(l, E, k, lane, st, cand + (size_t)wave * nb * 16);
+        wave_topk(l, E, k, lane, st, scr + (size_t)wave * tsb);
         __builtin_amdgcn_wave_barrier();
         const float m = st[0].v;
         float part = 0.0f;
@@ -237,14 +237,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_topk_kernel(
     int32_t *__restrict__ idx_out, float *__restrict__ w_out)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nb = (E + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     // per wave: the token's logits (E floats, 16-byte aligned), then candidates
     const size_t lbytes = ((size_t)E * sizeof(float) + 15) & ~(size_t)15;
-    float *l = reinterpret_cast<float *>(smem + (size_t)wave * (lbytes + (nb * 16 + 16) * sizeof(Cand)));
-    Cand *wc = reinterpret_cast<Cand *>(reinterpret_cast<unsigned char *>(l) + lbytes);
-    Cand *st = wc + nb * 16;
+    const size_t tsb = topk_scratch_bytes(E);
+    float *l = reinterpret_cast<float *>(smem + (size_t)wave * (lbytes + tsb + 16 * sizeof(Cand)));
+    unsigned char *wc = reinterpret_cast<unsigned char *>(l) + lbytes;
+    Cand *st = reinterpret_cast<Cand *>(wc + tsb);
     const int t = blockIdx.x * RT_WAVES + wave;
     if (t >= T)
         return;
@@ -294,9 +294,8 @@ int launch_route_batched(const void *x, const void *wr, const float *bias, int T
     default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
     }
     MOE_LAUNCH_CHECK("route_logits_kernel");
-    const size_t nb = (E + 63) / 64;
     const size_t lds = (size_t)RT_WAVES * ((((size_t)E * sizeof(float) + 15) & ~(size_t)15) +
-                                           (nb * 16 + 16) * sizeof(Cand));
+                                           topk_scratch_bytes(E) + 16 * sizeof(Cand));
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + RT_WAVES - 1) / RT_WAVES),
                        dim3(RT_WAVES * 64), lds, s, lg, T, E, k, flags, idx, w);
     MOE_LAUNCH_CHECK("route_topk_kernel");
@@ -314,7 +313,7 @@ int launch_route_batched(const void *x, const void *wr, const float *bias, int T
 // coherent path, and no workgroup ever waits for another.
 constexpr int RSPLIT_EPW = 4;
 
-template <int H, int TT, bool FUSE>
+template <int H, int TT, bool FUSE, bool BIGE>   // BIGE: E > 128
 __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
     const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
     int T, int E, int k, unsigned flags, unsigned *ticket, float *ws_logits,
@@ -392,10 +391,10 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
     if (!s_last)
         return;
 
-    const int nb = (E + 63) / 64;
+    const size_t tsb = topk_scratch_bytes(E);
     float *lg = reinterpret_cast<float *>(smem);                      // [T][E]
-    Cand *cand = reinterpret_cast<Cand *>(lg + (size_t)TT * E);       // [T][nb][k]
-    Cand *sel = cand + (size_t)TT * nb * 16;                          // [T][16]
+    unsigned char *scr = smem + ((((size_t)TT * E * sizeof(float)) + 15) & ~(size_t)15);   // [T][tsb]
+    Cand *sel = reinterpret_cast<Cand *>(scr + (size_t)TT * tsb);     // [T][16]
     int *sidx = reinterpret_cast<int *>(sel + TT * 16);               // [T*k]
     int *cnt = sidx + TT * 16;                                        // [E]
     for (int i = threadIdx.x; i < T * E; i += RSPLIT_EPW * 64)
@@ -407,7 +406,7 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
     // top-k, softmax and outputs: one wave per token
     for (int tt = wave; tt < T; tt += RSPLIT_EPW) {
         Cand *st = sel + tt * 16;
-        wave_topk(lg + tt * E, E, k, lane, st, cand + (size_t)tt * nb * 16);
+        wave_topk_t<BIGE ? 16 : 2>(lg + tt * E, E, k, lane, st, scr + (size_t)tt * tsb);
         __builtin_amdgcn_wave_barrier();
         const float m = st[0].v;
         float part = 0.0f;
@@ -435,10 +434,10 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
         }
     }
     if (FUSE) {
-        __syncthreads();
+        lds_barrier();   // the sort reads sidx from LDS; the idx/w stores need not land first
         if (wave == 0) {
             const int n = T * k;
-            if (E <= 128) {
+            if constexpr (!BIGE) {
                 wave_small_sort(sidx, n, E, counts, offsets, perm, inv_perm, lane);
             } else {
                 wave_count_scan(sidx, n, E, cnt, counts, offsets, lane);
@@ -460,14 +459,19 @@ static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, 
     unsigned *ticket = static_cast<unsigned *>(ws);
     float *lg = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
     const dim3 grid((E + RSPLIT_EPW - 1) / RSPLIT_EPW), block(RSPLIT_EPW * 64);
-    const size_t nb = (E + 63) / 64;
     const size_t xb = (size_t)8 * H * sizeof(f16);
-    const size_t lb = (size_t)8 * E * sizeof(float) + (size_t)8 * nb * 16 * sizeof(Cand) +
+    const size_t lb = (size_t)8 * E * sizeof(float) + 16 + (size_t)8 * topk_scratch_bytes(E) +
                       (size_t)8 * 16 * sizeof(Cand) + (size_t)(8 * 16 + E) * sizeof(int);
     const size_t lds = xb > lb ? xb : lb;
 #define MOE_RSPLIT(TT)                                                                          \
-    hipLaunchKernelGGL((route_split_kernel<H, TT, true>), grid, block, lds, s, x, wr, bias, T,  \
-                       E, k, flags, ticket, lg, idx, w, counts, offsets, perm, inv_perm)
+    if (E > 128)                                                                                \
+        hipLaunchKernelGGL((route_split_kernel<H, TT, true, true>), grid, block, lds, s, x, wr,  \
+                           bias, T, E, k, flags, ticket, lg, idx, w, counts, offsets, perm,      \
+                           inv_perm);                                                            \
+    else                                                                                        \
+        hipLaunchKernelGGL((route_split_kernel<H, TT, true, false>), grid, block, lds, s, x, wr, \
+                           bias, T, E, k, flags, ticket, lg, idx, w, counts, offsets, perm,      \
+                           inv_perm)
     if (T <= 1) MOE_RSPLIT(1);
     else if (T <= 2) MOE_RSPLIT(2);
     else if (T <= 4) MOE_RSPLIT(4);
@@ -500,10 +504,9 @@ template <int H>
 static int launch_route_h(const f16 *x, const f16 *wr, const float *bias, int T, int E, int k,
                           unsigned flags, int32_t *idx, float *w, hipStream_t s)
 {
-    const size_t nb = (E + 63) / 64;
     const size_t per_tok = (size_t)H * sizeof(f16) + (size_t)E * sizeof(float);
     auto lds_for = [&](int TT, int NW) {
-        return (size_t)TT * per_tok + (size_t)NW * (nb * 16 + 16) * sizeof(Cand);
+        return (size_t)TT * per_tok + 16 + (size_t)NW * (topk_scratch_bytes(E) + 16 * sizeof(Cand));
     };
 #define MOE_ROUTE_LAUNCH(TT, NW)                                                                 \
     hipLaunchKernelGGL((route_kernel<H, TT, NW>), dim3((T + TT - 1) / TT), dim3(NW * 64),        \

@@ -92,6 +92,14 @@ __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt) but not for its outstanding global loads or stores, which a
+// __syncthreads fence would drain first.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
     return (float)__builtin_bit_cast(f16, bits);
 }
