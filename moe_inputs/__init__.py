@@ -35,6 +35,7 @@ T_SHARED = 4     # shared (non-routed) expert weights ~ N(0, 0.02), fp16
 T_ZIPF = 5       # per-layer rank permutation for the Zipf logit bias
 T_PROMPT = 6     # partial-residency token streams (prompt, token)
 T_RESID = 7      # explicit residual input for single-layer cases
+T_SGATE = 8      # shared-expert gate vector ~ N(0, 0.02), fp16
 
 
 @dataclass(frozen=True)
@@ -53,6 +54,7 @@ class MoEConfig:
     layers: int = 1
     steps: int = 1
     Is: int = 0
+    shared_gate: bool = False
     zipf_s: float = 0.0
     residual: bool = False
     renorm: bool = False
@@ -78,7 +80,15 @@ PARTIAL = MoEConfig(5, "olmoe_partial", H=2048, E=64, k=8, I=1024, g=128,
                     capacity=30, spares=8, prompts=12, blocks=3,
                     tokens_per_prompt=128, warmup_tokens=64)
 
-CONFIGS = {c.cid: c for c in (TINY, OLMOE_DECODE, OLMOE_BATCHED, E512, PARTIAL)}
+# The 60-expert top-4 model family of the technical preview's residency table
+# (top4-fused-v1 rows).  The pages print no layer shape for it; these sizes are
+# the published Qwen1.5-MoE-A2.7B architecture (hidden 2048, 60 routed experts
+# of intermediate 1408, top-4 without renormalisation, one shared expert of
+# intermediate 5632 scaled by a per-token sigmoid gate).
+QWEN = MoEConfig(6, "qwen_gated_shared", H=2048, E=60, k=4, I=1408, g=128,
+                 T=(1, 256, 4096), Is=5632, shared_gate=True)
+
+CONFIGS = {c.cid: c for c in (TINY, OLMOE_DECODE, OLMOE_BATCHED, E512, PARTIAL, QWEN)}
 
 
 def rng_for(cid: int, tensor: int, layer: int = 0, expert: int = 0,
@@ -136,6 +146,11 @@ def gen_shared(cfg: MoEConfig):
     wu = _normal(rng, (cfg.Is, cfg.H), 0.02).astype(np.float16)
     wd = _normal(rng, (cfg.H, cfg.Is), 0.02).astype(np.float16)
     return wg, wu, wd
+
+
+def gen_shared_gate(cfg: MoEConfig) -> np.ndarray:
+    """Shared-expert gate vector [H] fp16, N(0, 0.02)."""
+    return _normal(rng_for(cfg.cid, T_SGATE), (cfg.H,), 0.02).astype(np.float16)
 
 
 def zipf_bias(cfg: MoEConfig, layer: int = 0, s: float | None = None) -> np.ndarray | None:

@@ -41,11 +41,13 @@ def lib():
         L.oracle_expert_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         vp, i32, vp]
         L.oracle_shared_ffn.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, i32, vp]
-        L.oracle_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.oracle_shared_gate.argtypes = [vp, vp, i32, i32, vp, i32, vp]
+        L.oracle_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
         L.oracle_pool_sim.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp]
         for name in ("oracle_blob_layout", "oracle_quantize_rows", "oracle_pack_expert",
                      "oracle_dequant_rows", "oracle_route", "oracle_permute",
-                     "oracle_expert_ffn", "oracle_shared_ffn", "oracle_combine",
+                     "oracle_expert_ffn", "oracle_shared_ffn", "oracle_shared_gate",
+                     "oracle_combine",
                      "oracle_pool_sim"):
             getattr(L, name).restype = i32
         _lib = L
@@ -200,8 +202,25 @@ def shared_ffn(x, wg, wu, wd, toks=None):
     return s
 
 
-def combine(y, inv_perm, w, shared=None, residual=None):
-    """Returns (out fp16 as np.float16 [T,H], pre-rounding fp64 value)."""
+def shared_gate(x, wsg, toks=None):
+    """Per-token sigmoid gate of the shared expert, fp64 [ntoks]."""
+    x = _u16(x)
+    wsg = _u16(wsg).reshape(-1)
+    T, H = x.shape
+    assert wsg.size == H
+    if toks is None:
+        tk, n = None, T
+    else:
+        tk = np.ascontiguousarray(toks, dtype=np.int32)
+        n = tk.size
+    gt = np.empty(n, np.float64)
+    _check(lib().oracle_shared_gate(_p(x), _p(wsg), T, H, _p(tk), n, _p(gt)), "shared_gate")
+    return gt
+
+
+def combine(y, inv_perm, w, shared=None, residual=None, shared_gate=None):
+    """Returns (out fp16 as np.float16 [T,H], pre-rounding fp64 value).
+    shared_gate (fp64 [T]) scales the shared rows when given."""
     y = np.ascontiguousarray(y, dtype=np.float64)
     inv = np.ascontiguousarray(inv_perm, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -209,9 +228,11 @@ def combine(y, inv_perm, w, shared=None, residual=None):
     H = y.shape[1]
     sh = None if shared is None else np.ascontiguousarray(shared, dtype=np.float64)
     res = None if residual is None else _u16(residual)
+    gt = None if shared_gate is None else np.ascontiguousarray(shared_gate, dtype=np.float64)
+    assert gt is None or (sh is not None and gt.size == T)
     out = np.empty((T, H), np.uint16)
     o64 = np.empty((T, H), np.float64)
-    _check(lib().oracle_combine(_p(y), _p(inv), _p(w), _p(sh), _p(res), T, H, k,
+    _check(lib().oracle_combine(_p(y), _p(inv), _p(w), _p(sh), _p(gt), _p(res), T, H, k,
                                 _p(out), _p(o64)), "combine")
     return out.view(np.float16), o64
 
@@ -230,13 +251,15 @@ def pool_sim(L, E, C_, shift, k, ev_layer, ev_ids):
 
 
 def moe_layer(x, wr, blobs, H, I, E, k, g, bias=None, renorm=False,
-              shared=None, residual=None):
+              shared=None, residual=None, shared_gate_w=None):
     """The whole layer in the oracle: route, permute, expert FFN (all rows),
-    optional shared FFN, combine.  Returns a dict of every intermediate."""
+    optional shared FFN (optionally gated), combine.  Returns a dict of every
+    intermediate."""
     idx, w, logits = route(x, wr, bias, k, renorm)
     counts, offsets, perm, inv = permute(idx, E)
     y = expert_ffn(x, perm, offsets, blobs, H, I, E, k, g)
     s = None if shared is None else shared_ffn(x, *shared)
-    out, o64 = combine(y, inv, w, s, residual)
+    gt = None if shared_gate_w is None else shared_gate(x, shared_gate_w)
+    out, o64 = combine(y, inv, w, s, residual, gt)
     return dict(idx=idx, w=w, logits=logits, counts=counts, offsets=offsets, perm=perm,
-                inv_perm=inv, y=y, shared=s, out=out, out_f64=o64)
+                inv_perm=inv, y=y, shared=s, gate=gt, out=out, out_f64=o64)

@@ -506,19 +506,48 @@ int oracle_shared_ffn(const uint16_t *x, const uint16_t *wg, const uint16_t *wu,
     return OR_OK;
 }
 
+/*
+ * Shared-expert gate.  The pages name a second model whose layers have 60
+ * routed experts with a top-4 executor ([HR] "Prévia Técnica", the
+ * top4-fused-v1 rows of the residency results) but print no layer shape and no
+ * form of its shared path.  READING: that model family scales its shared
+ * expert's output, per token, by a sigmoid of one more linear function of the
+ * token, g_t = 1 / (1 + exp(-sum_c x[t,c] * wsg[c])), wsg an fp16 vector of
+ * length H with no bias.  Evaluated in fp64 for the tokens in `toks` (NULL =
+ * all T); gate is [ntoks].
+ */
+int oracle_shared_gate(const uint16_t *x, const uint16_t *wsg, int T, int H,
+                       const int32_t *toks, int ntoks, double *gate)
+{
+    if (!x || !wsg || !gate || H <= 0 || T < 0)
+        return OR_EINVAL;
+    if (!toks)
+        ntoks = T;
+    for (int r = 0; r < ntoks; r++) {
+        int t = toks ? toks[r] : r;
+        double a = 0.0;
+        for (int c = 0; c < H; c++)
+            a += H2D(x[(int64_t)t * H + c]) * H2D(wsg[c]);
+        gate[r] = 1.0 / (1.0 + exp(-a));
+    }
+    return OR_OK;
+}
+
 /* --------------------------------------------------------------- combine */
 
 /*
  * Router-weighted combine ([HR] "03": the expert results go back to the rest
  * of the model weighted by the router).  READING:
- *   out[t] = fp16_rne( residual[t] + sum_j w[t,j] * y[inv_perm[t*k+j]] + s[t] )
- * evaluated in fp64; residual (fp16) and s (fp64) are optional (NULL).
- * y is indexed by sorted row: [T*k][H].  out_f64 (optional) gets the value
- * before the final rounding.
+ *   out[t] = fp16_rne( residual[t] + sum_j w[t,j] * y[inv_perm[t*k+j]] + G_t s[t] )
+ * evaluated in fp64; residual (fp16) and s (fp64) are optional (NULL).  G_t
+ * is shared_gate[t] when a gate is given (the gated shared expert above),
+ * else 1.  y is indexed by sorted row: [T*k][H].  out_f64 (optional) gets the
+ * value before the final rounding.
  */
 int oracle_combine(const double *y, const int32_t *inv_perm, const float *w,
-                   const double *shared, const uint16_t *residual,
-                   int T, int H, int k, uint16_t *out, double *out_f64)
+                   const double *shared, const double *shared_gate,
+                   const uint16_t *residual, int T, int H, int k, uint16_t *out,
+                   double *out_f64)
 {
     if (!y || !inv_perm || !w || !out || T < 0 || H <= 0 || k <= 0)
         return OR_EINVAL;
@@ -530,7 +559,7 @@ int oracle_combine(const double *y, const int32_t *inv_perm, const float *w,
                 acc += (double)w[(int64_t)t * k + j] * y[(int64_t)p * H + o];
             }
             if (shared)
-                acc += shared[(int64_t)t * H + o];
+                acc += (shared_gate ? shared_gate[t] : 1.0) * shared[(int64_t)t * H + o];
             out[(int64_t)t * H + o] = oracle_f64_to_f16(acc);
             if (out_f64)
                 out_f64[(int64_t)t * H + o] = acc;

@@ -384,3 +384,82 @@ def test_shared_ffn_equals_dense():
     assert np.allclose(s, d, rtol=1e-11, atol=1e-13)
     s2 = O.shared_ffn(x, wg, wu, wd, toks=[2, 0])
     assert np.array_equal(s2, s[[2, 0]])
+
+
+# ------------------------------------------------- gated shared expert
+
+def test_shared_gate_dot_matches_pinned_router_logit():
+    """The gate's logit is a dot of x with one more fp16 row: the oracle's
+    fp64 gate must be the sigmoid of a value within the recursive-summation
+    bound of the router's separately pinned fp32 logit for that row."""
+    cfg = MI.QWEN
+    x = MI.gen_x(cfg, 6)
+    wsg = MI.gen_shared_gate(cfg)
+    gt = O.shared_gate(x, wsg)
+    _, _, l = O.route(x, wsg[None, :], None, k=1)
+    absd = np.abs(x.astype(np.float64)) @ np.abs(wsg.astype(np.float64))
+    u = 2.0 ** -24
+    gamma = cfg.H * u / (1 - cfg.H * u)
+    a = np.log(gt / (1.0 - gt))          # logit recovered from the gate
+    assert np.all(np.abs(a - l[:, 0].astype(np.float64)) <= gamma * absd + 1e-12)
+    assert np.all((gt > 0.5) == (l[:, 0] > 0))
+
+
+def test_shared_gate_special_cases():
+    cfg = MI.QWEN
+    x = MI.gen_x(cfg, 5)
+    wsg = MI.gen_shared_gate(cfg)
+    # zero gate vector: exactly one half
+    assert np.all(O.shared_gate(x, np.zeros(cfg.H, np.float16)) == 0.5)
+    # negating the vector mirrors the gate about one half
+    g1 = O.shared_gate(x, wsg)
+    g2 = O.shared_gate(x, -wsg)
+    assert np.allclose(g1 + g2, 1.0, rtol=0, atol=1e-15)
+    # saturation: logit +H gives exactly 1, -H exactly 0 in fp64
+    ones = np.ones((2, cfg.H), np.float16)
+    assert np.all(O.shared_gate(ones, np.ones(cfg.H, np.float16)) == 1.0)
+    assert np.all(O.shared_gate(ones, -np.ones(cfg.H, np.float16)) == 0.0)
+    # token selection
+    assert np.array_equal(O.shared_gate(x, wsg, toks=[4, 1]), g1[[4, 1]])
+
+
+def test_gated_combine_scales_only_the_shared_term():
+    """Gating is the same as pre-scaling the shared rows; the routed and
+    residual terms are untouched (gate 0 removes only the shared term, gate 1
+    is the ungated combine)."""
+    rng = np.random.default_rng(8)
+    T, k, H = 5, 4, 64
+    y = rng.standard_normal((T * k, H))
+    inv = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    s = rng.standard_normal((T, H))
+    r = rng.standard_normal((T, H)).astype(np.float16)
+    gt = np.array([0.5, 0.25, 0.0, 1.0, 0.8125])
+    out, o64 = O.combine(y, inv, w, s, r, shared_gate=gt)
+    out2, o642 = O.combine(y, inv, w, gt[:, None] * s, r)
+    assert np.array_equal(o64, o642) and np.array_equal(out, out2)
+    _, none64 = O.combine(y, inv, w, None, r)
+    _, full64 = O.combine(y, inv, w, s, r)
+    assert np.array_equal(o64[2], none64[2])
+    assert np.array_equal(o64[3], full64[3])
+
+
+def test_gated_layer_is_routed_plus_gate_times_dense_shared():
+    cfg = MI.TINY
+    T = 4
+    x = MI.gen_x(cfg, T)
+    wr = MI.gen_router(cfg)
+    blobs = [O.pack_expert(*MI.gen_expert(cfg, 0, e), cfg.g) for e in range(cfg.E)]
+    rng = np.random.default_rng(3)
+    Is = 128
+    sh = tuple(rng.normal(0, 0.02, sz).astype(np.float16)
+               for sz in ((Is, cfg.H), (Is, cfg.H), (cfg.H, Is)))
+    wsg = rng.normal(0, 0.05, cfg.H).astype(np.float16)
+    r = O.moe_layer(x, wr, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, shared=sh,
+                    shared_gate_w=wsg)
+    r0 = O.moe_layer(x, wr, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g)
+    xs = x.astype(np.float64)
+    dense = _dense_swiglu(xs, *(a.astype(np.float64) for a in sh))
+    gate = 1.0 / (1.0 + np.exp(-(xs @ wsg.astype(np.float64))))
+    assert np.allclose(r["out_f64"], r0["out_f64"] + gate[:, None] * dense, rtol=1e-11,
+                       atol=1e-13)
