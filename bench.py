@@ -8,13 +8,15 @@ per step, x_{l+1} = fp16(x_l + MoE_l(x_l)).  A step is route -> permute ->
 routed expert FFN -> combine for all 16 layers.  Prints one JSON line.
 
     python bench.py [--steps 128] [--warmup 16] [--graph/--no-graph]
-                    [--no-cpu-baseline] [--workload decode|batched|e512|partial|copy] [--T ...]
+                    [--no-cpu-baseline] [--workload decode|batched|e512|qwen|partial|copy] [--T ...]
 
 Other workloads (one JSON line each, not the headline):
   batched  single OLMoE-shaped layers at T = 64, 512, 4096 (grouped INT4
            FP16-MFMA path): per-call times, MFMA and HBM fractions.
   e512     single 512-expert layers (top-10, I = 512, FP16 shared expert with
            I_s = 512, Zipf(1.1) router bias) at T = 1, 256, 4096.
+  qwen     single 60-expert layers (top-4, I = 1408, FP16 shared expert with
+           I_s = 5632 scaled by a per-token sigmoid gate) at T = 1, 256, 4096.
   partial  16 layers with 30 of 64 experts per layer in an HBM slot pool and
            the INT4 source in pinned host memory: tokens/s and H2D GiB.
   copy     a 1 GiB device copy, the reference for HBM byte counters.
@@ -281,21 +283,24 @@ def run_batched(args, torch, M, cfg):
     dev = "cuda:0"
     lays, blob_bytes = build_layers(cfg, 1, dev, torch, M)
     base = lays[0]
-    shared = None
+    shared = gate = None
     if cfg.Is:
         shared = tuple(torch.from_numpy(w).to(dev) for w in MI.gen_shared(cfg))
+        if cfg.shared_gate:
+            gate = torch.from_numpy(MI.gen_shared_gate(cfg)).to(dev)
     # at least 16 calls per captured graph, so that the replay's own launch
     # cost is shared (and the touched weights of 16 small-T calls still
-    # exceed the last-level cache)
+    # exceed the last-level cache); every copy has its own shared weights too
     nc = max(16, -(-3 * 256 * 2 ** 20 // (cfg.E * blob_bytes)))
     copies = [base]
     for _ in range(nc - 1):
         bl = base._blobs.clone()
+        sh = None if shared is None else tuple(w.clone() for w in shared)
         lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, base.router, blob_table(bl), base.bias,
-                       shared, device=dev)
+                       sh, device=dev, shared_gate=gate)
         lay._blobs = bl
         copies.append(lay)
-    base.shared = shared
+    base.shared, base.shared_gate = shared, gate
     Ts = [int(t) for t in args.T.split(",")] if args.T else list(cfg.T)
     reps = max(1, args.steps // nc)
     lines = []
@@ -321,7 +326,7 @@ def run_batched(args, torch, M, cfg):
                                  b.shared_ws.numel())
 
         parts = {"route_permute": each(lambda lay, b: lay.route_permute(x, b)),
-                 "expert_ffn": each(ffn), "combine": each(lambda lay, b: lay.combine(b)),
+                 "expert_ffn": each(ffn), "combine": each(lambda lay, b: lay.combine(b, x=x)),
                  "layer": each(lambda lay, b: lay.forward(x, b))}
         if shared is not None:
             parts["shared"] = each(shr)
@@ -333,7 +338,7 @@ def run_batched(args, torch, M, cfg):
         f_shared = 2.0 * T * 3 * cfg.H * cfg.Is
         f_router = 2.0 * T * cfg.E * cfg.H
         b_alg = (touched * blob_bytes + cfg.E * cfg.H * 2 + 3 * cfg.H * cfg.Is * 2
-                 + 2 * T * cfg.H * 2)
+                 + 2 * T * cfg.H * 2 + (cfg.H * 2 if cfg.shared_gate else 0))
         tf = f_routed / (us["expert_ffn"] * 1e-6) / 1e12
         ffn_bytes = touched * blob_bytes
         line = {"T": T, "regime": {1: "decode", 2: "batched", 3: "small"}.get(b.regime, b.regime),
@@ -347,11 +352,13 @@ def run_batched(args, torch, M, cfg):
                 "layer_hbm_frac": round(b_alg / (us["layer"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         if cfg.Is:
             line["shared_tflops"] = round(f_shared / (us["shared"] * 1e-6) / 1e12, 1)
+            line["shared_hbm_frac"] = round(3 * cfg.H * cfg.Is * 2 / (us["shared"] * 1e-6) / 1e9
+                                            / HBM_PEAK_GBS, 4)
         lines.append(line)
         log(str(line))
     return {"workload": cfg.name, "weight_copies": nc, "regime": args.regime,
             "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I, "g": cfg.g, "Is": cfg.Is,
-                       "zipf_s": cfg.zipf_s},
+                       "shared_gate": cfg.shared_gate, "zipf_s": cfg.zipf_s},
             "results": lines}
 
 
@@ -490,11 +497,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", choices=["decode", "batched", "e512", "partial", "copy"],
+    ap.add_argument("--workload", choices=["decode", "batched", "e512", "qwen", "partial", "copy"],
                     default="decode")
-    ap.add_argument("--T", default="", help="batched/e512: comma-separated batch sizes")
+    ap.add_argument("--T", default="", help="batched/e512/qwen: comma-separated batch sizes")
     ap.add_argument("--regime", choices=sorted(REGIMES), default="auto",
-                    help="batched/e512: routed-FFN regime (auto: the library's choice)")
+                    help="batched/e512/qwen: routed-FFN regime (auto: the library's choice)")
     ap.add_argument("--blocks", type=int, default=3)
     ap.add_argument("--prompts", type=int, default=12)
     ap.add_argument("--tokens", type=int, default=128)
@@ -516,10 +523,10 @@ def main():
     M.lib()
     if args.workload == "decode":
         res = run_decode(args, torch, M)
-    elif args.workload in ("batched", "e512"):
+    elif args.workload in ("batched", "e512", "qwen"):
         import moe_inputs as MI
-        res = run_batched(args, torch, M, MI.OLMOE_BATCHED if args.workload == "batched"
-                          else MI.E512)
+        res = run_batched(args, torch, M, {"batched": MI.OLMOE_BATCHED, "e512": MI.E512,
+                                           "qwen": MI.QWEN}[args.workload])
     elif args.workload == "partial":
         res = run_partial(args, torch, M)
     else:

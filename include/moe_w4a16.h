@@ -259,6 +259,26 @@ int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_per
                 const float *topk_w, const float *shared_f32, const void *residual_f16,
                 int T, int H, int k, void *out_f16, hipStream_t stream);
 
+/*
+ * Combine with a gated shared expert.  The pages run a second model family
+ * with 60 routed experts per layer and a top-4 executor (Horizon RunMap
+ * technical preview, residency results table, top4-fused-v1 rows) without
+ * printing its layer; in that family the shared expert's output is scaled per
+ * token by a sigmoid of one more linear function of the token (a reading; no
+ * bias term).  Same as moe_combine except that the shared term is
+ *   G_t * s[t,c],   G_t = 1 / (1 + exp(-sum_c x[t,c] * wsg[c])),
+ * the dot taken in fp32 (any order; G_t is not a discrete decision).
+ *   shared_f32         device fp32 [T][H], required
+ *   x_f16              device fp16 [T][H], the layer input; 16-byte aligned
+ *   shared_gate_w_f16  device fp16 [H]; 16-byte aligned
+ * Errors: MOE_EINVAL for a null shared/x/gate pointer or misalignment, else
+ * as moe_combine.
+ */
+int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                      const float *topk_w, const float *shared_f32, const void *x_f16,
+                      const void *shared_gate_w_f16, const void *residual_f16, int T, int H,
+                      int k, void *out_f16, hipStream_t stream);
+
 /* ------------------------------------------------- expert slot pool */
 /*
  * Partial residency (Horizon RunMap "03 / Arquitetura",

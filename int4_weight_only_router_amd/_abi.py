@@ -14,7 +14,7 @@ __all__ = [
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "PoolConfig", "PoolStats", "PoolLayerArgs",
+    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "PoolConfig", "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_retire",
     "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
@@ -32,7 +32,8 @@ EXPORTS = [
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "moe_pool_create", "moe_pool_prepare",
+    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "moe_pool_create",
+    "moe_pool_prepare",
     "moe_pool_layer_forward",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
 ]
@@ -96,6 +97,8 @@ def _declare(L):
         "moe_shared_ffn_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_shared_ffn_f16": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]),
         "moe_combine": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_combine_gated": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp,
+                                    vp]),
         "moe_pool_create": (i32, [C.POINTER(PoolConfig), vp, C.POINTER(vp)]),
         "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
         "moe_pool_layer_forward": (i32, [vp, i32, C.POINTER(PoolLayerArgs), vp,
@@ -242,6 +245,13 @@ def moe_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, residual_f16
     return _check(lib().moe_combine(_p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w),
                                     _p(shared_f32), _p(residual_f16), T, H, k, _p(out_f16),
                                     _s(stream)))
+
+
+def moe_combine_gated(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16, gate_w_f16,
+                      residual_f16, T, H, k, out_f16, stream=None):
+    return _check(lib().moe_combine_gated(_p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w),
+                                          _p(shared_f32), _p(x_f16), _p(gate_w_f16),
+                                          _p(residual_f16), T, H, k, _p(out_f16), _s(stream)))
 
 
 def moe_pool_create(cfg: PoolConfig, pinned_src_ptrs):

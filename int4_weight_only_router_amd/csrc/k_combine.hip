@@ -6,23 +6,57 @@
 //   Y_j = sum over slices of y[slice][inv_perm[t*k+j]][c] (slice order),
 // summed in fp32 in exactly that order (j ascending, then shared, then
 // residual), so repeated runs give identical bits.
+//
+// Gated shared expert (the 60-expert top-4 model family of the Horizon RunMap
+// technical preview, results table): the shared term becomes G_t * s[t,c] with
+// G_t = sigmoid(x_t . wsg), the dot taken in fp32 by the block that needs it.
 #include "moe_common.h"
 
 namespace moe {
 
+// Shared-expert gate of one token: fp32 dot of x_t with wsg by the block's 256
+// threads (8 columns per thread per pass), reduced over the block, then the
+// sigmoid.  Every thread returns the same value.
+__device__ inline float shared_gate_256(const f16 *__restrict__ xt, const f16 *__restrict__ wsg,
+                                        int H, float *red)
+{
+    float a = 0.0f;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        const half8_t xv = *reinterpret_cast<const half8_t *>(xt + c);
+        const half8_t wv = *reinterpret_cast<const half8_t *>(wsg + c);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            a = __builtin_fmaf((float)xv[m], (float)wv[m], a);
+    }
+#pragma unroll
+    for (int off = 32; off; off >>= 1)
+        a += __shfl_xor(a, off, 64);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = (red[0] + red[1]) + (red[2] + red[3]);
+    return 1.0f / (1.0f + expf(-a));
+}
+
 // Decode partials: fp32 y [S][T*k][H].  Block = 16 expert slots x 16 columns;
 // thread (j, c) sums the S slices of its (expert, column) sequentially, then
-// the j = 0 threads fold the k weighted values in order.
+// the j = 0 threads fold the k weighted values in order.  GATED: the shared
+// term is scaled by the token's gate (x, wsg).
+template <bool GATED>
 __global__ __launch_bounds__(256) void combine_slices_kernel(
     const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
-    const float *__restrict__ w, const float *__restrict__ shared, const f16 *residual, int T,
-    int H, int k, f16 *out)
+    const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
+    const f16 *__restrict__ wsg, const f16 *residual, int T, int H, int k, f16 *out)
 {
     __shared__ float part[16][17];
+    __shared__ float red[4];
     const int cc = threadIdx.x & 15, j = threadIdx.x >> 4;
     const int t = blockIdx.y;
     const int c = blockIdx.x * 16 + cc;
     const size_t ntk = (size_t)T * k;
+    float gate = 1.0f;
+    if constexpr (GATED)
+        gate = shared_gate_256(x + (size_t)t * H, wsg, H, red);
     if (j < k && c < H) {
         const size_t p = (size_t)inv_perm[(size_t)t * k + j];
         const float *src = y + p * H + c;
@@ -48,7 +82,7 @@ __global__ __launch_bounds__(256) void combine_slices_kernel(
         for (int jj = 0; jj < k; ++jj)
             acc += part[jj][cc];
         if (shared)
-            acc += shared[(size_t)t * H + c];
+            acc += GATED ? gate * shared[(size_t)t * H + c] : shared[(size_t)t * H + c];
         if (residual)
             acc += (float)residual[(size_t)t * H + c];
         out[(size_t)t * H + c] = (f16)acc;
@@ -97,19 +131,81 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
     *reinterpret_cast<half8_t *>(out + (size_t)t * H + c0) = o;
 }
 
+// One slice with the gated shared term: one block per token; the block first
+// forms the token's gate, then each thread handles 8 columns per pass.
+template <typename YT>
+__global__ __launch_bounds__(256) void combine_rows_gated_kernel(
+    const YT *__restrict__ y, const int32_t *__restrict__ inv_perm, const float *__restrict__ w,
+    const float *__restrict__ shared, const f16 *__restrict__ x, const f16 *__restrict__ wsg,
+    const f16 *residual, int H, int k, f16 *out)
+{
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const float gate = shared_gate_256(x + (size_t)t * H, wsg, H, red);
+    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const size_t p = (size_t)inv_perm[(size_t)t * k + j];
+            const float wj = w[(size_t)t * k + j];
+            const YT *src = y + p * H + c0;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                acc[m] += wj * (float)src[m];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m] += gate * shared[(size_t)t * H + c0 + m];
+        if (residual) {
+            const half8_t r = *reinterpret_cast<const half8_t *>(residual + (size_t)t * H + c0);
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                acc[m] += (float)r[m];
+        }
+        half8_t o;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            o[m] = (f16)acc[m];
+        *reinterpret_cast<half8_t *>(out + (size_t)t * H + c0) = o;
+    }
+}
+
 int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, const float *w,
-                   const float *shared, const void *residual, int T, int H, int k, void *out,
-                   hipStream_t s)
+                   const float *shared, const void *x_f16, const void *gate_w_f16,
+                   const void *residual, int T, int H, int k, void *out, hipStream_t s)
 {
     if (T == 0)
         return MOE_OK;
     const f16 *res = static_cast<const f16 *>(residual);
+    const f16 *xh = static_cast<const f16 *>(x_f16);
+    const f16 *gw = static_cast<const f16 *>(gate_w_f16);
+    const bool gated = gw != nullptr;
     f16 *o = static_cast<f16 *>(out);
     if (y_dtype == MOE_DTYPE_F32 && S > 1) {
         dim3 grid((H + 15) / 16, T);
-        hipLaunchKernelGGL(combine_slices_kernel, grid, dim3(256), 0, s,
-                           static_cast<const float *>(y), S, inv_perm, w, shared, res, T, H, k, o);
+        if (gated)
+            hipLaunchKernelGGL(combine_slices_kernel<true>, grid, dim3(256), 0, s,
+                               static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
+                               T, H, k, o);
+        else
+            hipLaunchKernelGGL(combine_slices_kernel<false>, grid, dim3(256), 0, s,
+                               static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
+                               T, H, k, o);
         MOE_LAUNCH_CHECK("combine_slices_kernel");
+        return MOE_OK;
+    }
+    if (gated) {
+        if (y_dtype == MOE_DTYPE_F32)
+            hipLaunchKernelGGL(combine_rows_gated_kernel<float>, dim3(T), dim3(256), 0, s,
+                               static_cast<const float *>(y), inv_perm, w, shared, xh, gw, res, H,
+                               k, o);
+        else
+            hipLaunchKernelGGL(combine_rows_gated_kernel<f16>, dim3(T), dim3(256), 0, s,
+                               static_cast<const f16 *>(y), inv_perm, w, shared, xh, gw, res, H,
+                               k, o);
+        MOE_LAUNCH_CHECK("combine_rows_gated_kernel");
         return MOE_OK;
     }
     const size_t n = (size_t)T * (H / 8);

@@ -50,7 +50,8 @@ int launch_shared_gemv(const void *, const void *, const void *, const void *, i
 int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
                           float *, void *, hipStream_t);
 int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
-                   const void *, int, int, int, void *, hipStream_t);
+                   const void *, const void *, const void *, int, int, int, void *,
+                   hipStream_t);
 int launch_quantize(const float *, const float *, const float *, int, int, int, int, void *,
                     hipStream_t);
 int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
@@ -364,26 +365,53 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
     return launch_shared_batched(x_f16, wg, wu, wd, T, H, Is, out_f32, ws, stream);
 }
 
+static int check_combine_args(const char *fn, const void *y, int y_dtype, int y_slices,
+                              const int32_t *inv_perm, const float *topk_w, int T, int H, int k,
+                              const void *out_f16)
+{
+    if (T < 0 || H <= 0 || k <= 0 || k > 16 || y_slices <= 0)
+        return set_error(MOE_EINVAL, "%s: bad sizes T=%d H=%d k=%d slices=%d", fn, T, H, k,
+                         y_slices);
+    if (y_dtype != MOE_DTYPE_F16 && y_dtype != MOE_DTYPE_F32)
+        return set_error(MOE_EINVAL, "%s: bad y dtype %d", fn, y_dtype);
+    if (y_dtype == MOE_DTYPE_F16 && y_slices != 1)
+        return set_error(MOE_EINVAL, "%s: fp16 y has exactly one slice", fn);
+    if (H % 8)
+        return set_error(MOE_EUNSUPPORTED, "%s: H=%d must be a multiple of 8", fn, H);
+    if (T > 0 && (!y || !inv_perm || !topk_w || !out_f16))
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    return MOE_OK;
+}
+
 int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
                 const float *topk_w, const float *shared_f32, const void *residual_f16, int T,
                 int H, int k, void *out_f16, hipStream_t stream)
 {
     clear_error();
-    if (T < 0 || H <= 0 || k <= 0 || k > 16 || y_slices <= 0)
-        return set_error(MOE_EINVAL, "moe_combine: bad sizes T=%d H=%d k=%d slices=%d", T, H, k,
-                         y_slices);
-    if (y_dtype != MOE_DTYPE_F16 && y_dtype != MOE_DTYPE_F32)
-        return set_error(MOE_EINVAL, "moe_combine: bad y dtype %d", y_dtype);
-    if (y_dtype == MOE_DTYPE_F16 && y_slices != 1)
-        return set_error(MOE_EINVAL, "moe_combine: fp16 y has exactly one slice");
-    if (H % 8)
-        return set_error(MOE_EUNSUPPORTED, "moe_combine: H=%d must be a multiple of 8", H);
-    if (T == 0)
-        return MOE_OK;
-    if (!y || !inv_perm || !topk_w || !out_f16)
-        return set_error(MOE_EINVAL, "moe_combine: null pointer");
-    return launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, residual_f16, T, H,
-                          k, out_f16, stream);
+    const int rc = check_combine_args("moe_combine", y, y_dtype, y_slices, inv_perm, topk_w, T,
+                                      H, k, out_f16);
+    if (rc || T == 0)
+        return rc;
+    return launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, nullptr, nullptr,
+                          residual_f16, T, H, k, out_f16, stream);
+}
+
+int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                      const float *topk_w, const float *shared_f32, const void *x_f16,
+                      const void *shared_gate_w_f16, const void *residual_f16, int T, int H,
+                      int k, void *out_f16, hipStream_t stream)
+{
+    clear_error();
+    const int rc = check_combine_args("moe_combine_gated", y, y_dtype, y_slices, inv_perm,
+                                      topk_w, T, H, k, out_f16);
+    if (rc || T == 0)
+        return rc;
+    if (!shared_f32 || !x_f16 || !shared_gate_w_f16)
+        return set_error(MOE_EINVAL, "moe_combine_gated: null shared, x or gate pointer");
+    if (((uintptr_t)x_f16 | (uintptr_t)shared_gate_w_f16) & 15)
+        return set_error(MOE_EINVAL, "moe_combine_gated: x and gate vector need 16-byte alignment");
+    return launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,
+                          shared_gate_w_f16, residual_f16, T, H, k, out_f16, stream);
 }
 
 }  // extern "C"

@@ -68,12 +68,15 @@ class MoELayer:
     """One W4A16 MoE layer resident on the device."""
 
     def __init__(self, H, I, E, k, group, router, table, bias=None, shared=None,
-                 renorm=False, device="cuda"):
+                 renorm=False, device="cuda", shared_gate=None):
         self.H, self.I, self.E, self.k, self.g = H, I, E, k, group
         self.router = router            # fp16 [E, H] device
         self.table = table              # int64 [E] device (blob addresses)
         self.bias = bias                # fp32 [E] device or None
         self.shared = shared            # (wg, wu, wd) fp16 device or None
+        self.shared_gate = shared_gate  # fp16 [H] device or None (sigmoid-gated shared)
+        if shared_gate is not None and shared is None:
+            raise ValueError("a shared-expert gate needs a shared expert")
         self.flags = A.MOE_RENORM if renorm else 0
         self.device = device
 
@@ -131,8 +134,15 @@ class MoELayer:
             A.moe_shared_ffn_f16(x, wg, wu, wd, b.T, self.H, wg.shape[0], b.shared_out,
                                  b.shared_ws, b.shared_ws.numel(), stream)
 
-    def combine(self, b: LayerBuffers, residual=None, out=None, stream=None):
+    def combine(self, b: LayerBuffers, residual=None, out=None, stream=None, x=None):
+        """x (the layer input) is needed only when the shared expert is gated."""
         out = b.out if out is None else out
+        if self.shared_gate is not None:
+            if x is None:
+                raise ValueError("the gated shared expert needs the layer input x")
+            A.moe_combine_gated(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, b.shared_out,
+                                x, self.shared_gate, residual, b.T, self.H, self.k, out, stream)
+            return out
         A.moe_combine(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, b.shared_out, residual,
                       b.T, self.H, self.k, out, stream)
         return out
@@ -157,4 +167,4 @@ class MoELayer:
     def forward(self, x, b: LayerBuffers, residual=None, out=None, stream=None):
         self.route_permute(x, b, stream)
         self.experts(x, b, stream=stream)
-        return self.combine(b, residual, out, stream)
+        return self.combine(b, residual, out, stream, x=x)

@@ -90,8 +90,9 @@ def make_layer(cfg, layer=0, shared=True):
     sh = None
     if shared and cfg.Is:
         sh = tuple(f16(w) for w in MI.gen_shared(cfg))
+    gate = f16(MI.gen_shared_gate(cfg)) if (sh is not None and cfg.shared_gate) else None
     lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, router, blob_table(dev), bias, sh,
-                   device=DEV)
+                   device=DEV, shared_gate=gate)
     lay._blobs = dev            # keep the storage alive
     return lay
 

@@ -327,12 +327,13 @@ def test_shared_ffn(T):
 
 # --------------------------------------------------------------- combine
 
-def _assert_combine_close(got, ref16, ref64, absum, nterms):
+def _assert_combine_close(got, ref16, ref64, absum, nterms, extra=0.0):
     """The GPU sums n terms in fp32, the oracle in fp64: they differ by at most
     the recursive-summation bound gamma_n * sum|terms| (Higham), and each is
-    then rounded once to fp16, adding at most one fp16 ulp between them."""
+    then rounded once to fp16, adding at most one fp16 ulp between them.
+    `extra` adds a known bound on the terms' own error (the fp32 gate)."""
     u = 2.0 ** -24
-    bound = nterms * u / (1 - nterms * u) * absum
+    bound = nterms * u / (1 - nterms * u) * absum + extra
     ulp = np.spacing(np.abs(ref16)).astype(np.float64)
     err = np.abs(got - ref16.astype(np.float64))
     r = err / (ulp + bound)
@@ -392,6 +393,61 @@ def test_combine_in_place_residual():
     _assert_combine_close(_np(buf).astype(np.float64), ref, ref64, absum, k + 1)
 
 
+@pytest.mark.parametrize("S,dt,T,H,res", [(44, M.MOE_DTYPE_F32, 1, 2048, True),
+                                           (44, M.MOE_DTYPE_F32, 3, 2048, False),
+                                           (1, M.MOE_DTYPE_F16, 37, 2048, True),
+                                           (1, M.MOE_DTYPE_F16, 300, 256, False),
+                                           (1, M.MOE_DTYPE_F32, 5, 1024, True)])
+def test_combine_gated(S, dt, T, H, res):
+    """Shared term scaled by sigmoid(x . wsg): against the oracle's fp64 gate."""
+    say("combine gated S=%d dt=%d T=%d H=%d" % (S, dt, T, H))
+    rng = np.random.default_rng(7 * S + T)
+    k = 4
+    ys = (rng.standard_normal((S, T * k, H)) * (0.05 if S > 1 else 0.3)).astype(
+        np.float32 if dt == M.MOE_DTYPE_F32 else np.float16)
+    inv = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    r = rng.standard_normal((T, H)).astype(np.float16) if res else None
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    wsg = (rng.standard_normal(H) * 0.02).astype(np.float16)
+    out = torch.empty((T, H), dtype=torch.float16, device=DEV)
+    M.moe_combine_gated(torch.from_numpy(ys).to(DEV), dt, S, torch.from_numpy(inv).to(DEV),
+                        torch.from_numpy(w).to(DEV), torch.from_numpy(sh).to(DEV), f16(x),
+                        f16(wsg), None if r is None else f16(r), T, H, k, out)
+    torch.cuda.synchronize()
+    gt = O.shared_gate(x, wsg)
+    yo = ys.astype(np.float64).sum(axis=0)
+    ref, ref64 = O.combine(yo, inv, w, sh.astype(np.float64), r, shared_gate=gt)
+    yabs = np.abs(ys.astype(np.float64)).sum(axis=0)
+    absum = sum(w[:, j:j + 1].astype(np.float64) * yabs[inv[np.arange(T) * k + j]]
+                for j in range(k)) + gt[:, None] * np.abs(sh)
+    if r is not None:
+        absum = absum + np.abs(r.astype(np.float64))
+    # the GPU's fp32 gate: its logit is within gamma_H * sum|x w| of the exact
+    # one, the sigmoid's slope is at most 1/4, plus a few ulps for exp and the
+    # division
+    u = 2.0 ** -24
+    dlogit = H * u / (1 - H * u) * (np.abs(x.astype(np.float64)) @ np.abs(wsg.astype(np.float64)))
+    extra = (0.25 * dlogit + 8 * u)[:, None] * np.abs(sh)
+    _assert_combine_close(_np(out).astype(np.float64), ref, ref64, absum, S * k + 2, extra)
+
+
+def test_combine_gated_rejects_bad_args():
+    T, k, H = 2, 4, 256
+    z = torch.zeros((T * k, H), dtype=torch.float16, device=DEV)
+    inv = torch.arange(T * k, dtype=torch.int32, device=DEV)
+    w = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    sh = torch.zeros((T, H), dtype=torch.float32, device=DEV)
+    x = torch.zeros((T, H + 8), dtype=torch.float16, device=DEV)
+    g = torch.zeros(H + 8, dtype=torch.float16, device=DEV)
+    out = torch.empty((T, H), dtype=torch.float16, device=DEV)
+    with pytest.raises(M.MoEError):
+        M.moe_combine_gated(z, M.MOE_DTYPE_F16, 1, inv, w, None, x, g, None, T, H, k, out)
+    with pytest.raises(M.MoEError):      # gate vector not 16-byte aligned
+        M.moe_combine_gated(z, M.MOE_DTYPE_F16, 1, inv, w, sh, x, g[1:], None, T, H, k, out)
+
+
 # ---------------------------------------------------------- whole layer
 
 def _oracle_tokens(cfg, x, toks, layer=0, residual=None, shared=True):
@@ -402,15 +458,18 @@ def _oracle_tokens(cfg, x, toks, layer=0, residual=None, shared=True):
     idx, _, _ = O.route(xs, wr, bias, cfg.k)
     blobs = OracleBlobs(cfg, layer).get(np.unique(idx))
     sh = MI.gen_shared(cfg) if (shared and cfg.Is) else None
+    gate = MI.gen_shared_gate(cfg) if (sh is not None and cfg.shared_gate) else None
     res = None if residual is None else residual[toks]
     return O.moe_layer(xs, wr, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, bias=bias,
-                       shared=sh, residual=res)
+                       shared=sh, residual=res, shared_gate_w=gate)
 
 
 @pytest.mark.parametrize("cfg,T", [(MI.TINY, 16), (MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 8),
                                    (MI.E512, 16), (MI.OLMOE_DECODE, 64),
                                    (MI.OLMOE_DECODE, 512), (MI.OLMOE_DECODE, 4096),
-                                   (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096), (G32, 300)],
+                                   (MI.E512, 1), (MI.E512, 256), (MI.E512, 4096), (G32, 300),
+                                   (MI.QWEN, 1), (MI.QWEN, 3), (MI.QWEN, 16), (MI.QWEN, 256),
+                                   (MI.QWEN, 4096)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_end_to_end(cfg, T):
     lay = make_layer(cfg, 0)
