@@ -292,15 +292,18 @@ def run_batched(args, torch, M, cfg):
     # cost is shared (and the touched weights of 16 small-T calls still
     # exceed the last-level cache); every copy has its own shared weights too
     nc = max(16, -(-3 * 256 * 2 ** 20 // (cfg.E * blob_bytes)))
+    # shared expert on a side stream when its weights are large (60-expert
+    # layer: 69 MB); with the 512-expert layer's 6 MB it only delays routing
+    overlap = bool(cfg.Is) and 3 * cfg.H * cfg.Is * 2 >= 32 * 2 ** 20
     copies = [base]
     for _ in range(nc - 1):
         bl = base._blobs.clone()
         sh = None if shared is None else tuple(w.clone() for w in shared)
         lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, base.router, blob_table(bl), base.bias,
-                       sh, device=dev, shared_gate=gate)
+                       sh, device=dev, shared_gate=gate, overlap_shared=overlap)
         lay._blobs = bl
         copies.append(lay)
-    base.shared, base.shared_gate = shared, gate
+    base.shared, base.shared_gate, base.overlap_shared = shared, gate, overlap
     Ts = [int(t) for t in args.T.split(",")] if args.T else list(cfg.T)
     reps = max(1, args.steps // nc)
     lines = []
@@ -358,7 +361,8 @@ def run_batched(args, torch, M, cfg):
         log(str(line))
     return {"workload": cfg.name, "weight_copies": nc, "regime": args.regime,
             "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I, "g": cfg.g, "Is": cfg.Is,
-                       "shared_gate": cfg.shared_gate, "zipf_s": cfg.zipf_s},
+                       "shared_gate": cfg.shared_gate, "zipf_s": cfg.zipf_s,
+                       "shared_on_side_stream": overlap},
             "results": lines}
 
 

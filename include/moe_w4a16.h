@@ -233,7 +233,15 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
  *   s_t = Wd (silu(Wg x_t) * (Wu x_t)),
  *   wg, wu: device fp16 [Is][H];  wd: device fp16 [H][Is]  (row-major)
  *   out_f32: device fp32 [T][H]
- * h is rounded to fp16 between the projections; fp32 accumulation.
+ *   ws:      device scratch of moe_shared_ffn_workspace_bytes(T, H, Is) bytes,
+ *            zero-filled by the caller before its first use.  Its first 2 KB
+ *            hold arrival counters of the split-K reduction; every call
+ *            leaves them zero again, so one zero-fill serves any number of
+ *            calls (and graph replays) with any T.  Calls that share a
+ *            workspace must not overlap.
+ * h is rounded to fp16 between the projections; fp32 accumulation.  The
+ * order of the fp32 additions depends on T, H and Is only, so repeated calls
+ * give identical bits.
  */
 size_t moe_shared_ffn_workspace_bytes(int T, int H, int Is);
 int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const void *wd,

@@ -60,6 +60,9 @@ struct GemmArgs {
     int g;                       // group size (W4)
     int ldo;                     // leading dim of the output (I for h, H for y/out)
     void *out;
+    int ksw;                     // split-K kernel: workgroups sharing one output tile's K
+    float *part;                 // split-K, ksw > 1: per-workgroup partial tiles
+    unsigned *ctr;               // split-K, ksw > 1: arrival counter per output tile (zero)
 };
 
 // ----------------------------------------------------------------------------
@@ -305,12 +308,17 @@ __device__ __forceinline__ void wait_steps(int younger)   // younger in 0..3
 // ----------------------------------------------------------------------------
 // FP16 GEMM of the shared expert at moderate T, when (row tiles) x (4-block
 // column tiles) would leave most CUs idle: one workgroup per (32-row tile,
-// 64-row weight block), its four waves splitting K.  Both operands come
-// straight from memory into the MFMA registers, 8 16-K steps in flight per
-// wave (the activation rows are a few MB at most and stay in L2; a weight
-// block is read once from HBM and then from the L2 of the XCD that holds all
-// its row tiles).  The waves' partial sums meet in LDS and are added in wave
-// order; the epilogue is the one of f16_gemm_kernel.
+// 64-row weight block, K part), its four waves splitting the part's K.  Both
+// operands come straight from memory into the MFMA registers, 8 16-K steps in
+// flight per wave (the activation rows are a few MB at most and stay in L2; a
+// weight slice is read once from HBM and then from the L2 of the XCD that
+// holds all its row tiles).  The waves' partial sums meet in LDS and are added
+// in wave order.  With ksw > 1 K parts (few row tiles and blocks, e.g. the
+// down projection at small T: 32 blocks of 64 rows for H = 2048) each
+// workgroup publishes its tile with coherent stores and takes a ticket; the
+// workgroup holding the last ticket adds the ksw tiles in part order (so the
+// bits do not depend on arrival order), resets the counter to zero for the
+// next call and runs the epilogue of f16_gemm_kernel.
 constexpr int SK_D = 8;
 
 template <int MODE>
@@ -326,19 +334,21 @@ __global__ __launch_bounds__(GT) void f16_splitk_kernel(GemmArgs a)
     const int col = lane & 31;
     const int half = lane >> 5;
     const int R = (a.rows + 31) / 32;
+    const int KSW = a.ksw;
     const int id = blockIdx.x;
-    int blk, rt;
-    if (a.nblk % NXCD == 0) {   // every row tile of a block on one XCD (workgroup i -> XCD i % 8)
+    int unit, rt;   // unit = (weight block, K part)
+    if ((a.nblk * KSW) % NXCD == 0) {   // all row tiles of a unit on one XCD (workgroup i -> XCD i % 8)
         const int xcd = id % NXCD, li = id / NXCD;
-        blk = xcd + NXCD * (li / R);
+        unit = xcd + NXCD * (li / R);
         rt = li % R;
     } else {
-        blk = id / R;
+        unit = id / R;
         rt = id % R;
     }
+    const int blk = unit / KSW, kz = unit % KSW;
     const int p0 = rt * 32, mrows = min(32, a.rows - p0);
-    const int K = a.K, KW = K / 4;
-    const int k0 = wave * KW + 8 * half;
+    const int K = a.K, KW = K / (4 * KSW);
+    const int k0 = kz * (K / KSW) + wave * KW + 8 * half;
     const int nst = KW / 16;
     const _Float16 *arow = a.A + (size_t)(p0 + min(col, mrows - 1)) * K + k0;
     const _Float16 *w0, *w1;
@@ -388,32 +398,79 @@ __global__ __launch_bounds__(GT) void f16_splitk_kernel(GemmArgs a)
                 red[wave - 1][n][r][lane] = acc[n][r];
     }
     __syncthreads();
-    if (wave != 0)
-        return;
+    // value r of lane l: token row 8*(r/4) + 4*(l/32) + (r%4), weight column l%32
+    auto emit = [&](int r, float v0, float v1) {
+        const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row >= mrows)
+            return;
+        const size_t p = (size_t)(p0 + row);
+        if constexpr (GATEUP) {
+            const float hv = v0 / (1.0f + expf(-v0)) * v1;
+            static_cast<_Float16 *>(a.out)[p * a.ldo + blk * 32 + col] = (_Float16)hv;
+        } else {
+            static_cast<float *>(a.out)[p * a.ldo + blk * 64 + col] = v0;
+            static_cast<float *>(a.out)[p * a.ldo + blk * 64 + 32 + col] = v1;
+        }
+    };
+    if (wave == 0) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[n][r] += red[w][n][r][lane];
+    }
+    if (KSW == 1) {
+        if (wave != 0)
+            return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            emit(r, acc[0][r], acc[1][r]);
+        return;
+    }
+    // K parts: publish this workgroup's tile, take a ticket; the last
+    // workgroup's four waves each add rows r in [4w, 4w+4) of the ksw tiles
+    // in part order and store them.
+    __shared__ unsigned s_last;
+    const int tile = blk * R + rt;
+    float *tp = a.part + (size_t)tile * KSW * 2048;   // [ksw][2][16][64]
+    if (wave == 0) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                acc[n][r] += red[w][n][r][lane];
-    // value r of lane l: token row 8*(r/4) + 4*(l/32) + (r%4), weight column l%32
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row >= mrows)
-            continue;
-        const size_t p = (size_t)(p0 + row);
-        if constexpr (GATEUP) {
-            const float gv = acc[0][r], uv = acc[1][r];
-            const float hv = gv / (1.0f + expf(-gv)) * uv;
-            static_cast<_Float16 *>(a.out)[p * a.ldo + blk * 32 + col] = (_Float16)hv;
-        } else {
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                static_cast<float *>(a.out)[p * a.ldo + blk * 64 + n * 32 + col] = acc[n][r];
+                __hip_atomic_store(tp + (size_t)kz * 2048 + (n * 16 + r) * 64 + lane, acc[n][r],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are acknowledged
+        if (lane == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (unsigned)(KSW - 1);
         }
     }
+    __syncthreads();
+    if (!s_last)
+        return;
+    float v[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[n][i] = 0.0f;
+    for (int z = 0; z < KSW; ++z)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[n][i] += __hip_atomic_load(
+                    tp + (size_t)z * 2048 + (n * 16 + 4 * wave + i) * 64 + lane,
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0 && lane == 0)
+        __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        emit(4 * wave + i, v[0][i], v[1][i]);
 }
 
 // Per-workgroup item record (LDS): expert, row range, column tile, blob.
@@ -812,14 +869,60 @@ static int launch_w4(hipStream_t s, const GemmArgs &a)
     return MOE_OK;
 }
 
-constexpr int SPLITK_MAX_ROWS = 1024;   // shared expert: split-K kernel up to this many tokens
+#ifndef SPLITK_MAX_ROWS_CFG
+#define SPLITK_MAX_ROWS_CFG 1024
+#endif
+constexpr int SPLITK_MAX_ROWS = SPLITK_MAX_ROWS_CFG;   // shared expert: split-K kernel up to this many tokens
+#ifndef SPLITK_TARGET_WGS
+#define SPLITK_TARGET_WGS 256
+#endif
+#ifndef SPLITK_MAX_KSW
+#define SPLITK_MAX_KSW 8
+#endif
+// arrival counters at the front of the workspace: one per output tile of a
+// launch with K parts, which has fewer than SPLITK_TARGET_WGS tiles
+constexpr int SPLITK_CTR_BYTES = SPLITK_TARGET_WGS * 4 > 2048 ? SPLITK_TARGET_WGS * 4 : 2048;
+
+// K parts per output tile: the fewest (a divisor of K/64, at most
+// SPLITK_MAX_KSW, each wave keeping at least four 16-K steps) that give
+// SPLITK_TARGET_WGS workgroups.  Fixed by the shape alone, so the workspace
+// size does not depend on the device.
+static int splitk_ksw(int rows, int K, int nblk)
+{
+    const int64_t tiles = (int64_t)((rows + 31) / 32) * nblk;
+    const int nk = K / 64;
+    int best = 1;
+    for (int d = 1; d <= nk && d <= SPLITK_MAX_KSW; ++d) {
+        if (nk % d)
+            continue;
+        if (d > 1 && nk / d < 4)
+            break;
+        best = d;
+        if (tiles * d >= SPLITK_TARGET_WGS)
+            break;
+    }
+    return best;
+}
+
+static bool splitk_used(int rows, int K)
+{
+    return rows <= SPLITK_MAX_ROWS && K % 64 == 0;
+}
+
+static size_t splitk_part_bytes(int rows, int K, int nblk)
+{
+    if (!splitk_used(rows, K))
+        return 0;
+    const int ksw = splitk_ksw(rows, K, nblk);
+    return ksw > 1 ? (size_t)((rows + 31) / 32) * nblk * ksw * 2048 * sizeof(float) : 0;
+}
 
 template <int MODE>
 static int launch_mode(hipStream_t s, const GemmArgs &a)
 {
     if constexpr (MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16) {
-        if (a.rows <= SPLITK_MAX_ROWS && a.K % 64 == 0) {
-            const int64_t grid = (int64_t)((a.rows + 31) / 32) * a.nblk;
+        if (splitk_used(a.rows, a.K)) {
+            const int64_t grid = (int64_t)((a.rows + 31) / 32) * a.nblk * a.ksw;
             hipLaunchKernelGGL((f16_splitk_kernel<MODE>), dim3((unsigned)grid), dim3(GT), 0, s, a);
             MOE_LAUNCH_CHECK("f16_splitk_kernel");
             return MOE_OK;
@@ -884,12 +987,27 @@ int launch_ffn_batched(const void *x, const int32_t *perm, const int32_t *offset
     return launch_mode<GM_DOWN_W4>(s, a);
 }
 
+// Workspace of the shared expert: [arrival counters, 2 KB, zero between
+// calls][h fp16 T x Is][split-K partial tiles].
+size_t shared_ffn_ws_bytes(int T, int H, int Is)
+{
+    if (T <= 0 || Is <= 0)
+        return 0;
+    const size_t part = std::max(splitk_part_bytes(T, H, Is / 32), splitk_part_bytes(T, Is, H / 64));
+    return SPLITK_CTR_BYTES + (size_t)al256((int64_t)T * Is * 2) + part;
+}
+
+_Float16 *shared_ffn_h(void *ws)
+{
+    return reinterpret_cast<_Float16 *>(static_cast<uint8_t *>(ws) + SPLITK_CTR_BYTES);
+}
+
 int launch_shared_batched(const void *x, const void *wg, const void *wu, const void *wd, int T,
                           int H, int Is, float *out, void *ws, hipStream_t s)
 {
     if (T == 0)
         return MOE_OK;
-    _Float16 *h = static_cast<_Float16 *>(ws);
+    _Float16 *h = shared_ffn_h(ws);
     GemmArgs a{};
     a.E = 1;
     a.rows = T;
@@ -900,6 +1018,11 @@ int launch_shared_batched(const void *x, const void *wg, const void *wu, const v
     a.nblk = Is / 32;
     a.ldo = Is;
     a.out = h;
+    a.ctr = static_cast<unsigned *>(ws);
+    a.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(h) + al256((int64_t)T * Is * 2));
+    a.ksw = splitk_ksw(a.rows, a.K, a.nblk);
+    if (a.ksw > 1 && (int64_t)((T + 31) / 32) * a.nblk * 4 > SPLITK_CTR_BYTES)
+        return set_error(MOE_EUNSUPPORTED, "shared expert: too many split-K tiles");
     int rc = launch_mode<GM_GATEUP_F16>(s, a);
     if (rc)
         return rc;
@@ -910,6 +1033,9 @@ int launch_shared_batched(const void *x, const void *wg, const void *wu, const v
     a.nblk = H / 64;
     a.ldo = H;
     a.out = out;
+    a.ksw = splitk_ksw(a.rows, a.K, a.nblk);
+    if (a.ksw > 1 && (int64_t)((T + 31) / 32) * a.nblk * 4 > SPLITK_CTR_BYTES)
+        return set_error(MOE_EUNSUPPORTED, "shared expert: too many split-K tiles");
     return launch_mode<GM_DOWN_F16>(s, a);
 }
 

@@ -10,46 +10,68 @@ namespace moe {
 // FP16 GEMV pair for the shared expert at small T (weights row-major fp16,
 // the layout the caller hands over).  One wave per output row, lanes along K
 // with 16-byte loads, every token's dot product from the same weight
-// registers, xor-butterfly reduction.
-//   swiglu=1: h[t][r] = fp16(silu(Wg[r].x_t) * (Wu[r].x_t)), r < R
-//   swiglu=0: out[t][r] = W[r].in_t (fp32), r < R
+// registers, xor-butterfly reduction.  A pass covers U chunks of 8 K per
+// lane and issues all of its loads (weights and the tokens' K slices, at
+// clamped indices, so none is conditional) before any arithmetic: a long row
+// costs a few round trips instead of one per chunk.
+//   SW=1: h[t][r] = fp16(silu(Wg[r].x_t) * (Wu[r].x_t)), r < R
+//   SW=0: out[t][r] = W[r].in_t (fp32), r < R
 constexpr int GEMV_WAVES = 4;
 
-template <int T_MAX>
+template <int T_MAX, int U, bool SW>
 __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
     const f16 *__restrict__ in, const f16 *__restrict__ wa, const f16 *__restrict__ wb, int T,
-    int R, int K, int swiglu, f16 *__restrict__ hout, float *__restrict__ fout)
+    int R, int K, f16 *__restrict__ hout, float *__restrict__ fout)
 {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6);
     if (r >= R)
         return;
     const int nch = K / 8;
+    const int npass = (nch + 64 * U - 1) / (64 * U);
     const uint4_t *ra = reinterpret_cast<const uint4_t *>(wa + (size_t)r * K);
-    const uint4_t *rb = swiglu ? reinterpret_cast<const uint4_t *>(wb + (size_t)r * K) : nullptr;
+    const uint4_t *rb = SW ? reinterpret_cast<const uint4_t *>(wb + (size_t)r * K) : nullptr;
+    const uint4_t *xr[T_MAX];
+#pragma unroll
+    for (int t = 0; t < T_MAX; ++t)
+        xr[t] = reinterpret_cast<const uint4_t *>(in + (size_t)min(t, T - 1) * K);
     float aa[T_MAX], bb[T_MAX];
 #pragma unroll
     for (int t = 0; t < T_MAX; ++t) {
         aa[t] = 0.0f;
         bb[t] = 0.0f;
     }
-    for (int c = lane; c < nch; c += 64) {
-        const half8_t va = __builtin_bit_cast(half8_t, ra[c]);
-        half8_t vb = {};
-        if (swiglu)
-            vb = __builtin_bit_cast(half8_t, rb[c]);
+    for (int pass = 0; pass < npass; ++pass) {
+        const int c0 = pass * 64 * U + lane;
+        uint4_t va[U], vb[U], xv[T_MAX][U];
 #pragma unroll
-        for (int t = 0; t < T_MAX; ++t) {
-            if (t < T) {
-                const half8_t xv = __builtin_bit_cast(
-                    half8_t, reinterpret_cast<const uint4_t *>(in + (size_t)t * K)[c]);
+        for (int u = 0; u < U; ++u) {
+            const int c = min(c0 + 64 * u, nch - 1);
+            va[u] = ra[c];
+            if constexpr (SW)
+                vb[u] = rb[c];
+#pragma unroll
+            for (int t = 0; t < T_MAX; ++t)
+                xv[t][u] = xr[t][c];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = c0 + 64 * u < nch;
+            const uint4_t z = {0u, 0u, 0u, 0u};
+            const half8_t a8 = __builtin_bit_cast(half8_t, ok ? va[u] : z);
+            half8_t b8 = {};
+            if constexpr (SW)
+                b8 = __builtin_bit_cast(half8_t, ok ? vb[u] : z);
+#pragma unroll
+            for (int t = 0; t < T_MAX; ++t) {
+                const half8_t x8 = __builtin_bit_cast(half8_t, xv[t][u]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    half2_t xp = {xv[2 * m], xv[2 * m + 1]};
-                    half2_t ap = {va[2 * m], va[2 * m + 1]};
+                    const half2_t xp = {x8[2 * m], x8[2 * m + 1]};
+                    const half2_t ap = {a8[2 * m], a8[2 * m + 1]};
                     aa[t] = dot2(ap, xp, aa[t]);
-                    if (swiglu) {
-                        half2_t bp = {vb[2 * m], vb[2 * m + 1]};
+                    if constexpr (SW) {
+                        const half2_t bp = {b8[2 * m], b8[2 * m + 1]};
                         bb[t] = dot2(bp, xp, bb[t]);
                     }
                 }
@@ -64,11 +86,11 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
 #pragma unroll
         for (int st = 32; st >= 1; st >>= 1) {
             a += __shfl_xor(a, st, 64);
-            if (swiglu)
+            if constexpr (SW)
                 b += __shfl_xor(b, st, 64);
         }
         if (lane == 0) {
-            if (swiglu)
+            if constexpr (SW)
                 hout[(size_t)t * R + r] = (f16)(a / (1.0f + expf(-a)) * b);
             else
                 fout[(size_t)t * R + r] = a;
@@ -76,37 +98,37 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
     }
 }
 
-template <int T_MAX>
+template <int T_MAX, int U>
 static int launch_gemv_pair(const void *x, const void *wg, const void *wu, const void *wd, int T,
                             int H, int Is, float *out, f16 *h, hipStream_t s)
 {
     dim3 b(GEMV_WAVES * 64);
-    hipLaunchKernelGGL(gemv_f16_kernel<T_MAX>, dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
-                       (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, 1, h,
+    hipLaunchKernelGGL((gemv_f16_kernel<T_MAX, U, true>), dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES),
+                       b, 0, s, (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, h,
                        (float *)nullptr);
     MOE_LAUNCH_CHECK("gemv_f16_kernel(gate/up)");
-    hipLaunchKernelGGL(gemv_f16_kernel<T_MAX>, dim3((H + GEMV_WAVES - 1) / GEMV_WAVES), b, 0, s,
-                       (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is, 0,
+    hipLaunchKernelGGL((gemv_f16_kernel<T_MAX, U, false>), dim3((H + GEMV_WAVES - 1) / GEMV_WAVES),
+                       b, 0, s, (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is,
                        (f16 *)nullptr, out);
     MOE_LAUNCH_CHECK("gemv_f16_kernel(down)");
     return MOE_OK;
 }
 
-// T <= 32: a weight row is read once and dotted with every token's row
+// Small T: a weight row is read once and dotted with every token's row
 // (accumulators for up to T_MAX tokens per lane).
 int launch_shared_gemv(const void *x, const void *wg, const void *wu, const void *wd, int T,
                        int H, int Is, float *out, void *ws, hipStream_t s)
 {
-    f16 *h = static_cast<f16 *>(ws);   // [T][Is]
+    f16 *h = shared_ffn_h(ws);   // [T][Is]
+    if (T <= 1)
+        return launch_gemv_pair<1, 8>(x, wg, wu, wd, T, H, Is, out, h, s);
+    if (T <= 2)
+        return launch_gemv_pair<2, 8>(x, wg, wu, wd, T, H, Is, out, h, s);
     if (T <= 4)
-        return launch_gemv_pair<4>(x, wg, wu, wd, T, H, Is, out, h, s);
+        return launch_gemv_pair<4, 4>(x, wg, wu, wd, T, H, Is, out, h, s);
     if (T <= 8)
-        return launch_gemv_pair<8>(x, wg, wu, wd, T, H, Is, out, h, s);
-    if (T <= 16)
-        return launch_gemv_pair<16>(x, wg, wu, wd, T, H, Is, out, h, s);
-    if (T <= 32)
-        return launch_gemv_pair<32>(x, wg, wu, wd, T, H, Is, out, h, s);
-    return set_error(MOE_EUNSUPPORTED, "shared GEMV: T=%d > 32", T);
+        return launch_gemv_pair<8, 2>(x, wg, wu, wd, T, H, Is, out, h, s);
+    return set_error(MOE_EUNSUPPORTED, "shared GEMV: T=%d > 8", T);
 }
 
 }  // namespace moe

@@ -60,7 +60,10 @@ constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tok
 constexpr int SMALL_MAX_T = 32;       // AUTO: small-batch kernel up to this many tokens
 constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
-constexpr int SHARED_GEMV_MAX_T = 8;  // shared expert: GEMV up to this many tokens
+#ifndef SHARED_GEMV_MAX_T_CFG
+#define SHARED_GEMV_MAX_T_CFG 8
+#endif
+constexpr int SHARED_GEMV_MAX_T = SHARED_GEMV_MAX_T_CFG;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
 {
@@ -336,10 +339,7 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
 
 size_t moe_shared_ffn_workspace_bytes(int T, int H, int Is)
 {
-    (void)H;
-    if (T <= 0 || Is <= 0)
-        return 0;
-    return (size_t)al256((int64_t)T * Is * 2);
+    return shared_ffn_ws_bytes(T, H, Is);
 }
 
 int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const void *wd, int T,

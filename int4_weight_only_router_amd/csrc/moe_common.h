@@ -37,6 +37,10 @@ void clear_error();
 
 inline int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// Shared-expert workspace (k_ffn_grouped.hip): its size, and where h starts.
+size_t shared_ffn_ws_bytes(int T, int H, int Is);
+_Float16 *shared_ffn_h(void *ws);
+
 // Canonical blob section offsets (format documented in moe_w4a16.h).
 struct CanonLayout {
     int64_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;

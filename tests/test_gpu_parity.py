@@ -316,7 +316,7 @@ def test_shared_ffn(T):
     x = MI.gen_x(cfg, T)
     out = torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)
     wsb = M.moe_shared_ffn_workspace_bytes(T, cfg.H, cfg.Is)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     M.moe_shared_ffn_f16(f16(x), f16(wg), f16(wu), f16(wd), T, cfg.H, cfg.Is, out, ws, wsb)
     torch.cuda.synchronize()
     toks = np.arange(T) if T <= 32 else np.sort(
@@ -594,3 +594,32 @@ def test_zero_tokens_is_noop():
     lay.forward(f16(np.zeros((0, cfg.H), np.float16)), b)
     torch.cuda.synchronize()
     assert np.all(_np(b.offsets) == 0) and np.all(_np(b.counts) == 0)
+
+
+@pytest.mark.parametrize("cfg,T", [(MI.E512, 1), (MI.QWEN, 8)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_shared_overlap_matches_serial_and_graph(cfg, T):
+    """The shared expert on a side stream (forked at the layer's start, joined
+    before the combine) gives the same bits as the one-stream order, eagerly
+    and in a captured graph replayed several times with eager work between."""
+    say("shared overlap %s T=%d" % (cfg.name, T))
+    lay = make_layer(cfg, 0)
+    x = f16(MI.gen_x(cfg, T))
+    ref = lay.forward(x, lay.buffers(T), overlap_shared=False).clone()
+    b = lay.buffers(T)
+    out = lay.forward(x, b, overlap_shared=True).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    bg = lay.buffers(T)
+    lay.forward(x, bg, overlap_shared=True)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        og = lay.forward(x, bg, overlap_shared=True)
+    for _ in range(3):
+        og.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(og.view(torch.int16), ref.view(torch.int16))
+        lay.forward(x, b, overlap_shared=True)   # eager work between replays
+        torch.cuda.synchronize()
