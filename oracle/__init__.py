@@ -44,11 +44,13 @@ def lib():
         L.oracle_shared_gate.argtypes = [vp, vp, i32, i32, vp, i32, vp]
         L.oracle_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
         L.oracle_pool_sim.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp]
+        L.oracle_profile_pin.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_pool_sim_pinned.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp]
         for name in ("oracle_blob_layout", "oracle_quantize_rows", "oracle_pack_expert",
                      "oracle_dequant_rows", "oracle_route", "oracle_permute",
                      "oracle_expert_ffn", "oracle_shared_ffn", "oracle_shared_gate",
                      "oracle_combine",
-                     "oracle_pool_sim"):
+                     "oracle_pool_sim", "oracle_profile_pin", "oracle_pool_sim_pinned"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -248,6 +250,31 @@ def pool_sim(L, E, C_, shift, k, ev_layer, ev_ids):
     _check(lib().oracle_pool_sim(L, E, C_, shift, k, _p(ev_layer), _p(ev_ids), n,
                                  _p(hits), _p(misses), _p(ml), _p(el)), "pool_sim")
     return hits, misses, ml, el
+
+
+def profile_pin(counts, C):
+    """counts [L, E] int64 routed-event counts -> pinned [L, C] int32 (the C
+    most counted experts per layer, ties to the lower id, ascending id)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int64)
+    L_, E = counts.shape
+    pinned = np.empty((L_, C), np.int32)
+    _check(lib().oracle_profile_pin(_p(counts), L_, E, C, _p(pinned)), "profile_pin")
+    return pinned
+
+
+def pool_sim_pinned(L, E, pinned, k, ev_layer, ev_ids):
+    """Replays events through the pinned policy: (hits, misses, miss_list)."""
+    pinned = np.ascontiguousarray(pinned, dtype=np.int32)
+    C_ = pinned.shape[1]
+    ev_layer = np.ascontiguousarray(ev_layer, dtype=np.int32)
+    ev_ids = np.ascontiguousarray(ev_ids, dtype=np.int32).reshape(-1, k)
+    n = ev_layer.size
+    hits = np.empty(n, np.int32)
+    misses = np.empty(n, np.int32)
+    ml = np.empty((n, k), np.int32)
+    _check(lib().oracle_pool_sim_pinned(L, E, C_, _p(pinned), k, _p(ev_layer), _p(ev_ids), n,
+                                        _p(hits), _p(misses), _p(ml)), "pool_sim_pinned")
+    return hits, misses, ml
 
 
 def moe_layer(x, wr, blobs, H, I, E, k, g, bias=None, renorm=False,

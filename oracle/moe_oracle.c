@@ -667,6 +667,97 @@ int oracle_pool_sim(int L, int E, int C, int shift, int k,
     return rc;
 }
 
+/*
+ * Profile-pinned residency ([LH] step 4: with VRAM for only part of the
+ * experts there are two obvious policies, keeping what was used last or
+ * measuring usage beforehand and fixing the most used; the profile needs a
+ * measurement pass and ages when the subject changes; no policy beats the
+ * summed probability of the experts that fit without guessing the future).
+ * READING: the profile is the number of routed events per (layer, expert) in a
+ * measurement pass; layer l pins the C experts with the highest counts (ties
+ * to the lower id), listed in ascending id in pinned[l*C .. l*C+C).
+ */
+int oracle_profile_pin(const int64_t *counts, int L, int E, int C, int32_t *pinned)
+{
+    if (!counts || !pinned || L <= 0 || E <= 0 || C <= 0 || C > E)
+        return OR_EINVAL;
+    char *take = malloc((size_t)E);
+    if (!take)
+        return OR_ENOMEM;
+    for (int l = 0; l < L; l++) {
+        const int64_t *c = counts + (size_t)l * E;
+        memset(take, 0, (size_t)E);
+        for (int i = 0; i < C; i++) {          /* C rounds of "best not yet taken" */
+            int b = -1;
+            for (int e = 0; e < E; e++)
+                if (!take[e] && (b < 0 || c[e] > c[b]))
+                    b = e;                       /* strict >: ties keep the lower id */
+            take[b] = 1;
+        }
+        int j = 0;
+        for (int e = 0; e < E; e++)
+            if (take[e])
+                pinned[(size_t)l * C + j++] = e;
+    }
+    free(take);
+    return OR_OK;
+}
+
+/*
+ * Replays a routing trace through the pinned policy.  READING: a routed
+ * expert in the layer's pinned set is a hit; every other routed expert is a
+ * miss, copied for that event only (the next use pays again); nothing is
+ * evicted.  miss_list[i*k ..] gets the misses in ascending id, padded by -1.
+ */
+int oracle_pool_sim_pinned(int L, int E, int C, const int32_t *pinned, int k,
+                           const int32_t *ev_layer, const int32_t *ev_ids, int n_ev,
+                           int32_t *ev_hits, int32_t *ev_misses, int32_t *miss_list)
+{
+    if (L <= 0 || E <= 0 || C <= 0 || C > E || k <= 0 || !pinned || !ev_layer || !ev_ids)
+        return OR_EINVAL;
+    char *res = calloc((size_t)L * E, 1);
+    char *inR = calloc((size_t)E, 1);
+    if (!res || !inR) {
+        free(res); free(inR);
+        return OR_ENOMEM;
+    }
+    int rc = OR_OK;
+    for (int l = 0; l < L && !rc; l++)
+        for (int i = 0; i < C; i++) {
+            int e = pinned[(size_t)l * C + i];
+            if (e < 0 || e >= E || res[(size_t)l * E + e]) { rc = OR_EINVAL; break; }
+            res[(size_t)l * E + e] = 1;
+        }
+    for (int i = 0; i < n_ev && !rc; i++) {
+        int l = ev_layer[i];
+        const int32_t *R = ev_ids + (int64_t)i * k;
+        if (l < 0 || l >= L) { rc = OR_EINVAL; break; }
+        memset(inR, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            if (R[j] < 0 || R[j] >= E || inR[R[j]]) { rc = OR_EINVAL; break; }
+            inR[R[j]] = 1;
+        }
+        if (rc) break;
+        int hits = 0, misses = 0;
+        for (int e = 0; e < E; e++) {
+            if (!inR[e])
+                continue;
+            if (res[(size_t)l * E + e])
+                hits++;
+            else {
+                if (miss_list) miss_list[(int64_t)i * k + misses] = e;
+                misses++;
+            }
+        }
+        for (int j = misses; j < k; j++)
+            if (miss_list) miss_list[(int64_t)i * k + j] = -1;
+        if (ev_hits) ev_hits[i] = hits;
+        if (ev_misses) ev_misses[i] = misses;
+    }
+    free(res); free(inR);
+    return rc;
+}
+
 /* ------------------------------------------------ array helpers (tests) */
 
 void oracle_f16_to_f64_n(const uint16_t *in, double *out, int64_t n)

@@ -191,3 +191,80 @@ def test_rejects_bad_capacity():
         O.pool_sim(1, 8, 1, 3, 2, np.zeros(1, np.int32), np.array([[0, 1]], np.int32))
     with pytest.raises(ValueError):
         O.pool_sim(1, 8, 9, 3, 2, np.zeros(1, np.int32), np.array([[0, 1]], np.int32))
+
+
+# --------------------------------------------- profile-pinned policy
+
+def test_profile_pin_brute_force_with_ties():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        L, E, C = 3, 10, 4
+        counts = rng.integers(0, 4, (L, E))          # many ties
+        got = O.profile_pin(counts, C)
+        for l in range(L):
+            want = sorted(sorted(range(E), key=lambda e: (-counts[l, e], e))[:C])
+            assert list(got[l]) == want
+
+
+def test_pinned_sim_is_set_membership():
+    rng = np.random.default_rng(4)
+    L, E, k, C = 2, 12, 3, 5
+    pinned = np.stack([np.sort(rng.choice(E, C, replace=False)) for _ in range(L)])
+    layers, ids = _trace(rng, 200, E, k, L=L)
+    h, m, ml = O.pool_sim_pinned(L, E, pinned, k, layers, ids)
+    for i, (l, R) in enumerate(zip(layers, ids)):
+        P = set(int(e) for e in pinned[l])
+        mis = sorted(set(int(e) for e in R) - P)
+        assert h[i] == len(set(int(e) for e in R) & P) and m[i] == len(mis)
+        assert list(ml[i][:len(mis)]) == mis and all(ml[i][len(mis):] == -1)
+    # every expert pinned: no misses at all
+    full = np.tile(np.arange(E, dtype=np.int32), (L, 1))
+    h, m, _ = O.pool_sim_pinned(L, E, full, k, layers, ids)
+    assert m.sum() == 0 and h.sum() == ids.size
+
+
+def test_pinned_by_own_profile_equals_static_ceiling():
+    """Pinning the C most counted experts of the very trace it replays gives
+    exactly the summed counts of those experts: the ceiling of any fixed set."""
+    rng = np.random.default_rng(5)
+    E, C, k, n = 64, 30, 8, 3000
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.0
+    p /= p.sum()
+    layers, ids = _trace(rng, n, E, k, p=p)
+    counts = np.bincount(ids.reshape(-1), minlength=E)[None, :]
+    h, m, _ = O.pool_sim_pinned(1, E, O.profile_pin(counts, C), k, layers, ids)
+    assert h.sum() == np.sort(counts[0])[::-1][:C].sum()
+
+
+def _zipf_trace(rng, n, E, k, perm):
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.0
+    p /= p.sum()
+    q = np.empty(E)
+    q[perm] = p                                   # expert perm[r] has rank r + 1
+    return _trace(rng, n, E, k, p=q)
+
+
+def test_profile_wins_stable_load_lru_wins_shifted_load():
+    """The explainer's comparison: with a stable workload a measured profile
+    beats recency (and sits at the ceiling); when the workload changes after
+    the profile was taken, the profile is stale and recency wins."""
+    rng = np.random.default_rng(6)
+    E, C, k = 64, 30, 8
+    pa, pb = rng.permutation(E), rng.permutation(E)
+    _, prof_ids = _zipf_trace(rng, 3000, E, k, pa)
+    counts = np.bincount(prof_ids.reshape(-1), minlength=E)[None, :]
+    pinned = O.profile_pin(counts, C)
+    # stable: same distribution as the profile
+    layers, ids = _zipf_trace(rng, 4000, E, k, pa)
+    hp, _, _ = O.pool_sim_pinned(1, E, pinned, k, layers, ids)
+    hl, _, _, _ = O.pool_sim(1, E, C, 0, k, layers, ids)
+    incl = np.bincount(ids.reshape(-1), minlength=E) / len(ids)
+    ceiling = np.sort(incl)[::-1][:C].sum() / k
+    rate_p, rate_l = hp.sum() / ids.size, hl.sum() / ids.size
+    assert rate_p > rate_l
+    assert ceiling - 0.01 <= rate_p <= ceiling + 1e-12
+    # shifted: the hot set moves after the profile
+    layers, ids = _zipf_trace(rng, 4000, E, k, pb)
+    hp, _, _ = O.pool_sim_pinned(1, E, pinned, k, layers, ids)
+    hl, _, _, _ = O.pool_sim(1, E, C, 0, k, layers, ids)
+    assert hl.sum() > hp.sum()
