@@ -373,7 +373,13 @@ def run_partial(args, torch, M):
     -> routed ids to the host -> prepare (misses copied H2D on a side stream)
     -> expert FFN through the published table -> retire -> combine.
     Protocol: `blocks`
-    fresh pools, each a 64-token warmup then `prompts` x `tokens` tokens."""
+    fresh pools, each a 64-token warmup then `prompts` x `tokens` tokens.
+    --policy pinned: a profile pass first (`profile_prompts` other prompts of
+    the same workload, through the decayed-counter pool) counts the routed
+    experts per layer; every block then pins each layer's C most counted
+    experts (moe_pool_pin).  Either way the report carries the static hit
+    ceiling of the measured trace: the C most routed experts of each layer in
+    hindsight, the most any fixed set can hit."""
     import numpy as np
     import moe_inputs as MI
     import oracle as O
@@ -398,6 +404,7 @@ def run_partial(args, torch, M):
     stream = torch.cuda.current_stream()
     step = M.PoolStats()
     trace_layers, trace_ids = [], []
+    pinned = None
 
     def token(x0, record):
         # one native call per layer: route, ids to the host, prepare (misses
@@ -418,8 +425,27 @@ def run_partial(args, torch, M):
 
     blocks = []
     try:
+        if args.policy == "pinned":
+            # profile pass: prompts of their own (ids past the measured ones)
+            M.moe_pool_reset(pool)
+            for p in range(args.profile_prompts):
+                for i in range(args.tokens):
+                    token(torch.from_numpy(MI.gen_prompt_token(cfg, 1000 + p, i)).to(dev), True)
+            torch.cuda.synchronize()
+            counts = np.zeros((L, cfg.E), np.int64)
+            for l, ids in zip(trace_layers, trace_ids):
+                counts[l, ids] += 1
+            trace_layers.clear()
+            trace_ids.clear()
+            # the C most counted experts per layer, ties to the lower id
+            pinned = np.sort(np.argsort(-counts, axis=1, kind="stable")[:, :cfg.capacity], axis=1)
+            assert np.array_equal(pinned, O.profile_pin(counts, cfg.capacity))
+            log("profile: %d tokens" % (args.profile_prompts * args.tokens))
         for blk in range(args.blocks):
             M.moe_pool_reset(pool)
+            if pinned is not None:
+                for l in range(L):
+                    M.moe_pool_pin(pool, l, pinned[l])
             for i in range(cfg.warmup_tokens):
                 token(torch.from_numpy(MI.gen_prompt_token(cfg, -1, i)).to(dev), blk == 0)
             torch.cuda.synchronize()
@@ -449,9 +475,18 @@ def run_partial(args, torch, M):
     # block (warmup included) gives the same misses
     tl = np.array(trace_layers, np.int32)
     ti = np.array(trace_ids, np.int32)
-    _, sim_m, _, _ = O.pool_sim(L, cfg.E, cfg.capacity, args.decay_shift, cfg.k, tl, ti)
+    if pinned is None:
+        _, sim_m, _, _ = O.pool_sim(L, cfg.E, cfg.capacity, args.decay_shift, cfg.k, tl, ti)
+    else:
+        _, sim_m, _ = O.pool_sim_pinned(L, cfg.E, pinned, cfg.k, tl, ti)
     nw = cfg.warmup_tokens * L
     sim_measured = int(sim_m[nw:].sum())
+    # static ceiling of block 0's measured trace: per layer the C experts
+    # routed most often in hindsight
+    mc = np.zeros((L, cfg.E), np.int64)
+    for l, ids in zip(tl[nw:], ti[nw:]):
+        mc[l, ids] += 1
+    ceiling = float(np.sort(mc, axis=1)[:, ::-1][:, :cfg.capacity].sum() / max(1, mc.sum()))
     rates = [b["tokens_per_s"] for b in blocks]
     tot_tok = args.blocks * args.prompts * (args.tokens - 1)
     tot_time = sum(args.prompts * (args.tokens - 1) / r for r in rates)
@@ -468,8 +503,11 @@ def run_partial(args, torch, M):
         "h2d_GiB_measured": round(h2d / 2 ** 30, 3),
         "hit_rate": round(hits / max(1, hits + misses), 4),
         "misses_per_token": round(misses / (args.blocks * args.prompts * args.tokens), 3),
+        "hit_ceiling_static_block0": round(ceiling, 4),
         "simulator_misses_block0": sim_measured, "pool_misses_block0": blocks[0]["misses"],
-        "decay_shift": args.decay_shift,
+        "policy": args.policy,
+        "decay_shift": args.decay_shift if pinned is None else None,
+        "profile_tokens": args.profile_prompts * args.tokens if pinned is not None else 0,
     }
 
 
@@ -510,6 +548,10 @@ def main():
     ap.add_argument("--prompts", type=int, default=12)
     ap.add_argument("--tokens", type=int, default=128)
     ap.add_argument("--decay-shift", type=int, default=3)
+    ap.add_argument("--policy", choices=["decay", "pinned"], default="decay",
+                    help="partial: decayed-counter eviction, or a profile-pinned resident set")
+    ap.add_argument("--profile-prompts", type=int, default=4,
+                    help="partial --policy pinned: prompts of the profile pass")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)

@@ -351,6 +351,23 @@ int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
                      hipStream_t compute, const void *const **d_table_out,
                      moe_pool_stats_t *step);
 
+/*
+ * Profile-pinned policy for one layer (local-inference explainer,
+ * lucashiago.com.br, step 4: besides keeping what was used last, one can
+ * measure usage first and fix the most used experts; such a profile ages when
+ * the workload changes).  experts[0..n): host int32, n must equal C, distinct
+ * ids in [0, E) -- typically the C most frequent experts of a measured
+ * profile.  They are copied into the layer's C resident slots (synchronously;
+ * the call waits for the device) and stay there: from now on a routed expert
+ * of the set is a hit, and every other routed expert is a miss copied into a
+ * spare slot for that generation only, dropped at the layer's next prepare
+ * (paid again at its next use; nothing is evicted, evictions stay 0).
+ * moe_pool_reset() returns every layer to the decayed-counter policy and the
+ * canonical placement.  MOE_EINVAL on bad ids or n != C; MOE_ESTATE if the
+ * layer's last generation was not retired.
+ */
+int moe_pool_pin(moe_pool_t pool, int layer, const int32_t *experts, int n);
+
 /* Record that every kernel enqueued on `compute` so far that reads the
  * layer's current generation has been issued; slots evicted by it become
  * reusable once those kernels finish.  MOE_ESTATE if nothing to retire. */

@@ -15,8 +15,8 @@ __all__ = [
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "PoolConfig", "PoolStats", "PoolLayerArgs",
-    "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_retire",
-    "moe_pool_stats", "moe_pool_reset",
+    "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
+    "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
 ]
 
@@ -34,7 +34,7 @@ EXPORTS = [
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "moe_pool_create",
     "moe_pool_prepare",
-    "moe_pool_layer_forward",
+    "moe_pool_layer_forward", "moe_pool_pin",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
 ]
 
@@ -103,6 +103,7 @@ def _declare(L):
         "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
         "moe_pool_layer_forward": (i32, [vp, i32, C.POINTER(PoolLayerArgs), vp,
                                          C.POINTER(PoolStats)]),
+        "moe_pool_pin": (i32, [vp, i32, vp, i32]),
         "moe_pool_retire": (i32, [vp, i32, vp]),
         "moe_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
         "moe_pool_reset": (i32, [vp]),
@@ -280,6 +281,13 @@ def moe_pool_layer_forward(pool, layer, args: PoolLayerArgs, stream=None, step=N
     st = PoolStats() if step is None else step
     _check(lib().moe_pool_layer_forward(pool, layer, C.byref(args), _s(stream), C.byref(st)))
     return st
+
+
+def moe_pool_pin(pool, layer, experts):
+    """experts: host sequence of C distinct expert ids (the pinned set)."""
+    import numpy as np
+    ids = np.ascontiguousarray(experts, dtype=np.int32)
+    return _check(lib().moe_pool_pin(pool, layer, ids.ctypes.data, ids.size))
 
 
 def moe_pool_retire(pool, layer, compute=None):

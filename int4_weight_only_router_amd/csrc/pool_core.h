@@ -14,6 +14,11 @@
 // c <- c - (c >> shift) per routed event of the layer, +65536 per routed
 // expert, hits then misses touched in ascending id on a use clock, victim =
 // resident non-routed expert with lowest (counter, last use, id).
+// Local-inference explainer (lucashiago.com.br), step 4: the other policy
+// measures usage first and fixes the most used experts.  A pinned layer
+// (pin()) keeps a fixed set of C experts; any other routed expert is copied
+// into a spare slot for that generation only and dropped at the next one, so
+// a non-pinned expert is paid at every use and nothing is ever evicted.
 //
 // The Backend provides: init(), slot_ptr(l, s), wait_retired(l),
 // copy(l, dst, src, n), upload_table(l, buf, entries) -> device table ptr,
@@ -46,6 +51,8 @@ class SlotPool {
         bool prepared = false;
         bool publish_pending = false;   // prepared with the compute-stream wait deferred
         const void *const *table = nullptr;
+        bool pinned = false;             // fixed resident set (pin())
+        std::vector<int> transient;      // pinned layer: this generation's copied misses
     };
     std::vector<Layer> layers;
     int64_t clock = 0;
@@ -136,6 +143,8 @@ class SlotPool {
             return set_error(MOE_ECAPACITY,
                              "moe_pool_prepare: %d distinct experts exceed capacity %d", nR,
                              cfg.capacity);
+        if (L0.pinned)
+            return prepare_pinned(l, inR, compute, table_out, step, defer_publish);
         // policy on a copy of the layer state
         Layer L = L0;
         int64_t clk = clock;
@@ -230,6 +239,150 @@ class SlotPool {
         tot.hits += st.hits;
         tot.misses += st.misses;
         tot.evictions += st.evictions;
+        tot.h2d_bytes += st.h2d_bytes;
+        tot.generation += 1;
+        st.generation = tot.generation;
+        if (step)
+            *step = st;
+        *table_out = dtab;
+        return MOE_OK;
+    }
+
+    // Fixes layer l's resident set to experts[0..n) (n = C, distinct): they
+    // are copied into the C resident slots (ascending id), the spares are
+    // emptied, and from now on the layer follows the pinned policy (until
+    // reset()).  Synchronous; the layer's last generation must be retired.
+    int pin(int l, const int32_t *experts, int n)
+    {
+        if (l < 0 || l >= cfg.layers || n != cfg.capacity || !experts)
+            return set_error(MOE_EINVAL, "moe_pool_pin: need layer in range and n = C = %d",
+                             cfg.capacity);
+        Layer &L = layers[l];
+        if (L.prepared)
+            return set_error(MOE_ESTATE, "moe_pool_pin: layer %d generation not retired", l);
+        const int E = cfg.experts;
+        std::vector<char> in(E, 0);
+        for (int i = 0; i < n; ++i) {
+            if (experts[i] < 0 || experts[i] >= E || in[experts[i]])
+                return set_error(MOE_EINVAL, "moe_pool_pin: bad or repeated expert id %d",
+                                 experts[i]);
+            in[experts[i]] = 1;
+        }
+        int rc = be.wait_retired(l);
+        if (rc)
+            return rc;
+        std::vector<int> slot_of(E, -1), expert_in(nslots(), -1);
+        int s = 0;
+        for (int e = 0; e < E; ++e)
+            if (in[e]) {
+                slot_of[e] = s;
+                expert_in[s] = e;
+                rc = be.copy(l, be.slot_ptr(l, s), src[(size_t)l * E + e], (size_t)cfg.expert_bytes);
+                if (rc)
+                    return rc;
+                ++s;
+            }
+        std::vector<const void *> tab(E, nullptr);
+        for (int e = 0; e < E; ++e)
+            if (slot_of[e] >= 0)
+                tab[e] = be.slot_ptr(l, slot_of[e]);
+        const void *const *dtab = nullptr;
+        const int nbuf = L.cur_buf ^ 1;
+        rc = be.upload_table(l, nbuf, tab.data(), &dtab);
+        if (rc)
+            return rc;
+        rc = be.sync();
+        if (rc)
+            return rc;
+        L.slot_of = std::move(slot_of);
+        L.expert_in = std::move(expert_in);
+        L.cnt.assign(E, 0);
+        L.last.assign(E, 0);
+        L.cur_buf = nbuf;
+        L.table = dtab;
+        L.pinned = true;
+        L.transient.clear();
+        return MOE_OK;
+    }
+
+    // Pinned layer: hits are the routed experts of the fixed set; every other
+    // routed expert (ascending id) is copied into a spare slot for this
+    // generation; the previous generation's copies are dropped first.
+    int prepare_pinned(int l, const std::vector<char> &inR, hipStream_t compute,
+                       const void *const **table_out, moe_pool_stats_t *step, bool defer_publish)
+    {
+        Layer &L0 = layers[l];
+        const int E = cfg.experts;
+        Layer L = L0;
+        const bool had_transient = !L.transient.empty();
+        for (int e : L.transient) {
+            L.expert_in[L.slot_of[e]] = -1;
+            L.slot_of[e] = -1;
+        }
+        L.transient.clear();
+        int hits = 0;
+        std::vector<int> misses;
+        for (int e = 0; e < E; ++e) {
+            if (!inR[e])
+                continue;
+            if (L.slot_of[e] >= 0)
+                ++hits;
+            else
+                misses.push_back(e);
+        }
+        std::vector<int> spares;
+        for (int s = 0; s < nslots(); ++s)
+            if (L.expert_in[s] < 0)
+                spares.push_back(s);
+        if (misses.size() > spares.size())
+            return set_error(MOE_ECAPACITY, "moe_pool_prepare: %d misses exceed %d spare slots",
+                             (int)misses.size(), (int)spares.size());
+        for (size_t i = 0; i < misses.size(); ++i) {
+            L.expert_in[spares[i]] = misses[i];
+            L.slot_of[misses[i]] = spares[i];
+            L.transient.push_back(misses[i]);
+        }
+        const void *const *dtab = L0.table;
+        if (!misses.empty() || had_transient) {
+            // the spare slots and the older table buffer are rewritten only
+            // after the kernels of earlier generations retired
+            int rc = be.wait_retired(l);
+            if (rc)
+                return rc;
+            if (!misses.empty()) {
+                for (size_t i = 0; i < misses.size(); ++i) {
+                    rc = be.copy(l, be.slot_ptr(l, spares[i]), src[(size_t)l * E + misses[i]],
+                                 (size_t)cfg.expert_bytes);
+                    if (rc)
+                        return rc;   // nothing published: previous generation intact
+                }
+            }
+            std::vector<const void *> tab(E, nullptr);
+            for (int e = 0; e < E; ++e)
+                if (L.slot_of[e] >= 0)
+                    tab[e] = be.slot_ptr(l, L.slot_of[e]);
+            const int nbuf = L.cur_buf ^ 1;
+            rc = be.upload_table(l, nbuf, tab.data(), &dtab);
+            if (rc)
+                return rc;
+            if (!defer_publish) {
+                rc = be.publish(l, compute);
+                if (rc)
+                    return rc;
+            }
+            L.publish_pending = defer_publish;
+            L.cur_buf = nbuf;
+        }
+        L.table = dtab;
+        L.prepared = true;
+        L0 = std::move(L);
+        moe_pool_stats_t st{};
+        st.hits = hits;
+        st.misses = (int64_t)misses.size();
+        st.evictions = 0;
+        st.h2d_bytes = st.misses * cfg.expert_bytes;
+        tot.hits += st.hits;
+        tot.misses += st.misses;
         tot.h2d_bytes += st.h2d_bytes;
         tot.generation += 1;
         st.generation = tot.generation;

@@ -110,6 +110,12 @@ int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *ids, int n, hipS
                 : moe::set_error(MOE_EINVAL, "null pool");
 }
 
+int moe_pool_pin(moe_pool_t pool, int layer, const int32_t *experts, int n)
+{
+    moe::g_err.clear();
+    return pool ? pool->p.pin(layer, experts, n) : moe::set_error(MOE_EINVAL, "null pool");
+}
+
 int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute)
 {
     moe::g_err.clear();

@@ -204,7 +204,10 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
     int resolved = 0;
     rc = moe_expert_ffn_plan(a->T, a->H, a->I, E, a->k, a->group, a->regime, &resolved, nullptr,
                              nullptr, nullptr);
-    const bool split = !rc && st.misses > 0 && st.hits > 0 && resolved == MOE_REGIME_DECODE;
+    // (a pinned layer's previous table can hold last generation's copies,
+    // whose slots this generation's copies may reuse: no split there)
+    const bool split = !rc && st.misses > 0 && st.hits > 0 && resolved == MOE_REGIME_DECODE &&
+                       !P.layers[layer].pinned;
     if (split) {
         rc = moe_expert_ffn_w4a16(a->x_f16, a->perm, a->offsets, old_table, a->T, a->H, a->I, E,
                                   a->k, a->group, a->regime, a->y, a->y_dtype, a->y_slices,
@@ -229,6 +232,14 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
         return rr;
     return moe_combine(a->y, a->y_dtype, a->y_slices, a->inv_perm, a->topk_w, a->shared_f32,
                        a->residual_f16, a->T, a->H, a->k, a->out_f16, stream);
+}
+
+int moe_pool_pin(moe_pool_t pool, int layer, const int32_t *experts, int n)
+{
+    moe::clear_error();
+    if (!pool)
+        return moe::set_error(MOE_EINVAL, "moe_pool_pin: null pool");
+    return pool->p.pin(layer, experts, n);
 }
 
 int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute)

@@ -184,3 +184,52 @@ def test_native_pooled_layer_equals_resident_decode():
         assert tot.misses == misses and tot.h2d_bytes == misses * total
     finally:
         M.moe_pool_destroy(pool)
+
+
+def test_pinned_pool_layer_equals_resident_decode():
+    """moe_pool_pin: each layer keeps a fixed set (here the C coldest experts
+    of its Zipf bias, so most routed experts miss and the same non-pinned
+    expert is copied again token after token).  The native pooled layer still
+    gives the resident decode's bits, and hits/misses follow the oracle's
+    pinned simulator."""
+    cfg = MI.PARTIAL
+    L, steps = 2, 6
+    say("pinned pooled layer L=%d steps=%d" % (L, steps))
+    src, devs, total = _pinned_source(cfg, L)
+    pool = _make_pool(src, cfg, L, cfg.capacity, cfg.spares, 3, total)
+    lays, pinned = [], []
+    for l in range(L):
+        b = MI.zipf_bias(cfg, l)
+        lays.append(MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, f16(MI.gen_router(cfg, l)),
+                             blob_table(devs[l]), torch.from_numpy(b).to(DEV), device=DEV))
+        pinned.append(np.sort(np.argsort(b, kind="stable")[:cfg.capacity]).astype(np.int32))
+    bref = [lay.buffers(1) for lay in lays]
+    bpool = [lay.buffers(1) for lay in lays]
+    host_ids = torch.empty(cfg.k, dtype=torch.int32, pin_memory=True)
+    args = [lay.pool_args(b, host_ids) for lay, b in zip(lays, bpool)]
+    stream = torch.cuda.current_stream()
+    ev_l, ev_ids, got = [], [], []
+    try:
+        for l in range(L):
+            M.moe_pool_pin(pool, l, pinned[l])
+        for s in range(steps):
+            x0 = f16(MI.gen_prompt_token(cfg, 2, s))
+            xr, xp = x0, x0
+            for l, lay in enumerate(lays):
+                outr = lay.forward(xr, bref[l], residual=xr, out=torch.empty_like(xr))
+                outp = torch.empty_like(xp)
+                a = args[l]
+                a.x_f16, a.residual_f16, a.out_f16 = xp.data_ptr(), xp.data_ptr(), outp.data_ptr()
+                st = M.moe_pool_layer_forward(pool, l, a, stream)
+                ev_l.append(l)
+                ev_ids.append(host_ids.numpy().copy())
+                got.append((st.hits, st.misses, st.evictions))
+                torch.cuda.synchronize()
+                assert torch.equal(outp.view(torch.int16), outr.view(torch.int16)), (s, l)
+                xr, xp = outr, outp
+        h, m, _ = O.pool_sim_pinned(L, cfg.E, np.stack(pinned), cfg.k, np.array(ev_l, np.int32),
+                                    np.array(ev_ids, np.int32))
+        assert [g[:2] for g in got] == list(zip(h.tolist(), m.tolist()))
+        assert all(g[2] == 0 for g in got) and m.sum() > h.sum()
+    finally:
+        M.moe_pool_destroy(pool)

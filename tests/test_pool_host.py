@@ -31,6 +31,7 @@ def L():
     lib.moe_pool_reset.argtypes = [vp]
     lib.moe_pool_destroy.argtypes = [vp]
     lib.moe_pool_fake_fail_after.argtypes = [vp, C.c_long]
+    lib.moe_pool_pin.argtypes = [vp, C.c_int, vp, C.c_int]
     lib.moe_last_error.restype = C.c_char_p
     return lib
 
@@ -213,4 +214,66 @@ def test_reset_restores_initial_placement(L):
     assert (st.hits, st.misses, st.generation) == (0, 0, 0)
     rc, tab, st = P.prepare(0, [0, 1])
     assert rc == 0 and st.hits == 2 and st.misses == 0
+    P.close()
+
+
+def _pin(L, P, layer, experts):
+    a = np.ascontiguousarray(experts, dtype=np.int32)
+    return L.moe_pool_pin(P.h, layer, a.ctypes.data, a.size)
+
+
+def test_pinned_pool_matches_simulator(L):
+    """moe_pool_pin: the profile's C experts stay resident; every other routed
+    expert is copied for one generation and dropped at the next (the oracle's
+    pinned simulator decides hits and misses)."""
+    Lyr, E, k, Cap, S = 2, 16, 3, 6, 3
+    P = FakePool(L, Lyr, E, k, Cap, S, 3)
+    assert P.rc == 0
+    _, prof = _trace(11, 400, Lyr, E, k)
+    prof_layers, _ = _trace(11, 400, Lyr, E, k)
+    counts = np.zeros((Lyr, E), np.int64)
+    for l, R in zip(prof_layers, prof):
+        counts[l, R] += 1
+    pinned = O.profile_pin(counts, Cap)
+    for l in range(Lyr):
+        assert _pin(L, P, l, pinned[l][::-1]) == 0      # any order
+    layers, ids = _trace(12, 300, Lyr, E, k)
+    hits, misses, ml = O.pool_sim_pinned(Lyr, E, pinned, k, layers, ids)
+    for i, (l, R) in enumerate(zip(layers, ids)):
+        rc, tab, st = P.prepare(int(l), R)
+        assert rc == 0, L.moe_last_error()
+        assert (st.hits, st.misses, st.evictions) == (hits[i], misses[i], 0)
+        assert st.h2d_bytes == misses[i] * P.nbytes
+        t = P.table(tab)
+        present = {e for e, ptr in enumerate(t) if ptr is not None}
+        assert present == set(int(e) for e in pinned[l]) | set(int(e) for e in R)
+        for e in present:
+            assert np.array_equal(P.slot_bytes(t[e]), P.src[l, e])
+        assert P.retire(int(l)) == 0
+    tot = P.stats()
+    assert (tot.hits, tot.misses, tot.evictions) == (hits.sum(), misses.sum(), 0)
+    assert np.array_equal(P.src, P.src_copy)
+    # reset: canonical placement and the decayed-counter policy again
+    assert L.moe_pool_reset(P.h) == 0
+    h2, m2, _, _ = O.pool_sim(Lyr, E, Cap, 3, k, layers[:50], ids[:50])
+    for i in range(50):
+        rc, tab, st = P.prepare(int(layers[i]), ids[i])
+        assert rc == 0 and (st.hits, st.misses) == (h2[i], m2[i])
+        assert P.retire(int(layers[i])) == 0
+    P.close()
+
+
+def test_pin_errors_keep_state(L):
+    P = FakePool(L, 1, 8, 2, 4, 2, 3)
+    assert _pin(L, P, 0, [0, 1, 2]) == M.MOE_EINVAL          # n != C
+    assert _pin(L, P, 0, [0, 1, 2, 2]) == M.MOE_EINVAL       # repeated id
+    assert _pin(L, P, 0, [0, 1, 2, 8]) == M.MOE_EINVAL       # out of range
+    assert _pin(L, P, 1, [0, 1, 2, 3]) == M.MOE_EINVAL       # no such layer
+    rc, _, _ = P.prepare(0, [5, 6])
+    assert rc == 0
+    assert _pin(L, P, 0, [4, 5, 6, 7]) == M.MOE_ESTATE       # generation not retired
+    assert P.retire(0) == 0
+    assert _pin(L, P, 0, [4, 5, 6, 7]) == 0
+    rc, tab, st = P.prepare(0, [5, 1])
+    assert rc == 0 and (st.hits, st.misses) == (1, 1)
     P.close()
