@@ -163,16 +163,18 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
 
 /*
  * moe_route followed by moe_permute, with the same arguments and results
- * (same passages and readings).  For T <= 8 both run in one launch: the
- * logits are spread over many workgroups, and the workgroup that finishes
- * last (an atomic ticket in ws; no workgroup ever waits for another) does the
- * top-k, the softmax and the stable sort -- the decode path's one launch
- * instead of two.  For larger T it runs moe_route's launches (logits into ws,
- * then top-k) followed by moe_permute's, on the same ws.
+ * (same passages and readings).  For small T (T <= 5 with E <= 128, T <= 4
+ * with E > 128, where one selecting workgroup still beats two launches) both
+ * run in one launch: the logits are spread over many workgroups, and the
+ * workgroup that finishes last (an atomic ticket in ws; no workgroup ever
+ * waits for another) does the top-k, the softmax and the stable sort -- the
+ * decode path's one launch instead of two.  For larger T it runs moe_route's
+ * launches (logits into ws, then top-k) followed by moe_permute's, on the
+ * same ws.
  * ws: device scratch of moe_route_permute_workspace_bytes(T, k, E) bytes.  It
  * must be zero-filled before its first use by this function; every completed
- * call leaves it reusable (the ticket back at zero).  Calls that share one
- * workspace must not run concurrently.
+ * call leaves it reusable (the ticket, its first 256 bytes, back at zero),
+ * for any T.  Calls that share one workspace must not run concurrently.
  */
 size_t moe_route_permute_workspace_bytes(int T, int k, int E);
 int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias,

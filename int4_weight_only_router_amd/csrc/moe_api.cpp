@@ -58,7 +58,23 @@ int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
 constexpr int SMALL_MAX_T = 32;       // AUTO: small-batch kernel up to this many tokens
-constexpr int ROUTE_FUSED_MAX_T = 8;  // moe_route_permute: one fused launch up to this T
+#ifndef ROUTE_FUSED_MAX_T_CFG
+#define ROUTE_FUSED_MAX_T_CFG 5
+#endif
+constexpr int ROUTE_FUSED_MAX_T = ROUTE_FUSED_MAX_T_CFG;  // moe_route_permute: one fused launch up to this T
+#ifndef ROUTE_FUSED_MAX_T_BIGE_CFG
+#define ROUTE_FUSED_MAX_T_BIGE_CFG 4
+#endif
+// E > 128: the fused launch's single selecting workgroup takes every token's
+// top-k in turn, so it pays only for the smallest T
+constexpr int ROUTE_FUSED_MAX_T_BIGE = ROUTE_FUSED_MAX_T_BIGE_CFG;
+
+constexpr size_t ROUTE_TICKET_BYTES = 256;   // the fused router's arrival ticket, ws[0..256)
+
+static bool route_fused(int T, int E)
+{
+    return T > 0 && T <= (E > 128 ? ROUTE_FUSED_MAX_T_BIGE : ROUTE_FUSED_MAX_T);
+}
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
 #ifndef SHARED_GEMV_MAX_T_CFG
 #define SHARED_GEMV_MAX_T_CFG 8
@@ -219,10 +235,11 @@ size_t moe_route_permute_workspace_bytes(int T, int k, int E)
 {
     if (T < 0 || k <= 0 || E <= 0)
         return 0;
-    if (T > 0 && T <= ROUTE_FUSED_MAX_T)
+    if (route_fused(T, E))
         return route_split_ws_bytes(T, E);
-    // logits of the batched router, then the permutation's scratch
-    return route_batched_ws_bytes(T, E) + permute_ws_bytes(T, k, E);
+    // the fused launch's ticket (left zero), logits of the batched router,
+    // then the permutation's scratch
+    return ROUTE_TICKET_BYTES + route_batched_ws_bytes(T, E) + permute_ws_bytes(T, k, E);
 }
 
 int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T,
@@ -241,16 +258,19 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
     if (need && (!ws || ws_bytes < need))
         return set_error(MOE_ENOMEM, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes,
                          need);
-    if (T > 0 && T <= ROUTE_FUSED_MAX_T)
+    if (route_fused(T, E))
         return launch_route_split(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
                                   topk_w, counts, offsets, perm, inv_perm, ws, stream);
     void *pws = nullptr;
     if (T > 0) {
+        // past the ticket, so one workspace serves batches on both sides of
+        // the fused/batched boundary
+        char *lws = static_cast<char *>(ws) + ROUTE_TICKET_BYTES;
         rc = launch_route_batched(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
-                                  topk_w, ws, stream);
+                                  topk_w, lws, stream);
         if (rc)
             return rc;
-        pws = static_cast<char *>(ws) + route_batched_ws_bytes(T, E);
+        pws = lws + route_batched_ws_bytes(T, E);
     }
     return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, pws, stream);
 }

@@ -155,8 +155,38 @@ def test_route_permute_fused_bit_exact(cfg, T):
       for got, ref, name in zip((counts, offsets, perm, inv), O.permute(oi, cfg.E),
                                 ("counts", "offsets", "perm", "inv_perm")):
           assert np.array_equal(_np(got), ref), name
-      if T <= 8:
-          assert int(_np(ws[:4].view(torch.int32))[0]) == 0   # ticket back at zero
+      assert int(_np(ws[:4].view(torch.int32))[0]) == 0   # ticket zero after either path
+
+
+@pytest.mark.parametrize("cfg,Ts", [(MI.OLMOE_DECODE, (3, 40, 3, 5, 6, 1)),
+                                    (MI.E512, (2, 9, 2, 4, 5, 1))],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_route_permute_one_workspace_across_batch_sizes(cfg, Ts):
+    """One workspace (sized for the largest T) serves batches on both sides
+    of the fused/two-launch boundary, in any order."""
+    say("route_permute shared ws %s" % cfg.name)
+    wr = f16(MI.gen_router(cfg))
+    b = MI.zipf_bias(cfg)
+    bias = None if b is None else torch.from_numpy(b).to(DEV)
+    wsb = max(M.moe_route_permute_workspace_bytes(T, cfg.k, cfg.E) for T in Ts)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    for i, T in enumerate(Ts):
+        x = MI.gen_x(cfg, T, step=20 + i)
+        n = T * cfg.k
+        idx = torch.empty((T, cfg.k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device=DEV)
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+        offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV)
+        perm = torch.empty(n, dtype=torch.int32, device=DEV)
+        inv = torch.empty(n, dtype=torch.int32, device=DEV)
+        M.moe_route_permute(f16(x), wr, bias, T, cfg.H, cfg.E, cfg.k, 0, idx, w, counts, offsets,
+                            perm, inv, ws, wsb)
+        torch.cuda.synchronize()
+        oi, ow, _ = O.route(x, MI.gen_router(cfg), b, cfg.k)
+        assert np.array_equal(_np(idx), oi), T
+        for got, ref in zip((counts, offsets, perm, inv), O.permute(oi, cfg.E)):
+            assert np.array_equal(_np(got), ref), T
+        assert int(_np(ws[:4].view(torch.int32))[0]) == 0
 
 
 @pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 5), (MI.E512, 1),
@@ -183,9 +213,9 @@ def test_router_logits_pinned_order(cfg, T):
     M.moe_route_permute(f16(x), f16(wr), None if b is None else torch.from_numpy(b).to(DEV),
                         T, cfg.H, cfg.E, cfg.k, 0, idx, w, counts, offsets, perm, inv, ws, wsb)
     torch.cuda.synchronize()
-    # T <= 8: one fused launch, logits after a 256-byte ticket; else the
-    # logits kernel's T x E buffer at the start of the workspace
-    off = 256 if T <= 8 else 0
+    # either path keeps the fused launch's 256-byte ticket first, then the
+    # T x E logits
+    off = 256
     got = _np(ws[off:off + T * cfg.E * 4].view(torch.float32)).reshape(T, cfg.E)
     _, _, ref = O.route(x, wr, b, cfg.k)
     assert np.array_equal(got.view(np.int32), ref.view(np.int32))
