@@ -7,26 +7,19 @@
 // With many tokens per expert the expert FFN is a dense contraction, so it
 // runs on the matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// Work item: (row tile of 32*MF sorted rows of one expert) x (256 output
-// columns = four 64-row blocks of the weight matrix).  The workgroup's four
-// waves share the activation tile, staged in LDS 64 K at a time (double
-// buffered); wave w owns weight block 4*nt + w and computes its 32*MF x 64
-// output tile.  The weights never pass through LDS: in the device layout the
-// 8 nibbles one MFMA lane needs for one 16-K step (8 consecutive K of one
-// weight row) sit in one dword, and bytes 0-7 / 8-15 of a 16-byte chunk word
-// are the two lane halves' K slices for two consecutive steps, so a lane
-// fetches its B operand with one 8-byte load per 32-K chunk and converts it
-// in registers to fp16(q*s) (one rounding).  Loads of step k+1 (activations
-// and weights) are in flight while step k computes.
+// Kernels (each described where it is defined):
+//  w4_gemm_kernel       routed experts, persistent, 8 waves, every operand
+//                       HBM -> LDS by direct-to-LDS loads in a 4-stage ring,
+//                       INT4 weights converted to fp16(q*s) in registers;
+//  f16_splitk_kernel    shared expert up to ~1024 tokens: one workgroup per
+//                       (32-row tile, 64-row weight block, K part);
+//  f16_dma_gemm_kernel  shared expert for larger batches: 64*RF x 128 tiles,
+//                       both operands through a 3-stage direct-to-LDS ring.
 //
-// Scheduling: the grid is persistent (as many workgroups as fit at once).
-// Workgroups are dealt to the 8 XCDs round-robin by id, so workgroup i works
-// for XCD i mod 8, and each XCD takes a contiguous range of row tiles with all
-// their column tiles: the row tile's activations and an expert's weight
-// blocks are then re-read from that XCD's L2 instead of from HBM.  A
-// workgroup first lists its items (expert, rows, source rows, blob) in LDS,
-// then runs them as one stream of K-steps, so the loads of the next item
-// start while the current one finishes and stores its results.
+// Scheduling: workgroups are dealt to the 8 XCDs round-robin by id
+// (workgroup i runs on XCD i mod 8); each kernel maps ids so that the row
+// tiles sharing a weight block (or the column tiles sharing activations) sit
+// on one XCD and re-read them from its L2 instead of from HBM.
 //
 // Modes
 //  GATEUP_W4 : A = x rows gathered through perm (token = perm[p] / k),
@@ -42,7 +35,6 @@ enum { GM_GATEUP_W4 = 0, GM_DOWN_W4 = 1, GM_GATEUP_F16 = 2, GM_DOWN_F16 = 3 };
 
 constexpr int GT = 256;       // threads per workgroup (4 waves)
 constexpr int BK = 64;        // K per pipeline step
-constexpr int LDK = BK + 8;   // LDS row stride in halfs (+8 spreads rows over banks)
 constexpr int NXCD = 8;       // XCDs of the part; workgroup i runs on XCD i mod 8
 
 struct GemmArgs {
@@ -64,169 +56,6 @@ struct GemmArgs {
     float *part;                 // split-K, ksw > 1: per-workgroup partial tiles
     unsigned *ctr;               // split-K, ksw > 1: arrival counter per output tile (zero)
 };
-
-// ----------------------------------------------------------------------------
-// FP16 GEMM of the shared expert (GATEUP_F16, DOWN_F16): one implicit expert
-// over all T rows.  Four waves; the row tile of activations (32*MF rows x
-// 64 K) is staged in LDS (double buffered) and shared, wave w owns 64 weight
-// rows (block 4*nt + w: 32 gate + 32 up rows, or 64 down rows) whose 16-byte
-// K slices go straight from memory into the MFMA B operand.  Loads of step
-// k+1 are in flight while step k computes.
-template <int MODE, int MF>
-__global__ __launch_bounds__(GT) void f16_gemm_kernel(GemmArgs a)
-{
-    static_assert(MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16, "FP16 modes only");
-    constexpr bool GATEUP = MODE == GM_GATEUP_F16;
-    constexpr int BM = 32 * MF;
-    static_assert(BM * (BK / 8) == GT * MF, "activation staging assumes 256 threads");
-
-    __shared__ __align__(16) _Float16 As[2][BM * LDK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int col = lane & 31;    // B column (weight row) of this lane inside a 32-wide fragment
-    const int half = lane >> 5;   // which 8-wide K slice of a 16-K step this lane feeds
-
-    const int R = (a.rows + BM - 1) / BM;
-    const int NT = (a.nblk + 3) / 4;
-    // XCD-contiguous row ranges when every XCD gets a row tile; with fewer
-    // row tiles than XCDs, all workgroups share the items
-    const bool split = R >= NXCD;
-    const int xcd = blockIdx.x % NXCD;
-    const int G = split ? (int)gridDim.x / NXCD : (int)gridDim.x;
-    const int r_lo = split ? (int)((int64_t)R * xcd / NXCD) : 0;
-    const int r_hi = split ? (int)((int64_t)R * (xcd + 1) / NXCD) : R;
-    const int nitems = (r_hi - r_lo) * NT;
-    const int K = a.K;
-    const int nk = K / BK;
-
-    for (int it = split ? (int)blockIdx.x / NXCD : (int)blockIdx.x; it < nitems; it += G) {
-        const int rt = r_lo + it / NT;
-        const int nt = it % NT;
-        const int p0 = rt * BM, mrows = min(BM, a.rows - p0);
-        __syncthreads();   // the previous item's LDS readers are done
-
-        // activation rows staged by this thread: row r = (tid + 256 i) / 8,
-        // 16-byte piece ks = tid % 8.  Rows past the tile's end re-read its
-        // first row: they only feed output rows that are never stored.
-        const _Float16 *arow[MF];
-        const int ks = tid & 7;
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            const int r = (tid + GT * i) >> 3;
-            arow[i] = a.A + (size_t)(p0 + (r < mrows ? r : 0)) * K + ks * 8;
-        }
-
-        // this wave's weight rows (a wave past the last block computes on the
-        // last block and stores nothing)
-        const int blk = nt * 4 + wave;
-        const bool wact = blk < a.nblk;
-        const int bb = wact ? blk : a.nblk - 1;
-        const _Float16 *wr0, *wr1;
-        if constexpr (GATEUP) {
-            wr0 = a.W0 + (size_t)(bb * 32 + col) * K + 8 * half;
-            wr1 = a.W1 + (size_t)(bb * 32 + col) * K + 8 * half;
-        } else {
-            wr0 = a.W0 + (size_t)(bb * 64 + col) * K + 8 * half;
-            wr1 = a.W0 + (size_t)(bb * 64 + 32 + col) * K + 8 * half;
-        }
-
-        uint4_t ra[MF];
-        auto load_a = [&](int kt) {
-#pragma unroll
-            for (int i = 0; i < MF; ++i)
-                ra[i] = ldg(reinterpret_cast<const uint4_t *>(arow[i] + kt * BK));
-        };
-        auto store_a = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < MF; ++i) {
-                const int r = (tid + GT * i) >> 3;
-                *reinterpret_cast<uint4_t *>(&As[buf][r * LDK + ks * 8]) = ra[i];
-            }
-        };
-        half8_t bc[2][4], bn[2][4];   // [fragment][16-K step]
-        auto load_b = [&](int kt, half8_t (&b)[2][4]) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                b[0][s] = ldg(reinterpret_cast<const half8_t *>(wr0 + kt * BK + 16 * s));
-                b[1][s] = ldg(reinterpret_cast<const half8_t *>(wr1 + kt * BK + 16 * s));
-            }
-        };
-
-        float16_t acc[MF][2];
-#pragma unroll
-        for (int m = 0; m < MF; ++m)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[m][n][r] = 0.0f;
-
-        load_a(0);
-        load_b(0, bc);
-        store_a(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) {
-                load_a(kt + 1);
-                load_b(kt + 1, bn);
-            }
-            const _Float16 *as = As[cur];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8_t af[MF];
-#pragma unroll
-                for (int m = 0; m < MF; ++m)
-                    af[m] = *reinterpret_cast<const half8_t *>(as + (m * 32 + col) * LDK + s * 16 +
-                                                               half * 8);
-#pragma unroll
-                for (int m = 0; m < MF; ++m)
-#pragma unroll
-                    for (int n = 0; n < 2; ++n)
-                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], bc[n][s],
-                                                                          acc[m][n], 0, 0, 0);
-            }
-            if (more)
-                store_a(cur ^ 1);
-            __syncthreads();
-            if (more) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        bc[n][s] = bn[n][s];
-            }
-        }
-
-        // epilogue.  32x32 accumulator layout: value r of lane l is
-        // row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
-        if (wact) {
-#pragma unroll
-            for (int m = 0; m < MF; ++m) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (row >= mrows)
-                        continue;
-                    const size_t p = (size_t)(p0 + row);
-                    if constexpr (GATEUP) {
-                        const float gv = acc[m][0][r], uv = acc[m][1][r];
-                        const float hv = gv / (1.0f + expf(-gv)) * uv;
-                        static_cast<_Float16 *>(a.out)[p * a.ldo + blk * 32 + col] = (_Float16)hv;
-                    } else {
-#pragma unroll
-                        for (int n = 0; n < 2; ++n)
-                            static_cast<float *>(a.out)[p * a.ldo + blk * 64 + n * 32 + col] =
-                                acc[m][n][r];
-                    }
-                }
-            }
-        }
-    }
-}
 
 // ----------------------------------------------------------------------------
 // INT4 grouped GEMM with a 4-stage global->LDS pipeline (GATEUP_W4, DOWN_W4).
@@ -318,7 +147,7 @@ __device__ __forceinline__ void wait_steps(int younger)   // younger in 0..3
 // workgroup publishes its tile with coherent stores and takes a ticket; the
 // workgroup holding the last ticket adds the ksw tiles in part order (so the
 // bits do not depend on arrival order), resets the counter to zero for the
-// next call and runs the epilogue of f16_gemm_kernel.
+// next call and runs the epilogue.
 constexpr int SK_D = 8;
 
 template <int MODE>
@@ -471,6 +300,160 @@ __global__ __launch_bounds__(GT) void f16_splitk_kernel(GemmArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         emit(4 * wave + i, v[0][i], v[1][i]);
+}
+
+// ----------------------------------------------------------------------------
+// FP16 GEMM of the shared expert at large T (GATEUP_F16, DOWN_F16): one
+// workgroup per (row tile of 64*RF tokens) x (128 weight rows), four waves in
+// a 2 x 2 grid, each owning 32*RF rows x 64 weight rows (RF x 2 fragments of
+// v_mfma_f32_32x32x16_f16, tokens as the first operand).  Both operands of a
+// 32-K step travel HBM -> LDS by direct-to-LDS loads in a 3-stage ring, so
+// nothing in flight holds registers and two workgroups share a CU; every
+// thread issues the same number of loads per step, so "step k has landed" is
+// an exact vmcnt followed by a bare barrier.  Rows are 64 B (32 halfs); the
+// 16-byte piece j of row r sits at slot j ^ f(r), f(r) = ((r >> 1) ^ (r >> 3))
+// & 3, so the 8 or 16 rows one ds_read_b128 pass touches hit distinct banks.
+// gate/up: a tile's weight rows are 64 gate rows then the same 64 up rows, and
+// wave column c takes gate fragment c and up fragment c, so each lane holds
+// both halves of its SwiGLU inputs; down: 128 output columns.
+constexpr int FG_NS = 3;   // stages
+constexpr int FG_BK = 32;  // K per stage
+
+template <int RF>
+constexpr int fg_stage_bytes() { return (64 * RF + 128) * FG_BK * 2; }
+
+template <int MODE, int RF>
+__global__ __launch_bounds__(GT, 2) void f16_dma_gemm_kernel(GemmArgs a)
+{
+    static_assert(MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16, "FP16 modes only");
+    constexpr bool GATEUP = MODE == GM_GATEUP_F16;
+    constexpr int BM = 64 * RF;
+    constexpr int A_BYTES = BM * 64;
+    constexpr int STAGE = fg_stage_bytes<RF>();
+    constexpr int A_DMA = A_BYTES / (GT * 16);     // 16-byte loads per thread per stage
+    constexpr int B_DMA = 128 * 64 / (GT * 16);
+    constexpr int PER = A_DMA + B_DMA;
+    static_assert(A_DMA * GT * 16 == A_BYTES && B_DMA == 2, "stage split");
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int wr = wave >> 1, wc = wave & 1;
+
+    const int R = (a.rows + BM - 1) / BM;
+    const int NT = a.nblk / 2;
+    const int id = blockIdx.x;
+    int nt, rt;
+    if (NT % NXCD == 0) {   // every row tile of a column tile on one XCD
+        const int xcd = id % NXCD, li = id / NXCD;
+        nt = xcd + NXCD * (li / R);
+        rt = li % R;
+    } else {
+        nt = id / R;
+        rt = id % R;
+    }
+    const int p0 = rt * BM, mrows = min(BM, a.rows - p0);
+    const int K = a.K, nk = K / FG_BK;
+
+    // load sources: load i of a wave covers 16 rows (1 KB); lane L fills slot
+    // L % 4 of row L / 4, i.e. piece (L % 4) ^ f(row)
+    auto fsw = [](int r) { return ((r >> 1) ^ (r >> 3)) & 3; };
+    const _Float16 *asrc[A_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int r = (i * 4 + wave) * 16 + (lane >> 2);
+        const int j = (lane & 3) ^ fsw(r);
+        asrc[i] = a.A + (size_t)(p0 + min(r, mrows - 1)) * K + j * 8;
+    }
+    const _Float16 *bsrc[B_DMA];
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const int r = (i * 4 + wave) * 16 + (lane >> 2);   // weight row of the tile, 0..127
+        const int j = (lane & 3) ^ fsw(r);
+        const _Float16 *w;
+        if constexpr (GATEUP)
+            w = (r < 64 ? a.W0 : a.W1) + (size_t)(nt * 64 + (r & 63)) * K;
+        else
+            w = a.W0 + (size_t)(nt * 128 + r) * K;
+        bsrc[i] = w + j * 8;
+    }
+    auto issue = [&](int kt) {   // unconditional: past the end re-reads the last step
+        const int kk = min(kt, nk - 1) * FG_BK;
+        unsigned char *st = smem + (size_t)(kt % FG_NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i)
+            dma16(asrc[i] + kk, st + (i * 4 + wave) * 1024);
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i)
+            dma16(bsrc[i] + kk, st + A_BYTES + (i * 4 + wave) * 1024);
+    };
+
+    float16_t acc[RF][2];
+#pragma unroll
+    for (int m = 0; m < RF; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[m][n][r] = 0.0f;
+
+    // this lane's fragment rows: A rows wr*32*RF + m*32 + col; B rows of
+    // fragment n (gate/up: gate rows wc*32.., up rows 64 + wc*32..)
+    const int fa = fsw(col);   // f(r) of rows congruent to col mod 32 (f depends on bits 1..4)
+    for (int i = 0; i < FG_NS - 1; ++i)
+        issue(i);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm<PER * (FG_NS - 2)>();   // this wave's loads of step kt have landed
+        lds_barrier();                  // everyone's have; stage kt-1 is free
+        issue(kt + FG_NS - 1);
+        const unsigned char *st = smem + (size_t)(kt % FG_NS) * STAGE;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int off = ((2 * s + half) ^ fa) << 4;
+            half8_t af[RF], bf[2];
+#pragma unroll
+            for (int m = 0; m < RF; ++m)
+                af[m] = *reinterpret_cast<const half8_t *>(st + (wr * 32 * RF + m * 32 + col) * 64 +
+                                                           off);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int br = GATEUP ? n * 64 + wc * 32 + col : wc * 64 + n * 32 + col;
+                bf[n] = *reinterpret_cast<const half8_t *>(st + A_BYTES + br * 64 + off);
+            }
+#pragma unroll
+            for (int m = 0; m < RF; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m], bf[n], acc[m][n],
+                                                                      0, 0, 0);
+        }
+    }
+    wait_vm<0>();   // the ring's trailing (clamped) loads are done before the wave ends
+
+    // value r of lane l: token row 8*(r/4) + 4*(l/32) + (r%4), weight row l%32
+#pragma unroll
+    for (int m = 0; m < RF; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wr * 32 * RF + m * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (row >= mrows)
+                continue;
+            const size_t p = (size_t)(p0 + row);
+            if constexpr (GATEUP) {
+                const float gv = acc[m][0][r], uv = acc[m][1][r];
+                const float hv = gv / (1.0f + expf(-gv)) * uv;
+                static_cast<_Float16 *>(a.out)[p * a.ldo + nt * 64 + wc * 32 + col] = (_Float16)hv;
+            } else {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    static_cast<float *>(a.out)[p * a.ldo + nt * 128 + wc * 64 + n * 32 + col] =
+                        acc[m][n][r];
+            }
+        }
+    }
 }
 
 // Per-workgroup item record (LDS): expert, row range, column tile, blob.
@@ -827,23 +810,22 @@ static int pick_mf(int rows, int E, int nblk)
 
 // Row-tile height of the FP16 shared-expert GEMM: the tallest that still
 // gives every CU about two workgroups.
-static int pick_f16_mf(int rows, int nblk)
+template <int MODE, int RF>
+static int launch_fg(hipStream_t s, const GemmArgs &a)
 {
-    const int NT = (nblk + 3) / 4;
-    int mf = 4;
-    while (mf > 1 && (((int64_t)rows + 32 * mf - 1) / (32 * mf)) * NT < 2 * num_cus())
-        mf /= 2;
-    return mf;
-}
-
-template <int MODE, int MF>
-static int launch_mf(hipStream_t s, const GemmArgs &a)
-{
-    const int64_t items = (((int64_t)a.rows + 32 * MF - 1) / (32 * MF)) * ((a.nblk + 3) / 4);
-    int64_t grid = std::min<int64_t>(items, (int64_t)2 * num_cus());
-    grid = std::max<int64_t>(NXCD, (grid + NXCD - 1) / NXCD * NXCD);
-    hipLaunchKernelGGL((f16_gemm_kernel<MODE, MF>), dim3((unsigned)grid), dim3(GT), 0, s, a);
-    MOE_LAUNCH_CHECK("f16_gemm_kernel");
+    constexpr size_t lds = (size_t)FG_NS * fg_stage_bytes<RF>();
+    static_assert(2 * lds <= 160 * 1024, "two workgroups per CU");
+    static bool attr_set = false;   // raising the LDS limit is idempotent
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void *)f16_dma_gemm_kernel<MODE, RF>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess)
+            return set_error(MOE_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
+        attr_set = true;
+    }
+    const int64_t grid = (((int64_t)a.rows + 64 * RF - 1) / (64 * RF)) * (a.nblk / 2);
+    hipLaunchKernelGGL((f16_dma_gemm_kernel<MODE, RF>), dim3((unsigned)grid), dim3(GT), lds, s, a);
+    MOE_LAUNCH_CHECK("f16_dma_gemm_kernel");
     return MOE_OK;
 }
 
@@ -921,7 +903,11 @@ template <int MODE>
 static int launch_mode(hipStream_t s, const GemmArgs &a)
 {
     if constexpr (MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16) {
-        if (splitk_used(a.rows, a.K)) {
+        // the DMA GEMM once it has enough tiles (measured: it wins from 512
+        // tokens on with I_s = 5632, from 1024 with I_s = 512)
+        const int64_t fg_tiles = (((int64_t)a.rows + 127) / 128) * (a.nblk / 2);
+        const bool fg = a.rows > SPLITK_MAX_ROWS || (a.rows > 256 && fg_tiles >= 64);
+        if (splitk_used(a.rows, a.K) && !fg) {
             const int64_t grid = (int64_t)((a.rows + 31) / 32) * a.nblk * a.ksw;
             hipLaunchKernelGGL((f16_splitk_kernel<MODE>), dim3((unsigned)grid), dim3(GT), 0, s, a);
             MOE_LAUNCH_CHECK("f16_splitk_kernel");
@@ -935,11 +921,12 @@ static int launch_mode(hipStream_t s, const GemmArgs &a)
         default: return launch_w4<MODE, 1>(s, a);
         }
     } else {
-        switch (pick_f16_mf(a.rows, a.nblk)) {
-        case 4: return launch_mf<MODE, 4>(s, a);
-        case 2: return launch_mf<MODE, 2>(s, a);
-        default: return launch_mf<MODE, 1>(s, a);
-        }
+        if (a.nblk % 2 || a.K % FG_BK)
+            return set_error(MOE_EUNSUPPORTED, "shared expert: sizes outside the FP16 GEMM tiles");
+        const int64_t r4 = ((int64_t)a.rows + 255) / 256;
+        if (r4 * (a.nblk / 2) >= 2 * num_cus())
+            return launch_fg<MODE, 4>(s, a);
+        return launch_fg<MODE, 2>(s, a);
     }
 }
 
