@@ -89,8 +89,61 @@ __global__ __launch_bounds__(256) void combine_slices_kernel(
     }
 }
 
-// One slice (fp16 or fp32 y [T*k][H]): thread per (token, 8 columns).
+// 8 consecutive columns of one y row, loaded as one (fp16) or two (fp32)
+// 16-byte vectors; converted only when summed, so a thread's loads of all k
+// rows can be in flight together.
+typedef float float4_t __attribute__((ext_vector_type(4)));
 template <typename YT>
+struct Row8;
+template <>
+struct Row8<f16> {
+    half8_t v;
+    __device__ void load(const f16 *p) { v = *reinterpret_cast<const half8_t *>(p); }
+    __device__ float at(int m) const { return (float)v[m]; }
+};
+template <>
+struct Row8<float> {
+    float4_t a, b;
+    __device__ void load(const float *p)
+    {
+        a = reinterpret_cast<const float4_t *>(p)[0];
+        b = reinterpret_cast<const float4_t *>(p)[1];
+    }
+    __device__ float at(int m) const { return m < 4 ? a[m] : b[m - 4]; }
+};
+
+// Adds sum_j w[t,j] * y[inv_perm[t*k+j]][c0..c0+8) to acc in j order.  KMAX
+// >= k: every index, weight and row load is issued before the first add (at
+// clamped j, so none is conditional); rows past k are loaded again, not added.
+template <typename YT, int KMAX>
+__device__ __forceinline__ void routed_sum8(const YT *__restrict__ y,
+                                            const int32_t *__restrict__ inv_perm,
+                                            const float *__restrict__ w, int t, int H, int k,
+                                            int c0, float (&acc)[8])
+{
+    int32_t pj[KMAX];
+    float wj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const int jj = min(j, k - 1);
+        pj[j] = inv_perm[(size_t)t * k + jj];
+        wj[j] = w[(size_t)t * k + jj];
+    }
+    Row8<YT> r[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        r[j].load(y + (size_t)pj[j] * H + c0);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (j < k) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                acc[m] += wj[j] * r[j].at(m);
+        }
+}
+
+// One slice (fp16 or fp32 y [T*k][H]): thread per (token, 8 columns).
+template <typename YT, int KMAX>
 __global__ __launch_bounds__(256) void combine_rows_kernel(
     const YT *__restrict__ y, const int32_t *__restrict__ inv_perm, const float *__restrict__ w,
     const float *__restrict__ shared, const f16 *residual, int T, int H, int k, f16 *out)
@@ -105,14 +158,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 #pragma unroll
     for (int m = 0; m < 8; ++m)
         acc[m] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const size_t p = (size_t)inv_perm[(size_t)t * k + j];
-        const float wj = w[(size_t)t * k + j];
-        const YT *src = y + p * H + c0;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            acc[m] += wj * (float)src[m];
-    }
+    routed_sum8<YT, KMAX>(y, inv_perm, w, t, H, k, c0, acc);
     if (shared) {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -133,7 +179,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 
 // One slice with the gated shared term: one block per token; the block first
 // forms the token's gate, then each thread handles 8 columns per pass.
-template <typename YT>
+template <typename YT, int KMAX>
 __global__ __launch_bounds__(256) void combine_rows_gated_kernel(
     const YT *__restrict__ y, const int32_t *__restrict__ inv_perm, const float *__restrict__ w,
     const float *__restrict__ shared, const f16 *__restrict__ x, const f16 *__restrict__ wsg,
@@ -147,14 +193,7 @@ __global__ __launch_bounds__(256) void combine_rows_gated_kernel(
 #pragma unroll
         for (int m = 0; m < 8; ++m)
             acc[m] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const size_t p = (size_t)inv_perm[(size_t)t * k + j];
-            const float wj = w[(size_t)t * k + j];
-            const YT *src = y + p * H + c0;
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-                acc[m] += wj * (float)src[m];
-        }
+        routed_sum8<YT, KMAX>(y, inv_perm, w, t, H, k, c0, acc);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
             acc[m] += gate * shared[(size_t)t * H + c0 + m];
@@ -170,6 +209,38 @@ __global__ __launch_bounds__(256) void combine_rows_gated_kernel(
             o[m] = (f16)acc[m];
         *reinterpret_cast<half8_t *>(out + (size_t)t * H + c0) = o;
     }
+}
+
+template <typename YT, int KMAX, bool GATED>
+static int launch_rows(const YT *y, const int32_t *inv_perm, const float *w, const float *shared,
+                       const f16 *x, const f16 *gw, const f16 *res, int T, int H, int k, f16 *o,
+                       hipStream_t s)
+{
+    if constexpr (GATED) {
+        hipLaunchKernelGGL((combine_rows_gated_kernel<YT, KMAX>), dim3(T), dim3(256), 0, s, y,
+                           inv_perm, w, shared, x, gw, res, H, k, o);
+        MOE_LAUNCH_CHECK("combine_rows_gated_kernel");
+    } else {
+        const size_t n = (size_t)T * (H / 8);
+        hipLaunchKernelGGL((combine_rows_kernel<YT, KMAX>), dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), 0, s, y, inv_perm, w, shared, res, T, H, k, o);
+        MOE_LAUNCH_CHECK("combine_rows_kernel");
+    }
+    return MOE_OK;
+}
+
+template <typename YT, bool GATED>
+static int launch_rows_k(const YT *y, const int32_t *inv_perm, const float *w, const float *shared,
+                         const f16 *x, const f16 *gw, const f16 *res, int T, int H, int k, f16 *o,
+                         hipStream_t s)
+{
+    if (k <= 4)
+        return launch_rows<YT, 4, GATED>(y, inv_perm, w, shared, x, gw, res, T, H, k, o, s);
+    if (k <= 8)
+        return launch_rows<YT, 8, GATED>(y, inv_perm, w, shared, x, gw, res, T, H, k, o, s);
+    if (k <= 12)
+        return launch_rows<YT, 12, GATED>(y, inv_perm, w, shared, x, gw, res, T, H, k, o, s);
+    return launch_rows<YT, 16, GATED>(y, inv_perm, w, shared, x, gw, res, T, H, k, o, s);
 }
 
 int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, const float *w,
@@ -198,26 +269,16 @@ int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, c
     }
     if (gated) {
         if (y_dtype == MOE_DTYPE_F32)
-            hipLaunchKernelGGL(combine_rows_gated_kernel<float>, dim3(T), dim3(256), 0, s,
-                               static_cast<const float *>(y), inv_perm, w, shared, xh, gw, res, H,
-                               k, o);
-        else
-            hipLaunchKernelGGL(combine_rows_gated_kernel<f16>, dim3(T), dim3(256), 0, s,
-                               static_cast<const f16 *>(y), inv_perm, w, shared, xh, gw, res, H,
-                               k, o);
-        MOE_LAUNCH_CHECK("combine_rows_gated_kernel");
-        return MOE_OK;
+            return launch_rows_k<float, true>(static_cast<const float *>(y), inv_perm, w, shared,
+                                              xh, gw, res, T, H, k, o, s);
+        return launch_rows_k<f16, true>(static_cast<const f16 *>(y), inv_perm, w, shared, xh, gw,
+                                        res, T, H, k, o, s);
     }
-    const size_t n = (size_t)T * (H / 8);
-    dim3 grid((unsigned)((n + 255) / 256));
     if (y_dtype == MOE_DTYPE_F32)
-        hipLaunchKernelGGL(combine_rows_kernel<float>, grid, dim3(256), 0, s,
-                           static_cast<const float *>(y), inv_perm, w, shared, res, T, H, k, o);
-    else
-        hipLaunchKernelGGL(combine_rows_kernel<f16>, grid, dim3(256), 0, s,
-                           static_cast<const f16 *>(y), inv_perm, w, shared, res, T, H, k, o);
-    MOE_LAUNCH_CHECK("combine_rows_kernel");
-    return MOE_OK;
+        return launch_rows_k<float, false>(static_cast<const float *>(y), inv_perm, w, shared,
+                                           xh, gw, res, T, H, k, o, s);
+    return launch_rows_k<f16, false>(static_cast<const f16 *>(y), inv_perm, w, shared, xh, gw,
+                                     res, T, H, k, o, s);
 }
 
 }  // namespace moe
