@@ -17,7 +17,8 @@ namespace moe {
 // token and chunk.  Pair p of a 32-element chunk is a high-field pair iff p is
 // odd (device nibble layout).  The fp32 running sums stay within a few
 // thousand, so rounding is ~1e-7 relative to them: far inside the budget.
-__device__ __forceinline__ float dot_chunk(uint4_t w, const half2_t *xp, float d)
+// The 16 magic-value pairs of one chunk word, in activation-pair order.
+__device__ __forceinline__ void unpack_chunk(uint4_t w, half2_t (&m)[16])
 {
     const uint32_t M = 0x64006400u;
     // device chunk words hold elements 0-7, 16-23, 8-15, 24-31 in that order
@@ -25,22 +26,31 @@ __device__ __forceinline__ float dot_chunk(uint4_t w, const half2_t *xp, float d
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t v = ws[j], v8 = ws[j] >> 8;
-        d = dot2(__builtin_bit_cast(half2_t, (v & 0x000F000Fu) | M), xp[4 * j + 0], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v & 0x00F000F0u) | M), xp[4 * j + 1], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x000F000Fu) | M), xp[4 * j + 2], d);
-        d = dot2(__builtin_bit_cast(half2_t, (v8 & 0x00F000F0u) | M), xp[4 * j + 3], d);
+        m[4 * j + 0] = __builtin_bit_cast(half2_t, (v & 0x000F000Fu) | M);
+        m[4 * j + 1] = __builtin_bit_cast(half2_t, (v & 0x00F000F0u) | M);
+        m[4 * j + 2] = __builtin_bit_cast(half2_t, (v8 & 0x000F000Fu) | M);
+        m[4 * j + 3] = __builtin_bit_cast(half2_t, (v8 & 0x00F000F0u) | M);
     }
+}
+
+// d + the chunk's dot product from unpacked magic values and prepared
+// activations (d starts at the chunk's correction constant).
+__device__ __forceinline__ float dot_unpacked(const half2_t (&m)[16], const half2_t *xp, float d)
+{
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        d = dot2(m[j], xp[j], d);
     return d;
 }
 
-// Prepares one 32-element chunk of activations: pairs with odd index divided
-// by 16, and the chunk's correction constant.
-__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr)
+// Prepares one 32-element chunk of activations (already in registers):
+// pairs with odd index divided by 16, and the chunk's correction constant.
+__device__ __forceinline__ void prep_chunk_regs(const half8_t (&xv)[4], half2_t *dst, float *corr)
 {
     float slo = 0.0f, shi = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const half8_t v = *reinterpret_cast<const half8_t *>(src + 8 * q);
+        const half8_t v = xv[q];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f16 a = v[2 * m], b = v[2 * m + 1];
@@ -54,6 +64,16 @@ __device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *
         }
     }
     *corr = -1032.0f * slo - 72.0f * shi;
+}
+
+// The same, loading the chunk from memory first.
+__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr)
+{
+    half8_t xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        xv[q] = *reinterpret_cast<const half8_t *>(src + 8 * q);
+    prep_chunk_regs(xv, dst, corr);
 }
 
 }  // namespace moe

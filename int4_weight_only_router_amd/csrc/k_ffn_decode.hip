@@ -21,22 +21,28 @@
 // arithmetic, so a workgroup keeps its whole ~96 KB in flight.
 #include "k_decode_frag.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // Finds the a-th expert (in id order) with at least one routed row; -1 if
-// none.  The blob pointers are fetched in the same sweep as the offsets, so
-// the expert's weight address is known one memory round trip after entry.
+// none.  The blob pointer and the expert's row range are fetched in the same
+// sweep as the offsets, so all three are known one memory round trip after
+// entry.  Every wave runs it on its own (the same addresses: one trip to
+// memory, the rest hit the caches), so no wave waits on a barrier before it
+// issues its weight loads.
 __device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ offsets,
                                                  const uint8_t *const *__restrict__ blobs, int E,
-                                                 int a, int lane, const uint8_t **blob_out)
+                                                 int a, int lane, const uint8_t **blob_out,
+                                                 int *p0_out, int *p1_out)
 {
     int seen = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
         const bool inb = e < E;
-        const int o0 = inb ? offsets[e] : 0;
-        const int o1 = inb ? offsets[e + 1] : 0;
-        const uint8_t *bp = inb ? blobs[e] : nullptr;
+        const int o0 = inb ? ldg(offsets + e) : 0;
+        const int o1 = inb ? ldg(offsets + e + 1) : 0;
+        const uint8_t *bp = inb ? ldg(blobs + e) : nullptr;
         const bool act = o1 > o0;
         const uint64_t m = __ballot(act);
         const int n = __popcll(m);
@@ -45,8 +51,13 @@ __device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ off
             const int rank = __popcll(m & ((1ull << lane) - 1ull));
             const uint64_t hit = __ballot(act && rank == r);
             const int src = __ffsll((long long)hit) - 1;
-            *blob_out = reinterpret_cast<const uint8_t *>(
-                __shfl(reinterpret_cast<long long>(bp), src, 64));
+            // readlane moves 32 bits: the pointer goes over in two halves
+            const uint64_t b = reinterpret_cast<uint64_t>(bp);
+            const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, src);
+            const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+            *blob_out = reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+            *p0_out = __builtin_amdgcn_readlane(o0, src);
+            *p1_out = __builtin_amdgcn_readlane(o1, src);
             return e0 + src;
         }
         seen += n;
@@ -54,28 +65,49 @@ __device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ off
     return -1;
 }
 
-constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are staged at entry
+// Marks a weight register as rewritten here, so that its unpacking is not
+// hoisted above the point where the pipeline expects the load to have landed
+// (a hoisted unpack waits for every load issued before it).
+__device__ __forceinline__ void opaque(uint4_t &w) { asm volatile("" : "+v"(w)); }
 
-template <int H, int NW>
+constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are staged at entry
+constexpr int DECODE_RG = 4;     // routed rows computed together from one weight unpack
+
+// Memory behaviour the schedule is built around:
+//  * the vector memory counter retires loads in issue order, so a value is
+//    usable once it and every load issued before it have landed;
+//  * a CU accepts only so many loads in flight: issuing the whole ~96 KB of
+//    a workgroup up front stalls the issuing wave until most of it has come
+//    back, and no arithmetic can run meanwhile.
+// So each wave keeps PD weight chunks in flight and issues chunk i + PD just
+// before it computes chunk i: the dot products run while later chunks
+// stream.  Scales and activations go first (small).  Every weight address is
+// in the global address space (a flat load would also count against the LDS
+// counter and force a full drain at every LDS wait); no load is conditional.
+template <int H, int G, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
-    const uint8_t *const *__restrict__ skip, int I, int E, int k, int g, int ntk,
+    const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk,
     int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, float *__restrict__ y)
 {
     constexpr int NK = H / 32;                 // input chunks of gate/up rows
-    constexpr int CPW = NK / NW;               // chunks per wave
+    constexpr int CPW = NK / NW;               // gate/up chunks per wave
     constexpr int NRB = H / 64;                // 64-row blocks of the down projection
-    constexpr int RBW = (NRB + NW - 1) / NW;   // down blocks per wave
-    static_assert(NK % NW == 0, "H/32 must be a multiple of the wave count");
+    constexpr int RBW = NRB / NW;              // down blocks (chunks) per wave
+    constexpr int NCH = CPW + RBW;             // weight chunks per wave
+    constexpr int RG = DECODE_RG;
+    constexpr int CPG = G / 32;                // chunks per scale group
+    constexpr int NSG = CPW >= CPG ? CPW / CPG : 1;   // scale groups among a wave's chunks
+    static_assert(NK % NW == 0 && NRB % NW == 0, "H/64 must be a multiple of the wave count");
+    static_assert(NW >= RG, "one wave per row of a group does its SwiGLU");
+    static_assert(DECODE_XPRE * CPW <= 64, "a wave stages its chunks of every token, a lane each");
 
     __shared__ __align__(16) half2_t xp[DECODE_XPRE][H / 2];   // prepared activations
     __shared__ float xc[DECODE_XPRE][NK];                     // their chunk constants
-    __shared__ float red[NW * 64];
-    __shared__ __align__(16) half2_t hp[16];                  // prepared h chunk
-    __shared__ float hcorr;
-    __shared__ int s_e;
-    __shared__ const uint8_t *s_blob;
+    __shared__ float red[NW][RG][64];
+    __shared__ __align__(16) half2_t hp[RG][16];              // prepared h chunks
+    __shared__ int s_tok[RG];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -83,128 +115,232 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const int T = ntk / k;
     const bool xpre = T <= DECODE_XPRE;
 
-    // activations of the whole (small) batch are prepared while the expert
-    // is looked up: thread -> (token, chunk)
-    if (xpre) {
-        for (int i = threadIdx.x; i < T * NK; i += NW * 64) {
-            const int t = i / NK, c = i % NK;
-            prep_chunk(x + (size_t)t * H + c * 32, &xp[t][c * 16], &xc[t][c]);
-        }
+    // activations of the whole (small) batch, each wave only the chunks it
+    // multiplies: lane -> (token, chunk of the wave).  The loads go out now
+    // and land during the expert lookup; each wave stages its own chunks, so
+    // no workgroup barrier stands before the weight stream.
+    half8_t xr[4];
+    const bool xmine = xpre && lane < T * CPW;
+    const int xt = lane / CPW, xcn = wave * CPW + lane % CPW;
+    if (xmine) {
+        const f16 *src = x + (size_t)xt * H + xcn * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xr[q] = ldg(reinterpret_cast<const half8_t *>(src + 8 * q));
     }
-    if (wave == 0) {
-        const uint8_t *bp = nullptr;
-        int e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &bp);
-        // an expert without weights in the table, or one that `skip` lists
-        // (done by an earlier launch), is left to another launch
-        if (e >= 0 && (bp == nullptr || (skip != nullptr && skip[e] != nullptr)))
-            e = -1;
-        if (lane == 0) {
-            s_e = e;
-            s_blob = bp;
-        }
-    }
-    __syncthreads();
-    const int e = s_e;
-    if (e < 0)
-        return;
-    const int p0 = offsets[e], p1 = offsets[e + 1];
-    const uint8_t *blob = s_blob;
-    const int IC = I / 32;                     // input chunks of the down rows
 
-    // ---- issue every weight load of this workgroup up front
+    const uint8_t *blob = nullptr;
+    int p0 = 0, p1 = 0;
+    int e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &blob, &p0, &p1);
+    // an expert without weights in the table, or one that `skip` lists (done
+    // by an earlier launch), is left to another launch
+    if (e >= 0 && (blob == nullptr || (skip != nullptr && ldg(skip + e) != nullptr)))
+        e = -1;
+    if (e < 0)
+        return;   // uniform over the workgroup: every wave found the same expert
+    const int IC = I / 32;                     // input chunks of the down rows
+    constexpr int HG = H / G;
+    const int IG = I / G;
+    const int nrows = p1 - p0;
+
+    // token ids of the expert's first 64 rows (decode: at most 4 rows)
+    const int prow = (T > 1 && lane < nrows) ? ldg(perm + p0 + lane) : 0;
+
+    // scales: one per scale group among this wave's gate/up chunks, one per
+    // down block (2 bytes per lane each)
+    const uint16_t *gus = reinterpret_cast<const uint16_t *>(blob + off_gus) +
+                          (size_t)slice * HG * 64 + lane;
+    uint16_t sgu[NSG];
+#pragma unroll
+    for (int j = 0; j < NSG; ++j)
+        sgu[j] = ldg(gus + (size_t)(((wave * CPW + j * CPG) * 32) / G) * 64);
+    const uint16_t *dsc = reinterpret_cast<const uint16_t *>(blob + off_ds);
+    uint16_t sd[RBW];
+#pragma unroll
+    for (int r = 0; r < RBW; ++r)
+        sd[r] = ldg(dsc + ((size_t)(wave * RBW + r) * IG + (slice * 32) / G) * 64 + lane);
+
+    // weight chunks of this wave: gate/up chunks 0..CPW-1 (one 1 KB run of the
+    // fused 64-row block each), then its down blocks (the slice's 16-byte
+    // column of 64 down rows each)
     const uint4_t *guq = reinterpret_cast<const uint4_t *>(blob + off_guq) +
                          ((size_t)slice * NK + (size_t)wave * CPW) * 64 + lane;
-    uint4_t wq[CPW];
+    const uint4_t *dqw = reinterpret_cast<const uint4_t *>(blob + off_dq) +
+                         ((size_t)wave * RBW * IC + slice) * 64 + lane;
+    uint4_t w[NCH];
+    auto issue = [&](int i) {
+        if (i < CPW)
+            w[i] = ldg(guq + (size_t)i * 64);
+        else if (i < NCH)
+            w[i] = ldg(dqw + (size_t)(i - CPW) * IC * 64);
+    };
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
-        wq[i] = guq[(size_t)i * 64];
-    const uint4_t *dqb = reinterpret_cast<const uint4_t *>(blob + off_dq);
-    uint4_t dq[RBW];
+    for (int i = 0; i < PD && i < NCH; ++i)
+        issue(i);
+
+    if (xmine) {
+        // pinned here: prepared any earlier, the wait for x would come
+        // before the expert lookup is even issued
 #pragma unroll
-    for (int r = 0; r < RBW; ++r) {
-        const int rb = wave * RBW + r;
-        dq[r] = (rb < NRB) ? dqb[((size_t)rb * IC + slice) * 64 + lane] : uint4_t{0u, 0u, 0u, 0u};
-    }
-    const uint16_t *gus = reinterpret_cast<const uint16_t *>(blob + off_gus);
-    const uint16_t *dsc = reinterpret_cast<const uint16_t *>(blob + off_ds);
-    const int HG = H / g, IG = I / g;
-    float sgu[CPW];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int c = wave * CPW + i;
-        sgu[i] = h2f(gus[((size_t)slice * HG + (c * 32) / g) * 64 + lane]);
-    }
-    float sd[RBW];
-#pragma unroll
-    for (int r = 0; r < RBW; ++r) {
-        const int rb = wave * RBW + r;
-        sd[r] = (rb < NRB) ? h2f(dsc[((size_t)rb * IG + (slice * 32) / g) * 64 + lane]) : 0.0f;
+        for (int q = 0; q < 4; ++q)
+            asm volatile("" : "+v"(xr[q]));
+        prep_chunk_regs(xr, &xp[xt][xcn * 16], &xc[xt][xcn]);
     }
 
-    for (int p = p0; p < p1; ++p) {
-        const int t = perm[p] / k;
-        int slot = t;
+    // One group of R routed rows (R a constant, so that no register is held
+    // for absent rows).  FIRST: the weights are still streaming in and the
+    // group issues the rest of them as it goes.
+    auto group = [&](auto first, auto rows, int r0) {
+        constexpr bool FIRST = decltype(first)::value;
+        constexpr int R = decltype(rows)::value;
         if (!xpre) {
-            slot = 0;
-            for (int c = threadIdx.x; c < NK; c += NW * 64)
-                prep_chunk(x + (size_t)t * H + c * 32, &xp[0][c * 16], &xc[0][c]);
+            // stage this group's rows in slots 0..R-1
+            if ((int)threadIdx.x < R)
+                s_tok[threadIdx.x] = ldg(perm + p0 + r0 + threadIdx.x) / k;
             __syncthreads();
+            for (int i = threadIdx.x; i < R * NK; i += NW * 64) {
+                const int r = i / NK, c = i % NK;
+                prep_chunk(x + (size_t)s_tok[r] * H + c * 32, &xp[r][c * 16], &xc[r][c]);
+            }
+            lds_barrier();
+        } else {
+            wave_lds_sync();   // this wave's own staged chunks
+        }
+        // activation slot of each row: the token (all tokens staged), or the
+        // row's place in the group; read after the barrier, so that the
+        // token-id load never delays it
+        int slot[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = r0 + r;
+            if (!xpre)
+                slot[r] = r;
+            else if (T == 1)
+                slot[r] = 0;
+            else
+                slot[r] = ((rr < 64) ? __shfl(prow, rr, 64) : ldg(perm + p0 + rr)) / k;
         }
 
         // gate/up rows (lane = row of the fused block), K split over waves
-        float acc = 0.0f;
+        float acc[R] = {};
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
+            if constexpr (FIRST)
+                issue(i + PD);
+            opaque(w[i]);
+            half2_t m[16];
+            unpack_chunk(w[i], m);
             const int c = wave * CPW + i;
-            const float d = dot_chunk(wq[i], &xp[slot][c * 16], xc[slot][c]);
-            acc = fmaf(d, sgu[i], acc);
+            const float s = h2f(sgu[CPW >= CPG ? i / CPG : 0]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = fmaf(dot_unpacked(m, &xp[slot[r]][c * 16], xc[slot[r]][c]), s, acc[r]);
         }
-        red[wave * 64 + lane] = acc;
-        __syncthreads();
-        if (wave == 0) {
+        if constexpr (FIRST) {
+#pragma unroll
+            for (int i = CPW + PD; i < NCH; ++i)
+                issue(i);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            red[wave][r][lane] = acc[r];
+        // unpack the down chunks while the other waves finish their gate/up
+        // (up to two rows; with more, the registers of the unpacked chunks
+        // are not there and each chunk is unpacked where it is used)
+        constexpr bool PRE = R <= 2;
+        half2_t md[PRE ? RBW : 1][16];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+                opaque(w[CPW + j]);
+                unpack_chunk(w[CPW + j], md[j]);
+#pragma unroll
+                for (int q = 0; q < 16; ++q)   // materialised here, not sunk past the barrier
+                    asm volatile("" : "+v"(md[j][q]));
+            }
+        }
+        lds_barrier();
+        if (wave < R) {
+            // wave r: h of row r for intermediate index lane (lanes < 32), fp16
+            const int r = wave;
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w)
-                v += red[w * 64 + lane];
+            for (int w2 = 0; w2 < NW; ++w2)
+                v += red[w2][r][lane];
             const float up = __shfl(v, (lane + 32) & 63, 64);
-            // h for intermediate index lane (lanes < 32), rounded to fp16
-            const f16 hq = (f16)(v / (1.0f + expf(-v)) * up);
+            const f16 hq = (f16)swiglu_fast(v, up);
             const bool odd = (lane >> 1) & 1;
-            float cc = 0.0f;
-            if (lane < 32) {
-                reinterpret_cast<f16 *>(hp)[lane] = odd ? hq * (f16)0.0625f : hq;
-                cc = (odd ? -72.0f : -1032.0f) * (float)hq;
-            }
-#pragma unroll
-            for (int st = 16; st >= 1; st >>= 1)
-                cc += __shfl_xor(cc, st, 64);
-            if (lane == 0)
-                hcorr = cc;
+            if (lane < 32)
+                reinterpret_cast<f16 *>(hp[r])[lane] = odd ? hq * (f16)0.0625f : hq;
         }
-        __syncthreads();
+        lds_barrier();
+
+        // each row's correction constant (see k_decode_frag.h): -1032 per
+        // low-field h, -72 per high-field h = -1152 per prepared (h/16) value
+        float hc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            hc[r] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                hc[r] = dot2(hp[r][j], (j & 1) ? half2_t{(f16)-1152.0f, (f16)-1152.0f}
+                                               : half2_t{(f16)-1032.0f, (f16)-1032.0f}, hc[r]);
+        }
 
         // down strip: lane = output row, the 32 prepared h values from LDS
-        float *yrow = y + ((size_t)slice * ntk + p) * H;
-        const float hc = hcorr;
 #pragma unroll
-        for (int r = 0; r < RBW; ++r) {
-            const int rb = wave * RBW + r;
-            if (rb < NRB)
-                yrow[rb * 64 + lane] = dot_chunk(dq[r], hp, hc) * sd[r];
+        for (int j = 0; j < RBW; ++j) {
+            const int rb = wave * RBW + j;
+            const float s = h2f(sd[j]);
+            half2_t mj[16];
+            if constexpr (!PRE) {
+                opaque(w[CPW + j]);
+                unpack_chunk(w[CPW + j], mj);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                y[((size_t)slice * ntk + p0 + r0 + r) * H + rb * 64 + lane] =
+                        dot_unpacked(PRE ? md[j] : mj, hp[r], hc[r]) * s;
         }
-        __syncthreads();
+    };
+
+    using std::integral_constant;
+    using std::true_type;
+    const int R0 = min(RG, nrows);
+    switch (R0) {
+    case 1: group(true_type{}, integral_constant<int, 1>{}, 0); break;
+    case 2: group(true_type{}, integral_constant<int, 2>{}, 0); break;
+    case 3: group(true_type{}, integral_constant<int, 3>{}, 0); break;
+    default: group(true_type{}, integral_constant<int, 4>{}, 0); break;
+    }
+    // more rows than a group (only with more than DECODE_XPRE tokens): one
+    // row at a time from the weights now in registers
+    for (int r0 = R0; r0 < nrows; ++r0) {
+        lds_barrier();   // the previous group is done with xp, red and hp
+        group(std::false_type{}, integral_constant<int, 1>{}, r0);
     }
 }
 
+constexpr int DECODE_PD = 4;   // weight chunks each wave keeps in flight
+
 template <int H>
-static void launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
-                            const int32_t *offsets, const uint8_t *const *blobs,
-                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
-                            const DevLayout &L, float *y)
+static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
+                           const int32_t *offsets, const uint8_t *const *blobs,
+                           const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
+                           const DevLayout &L, float *y)
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
-    hipLaunchKernelGGL((ffn_decode_kernel<H, NW>), grid, dim3(NW * 64), 0, s, x, perm, offsets,
-                       blobs, skip, I, E, k, g, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y);
+#define MOE_DECODE_LAUNCH(G)                                                                  \
+    hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD>), grid, dim3(NW * 64), 0, s, x, \
+                       perm, offsets, blobs, skip, I, E, k, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y)
+    switch (g) {
+    case 32: MOE_DECODE_LAUNCH(32); break;
+    case 64: MOE_DECODE_LAUNCH(64); break;
+    case 128: MOE_DECODE_LAUNCH(128); break;
+    default: return set_error(MOE_EUNSUPPORTED, "decode kernel: group %d not instantiated", g);
+    }
+#undef MOE_DECODE_LAUNCH
+    return MOE_OK;
 }
 
 // skip (may be null): a device table of E pointers; experts with a non-null
@@ -222,13 +358,16 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
     const f16 *xh = static_cast<const f16 *>(x);
     const uint8_t *const *b = reinterpret_cast<const uint8_t *const *>(blobs);
     const uint8_t *const *sk = reinterpret_cast<const uint8_t *const *>(skip);
+    int rc;
     switch (H) {
-    case 256: launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 512: launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 1024: launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 2048: launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 256: rc = launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 512: rc = launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 1024: rc = launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 2048: rc = launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
+    if (rc != MOE_OK)
+        return rc;
     MOE_LAUNCH_CHECK("ffn_decode_kernel");
     return MOE_OK;
 }

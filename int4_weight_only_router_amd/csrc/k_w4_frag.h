@@ -36,22 +36,4 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, uint32_t mag
     return r;
 }
 
-// Loads through the global address space (plain pointers derived from a
-// loaded blob address would otherwise become flat loads, which the hardware
-// also counts against the LDS wait counter).
-template <typename T>
-__device__ __forceinline__ T ldg(const T *p)
-{
-    typedef const __attribute__((address_space(1))) T gT;
-    return *(gT *)(p);
-}
-
-// SiLU(g) * u with the hardware exp2 / reciprocal (about 1 ulp each in fp32;
-// the result is rounded to fp16).
-__device__ __forceinline__ float swiglu_fast(float g, float u)
-{
-    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
-    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
 }  // namespace moe

@@ -104,6 +104,31 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Loads through the global address space (plain pointers derived from a
+// loaded blob address would otherwise become flat loads, which the hardware
+// also counts against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T ldg(const T *p)
+{
+    typedef const __attribute__((address_space(1))) T gT;
+    return *(gT *)(p);
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads (LDS
+// serves one wave's requests in order); no other wave is involved.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// SiLU(g) * u with the hardware exp2 / reciprocal (about 1 ulp each in fp32;
+// the result is rounded to fp16).
+__device__ __forceinline__ float swiglu_fast(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
     return (float)__builtin_bit_cast(f16, bits);
 }
