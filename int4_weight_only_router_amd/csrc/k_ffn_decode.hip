@@ -153,12 +153,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     uint16_t sgu[NSG];
 #pragma unroll
     for (int j = 0; j < NSG; ++j)
-        sgu[j] = ldg(gus + (size_t)(((wave * CPW + j * CPG) * 32) / G) * 64);
+        sgu[j] = ldg_nt(gus + (size_t)(((wave * CPW + j * CPG) * 32) / G) * 64);
     const uint16_t *dsc = reinterpret_cast<const uint16_t *>(blob + off_ds);
     uint16_t sd[RBW];
 #pragma unroll
     for (int r = 0; r < RBW; ++r)
-        sd[r] = ldg(dsc + ((size_t)(wave * RBW + r) * IG + (slice * 32) / G) * 64 + lane);
+        sd[r] = ldg_nt(dsc + ((size_t)(wave * RBW + r) * IG + (slice * 32) / G) * 64 + lane);
 
     // weight chunks of this wave: gate/up chunks 0..CPW-1 (one 1 KB run of the
     // fused 64-row block each), then its down blocks (the slice's 16-byte
@@ -170,9 +170,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     uint4_t w[NCH];
     auto issue = [&](int i) {
         if (i < CPW)
-            w[i] = ldg(guq + (size_t)i * 64);
+            w[i] = ldg_nt(guq + (size_t)i * 64);
         else if (i < NCH)
-            w[i] = ldg(dqw + (size_t)(i - CPW) * IC * 64);
+            w[i] = ldg_nt(dqw + (size_t)(i - CPW) * IC * 64);
     };
 #pragma unroll
     for (int i = 0; i < PD && i < NCH; ++i)

@@ -183,11 +183,12 @@ __global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs
     uint16_t sc[SB_D][2];   // their group scales
     auto load = [&](int i, int c) {   // c: absolute chunk of the block
         const uint8_t *q = qb + (size_t)c * 1024;
-        wq[i][0] = ldg(reinterpret_cast<const uint2_t *>(q));
-        wq[i][1] = ldg(reinterpret_cast<const uint2_t *>(q + 512));
+        // expert weights are streamed once per call: non-temporal
+        wq[i][0] = ldg_nt(reinterpret_cast<const uint2_t *>(q));
+        wq[i][1] = ldg_nt(reinterpret_cast<const uint2_t *>(q + 512));
         const uint8_t *sp = sb + (size_t)((c * 32) >> gshift) * 128;
-        sc[i][0] = ldg(reinterpret_cast<const uint16_t *>(sp));
-        sc[i][1] = ldg(reinterpret_cast<const uint16_t *>(sp + 64));
+        sc[i][0] = ldg_nt(reinterpret_cast<const uint16_t *>(sp));
+        sc[i][1] = ldg_nt(reinterpret_cast<const uint16_t *>(sp + 64));
     };
     // absolute chunk of this wave's f-th chunk in phase ph
     auto chunk_of = [&](int ph, int f) { return ph * (NKc / P) + ks * nckp + f; };

@@ -47,9 +47,9 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = min(c0 + 64 * u, nch - 1);
-            va[u] = ra[c];
+            va[u] = ldg_nt(ra + c);   // weights: read once per call
             if constexpr (SW)
-                vb[u] = rb[c];
+                vb[u] = ldg_nt(rb + c);
 #pragma unroll
             for (int t = 0; t < T_MAX; ++t)
                 xv[t][u] = xr[t][c];

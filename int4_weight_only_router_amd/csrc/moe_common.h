@@ -129,6 +129,16 @@ __device__ __forceinline__ float swiglu_fast(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// The same with the non-temporal hint: for data streamed once per use that
+// does not fit the last-level cache anyway (expert weights), so that it does
+// not evict the small data that does (router weights, tables, activations).
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const T *p)
+{
+    typedef const __attribute__((address_space(1))) T gT;
+    return __builtin_nontemporal_load((gT *)p);
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
     return (float)__builtin_bit_cast(f16, bits);
 }
