@@ -108,64 +108,13 @@ __device__ __forceinline__ void wave_count_scan(const int32_t *__restrict__ idx,
     __builtin_amdgcn_wave_barrier();
 }
 
-// Selection order of the router: a ranks before b iff its logit is larger,
-// or equal with a lower expert index (a strict total order).
-__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb)
-{
-    // bitwise, not short-circuit: no branch per comparison
-    return (va > vb) | ((va == vb) & (ea < eb));
-}
-
 struct Cand {
     float v;
     int e;   // -1: empty slot
 };
 
-// Top-k of one token's E logits by one wave (E <= 64*NV): lane l holds
-// experts l, l+64, ...; k rounds, each taking the best remaining pair by
-// (logit desc, index asc) -- a per-lane scan, then an xor-butterfly
-// reduction under the same strict order, so every lane agrees -- and
-// removing it from its owner lane.  sel[0..k) receives the pairs in order.
-template <int NV>
-__device__ __forceinline__ void wave_topk_nv(const float *l, int E, int k, int lane, Cand *sel)
-{
-    float v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = (e < E) ? l[e] : 0.0f;
-    }
-    unsigned live = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        live |= (lane + 64 * i < E) ? (1u << i) : 0u;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int be = -1;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + 64 * i;
-            const bool take = ((live >> i) & 1u) & ((be < 0) | ranks_before(v[i], e, bv, be));
-            bv = take ? v[i] : bv;
-            be = take ? e : be;
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            const bool take = (oe >= 0) & ((be < 0) | ranks_before(ov, oe, bv, be));
-            bv = take ? ov : bv;
-            be = take ? oe : be;
-        }
-        if (lane == 0)
-            sel[j] = Cand{bv, be};
-        if ((be & 63) == lane)
-            live &= ~(1u << (be >> 6));
-    }
-}
-
-// Selection key: a strictly larger key ranks before (ranks_before as one
-// unsigned 64-bit compare).  High word: the logit's bits made monotonic
+// Selection key: a strictly larger key ranks before in the selection order
+// (logit descending, then lower expert index), as one unsigned 64-bit compare.  High word: the logit's bits made monotonic
 // (negative values inverted, positive ones offset by the sign bit; -0 is
 // first turned into +0 so that equal logits tie); low word: 0xFFFF - e, so
 // that on a tie the lower expert index ranks first.  Empty slots use key 0,
@@ -175,6 +124,74 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e)
     const int u = __builtin_bit_cast(int, v + 0.0f);
     const uint32_t o = (uint32_t)(u ^ ((u >> 31) | (int)0x80000000));
     return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
+}
+
+// One step of a wave-wide maximum of 64-bit keys: each lane takes the larger
+// of its key and that of the lane DPP pattern CTRL names (a permutation
+// inside each 16-lane row, so every source lane exists).  Register moves
+// only: no LDS round trip per step.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t a)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)a, CTRL, 0xF, 0xF,
+                                                              false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(a >> 32), CTRL,
+                                                              0xF, 0xF, false);
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    return b > a ? b : a;
+}
+
+// Maximum of one key per lane over the wave, returned to every lane: within
+// each row by quad swaps (xor 1, xor 2), the half-row mirror and the row
+// mirror, then across the four rows by reading lanes 0, 16, 32 and 48.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t a)
+{
+    a = dpp_max_step<0xB1>(a);    // quad_perm [1,0,3,2]
+    a = dpp_max_step<0x4E>(a);    // quad_perm [2,3,0,1]
+    a = dpp_max_step<0x141>(a);   // row_half_mirror: 8-lane halves
+    a = dpp_max_step<0x140>(a);   // row_mirror: 16-lane rows
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), 16 * r);
+        const uint64_t v = ((uint64_t)hi << 32) | lo;
+        m = v > m ? v : m;
+    }
+    return m;
+}
+
+// Top-k of one token's E logits by one wave (E <= 64*NV): lane l holds the
+// selection keys of experts l, l+64, ...; k rounds, each taking the largest
+// remaining key (a per-lane scan, then wave_max_u64, so every lane agrees)
+// and clearing it at its owner lane.  The key orders exactly as the
+// selection order (logit desc, index asc); the logit is recovered from the
+// key's high word.  sel[0..k) receives the pairs in order.
+template <int NV>
+__device__ __forceinline__ void wave_topk_nv(const float *l, int E, int k, int lane, Cand *sel)
+{
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? topk_key(l[e], e) : 0ull;
+    }
+    for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i)
+            b = key[i] > b ? key[i] : b;
+        b = wave_max_u64(b);
+        const int e = 0xFFFF - (int)(uint32_t)(b & 0xFFFFu);
+        const uint32_t o = (uint32_t)(b >> 32);
+        const uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+        if (lane == 0)
+            sel[j] = Cand{__builtin_bit_cast(float, u), e};
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (e == lane + 64 * i)
+                key[i] = 0ull;
+    }
 }
 
 // LDS scratch of one wave_topk call: the blocks' candidates (nb*16), their

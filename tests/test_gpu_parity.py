@@ -238,6 +238,45 @@ def test_route_ties_go_to_lower_index():
     assert np.max(np.abs(w - ow)) <= WTOL
 
 
+@pytest.mark.parametrize("T,fused", [(1, True), (3, True), (8, False), (64, False)])
+def test_route_ties_512_experts(T, fused):
+    """The 512-expert selection (k rounds of a wave-wide key maximum) keeps
+    the lower expert index first on exact ties, also across lanes and key
+    slots, on the fused (route + sort) and the separate router paths."""
+    cfg = MI.E512
+    say("route ties E=512 T=%d fused=%d" % (T, fused))
+    x = MI.gen_x(cfg, T)
+    x[0] = 0.0                                  # all 512 logits equal -> experts 0..k-1
+    wr = MI.gen_router(cfg)
+    wr[400] = wr[3]                             # duplicated rows -> exact ties in other
+    wr[511] = wr[3]                             # lanes and key slots
+    wr[64] = wr[9]
+    wr[137] = wr[200]
+    if fused:
+        n = T * cfg.k
+        idx_t = torch.empty((T, cfg.k), dtype=torch.int32, device=DEV)
+        w_t = torch.empty((T, cfg.k), dtype=torch.float32, device=DEV)
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+        offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV)
+        perm = torch.empty(n, dtype=torch.int32, device=DEV)
+        inv = torch.empty(n, dtype=torch.int32, device=DEV)
+        wsb = M.moe_route_permute_workspace_bytes(T, cfg.k, cfg.E)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+        M.moe_route_permute(f16(x), f16(wr), None, T, cfg.H, cfg.E, cfg.k, 0, idx_t, w_t, counts,
+                            offsets, perm, inv, ws, wsb)
+        torch.cuda.synchronize()
+        idx, w = _np(idx_t), _np(w_t)
+        oi, ow, _ = O.route(x, wr, None, cfg.k)
+        c_ref, o_ref, p_ref, _ = O.permute(oi, cfg.E)
+        assert np.array_equal(_np(offsets), o_ref) and np.array_equal(_np(perm), p_ref[:n])
+    else:
+        idx, w = _route_gpu(f16(x), f16(wr), None, T, cfg.H, cfg.E, cfg.k)
+        oi, ow, _ = O.route(x, wr, None, cfg.k)
+    assert np.array_equal(idx, oi)
+    assert np.array_equal(idx[0], np.arange(cfg.k))
+    assert np.max(np.abs(w - ow)) <= WTOL
+
+
 # ----------------------------------------------------------- permutation
 
 def _permute_gpu(idx_np, E):
