@@ -10,7 +10,7 @@ namespace moe {
 // FP16 GEMV pair for the shared expert at small T (weights row-major fp16,
 // the layout the caller hands over).  One wave per output row, lanes along K
 // with 16-byte loads, every token's dot product from the same weight
-// registers, xor-butterfly reduction.  A pass covers U chunks of 8 K per
+// registers, a DPP wave sum at the end.  A pass covers U chunks of 8 K per
 // lane and issues all of its loads (weights and the tokens' K slices, at
 // clamped indices, so none is conditional) before any arithmetic: a long row
 // costs a few round trips instead of one per chunk.
@@ -82,13 +82,8 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
     for (int t = 0; t < T_MAX; ++t) {
         if (t >= T)
             continue;
-        float a = aa[t], b = bb[t];
-#pragma unroll
-        for (int st = 32; st >= 1; st >>= 1) {
-            a += __shfl_xor(a, st, 64);
-            if constexpr (SW)
-                b += __shfl_xor(b, st, 64);
-        }
+        const float a = wave_sum_f32(aa[t]);
+        const float b = SW ? wave_sum_f32(bb[t]) : 0.0f;
         if (lane == 0) {
             if constexpr (SW)
                 hout[(size_t)t * R + r] = (f16)(a / (1.0f + expf(-a)) * b);
@@ -98,18 +93,48 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_f16_kernel(
     }
 }
 
+// Chunks per lane and pass: no more than a row has (a clamped duplicate load
+// still costs an instruction), at most UMAX (registers).
+template <int UMAX>
+static int gemv_u(int K)
+{
+    const int per_lane = (K / 8 + 63) / 64;
+    int u = 2;
+    while (u < UMAX && u < per_lane)
+        u *= 2;
+    return u;
+}
+
+template <int T_MAX, int U, bool SW>
+static void launch_gemv(int R, hipStream_t s, const f16 *in, const f16 *wa, const f16 *wb, int T,
+                        int K, f16 *h, float *out)
+{
+    hipLaunchKernelGGL((gemv_f16_kernel<T_MAX, U, SW>), dim3((R + GEMV_WAVES - 1) / GEMV_WAVES),
+                       dim3(GEMV_WAVES * 64), 0, s, in, wa, wb, T, R, K, h, out);
+}
+
+template <int T_MAX, int UMAX, bool SW>
+static void launch_gemv_u(int R, hipStream_t s, const f16 *in, const f16 *wa, const f16 *wb, int T,
+                          int K, f16 *h, float *out)
+{
+    const int u = gemv_u<UMAX>(K);
+    if (u <= 2)
+        launch_gemv<T_MAX, (UMAX < 2 ? UMAX : 2), SW>(R, s, in, wa, wb, T, K, h, out);
+    else if (u <= 4)
+        launch_gemv<T_MAX, (UMAX < 4 ? UMAX : 4), SW>(R, s, in, wa, wb, T, K, h, out);
+    else
+        launch_gemv<T_MAX, UMAX, SW>(R, s, in, wa, wb, T, K, h, out);
+}
+
 template <int T_MAX, int U>
 static int launch_gemv_pair(const void *x, const void *wg, const void *wu, const void *wd, int T,
                             int H, int Is, float *out, f16 *h, hipStream_t s)
 {
-    dim3 b(GEMV_WAVES * 64);
-    hipLaunchKernelGGL((gemv_f16_kernel<T_MAX, U, true>), dim3((Is + GEMV_WAVES - 1) / GEMV_WAVES),
-                       b, 0, s, (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, Is, H, h,
-                       (float *)nullptr);
+    launch_gemv_u<T_MAX, U, true>(Is, s, (const f16 *)x, (const f16 *)wg, (const f16 *)wu, T, H, h,
+                                  (float *)nullptr);
     MOE_LAUNCH_CHECK("gemv_f16_kernel(gate/up)");
-    hipLaunchKernelGGL((gemv_f16_kernel<T_MAX, U, false>), dim3((H + GEMV_WAVES - 1) / GEMV_WAVES),
-                       b, 0, s, (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T, H, Is,
-                       (f16 *)nullptr, out);
+    launch_gemv_u<T_MAX, U, false>(H, s, (const f16 *)h, (const f16 *)wd, (const f16 *)nullptr, T,
+                                   Is, (f16 *)nullptr, out);
     MOE_LAUNCH_CHECK("gemv_f16_kernel(down)");
     return MOE_OK;
 }

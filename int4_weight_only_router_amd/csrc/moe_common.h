@@ -139,6 +139,32 @@ __device__ __forceinline__ T ldg_nt(const T *p)
     return __builtin_nontemporal_load((gT *)p);
 }
 
+// Sum of one fp32 value per lane over the wave, in a fixed order: quad
+// swaps (xor 1, xor 2), the half-row and row mirrors (register moves inside
+// each 16-lane row; after the quad steps a mirror pairs whole quads and
+// 8-lane halves), then the four row sums in row order.  Every lane gets the
+// result.  For sums that decide no discrete choice (the pinned router order
+// keeps its own butterfly).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_step(float a)
+{
+    return a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                              0, __builtin_bit_cast(int, a), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float a)
+{
+    a = dpp_add_step<0xB1>(a);    // quad_perm [1,0,3,2]
+    a = dpp_add_step<0x4E>(a);    // quad_perm [2,3,0,1]
+    a = dpp_add_step<0x141>(a);   // row_half_mirror
+    a = dpp_add_step<0x140>(a);   // row_mirror
+    const int ai = __builtin_bit_cast(int, a);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
     return (float)__builtin_bit_cast(f16, bits);
 }
