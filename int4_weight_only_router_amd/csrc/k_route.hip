@@ -118,17 +118,13 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
         float part = 0.0f;
         for (int e = lane; e < E; e += 64)
             part += expf(l[e] - m);
-#pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1)
-            part += __shfl_xor(part, sh, 64);
+        part = wave_sum_f32(part);   // softmax denominator (order fixed, not pinned)
         float p = 0.0f;
         if (lane < k)
             p = expf(st[lane].v - m) / part;
         if (flags & MOE_RENORM) {
             float ws = p;
-#pragma unroll
-            for (int sh = 32; sh >= 1; sh >>= 1)
-                ws += __shfl_xor(ws, sh, 64);
+            ws = wave_sum_f32(ws);
             p = p / ws;
         }
         if (lane < k) {
@@ -258,17 +254,13 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_topk_kernel(
     float part = 0.0f;
     for (int e = lane; e < E; e += 64)
         part += expf(l[e] - m);
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1)
-        part += __shfl_xor(part, sh, 64);
+    part = wave_sum_f32(part);   // softmax denominator (order fixed, not pinned)
     float p = 0.0f;
     if (lane < k)
         p = expf(st[lane].v - m) / part;
     if (flags & MOE_RENORM) {
         float ws = p;
-#pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1)
-            ws += __shfl_xor(ws, sh, 64);
+        ws = wave_sum_f32(ws);
         p = p / ws;
     }
     if (lane < k) {
@@ -412,18 +404,14 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
         float part = 0.0f;
         for (int ee = lane; ee < E; ee += 64)
             part += expf(lg[tt * E + ee] - m);
-#pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1)
-            part += __shfl_xor(part, sh, 64);
+        part = wave_sum_f32(part);   // softmax denominator (order fixed, not pinned)
         const float den = part;
         float p = 0.0f;
         if (lane < k)
             p = expf(st[lane].v - m) / den;
         if (flags & MOE_RENORM) {
             float ws = p;
-#pragma unroll
-            for (int sh = 32; sh >= 1; sh >>= 1)
-                ws += __shfl_xor(ws, sh, 64);
+            ws = wave_sum_f32(ws);
             p = p / ws;
         }
         if (lane < k) {

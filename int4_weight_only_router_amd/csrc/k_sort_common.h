@@ -275,10 +275,15 @@ __device__ __forceinline__ void wave_topk_t(const float *l, int E, int k, int la
         Cand *cand = reinterpret_cast<Cand *>(scratch);
         uint64_t *ckey = reinterpret_cast<uint64_t *>(cand + nb * 16);
         uint64_t *bkey = ckey + nb * 16;
-        for (int b = 0; b < nb; ++b)
-            block_topk(l, E, k, b, lane, cand + b * k, ckey + b * k, bkey);
-        __builtin_amdgcn_wave_barrier();
-        merge_topk(cand, ckey, nb * k, k, lane, sel);
+        if (nb == 1) {
+            // one block: its ranks are the final ones (k <= E fills every slot)
+            block_topk(l, E, k, 0, lane, sel, ckey, bkey);
+        } else {
+            for (int b = 0; b < nb; ++b)
+                block_topk(l, E, k, b, lane, cand + b * k, ckey + b * k, bkey);
+            __builtin_amdgcn_wave_barrier();
+            merge_topk(cand, ckey, nb * k, k, lane, sel);
+        }
     } else if constexpr (NVMAX > 2) {
         if (NVMAX <= 4 || nb <= 4)
             wave_topk_nv<4>(l, E, k, lane, sel);
