@@ -66,6 +66,9 @@ enum {
 
 enum { MOE_RENORM = 1u };                       /* moe_route flag */
 enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2, MOE_REGIME_SMALL = 3 };
+/* OR'd into the regime of moe_expert_ffn_plan / moe_expert_ffn_w4a16: y rows
+ * in token order (row t*k + j) instead of sorted order; see below. */
+enum { MOE_Y_TOKEN_ORDER = 0x100 };
 enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
 
 /* Thread-local text of the last error on this thread ("" if none). */
@@ -196,6 +199,8 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
  *            multiplied on the matrix cores; gate/up then down, h in ws.
  *            T > 32 is MOE_EUNSUPPORTED.  y is fp16 [1][T*k][H].
  *   BATCHED: tiled grouped GEMM, any T.  y is fp16 [1][T*k][H].
+ * regime may carry MOE_Y_TOKEN_ORDER (DECODE only: MOE_EUNSUPPORTED when the
+ * resolved regime is another); resolved_regime is returned without it.
  */
 int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
                         int *resolved_regime, int *y_dtype, int *y_slices,
@@ -216,7 +221,11 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
  *                  where a routed expert with a NULL entry is skipped (its y
  *                  rows are left unwritten for another launch to fill)
  *   y              device output, layout from moe_expert_ffn_plan; y_dtype
- *                  and y_slices must equal the plan's (MOE_EINVAL otherwise)
+ *                  and y_slices must equal the plan's (MOE_EINVAL otherwise).
+ *                  Row p holds sorted row p; with MOE_Y_TOKEN_ORDER in regime
+ *                  (DECODE only) the result of sorted row p goes to row
+ *                  perm[p] = t*k + j instead, so that moe_combine needs no
+ *                  inv_perm (one dependent memory round trip less)
  *   ws             device scratch of the plan's size (may be NULL if 0)
  * Rounding: DECODE converts h to fp16 before the down projection; SMALL and
  * BATCHED convert the weights to fp16(q * s) and store h and y as fp16.
@@ -260,7 +269,9 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
  * shared-expert output or 0.  fp32 sum in the order: experts j = 0..k-1
  * (each the slice sum), shared, residual; one final rounding.
  *   y            device, from moe_expert_ffn_w4a16
- *   inv_perm     device int32 [T*k];  topk_w device fp32 [T][k]
+ *   inv_perm     device int32 [T*k], or NULL when y is in token order
+ *                (MOE_Y_TOKEN_ORDER): then Y(t*k+j, c) is read directly
+ *   topk_w       device fp32 [T][k]
  *   shared_f32   device fp32 [T][H] or NULL
  *   residual_f16 device fp16 [T][H] or NULL (may alias out_f16)
  *   out_f16      device fp16 [T][H]

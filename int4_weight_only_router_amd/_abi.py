@@ -9,7 +9,8 @@ from . import build as _build
 __all__ = [
     "MoEError", "lib", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOMEM", "MOE_EHIP",
     "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
-    "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_DTYPE_F16", "MOE_DTYPE_F32", "EXPORTS",
+    "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_DTYPE_F16",
+    "MOE_DTYPE_F32", "EXPORTS",
     "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
@@ -24,6 +25,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_E
     0, -1, -2, -3, -4, -5, -6
 MOE_RENORM = 1
 MOE_REGIME_AUTO, MOE_REGIME_DECODE, MOE_REGIME_BATCHED, MOE_REGIME_SMALL = 0, 1, 2, 3
+MOE_Y_TOKEN_ORDER = 0x100   # OR'd into a regime: decode y rows in token order
 MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
 
 # every symbol include/moe_w4a16.h declares

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void combine_slices_kernel(
     if constexpr (GATED)
         gate = shared_gate_256(x + (size_t)t * H, wsg, H, red);
     if (j < k && c < H) {
-        const size_t p = (size_t)inv_perm[(size_t)t * k + j];
+        const size_t f = (size_t)t * k + j;
+        const size_t p = inv_perm ? (size_t)inv_perm[f] : f;   // NULL: y in token order
         const float *src = y + p * H + c;
         const size_t stride = ntk * H;
         float v = 0.0f;
@@ -126,7 +127,7 @@ __device__ __forceinline__ void routed_sum8(const YT *__restrict__ y,
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         const int jj = min(j, k - 1);
-        pj[j] = inv_perm[(size_t)t * k + jj];
+        pj[j] = inv_perm ? inv_perm[(size_t)t * k + jj] : t * k + jj;   // NULL: token order
         wj[j] = w[(size_t)t * k + jj];
     }
     Row8<YT> r[KMAX];

@@ -88,7 +88,7 @@ template <int H, int G, int NW, int PD>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
-    const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk,
+    const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk, int tok_order,
     int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, float *__restrict__ y)
 {
     constexpr int NK = H / 32;                 // input chunks of gate/up rows
@@ -143,8 +143,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const int IG = I / G;
     const int nrows = p1 - p0;
 
-    // token ids of the expert's first 64 rows (decode: at most 4 rows)
-    const int prow = (T > 1 && lane < nrows) ? ldg(perm + p0 + lane) : 0;
+    // flat indices t*k + j of the expert's first 64 rows (decode: at most 4
+    // rows); needed for the token of a row (T > 1) and for a token-order y
+    const int prow = ((T > 1 || tok_order) && lane < nrows) ? ldg(perm + p0 + lane) : 0;
 
     // scales: one per scale group among this wave's gate/up chunks, one per
     // down block (2 bytes per lane each)
@@ -288,6 +289,16 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
         }
 
         // down strip: lane = output row, the 32 prepared h values from LDS
+        // y row of each row of the group: its sorted position, or t*k + j
+        int yrow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = r0 + r;
+            if (tok_order)   // uniform: every lane takes the same branch
+                yrow[r] = (rr < 64) ? __shfl(prow, rr, 64) : ldg(perm + p0 + rr);
+            else
+                yrow[r] = p0 + rr;
+        }
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             const int rb = wave * RBW + j;
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
             }
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                y[((size_t)slice * ntk + p0 + r0 + r) * H + rb * 64 + lane] =
+                y[((size_t)slice * ntk + yrow[r]) * H + rb * 64 + lane] =
                         dot_unpacked(PRE ? md[j] : mj, hp[r], hc[r]) * s;
         }
     };
@@ -327,12 +338,13 @@ template <int H>
 static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
                            const int32_t *offsets, const uint8_t *const *blobs,
                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
-                           const DevLayout &L, float *y)
+                           bool tok_order, const DevLayout &L, float *y)
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
 #define MOE_DECODE_LAUNCH(G)                                                                  \
     hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD>), grid, dim3(NW * 64), 0, s, x, \
-                       perm, offsets, blobs, skip, I, E, k, ntk, L.gu_q, L.d_q, L.gu_s, L.d_s, y)
+                       perm, offsets, blobs, skip, I, E, k, ntk, tok_order ? 1 : 0, L.gu_q, L.d_q,  \
+                       L.gu_s, L.d_s, y)
     switch (g) {
     case 32: MOE_DECODE_LAUNCH(32); break;
     case 64: MOE_DECODE_LAUNCH(64); break;
@@ -348,7 +360,7 @@ static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t
 // null entry in `blobs` are not computed either.
 int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
                       const void *const *blobs, const void *const *skip, int T, int H, int I,
-                      int E, int k, int g, float *y, hipStream_t s)
+                      int E, int k, int g, bool tok_order, float *y, hipStream_t s)
 {
     const int ntk = T * k;
     if (ntk == 0)
@@ -360,10 +372,10 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
     const uint8_t *const *sk = reinterpret_cast<const uint8_t *const *>(skip);
     int rc;
     switch (H) {
-    case 256: rc = launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 512: rc = launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 1024: rc = launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
-    case 2048: rc = launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, L, y); break;
+    case 256: rc = launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
+    case 512: rc = launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
+    case 1024: rc = launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
+    case 2048: rc = launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
     if (rc != MOE_OK)

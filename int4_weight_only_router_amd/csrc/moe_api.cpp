@@ -38,7 +38,8 @@ int launch_route_split(const void *, const void *, const float *, int, int, int,
 int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
                    void *, hipStream_t);
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
-                      const void *const *, int, int, int, int, int, int, float *, hipStream_t);
+                      const void *const *, int, int, int, int, int, int, bool, float *,
+                      hipStream_t);
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
                        int, int, int, int, int, void *, void *, hipStream_t);
@@ -307,9 +308,15 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
     rc = check_expert_shape("moe_expert_ffn_plan", H, I, group);
     if (rc)
         return rc;
+    const bool tok = (regime & MOE_Y_TOKEN_ORDER) != 0;
+    regime &= ~MOE_Y_TOKEN_ORDER;
     if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_SMALL)
         return set_error(MOE_EINVAL, "moe_expert_ffn_plan: bad regime %d", regime);
     const int r = resolve_regime(T, H, I, regime);
+    if (tok && r != MOE_REGIME_DECODE)
+        return set_error(MOE_EUNSUPPORTED,
+                         "moe_expert_ffn_plan: token-order y is a DECODE-regime option "
+                         "(resolved regime %d)", r);
     if (r == MOE_REGIME_SMALL && !ffn_small_fits(T, H, I))
         return set_error(MOE_EUNSUPPORTED,
                          "moe_expert_ffn_plan: small-batch regime takes T <= 32 (T=%d)", T);
@@ -348,7 +355,7 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
                          need);
     if (r == MOE_REGIME_DECODE)
         return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
-                                 group,
+                                 group, (regime & MOE_Y_TOKEN_ORDER) != 0,
                                  static_cast<float *>(y), stream);
     if (r == MOE_REGIME_SMALL)
         return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
@@ -398,7 +405,7 @@ static int check_combine_args(const char *fn, const void *y, int y_dtype, int y_
         return set_error(MOE_EINVAL, "%s: fp16 y has exactly one slice", fn);
     if (H % 8)
         return set_error(MOE_EUNSUPPORTED, "%s: H=%d must be a multiple of 8", fn, H);
-    if (T > 0 && (!y || !inv_perm || !topk_w || !out_f16))
+    if (T > 0 && (!y || !topk_w || !out_f16))   // inv_perm NULL: y in token order
         return set_error(MOE_EINVAL, "%s: null pointer", fn);
     return MOE_OK;
 }

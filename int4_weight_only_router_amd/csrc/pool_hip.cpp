@@ -125,7 +125,8 @@ struct HipPoolBackend {
 
 namespace moe {
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
-                      const void *const *, int, int, int, int, int, int, float *, hipStream_t);
+                      const void *const *, int, int, int, int, int, int, bool, float *,
+                      hipStream_t);
 }
 
 struct moe_pool {
@@ -201,6 +202,7 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
         return rc;
     if (step)
         *step = st;
+    const bool tok = (a->regime & MOE_Y_TOKEN_ORDER) != 0;   // decode: y in token order
     int resolved = 0;
     rc = moe_expert_ffn_plan(a->T, a->H, a->I, E, a->k, a->group, a->regime, &resolved, nullptr,
                              nullptr, nullptr);
@@ -216,7 +218,7 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
             rc = P.publish(layer, stream);
         if (!rc)
             rc = moe::launch_ffn_decode(a->x_f16, a->perm, a->offsets, table, old_table, a->T,
-                                        a->H, a->I, E, a->k, a->group,
+                                        a->H, a->I, E, a->k, a->group, tok,
                                         static_cast<float *>(a->y), stream);
     } else if (!rc) {
         rc = P.publish(layer, stream);
@@ -230,7 +232,8 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
         return rc;
     if (rr)
         return rr;
-    return moe_combine(a->y, a->y_dtype, a->y_slices, a->inv_perm, a->topk_w, a->shared_f32,
+    return moe_combine(a->y, a->y_dtype, a->y_slices, tok ? nullptr : a->inv_perm, a->topk_w,
+                       a->shared_f32,
                        a->residual_f16, a->T, a->H, a->k, a->out_f16, stream);
 }
 

@@ -86,6 +86,10 @@ class MoELayer:
         d = self.device
         r, ydt, ysl, ffn_ws = A.moe_expert_ffn_plan(T, self.H, self.I, self.E, self.k, self.g,
                                                     regime)
+        if r == A.MOE_REGIME_DECODE:
+            # decode partials straight in token order: the combine then reads
+            # them without inv_perm (one dependent round trip less)
+            r |= A.MOE_Y_TOKEN_ORDER
         # route/permute scratch; zero-filled once (the fused router keeps an
         # atomic ticket in it)
         pws = max(A.moe_permute_workspace_bytes(T, self.k, self.E),
@@ -144,13 +148,14 @@ class MoELayer:
     def combine(self, b: LayerBuffers, residual=None, out=None, stream=None, x=None):
         """x (the layer input) is needed only when the shared expert is gated."""
         out = b.out if out is None else out
+        inv = None if b.regime & A.MOE_Y_TOKEN_ORDER else b.inv_perm
         if self.shared_gate is not None:
             if x is None:
                 raise ValueError("the gated shared expert needs the layer input x")
-            A.moe_combine_gated(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, b.shared_out,
+            A.moe_combine_gated(b.y, b.y_dtype, b.y_slices, inv, b.topk_w, b.shared_out,
                                 x, self.shared_gate, residual, b.T, self.H, self.k, out, stream)
             return out
-        A.moe_combine(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, b.shared_out, residual,
+        A.moe_combine(b.y, b.y_dtype, b.y_slices, inv, b.topk_w, b.shared_out, residual,
                       b.T, self.H, self.k, out, stream)
         return out
 

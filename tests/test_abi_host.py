@@ -55,6 +55,12 @@ def test_plan_regimes():
     assert M.moe_expert_ffn_plan(32, 2048, 8192, 64, 8, 128)[0] == M.MOE_REGIME_SMALL
     assert M.moe_expert_ffn_plan(4, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_DECODE
     assert M.moe_expert_ffn_plan(5, 2048, 1024, 64, 8, 128)[0] == M.MOE_REGIME_SMALL
+    # token-order y: a decode option; the resolved regime comes back without it
+    tok = M.MOE_Y_TOKEN_ORDER
+    assert M.moe_expert_ffn_plan(1, 2048, 1024, 64, 8, 128, tok) == (M.MOE_REGIME_DECODE,
+                                                                     M.MOE_DTYPE_F32, 32, 0)
+    assert M.moe_expert_ffn_plan(3, 2048, 1024, 64, 8, 128, M.MOE_REGIME_DECODE | tok)[0] == \
+        M.MOE_REGIME_DECODE
 
 
 @pytest.mark.parametrize("args,code", [
@@ -68,6 +74,9 @@ def test_plan_regimes():
     ((-1, 2048, 1024, 64, 8, 128), M.MOE_EINVAL),        # T < 0
     ((1, 2048, 1024, 64, 8, 128, 4), M.MOE_EINVAL),      # unknown regime
     ((33, 2048, 1024, 64, 8, 128, M.MOE_REGIME_SMALL), M.MOE_EUNSUPPORTED),   # T > 32
+    ((64, 2048, 1024, 64, 8, 128, M.MOE_Y_TOKEN_ORDER), M.MOE_EUNSUPPORTED),  # token order
+    ((1, 2048, 1024, 64, 8, 128, M.MOE_REGIME_BATCHED | M.MOE_Y_TOKEN_ORDER),
+     M.MOE_EUNSUPPORTED),                                                     # off decode
 ])
 def test_plan_rejections(args, code):
     with pytest.raises(M.MoEError) as ei:

@@ -349,8 +349,38 @@ def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
     blobs = OracleBlobs(cfg, layer).get(used)
     y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
     y = _np(b.y).astype(np.float64)
-    y_rows = y.sum(axis=0)[rows] if b.y_dtype == M.MOE_DTYPE_F32 else y[0][rows]
+    # decode partials are in token order: sorted row p sits at row perm[p]
+    yr = perm[rows] if b.regime & M.MOE_Y_TOKEN_ORDER else rows
+    y_rows = y.sum(axis=0)[yr] if b.y_dtype == M.MOE_DTYPE_F32 else y[0][yr]
     return check_close(y_rows, y_ref, "y %s T=%d" % (cfg.name, T))
+
+
+@pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 3), (MI.TINY, 16),
+                                   (MI.E512, 4)], ids=lambda v: getattr(v, "name", str(v)))
+def test_decode_token_order_y(cfg, T):
+    """Decode partials written in token order (MOE_Y_TOKEN_ORDER) are the
+    sorted-order partials moved to row perm[p], bit for bit, and the combine
+    reading them without inv_perm gives the same output bits as the sorted
+    partials combined through inv_perm."""
+    say("decode token order %s T=%d" % (cfg.name, T))
+    lay = make_layer(cfg, 0, shared=False)
+    xd = f16(MI.gen_x(cfg, T))
+    b = lay.buffers(T, M.MOE_REGIME_DECODE)
+    assert b.regime == M.MOE_REGIME_DECODE | M.MOE_Y_TOKEN_ORDER
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    out_tok = lay.combine(b).clone()
+    y_tok = b.y.clone()
+    b.y.fill_(7.0)
+    M.moe_expert_ffn_w4a16(xd, b.perm, b.offsets, lay.table, T, cfg.H, cfg.I, cfg.E, cfg.k,
+                           cfg.g, M.MOE_REGIME_DECODE, b.y, b.y_dtype, b.y_slices)
+    out_sorted = torch.empty_like(out_tok)
+    M.moe_combine(b.y, b.y_dtype, b.y_slices, b.inv_perm, b.topk_w, None, None, T, cfg.H, cfg.k,
+                  out_sorted)
+    torch.cuda.synchronize()
+    perm = _np(b.perm)
+    assert np.array_equal(_np(y_tok)[:, perm, :].view(np.int32), _np(b.y).view(np.int32))
+    assert np.array_equal(_np(out_tok).view(np.int16), _np(out_sorted).view(np.int16))
 
 
 @pytest.mark.parametrize("cfg,T,regime", [
