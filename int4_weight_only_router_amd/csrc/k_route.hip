@@ -94,9 +94,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             float a = acc[tt];
-#pragma unroll
-            for (int st = 32; st >= 1; st >>= 1)
-                a = a + __shfl_xor(a, st, 64);
+            a = pinned_xor_sum(a, lane);
             if (bias)
                 a = a + b;
             if (lane == 0)
@@ -362,9 +360,7 @@ __global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             float a = acc[tt];
-#pragma unroll
-            for (int st = 32; st >= 1; st >>= 1)
-                a = a + __shfl_xor(a, st, 64);
+            a = pinned_xor_sum(a, lane);
             if (bias)
                 a = a + b;
             if (lane == 0 && tt < T)

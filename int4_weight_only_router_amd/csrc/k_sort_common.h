@@ -108,6 +108,32 @@ __device__ __forceinline__ void wave_count_scan(const int32_t *__restrict__ idx,
     __builtin_amdgcn_wave_barrier();
 }
 
+// The router's pinned cross-lane sum of 64 partials: a_j += a_(j xor off)
+// for off = 32, 16, 8, 4, 2, 1 in that order, every lane ending with the
+// same value.  Each step adds exactly the value of lane j xor off, fetched
+// with the cheapest exchange that gives it: a permute across the two
+// halves (32), a swizzle inside each 32 lanes (16), and register moves
+// inside each 16-lane row -- rotate by 8 (8); shift left / right by 4, each
+// lane taking the side that lands on j xor 4 (4); quad permutes (2, 1).
+// Bit-identical to six __shfl_xor steps; all 64 lanes must be active.
+__device__ __forceinline__ float pinned_xor_sum(float a, int lane)
+{
+    a = a + __shfl_xor(a, 32, 64);
+    a = a + __builtin_bit_cast(float,
+                               __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, a), 0x401F));
+    a = a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                  0x128, 0xF, 0xF, false));
+    const int ai = __builtin_bit_cast(int, a);
+    const int up = __builtin_amdgcn_update_dpp(0, ai, 0x104, 0xF, 0xF, false);   // from j + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, ai, 0x114, 0xF, 0xF, false);   // from j - 4
+    a = a + __builtin_bit_cast(float, (lane & 4) ? dn : up);
+    a = a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                  0x4E, 0xF, 0xF, false));
+    a = a + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                  0xB1, 0xF, 0xF, false));
+    return a;
+}
+
 struct Cand {
     float v;
     int e;   // -1: empty slot
