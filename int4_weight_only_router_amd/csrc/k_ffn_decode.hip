@@ -114,16 +114,22 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const int slice = blockIdx.x;
     const int T = ntk / k;
     const bool xpre = T <= DECODE_XPRE;
+    // the blob section offsets are read now, while the expert lookup is in
+    // flight, not after it (a late kernel-argument load would be waited for
+    // at the first LDS wait)
+    asm volatile("" ::"s"(off_guq), "s"(off_dq), "s"(off_gus), "s"(off_ds));
 
     // activations of the whole (small) batch, each wave only the chunks it
     // multiplies: lane -> (token, chunk of the wave).  The loads go out now
     // and land during the expert lookup; each wave stages its own chunks, so
     // no workgroup barrier stands before the weight stream.
+    // Unconditional loads (a lane without a chunk reads token 0's): no
+    // branch around them, so the compiler's wait counts stay exact after it.
     half8_t xr[4];
     const bool xmine = xpre && lane < T * CPW;
     const int xt = lane / CPW, xcn = wave * CPW + lane % CPW;
-    if (xmine) {
-        const f16 *src = x + (size_t)xt * H + xcn * 32;
+    {
+        const f16 *src = x + (size_t)(xmine ? xt : 0) * H + xcn * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             xr[q] = ldg(reinterpret_cast<const half8_t *>(src + 8 * q));
@@ -179,14 +185,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     for (int i = 0; i < PD && i < NCH; ++i)
         issue(i);
 
-    if (xmine) {
-        // pinned here: prepared any earlier, the wait for x would come
-        // before the expert lookup is even issued
+    // pinned here: prepared any earlier, the wait for x would come before
+    // the expert lookup is even issued
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            asm volatile("" : "+v"(xr[q]));
+    for (int q = 0; q < 4; ++q)
+        asm volatile("" : "+v"(xr[q]));
+    if (xmine)
         prep_chunk_regs(xr, &xp[xt][xcn * 16], &xc[xt][xcn]);
-    }
 
     // One group of R routed rows (R a constant, so that no register is held
     // for absent rows).  FIRST: the weights are still streaming in and the
@@ -290,12 +295,16 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
         // down strip: lane = output row, the 32 prepared h values from LDS
         // y row of each row of the group: its sorted position, or t*k + j
+        // (pinned here: hoisted above the gate/up loop, the wait for the
+        // token-id load would hold the first dot product)
+        int pr = prow;
+        asm volatile("" : "+v"(pr));
         int yrow[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int rr = r0 + r;
             if (tok_order)   // uniform: every lane takes the same branch
-                yrow[r] = (rr < 64) ? __shfl(prow, rr, 64) : ldg(perm + p0 + rr);
+                yrow[r] = (rr < 64) ? __shfl(pr, rr, 64) : ldg(perm + p0 + rr);
             else
                 yrow[r] = p0 + rr;
         }
