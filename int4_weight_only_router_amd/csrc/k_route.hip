@@ -301,15 +301,19 @@ int launch_route_batched(const void *x, const void *wr, const float *bias, int T
 // and, when FUSE, the stable sort, then returns the counter to zero.  No
 // cache-wide fence is needed because all shared data moves through the
 // coherent path, and no workgroup ever waits for another.
-constexpr int RSPLIT_EPW = 4;
+// Experts (waves) per workgroup: 4 up to 128 experts; 16 above, so that 512
+// experts take 32 workgroups and 32 ticket arrivals rather than 128 (one
+// device-scope atomic on one address serialises at about 11 ns).
+constexpr int rsplit_epw(bool bige) { return bige ? 16 : 4; }
 
 template <int H, int TT, bool FUSE, bool BIGE>   // BIGE: E > 128
-__global__ __launch_bounds__(RSPLIT_EPW * 64) void route_split_kernel(
+__global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
     const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
     int T, int E, int k, unsigned flags, unsigned *ticket, float *ws_logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
 {
+    constexpr int RSPLIT_EPW = rsplit_epw(BIGE);
     constexpr int NCH = H / 8;
     constexpr int NCL = (NCH + 63) / 64;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -442,7 +446,8 @@ static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, 
 {
     unsigned *ticket = static_cast<unsigned *>(ws);
     float *lg = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
-    const dim3 grid((E + RSPLIT_EPW - 1) / RSPLIT_EPW), block(RSPLIT_EPW * 64);
+    const int epw = rsplit_epw(E > 128);
+    const dim3 grid((E + epw - 1) / epw), block(epw * 64);
     const size_t xb = (size_t)8 * H * sizeof(f16);
     const size_t lb = (size_t)8 * E * sizeof(float) + 16 + (size_t)8 * topk_scratch_bytes(E) +
                       (size_t)8 * 16 * sizeof(Cand) + (size_t)(8 * 16 + E) * sizeof(int);
