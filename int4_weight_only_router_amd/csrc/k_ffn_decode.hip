@@ -16,9 +16,10 @@
 // needed along K.  The waves split K, their partial sums meet in LDS, SwiGLU
 // is applied, and the 32 fp16 h values then multiply the slice's 32-column
 // strip of the down projection (one 1 KB run per 64 output rows).  Each
-// workgroup writes an fp32 partial y for its slice; moe_combine adds the
-// slices in order.  All weight loads of a workgroup are issued before any
-// arithmetic, so a workgroup keeps its whole ~96 KB in flight.
+// workgroup writes an fp32 partial y for its slice (at the row's sorted
+// position, or at t*k + j with MOE_Y_TOKEN_ORDER); moe_combine adds the
+// slices in order.  Each wave keeps a few weight chunks in flight and
+// computes each chunk as it lands (schedule notes at the kernel).
 #include "k_decode_frag.h"
 
 #include <type_traits>
