@@ -686,6 +686,41 @@ def test_small_batch_idle_waves_and_parts():
     check_close(_np(b.y)[0][rows].astype(np.float64), y_ref, "small batch idle waves y")
 
 
+@pytest.mark.parametrize("H,I,g,E,k,T", [(1024, 448, 64, 160, 16, 1), (1024, 448, 64, 160, 16, 4),
+                                          (2048, 256, 32, 16, 4, 2), (2048, 256, 64, 16, 4, 3),
+                                          (512, 192, 32, 16, 4, 4)])
+def test_decode_row_groups_and_shapes(H, I, g, E, k, T):
+    """Decode regime at the instantiated H and group sizes with every token
+    routed to the same k experts, so each expert holds T rows: one group of
+    1..4 rows sharing each weight unpack (down chunks unpacked ahead for up
+    to two rows, where used above), partials written in token order."""
+    cfg = MI.MoEConfig(93, "dec_h%d_g%d_t%d" % (H, g, T), H=H, E=E, k=k, I=I, g=g)
+    say("decode groups %s" % cfg.name)
+    lay = make_layer(cfg, 0, shared=False)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[3:3 + cfg.k] = 100.0
+    lay.bias = torch.from_numpy(bias).to(DEV)
+    x = MI.gen_x(cfg, T)
+    b = lay.buffers(T, M.MOE_REGIME_DECODE)
+    assert b.regime == M.MOE_REGIME_DECODE | M.MOE_Y_TOKEN_ORDER
+    xd = f16(x)
+    lay.route_permute(xd, b)
+    lay.experts(xd, b)
+    out = lay.combine(b)
+    torch.cuda.synchronize()
+    oi, ow, _ = O.route(x, MI.gen_router(cfg), bias, cfg.k)
+    assert np.array_equal(_np(b.topk_idx), oi)
+    counts, offsets, perm, inv = O.permute(oi, cfg.E)
+    assert np.all(counts[3:3 + cfg.k] == T)
+    rows = np.arange(T * cfg.k, dtype=np.int32)
+    blobs = OracleBlobs(cfg, 0).get(range(3, 3 + cfg.k))
+    y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
+    check_close(_np(b.y).astype(np.float64).sum(axis=0)[perm[rows]], y_ref, "y %s" % cfg.name)
+    ref = O.moe_layer(x, MI.gen_router(cfg), blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g,
+                      bias=bias)   # only the routed experts' blobs are packed
+    check_close(_np(out).astype(np.float64), ref["out_f64"], "out %s" % cfg.name)
+
+
 def test_zero_tokens_is_noop():
     cfg = MI.OLMOE_DECODE
     lay = make_layer(cfg, 0, shared=False)
