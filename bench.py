@@ -560,8 +560,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=2)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the hot path is built for one MI355X and no "
-              "multi-GPU path exists in this build (see the sharding notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the layer on one MI355X and "
+              "has no multi-GPU path (expert-parallel sharding is described in the design "
+              "notes, not implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
     import int4_weight_only_router_amd as M
