@@ -265,16 +265,20 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
  * of the model).  For each token t and column c:
  *   out[t,c] = fp16_rne( r + sum_j w[t,j] * Y(inv_perm[t*k+j], c) + s[t,c] )
  * where Y(p,c) is y[p,c] (y_dtype F16, y_slices 1) or the sum over slices of
- * y[slice][p][c] (F32) taken in slice order, r = residual[t,c] or 0, s the
+ * y[slice][p][c] (F32; the slices summed in two contiguous halves, each in
+ * slice order, then the halves added), r = residual[t,c] or 0, s the
  * shared-expert output or 0.  fp32 sum in the order: experts j = 0..k-1
  * (each the slice sum), shared, residual; one final rounding.
- *   y            device, from moe_expert_ffn_w4a16
+ *   y            device, from moe_expert_ffn_w4a16; 16-byte aligned
  *   inv_perm     device int32 [T*k], or NULL when y is in token order
  *                (MOE_Y_TOKEN_ORDER): then Y(t*k+j, c) is read directly
  *   topk_w       device fp32 [T][k]
  *   shared_f32   device fp32 [T][H] or NULL
  *   residual_f16 device fp16 [T][H] or NULL (may alias out_f16)
  *   out_f16      device fp16 [T][H]
+ * Errors: MOE_EINVAL for bad sizes or dtype (k outside 1..16, F16 y with
+ * more than one slice), a null y/topk_w/out pointer or a misaligned y;
+ * MOE_EUNSUPPORTED when H is not a multiple of 8.
  */
 int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
                 const float *topk_w, const float *shared_f32, const void *residual_f16,

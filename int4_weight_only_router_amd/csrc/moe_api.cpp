@@ -407,6 +407,8 @@ static int check_combine_args(const char *fn, const void *y, int y_dtype, int y_
         return set_error(MOE_EUNSUPPORTED, "%s: H=%d must be a multiple of 8", fn, H);
     if (T > 0 && (!y || !topk_w || !out_f16))   // inv_perm NULL: y in token order
         return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    if (reinterpret_cast<uintptr_t>(y) % 16)
+        return set_error(MOE_EINVAL, "%s: y must be 16-byte aligned", fn);
     return MOE_OK;
 }
 

@@ -106,6 +106,10 @@ def test_compute_calls_reject_before_launch():
     with pytest.raises(M.MoEError) as ei:
         M.moe_combine(1, M.MOE_DTYPE_F16, 4, 1, 1, None, None, 1, 2048, 8, 1, stream=0)
     assert ei.value.code == M.MOE_EINVAL
+    with pytest.raises(M.MoEError) as ei:   # y not 16-byte aligned
+        M.moe_combine(4104, M.MOE_DTYPE_F32, 32, None, 256, None, None, 1, 2048, 8, 512,
+                      stream=0)
+    assert ei.value.code == M.MOE_EINVAL and "aligned" in str(ei.value)
     with pytest.raises(M.MoEError) as ei:   # overlapping prepack buffers
         M.moe_prepack_experts(4096, 2, 256, 512, 64, 4096 + 256, stream=0)
     assert ei.value.code == M.MOE_EINVAL
