@@ -20,6 +20,10 @@ pytestmark = pytest.mark.gpu
 # group size 32 and an intermediate size (192) that leaves the last 256-column
 # tile of the fused gate/up matrix half empty
 G32 = MI.MoEConfig(91, "g32_i192", H=512, E=16, k=4, I=192, g=32)
+# fused router above 128 experts with a ragged last 64-expert block, up to the
+# largest expert count and k
+E1000 = MI.MoEConfig(94, "h256_e1000_k16", H=256, E=1000, k=16, I=128, g=64, zipf_s=1.1)
+E200 = MI.MoEConfig(95, "h512_e200_k3", H=512, E=200, k=3, I=128, g=64)
 
 
 def _np(t):
@@ -129,7 +133,8 @@ def test_route_bit_exact(cfg, T, renorm):
 
 @pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 3),
                                    (MI.OLMOE_DECODE, 8), (MI.OLMOE_DECODE, 9), (MI.E512, 1),
-                                   (MI.E512, 5), (MI.TINY, 16), (MI.E512, 70)],
+                                   (MI.E512, 5), (MI.TINY, 16), (MI.E512, 70), (E1000, 1),
+                                   (E1000, 4), (E200, 2), (E200, 3)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_route_permute_fused_bit_exact(cfg, T):
     say("route_permute %s T=%d" % (cfg.name, T))
