@@ -243,13 +243,18 @@ __device__ __forceinline__ void block_topk(const float *l, int E, int k, int b, 
     const uint64_t key = valid ? topk_key(v, e) : 0ull;
     bkey[lane] = key;
     __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
-    int rank = 0;
+    // four independent counts, so the compares do not form one serial chain
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
 #pragma unroll
-    for (int j = 0; j < 64; j += 2) {
+    for (int j = 0; j < 64; j += 4) {
         const uint4_t q = *reinterpret_cast<const uint4_t *>(bkey + j);
-        rank += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
-        rank += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
+        const uint4_t p = *reinterpret_cast<const uint4_t *>(bkey + j + 2);
+        r0 += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
+        r1 += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
+        r2 += (((uint64_t)p.y << 32) | p.x) > key ? 1 : 0;
+        r3 += (((uint64_t)p.w << 32) | p.z) > key ? 1 : 0;
     }
+    const int rank = (r0 + r1) + (r2 + r3);
     __builtin_amdgcn_wave_barrier();   // bkey is reused by the next block
     if (valid && rank < k) {
         cand[rank] = Cand{v, e};
