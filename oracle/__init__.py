@@ -46,6 +46,10 @@ def lib():
         L.oracle_pool_sim.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp]
         L.oracle_profile_pin.argtypes = [vp, i32, i32, i32, vp]
         L.oracle_pool_sim_pinned.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp]
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = None
+        L.oracle_get_threads.argtypes = []
+        L.oracle_get_threads.restype = i32
         for name in ("oracle_blob_layout", "oracle_quantize_rows", "oracle_pack_expert",
                      "oracle_dequant_rows", "oracle_route", "oracle_permute",
                      "oracle_expert_ffn", "oracle_shared_ffn", "oracle_shared_gate",
@@ -71,6 +75,18 @@ def _u16(a):
         a = a.view(np.uint16)
     assert a.dtype == np.uint16
     return a
+
+
+# ---------------------------------------------------------------- threads
+
+def set_threads(n: int) -> None:
+    """Worker threads of the per-row loops (route, expert FFN, shared FFN);
+    n <= 0 restores the OpenMP default.  Results do not depend on it."""
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().oracle_get_threads())
 
 
 # ------------------------------------------------------------------- fp16

@@ -15,7 +15,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fopenmp",
            "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)

@@ -32,10 +32,14 @@
  * bit for bit, and (b) the quantiser, whose codes are decided in fp32 like
  * the GPU quantiser.  Only the final layer output is rounded to fp16 (RNE).
  *
- * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off moe_oracle.c -lm
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fopenmp moe_oracle.c -lm
+ * (OpenMP only spreads independent rows over threads; see oracle_set_threads).
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -62,18 +66,47 @@ double oracle_f16_to_f64(uint16_t h)
 }
 
 /* Decode table of all 65536 fp16 values (filled once from the function
- * above; lookups return exactly the same doubles). */
+ * above; lookups return exactly the same doubles).  Filled before any
+ * parallel region starts, so worker threads only read it. */
 static double f16tab[65536];
 static int f16tab_ready = 0;
 
-static double H2D(uint16_t h)
+static void f16tab_init(void)
 {
     if (!f16tab_ready) {
         for (int i = 0; i < 65536; i++)
             f16tab[i] = oracle_f16_to_f64((uint16_t)i);
         f16tab_ready = 1;
     }
+}
+
+static double H2D(uint16_t h)
+{
+    f16tab_init();
     return f16tab[h];
+}
+
+/* ------------------------------------------------------------- threads */
+
+/*
+ * Worker threads for the per-row loops below (route: tokens; expert FFN:
+ * sorted rows; shared FFN: tokens).  Every row is computed by one thread with
+ * exactly the same operations in the same order as with one thread, so the
+ * results do not depend on the thread count; only the wall time does.
+ * n <= 0 restores the OpenMP default.  Without OpenMP everything runs on one
+ * thread.
+ */
+static int or_threads = 0;
+
+void oracle_set_threads(int n) { or_threads = n > 0 ? n : 0; }
+
+int oracle_get_threads(void)
+{
+#ifdef _OPENMP
+    return or_threads > 0 ? or_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* double -> IEEE binary16, round to nearest, ties to even. */
@@ -269,68 +302,90 @@ static float logit_pinned(const float *x, const float *w, int H)
  * not renormalised unless `renorm` is set.
  * Outputs: idx[T][k] int32, w[T][k] fp32, optionally logits[T][E] fp32.
  */
+/* Top-k, softmax weights and optional logits of one token (the steps of
+ * oracle_route below; l, p, taken are scratch of E entries). */
+static void route_token(const float *xf, const float *wf, const float *bias, int H, int E,
+                        int k, int renorm, float *l, double *p, char *taken, int32_t *idx,
+                        float *w, float *logits)
+{
+    for (int e = 0; e < E; e++) {
+        float v = logit_pinned(xf, wf + (int64_t)e * H, H);
+        if (bias)
+            v = v + bias[e];
+        l[e] = v;
+        if (logits)
+            logits[e] = v;
+    }
+    /* top-k by (logit descending, index ascending) */
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; j++) {
+        int best = -1;
+        for (int e = 0; e < E; e++) {
+            if (taken[e])
+                continue;
+            if (best < 0 || l[e] > l[best])
+                best = e;
+        }
+        taken[best] = 1;
+        idx[j] = best;
+    }
+    /* softmax over all E, fp64 */
+    double m = l[0];
+    for (int e = 1; e < E; e++)
+        if (l[e] > m) m = l[e];
+    double den = 0.0;
+    for (int e = 0; e < E; e++) {
+        p[e] = exp((double)l[e] - m);
+        den += p[e];
+    }
+    double sel = 0.0;
+    for (int j = 0; j < k; j++)
+        sel += p[idx[j]] / den;
+    for (int j = 0; j < k; j++) {
+        double pj = p[idx[j]] / den;
+        if (renorm)
+            pj = pj / sel;
+        w[j] = (float)pj;
+    }
+}
+
 int oracle_route(const uint16_t *x, const uint16_t *wr, const float *bias,
                  int T, int H, int E, int k, int renorm,
                  int32_t *idx, float *w, float *logits)
 {
     if (!x || !wr || !idx || !w || T < 0 || H <= 0 || H % 8 || E <= 0 || k <= 0 || k > E)
         return OR_EINVAL;
-    float *l = malloc(sizeof(float) * (size_t)E);
-    double *p = malloc(sizeof(double) * (size_t)E);
-    char *taken = malloc((size_t)E);
+    f16tab_init();
     float *wf = malloc(sizeof(float) * (size_t)E * H);   /* fp16 values, exact in fp32 */
-    float *xf = malloc(sizeof(float) * (size_t)H);
-    if (!l || !p || !taken || !wf || !xf) {
-        free(l); free(p); free(taken); free(wf); free(xf);
+    if (!wf)
         return OR_ENOMEM;
-    }
     for (int64_t i = 0; i < (int64_t)E * H; i++)
         wf[i] = (float)H2D(wr[i]);
-    for (int t = 0; t < T; t++) {
-        for (int h = 0; h < H; h++)
-            xf[h] = (float)H2D(x[(int64_t)t * H + h]);
-        for (int e = 0; e < E; e++) {
-            float v = logit_pinned(xf, wf + (int64_t)e * H, H);
-            if (bias)
-                v = v + bias[e];
-            l[e] = v;
-            if (logits)
-                logits[(int64_t)t * E + e] = v;
+    int rc = OR_OK;
+#pragma omp parallel num_threads(oracle_get_threads()) if (T > 1)
+    {
+        float *l = malloc(sizeof(float) * (size_t)E);
+        double *p = malloc(sizeof(double) * (size_t)E);
+        char *taken = malloc((size_t)E);
+        float *xf = malloc(sizeof(float) * (size_t)H);
+        int ok = l && p && taken && xf;
+        if (!ok) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
         }
-        /* top-k by (logit descending, index ascending) */
-        memset(taken, 0, (size_t)E);
-        for (int j = 0; j < k; j++) {
-            int best = -1;
-            for (int e = 0; e < E; e++) {
-                if (taken[e])
-                    continue;
-                if (best < 0 || l[e] > l[best])
-                    best = e;
-            }
-            taken[best] = 1;
-            idx[(int64_t)t * k + j] = best;
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; t++) {
+            if (!ok)
+                continue;
+            for (int h = 0; h < H; h++)
+                xf[h] = (float)H2D(x[(int64_t)t * H + h]);
+            route_token(xf, wf, bias, H, E, k, renorm, l, p, taken, idx + (int64_t)t * k,
+                        w + (int64_t)t * k, logits ? logits + (int64_t)t * E : NULL);
         }
-        /* softmax over all E, fp64 */
-        double m = l[0];
-        for (int e = 1; e < E; e++)
-            if (l[e] > m) m = l[e];
-        double den = 0.0;
-        for (int e = 0; e < E; e++) {
-            p[e] = exp((double)l[e] - m);
-            den += p[e];
-        }
-        double sel = 0.0;
-        for (int j = 0; j < k; j++)
-            sel += p[idx[(int64_t)t * k + j]] / den;
-        for (int j = 0; j < k; j++) {
-            double pj = p[idx[(int64_t)t * k + j]] / den;
-            if (renorm)
-                pj = pj / sel;
-            w[(int64_t)t * k + j] = (float)pj;
-        }
+        free(l); free(p); free(taken); free(xf);
     }
-    free(l); free(p); free(taken); free(wf); free(xf);
-    return OR_OK;
+    free(wf);
+    return rc;
 }
 
 /* ----------------------------------------------------------- permutation */
@@ -395,71 +450,87 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *off
         return OR_EINVAL;
     if (oracle_blob_layout(H, I, g, off, &total))
         return OR_EINVAL;
+    f16tab_init();
     int n = T * k;
     if (!rows)
         nrows = n;
-    double *xv = malloc(sizeof(double) * (size_t)H);
-    double *hv = malloc(sizeof(double) * (size_t)I);
-    /* dequantised matrices of the expert in use (decoded once per expert) */
-    double *Wg = malloc(sizeof(double) * (size_t)I * H);
-    double *Wu = malloc(sizeof(double) * (size_t)I * H);
-    double *Wd = malloc(sizeof(double) * (size_t)H * I);
-    int rc = OR_OK, cur = -1;
-    if (!xv || !hv || !Wg || !Wu || !Wd) {
-        rc = OR_ENOMEM;
-        goto done;
-    }
+    /* expert of every requested row, checked before any arithmetic */
+    int *ex = malloc(sizeof(int) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!ex)
+        return OR_ENOMEM;
     for (int r = 0; r < nrows; r++) {
         int p = rows ? rows[r] : r;
-        if (p < 0 || p >= n) {
-            rc = OR_EINVAL;
-            goto done;
-        }
         int e = 0;
-        while (e < E && !(offsets[e] <= p && p < offsets[e + 1]))
-            e++;
-        if (e == E || !blobs[e]) {
-            rc = OR_EINVAL;
-            goto done;
+        if (p >= 0 && p < n)
+            while (e < E && !(offsets[e] <= p && p < offsets[e + 1]))
+                e++;
+        if (p < 0 || p >= n || e == E || !blobs[e]) {
+            free(ex);
+            return OR_EINVAL;
         }
-        if (e != cur) {
-            const uint8_t *b = blobs[e];
-            const uint8_t *gq = b + off[0], *uq = b + off[1], *dq = b + off[2];
-            const uint16_t *gs = (const uint16_t *)(b + off[3]);
-            const uint16_t *us = (const uint16_t *)(b + off[4]);
-            const uint16_t *ds = (const uint16_t *)(b + off[5]);
-            for (int i = 0; i < I; i++)
-                for (int c = 0; c < H; c++) {
-                    Wg[(int64_t)i * H + c] = deq(gq, gs, H, g, i, c);
-                    Wu[(int64_t)i * H + c] = deq(uq, us, H, g, i, c);
-                }
-            for (int o = 0; o < H; o++)
-                for (int i = 0; i < I; i++)
-                    Wd[(int64_t)o * I + i] = deq(dq, ds, I, g, o, i);
-            cur = e;
-        }
-        int t = perm[p] / k;
-        for (int c = 0; c < H; c++)
-            xv[c] = H2D(x[(int64_t)t * H + c]);
-        for (int i = 0; i < I; i++) {
-            double a = 0.0, u = 0.0;
-            const double *wg = Wg + (int64_t)i * H, *wu = Wu + (int64_t)i * H;
-            for (int c = 0; c < H; c++) {
-                a += wg[c] * xv[c];
-                u += wu[c] * xv[c];
-            }
-            hv[i] = silu(a) * u;
-        }
-        for (int o = 0; o < H; o++) {
-            double acc = 0.0;
-            const double *wd = Wd + (int64_t)o * I;
-            for (int i = 0; i < I; i++)
-                acc += wd[i] * hv[i];
-            y[(int64_t)r * H + o] = acc;
-        }
+        ex[r] = e;
     }
-done:
-    free(xv); free(hv); free(Wg); free(Wu); free(Wd);
+    int rc = OR_OK;
+    /* rows in contiguous runs per thread: sorted rows of one expert stay
+     * together, so each thread decodes few experts */
+#pragma omp parallel num_threads(oracle_get_threads()) if (nrows > 1)
+    {
+        double *xv = malloc(sizeof(double) * (size_t)H);
+        double *hv = malloc(sizeof(double) * (size_t)I);
+        /* dequantised matrices of the expert in use (decoded once per expert) */
+        double *Wg = malloc(sizeof(double) * (size_t)I * H);
+        double *Wu = malloc(sizeof(double) * (size_t)I * H);
+        double *Wd = malloc(sizeof(double) * (size_t)H * I);
+        int ok = xv && hv && Wg && Wu && Wd, cur = -1;
+        if (!ok) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int r = 0; r < nrows; r++) {
+            if (!ok)
+                continue;
+            int p = rows ? rows[r] : r;
+            int e = ex[r];
+            if (e != cur) {
+                const uint8_t *b = blobs[e];
+                const uint8_t *gq = b + off[0], *uq = b + off[1], *dq = b + off[2];
+                const uint16_t *gs = (const uint16_t *)(b + off[3]);
+                const uint16_t *us = (const uint16_t *)(b + off[4]);
+                const uint16_t *ds = (const uint16_t *)(b + off[5]);
+                for (int i = 0; i < I; i++)
+                    for (int c = 0; c < H; c++) {
+                        Wg[(int64_t)i * H + c] = deq(gq, gs, H, g, i, c);
+                        Wu[(int64_t)i * H + c] = deq(uq, us, H, g, i, c);
+                    }
+                for (int o = 0; o < H; o++)
+                    for (int i = 0; i < I; i++)
+                        Wd[(int64_t)o * I + i] = deq(dq, ds, I, g, o, i);
+                cur = e;
+            }
+            int t = perm[p] / k;
+            for (int c = 0; c < H; c++)
+                xv[c] = H2D(x[(int64_t)t * H + c]);
+            for (int i = 0; i < I; i++) {
+                double a = 0.0, u = 0.0;
+                const double *wg = Wg + (int64_t)i * H, *wu = Wu + (int64_t)i * H;
+                for (int c = 0; c < H; c++) {
+                    a += wg[c] * xv[c];
+                    u += wu[c] * xv[c];
+                }
+                hv[i] = silu(a) * u;
+            }
+            for (int o = 0; o < H; o++) {
+                double acc = 0.0;
+                const double *wd = Wd + (int64_t)o * I;
+                for (int i = 0; i < I; i++)
+                    acc += wd[i] * hv[i];
+                y[(int64_t)r * H + o] = acc;
+            }
+        }
+        free(xv); free(hv); free(Wg); free(Wu); free(Wd);
+    }
+    free(ex);
     return rc;
 }
 
@@ -475,35 +546,44 @@ int oracle_shared_ffn(const uint16_t *x, const uint16_t *wg, const uint16_t *wu,
 {
     if (!x || !wg || !wu || !wd || !s || H <= 0 || Is <= 0)
         return OR_EINVAL;
+    f16tab_init();
     if (!toks)
         ntoks = T;
-    double *xv = malloc(sizeof(double) * (size_t)H);
-    double *hv = malloc(sizeof(double) * (size_t)Is);
-    if (!xv || !hv) {
-        free(xv); free(hv);
-        return OR_ENOMEM;
-    }
-    for (int r = 0; r < ntoks; r++) {
-        int t = toks ? toks[r] : r;
-        for (int c = 0; c < H; c++)
-            xv[c] = H2D(x[(int64_t)t * H + c]);
-        for (int i = 0; i < Is; i++) {
-            double a = 0.0, u = 0.0;
-            for (int c = 0; c < H; c++) {
-                a += H2D(wg[(int64_t)i * H + c]) * xv[c];
-                u += H2D(wu[(int64_t)i * H + c]) * xv[c];
+    int rc = OR_OK;
+#pragma omp parallel num_threads(oracle_get_threads()) if (ntoks > 1)
+    {
+        double *xv = malloc(sizeof(double) * (size_t)H);
+        double *hv = malloc(sizeof(double) * (size_t)Is);
+        int ok = xv && hv;
+        if (!ok) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int r = 0; r < ntoks; r++) {
+            if (!ok)
+                continue;
+            int t = toks ? toks[r] : r;
+            for (int c = 0; c < H; c++)
+                xv[c] = H2D(x[(int64_t)t * H + c]);
+            for (int i = 0; i < Is; i++) {
+                double a = 0.0, u = 0.0;
+                for (int c = 0; c < H; c++) {
+                    a += H2D(wg[(int64_t)i * H + c]) * xv[c];
+                    u += H2D(wu[(int64_t)i * H + c]) * xv[c];
+                }
+                hv[i] = silu(a) * u;
             }
-            hv[i] = silu(a) * u;
+            for (int o = 0; o < H; o++) {
+                double acc = 0.0;
+                for (int i = 0; i < Is; i++)
+                    acc += H2D(wd[(int64_t)o * Is + i]) * hv[i];
+                s[(int64_t)r * H + o] = acc;
+            }
         }
-        for (int o = 0; o < H; o++) {
-            double acc = 0.0;
-            for (int i = 0; i < Is; i++)
-                acc += H2D(wd[(int64_t)o * Is + i]) * hv[i];
-            s[(int64_t)r * H + o] = acc;
-        }
+        free(xv); free(hv);
     }
-    free(xv); free(hv);
-    return OR_OK;
+    return rc;
 }
 
 /*

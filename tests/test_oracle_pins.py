@@ -463,3 +463,80 @@ def test_gated_layer_is_routed_plus_gate_times_dense_shared():
     gate = 1.0 / (1.0 + np.exp(-(xs @ wsg.astype(np.float64))))
     assert np.allclose(r["out_f64"], r0["out_f64"] + gate[:, None] * dense, rtol=1e-11,
                        atol=1e-13)
+
+
+# -------------------------------------------------------- threads, coverage
+
+def test_thread_count_does_not_change_results():
+    """The per-row loops spread rows over threads; every row keeps its own
+    order of operations, so one thread and several give identical bits."""
+    cfg = MI.MoEConfig(97, "thr", H=256, E=8, k=2, I=128, g=64)
+    T = 37
+    x = MI.gen_x(cfg, T)
+    wr = MI.gen_router(cfg)
+    blobs = [O.pack_expert(*MI.gen_expert(cfg, 0, e), cfg.g) for e in range(cfg.E)]
+    wsh = tuple((np.random.default_rng(5).standard_normal(s) * 0.02).astype(np.float16)
+                for s in ((64, cfg.H), (64, cfg.H), (cfg.H, 64)))
+    outs = []
+    try:
+        for n in (1, 4):
+            O.set_threads(n)
+            r = O.moe_layer(x, wr, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, shared=wsh)
+            outs.append(r)
+    finally:
+        O.set_threads(0)
+    for key in ("idx", "w", "logits", "perm", "y", "shared", "out_f64"):
+        assert np.array_equal(np.asarray(outs[0][key]).view(np.uint8),
+                              np.asarray(outs[1][key]).view(np.uint8)), key
+
+
+def _distinct_moments(E, k, n):
+    """Exact mean and variance of the number of distinct experts touched by n
+    tokens that each pick a uniformly random set of k distinct experts."""
+    p0 = (1.0 - k / E) ** n                                   # one expert untouched
+    p00 = ((E - k) * (E - k - 1) / (E * (E - 1))) ** n if E > 1 else 0.0   # two untouched
+    mean = E * (1.0 - p0)
+    var = E * p0 * (1.0 - p0) + E * (E - 1) * (p00 - p0 * p0)
+    return mean, var
+
+
+@pytest.mark.parametrize("E,k,n", [(64, 8, 1), (64, 8, 4), (64, 8, 16), (512, 10, 30),
+                                   (8, 2, 5), (60, 4, 12)])
+def test_coverage_of_uniform_traces(E, k, n):
+    """Coverage formula of the local-inference explainer (step 3, how many
+    experts a prompt touches): with uniform ("hash") routing, n tokens touch
+    E (1 - (1 - k/E)^n) distinct experts on average.  Uniform routing is made
+    through the oracle's own router: zero activations and router weights and a
+    fresh iid fp32 bias per token, so the top-k of each token is a uniformly
+    random k-subset (exchangeable logits, ties of probability ~0); the
+    distinct count is the number of non-empty buckets of the oracle's
+    permutation.  The trial mean must lie within 3 standard errors."""
+    H = 8
+    trials = 150
+    rng = np.random.default_rng(E * 1000 + k * 10 + n)
+    x = np.zeros((1, H), np.float16)
+    wr = np.zeros((E, H), np.float16)
+    d = []
+    for _ in range(trials):
+        idx = np.concatenate([O.route(x, wr, rng.standard_normal(E).astype(np.float32), k)[0]
+                              for _ in range(n)])
+        counts, _, _, _ = O.permute(idx, E)
+        dt = int((counts > 0).sum())
+        assert k <= dt <= min(E, n * k)
+        d.append(dt)
+    mean, var = _distinct_moments(E, k, n)
+    se = math.sqrt(max(var, 0.0) / trials)
+    assert abs(np.mean(d) - mean) <= 3 * se + 1e-9, (np.mean(d), mean, se)
+    if n == 1:
+        assert all(v == k for v in d)
+
+
+def test_coverage_moments_brute_force():
+    """The closed-form moments above against exhaustive enumeration on a tiny
+    case (E = 5, k = 2, n = 3: every sequence of 2-subsets)."""
+    E, k, n = 5, 2, 3
+    subsets = list(itertools.combinations(range(E), k))
+    vals = [len(set().union(*seq)) for seq in itertools.product(subsets, repeat=n)]
+    mean, var = _distinct_moments(E, k, n)
+    assert math.isclose(np.mean(vals), mean, rel_tol=1e-12)
+    assert math.isclose(np.var(vals), var, rel_tol=1e-12)
