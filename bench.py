@@ -82,32 +82,63 @@ def build_layers(cfg, layers, dev, torch, M):
 
 # ------------------------------------------------------------- CPU baseline
 
-def cpu_baseline_decode(cfg, layers, steps):
-    """The oracle (plain C, one thread) on `steps` decode steps of the same
-    16-layer chain; weight generation and oracle packing of the routed
-    experts happen outside the timer."""
+def host_cpu():
+    """CPU model, physical cores (lscpu: cores per socket x sockets) and the
+    threads this process may use (affinity mask, OMP_NUM_THREADS)."""
+    import subprocess
+    model, cores, sockets = "unknown", None, None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            v = v.strip()
+            if k.strip() == "Model name":
+                model = v
+            elif k.strip() == "Core(s) per socket":
+                cores = int(v)
+            elif k.strip() == "Socket(s)":
+                sockets = int(v)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    physical = cores * sockets if cores and sockets else os.cpu_count() or 1
+    allowed = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(physical, allowed, omp) if omp > 0 else min(physical, allowed)
+    return {"model": model, "physical_cores": physical, "allowed_cpus": allowed,
+            "omp_num_threads": omp or None, "threads": max(1, threads)}
+
+
+def cpu_baseline_decode(cfg, layers, steps, threads=1):
+    """The oracle (plain C) on `steps` decode steps of the same 16-layer chain
+    with `threads` worker threads (its rows spread over them; one token has
+    k = 8 rows per layer, so at most 8 are busy); weight generation and
+    oracle packing of the routed experts happen outside the timer."""
     import numpy as np
     import moe_inputs as MI
     import oracle as O
+    O.set_threads(threads)
     routers = [MI.gen_router(cfg, l) for l in range(layers)]
     cache = {}
     busy = 0.0
-    for s in range(steps):
-        x = MI.gen_x(cfg, 1, step=s)
-        for l in range(layers):
-            t0 = time.perf_counter()
-            idx, w, _ = O.route(x, routers[l], None, cfg.k)
-            counts, offsets, perm, inv = O.permute(idx, cfg.E)
-            busy += time.perf_counter() - t0
-            need = [e for e in np.unique(idx) if (l, int(e)) not in cache]
-            for e, wts in MI.gen_experts(cfg, l, need):
-                cache[(l, int(e))] = O.pack_expert(*wts, cfg.g)
-            blobs = [cache.get((l, e)) for e in range(cfg.E)]
-            t0 = time.perf_counter()
-            y = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g)
-            out, _ = O.combine(y, inv, w, None, x)
-            busy += time.perf_counter() - t0
-            x = out
+    try:
+        for s in range(steps):
+            x = MI.gen_x(cfg, 1, step=s)
+            for l in range(layers):
+                t0 = time.perf_counter()
+                idx, w, _ = O.route(x, routers[l], None, cfg.k)
+                counts, offsets, perm, inv = O.permute(idx, cfg.E)
+                busy += time.perf_counter() - t0
+                need = [e for e in np.unique(idx) if (l, int(e)) not in cache]
+                for e, wts in MI.gen_experts(cfg, l, need):
+                    cache[(l, int(e))] = O.pack_expert(*wts, cfg.g)
+                blobs = [cache.get((l, e)) for e in range(cfg.E)]
+                t0 = time.perf_counter()
+                y = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g)
+                out, _ = O.combine(y, inv, w, None, x)
+                busy += time.perf_counter() - t0
+                x = out
+    finally:
+        O.set_threads(0)
     return steps / busy, busy
 
 
@@ -145,17 +176,35 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def _profile_traffic(kernel_srcs, key):
-    """HBM bytes per launch measured by rocprofv3 counters and recorded under
-    profiles/, if the kernel's sources have not changed since (else None)."""
+def _profile_record(kernel_srcs, key):
+    """The rocprofv3 figures recorded under profiles/traffic.json for a kernel
+    (counter HBM bytes per launch, kernel-trace average duration), if the
+    kernel's sources have not changed since they were taken (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))[key]
         if sources_sha256(kernel_srcs) != rec["source_sha256"]:
             return None
-        return int(rec["hbm_bytes_per_launch"])
+        return rec
     except (OSError, KeyError, ValueError):
         return None
+
+
+def hardware(torch):
+    p = torch.cuda.get_device_properties(0)
+    hw = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None),
+          "compute_units": p.multi_processor_count,
+          "hbm_GiB": round(p.total_memory / 2 ** 30, 1),
+          "rocm_hip": torch.version.hip, "torch": torch.__version__}
+    try:   # current and top shader clock as the driver reports them
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        hw["sclk"] = card.get("sclk clock speed:") or card.get("sclk")
+    except Exception:
+        hw["sclk"] = None
+    return hw
 
 
 def run_decode(args, torch, M):
@@ -230,7 +279,9 @@ def run_decode(args, torch, M):
     ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
     achieved = ffn_bytes / (t_ffn * 1e-3) / 1e9
     ms_step = elapsed * 1e3 / K
-    traffic = _profile_traffic(DECODE_KERNEL_SOURCES, "ffn_decode_kernel olmoe_decode")
+    prof = _profile_record(DECODE_KERNEL_SOURCES, "ffn_decode_kernel olmoe_decode") or {}
+    traffic = prof.get("hbm_bytes_per_launch")
+    trace_us = prof.get("trace_avg_us")
     res = {
         "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (batched), W4A16",
         "value": round(K / elapsed, 2),
@@ -253,16 +304,40 @@ def run_decode(args, torch, M):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "alg_bytes_per_launch": ffn_bytes,
-                     "avg_launch_us": round(t_ffn * 1e3, 3)},
+                     "avg_launch_us": round(t_ffn * 1e3, 3),
+                     "timing": "HIP events around a graph of the kernel's 16 layer launches "
+                               "on its launch stream, averaged per launch",
+                     # the same kernel's average duration in the committed
+                     # rocprofv3 kernel trace (null once the sources changed)
+                     "trace_avg_launch_us": trace_us,
+                     "frac_trace": None if not trace_us else
+                     round(ffn_bytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    res["hardware"] = hardware(torch)
+    if args.extras:
+        log("batched leg: one OLMoE-shaped layer at 4096 tokens")
+        res["batched_olmoe_t4096"] = batched_leg(torch, M)
+        torch.cuda.empty_cache()
+        log("partial-residency leg")
+        res["partial_residency"] = partial_leg(torch, M)
     if args.cpu_baseline:
+        cpu = host_cpu()
         log("cpu baseline (oracle, 1 thread)")
-        sps, busy = cpu_baseline_decode(cfg, L, args.cpu_steps)
-        res["cpu_baseline"] = {"value": round(sps, 4), "unit": "tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": "%d decode steps x 16 layers (route, permute, fp64 "
-                                         "expert FFN, combine; %.1f s of CPU work)"
-                                         % (args.cpu_steps, busy)}
+        sps1, busy1 = cpu_baseline_decode(cfg, L, args.cpu_steps, 1)
+        nt = cpu["threads"]
+        log("cpu baseline (oracle, %d threads)" % nt)
+        spsn, busyn = cpu_baseline_decode(cfg, L, args.cpu_steps_mt, nt)
+        used = min(nt, cfg.k)   # one token: k rows per layer to spread
+        res["cpu_baseline"] = {
+            "value": round(spsn, 4), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%d decode steps x 16 layers (route, permute, fp64 expert FFN, combine) "
+                      "with %d OpenMP threads, %d of them busy (k = 8 rows per layer); "
+                      "%.1f s of CPU work" % (args.cpu_steps_mt, nt, used, busyn),
+            "cpu_model": cpu["model"], "physical_cores": cpu["physical_cores"],
+            "allowed_cpus": cpu["allowed_cpus"], "threads": nt,
+            "single_thread": {"value": round(sps1, 4), "unit": "tokens/s", "cores": 1,
+                              "sample": "%d decode steps x 16 layers, %.1f s of CPU work"
+                                        % (args.cpu_steps, busy1)}}
     return res
 
 
@@ -384,7 +459,6 @@ def run_partial(args, torch, M):
     hindsight, the most any fixed set can hit."""
     import numpy as np
     import moe_inputs as MI
-    import oracle as O
     cfg = MI.PARTIAL
     dev = "cuda:0"
     L = cfg.layers
@@ -395,6 +469,23 @@ def run_partial(args, torch, M):
         lay._blobs = None
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    # pinned -> HBM rate of one expert blob copy (the miss path's unit), median
+    # of 16 copies timed with events on a side stream
+    tmp = torch.empty(blob_bytes, dtype=torch.uint8, device=dev)
+    cs = torch.cuda.Stream()
+    cms = []
+    with torch.cuda.stream(cs):
+        for e in range(17):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cs)
+            tmp.copy_(src[e % L, e % cfg.E], non_blocking=True)
+            e1.record(cs)
+            e1.synchronize()
+            if e:
+                cms.append(e0.elapsed_time(e1))
+    del tmp
+    cms.sort()
+    h2d_gbs = blob_bytes / (cms[len(cms) // 2] * 1e-3) / 1e9
     ptrs = [src[l, e].data_ptr() for l in range(L) for e in range(cfg.E)]
     pc = M.PoolConfig(layers=L, experts=cfg.E, topk=cfg.k, capacity=cfg.capacity,
                       spares=cfg.spares, decay_shift=args.decay_shift, expert_bytes=blob_bytes)
@@ -441,7 +532,6 @@ def run_partial(args, torch, M):
             trace_ids.clear()
             # the C most counted experts per layer, ties to the lower id
             pinned = np.sort(np.argsort(-counts, axis=1, kind="stable")[:, :cfg.capacity], axis=1)
-            assert np.array_equal(pinned, O.profile_pin(counts, cfg.capacity))
             log("profile: %d tokens" % (args.profile_prompts * args.tokens))
         for blk in range(args.blocks):
             M.moe_pool_reset(pool)
@@ -473,16 +563,9 @@ def run_partial(args, torch, M):
                 blk, blocks[-1]["tokens_per_s"], blocks[-1]["h2d_bytes"] / 2 ** 30))
     finally:
         M.moe_pool_destroy(pool)
-    # the policy replayed by the oracle's simulator on the recorded first
-    # block (warmup included) gives the same misses
     tl = np.array(trace_layers, np.int32)
     ti = np.array(trace_ids, np.int32)
-    if pinned is None:
-        _, sim_m, _, _ = O.pool_sim(L, cfg.E, cfg.capacity, args.decay_shift, cfg.k, tl, ti)
-    else:
-        _, sim_m, _ = O.pool_sim_pinned(L, cfg.E, pinned, cfg.k, tl, ti)
     nw = cfg.warmup_tokens * L
-    sim_measured = int(sim_m[nw:].sum())
     # static ceiling of block 0's measured trace: per layer the C experts
     # routed most often in hindsight
     mc = np.zeros((L, cfg.E), np.int64)
@@ -495,6 +578,20 @@ def run_partial(args, torch, M):
     h2d = sum(b["h2d_bytes"] for b in blocks)
     hits = sum(b["hits"] for b in blocks)
     misses = sum(b["misses"] for b in blocks)
+    # the local-inference explainer's step-5 model of a token's time:
+    # t_token = t_calc + bytes outside HBM / link bandwidth.  t_calc is the
+    # HBM roofline of the resident work (per layer: k routed blobs, router,
+    # x/out/residual); bytes outside = misses per token x blob bytes
+    mpt = misses / max(1, args.blocks * args.prompts * args.tokens)
+    t_calc = L * (cfg.k * blob_bytes + cfg.E * cfg.H * 2 + 3 * cfg.H * 2) / (HBM_PEAK_GBS * 1e9)
+    t_meas = tot_time / tot_tok
+    bound = {"t_calc_ms": round(t_calc * 1e3, 4),
+             "h2d_GBs_measured_one_blob": round(h2d_gbs, 1),
+             "t_token_bound_ms": round((t_calc + mpt * blob_bytes / (h2d_gbs * 1e9)) * 1e3, 4),
+             "t_token_measured_ms": round(t_meas * 1e3, 4),
+             "frac": round((t_calc + mpt * blob_bytes / (h2d_gbs * 1e9)) / t_meas, 4),
+             "t_token_bound_pcie5_ms": round((t_calc + mpt * blob_bytes / 64e9) * 1e3, 4),
+             "frac_pcie5": round((t_calc + mpt * blob_bytes / 64e9) / t_meas, 4)}
     return {
         "workload": "olmoe_partial: 16 layers, %d of 64 experts resident + %d spares per layer, "
                     "Zipf(1.0) router bias, %d blocks x (64 warmup + %d prompts x %d tokens)"
@@ -506,11 +603,39 @@ def run_partial(args, torch, M):
         "hit_rate": round(hits / max(1, hits + misses), 4),
         "misses_per_token": round(misses / (args.blocks * args.prompts * args.tokens), 3),
         "hit_ceiling_static_block0": round(ceiling, 4),
-        "simulator_misses_block0": sim_measured, "pool_misses_block0": blocks[0]["misses"],
+        "pool_misses_block0": blocks[0]["misses"],
         "policy": args.policy,
         "decay_shift": args.decay_shift if pinned is None else None,
         "profile_tokens": args.profile_prompts * args.tokens if pinned is not None else 0,
+        "t_token_model": bound,
     }
+
+
+def batched_leg(torch, M, T=4096):
+    """The batched OLMoE-shaped layer at T tokens (grouped INT4 -> FP16 MFMA
+    path), timed as `--workload batched` does: routed-FFN MFMA fraction on
+    the routed FLOPs and the whole layer's time."""
+    import moe_inputs as MI
+    a = argparse.Namespace(T=str(T), regime="auto", steps=64, warmup=2)
+    r = run_batched(a, torch, M, MI.OLMOE_BATCHED)
+    line = r["results"][0]
+    return {"workload": "olmoe_batched: one layer H=2048 E=64 top-8 I=1024 g=128, T=%d" % T,
+            "regime": line["regime"], "us": line["us"],
+            "routed_tflops": line["routed_tflops"], "routed_mfma_frac": line["routed_mfma_frac"],
+            "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+            "layer_tokens_per_s": round(T / (line["us"]["layer"] * 1e-6), 1),
+            "weight_copies": r["weight_copies"]}
+
+
+def partial_leg(torch, M, prompts=2, tokens=64):
+    """A short partial-residency run (one block: 64 warmup tokens, then
+    `prompts` x `tokens` tokens) with the explainer's t_token bound."""
+    a = argparse.Namespace(blocks=1, prompts=prompts, tokens=tokens, decay_shift=3,
+                           policy="decay", profile_prompts=0)
+    r = run_partial(a, torch, M)
+    keep = ("workload", "decode_tokens_per_s_pooled", "h2d_GiB_measured", "hit_rate",
+            "misses_per_token", "pool_misses_block0", "t_token_model")
+    return {k: r[k] for k in keep}
 
 
 def run_copy(args, torch, M):
@@ -557,7 +682,12 @@ def main():
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=2,
+                    help="decode steps of the one-thread oracle leg")
+    ap.add_argument("--cpu-steps-mt", type=int, default=8,
+                    help="decode steps of the multi-threaded oracle leg")
+    ap.add_argument("--no-extras", dest="extras", action="store_false", default=True,
+                    help="decode: skip the batched (4096 tokens) and partial-residency legs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library runs the layer on one MI355X and "

@@ -74,6 +74,18 @@ enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *moe_last_error(void);
 
+/*
+ * Zero-fills ws_bytes bytes of a device workspace with a kernel on `stream`
+ * (no hipMemsetAsync, so it may be recorded in a captured graph).  It is the
+ * initial fill that moe_route_permute and moe_shared_ffn_f16 require, and the
+ * way back after a call that did not run to completion (a failed launch, an
+ * aborted graph replay): those calls keep an arrival ticket / arrival counters
+ * at the start of their workspace, every completed call leaves them zero, and
+ * a non-zero leftover would make the next call skip its final reduction.
+ * Any address and size; MOE_EINVAL for a null ws with ws_bytes > 0.
+ */
+int moe_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------- expert blob */
 /*
  * Canonical expert blob (Horizon RunMap "02 / A solução": compact weights

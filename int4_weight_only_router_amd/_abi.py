@@ -11,7 +11,8 @@ __all__ = [
     "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
     "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_DTYPE_F16",
     "MOE_DTYPE_F32", "EXPORTS",
-    "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
+    "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts",
+    "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
@@ -30,7 +31,7 @@ MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
 
 # every symbol include/moe_w4a16.h declares
 EXPORTS = [
-    "moe_last_error", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
+    "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
@@ -82,6 +83,7 @@ vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
 def _declare(L):
     sig = {
         "moe_last_error": (C.c_char_p, []),
+        "moe_workspace_clear": (i32, [vp, sz, vp]),
         "moe_blob_layout": (i32, [i32, i32, i32, vp, vp]),
         "moe_quantize_experts": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_prepack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
@@ -166,6 +168,12 @@ def _s(stream):
 
 
 # ---------------------------------------------------------------- entries
+
+def moe_workspace_clear(ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().moe_workspace_clear(_p(ws), ws_bytes, _s(stream)))
+
 
 def moe_blob_layout(H, I, group):
     off = (C.c_int64 * 6)()

@@ -273,7 +273,10 @@ __global__ __launch_bounds__(GT) void f16_splitk_kernel(GemmArgs a)
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are acknowledged
         if (lane == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED,
+            // acquire-release at agent scope: this tile's partials are
+            // visible before the counter moves, and the last workgroup reads
+            // the others' partials only after their releases
+            const unsigned prev = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_ACQ_REL,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             s_last = prev == (unsigned)(KSW - 1);
         }
@@ -851,10 +854,7 @@ static int launch_w4(hipStream_t s, const GemmArgs &a)
     return MOE_OK;
 }
 
-#ifndef SPLITK_MAX_ROWS_CFG
-#define SPLITK_MAX_ROWS_CFG 1024
-#endif
-constexpr int SPLITK_MAX_ROWS = SPLITK_MAX_ROWS_CFG;   // shared expert: split-K kernel up to this many tokens
+constexpr int SPLITK_MAX_ROWS = 1024;   // shared expert: split-K kernel up to this many tokens
 #ifndef SPLITK_TARGET_WGS
 #define SPLITK_TARGET_WGS 256
 #endif

@@ -38,14 +38,8 @@ namespace moe {
 
 enum { SB_GATEUP = 0, SB_DOWN = 1 };
 
-#ifndef SB_WAVES_CFG
-#define SB_WAVES_CFG 4
-#endif
-#ifndef SB_WANT_CFG
-#define SB_WANT_CFG 2
-#endif
-constexpr int SB_WAVES = SB_WAVES_CFG;   // waves per workgroup
-constexpr int SB_WANT = SB_WANT_CFG;     // K split sized for this many workgroups per CU
+constexpr int SB_WAVES = 4;   // waves per workgroup
+constexpr int SB_WANT = 2;     // K split sized for this many workgroups per CU
 constexpr int SB_T = SB_WAVES * 64;
 constexpr int SB_D = 8;          // 32-K chunks in flight per wave
 constexpr int SB_MAXR = 32;      // rows of one expert (one MFMA column operand)

@@ -7,6 +7,8 @@
 // the input dimension, s = fp16_rne(amax / 7) with amax / 7 in fp32,
 // q = clamp(rne(w / s), -7, 7) with w / s in fp32, q = 0 when s = 0; stored as
 // u = q + 8, element 2b in the low nibble of byte b.
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -89,6 +91,40 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4_t *p, int64_t n16)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
          i += (int64_t)gridDim.x * blockDim.x)
         p[i] = uint4_t{0u, 0u, 0u, 0u};
+}
+
+// Byte-granular zero fill (any address and size): 16-byte stores over the
+// aligned middle, single bytes at the ends.
+__global__ __launch_bounds__(256) void zero_bytes_kernel(uint8_t *p, int64_t head, int64_t n16,
+                                                         int64_t tail)
+{
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = tid; i < head; i += stride)
+        p[i] = 0;
+    uint4_t *m = reinterpret_cast<uint4_t *>(p + head);
+    for (int64_t i = tid; i < n16; i += stride)
+        m[i] = uint4_t{0u, 0u, 0u, 0u};
+    uint8_t *t = p + head + 16 * n16;
+    for (int64_t i = tid; i < tail; i += stride)
+        t[i] = 0;
+}
+
+int launch_zero_bytes(void *p, size_t bytes, hipStream_t s)
+{
+    if (bytes == 0)
+        return MOE_OK;
+    uint8_t *b = static_cast<uint8_t *>(p);
+    int64_t head = (int64_t)((16 - (reinterpret_cast<uintptr_t>(b) & 15)) & 15);
+    if (head > (int64_t)bytes)
+        head = (int64_t)bytes;
+    const int64_t n16 = ((int64_t)bytes - head) / 16;
+    const int64_t tail = (int64_t)bytes - head - 16 * n16;
+    const int64_t work = std::max<int64_t>(std::max(head, tail), n16);
+    const unsigned blocks = (unsigned)std::min<int64_t>(1024, (work + 255) / 256);
+    hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, s, b, head, n16, tail);
+    MOE_LAUNCH_CHECK("zero_bytes_kernel");
+    return MOE_OK;
 }
 
 // Item ranges: [0,nguq) fused gate/up 16-byte chunks, then down chunks, then

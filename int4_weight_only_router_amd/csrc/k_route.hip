@@ -296,11 +296,10 @@ int launch_route_batched(const void *x, const void *wr, const float *bias, int T
 // the logits of experts 4g..4g+3 (one wave each, every router load issued at
 // once) for all T tokens and stores them to the workspace with agent-scope
 // (write-through) stores; once they are acknowledged, one thread takes a
-// ticket from an atomic counter.  The workgroup holding the last ticket reads
-// every logit back with agent-scope loads and does the top-k, the softmax
-// and, when FUSE, the stable sort, then returns the counter to zero.  No
-// cache-wide fence is needed because all shared data moves through the
-// coherent path, and no workgroup ever waits for another.
+// ticket from an atomic counter (acquire-release at agent scope).  The
+// workgroup holding the last ticket reads every logit back with agent-scope
+// loads and does the top-k, the softmax and, when FUSE, the stable sort, then
+// returns the counter to zero.  No workgroup ever waits for another.
 // Experts (waves) per workgroup: 4 up to 128 experts; 16 above, so that 512
 // experts take 32 workgroups and 32 ticket arrivals rather than 128 (one
 // device-scope atomic on one address serialises at about 11 ns).
@@ -375,8 +374,12 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
     __builtin_amdgcn_s_waitcnt(0);   // this wave's logit stores are acknowledged
     __syncthreads();
     if (threadIdx.x == 0) {
+        // release: the workgroup's logit stores (ordered before it by the
+        // barrier) are visible at agent scope before the ticket moves;
+        // acquire: the last workgroup's reads below come after every other
+        // workgroup's release
         const unsigned prev =
-            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.x - 1);
     }
     __syncthreads();

@@ -56,19 +56,14 @@ int launch_combine(const void *, int, int, const int32_t *, const float *, const
 int launch_quantize(const float *, const float *, const float *, int, int, int, int, void *,
                     hipStream_t);
 int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
+int launch_zero_bytes(void *, size_t, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
 constexpr int SMALL_MAX_T = 32;       // AUTO: small-batch kernel up to this many tokens
-#ifndef ROUTE_FUSED_MAX_T_CFG
-#define ROUTE_FUSED_MAX_T_CFG 5
-#endif
-constexpr int ROUTE_FUSED_MAX_T = ROUTE_FUSED_MAX_T_CFG;  // moe_route_permute: one fused launch up to this T
-#ifndef ROUTE_FUSED_MAX_T_BIGE_CFG
-#define ROUTE_FUSED_MAX_T_BIGE_CFG 4
-#endif
+constexpr int ROUTE_FUSED_MAX_T = 5;  // moe_route_permute: one fused launch up to this T
 // E > 128: the fused launch's single selecting workgroup takes every token's
 // top-k in turn, so it pays only for the smallest T
-constexpr int ROUTE_FUSED_MAX_T_BIGE = ROUTE_FUSED_MAX_T_BIGE_CFG;
+constexpr int ROUTE_FUSED_MAX_T_BIGE = 4;
 
 constexpr size_t ROUTE_TICKET_BYTES = 256;   // the fused router's arrival ticket, ws[0..256)
 
@@ -77,10 +72,7 @@ static bool route_fused(int T, int E)
     return T > 0 && T <= (E > 128 ? ROUTE_FUSED_MAX_T_BIGE : ROUTE_FUSED_MAX_T);
 }
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
-#ifndef SHARED_GEMV_MAX_T_CFG
-#define SHARED_GEMV_MAX_T_CFG 8
-#endif
-constexpr int SHARED_GEMV_MAX_T = SHARED_GEMV_MAX_T_CFG;  // shared expert: GEMV up to this many tokens
+constexpr int SHARED_GEMV_MAX_T = 8;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
 {
@@ -129,6 +121,16 @@ using namespace moe;
 extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
+
+int moe_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (ws_bytes == 0)
+        return MOE_OK;
+    if (!ws)
+        return set_error(MOE_EINVAL, "moe_workspace_clear: null workspace");
+    return launch_zero_bytes(ws, ws_bytes, stream);
+}
 
 int moe_blob_layout(int H, int I, int group, int64_t offsets[6], int64_t *total_bytes)
 {

@@ -3,6 +3,7 @@
 from the same draws by the oracle's own quantiser, tolerance checks, and a
 progress line on the real stderr before each GPU step."""
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -64,8 +65,13 @@ class OracleBlobs:
     def get(self, experts):
         c = self.cfg
         need = [e for e in sorted(set(int(e) for e in experts)) if e not in self.cache]
-        for e, w in MI.gen_experts(c, self.layer, need):
-            self.cache[e] = O.pack_expert(*w, c.g)
+        # draws and oracle packing in threads (numpy and the C oracle release
+        # the GIL); every expert is still packed by the oracle's quantiser
+        with ThreadPoolExecutor(8) as ex:
+            packed = ex.map(lambda e: (e, O.pack_expert(*MI.gen_expert(c, self.layer, e), c.g)),
+                            need)
+            for e, blob in packed:
+                self.cache[e] = blob
         return [self.cache.get(e) for e in range(c.E)]
 
 
@@ -109,20 +115,21 @@ def check_close(got, ref, what, atol=ATOL, rtol_l2=RTOL_L2):
     return mx, l2
 
 
-def sample_rows(offsets, n_per_expert=2, max_rows=64, seed=0):
-    """Sorted rows to check: first and last row of each non-empty expert bucket
-    (tile edges), plus seeded random rows, capped."""
+def sample_rows(offsets, n_per_expert=2, max_extra=64, seed=0):
+    """Sorted rows to check: the first and last row of every non-empty expert
+    bucket (tile edges: at most 2E rows, always all of them), plus up to
+    `max_extra` seeded random rows from inside the buckets."""
     rng = np.random.default_rng(seed)
-    rows = set()
+    edges, extra = set(), set()
     E = len(offsets) - 1
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
-            rows.add(a)
-            rows.add(b - 1)
+            edges.add(a)
+            edges.add(b - 1)
             for r in rng.integers(a, b, n_per_expert):
-                rows.add(int(r))
-    rows = sorted(rows)
-    if len(rows) > max_rows:
-        rows = sorted(rng.choice(rows, max_rows, replace=False).tolist())
-    return np.array(rows, np.int32)
+                extra.add(int(r))
+    extra = sorted(extra - edges)
+    if len(extra) > max_extra:
+        extra = rng.choice(extra, max_extra, replace=False).tolist()
+    return np.array(sorted(edges | set(extra)), np.int32)

@@ -2,8 +2,10 @@
 the same seeded inputs.  Integer results (quantised codes, routing indices,
 counts, offsets, permutations) must match bit for bit; floating results
 within max|d| <= 2e-2 and relative L2 <= 1e-2 (routing weights within 1e-5).
-At full sizes the oracle checks sampled rows/tokens, always including the
-first and last row of every expert bucket (tile edges)."""
+The routed FFN is compared on every row at every size (the oracle spreads
+rows over threads); whole layers on every token up to 512 tokens and, at
+4096, on the tokens of the first and last row of every expert bucket (tile
+edges) plus seeded random tokens."""
 import numpy as np
 import pytest
 import torch
@@ -334,7 +336,7 @@ def test_permute_hot_expert():
 
 # ------------------------------------------------------------ expert FFN
 
-def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
+def _ffn_case(cfg, T, regime, layer=0):
     lay = make_layer(cfg, layer, shared=False)
     x = MI.gen_x(cfg, T)
     b = lay.buffers(T, regime)
@@ -348,8 +350,7 @@ def _ffn_case(cfg, T, regime, layer=0, max_rows=48):
     assert np.array_equal(_np(b.topk_idx), oi)
     counts, offsets, perm, inv = O.permute(oi, cfg.E)
     assert np.array_equal(_np(b.offsets), offsets) and np.array_equal(_np(b.perm), perm[:T * cfg.k])
-    rows = sample_rows(offsets, max_rows=max_rows) if T * cfg.k > max_rows else \
-        np.arange(T * cfg.k, dtype=np.int32)
+    rows = np.arange(T * cfg.k, dtype=np.int32)   # every row, every bucket edge
     used = np.unique(oi)
     blobs = OracleBlobs(cfg, layer).get(used)
     y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
@@ -583,8 +584,16 @@ def test_layer_end_to_end(cfg, T):
     say("layer %s T=%d regime=%d" % (cfg.name, T, b.regime))
     out = lay.forward(f16(x), b, None if res is None else f16(res))
     torch.cuda.synchronize()
-    toks = np.arange(T) if T <= 16 else np.sort(
-        np.random.default_rng(T).choice(T, 12, replace=False))
+    if T <= 512:
+        toks = np.arange(T)
+    else:
+        # tokens owning the first and last row of every expert bucket, plus
+        # random ones
+        bias = MI.zipf_bias(cfg, 0)
+        oi, _, _ = O.route(x, MI.gen_router(cfg, 0), bias, cfg.k)
+        _, offsets, perm, _ = O.permute(oi, cfg.E)
+        rows = sample_rows(offsets, max_extra=128, seed=T)
+        toks = np.unique(perm[rows] // cfg.k)
     ref = _oracle_tokens(cfg, x, toks, residual=res)
     assert np.array_equal(_np(b.topk_idx)[toks], ref["idx"])
     check_close(_np(out)[toks].astype(np.float64), ref["out_f64"], "out %s T=%d" % (cfg.name, T))
@@ -762,3 +771,47 @@ def test_layer_shared_overlap_matches_serial_and_graph(cfg, T):
         assert torch.equal(og.view(torch.int16), ref.view(torch.int16))
         lay.forward(x, b, overlap_shared=True)   # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------ workspace recovery
+
+def test_workspace_clear_recovers_a_stale_ticket():
+    """A fused route+permute workspace whose ticket was left non-zero (as by
+    an interrupted call) skips the top-k; moe_workspace_clear restores it.
+    The fill touches exactly the bytes asked for, at any alignment."""
+    cfg = MI.OLMOE_DECODE
+    T = 1
+    say("workspace clear")
+    x = MI.gen_x(cfg, T, step=3)
+    wr = MI.gen_router(cfg)
+    n = T * cfg.k
+    wsb = M.moe_route_permute_workspace_bytes(T, cfg.k, cfg.E)
+    ws = torch.zeros(wsb + 64, dtype=torch.uint8, device=DEV)
+    # a stale ticket far from any arrival count: no workgroup takes the last
+    # ticket, so no top-k runs and the outputs keep their fill
+    ws[:4] = torch.tensor([0xE8, 0x03, 0, 0], dtype=torch.uint8)   # 1000
+    outs = [torch.full((T, cfg.k), -7, dtype=torch.int32, device=DEV),
+            torch.empty((T, cfg.k), dtype=torch.float32, device=DEV),
+            torch.empty(cfg.E, dtype=torch.int32, device=DEV),
+            torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV),
+            torch.empty(n, dtype=torch.int32, device=DEV),
+            torch.empty(n, dtype=torch.int32, device=DEV)]
+    M.moe_route_permute(f16(x), f16(wr), None, T, cfg.H, cfg.E, cfg.k, 0, *outs, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.all(_np(outs[0]) == -7)        # the stale ticket made every workgroup skip
+    M.moe_workspace_clear(ws, wsb)
+    outs[0].fill_(-7)
+    M.moe_route_permute(f16(x), f16(wr), None, T, cfg.H, cfg.E, cfg.k, 0, *outs, ws, wsb)
+    torch.cuda.synchronize()
+    oi, _, _ = O.route(x, wr, None, cfg.k)
+    assert np.array_equal(_np(outs[0]), oi)
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    # exact extent at odd addresses and sizes
+    buf = torch.full((4096,), 0xAB, dtype=torch.uint8, device=DEV)
+    for off, nb in [(3, 1), (5, 100), (16, 2048), (7, 3001), (0, 4096)]:
+        buf.fill_(0xAB)
+        M.moe_workspace_clear(buf.data_ptr() + off, nb)
+        torch.cuda.synchronize()
+        v = _np(buf)
+        assert np.all(v[off:off + nb] == 0) and np.all(v[:off] == 0xAB) and \
+            np.all(v[off + nb:] == 0xAB), (off, nb)
