@@ -198,6 +198,26 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
                       int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/*
+ * moe_route_permute without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus ws), results and
+ * errors as moe_route_permute; it calls no hipMalloc/hipFree and no
+ * allocating routine.  Its workspace is a 16 MiB array inside the library, one
+ * per GPU, held until the process ends; on the first call on a device its
+ * ticket is cleared by a kernel on `stream`, and every completed call leaves
+ * it clear again.  Shapes whose workspace (moe_route_permute_workspace_bytes)
+ * exceeds 16 MiB are rejected with MOE_ENOMEM before anything is launched
+ * (T = 4096 tokens with E = 512 experts and k = 10 need 8.7 MB; the
+ * workspace grows as 4*T*E bytes).  Every call on one GPU shares that
+ * array: calls that overlap in time on one GPU (different streams, or
+ * threads) race and must not be made.
+ */
+int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,
+                              const float *logit_bias, int T, int H, int E, int k, unsigned flags,
+                              int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets,
+                              int32_t *perm, int32_t *inv_perm, hipStream_t stream);
+
 /* ------------------------------------------------ routed expert FFN */
 /*
  * What moe_expert_ffn_w4a16 will do for a shape: the resolved regime, the

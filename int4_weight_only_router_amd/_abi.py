@@ -15,6 +15,7 @@ __all__ = [
     "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
+    "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "PoolConfig", "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
@@ -34,6 +35,7 @@ EXPORTS = [
     "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
+    "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "moe_pool_create",
     "moe_pool_prepare",
@@ -95,6 +97,8 @@ def _declare(L):
         "moe_route_permute_workspace_bytes": (sz, [i32, i32, i32]),
         "moe_route_permute": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp, vp, vp,
                                     vp, vp, vp, sz, vp]),
+        "moe_route_permute_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, C.c_uint, vp, vp,
+                                            vp, vp, vp, vp, vp]),
         "moe_expert_ffn_plan": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
         "moe_expert_ffn_w4a16": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        vp, i32, i32, vp, sz, vp]),
@@ -225,6 +229,13 @@ def moe_route_permute(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk
                                           flags, _p(topk_idx), _p(topk_w), _p(counts),
                                           _p(offsets), _p(perm), _p(inv_perm), _p(ws), ws_bytes,
                                           _s(stream)))
+
+
+def moe_route_permute_noalloc(x, w_router, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
+                              counts, offsets, perm, inv_perm, stream=None):
+    _check(lib().moe_route_permute_noalloc(_p(x), _p(w_router), _p(logit_bias), T, H, E, k,
+                                           flags, _p(topk_idx), _p(topk_w), _p(counts),
+                                           _p(offsets), _p(perm), _p(inv_perm), _s(stream)))
 
 
 def moe_expert_ffn_plan(T, H, I, E, k, group, regime=MOE_REGIME_AUTO):

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe_common.h"
@@ -72,6 +73,42 @@ static bool route_fused(int T, int E)
     return T > 0 && T <= (E > 128 ? ROUTE_FUSED_MAX_T_BIGE : ROUTE_FUSED_MAX_T);
 }
 constexpr int ROUTE_SMALL_MAX_T = 8;  // moe_route: one-workgroup kernel up to this T
+
+// Workspace of moe_route_permute_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (in host code it is only a stand-in for the symbol): each
+// device's address comes from hipGetSymbolAddress at set-up.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[MAX_DEVICES];
+
+// This device's scratch address; on the first call on a device (with that
+// device current) it is looked up and the fused router's ticket is cleared
+// by a kernel on `stream`, ordered before the caller's launches.
+static int noalloc_scratch(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    MOE_HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return set_error(MOE_EUNSUPPORTED, "moe_route_permute_noalloc: device %d out of range",
+                         dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        MOE_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p)
+            return set_error(MOE_EHIP, "moe_route_permute_noalloc: no address for the scratch");
+        const int rc = launch_zero_bytes(p, ROUTE_TICKET_BYTES, stream);
+        if (rc)
+            return rc;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
 constexpr int SHARED_GEMV_MAX_T = 8;  // shared expert: GEMV up to this many tokens
 
 static int check_expert_shape(const char *fn, int H, int I, int g)
@@ -276,6 +313,32 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
         pws = lws + route_batched_ws_bytes(T, E);
     }
     return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, pws, stream);
+}
+
+int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,
+                              const float *logit_bias, int T, int H, int E, int k, unsigned flags,
+                              int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets,
+                              int32_t *perm, int32_t *inv_perm, hipStream_t stream)
+{
+    clear_error();
+    int rc = check_route_args("moe_route_permute_noalloc", x_f16, w_router_f16, T, H, E, k,
+                              flags, topk_idx, topk_w);
+    if (rc)
+        return rc;
+    if (!counts || !offsets || (T > 0 && (!perm || !inv_perm)))
+        return set_error(MOE_EINVAL, "moe_route_permute_noalloc: null pointer");
+    const size_t need = moe_route_permute_workspace_bytes(T, k, E);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return set_error(MOE_ENOMEM,
+                         "moe_route_permute_noalloc: T=%d E=%d k=%d needs %zu bytes of scratch; "
+                         "the library holds %zu (use moe_route_permute with a workspace)",
+                         T, E, k, need, NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    rc = noalloc_scratch(stream, &ws);
+    if (rc)
+        return rc;
+    return moe_route_permute(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx, topk_w,
+                             counts, offsets, perm, inv_perm, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_permute_workspace_bytes(int T, int k, int E)
