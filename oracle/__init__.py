@@ -46,6 +46,12 @@ def lib():
         L.oracle_pool_sim.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp]
         L.oracle_profile_pin.argtypes = [vp, i32, i32, i32, vp]
         L.oracle_pool_sim_pinned.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, vp, vp, vp]
+        L.oracle_blob_layout_zp.argtypes = [i32, i32, i32, vp, vp]
+        L.oracle_quantize_rows_zp.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.oracle_pack_expert_zp.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.oracle_dequant_rows_zp.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.oracle_expert_ffn_fmt.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            vp, i32, vp]
         L.oracle_set_threads.argtypes = [i32]
         L.oracle_set_threads.restype = None
         L.oracle_get_threads.argtypes = []
@@ -54,7 +60,9 @@ def lib():
                      "oracle_dequant_rows", "oracle_route", "oracle_permute",
                      "oracle_expert_ffn", "oracle_shared_ffn", "oracle_shared_gate",
                      "oracle_combine",
-                     "oracle_pool_sim", "oracle_profile_pin", "oracle_pool_sim_pinned"):
+                     "oracle_pool_sim", "oracle_profile_pin", "oracle_pool_sim_pinned",
+                     "oracle_blob_layout_zp", "oracle_quantize_rows_zp", "oracle_pack_expert_zp",
+                     "oracle_dequant_rows_zp", "oracle_expert_ffn_fmt"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -108,10 +116,16 @@ def f64_to_f16(v) -> np.ndarray:
 
 # ------------------------------------------------------- blob & quantiser
 
-def blob_layout(H, I, g):
-    off = np.zeros(6, np.int64)
+FMT_SYM, FMT_ZP = 0, 1   # blob formats: symmetric (z = 8), zero point per group
+
+
+def blob_layout(H, I, g, fmt=FMT_SYM):
+    """Section offsets (6 symmetric, 9 with zero points) and total bytes."""
+    n = 9 if fmt == FMT_ZP else 6
+    off = np.zeros(n, np.int64)
     tot = np.zeros(1, np.int64)
-    _check(lib().oracle_blob_layout(H, I, g, _p(off), _p(tot)), "blob_layout")
+    f = lib().oracle_blob_layout_zp if fmt == FMT_ZP else lib().oracle_blob_layout
+    _check(f(H, I, g, _p(off), _p(tot)), "blob_layout")
     return [int(o) for o in off], int(tot[0])
 
 
@@ -124,14 +138,28 @@ def quantize_rows(w, g):
     return q, s
 
 
-def pack_expert(wg, wu, wd, g):
+def quantize_rows_zp(w, g):
+    """Zero-point quantiser: codes u [rows, K/2] u8, scales [rows, K/g] fp16
+    bits, zero points [rows, K/g] u8."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    q = np.empty((rows, K // 2), np.uint8)
+    s = np.empty((rows, K // g), np.uint16)
+    z = np.empty((rows, K // g), np.uint8)
+    _check(lib().oracle_quantize_rows_zp(_p(w), rows, K, g, _p(q), _p(s), _p(z)),
+           "quantize_rows_zp")
+    return q, s, z
+
+
+def pack_expert(wg, wu, wd, g, fmt=FMT_SYM):
     wg = np.ascontiguousarray(wg, dtype=np.float32)
     wu = np.ascontiguousarray(wu, dtype=np.float32)
     wd = np.ascontiguousarray(wd, dtype=np.float32)
     I, H = wg.shape
-    _, tot = blob_layout(H, I, g)
+    _, tot = blob_layout(H, I, g, fmt)
     blob = np.empty(tot, np.uint8)
-    _check(lib().oracle_pack_expert(_p(wg), _p(wu), _p(wd), H, I, g, _p(blob)), "pack_expert")
+    f = lib().oracle_pack_expert_zp if fmt == FMT_ZP else lib().oracle_pack_expert
+    _check(f(_p(wg), _p(wu), _p(wd), H, I, g, _p(blob)), "pack_expert")
     return blob
 
 
@@ -144,16 +172,33 @@ def dequant_rows(q, s, g):
     return out
 
 
-def blob_sections(blob, H, I, g):
-    """Views (gate_q, up_q, down_q, gate_s, up_s, down_s) of a canonical blob."""
-    off, _ = blob_layout(H, I, g)
+def dequant_rows_zp(q, s, z, g):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = _u16(s)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    rows, K2 = q.shape
+    out = np.empty((rows, 2 * K2), np.float64)
+    _check(lib().oracle_dequant_rows_zp(_p(q), _p(s), _p(z), rows, 2 * K2, g, _p(out)),
+           "dequant_rows_zp")
+    return out
+
+
+def blob_sections(blob, H, I, g, fmt=FMT_SYM):
+    """Views (gate_q, up_q, down_q, gate_s, up_s, down_s[, gate_z, up_z,
+    down_z]) of a canonical blob."""
+    off, _ = blob_layout(H, I, g, fmt)
     gq = blob[off[0]:off[0] + I * H // 2].reshape(I, H // 2)
     uq = blob[off[1]:off[1] + I * H // 2].reshape(I, H // 2)
     dq = blob[off[2]:off[2] + H * I // 2].reshape(H, I // 2)
     gs = blob[off[3]:off[3] + I * (H // g) * 2].view(np.uint16).reshape(I, H // g)
     us = blob[off[4]:off[4] + I * (H // g) * 2].view(np.uint16).reshape(I, H // g)
     ds = blob[off[5]:off[5] + H * (I // g) * 2].view(np.uint16).reshape(H, I // g)
-    return gq, uq, dq, gs, us, ds
+    if fmt != FMT_ZP:
+        return gq, uq, dq, gs, us, ds
+    gz = blob[off[6]:off[6] + I * (H // g)].reshape(I, H // g)
+    uz = blob[off[7]:off[7] + I * (H // g)].reshape(I, H // g)
+    dz = blob[off[8]:off[8] + H * (I // g)].reshape(H, I // g)
+    return gq, uq, dq, gs, us, ds, gz, uz, dz
 
 
 # ------------------------------------------------------------ layer steps
@@ -184,9 +229,10 @@ def permute(idx, E):
     return counts, offsets, perm, inv
 
 
-def expert_ffn(x, perm, offsets, blobs, H, I, E, k, g, rows=None):
+def expert_ffn(x, perm, offsets, blobs, H, I, E, k, g, rows=None, fmt=FMT_SYM):
     """y[len(rows) or T*k, H] fp64 for the selected sorted rows.  `blobs` is a
-    list of E canonical blobs (numpy uint8) or None for experts not needed."""
+    list of E canonical blobs (numpy uint8) or None for experts not needed;
+    fmt is their format (FMT_SYM or FMT_ZP)."""
     x = _u16(x)
     T = x.shape[0]
     perm = np.ascontiguousarray(perm, dtype=np.int32)
@@ -199,8 +245,9 @@ def expert_ffn(x, perm, offsets, blobs, H, I, E, k, g, rows=None):
         r = np.ascontiguousarray(rows, dtype=np.int32)
         n = r.size
     y = np.empty((n, H), np.float64)
-    _check(lib().oracle_expert_ffn(_p(x), _p(perm), _p(offsets), C.cast(ptrs, C.c_void_p),
-                                   T, H, I, E, k, g, _p(r), n, _p(y)), "expert_ffn")
+    _check(lib().oracle_expert_ffn_fmt(_p(x), _p(perm), _p(offsets), C.cast(ptrs, C.c_void_p),
+                                       T, H, I, E, k, g, int(fmt), _p(r), n, _p(y)),
+           "expert_ffn")
     return y
 
 
@@ -294,13 +341,13 @@ def pool_sim_pinned(L, E, pinned, k, ev_layer, ev_ids):
 
 
 def moe_layer(x, wr, blobs, H, I, E, k, g, bias=None, renorm=False,
-              shared=None, residual=None, shared_gate_w=None):
+              shared=None, residual=None, shared_gate_w=None, fmt=FMT_SYM):
     """The whole layer in the oracle: route, permute, expert FFN (all rows),
     optional shared FFN (optionally gated), combine.  Returns a dict of every
     intermediate."""
     idx, w, logits = route(x, wr, bias, k, renorm)
     counts, offsets, perm, inv = permute(idx, E)
-    y = expert_ffn(x, perm, offsets, blobs, H, I, E, k, g)
+    y = expert_ffn(x, perm, offsets, blobs, H, I, E, k, g, fmt=fmt)
     s = None if shared is None else shared_ffn(x, *shared)
     gt = None if shared_gate_w is None else shared_gate(x, shared_gate_w)
     out, o64 = combine(y, inv, w, s, residual, gt)

@@ -261,6 +261,136 @@ int oracle_dequant_rows(const uint8_t *q, const uint16_t *s, int rows, int K, in
     return OR_OK;
 }
 
+/* ------------------------------------------- zero-point (asymmetric) INT4 */
+
+/*
+ * Asymmetric variant of the format: the local-inference explainer's step 1
+ * ([LH], the file-size formula) gives every block of weights a scale and a
+ * zero point.  Canonical blob: the six sections above (codes and fp16
+ * scales, same places) followed by three more, each 256-byte aligned:
+ *   gate_z [I][H/g], up_z [I][H/g], down_z [H][I/g]    (u8, one per group)
+ * A stored nibble u in [0, 15] means W = (u - z) * s.  (The symmetric format
+ * is the case z = 8 for every group.)
+ */
+int oracle_blob_layout_zp(int H, int I, int g, int64_t off[9], int64_t *total)
+{
+    int64_t o6[6], t6;
+    int rc = oracle_blob_layout(H, I, g, o6, &t6);
+    if (rc)
+        return rc;
+    for (int i = 0; i < 6; i++)
+        off[i] = o6[i];
+    int64_t sz[3] = {(int64_t)I * (H / g), (int64_t)I * (H / g), (int64_t)H * (I / g)};
+    int64_t o = t6;
+    for (int i = 0; i < 3; i++) {
+        off[6 + i] = o;
+        o = al256(o + sz[i]);
+    }
+    *total = o;
+    return OR_OK;
+}
+
+/*
+ * Group-wise asymmetric INT4 quantisation of a [rows][K] fp32 matrix.
+ * READING (the explainer names the zero point, not its rule; this is the
+ * usual min/max affine rule, with zero kept inside the range):
+ *   lo = min(min w, 0), hi = max(max w, 0)                   (fp32)
+ *   s  = fp16_rne((hi - lo) / 15), the quotient in fp32
+ *   z  = clamp(rne(-lo / s), 0, 15), the quotient in fp32
+ *   u  = clamp(rne(w / s) + z, 0, 15), w / s in fp32
+ *   s == 0 (an all-zero group): z = 0 and u = 0.
+ * Codes are decided in fp32 so a GPU quantiser can make the same decisions.
+ */
+int oracle_quantize_rows_zp(const float *w, int rows, int K, int g,
+                            uint8_t *q, uint16_t *s, uint8_t *z)
+{
+    if (!w || !q || !s || !z || rows < 0 || K <= 0 || g <= 0 || K % g || K % 2)
+        return OR_EINVAL;
+    int ng = K / g;
+    for (int r = 0; r < rows; r++) {
+        const float *wr = w + (int64_t)r * K;
+        uint8_t *qr = q + (int64_t)r * (K / 2);
+        memset(qr, 0, (size_t)(K / 2));
+        for (int G = 0; G < ng; G++) {
+            float lo = 0.0f, hi = 0.0f;
+            for (int i = 0; i < g; i++) {
+                float v = wr[G * g + i];
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            float sf = (hi - lo) / 15.0f;
+            uint16_t sh = oracle_f64_to_f16((double)sf);
+            s[(int64_t)r * ng + G] = sh;
+            float sv = (float)oracle_f16_to_f64(sh);
+            int zi = 0;
+            if (sv != 0.0f) {
+                float t = -lo / sv;
+                double rz = nearbyint((double)t);
+                if (rz < 0.0) rz = 0.0;
+                if (rz > 15.0) rz = 15.0;
+                zi = (int)rz;
+            }
+            z[(int64_t)r * ng + G] = (uint8_t)zi;
+            for (int i = 0; i < g; i++) {
+                int c = G * g + i;
+                int ui = 0;
+                if (sv != 0.0f) {
+                    float t = wr[c] / sv;
+                    double ru = nearbyint((double)t) + zi;
+                    if (ru < 0.0) ru = 0.0;
+                    if (ru > 15.0) ru = 15.0;
+                    ui = (int)ru;
+                }
+                if (c & 1)
+                    qr[c / 2] |= (uint8_t)(ui << 4);
+                else
+                    qr[c / 2] |= (uint8_t)ui;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Quantise one expert's three projections into a zero-point canonical blob. */
+int oracle_pack_expert_zp(const float *wg, const float *wu, const float *wd,
+                          int H, int I, int g, uint8_t *blob)
+{
+    int64_t off[9], total;
+    int rc = oracle_blob_layout_zp(H, I, g, off, &total);
+    if (rc) return rc;
+    memset(blob, 0, (size_t)total);
+    rc = oracle_quantize_rows_zp(wg, I, H, g, blob + off[0], (uint16_t *)(blob + off[3]),
+                                 blob + off[6]);
+    if (rc) return rc;
+    rc = oracle_quantize_rows_zp(wu, I, H, g, blob + off[1], (uint16_t *)(blob + off[4]),
+                                 blob + off[7]);
+    if (rc) return rc;
+    return oracle_quantize_rows_zp(wd, H, I, g, blob + off[2], (uint16_t *)(blob + off[5]),
+                                   blob + off[8]);
+}
+
+/* Dequantised element (r, c) of a zero-point [rows][K] section: (u - z) * s,
+ * exact in fp64. */
+static double deq_zp(const uint8_t *qs, const uint16_t *ss, const uint8_t *zs, int K, int g,
+                     int r, int c)
+{
+    uint8_t b = qs[(int64_t)r * (K / 2) + c / 2];
+    int u = (c & 1) ? (b >> 4) : (b & 15);
+    int64_t G = (int64_t)r * (K / g) + c / g;
+    return (double)(u - (int)zs[G]) * H2D(ss[G]);
+}
+
+int oracle_dequant_rows_zp(const uint8_t *q, const uint16_t *s, const uint8_t *z, int rows,
+                           int K, int g, double *out)
+{
+    if (!q || !s || !z || !out || K % g || K % 2)
+        return OR_EINVAL;
+    for (int r = 0; r < rows; r++)
+        for (int c = 0; c < K; c++)
+            out[(int64_t)r * K + c] = deq_zp(q, s, z, K, g, r, c);
+    return OR_OK;
+}
+
 /* ---------------------------------------------------------------- router */
 
 /*
@@ -437,18 +567,21 @@ static double silu(double a) { return a / (1.0 + exp(-a)); }
  * reads compact weights and scales, uses the FP16 activations and never keeps
  * an expanded expert; here each element is decoded on use).  READING: SwiGLU,
  *   h = silu(Wg x) * (Wu x),  y = Wd h,  W = q * s,  all in fp64.
+ * W is decoded per the blob format fmt: 0 symmetric ((u - 8) s), 1 zero
+ * point ((u - z) s, oracle_blob_layout_zp).
  * Sorted row p (offsets[e] <= p < offsets[e+1]) belongs to expert e and to
  * token t = perm[p] / k.  `rows` (length nrows) selects sorted rows to
  * compute; NULL means all T*k rows.  y is [nrows][H] fp64.
  */
-int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
-                      const uint8_t *const *blobs, int T, int H, int I, int E, int k, int g,
-                      const int32_t *rows, int nrows, double *y)
+int oracle_expert_ffn_fmt(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
+                          const uint8_t *const *blobs, int T, int H, int I, int E, int k, int g,
+                          int fmt, const int32_t *rows, int nrows, double *y)
 {
-    int64_t off[6], total;
-    if (!x || !perm || !offsets || !blobs || !y || k <= 0)
+    int64_t off[9], total;
+    if (!x || !perm || !offsets || !blobs || !y || k <= 0 || (fmt != 0 && fmt != 1))
         return OR_EINVAL;
-    if (oracle_blob_layout(H, I, g, off, &total))
+    if (fmt == 1 ? oracle_blob_layout_zp(H, I, g, off, &total)
+                 : oracle_blob_layout(H, I, g, off, &total))
         return OR_EINVAL;
     f16tab_init();
     int n = T * k;
@@ -498,14 +631,19 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *off
                 const uint16_t *gs = (const uint16_t *)(b + off[3]);
                 const uint16_t *us = (const uint16_t *)(b + off[4]);
                 const uint16_t *ds = (const uint16_t *)(b + off[5]);
+                const uint8_t *gz = fmt ? b + off[6] : NULL, *uz = fmt ? b + off[7] : NULL,
+                              *dz = fmt ? b + off[8] : NULL;
                 for (int i = 0; i < I; i++)
                     for (int c = 0; c < H; c++) {
-                        Wg[(int64_t)i * H + c] = deq(gq, gs, H, g, i, c);
-                        Wu[(int64_t)i * H + c] = deq(uq, us, H, g, i, c);
+                        Wg[(int64_t)i * H + c] = fmt ? deq_zp(gq, gs, gz, H, g, i, c)
+                                                     : deq(gq, gs, H, g, i, c);
+                        Wu[(int64_t)i * H + c] = fmt ? deq_zp(uq, us, uz, H, g, i, c)
+                                                     : deq(uq, us, H, g, i, c);
                     }
                 for (int o = 0; o < H; o++)
                     for (int i = 0; i < I; i++)
-                        Wd[(int64_t)o * I + i] = deq(dq, ds, I, g, o, i);
+                        Wd[(int64_t)o * I + i] = fmt ? deq_zp(dq, ds, dz, I, g, o, i)
+                                                     : deq(dq, ds, I, g, o, i);
                 cur = e;
             }
             int t = perm[p] / k;
@@ -532,6 +670,14 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *off
     }
     free(ex);
     return rc;
+}
+
+/* The symmetric format (z = 8): the entry point the tests use by default. */
+int oracle_expert_ffn(const uint16_t *x, const int32_t *perm, const int32_t *offsets,
+                      const uint8_t *const *blobs, int T, int H, int I, int E, int k, int g,
+                      const int32_t *rows, int nrows, double *y)
+{
+    return oracle_expert_ffn_fmt(x, perm, offsets, blobs, T, H, I, E, k, g, 0, rows, nrows, y);
 }
 
 /*
