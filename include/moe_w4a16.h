@@ -70,6 +70,12 @@ enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2, MOE_R
  * in token order (row t*k + j) instead of sorted order; see below. */
 enum { MOE_Y_TOKEN_ORDER = 0x100 };
 enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
+/* Expert blob formats: symmetric codes, or codes with a zero point per group
+ * (lucashiago.com.br explainer, step 1: each block carries a scale and a zero
+ * point).  MOE_W4_ZERO_POINT is OR'd into the regime of moe_expert_ffn_plan /
+ * moe_expert_ffn_w4a16 / moe_pool_layer_args when the blobs are FMT_ZP. */
+enum { MOE_FMT_SYM = 0, MOE_FMT_ZP = 1 };
+enum { MOE_W4_ZERO_POINT = 0x200 };
 
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *moe_last_error(void);
@@ -130,6 +136,32 @@ int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *d
 /* Inverse of moe_prepack_experts (for inspection and tests). */
 int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *dst,
                        hipStream_t stream);
+
+/*
+ * Zero-point (asymmetric) INT4 blobs (lucashiago.com.br explainer, step 1:
+ * each block of weights carries a scale and a zero point).  Canonical blob:
+ * the six sections above at the same offsets, then gate_z[I][H/g],
+ * up_z[I][H/g], down_z[H][I/g] (u8, one zero point z in [0, 15] per group),
+ * each 256-byte aligned; a stored nibble u in [0, 15] means W = (u - z) * s.
+ * (MOE_FMT_SYM is the case z = 8 with no zero-point sections.)
+ * moe_blob_layout_fmt: offsets[0..8] (the last three 0 for MOE_FMT_SYM).
+ * moe_quantize_experts_fmt with MOE_FMT_ZP quantises per group with the
+ * reading lo = min(min w, 0), hi = max(max w, 0), s = fp16_rne((hi - lo)/15),
+ * z = clamp(rne(-lo/s), 0, 15), u = clamp(rne(w/s) + z, 0, 15), quotients in
+ * fp32; s = 0 gives z = u = 0.  moe_prepack_experts_fmt /
+ * moe_unpack_experts_fmt: the device layout of moe_prepack_experts plus the
+ * zero points in the scales' order (one byte each) after the scales.  The
+ * expert kernels read such blobs when MOE_W4_ZERO_POINT is OR'd into the
+ * regime.  MOE_EINVAL for an unknown fmt, else as the symmetric calls.
+ */
+int moe_blob_layout_fmt(int H, int I, int group, int fmt, int64_t offsets[9],
+                        int64_t *total_bytes);
+int moe_quantize_experts_fmt(const float *wg, const float *wu, const float *wd, int n, int H,
+                             int I, int group, int fmt, void *blobs, hipStream_t stream);
+int moe_prepack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
+                            hipStream_t stream);
+int moe_unpack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
+                           hipStream_t stream);
 
 /* ------------------------------------------------------------ router */
 /*
@@ -232,7 +264,8 @@ int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,
  *            T > 32 is MOE_EUNSUPPORTED.  y is fp16 [1][T*k][H].
  *   BATCHED: tiled grouped GEMM, any T.  y is fp16 [1][T*k][H].
  * regime may carry MOE_Y_TOKEN_ORDER (DECODE only: MOE_EUNSUPPORTED when the
- * resolved regime is another); resolved_regime is returned without it.
+ * resolved regime is another) and MOE_W4_ZERO_POINT (any regime: the blobs
+ * are MOE_FMT_ZP); resolved_regime is returned without them.
  */
 int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
                         int *resolved_regime, int *y_dtype, int *y_slices,

@@ -10,7 +10,9 @@ __all__ = [
     "MoEError", "lib", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOMEM", "MOE_EHIP",
     "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
     "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_DTYPE_F16",
-    "MOE_DTYPE_F32", "EXPORTS",
+    "MOE_DTYPE_F32", "MOE_FMT_SYM", "MOE_FMT_ZP", "MOE_W4_ZERO_POINT", "EXPORTS",
+    "moe_blob_layout_fmt", "moe_quantize_experts_fmt", "moe_prepack_experts_fmt",
+    "moe_unpack_experts_fmt",
     "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts",
     "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
@@ -29,9 +31,13 @@ MOE_RENORM = 1
 MOE_REGIME_AUTO, MOE_REGIME_DECODE, MOE_REGIME_BATCHED, MOE_REGIME_SMALL = 0, 1, 2, 3
 MOE_Y_TOKEN_ORDER = 0x100   # OR'd into a regime: decode y rows in token order
 MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
+MOE_FMT_SYM, MOE_FMT_ZP = 0, 1   # expert blob formats (zero point per group)
+MOE_W4_ZERO_POINT = 0x200        # OR'd into a regime: the blobs are MOE_FMT_ZP
 
 # every symbol include/moe_w4a16.h declares
 EXPORTS = [
+    "moe_blob_layout_fmt", "moe_quantize_experts_fmt", "moe_prepack_experts_fmt",
+    "moe_unpack_experts_fmt",
     "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
@@ -87,6 +93,10 @@ def _declare(L):
         "moe_last_error": (C.c_char_p, []),
         "moe_workspace_clear": (i32, [vp, sz, vp]),
         "moe_blob_layout": (i32, [i32, i32, i32, vp, vp]),
+        "moe_blob_layout_fmt": (i32, [i32, i32, i32, i32, vp, vp]),
+        "moe_quantize_experts_fmt": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+        "moe_prepack_experts_fmt": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
+        "moe_unpack_experts_fmt": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
         "moe_quantize_experts": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_prepack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
         "moe_unpack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
@@ -184,6 +194,26 @@ def moe_blob_layout(H, I, group):
     tot = C.c_int64()
     _check(lib().moe_blob_layout(H, I, group, off, C.byref(tot)))
     return list(off), tot.value
+
+
+def moe_blob_layout_fmt(H, I, group, fmt):
+    off = (C.c_int64 * 9)()
+    tot = C.c_int64()
+    _check(lib().moe_blob_layout_fmt(H, I, group, fmt, off, C.byref(tot)))
+    return list(off), tot.value
+
+
+def moe_quantize_experts_fmt(wg, wu, wd, n, H, I, group, fmt, blobs, stream=None):
+    _check(lib().moe_quantize_experts_fmt(_p(wg), _p(wu), _p(wd), n, H, I, group, fmt,
+                                          _p(blobs), _s(stream)))
+
+
+def moe_prepack_experts_fmt(src, n, H, I, group, fmt, dst, stream=None):
+    _check(lib().moe_prepack_experts_fmt(_p(src), n, H, I, group, fmt, _p(dst), _s(stream)))
+
+
+def moe_unpack_experts_fmt(src, n, H, I, group, fmt, dst, stream=None):
+    _check(lib().moe_unpack_experts_fmt(_p(src), n, H, I, group, fmt, _p(dst), _s(stream)))
 
 
 def moe_quantize_experts(wg, wu, wd, n, H, I, group, blobs, stream=None):

@@ -45,7 +45,13 @@ __device__ __forceinline__ float dot_unpacked(const half2_t (&m)[16], const half
 
 // Prepares one 32-element chunk of activations (already in registers):
 // pairs with odd index divided by 16, and the chunk's correction constant.
-__device__ __forceinline__ void prep_chunk_regs(const half8_t (&xv)[4], half2_t *dst, float *corr)
+// Symmetric codes (z = 8): corr = -1032 * (low-field sum) - 72 * (high-field
+// sum).  With a zero point z per group the constant is corr - z * sum, so the
+// zero-point format keeps corr = -1024 * low - 64 * high and the plain sum
+// (*sum) for the per-row term.
+template <bool ZP = false>
+__device__ __forceinline__ void prep_chunk_regs(const half8_t (&xv)[4], half2_t *dst, float *corr,
+                                                float *sum = nullptr)
 {
     float slo = 0.0f, shi = 0.0f;
 #pragma unroll
@@ -63,17 +69,24 @@ __device__ __forceinline__ void prep_chunk_regs(const half8_t (&xv)[4], half2_t 
             }
         }
     }
-    *corr = -1032.0f * slo - 72.0f * shi;
+    if constexpr (ZP) {
+        *corr = -1024.0f * slo - 64.0f * shi;
+        *sum = slo + shi;
+    } else {
+        *corr = -1032.0f * slo - 72.0f * shi;
+    }
 }
 
 // The same, loading the chunk from memory first.
-__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr)
+template <bool ZP = false>
+__device__ __forceinline__ void prep_chunk(const f16 *src, half2_t *dst, float *corr,
+                                           float *sum = nullptr)
 {
     half8_t xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         xv[q] = *reinterpret_cast<const half8_t *>(src + 8 * q);
-    prep_chunk_regs(xv, dst, corr);
+    prep_chunk_regs<ZP>(xv, dst, corr, sum);
 }
 
 }  // namespace moe

@@ -85,12 +85,16 @@ constexpr int DECODE_RG = 4;     // routed rows computed together from one weigh
 // stream.  Scales and activations go first (small).  Every weight address is
 // in the global address space (a flat load would also count against the LDS
 // counter and force a full drain at every LDS wait); no load is conditional.
-template <int H, int G, int NW, int PD>
+// ZP: zero-point blobs (W = (u - z) s, z one byte per row and group in the
+// scales' order); the correction constant of a chunk becomes per row:
+// corr - z * sum (k_decode_frag.h).
+template <int H, int G, int NW, int PD, bool ZP>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
     const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk, int tok_order,
-    int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, float *__restrict__ y)
+    int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, int64_t off_guz,
+    int64_t off_dz, float *__restrict__ y)
 {
     constexpr int NK = H / 32;                 // input chunks of gate/up rows
     constexpr int CPW = NK / NW;               // gate/up chunks per wave
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
     __shared__ __align__(16) half2_t xp[DECODE_XPRE][H / 2];   // prepared activations
     __shared__ float xc[DECODE_XPRE][NK];                     // their chunk constants
+    __shared__ float xsum[ZP ? DECODE_XPRE : 1][ZP ? NK : 1];  // ZP: their chunk sums
     __shared__ float red[NW][RG][64];
     __shared__ __align__(16) half2_t hp[RG][16];              // prepared h chunks
     __shared__ int s_tok[RG];
@@ -119,6 +124,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     // flight, not after it (a late kernel-argument load would be waited for
     // at the first LDS wait)
     asm volatile("" ::"s"(off_guq), "s"(off_dq), "s"(off_gus), "s"(off_ds));
+    if constexpr (ZP)
+        asm volatile("" ::"s"(off_guz), "s"(off_dz));
 
     // activations of the whole (small) batch, each wave only the chunks it
     // multiplies: lane -> (token, chunk of the wave).  The loads go out now
@@ -167,6 +174,18 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 #pragma unroll
     for (int r = 0; r < RBW; ++r)
         sd[r] = ldg_nt(dsc + ((size_t)(wave * RBW + r) * IG + (slice * 32) / G) * 64 + lane);
+    // zero points, in the scales' order (one byte each)
+    uint8_t zgu[ZP ? NSG : 1], zd[ZP ? RBW : 1];
+    if constexpr (ZP) {
+        const uint8_t *guz = blob + off_guz + (size_t)slice * HG * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < NSG; ++j)
+            zgu[j] = ldg_nt(guz + (size_t)(((wave * CPW + j * CPG) * 32) / G) * 64);
+        const uint8_t *dz = blob + off_dz;
+#pragma unroll
+        for (int r = 0; r < RBW; ++r)
+            zd[r] = ldg_nt(dz + ((size_t)(wave * RBW + r) * IG + (slice * 32) / G) * 64 + lane);
+    }
 
     // weight chunks of this wave: gate/up chunks 0..CPW-1 (one 1 KB run of the
     // fused 64-row block each), then its down blocks (the slice's 16-byte
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     for (int q = 0; q < 4; ++q)
         asm volatile("" : "+v"(xr[q]));
     if (xmine)
-        prep_chunk_regs(xr, &xp[xt][xcn * 16], &xc[xt][xcn]);
+        prep_chunk_regs<ZP>(xr, &xp[xt][xcn * 16], &xc[xt][xcn], &xsum[ZP ? xt : 0][ZP ? xcn : 0]);
 
     // One group of R routed rows (R a constant, so that no register is held
     // for absent rows).  FIRST: the weights are still streaming in and the
@@ -207,7 +226,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
             __syncthreads();
             for (int i = threadIdx.x; i < R * NK; i += NW * 64) {
                 const int r = i / NK, c = i % NK;
-                prep_chunk(x + (size_t)s_tok[r] * H + c * 32, &xp[r][c * 16], &xc[r][c]);
+                prep_chunk<ZP>(x + (size_t)s_tok[r] * H + c * 32, &xp[r][c * 16], &xc[r][c],
+                               &xsum[ZP ? r : 0][ZP ? c : 0]);
             }
             lds_barrier();
         } else {
@@ -240,8 +260,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
             const int c = wave * CPW + i;
             const float s = h2f(sgu[CPW >= CPG ? i / CPG : 0]);
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                acc[r] = fmaf(dot_unpacked(m, &xp[slot[r]][c * 16], xc[slot[r]][c]), s, acc[r]);
+            for (int r = 0; r < R; ++r) {
+                float c0 = xc[slot[r]][c];
+                if constexpr (ZP)
+                    c0 = fmaf(-(float)zgu[CPW >= CPG ? i / CPG : 0], xsum[slot[r]][c], c0);
+                acc[r] = fmaf(dot_unpacked(m, &xp[slot[r]][c * 16], c0), s, acc[r]);
+            }
         }
         if constexpr (FIRST) {
 #pragma unroll
@@ -283,15 +307,28 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
         lds_barrier();
 
         // each row's correction constant (see k_decode_frag.h): -1032 per
-        // low-field h, -72 per high-field h = -1152 per prepared (h/16) value
-        float hc[R];
+        // low-field h, -72 per high-field h = -1152 per prepared (h/16) value.
+        // ZP: -1024 per low-field h, -64 per high-field h (-1024 per prepared
+        // value), and the plain sum of h for the per-row -z * sum term
+        float hc[R], hs[ZP ? R : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             hc[r] = 0.0f;
+            if constexpr (ZP) {
+                hs[r] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                hc[r] = dot2(hp[r][j], (j & 1) ? half2_t{(f16)-1152.0f, (f16)-1152.0f}
-                                               : half2_t{(f16)-1032.0f, (f16)-1032.0f}, hc[r]);
+                for (int j = 0; j < 16; ++j) {
+                    hc[r] = dot2(hp[r][j], half2_t{(f16)-1024.0f, (f16)-1024.0f}, hc[r]);
+                    hs[r] = dot2(hp[r][j], (j & 1) ? half2_t{(f16)16.0f, (f16)16.0f}
+                                                   : half2_t{(f16)1.0f, (f16)1.0f}, hs[r]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    hc[r] = dot2(hp[r][j], (j & 1) ? half2_t{(f16)-1152.0f, (f16)-1152.0f}
+                                                   : half2_t{(f16)-1032.0f, (f16)-1032.0f},
+                                 hc[r]);
+            }
         }
 
         // down strip: lane = output row, the 32 prepared h values from LDS
@@ -319,9 +356,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
                 unpack_chunk(w[CPW + j], mj);
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r) {
+                float c0 = hc[r];
+                if constexpr (ZP)
+                    c0 = fmaf(-(float)zd[j], hs[r], c0);
                 y[((size_t)slice * ntk + yrow[r]) * H + rb * 64 + lane] =
-                        dot_unpacked(PRE ? md[j] : mj, hp[r], hc[r]) * s;
+                        dot_unpacked(PRE ? md[j] : mj, hp[r], c0) * s;
+            }
         }
     };
 
@@ -344,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
 constexpr int DECODE_PD = 4;   // weight chunks each wave keeps in flight
 
-template <int H>
+template <int H, bool ZP>
 static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
                            const int32_t *offsets, const uint8_t *const *blobs,
                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
@@ -352,9 +393,9 @@ static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
 #define MOE_DECODE_LAUNCH(G)                                                                  \
-    hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD>), grid, dim3(NW * 64), 0, s, x, \
-                       perm, offsets, blobs, skip, I, E, k, ntk, tok_order ? 1 : 0, L.gu_q, L.d_q,  \
-                       L.gu_s, L.d_s, y)
+    hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD, ZP>), grid, dim3(NW * 64), 0, s, \
+                       x, perm, offsets, blobs, skip, I, E, k, ntk, tok_order ? 1 : 0, L.gu_q,    \
+                       L.d_q, L.gu_s, L.d_s, L.gu_z, L.d_z, y)
     switch (g) {
     case 32: MOE_DECODE_LAUNCH(32); break;
     case 64: MOE_DECODE_LAUNCH(64); break;
@@ -370,24 +411,31 @@ static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t
 // null entry in `blobs` are not computed either.
 int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
                       const void *const *blobs, const void *const *skip, int T, int H, int I,
-                      int E, int k, int g, bool tok_order, float *y, hipStream_t s)
+                      int E, int k, int g, int fmt, bool tok_order, float *y, hipStream_t s)
 {
     const int ntk = T * k;
     if (ntk == 0)
         return MOE_OK;
-    const DevLayout L = dev_layout(H, I, g);
+    const DevLayout L = dev_layout(H, I, g, fmt);
     dim3 grid(I / 32, (unsigned)min(E, ntk));
     const f16 *xh = static_cast<const f16 *>(x);
     const uint8_t *const *b = reinterpret_cast<const uint8_t *const *>(blobs);
     const uint8_t *const *sk = reinterpret_cast<const uint8_t *const *>(skip);
     int rc;
+#define MOE_DECODE_H(HH)                                                                       \
+    rc = fmt == FMT_ZP                                                                         \
+             ? launch_decode_h<HH, true>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,    \
+                                         tok_order, L, y)                                      \
+             : launch_decode_h<HH, false>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,   \
+                                          tok_order, L, y)
     switch (H) {
-    case 256: rc = launch_decode_h<256>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
-    case 512: rc = launch_decode_h<512>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
-    case 1024: rc = launch_decode_h<1024>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
-    case 2048: rc = launch_decode_h<2048>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, tok_order, L, y); break;
+    case 256: MOE_DECODE_H(256); break;
+    case 512: MOE_DECODE_H(512); break;
+    case 1024: MOE_DECODE_H(1024); break;
+    case 2048: MOE_DECODE_H(2048); break;
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
+#undef MOE_DECODE_H
     if (rc != MOE_OK)
         return rc;
     MOE_LAUNCH_CHECK("ffn_decode_kernel");

@@ -43,6 +43,7 @@ struct GemmArgs {
     const int32_t *offsets;      // W4 modes: [E+1]; null for the shared expert
     const uint8_t *const *blobs; // W4 modes
     int64_t off_q, off_s;        // W4: section offsets inside a blob
+    int64_t off_z;               // W4, zero-point format: zero points (scales' order, u8)
     const _Float16 *W0, *W1;     // F16 modes: gate/up or down (row-major)
     int k;                       // top-k (token = perm[p] / k)
     int E;                       // experts (1 for the shared expert)
@@ -90,16 +91,17 @@ constexpr int W4_NS = 4;     // pipeline stages
 constexpr int W4_WAVES = 8;  // waves per workgroup
 constexpr int W4_T = W4_WAVES * 64;
 
-template <int MF>
+template <int MF, bool ZP = false>
 struct W4Stage {
     static constexpr int A = 32 * MF * 128;          // activation tile
     static constexpr int B = W4_WAVES * 2 * 1024;    // per wave: 2 chunk runs
     static constexpr int S = W4_WAVES * 256;         // per wave: [2 chunks][64 rows] fp16
-    static constexpr int BYTES = A + B + S;
+    static constexpr int Z = ZP ? W4_WAVES * 128 : 0;   // per wave: [2 chunks][64 rows] u8
+    static constexpr int BYTES = A + B + S + Z;
 };
 
-template <int MF>
-constexpr size_t w4_lds_bytes() { return (size_t)W4_NS * W4Stage<MF>::BYTES; }
+template <int MF, bool ZP = false>
+constexpr size_t w4_lds_bytes() { return (size_t)W4_NS * W4Stage<MF, ZP>::BYTES; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -466,14 +468,17 @@ struct W4Item {
 };
 constexpr int W4_MAXI = 16;   // items listed per batch
 
-template <int MF>
+template <int MF, bool ZP = false>
 constexpr size_t w4_lds_total()
 {
-    return w4_lds_bytes<MF>() + (size_t)W4_MAXI * sizeof(W4Item) +
+    return w4_lds_bytes<MF, ZP>() + (size_t)W4_MAXI * sizeof(W4Item) +
            (size_t)W4_MAXI * 32 * MF * sizeof(int);
 }
 
-template <int MODE, int MF>
+// ZP: zero-point blobs; one more direct-to-LDS load per step and wave (4 bytes
+// on lanes 0-31) brings the two chunks' zero points (64 rows x u8 each), and
+// the weights are converted to fp16((u - z) s).
+template <int MODE, int MF, bool ZP>
 __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
 {
     static_assert(MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4, "INT4 modes only");
@@ -481,8 +486,8 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
     constexpr int BM = 32 * MF;
     constexpr int RPW = BM / W4_WAVES;        // activation rows loaded per wave (4*MF)
     constexpr int NA = (RPW + 7) / 8;         // their 64-lane loads (lanes 8 per row)
-    constexpr int PER = NA + 3;               // direct-to-LDS loads per step and wave
-    using St = W4Stage<MF>;
+    constexpr int PER = NA + 3 + (ZP ? 1 : 0);   // direct-to-LDS loads per step and wave
+    using St = W4Stage<MF, ZP>;
 
     extern __shared__ __align__(16) unsigned char smem[];
     W4Item *items = reinterpret_cast<W4Item *>(smem + (size_t)W4_NS * St::BYTES);   // [MAXI]
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
         // to the next item): this lane's activation rows, weight chunk runs
         // and scale rows
         const _Float16 *asrc[NA];
-        uint64_t qbase = 0, sbase = 0;   // wave-uniform (scalar registers)
+        uint64_t qbase = 0, sbase = 0, zbase = 0;   // wave-uniform (scalar registers)
         auto item_sources = [&]() {
 #pragma unroll
             for (int i = 0; i < NA; ++i) {
@@ -617,6 +622,8 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
             const int bb = min(nt * W4_WAVES + wave, a.nblk - 1);
             qbase = ub + a.off_q + (uint64_t)bb * (K / 32) * 64 * 16;
             sbase = ub + a.off_s + (uint64_t)bb * (K >> gshift) * 64 * 2;
+            if constexpr (ZP)
+                zbase = ub + a.off_z + (uint64_t)bb * (K >> gshift) * 64;
         };
         item_sources();
         auto issue_next = [&]() {
@@ -633,6 +640,15 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
             const int grp = ((2 * ikt + half) * 32) >> gshift;
             dma4(reinterpret_cast<const uint8_t *>(sbase) + (size_t)grp * 128 + col * 4,
                  st + St::A + St::B + wave * 256);
+            if constexpr (ZP) {
+                // the same rows' zero points: lanes 0-15 rows 4l..4l+3 of
+                // chunk 2kt, lanes 16-31 those of chunk 2kt+1 (4 bytes each)
+                const int zg = ((2 * ikt + (lane >> 4)) * 32) >> gshift;
+                if (lane < 32)
+                    dma4(reinterpret_cast<const uint8_t *>(zbase) + (size_t)zg * 64 +
+                             (lane & 15) * 4,
+                         st + St::A + St::B + St::S + wave * 128);
+            }
             if (++ikt == nk) {
                 ikt = 0;
                 if (++iq < nb)
@@ -644,6 +660,7 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
         struct StepW {
             uint2_t q[2][2];
             f16 s[2][2];
+            uint8_t z[ZP ? 2 : 1][2];
         };
         auto read_w = [&](int g, StepW &w) {
             const unsigned char *st = smem + (size_t)(g % W4_NS) * St::BYTES;
@@ -656,6 +673,8 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
                     w.q[n][c] = *reinterpret_cast<const uint2_t *>(bq + c * 1024 +
                                                                    (n * 32 + col) * 16 + half * 8);
                     w.s[n][c] = *reinterpret_cast<const f16 *>(sq + c * 128 + (n * 32 + col) * 2);
+                    if constexpr (ZP)
+                        w.z[n][c] = *(st + St::A + St::B + St::S + wave * 128 + c * 64 + n * 32 + col);
                 }
         };
         auto fetch = [&](int g, int s, const StepW &w, half8_t *a_, half8_t *b_) {
@@ -668,7 +687,13 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
             for (int n = 0; n < 2; ++n) {
                 const uint2_t q = w.q[n][s >> 1];
                 const f16 c = w.s[n][s >> 1];
-                b_[n] = dequant8((s & 1) ? q.y : q.x, half2_t{c, c}, magic);
+                if constexpr (ZP) {
+                    half2_t klo, khi;
+                    zp_offsets(w.z[n][s >> 1], klo, khi);
+                    b_[n] = dequant8_zp((s & 1) ? q.y : q.x, half2_t{c, c}, magic, klo, khi);
+                } else {
+                    b_[n] = dequant8((s & 1) ? q.y : q.x, half2_t{c, c}, magic);
+                }
             }
         };
 
@@ -832,14 +857,14 @@ static int launch_fg(hipStream_t s, const GemmArgs &a)
     return MOE_OK;
 }
 
-template <int MODE, int MF>
+template <int MODE, int MF, bool ZP>
 static int launch_w4(hipStream_t s, const GemmArgs &a)
 {
-    constexpr size_t lds = w4_lds_total<MF>();
-    static_assert(w4_lds_total<MF>() <= 160 * 1024, "LDS of one workgroup");
+    constexpr size_t lds = w4_lds_total<MF, ZP>();
+    static_assert(w4_lds_total<MF, ZP>() <= 160 * 1024, "LDS of one workgroup");
     static bool attr_set = false;   // raising the LDS limit is idempotent
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void *)w4_gemm_kernel<MODE, MF>,
+        hipError_t err = hipFuncSetAttribute((const void *)w4_gemm_kernel<MODE, MF, ZP>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess)
             return set_error(MOE_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
@@ -849,18 +874,15 @@ static int launch_w4(hipStream_t s, const GemmArgs &a)
     const int64_t items = tile_bound(a.rows, a.E, 32 * MF) * ((a.nblk + W4_WAVES - 1) / W4_WAVES);
     int64_t grid = std::min<int64_t>(items, num_cus());
     grid = std::max<int64_t>(NXCD, (grid + NXCD - 1) / NXCD * NXCD);
-    hipLaunchKernelGGL((w4_gemm_kernel<MODE, MF>), dim3((unsigned)grid), dim3(W4_T), lds, s, a);
+    hipLaunchKernelGGL((w4_gemm_kernel<MODE, MF, ZP>), dim3((unsigned)grid), dim3(W4_T), lds, s,
+                       a);
     MOE_LAUNCH_CHECK("w4_gemm_kernel");
     return MOE_OK;
 }
 
 constexpr int SPLITK_MAX_ROWS = 1024;   // shared expert: split-K kernel up to this many tokens
-#ifndef SPLITK_TARGET_WGS
-#define SPLITK_TARGET_WGS 256
-#endif
-#ifndef SPLITK_MAX_KSW
-#define SPLITK_MAX_KSW 8
-#endif
+constexpr int SPLITK_TARGET_WGS = 256;   // split-K: workgroups aimed for
+constexpr int SPLITK_MAX_KSW = 8;        // split-K: most K parts per output tile
 // arrival counters at the front of the workspace: one per output tile of a
 // launch with K parts, which has fewer than SPLITK_TARGET_WGS tiles
 constexpr int SPLITK_CTR_BYTES = SPLITK_TARGET_WGS * 4 > 2048 ? SPLITK_TARGET_WGS * 4 : 2048;
@@ -899,7 +921,7 @@ static size_t splitk_part_bytes(int rows, int K, int nblk)
     return ksw > 1 ? (size_t)((rows + 31) / 32) * nblk * ksw * 2048 * sizeof(float) : 0;
 }
 
-template <int MODE>
+template <int MODE, bool ZP = false>
 static int launch_mode(hipStream_t s, const GemmArgs &a)
 {
     if constexpr (MODE == GM_GATEUP_F16 || MODE == GM_DOWN_F16) {
@@ -916,9 +938,9 @@ static int launch_mode(hipStream_t s, const GemmArgs &a)
     }
     if constexpr (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
         switch (pick_mf(a.rows, a.E, a.nblk)) {
-        case 4: return launch_w4<MODE, 4>(s, a);
-        case 2: return launch_w4<MODE, 2>(s, a);
-        default: return launch_w4<MODE, 1>(s, a);
+        case 4: return launch_w4<MODE, 4, ZP>(s, a);
+        case 2: return launch_w4<MODE, 2, ZP>(s, a);
+        default: return launch_w4<MODE, 1, ZP>(s, a);
         }
     } else {
         if (a.nblk % 2 || a.K % FG_BK)
@@ -937,12 +959,13 @@ size_t ffn_batched_ws_bytes(int T, int I, int k)
 
 int launch_ffn_batched(const void *x, const int32_t *perm, const int32_t *offsets,
                        const void *const *blobs, int T, int H, int I, int E, int k, int g,
-                       void *y, void *ws, hipStream_t s)
+                       int fmt, void *y, void *ws, hipStream_t s)
 {
     const int rows = T * k;
     if (rows == 0)
         return MOE_OK;
-    const DevLayout L = dev_layout(H, I, g);
+    const bool zp = fmt == FMT_ZP;
+    const DevLayout L = dev_layout(H, I, g, fmt);
     _Float16 *h = static_cast<_Float16 *>(ws);
     GemmArgs a{};
     a.perm = perm;
@@ -956,22 +979,24 @@ int launch_ffn_batched(const void *x, const int32_t *perm, const int32_t *offset
     a.A = static_cast<const _Float16 *>(x);
     a.off_q = L.gu_q;
     a.off_s = L.gu_s;
+    a.off_z = L.gu_z;
     a.K = H;
     a.nblk = I / 32;
     a.ldo = I;
     a.out = h;
-    int rc = launch_mode<GM_GATEUP_W4>(s, a);
+    int rc = zp ? launch_mode<GM_GATEUP_W4, true>(s, a) : launch_mode<GM_GATEUP_W4>(s, a);
     if (rc)
         return rc;
     // down: H/64 blocks, K = I, out y [rows][H] fp16
     a.A = h;
     a.off_q = L.d_q;
     a.off_s = L.d_s;
+    a.off_z = L.d_z;
     a.K = I;
     a.nblk = H / 64;
     a.ldo = H;
     a.out = y;
-    return launch_mode<GM_DOWN_W4>(s, a);
+    return zp ? launch_mode<GM_DOWN_W4, true>(s, a) : launch_mode<GM_DOWN_W4>(s, a);
 }
 
 // Workspace of the shared expert: [arrival counters, 2 KB, zero between

@@ -56,6 +56,7 @@ struct SmallArgs {
     const int32_t *offsets;        // [E+1] sorted-row ranges per expert
     const uint8_t *const *blobs;   // [E] device blobs (null: expert not computed)
     int64_t off_q, off_s;          // weight / scale sections inside a blob
+    int64_t off_z;                 // zero points (zero-point format; scales' order, u8)
     int k, E, K, nblk, g, ldo, rmax;
     int phases;                    // the rows are staged in this many parts of K
     _Float16 *out;                 // h [T*k][I] or y [T*k][H]
@@ -76,7 +77,7 @@ static size_t sb_lds_bytes(int rmax, int K, int P)
     return std::max(xs, red);
 }
 
-template <int MODE, int KS>
+template <int MODE, int KS, bool ZP>
 __global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs a)
 {
     constexpr bool GATEUP = MODE == SB_GATEUP;
@@ -173,8 +174,11 @@ __global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs
     const uint8_t *qb = blob + a.off_q + (size_t)bb * NKc * 1024 + col * 16 + half * 8;
     const uint8_t *sb = blob + a.off_s + (size_t)bb * (K >> gshift) * 128 + col * 2;
 
+    const uint8_t *zb = blob + a.off_z + (size_t)bb * (K >> gshift) * 64 + col;
+
     uint2_t wq[SB_D][2];    // [ring][tile]: rows col and 32 + col of the chunk
     uint16_t sc[SB_D][2];   // their group scales
+    uint8_t zc[ZP ? SB_D : 1][2];   // ZP: their zero points
     auto load = [&](int i, int c) {   // c: absolute chunk of the block
         const uint8_t *q = qb + (size_t)c * 1024;
         // expert weights are streamed once per call: non-temporal
@@ -183,6 +187,11 @@ __global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs
         const uint8_t *sp = sb + (size_t)((c * 32) >> gshift) * 128;
         sc[i][0] = ldg_nt(reinterpret_cast<const uint16_t *>(sp));
         sc[i][1] = ldg_nt(reinterpret_cast<const uint16_t *>(sp + 64));
+        if constexpr (ZP) {
+            const uint8_t *zp = zb + (size_t)((c * 32) >> gshift) * 64;
+            zc[i][0] = ldg_nt(zp);
+            zc[i][1] = ldg_nt(zp + 32);
+        }
     };
     // absolute chunk of this wave's f-th chunk in phase ph
     auto chunk_of = [&](int ph, int f) { return ph * (NKc / P) + ks * nckp + f; };
@@ -241,11 +250,22 @@ __global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs
     auto compute = [&](int i, int f) {   // f: chunk within this wave's share of the part
         const f16 s0 = __builtin_bit_cast(f16, sc[i][0]);
         const f16 s1 = __builtin_bit_cast(f16, sc[i][1]);
+        half2_t klo0, khi0, klo1, khi1;
+        if constexpr (ZP) {
+            zp_offsets(zc[i][0], klo0, khi0);
+            zp_offsets(zc[i][1], klo1, khi1);
+        }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             const half8_t av = *reinterpret_cast<const half8_t *>(xa + f * 32 + kh * 16);
-            const half8_t b0 = dequant8(kh ? wq[i][0].y : wq[i][0].x, half2_t{s0, s0}, magic);
-            const half8_t b1 = dequant8(kh ? wq[i][1].y : wq[i][1].x, half2_t{s1, s1}, magic);
+            half8_t b0, b1;
+            if constexpr (ZP) {
+                b0 = dequant8_zp(kh ? wq[i][0].y : wq[i][0].x, half2_t{s0, s0}, magic, klo0, khi0);
+                b1 = dequant8_zp(kh ? wq[i][1].y : wq[i][1].x, half2_t{s1, s1}, magic, klo1, khi1);
+            } else {
+                b0 = dequant8(kh ? wq[i][0].y : wq[i][0].x, half2_t{s0, s0}, magic);
+                b1 = dequant8(kh ? wq[i][1].y : wq[i][1].x, half2_t{s1, s1}, magic);
+            }
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, av, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, av, acc[1], 0, 0, 0);
         }
@@ -341,7 +361,7 @@ static int sb_num_cus()
     return n;
 }
 
-template <int MODE, int KS>
+template <int MODE, int KS, bool ZP>
 static int launch_small_ks(hipStream_t s, const SmallArgs &a, int active_max)
 {
     const size_t lds = sb_lds_bytes<KS>(a.rmax, a.K, a.phases);
@@ -349,7 +369,7 @@ static int launch_small_ks(hipStream_t s, const SmallArgs &a, int active_max)
         return set_error(MOE_EUNSUPPORTED, "small-batch kernel: %zu bytes of LDS", lds);
     static size_t attr = 0;   // dynamic LDS limit raised so far (idempotent, only grows)
     if (lds > attr) {
-        hipError_t err = hipFuncSetAttribute((const void *)w4_small_kernel<MODE, KS>,
+        hipError_t err = hipFuncSetAttribute((const void *)w4_small_kernel<MODE, KS, ZP>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess)
             return set_error(MOE_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
@@ -357,7 +377,7 @@ static int launch_small_ks(hipStream_t s, const SmallArgs &a, int active_max)
     }
     constexpr int BPW = SB_WAVES / KS;
     dim3 grid((unsigned)((a.nblk + BPW - 1) / BPW), (unsigned)active_max);
-    hipLaunchKernelGGL((w4_small_kernel<MODE, KS>), grid, dim3(SB_T), lds, s, a);
+    hipLaunchKernelGGL((w4_small_kernel<MODE, KS, ZP>), grid, dim3(SB_T), lds, s, a);
     MOE_LAUNCH_CHECK("w4_small_kernel");
     return MOE_OK;
 }
@@ -397,22 +417,23 @@ static int pick_phases(int rmax, int K, int ks)
     return best;
 }
 
-template <int MODE, int KS>
+template <int MODE, int KS, bool ZP>
 static int launch_small_at_most(hipStream_t s, const SmallArgs &a, int active_max, int ks)
 {
     if constexpr (KS > 1) {
         if (ks < KS)
-            return launch_small_at_most<MODE, KS / 2>(s, a, active_max, ks);
+            return launch_small_at_most<MODE, KS / 2, ZP>(s, a, active_max, ks);
     }
-    return launch_small_ks<MODE, KS>(s, a, active_max);
+    return launch_small_ks<MODE, KS, ZP>(s, a, active_max);
 }
 
 template <int MODE>
-static int launch_small(hipStream_t s, SmallArgs a, int active_max, double active)
+static int launch_small(hipStream_t s, SmallArgs a, int active_max, double active, bool zp)
 {
     const int ks = pick_ks(active, a.nblk, a.K / 32);
     a.phases = pick_phases(a.rmax, a.K, ks);
-    return launch_small_at_most<MODE, SB_WAVES>(s, a, active_max, ks);
+    return zp ? launch_small_at_most<MODE, SB_WAVES, true>(s, a, active_max, ks)
+              : launch_small_at_most<MODE, SB_WAVES, false>(s, a, active_max, ks);
 }
 
 // The staged rows always fit once split along K (32 rows of at most 8192/8
@@ -427,15 +448,16 @@ bool ffn_small_fits(int T, int H, int I)
 // Gate/up then down for T <= 32 tokens; h lives in ws (the batched regime's
 // workspace), y is [T*k][H] fp16.
 int launch_ffn_small(const void *x, const int32_t *perm, const int32_t *offsets,
-                     const void *const *blobs, int T, int H, int I, int E, int k, int g, void *y,
-                     void *ws, hipStream_t s)
+                     const void *const *blobs, int T, int H, int I, int E, int k, int g, int fmt,
+                     void *y, void *ws, hipStream_t s)
 {
     const int rows = T * k;
     if (rows == 0)
         return MOE_OK;
     if (!ffn_small_fits(T, H, I))
         return set_error(MOE_EUNSUPPORTED, "small-batch kernel: T=%d with H=%d, I=%d", T, H, I);
-    const DevLayout L = dev_layout(H, I, g);
+    const DevLayout L = dev_layout(H, I, g, fmt);
+    const bool zp = fmt == FMT_ZP;
     const int active_max = std::min(E, rows);
     const double active = E * (1.0 - std::pow(1.0 - (double)k / E, (double)T));
     SmallArgs a{};
@@ -450,22 +472,24 @@ int launch_ffn_small(const void *x, const int32_t *perm, const int32_t *offsets,
     a.A = static_cast<const _Float16 *>(x);
     a.off_q = L.gu_q;
     a.off_s = L.gu_s;
+    a.off_z = L.gu_z;
     a.K = H;
     a.nblk = I / 32;
     a.ldo = I;
     a.out = static_cast<_Float16 *>(ws);
-    int rc = launch_small<SB_GATEUP>(s, a, active_max, active);
+    int rc = launch_small<SB_GATEUP>(s, a, active_max, active, zp);
     if (rc)
         return rc;
     // down: H/64 blocks, K = I, out y [rows][H]
     a.A = static_cast<const _Float16 *>(ws);
     a.off_q = L.d_q;
     a.off_s = L.d_s;
+    a.off_z = L.d_z;
     a.K = I;
     a.nblk = H / 64;
     a.ldo = H;
     a.out = static_cast<_Float16 *>(y);
-    return launch_small<SB_DOWN>(s, a, active_max, active);
+    return launch_small<SB_DOWN>(s, a, active_max, active, zp);
 }
 
 }  // namespace moe

@@ -3,10 +3,11 @@
 //
 // Horizon RunMap "08 / Comportamento do modelo": routed expert weights are
 // stored as INT4 with FP16 scales; lucashiago.com.br explainer, step 1: each
-// block of weights carries its scale.  Reading: symmetric groups of g along
-// the input dimension, s = fp16_rne(amax / 7) with amax / 7 in fp32,
-// q = clamp(rne(w / s), -7, 7) with w / s in fp32, q = 0 when s = 0; stored as
-// u = q + 8, element 2b in the low nibble of byte b.
+// block of weights carries its scale (and, in the zero-point format, its zero
+// point).  Reading: groups of g along the input dimension; symmetric:
+// s = fp16_rne(amax / 7) with amax / 7 in fp32, q = clamp(rne(w / s), -7, 7)
+// with w / s in fp32, q = 0 when s = 0, stored as u = q + 8; zero point: see
+// quantize_rows_kernel.  Element 2b in the low nibble of byte b.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -14,10 +15,15 @@
 namespace moe {
 
 // One thread per 32-element chunk of a row; a group of g spans g/32 adjacent
-// threads of one wave, which share the group maximum through lane shuffles.
+// threads of one wave, which share the group's extremes through lane
+// shuffles.  ZP: the zero-point format (reading: lo = min(min w, 0),
+// hi = max(max w, 0), s = fp16_rne((hi - lo) / 15), z = clamp(rne(-lo / s),
+// 0, 15), u = clamp(rne(w / s) + z, 0, 15); s = 0 gives z = u = 0; the
+// quotients in fp32); off_z receives one byte per group.
+template <bool ZP>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const float *__restrict__ w, int64_t w_stride, int rows, int K, int g,
-    uint8_t *__restrict__ blobs, int64_t blob_stride, int64_t off_q, int64_t off_s)
+    uint8_t *__restrict__ blobs, int64_t blob_stride, int64_t off_q, int64_t off_s, int64_t off_z)
 {
     const int n = blockIdx.y;
     const int nch = K / 32;
@@ -27,7 +33,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const int c = valid ? (int)(cid % nch) : 0;
     const float *src = w + n * w_stride + (int64_t)row * K + c * 32;
     float v[32];
-    float amax = 0.0f;
+    float amax = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float4_t f = valid ? *reinterpret_cast<const float4_t *>(src + 4 * i)
@@ -36,32 +42,44 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
         for (int m = 0; m < 4; ++m) {
             v[4 * i + m] = f[m];
             amax = fmaxf(amax, fabsf(f[m]));
+            lo = fminf(lo, f[m]);
+            hi = fmaxf(hi, f[m]);
         }
     }
     const int span = g / 32;   // 1, 2 or 4 threads per group
-    for (int st = 1; st < span; st <<= 1)
+    for (int st = 1; st < span; st <<= 1) {
         amax = fmaxf(amax, __shfl_xor(amax, st, 64));
+        lo = fminf(lo, __shfl_xor(lo, st, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, st, 64));
+    }
     if (!valid)
         return;
-    const f16 sh = (f16)(amax / 7.0f);
+    const f16 sh = ZP ? (f16)((hi - lo) / 15.0f) : (f16)(amax / 7.0f);
     const float sv = (float)sh;
+    int zi = 8;   // symmetric: u = q + 8
+    if (ZP)
+        zi = sv != 0.0f ? (int)fminf(fmaxf(rintf(-lo / sv), 0.0f), 15.0f) : 0;
     uint32_t words[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        int q = 0;
+        int u = 0;
         if (sv != 0.0f) {
-            float r = rintf(v[i] / sv);
-            r = fminf(fmaxf(r, -7.0f), 7.0f);
-            q = (int)r;
+            const float r = rintf(v[i] / sv);
+            u = ZP ? (int)fminf(fmaxf(r + (float)zi, 0.0f), 15.0f)
+                   : (int)fminf(fmaxf(r, -7.0f), 7.0f) + 8;
+        } else {
+            u = ZP ? 0 : 8;
         }
-        const uint32_t u = (uint32_t)(q + 8);
-        words[i >> 3] |= u << (4 * (i & 7));   // canonical: element i at bits 4i of the chunk
+        words[i >> 3] |= (uint32_t)u << (4 * (i & 7));   // canonical: element i at bits 4i
     }
     uint8_t *blob = blobs + n * blob_stride;
     *reinterpret_cast<uint4_t *>(blob + off_q + (int64_t)row * (K / 2) + c * 16) =
         uint4_t{words[0], words[1], words[2], words[3]};
-    if ((c * 32) % g == 0)
+    if ((c * 32) % g == 0) {
         reinterpret_cast<f16 *>(blob + off_s)[(int64_t)row * (K / g) + (c * 32) / g] = sh;
+        if (ZP)
+            blob[off_z + (int64_t)row * (K / g) + (c * 32) / g] = (uint8_t)zi;
+    }
 }
 
 __device__ __forceinline__ uint32_t canon_to_dev(uint32_t cw)
@@ -135,7 +153,7 @@ int launch_zero_bytes(void *p, size_t bytes, hipStream_t s)
 __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict__ src,
                                                       uint8_t *__restrict__ dst, int H, int I,
                                                       int g, int64_t stride, CanonLayout C,
-                                                      DevLayout D, int dir)
+                                                      DevLayout D, int dir, int zp)
 {
     const int n = blockIdx.y;
     const int NKH = H / 32, NKI = I / 32, HG = H / g, IG = I / g;
@@ -143,12 +161,14 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict_
     const int64_t ndq = (int64_t)(H / 64) * NKI * 64;
     const int64_t ngus = (int64_t)(I / 32) * HG * 64;
     const int64_t nds = (int64_t)(H / 64) * IG * 64;
+    const int64_t nsec = nguq + ndq + ngus + nds;
+    const int64_t ntot = nsec + (zp ? ngus + nds : 0);   // zero points: one byte per scale
     const uint8_t *s = src + n * stride;
     uint8_t *d = dst + n * stride;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nguq + ndq + ngus + nds;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ntot;
          i += (int64_t)gridDim.x * blockDim.x) {
         int64_t devoff, canoff;
-        int kind;   // 0 = 16-byte nibble chunk, 1 = 2-byte scale
+        int kind;   // 0 = 16-byte nibble chunk, 1 = 2-byte scale, 2 = 1-byte zero point
         if (i < nguq) {
             const int64_t b = i / (NKH * 64), c = (i / 64) % NKH, r = i % 64;
             const int64_t row = 32 * b + (r & 31);
@@ -161,18 +181,23 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict_
             devoff = D.d_q + j * 16;
             canoff = C.down_q + (64 * b + r) * (I / 2) + c * 16;
             kind = 0;
-        } else if (i < nguq + ndq + ngus) {
-            const int64_t j = i - nguq - ndq;
+        } else if (i < nguq + ndq + ngus || (i >= nsec && i < nsec + ngus)) {
+            const bool z = i >= nsec;
+            const int64_t j = z ? i - nsec : i - nguq - ndq;
             const int64_t b = j / (HG * 64), G = (j / 64) % HG, r = j % 64;
-            devoff = D.gu_s + j * 2;
-            canoff = (r < 32 ? C.gate_s : C.up_s) + ((32 * b + (r & 31)) * HG + G) * 2;
-            kind = 1;
+            const int64_t cr = (32 * b + (r & 31)) * HG + G;
+            devoff = z ? D.gu_z + j : D.gu_s + j * 2;
+            canoff = z ? (r < 32 ? C.gate_z : C.up_z) + cr
+                       : (r < 32 ? C.gate_s : C.up_s) + cr * 2;
+            kind = z ? 2 : 1;
         } else {
-            const int64_t j = i - nguq - ndq - ngus;
+            const bool z = i >= nsec;
+            const int64_t j = z ? i - nsec - ngus : i - nguq - ndq - ngus;
             const int64_t b = j / (IG * 64), G = (j / 64) % IG, r = j % 64;
-            devoff = D.d_s + j * 2;
-            canoff = C.down_s + ((64 * b + r) * IG + G) * 2;
-            kind = 1;
+            const int64_t cr = (64 * b + r) * IG + G;
+            devoff = z ? D.d_z + j : D.d_s + j * 2;
+            canoff = z ? C.down_z + cr : C.down_s + cr * 2;
+            kind = z ? 2 : 1;
         }
         if (kind == 0) {
             // dwords 1 and 2 trade places (the swap is its own inverse)
@@ -185,43 +210,52 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict_
                 o = uint4_t{dev_to_canon(v.x), dev_to_canon(v.z), dev_to_canon(v.y),
                             dev_to_canon(v.w)};
             *reinterpret_cast<uint4_t *>(d + (dir == 0 ? devoff : canoff)) = o;
-        } else {
+        } else if (kind == 1) {
             *reinterpret_cast<uint16_t *>(d + (dir == 0 ? devoff : canoff)) =
                 *reinterpret_cast<const uint16_t *>(s + (dir == 0 ? canoff : devoff));
+        } else {
+            d[dir == 0 ? devoff : canoff] = s[dir == 0 ? canoff : devoff];
         }
     }
 }
 
 int launch_quantize(const float *wg, const float *wu, const float *wd, int n, int H, int I, int g,
-                    void *blobs, hipStream_t s)
+                    int fmt, void *blobs, hipStream_t s)
 {
-    const CanonLayout C = canon_layout(H, I, g);
+    const CanonLayout C = canon_layout(H, I, g, fmt);
     uint8_t *b = static_cast<uint8_t *>(blobs);
     hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, s, (uint4_t *)b,
                        (int64_t)n * C.total / 16);
     MOE_LAUNCH_CHECK("zero_kernel");
-    struct P { const float *w; int rows, K; int64_t q, sc; } ps[3] = {
-        {wg, I, H, C.gate_q, C.gate_s}, {wu, I, H, C.up_q, C.up_s}, {wd, H, I, C.down_q, C.down_s}};
+    struct P { const float *w; int rows, K; int64_t q, sc, z; } ps[3] = {
+        {wg, I, H, C.gate_q, C.gate_s, C.gate_z}, {wu, I, H, C.up_q, C.up_s, C.up_z},
+        {wd, H, I, C.down_q, C.down_s, C.down_z}};
     for (const P &p : ps) {
         const int64_t chunks = (int64_t)p.rows * (p.K / 32);
         dim3 grid((unsigned)((chunks + 255) / 256), n);
-        hipLaunchKernelGGL(quantize_rows_kernel, grid, dim3(256), 0, s, p.w,
-                           (int64_t)p.rows * p.K, p.rows, p.K, g, b, C.total, p.q, p.sc);
+        if (fmt == FMT_ZP)
+            hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, dim3(256), 0, s, p.w,
+                               (int64_t)p.rows * p.K, p.rows, p.K, g, b, C.total, p.q, p.sc, p.z);
+        else
+            hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, dim3(256), 0, s, p.w,
+                               (int64_t)p.rows * p.K, p.rows, p.K, g, b, C.total, p.q, p.sc,
+                               (int64_t)0);
         MOE_LAUNCH_CHECK("quantize_rows_kernel");
     }
     return MOE_OK;
 }
 
-int launch_prepack(const void *src, int n, int H, int I, int g, void *dst, int dir, hipStream_t s)
+int launch_prepack(const void *src, int n, int H, int I, int g, int fmt, void *dst, int dir,
+                   hipStream_t s)
 {
-    const CanonLayout C = canon_layout(H, I, g);
-    const DevLayout D = dev_layout(H, I, g);
+    const CanonLayout C = canon_layout(H, I, g, fmt);
+    const DevLayout D = dev_layout(H, I, g, fmt);
     hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, s, (uint4_t *)dst,
                        (int64_t)n * C.total / 16);
     MOE_LAUNCH_CHECK("zero_kernel");
     hipLaunchKernelGGL(prepack_kernel, dim3(512, n), dim3(256), 0, s,
                        static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), H, I, g,
-                       C.total, C, D, dir);
+                       C.total, C, D, dir, fmt == FMT_ZP ? 1 : 0);
     MOE_LAUNCH_CHECK("prepack_kernel");
     return MOE_OK;
 }

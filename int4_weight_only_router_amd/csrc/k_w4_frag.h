@@ -36,4 +36,35 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, uint32_t mag
     return r;
 }
 
+// Zero-point codes: the same conversion with the offsets of the row's group,
+// klo = -(1024 + z) and khi = -(64 + z) (both exact in fp16), giving
+// fp16((u - z) * s) with one rounding.
+__device__ __forceinline__ half8_t dequant8_zp(uint32_t w, half2_t s2, uint32_t magic,
+                                               half2_t klo, half2_t khi)
+{
+    const uint32_t w8 = w >> 8;
+    const half2_t s16 = {(f16)0.0625f, (f16)0.0625f};
+    half2_t q[4];
+    q[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | magic) + klo;
+    q[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | magic) * s16 + khi;
+    q[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | magic) + klo;
+    q[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | magic) * s16 + khi;
+    half8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half2_t v = q[i] * s2;
+        r[2 * i] = v[0];
+        r[2 * i + 1] = v[1];
+    }
+    return r;
+}
+
+// The two offsets of zero point z as half2 pairs.
+__device__ __forceinline__ void zp_offsets(uint32_t z, half2_t &klo, half2_t &khi)
+{
+    const f16 lo = (f16)(-1024.0f - (float)z), hi = (f16)(-64.0f - (float)z);
+    klo = half2_t{lo, lo};
+    khi = half2_t{hi, hi};
+}
+
 }  // namespace moe

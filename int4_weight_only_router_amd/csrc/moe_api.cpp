@@ -39,14 +39,14 @@ int launch_route_split(const void *, const void *, const float *, int, int, int,
 int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
                    void *, hipStream_t);
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
-                      const void *const *, int, int, int, int, int, int, bool, float *,
+                      const void *const *, int, int, int, int, int, int, int, bool, float *,
                       hipStream_t);
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
-                       int, int, int, int, int, void *, void *, hipStream_t);
+                       int, int, int, int, int, int, void *, void *, hipStream_t);
 bool ffn_small_fits(int T, int H, int I);
 int launch_ffn_small(const void *, const int32_t *, const int32_t *, const void *const *, int, int,
-                     int, int, int, int, void *, void *, hipStream_t);
+                     int, int, int, int, int, void *, void *, hipStream_t);
 int launch_shared_gemv(const void *, const void *, const void *, const void *, int, int, int,
                        float *, void *, hipStream_t);
 int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
@@ -54,9 +54,9 @@ int launch_shared_batched(const void *, const void *, const void *, const void *
 int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
                    const void *, const void *, const void *, int, int, int, void *,
                    hipStream_t);
-int launch_quantize(const float *, const float *, const float *, int, int, int, int, void *,
+int launch_quantize(const float *, const float *, const float *, int, int, int, int, int, void *,
                     hipStream_t);
-int launch_prepack(const void *, int, int, int, int, void *, int, hipStream_t);
+int launch_prepack(const void *, int, int, int, int, int, void *, int, hipStream_t);
 int launch_zero_bytes(void *, size_t, hipStream_t);
 
 constexpr int DECODE_MAX_T = 4;       // AUTO: decode kernel up to this many tokens
@@ -169,62 +169,104 @@ int moe_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream)
     return launch_zero_bytes(ws, ws_bytes, stream);
 }
 
-int moe_blob_layout(int H, int I, int group, int64_t offsets[6], int64_t *total_bytes)
+int moe_blob_layout_fmt(int H, int I, int group, int fmt, int64_t offsets[9],
+                        int64_t *total_bytes)
 {
     clear_error();
     if (!offsets || !total_bytes || H <= 0 || I <= 0 || group <= 0 || H % group || I % group ||
-        H % 2 || I % 2)
-        return set_error(MOE_EINVAL, "moe_blob_layout: bad arguments (H=%d I=%d g=%d)", H, I,
-                         group);
-    const CanonLayout L = canon_layout(H, I, group);
-    offsets[0] = L.gate_q;
-    offsets[1] = L.up_q;
-    offsets[2] = L.down_q;
-    offsets[3] = L.gate_s;
-    offsets[4] = L.up_s;
-    offsets[5] = L.down_s;
+        H % 2 || I % 2 || (fmt != MOE_FMT_SYM && fmt != MOE_FMT_ZP))
+        return set_error(MOE_EINVAL, "moe_blob_layout_fmt: bad arguments (H=%d I=%d g=%d fmt=%d)",
+                         H, I, group, fmt);
+    const CanonLayout L = canon_layout(H, I, group, fmt);
+    const int64_t o[9] = {L.gate_q, L.up_q, L.down_q, L.gate_s, L.up_s, L.down_s,
+                          L.gate_z, L.up_z, L.down_z};
+    for (int i = 0; i < 9; ++i)
+        offsets[i] = o[i];
     *total_bytes = L.total;
     return MOE_OK;
+}
+
+int moe_blob_layout(int H, int I, int group, int64_t offsets[6], int64_t *total_bytes)
+{
+    int64_t o[9];
+    if (!offsets)
+        return set_error(MOE_EINVAL, "moe_blob_layout: null offsets");
+    const int rc = moe_blob_layout_fmt(H, I, group, MOE_FMT_SYM, o, total_bytes);
+    if (rc)
+        return rc;
+    for (int i = 0; i < 6; ++i)
+        offsets[i] = o[i];
+    return MOE_OK;
+}
+
+static int check_fmt(const char *fn, int fmt)
+{
+    if (fmt != MOE_FMT_SYM && fmt != MOE_FMT_ZP)
+        return set_error(MOE_EINVAL, "%s: unknown blob format %d", fn, fmt);
+    return MOE_OK;
+}
+
+int moe_quantize_experts_fmt(const float *wg, const float *wu, const float *wd, int n, int H,
+                             int I, int group, int fmt, void *blobs, hipStream_t stream)
+{
+    clear_error();
+    if (!wg || !wu || !wd || !blobs || n < 0)
+        return set_error(MOE_EINVAL, "moe_quantize_experts: null pointer or n < 0");
+    int rc = check_fmt("moe_quantize_experts", fmt);
+    if (!rc)
+        rc = check_expert_shape("moe_quantize_experts", H, I, group);
+    if (rc || n == 0)
+        return rc;
+    return launch_quantize(wg, wu, wd, n, H, I, group, fmt, blobs, stream);
 }
 
 int moe_quantize_experts(const float *wg, const float *wu, const float *wd, int n, int H, int I,
                          int group, void *blobs, hipStream_t stream)
 {
-    clear_error();
-    if (!wg || !wu || !wd || !blobs || n < 0)
-        return set_error(MOE_EINVAL, "moe_quantize_experts: null pointer or n < 0");
-    int rc = check_expert_shape("moe_quantize_experts", H, I, group);
-    if (rc || n == 0)
-        return rc;
-    return launch_quantize(wg, wu, wd, n, H, I, group, blobs, stream);
+    return moe_quantize_experts_fmt(wg, wu, wd, n, H, I, group, MOE_FMT_SYM, blobs, stream);
 }
 
 static int prepack_common(const char *fn, const void *src, int n, int H, int I, int group,
-                          void *dst, int dir, hipStream_t stream)
+                          int fmt, void *dst, int dir, hipStream_t stream)
 {
     clear_error();
     if (!src || !dst || n < 0)
         return set_error(MOE_EINVAL, "%s: null pointer or n < 0", fn);
-    int rc = check_expert_shape(fn, H, I, group);
+    int rc = check_fmt(fn, fmt);
+    if (!rc)
+        rc = check_expert_shape(fn, H, I, group);
     if (rc || n == 0)
         return rc;
-    const int64_t tot = canon_layout(H, I, group).total * (int64_t)n;
+    const int64_t tot = canon_layout(H, I, group, fmt).total * (int64_t)n;
     const char *a = static_cast<const char *>(src), *b = static_cast<const char *>(dst);
     if (a < b + tot && b < a + tot)
         return set_error(MOE_EINVAL, "%s: src and dst overlap", fn);
-    return launch_prepack(src, n, H, I, group, dst, dir, stream);
+    return launch_prepack(src, n, H, I, group, fmt, dst, dir, stream);
 }
 
 int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *dst,
                         hipStream_t stream)
 {
-    return prepack_common("moe_prepack_experts", src, n, H, I, group, dst, 0, stream);
+    return prepack_common("moe_prepack_experts", src, n, H, I, group, MOE_FMT_SYM, dst, 0,
+                          stream);
 }
 
 int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *dst,
                        hipStream_t stream)
 {
-    return prepack_common("moe_unpack_experts", src, n, H, I, group, dst, 1, stream);
+    return prepack_common("moe_unpack_experts", src, n, H, I, group, MOE_FMT_SYM, dst, 1, stream);
+}
+
+int moe_prepack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
+                            hipStream_t stream)
+{
+    return prepack_common("moe_prepack_experts_fmt", src, n, H, I, group, fmt, dst, 0, stream);
+}
+
+int moe_unpack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
+                           hipStream_t stream)
+{
+    return prepack_common("moe_unpack_experts_fmt", src, n, H, I, group, fmt, dst, 1, stream);
 }
 
 static int check_route_args(const char *fn, const void *x_f16, const void *w_router_f16, int T,
@@ -374,7 +416,7 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
     if (rc)
         return rc;
     const bool tok = (regime & MOE_Y_TOKEN_ORDER) != 0;
-    regime &= ~MOE_Y_TOKEN_ORDER;
+    regime &= ~(MOE_Y_TOKEN_ORDER | MOE_W4_ZERO_POINT);
     if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_SMALL)
         return set_error(MOE_EINVAL, "moe_expert_ffn_plan: bad regime %d", regime);
     const int r = resolve_regime(T, H, I, regime);
@@ -418,15 +460,16 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
     if (need && (!ws || ws_bytes < need))
         return set_error(MOE_ENOMEM, "moe_expert_ffn_w4a16: workspace %zu < %zu bytes", ws_bytes,
                          need);
+    const int fmt = (regime & MOE_W4_ZERO_POINT) ? MOE_FMT_ZP : MOE_FMT_SYM;
     if (r == MOE_REGIME_DECODE)
         return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
-                                 group, (regime & MOE_Y_TOKEN_ORDER) != 0,
+                                 group, fmt, (regime & MOE_Y_TOKEN_ORDER) != 0,
                                  static_cast<float *>(y), stream);
     if (r == MOE_REGIME_SMALL)
-        return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
-                                stream);
-    return launch_ffn_batched(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, y, ws,
-                              stream);
+        return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, fmt, y,
+                                ws, stream);
+    return launch_ffn_batched(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, fmt, y,
+                              ws, stream);
 }
 
 size_t moe_shared_ffn_workspace_bytes(int T, int H, int Is)

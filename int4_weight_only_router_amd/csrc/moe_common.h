@@ -41,11 +41,16 @@ inline int64_t al256(int64_t x) { return (x + 255) & ~int64_t(255); }
 size_t shared_ffn_ws_bytes(int T, int H, int Is);
 _Float16 *shared_ffn_h(void *ws);
 
-// Canonical blob section offsets (format documented in moe_w4a16.h).
+// Blob formats: symmetric codes (W = (u - 8) s) or a zero point per group
+// (W = (u - z) s, one u8 per group of each projection after the scales).
+enum { FMT_SYM = 0, FMT_ZP = 1 };
+
+// Canonical blob section offsets (format documented in moe_w4a16.h); the
+// zero-point sections exist only for FMT_ZP (else 0).
 struct CanonLayout {
-    int64_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+    int64_t gate_q, up_q, down_q, gate_s, up_s, down_s, gate_z, up_z, down_z, total;
 };
-inline CanonLayout canon_layout(int H, int I, int g) {
+inline CanonLayout canon_layout(int H, int I, int g, int fmt = FMT_SYM) {
     CanonLayout L;
     int64_t o = 0;
     L.gate_q = o; o = al256(o + int64_t(I) * H / 2);
@@ -54,6 +59,12 @@ inline CanonLayout canon_layout(int H, int I, int g) {
     L.gate_s = o; o = al256(o + int64_t(I) * (H / g) * 2);
     L.up_s = o;   o = al256(o + int64_t(I) * (H / g) * 2);
     L.down_s = o; o = al256(o + int64_t(H) * (I / g) * 2);
+    L.gate_z = L.up_z = L.down_z = 0;
+    if (fmt == FMT_ZP) {
+        L.gate_z = o; o = al256(o + int64_t(I) * (H / g));
+        L.up_z = o;   o = al256(o + int64_t(I) * (H / g));
+        L.down_z = o; o = al256(o + int64_t(H) * (I / g));
+    }
     L.total = o;
     return L;
 }
@@ -63,16 +74,23 @@ inline CanonLayout canon_layout(int H, int I, int g) {
 //   d_q  : down INT4, H/64 blocks x (I/32 chunks) x 64 rows x 16 B
 //   gu_s : fused gate/up scales, I/32 blocks x (H/g) x 64 rows fp16
 //   d_s  : down scales, H/64 blocks x (I/g) x 64 rows fp16
+//   gu_z, d_z (FMT_ZP only): zero points in the scales' order, u8
 struct DevLayout {
-    int64_t gu_q, d_q, gu_s, d_s, end;
+    int64_t gu_q, d_q, gu_s, d_s, gu_z, d_z, end;
 };
-inline DevLayout dev_layout(int H, int I, int g) {
+inline DevLayout dev_layout(int H, int I, int g, int fmt = FMT_SYM) {
     DevLayout L;
     int64_t o = 0;
     L.gu_q = o; o = al256(o + int64_t(I) * H);
     L.d_q = o;  o = al256(o + int64_t(H) * I / 2);
     L.gu_s = o; o = al256(o + int64_t(2) * I * (H / g) * 2);
     L.d_s = o;  o = o + int64_t(H) * (I / g) * 2;
+    L.gu_z = L.d_z = 0;
+    if (fmt == FMT_ZP) {
+        o = al256(o);
+        L.gu_z = o; o = al256(o + int64_t(2) * I * (H / g));
+        L.d_z = o;  o = o + int64_t(H) * (I / g);
+    }
     L.end = o;
     return L;
 }

@@ -12,16 +12,17 @@ import torch
 from . import _abi as A
 
 
-def load_experts(weights, H, I, group, device="cuda", stream=None):
+def load_experts(weights, H, I, group, device="cuda", stream=None, fmt=A.MOE_FMT_SYM):
     """Quantise and prepack experts on the device.
 
     weights: iterable of (wg [I,H], wu [I,H], wd [H,I]) float32 arrays
     (numpy or torch).  Returns a uint8 device tensor [n, blob_bytes] in the
-    device layout.  Quantisation and prepacking run in the library's kernels.
+    device layout (and the canonical blobs).  Quantisation and prepacking run
+    in the library's kernels; fmt is MOE_FMT_SYM or MOE_FMT_ZP.
     """
     weights = list(weights)
     n = len(weights)
-    _, total = A.moe_blob_layout(H, I, group)
+    _, total = A.moe_blob_layout_fmt(H, I, group, fmt)
     dev = torch.empty((n, total), dtype=torch.uint8, device=device)
     canon = torch.empty((n, total), dtype=torch.uint8, device=device)
     wg = torch.empty((n, I, H), dtype=torch.float32, device=device)
@@ -31,8 +32,8 @@ def load_experts(weights, H, I, group, device="cuda", stream=None):
         wg[e].copy_(torch.as_tensor(g_))
         wu[e].copy_(torch.as_tensor(u_))
         wd[e].copy_(torch.as_tensor(d_))
-    A.moe_quantize_experts(wg, wu, wd, n, H, I, group, canon, stream)
-    A.moe_prepack_experts(canon, n, H, I, group, dev, stream)
+    A.moe_quantize_experts_fmt(wg, wu, wd, n, H, I, group, fmt, canon, stream)
+    A.moe_prepack_experts_fmt(canon, n, H, I, group, fmt, dev, stream)
     return dev, canon
 
 
@@ -68,8 +69,10 @@ class MoELayer:
     """One W4A16 MoE layer resident on the device."""
 
     def __init__(self, H, I, E, k, group, router, table, bias=None, shared=None,
-                 renorm=False, device="cuda", shared_gate=None, overlap_shared=False):
+                 renorm=False, device="cuda", shared_gate=None, overlap_shared=False,
+                 fmt=A.MOE_FMT_SYM):
         self.H, self.I, self.E, self.k, self.g = H, I, E, k, group
+        self.fmt = fmt                  # blob format of the routed experts
         self.router = router            # fp16 [E, H] device
         self.table = table              # int64 [E] device (blob addresses)
         self.bias = bias                # fp32 [E] device or None
@@ -90,6 +93,8 @@ class MoELayer:
             # decode partials straight in token order: the combine then reads
             # them without inv_perm (one dependent round trip less)
             r |= A.MOE_Y_TOKEN_ORDER
+        if self.fmt == A.MOE_FMT_ZP:
+            r |= A.MOE_W4_ZERO_POINT
         # route/permute scratch; zero-filled once (the fused router keeps an
         # atomic ticket in it)
         pws = max(A.moe_permute_workspace_bytes(T, self.k, self.E),

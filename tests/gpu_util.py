@@ -28,10 +28,10 @@ def f16(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def device_experts(cfg, layer, experts=None, batch=32):
+def device_experts(cfg, layer, experts=None, batch=32, fmt=M.MOE_FMT_SYM):
     """Prepacked device blobs [E, bytes] of a layer; canonical blobs too."""
     experts = list(range(cfg.E)) if experts is None else list(experts)
-    _, total = M.moe_blob_layout(cfg.H, cfg.I, cfg.g)
+    _, total = M.moe_blob_layout_fmt(cfg.H, cfg.I, cfg.g, fmt)
     dev = torch.empty((cfg.E, total), dtype=torch.uint8, device=DEV)
     canon = torch.empty((cfg.E, total), dtype=torch.uint8, device=DEV)
     for b0 in range(0, len(experts), batch):
@@ -46,8 +46,8 @@ def device_experts(cfg, layer, experts=None, batch=32):
             wd[i].copy_(torch.from_numpy(d_))
         cb = torch.empty((n, total), dtype=torch.uint8, device=DEV)
         db = torch.empty((n, total), dtype=torch.uint8, device=DEV)
-        M.moe_quantize_experts(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, cb)
-        M.moe_prepack_experts(cb, n, cfg.H, cfg.I, cfg.g, db)
+        M.moe_quantize_experts_fmt(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, fmt, cb)
+        M.moe_prepack_experts_fmt(cb, n, cfg.H, cfg.I, cfg.g, fmt, db)
         idx = torch.tensor(ids, device=DEV)
         dev[idx] = db
         canon[idx] = cb
@@ -59,8 +59,8 @@ def device_experts(cfg, layer, experts=None, batch=32):
 class OracleBlobs:
     """Lazily packed oracle blobs of one layer (same draws, oracle quantiser)."""
 
-    def __init__(self, cfg, layer):
-        self.cfg, self.layer, self.cache = cfg, layer, {}
+    def __init__(self, cfg, layer, fmt=O.FMT_SYM):
+        self.cfg, self.layer, self.fmt, self.cache = cfg, layer, fmt, {}
 
     def get(self, experts):
         c = self.cfg
@@ -68,8 +68,8 @@ class OracleBlobs:
         # draws and oracle packing in threads (numpy and the C oracle release
         # the GIL); every expert is still packed by the oracle's quantiser
         with ThreadPoolExecutor(8) as ex:
-            packed = ex.map(lambda e: (e, O.pack_expert(*MI.gen_expert(c, self.layer, e), c.g)),
-                            need)
+            packed = ex.map(lambda e: (e, O.pack_expert(*MI.gen_expert(c, self.layer, e), c.g,
+                                                        self.fmt)), need)
             for e, blob in packed:
                 self.cache[e] = blob
         return [self.cache.get(e) for e in range(c.E)]
@@ -78,18 +78,18 @@ class OracleBlobs:
 _EXPERT_CACHE = {}
 
 
-def cached_experts(cfg, layer):
-    key = (cfg.cid, cfg.H, cfg.E, cfg.I, cfg.g, layer)
+def cached_experts(cfg, layer, fmt=M.MOE_FMT_SYM):
+    key = (cfg.cid, cfg.H, cfg.E, cfg.I, cfg.g, layer, fmt)
     if key not in _EXPERT_CACHE:
         if len(_EXPERT_CACHE) >= 3:
             _EXPERT_CACHE.pop(next(iter(_EXPERT_CACHE)))
-        say("build experts cfg=%s layer=%d" % (cfg.name, layer))
-        _EXPERT_CACHE[key] = device_experts(cfg, layer)[0]
+        say("build experts cfg=%s layer=%d fmt=%d" % (cfg.name, layer, fmt))
+        _EXPERT_CACHE[key] = device_experts(cfg, layer, fmt=fmt)[0]
     return _EXPERT_CACHE[key]
 
 
-def make_layer(cfg, layer=0, shared=True):
-    dev = cached_experts(cfg, layer)
+def make_layer(cfg, layer=0, shared=True, fmt=M.MOE_FMT_SYM):
+    dev = cached_experts(cfg, layer, fmt)
     router = f16(MI.gen_router(cfg, layer))
     b = MI.zipf_bias(cfg, layer)
     bias = None if b is None else torch.from_numpy(b).to(DEV)
@@ -98,7 +98,7 @@ def make_layer(cfg, layer=0, shared=True):
         sh = tuple(f16(w) for w in MI.gen_shared(cfg))
     gate = f16(MI.gen_shared_gate(cfg)) if (sh is not None and cfg.shared_gate) else None
     lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, router, blob_table(dev), bias, sh,
-                   device=DEV, shared_gate=gate)
+                   device=DEV, shared_gate=gate, fmt=fmt)
     lay._blobs = dev            # keep the storage alive
     return lay
 

@@ -43,9 +43,10 @@ def test_quantize_bit_exact(cfg):
         assert np.array_equal(_np(canon[e]), ob[e]), "expert %d blob differs" % e
 
 
-def _numpy_prepack(canon, H, I, g):
+def _numpy_prepack(canon, H, I, g, fmt=O.FMT_SYM):
     """Independent rendering of the documented device layout (format only)."""
-    gq, uq, dq, gs, us, ds = O.blob_sections(canon, H, I, g)
+    sec = O.blob_sections(canon, H, I, g, fmt)
+    gq, uq, dq, gs, us, ds = sec[:6]
     out = np.zeros_like(canon)
 
     def relayout(chunk):   # 16 canonical bytes -> 16 device bytes
@@ -85,6 +86,23 @@ def _numpy_prepack(canon, H, I, g):
             for r in range(64):
                 v[j] = ds[64 * b + r, G]
                 j += 1
+    if fmt == O.FMT_ZP:
+        # zero points in the scales' order, one byte each
+        gz, uz, dz = sec[6:]
+        o3 = -(-(o2 + 2 * j) // 256) * 256
+        j = 0
+        for b in range(I // 32):
+            for G in range(H // g):
+                for r in range(64):
+                    out[o3 + j] = (gz if r < 32 else uz)[32 * b + (r & 31), G]
+                    j += 1
+        o4 = -(-(o3 + j) // 256) * 256
+        j = 0
+        for b in range(H // 64):
+            for G in range(I // g):
+                for r in range(64):
+                    out[o4 + j] = dz[64 * b + r, G]
+                    j += 1
     return out
 
 
@@ -336,8 +354,8 @@ def test_permute_hot_expert():
 
 # ------------------------------------------------------------ expert FFN
 
-def _ffn_case(cfg, T, regime, layer=0):
-    lay = make_layer(cfg, layer, shared=False)
+def _ffn_case(cfg, T, regime, layer=0, fmt=M.MOE_FMT_SYM):
+    lay = make_layer(cfg, layer, shared=False, fmt=fmt)
     x = MI.gen_x(cfg, T)
     b = lay.buffers(T, regime)
     say("ffn %s T=%d regime=%d" % (cfg.name, T, b.regime))
@@ -352,8 +370,9 @@ def _ffn_case(cfg, T, regime, layer=0):
     assert np.array_equal(_np(b.offsets), offsets) and np.array_equal(_np(b.perm), perm[:T * cfg.k])
     rows = np.arange(T * cfg.k, dtype=np.int32)   # every row, every bucket edge
     used = np.unique(oi)
-    blobs = OracleBlobs(cfg, layer).get(used)
-    y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
+    blobs = OracleBlobs(cfg, layer, fmt).get(used)
+    y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows,
+                         fmt=fmt)
     y = _np(b.y).astype(np.float64)
     # decode partials are in token order: sorted row p sits at row perm[p]
     yr = perm[rows] if b.regime & M.MOE_Y_TOKEN_ORDER else rows
@@ -815,3 +834,71 @@ def test_workspace_clear_recovers_a_stale_ticket():
         v = _np(buf)
         assert np.all(v[off:off + nb] == 0) and np.all(v[:off] == 0xAB) and \
             np.all(v[off + nb:] == 0xAB), (off, nb)
+
+
+# ------------------------------------------------------ zero-point format
+
+@pytest.mark.parametrize("cfg", [MI.TINY, MI.OLMOE_DECODE, MI.E512, G32], ids=lambda c: c.name)
+def test_quantize_zero_point_bit_exact(cfg):
+    """The library's zero-point quantiser makes the oracle's decisions: the
+    canonical blobs (codes, scales, zero points) are identical bytes."""
+    say("quantize zp %s" % cfg.name)
+    ex = [0, 1, cfg.E - 1]
+    _, canon = device_experts(cfg, 0, experts=ex, fmt=M.MOE_FMT_ZP)
+    ob = OracleBlobs(cfg, 0, O.FMT_ZP).get(ex)
+    assert M.moe_blob_layout_fmt(cfg.H, cfg.I, cfg.g, M.MOE_FMT_ZP) == \
+        tuple(O.blob_layout(cfg.H, cfg.I, cfg.g, O.FMT_ZP))
+    for e in ex:
+        assert np.array_equal(_np(canon[e]), ob[e]), "expert %d blob differs" % e
+
+
+@pytest.mark.parametrize("cfg", [MI.TINY, G32], ids=lambda c: c.name)
+def test_prepack_zero_point_layout_and_round_trip(cfg):
+    say("prepack zp %s" % cfg.name)
+    dev, canon = device_experts(cfg, 0, experts=[0, 3], fmt=M.MOE_FMT_ZP)
+    for e in (0, 3):
+        ref = _numpy_prepack(_np(canon[e]), cfg.H, cfg.I, cfg.g, O.FMT_ZP)
+        assert np.array_equal(_np(dev[e]), ref)
+    back = torch.empty_like(dev)
+    M.moe_unpack_experts_fmt(dev, cfg.E, cfg.H, cfg.I, cfg.g, M.MOE_FMT_ZP, back)
+    torch.cuda.synchronize()
+    for e in (0, 3):
+        assert np.array_equal(_np(back[e]), _np(canon[e]))
+
+
+@pytest.mark.parametrize("cfg,T,regime", [
+    (MI.TINY, 16, M.MOE_REGIME_DECODE), (MI.TINY, 16, M.MOE_REGIME_SMALL),
+    (MI.TINY, 16, M.MOE_REGIME_BATCHED), (MI.TINY, 300, M.MOE_REGIME_BATCHED),
+    (MI.OLMOE_DECODE, 1, M.MOE_REGIME_AUTO), (MI.OLMOE_DECODE, 3, M.MOE_REGIME_AUTO),
+    (MI.OLMOE_DECODE, 8, M.MOE_REGIME_AUTO), (MI.OLMOE_DECODE, 32, M.MOE_REGIME_SMALL),
+    (MI.OLMOE_DECODE, 64, M.MOE_REGIME_BATCHED), (MI.OLMOE_DECODE, 512, M.MOE_REGIME_BATCHED),
+    (MI.OLMOE_DECODE, 4096, M.MOE_REGIME_BATCHED), (MI.E512, 1, M.MOE_REGIME_AUTO),
+    (MI.E512, 256, M.MOE_REGIME_BATCHED), (G32, 3, M.MOE_REGIME_DECODE),
+    (G32, 32, M.MOE_REGIME_SMALL), (G32, 300, M.MOE_REGIME_BATCHED)],
+    ids=lambda v: getattr(v, "name", str(v)))
+def test_expert_ffn_zero_point(cfg, T, regime):
+    """Routed FFN from zero-point blobs in every regime, every row against the
+    oracle's zero-point decoder."""
+    _ffn_case(cfg, T, regime, fmt=M.MOE_FMT_ZP)
+
+
+@pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 16),
+                                   (MI.E512, 300)], ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_zero_point(cfg, T):
+    """Whole layers (route, permute, zero-point FFN, shared expert, combine)."""
+    lay = make_layer(cfg, 0, fmt=M.MOE_FMT_ZP)
+    x = MI.gen_x(cfg, T, step=5)
+    res = MI.gen_residual(cfg, T) if cfg.residual else None
+    b = lay.buffers(T)
+    assert b.regime & M.MOE_W4_ZERO_POINT
+    say("layer zp %s T=%d regime=%d" % (cfg.name, T, b.regime))
+    out = lay.forward(f16(x), b, None if res is None else f16(res))
+    torch.cuda.synchronize()
+    wr = MI.gen_router(cfg, 0)
+    bias = MI.zipf_bias(cfg, 0)
+    idx, _, _ = O.route(x, wr, bias, cfg.k)
+    sh = MI.gen_shared(cfg) if cfg.Is else None
+    ref = O.moe_layer(x, wr, OracleBlobs(cfg, 0, O.FMT_ZP).get(np.unique(idx)), cfg.H, cfg.I,
+                      cfg.E, cfg.k, cfg.g, bias=bias, shared=sh, residual=res, fmt=O.FMT_ZP)
+    assert np.array_equal(_np(b.topk_idx), ref["idx"])
+    check_close(_np(out).astype(np.float64), ref["out_f64"], "zp layer %s T=%d" % (cfg.name, T))
