@@ -163,6 +163,16 @@ int moe_prepack_experts_fmt(const void *src, int n, int H, int I, int group, int
 int moe_unpack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
                            hipStream_t stream);
 
+/*
+ * The same bijection on the host, one blob (src and dst host memory of the
+ * canonical blob size, not overlapping): for a source that lives in host
+ * memory, such as the pinned INT4 source of the slot pool, so that loading it
+ * needs no device round trip.  Bytes identical to moe_prepack_experts_fmt /
+ * moe_unpack_experts_fmt.  No GPU needed.  MOE_EINVAL on bad arguments.
+ */
+int moe_prepack_expert_host(const void *src, int H, int I, int group, int fmt, void *dst);
+int moe_unpack_expert_host(const void *src, int H, int I, int group, int fmt, void *dst);
+
 /* ------------------------------------------------------------ router */
 /*
  * Router softmax + top-k (Horizon RunMap "03 / Arquitetura": the router

@@ -12,7 +12,7 @@ __all__ = [
     "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_DTYPE_F16",
     "MOE_DTYPE_F32", "MOE_FMT_SYM", "MOE_FMT_ZP", "MOE_W4_ZERO_POINT", "EXPORTS",
     "moe_blob_layout_fmt", "moe_quantize_experts_fmt", "moe_prepack_experts_fmt",
-    "moe_unpack_experts_fmt",
+    "moe_unpack_experts_fmt", "moe_prepack_expert_host", "moe_unpack_expert_host",
     "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts",
     "moe_prepack_experts",
     "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
@@ -37,9 +37,9 @@ MOE_W4_ZERO_POINT = 0x200        # OR'd into a regime: the blobs are MOE_FMT_ZP
 # every symbol include/moe_w4a16.h declares
 EXPORTS = [
     "moe_blob_layout_fmt", "moe_quantize_experts_fmt", "moe_prepack_experts_fmt",
-    "moe_unpack_experts_fmt",
-    "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts", "moe_prepack_experts",
-    "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
+    "moe_unpack_experts_fmt", "moe_prepack_expert_host", "moe_unpack_expert_host",
+    "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts",
+    "moe_prepack_experts", "moe_unpack_experts", "moe_route_workspace_bytes", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
@@ -97,6 +97,8 @@ def _declare(L):
         "moe_quantize_experts_fmt": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
         "moe_prepack_experts_fmt": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
         "moe_unpack_experts_fmt": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
+        "moe_prepack_expert_host": (i32, [vp, i32, i32, i32, i32, vp]),
+        "moe_unpack_expert_host": (i32, [vp, i32, i32, i32, i32, vp]),
         "moe_quantize_experts": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_prepack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
         "moe_unpack_experts": (i32, [vp, i32, i32, i32, i32, vp, vp]),
@@ -214,6 +216,25 @@ def moe_prepack_experts_fmt(src, n, H, I, group, fmt, dst, stream=None):
 
 def moe_unpack_experts_fmt(src, n, H, I, group, fmt, dst, stream=None):
     _check(lib().moe_unpack_experts_fmt(_p(src), n, H, I, group, fmt, _p(dst), _s(stream)))
+
+
+def moe_prepack_expert_host(src, H, I, group, fmt, dst):
+    """One canonical blob to the device layout on the host (numpy uint8 arrays,
+    or host addresses as ints)."""
+    _check(lib().moe_prepack_expert_host(_hp(src), H, I, group, fmt, _hp(dst)))
+
+
+def moe_unpack_expert_host(src, H, I, group, fmt, dst):
+    _check(lib().moe_unpack_expert_host(_hp(src), H, I, group, fmt, _hp(dst)))
+
+
+def _hp(a):
+    """Host address of a numpy array (or an int address)."""
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "ctypes"):
+        return a.ctypes.data
+    return a.data_ptr()
 
 
 def moe_quantize_experts(wg, wu, wd, n, H, I, group, blobs, stream=None):

@@ -1,13 +1,16 @@
 // pool_fake.cpp -- host-only build of the slot pool for CPU tests: "device"
 // slots and tables are host memory, copies are memcpy, streams and events do
-// nothing, and copy failures can be injected.  Built into
-// libmoe_pool_host.so; exports the same moe_pool_* entry points plus
-// moe_pool_fake_fail_after().  Not part of the GPU library.
+// nothing, and copy failures can be injected.  Copies can also be held back
+// (queued, applied only when the test says so) to check that the previous
+// generation stays intact while a generation's copies are in flight.  Built
+// into libmoe_pool_host.so; exports the same moe_pool_* entry points plus the
+// moe_pool_fake_* test hooks.  Not part of the GPU library.
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "pool_core.h"
 
@@ -33,6 +36,13 @@ struct FakeBackend {
     const void **tables = nullptr;
     long fail_after = -1;   // copies allowed before one fails; -1 = never
     long copies = 0;
+    bool delay = false;     // queue copies until complete_copies()
+    struct Pending {
+        void *dst;
+        const void *src;
+        size_t n;
+    };
+    std::vector<Pending> pending;
 
     int init(const moe_pool_config &c)
     {
@@ -50,7 +60,10 @@ struct FakeBackend {
     {
         if (fail_after >= 0 && copies >= fail_after)
             return set_error(MOE_EHIP, "fake pool: injected copy failure after %ld copies", copies);
-        memcpy(dst, src, n);
+        if (delay)
+            pending.push_back({dst, src, n});
+        else
+            memcpy(dst, src, n);
         ++copies;
         return MOE_OK;
     }
@@ -64,7 +77,19 @@ struct FakeBackend {
     }
     int publish(int, hipStream_t) { return MOE_OK; }
     int retire(int, hipStream_t) { return MOE_OK; }
-    int sync() { return MOE_OK; }
+    int sync()
+    {
+        complete_copies();   // a synchronisation point lands every copy
+        return MOE_OK;
+    }
+    long complete_copies()
+    {
+        for (const Pending &p : pending)
+            memcpy(p.dst, p.src, p.n);
+        const long n = (long)pending.size();
+        pending.clear();
+        return n;
+    }
     void destroy()
     {
         free(slots);
@@ -151,6 +176,35 @@ int moe_pool_fake_fail_after(moe_pool_t pool, long n)
         return MOE_EINVAL;
     pool->p.be.fail_after = n < 0 ? -1 : pool->p.be.copies + n;
     return MOE_OK;
+}
+
+// Held-back copies: on != 0 queues every later copy until
+// moe_pool_fake_complete_copies() (or a synchronising call) applies them in
+// order.  pending() is the queue length, pending_dst(i) the destination of
+// queued copy i (NULL out of range).
+int moe_pool_fake_set_delay(moe_pool_t pool, int on)
+{
+    if (!pool)
+        return MOE_EINVAL;
+    pool->p.be.delay = on != 0;
+    return MOE_OK;
+}
+
+long moe_pool_fake_complete_copies(moe_pool_t pool)
+{
+    return pool ? pool->p.be.complete_copies() : -1;
+}
+
+long moe_pool_fake_pending(moe_pool_t pool)
+{
+    return pool ? (long)pool->p.be.pending.size() : -1;
+}
+
+void *moe_pool_fake_pending_dst(moe_pool_t pool, long i)
+{
+    if (!pool || i < 0 || i >= (long)pool->p.be.pending.size())
+        return nullptr;
+    return pool->p.be.pending[(size_t)i].dst;
 }
 
 }  // extern "C"

@@ -4,6 +4,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 import int4_weight_only_router_amd as M
@@ -147,3 +148,25 @@ def test_pool_layer_forward_rejects_null_arguments():
     with pytest.raises(M.MoEError) as ei:
         M.moe_pool_layer_forward(None, 0, args, stream=0)
     assert ei.value.code == M.MOE_EINVAL
+
+
+@pytest.mark.parametrize("H,I,g,fmt", [(256, 512, 64, 0), (256, 512, 64, 1), (512, 192, 32, 1),
+                                       (1024, 128, 128, 0)])
+def test_host_prepack_matches_layout_and_round_trips(H, I, g, fmt):
+    """moe_prepack_expert_host renders an oracle-packed canonical blob into the
+    documented device layout (checked against an independent numpy
+    rendering), and moe_unpack_expert_host inverts it exactly."""
+    import moe_inputs as MI
+    from tests.layout_util import numpy_prepack
+    cfg = MI.MoEConfig(96, "hp", H=H, E=1, k=1, I=I, g=g)
+    canon = O.pack_expert(*MI.gen_expert(cfg, 0, 0), g, fmt)
+    dev = np.full_like(canon, 0xAB)
+    M.moe_prepack_expert_host(canon, H, I, g, fmt, dev)
+    assert np.array_equal(dev, numpy_prepack(canon, H, I, g, fmt))
+    back = np.full_like(canon, 0xCD)
+    M.moe_unpack_expert_host(dev, H, I, g, fmt, back)
+    assert np.array_equal(back, canon)
+    with pytest.raises(M.MoEError):
+        M.moe_prepack_expert_host(canon, H, I, 48, fmt, dev)
+    with pytest.raises(M.MoEError):
+        M.moe_prepack_expert_host(canon, H, I, g, 7, dev)

@@ -32,6 +32,13 @@ def L():
     lib.moe_pool_destroy.argtypes = [vp]
     lib.moe_pool_fake_fail_after.argtypes = [vp, C.c_long]
     lib.moe_pool_pin.argtypes = [vp, C.c_int, vp, C.c_int]
+    lib.moe_pool_fake_set_delay.argtypes = [vp, C.c_int]
+    lib.moe_pool_fake_complete_copies.argtypes = [vp]
+    lib.moe_pool_fake_complete_copies.restype = C.c_long
+    lib.moe_pool_fake_pending.argtypes = [vp]
+    lib.moe_pool_fake_pending.restype = C.c_long
+    lib.moe_pool_fake_pending_dst.argtypes = [vp, C.c_long]
+    lib.moe_pool_fake_pending_dst.restype = C.c_void_p
     lib.moe_last_error.restype = C.c_char_p
     return lib
 
@@ -277,3 +284,61 @@ def test_pin_errors_keep_state(L):
     rc, tab, st = P.prepare(0, [5, 1])
     assert rc == 0 and (st.hits, st.misses) == (1, 1)
     P.close()
+
+
+@pytest.mark.parametrize("pinned", [False, True])
+def test_previous_generation_intact_while_copies_are_in_flight(L, pinned):
+    """Copies held back (as if the side stream had not run yet): after each
+    prepare, every expert of the previous generation's table still holds its
+    source bytes, no queued copy writes into a slot that table references,
+    and once the copies land every expert of the new table holds its bytes;
+    the victims' slots are reused only after a retire (resident-qpacked-cache-v1:
+    readers keep the previous generation until the new one is published).
+    Pinned layers: the previous generation's one-off copies (experts outside
+    the pinned set) are dropped at the next prepare, after the retire, so
+    only the pinned experts' slots are held to this."""
+    Lyr, E, k, Cap, S = 2, 12, 3, 5, 3
+    P = FakePool(L, Lyr, E, k, Cap, S, 3, nbytes=256, seed=4)
+    assert P.rc == 0
+    pin_set = set(range(1, 1 + Cap))
+    try:
+        if pinned:
+            for l in range(Lyr):
+                assert L.moe_pool_pin(P.h, l, np.arange(1, 1 + Cap, dtype=np.int32).ctypes.data,
+                                      Cap) == 0
+        assert L.moe_pool_fake_set_delay(P.h, 1) == 0
+        layers, ids = _trace(11, 300, Lyr, E, k, s=0.5)
+        prev = {}
+        for l in range(Lyr):   # the published table of each layer before the trace
+            rc, tab, _ = P.prepare(l, np.arange(k, dtype=np.int32) + 1)
+            assert rc == 0 and L.moe_pool_fake_complete_copies(P.h) >= 0
+            assert P.retire(l) == 0
+            prev[l] = P.table(tab)
+        in_flight = 0
+        for l, R in zip(layers, ids):
+            l = int(l)
+            rc, tab, st = P.prepare(l, R)
+            assert rc == 0, L.moe_last_error()
+            npend = L.moe_pool_fake_pending(P.h)
+            assert npend == st.misses
+            in_flight += npend
+            old = [p if (not pinned or e in pin_set) else None for e, p in enumerate(prev[l])]
+            old_slots = {p for p in old if p}
+            for i in range(npend):
+                assert L.moe_pool_fake_pending_dst(P.h, i) not in old_slots
+            for e, ptr in enumerate(old):
+                if ptr:
+                    assert np.array_equal(P.slot_bytes(ptr), P.src[l, e]), (l, e)
+            assert L.moe_pool_fake_complete_copies(P.h) == npend
+            new = P.table(tab)
+            for e in R:
+                assert new[int(e)]
+            for e, ptr in enumerate(new):
+                if ptr:
+                    assert np.array_equal(P.slot_bytes(ptr), P.src[l, e]), (l, e)
+            assert P.retire(l) == 0
+            prev[l] = new
+        assert in_flight > 0
+        assert np.array_equal(P.src, P.src_copy)
+    finally:
+        P.close()
