@@ -83,24 +83,30 @@ def build_layers(cfg, layers, dev, torch, M):
 # ------------------------------------------------------------- CPU baseline
 
 def host_cpu():
-    """CPU model, physical cores (lscpu: cores per socket x sockets) and the
-    threads this process may use (affinity mask, OMP_NUM_THREADS)."""
-    import subprocess
-    model, cores, sockets = "unknown", None, None
+    """CPU model, physical cores (distinct (package, core) pairs in
+    /proc/cpuinfo, i.e. cores per socket x sockets) and the threads this
+    process may use (affinity mask, OMP_NUM_THREADS).  Read from files; no
+    tool is started."""
+    model, cores = "unknown", set()
     try:
-        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for line in out.splitlines():
+        phys = core = None
+        for line in open("/proc/cpuinfo"):
             k, _, v = line.partition(":")
-            v = v.strip()
-            if k.strip() == "Model name":
+            k, v = k.strip(), v.strip()
+            if k == "model name" and model == "unknown":
                 model = v
-            elif k.strip() == "Core(s) per socket":
-                cores = int(v)
-            elif k.strip() == "Socket(s)":
-                sockets = int(v)
-    except (OSError, ValueError, subprocess.SubprocessError):
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                core = v
+            elif not k and phys is not None:
+                cores.add((phys, core))
+                phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
         pass
-    physical = cores * sockets if cores and sockets else os.cpu_count() or 1
+    physical = len(cores) or os.cpu_count() or 1
     allowed = len(os.sched_getaffinity(0))
     omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     threads = min(physical, allowed, omp) if omp > 0 else min(physical, allowed)
@@ -192,18 +198,23 @@ def _profile_record(kernel_srcs, key):
 
 def hardware(torch):
     p = torch.cuda.get_device_properties(0)
-    hw = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None),
+    hw = {"gpu": p.name or "MI355X (gfx950)", "arch": getattr(p, "gcnArchName", None),
           "compute_units": p.multi_processor_count,
           "hbm_GiB": round(p.total_memory / 2 ** 30, 1),
           "rocm_hip": torch.version.hip, "torch": torch.__version__}
-    try:   # current and top shader clock as the driver reports them
-        import subprocess
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                             text=True, timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        hw["sclk"] = card.get("sclk clock speed:") or card.get("sclk")
-    except Exception:
-        hw["sclk"] = None
+    # shader clock levels from sysfs (the level marked '*' is the current one);
+    # read as a file, no tool is started
+    hw["sclk"] = None
+    try:
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            levels = [l.strip() for l in open(f) if l.strip()]
+            if levels:
+                cur = [l for l in levels if l.endswith("*")]
+                hw["sclk"] = {"current": cur[0] if cur else None, "levels": levels}
+                break
+    except OSError:
+        pass
     return hw
 
 
