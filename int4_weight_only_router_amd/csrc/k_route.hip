@@ -386,6 +386,69 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
     if (!s_last)
         return;
 
+    if constexpr (FUSE && !BIGE && TT == 1) {
+        if (E <= 64) {
+            // One token of at most 64 experts: wave 0 alone, lane e holding
+            // expert e, the selection and the sort in registers (same keys,
+            // ranks and softmax terms as the general path below).
+            if (wave != 0)
+                return;
+            const int e = lane;
+            const bool valid = e < E;
+            const float l = valid ? __hip_atomic_load(ws_logits + e, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.0f;
+            if (lane == 0)
+                __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t key = valid ? topk_key(l, e) : 0ull;
+            uint64_t *bkey = reinterpret_cast<uint64_t *>(smem);   // the 64 keys
+            bkey[lane] = key;
+            __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+            int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll
+            for (int j = 0; j < 64; j += 4) {
+                const uint4_t q = *reinterpret_cast<const uint4_t *>(bkey + j);
+                const uint4_t p = *reinterpret_cast<const uint4_t *>(bkey + j + 2);
+                r0 += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
+                r1 += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
+                r2 += (((uint64_t)p.y << 32) | p.x) > key ? 1 : 0;
+                r3 += (((uint64_t)p.w << 32) | p.z) > key ? 1 : 0;
+            }
+            const int rank = (r0 + r1) + (r2 + r3);
+            const bool sel = valid && rank < k;
+            // softmax over all E: the maximum is the logit ranked first
+            const int top = __ffsll((long long)__ballot(valid && rank == 0)) - 1;
+            const float m = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), top));
+            const float pe = valid ? expf(l - m) : 0.0f;
+            const float den = wave_sum_f32(pe);   // softmax denominator (order fixed, not pinned)
+            float p = pe / den;
+            if (flags & MOE_RENORM) {
+                const float ws = wave_sum_f32(sel ? p : 0.0f);
+                p = p / ws;
+            }
+            if (sel) {
+                idx_out[rank] = e;
+                w_out[rank] = p;
+            }
+            // the stable sort of k distinct experts of one token: position =
+            // selected experts of lower id, flat index = rank
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            const int off = __popcll(__ballot(sel) & below);
+            if (valid) {
+                counts[e] = sel ? 1 : 0;
+                offsets[e] = off;
+            }
+            if (lane == E - 1)
+                offsets[E] = k;
+            if (sel) {
+                perm[off] = rank;
+                inv_perm[rank] = off;
+            }
+            return;
+        }
+    }
+
     const size_t tsb = topk_scratch_bytes(E);
     float *lg = reinterpret_cast<float *>(smem);                      // [T][E]
     unsigned char *scr = smem + ((((size_t)TT * E * sizeof(float)) + 15) & ~(size_t)15);   // [T][tsb]

@@ -843,3 +843,49 @@ def test_layer_zero_point(cfg, T):
                       cfg.E, cfg.k, cfg.g, bias=bias, shared=sh, residual=res, fmt=O.FMT_ZP)
     assert np.array_equal(_np(b.topk_idx), ref["idx"])
     check_close(_np(out).astype(np.float64), ref["out_f64"], "zp layer %s T=%d" % (cfg.name, T))
+
+
+E33 = MI.MoEConfig(89, "h512_e33_k16", H=512, E=33, k=16, I=128, g=64)
+
+
+@pytest.mark.parametrize("cfg", [MI.TINY, MI.QWEN, E33, MI.OLMOE_DECODE, MI.E512],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("case", ["plain", "renorm", "ties", "zero"])
+def test_route_permute_one_token(cfg, case):
+    """One token through the fused route+sort (the decode path; up to 64
+    experts it selects and sorts in registers): routing, weights, counts,
+    offsets, permutation against the oracle, with renormalisation, exact ties
+    (duplicated router rows: lower index first) and a zero input (all logits
+    equal: experts 0..k-1)."""
+    say("route_permute one token %s %s" % (cfg.name, case))
+    T, k, E = 1, cfg.k, cfg.E
+    x = MI.gen_x(cfg, T, step=31)
+    wr = MI.gen_router(cfg)
+    if case == "ties":
+        wr[E - 1] = wr[1]
+        wr[E // 2] = wr[1]
+        wr[2] = wr[0]
+    if case == "zero":
+        x[:] = 0.0
+    b = MI.zipf_bias(cfg) if case != "zero" else None
+    renorm = case == "renorm"
+    outs = [torch.full((T, k), -7, dtype=torch.int32, device=DEV),
+            torch.full((T, k), -7.0, dtype=torch.float32, device=DEV),
+            torch.full((E,), -7, dtype=torch.int32, device=DEV),
+            torch.full((E + 1,), -7, dtype=torch.int32, device=DEV),
+            torch.full((k,), -7, dtype=torch.int32, device=DEV),
+            torch.full((k,), -7, dtype=torch.int32, device=DEV)]
+    wsb = M.moe_route_permute_workspace_bytes(T, k, E)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        M.moe_route_permute(f16(x), f16(wr), None if b is None else torch.from_numpy(b).to(DEV),
+                            T, cfg.H, E, k, M.MOE_RENORM if renorm else 0, *outs, ws, wsb)
+        torch.cuda.synchronize()
+        oi, ow, _ = O.route(x, wr, b, k, renorm)
+        assert np.array_equal(_np(outs[0]), oi)
+        assert np.max(np.abs(_np(outs[1]) - ow)) <= WTOL
+        for got, ref, name in zip(outs[2:], O.permute(oi, E), ("counts", "offsets", "perm", "inv")):
+            assert np.array_equal(_np(got), ref), name
+        assert int(_np(ws[:4].view(torch.int32))[0]) == 0
+    if case == "zero":
+        assert np.array_equal(oi[0], np.arange(k))
