@@ -103,24 +103,6 @@ struct W4Stage {
 template <int MF, bool ZP = false>
 constexpr size_t w4_lds_bytes() { return (size_t)W4_NS * W4Stage<MF, ZP>::BYTES; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void *g, unsigned char *l)
-{
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *g, unsigned char *l)
-{
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
-}
-
-// Waits until at most N vector-memory instructions of this wave are pending.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 template <int PER>
 __device__ __forceinline__ void wait_steps(int younger)   // younger in 0..3
 {

@@ -183,6 +183,27 @@ __device__ __forceinline__ float wave_sum_f32(float a)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Direct-to-LDS loads (global_load_lds): lane i's bytes land at the
+// wave-uniform LDS address l + i * size; completion is counted by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void *g, unsigned char *l)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, unsigned char *l)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
+}
+
+// Waits until at most N vector-memory instructions of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
     return (float)__builtin_bit_cast(f16, bits);
 }

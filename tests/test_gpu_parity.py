@@ -155,9 +155,17 @@ def test_route_permute_one_workspace_across_batch_sizes(cfg, Ts):
         assert int(_np(ws[:4].view(torch.int32))[0]) == 0
 
 
+H1024 = MI.MoEConfig(88, "h1024_e64", H=1024, E=64, k=6, I=128, g=64)
+
+
+# the fused launch (one token to a few), the one-workgroup router and the
+# register-tiled logits kernel up to 8200 tokens: H = 256, 512, 1024, 2048;
+# ragged T and E tails
 @pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 5), (MI.E512, 1),
                                    (MI.E512, 7), (MI.TINY, 16), (MI.OLMOE_DECODE, 64),
-                                   (MI.E512, 300)],
+                                   (MI.E512, 300), (MI.E512, 4096), (MI.OLMOE_DECODE, 4096),
+                                   (MI.QWEN, 4100), (MI.TINY, 8200), (E1000, 300), (E200, 1300),
+                                   (H1024, 4096)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_router_logits_pinned_order(cfg, T):
     """The logits the router kernels leave in their workspace equal the
