@@ -42,14 +42,15 @@ def log(msg):
 
 
 REGIMES = {"auto": 0, "decode": 1, "batched": 2, "small": 3}   # MOE_REGIME_* values
+FMTS = {"sym": 0, "zp": 1}                                      # MOE_FMT_* values
 
 
-def build_layers(cfg, layers, dev, torch, M):
+def build_layers(cfg, layers, dev, torch, M, fmt=0):
     """Device-resident layers: weights drawn by moe_inputs (numpy), quantised
-    and prepacked by the library's kernels."""
+    and prepacked by the library's kernels (fmt: MOE_FMT_SYM or MOE_FMT_ZP)."""
     import moe_inputs as MI
     from int4_weight_only_router_amd.layer import MoELayer, blob_table
-    _, total = M.moe_blob_layout(cfg.H, cfg.I, cfg.g)
+    _, total = M.moe_blob_layout_fmt(cfg.H, cfg.I, cfg.g, fmt)
     out = []
     for l in range(layers):
         t0 = time.time()
@@ -65,14 +66,14 @@ def build_layers(cfg, layers, dev, torch, M):
                 wu[i].copy_(torch.from_numpy(u_))
                 wd[i].copy_(torch.from_numpy(d_))
             canon = torch.empty((n, total), dtype=torch.uint8, device=dev)
-            M.moe_quantize_experts(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, canon)
-            M.moe_prepack_experts(canon, n, cfg.H, cfg.I, cfg.g, blobs[b0:b0 + n])
+            M.moe_quantize_experts_fmt(wg, wu, wd, n, cfg.H, cfg.I, cfg.g, fmt, canon)
+            M.moe_prepack_experts_fmt(canon, n, cfg.H, cfg.I, cfg.g, fmt, blobs[b0:b0 + n])
             del wg, wu, wd, canon
         router = torch.from_numpy(MI.gen_router(cfg, l)).to(dev)
         b = MI.zipf_bias(cfg, l)
         bias = None if b is None else torch.from_numpy(b).to(dev)
         lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, router, blob_table(blobs), bias,
-                       device=dev)
+                       device=dev, fmt=fmt)
         lay._blobs = blobs
         out.append(lay)
         torch.cuda.synchronize()
@@ -224,11 +225,12 @@ def run_decode(args, torch, M):
     cfg = MI.OLMOE_DECODE
     dev = "cuda:0"
     L = cfg.layers
-    lays, blob_bytes = build_layers(cfg, L, dev, torch, M)
+    fmt = FMTS[getattr(args, "fmt", "sym")]
+    lays, blob_bytes = build_layers(cfg, L, dev, torch, M, fmt)
     K, W = args.steps, args.warmup
     xs = torch.from_numpy(np.concatenate([MI.gen_x(cfg, 1, step=s) for s in range(K + W)])).to(dev)
     bufs = [lay.buffers(1) for lay in lays]
-    assert bufs[0].regime & ~M.MOE_Y_TOKEN_ORDER == M.MOE_REGIME_DECODE
+    assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_W4_ZERO_POINT) == M.MOE_REGIME_DECODE
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
 
     def step_from(x):
@@ -300,12 +302,14 @@ def run_decode(args, torch, M):
         "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4-weights/f16-activations/f32-accumulate",
+        "dtype": "int4-weights/f16-activations/f32-accumulate" if fmt == 0 else
+                 "int4-zero-point-weights/f16-activations/f32-accumulate",
         "data": "synthetic (seeded numpy draws: x ~ N(0,1), router ~ N(0,0.02), experts "
-                "~ N(0,0.02) quantised INT4 g128)",
+                "~ N(0,0.02) quantised INT4 g128%s)" % ("" if fmt == 0 else ", zero point per group"),
         "config": {"workload": "olmoe_decode: 16 MoE layers H=2048 E=64 top-8 I=1024 g=128, "
                                "1 token/step, all experts resident",
-                   "layers": L, "tokens_per_step": 1, "graph": bool(graph)},
+                   "layers": L, "tokens_per_step": 1, "graph": bool(graph),
+                   "format": "sym" if fmt == 0 else "zp"},
         "layer_tokens_per_s": round(K * L / elapsed, 1),
         "per_layer_us": {"route+permute": round(t_route * 1e3, 2),
                          "expert_ffn": round(t_ffn * 1e3, 2),
@@ -368,7 +372,7 @@ def run_batched(args, torch, M, cfg):
     import moe_inputs as MI
     from int4_weight_only_router_amd.layer import MoELayer, blob_table
     dev = "cuda:0"
-    lays, blob_bytes = build_layers(cfg, 1, dev, torch, M)
+    lays, blob_bytes = build_layers(cfg, 1, dev, torch, M, FMTS[getattr(args, "fmt", "sym")])
     base = lays[0]
     shared = gate = None
     if cfg.Is:
@@ -387,7 +391,7 @@ def run_batched(args, torch, M, cfg):
         bl = base._blobs.clone()
         sh = None if shared is None else tuple(w.clone() for w in shared)
         lay = MoELayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, base.router, blob_table(bl), base.bias,
-                       sh, device=dev, shared_gate=gate, overlap_shared=overlap)
+                       sh, device=dev, shared_gate=gate, overlap_shared=overlap, fmt=base.fmt)
         lay._blobs = bl
         copies.append(lay)
     base.shared, base.shared_gate, base.overlap_shared = shared, gate, overlap
@@ -431,7 +435,7 @@ def run_batched(args, torch, M, cfg):
                  + 2 * T * cfg.H * 2 + (cfg.H * 2 if cfg.shared_gate else 0))
         tf = f_routed / (us["expert_ffn"] * 1e-6) / 1e12
         ffn_bytes = touched * blob_bytes
-        reg = b.regime & ~M.MOE_Y_TOKEN_ORDER
+        reg = b.regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_W4_ZERO_POINT)
         line = {"T": T, "regime": {1: "decode", 2: "batched", 3: "small"}.get(reg, reg),
                 "experts_touched": touched, "max_rows_per_expert": int(counts.max()),
                 "us": {k: round(v, 1) for k, v in us.items()},
@@ -448,6 +452,7 @@ def run_batched(args, torch, M, cfg):
         lines.append(line)
         log(str(line))
     return {"workload": cfg.name, "weight_copies": nc, "regime": args.regime,
+            "format": getattr(args, "fmt", "sym"),
             "config": {"H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I, "g": cfg.g, "Is": cfg.Is,
                        "shared_gate": cfg.shared_gate, "zipf_s": cfg.zipf_s,
                        "shared_on_side_stream": overlap},
@@ -680,6 +685,9 @@ def main():
     ap.add_argument("--workload", choices=["decode", "batched", "e512", "qwen", "partial", "copy"],
                     default="decode")
     ap.add_argument("--T", default="", help="batched/e512/qwen: comma-separated batch sizes")
+    ap.add_argument("--fmt", choices=["sym", "zp"], default="sym",
+                    help="expert blob format: symmetric INT4, or INT4 with a zero point per "
+                         "group (decode/batched/e512/qwen)")
     ap.add_argument("--regime", choices=sorted(REGIMES), default="auto",
                     help="batched/e512/qwen: routed-FFN regime (auto: the library's choice)")
     ap.add_argument("--blocks", type=int, default=3)
