@@ -233,12 +233,20 @@ def run_decode(args, torch, M):
     assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_W4_ZERO_POINT) == M.MOE_REGIME_DECODE
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
 
+    fuse = not getattr(args, "no_fuse", False)
+
     def step_from(x):
+        # with fuse, layer l's combine and layer l+1's route + permute are
+        # one launch (moe_combine_route_permute); the same bits either way
         for l, lay in enumerate(lays):
             out = act[l & 1]
-            lay.route_permute(x, bufs[l])
+            if l == 0 or not fuse:
+                lay.route_permute(x, bufs[l])
             lay.experts(x, bufs[l])
-            lay.combine(bufs[l], residual=x, out=out)
+            if fuse and l + 1 < L:
+                lay.combine_route_next(bufs[l], lays[l + 1], bufs[l + 1], residual=x, out=out)
+            else:
+                lay.combine(bufs[l], residual=x, out=out)
             x = out
         return x
 
@@ -289,6 +297,10 @@ def run_decode(args, torch, M):
     t_comb = _graph_time(torch, lambda: [lay.combine(bufs[l], residual=x0, out=act[0])
                                          for l, lay in enumerate(lays)], reps) / L
     touched = [int((b.counts.cpu().numpy() > 0).sum()) for b in bufs]
+    t_cr = _graph_time(torch, lambda: [lays[l].combine_route_next(bufs[l], lays[l + 1],
+                                                                  bufs[l + 1], residual=x0,
+                                                                  out=act[0])
+                                       for l in range(L - 1)], reps) / (L - 1)
     ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
     achieved = ffn_bytes / (t_ffn * 1e-3) / 1e9
     ms_step = elapsed * 1e3 / K
@@ -309,11 +321,12 @@ def run_decode(args, torch, M):
         "config": {"workload": "olmoe_decode: 16 MoE layers H=2048 E=64 top-8 I=1024 g=128, "
                                "1 token/step, all experts resident",
                    "layers": L, "tokens_per_step": 1, "graph": bool(graph),
-                   "format": "sym" if fmt == 0 else "zp"},
+                   "format": "sym" if fmt == 0 else "zp", "combine_route_fused": fuse},
         "layer_tokens_per_s": round(K * L / elapsed, 1),
         "per_layer_us": {"route+permute": round(t_route * 1e3, 2),
                          "expert_ffn": round(t_ffn * 1e3, 2),
-                         "combine": round(t_comb * 1e3, 2)},
+                         "combine": round(t_comb * 1e3, 2),
+                         "combine+next_route": round(t_cr * 1e3, 2)},
         "roofline": {"kernel": "ffn_decode_kernel (moe_expert_ffn_w4a16, DECODE)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -698,6 +711,8 @@ def main():
                     help="partial: decayed-counter eviction, or a profile-pinned resident set")
     ap.add_argument("--profile-prompts", type=int, default=4,
                     help="partial --policy pinned: prompts of the profile pass")
+    ap.add_argument("--no-fuse", dest="no_fuse", action="store_true", default=False,
+                    help="decode: separate combine and next-layer route launches")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)

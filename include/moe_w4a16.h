@@ -190,9 +190,10 @@ int moe_unpack_expert_host(const void *src, int H, int I, int group, int fmt, vo
  *                 (0 for T <= 8, where ws may be NULL; above that it holds the
  *                 T x E fp32 logits between the logit and top-k launches;
  *                 contents need no initialisation); MOE_ENOMEM if too small
- * Logits are fp32 in a fixed summation order (chunks of 8 elements of H go
- * to partial (chunk mod 64) in increasing order, partials combined by an xor
- * butterfly 32,16,8,4,2,1), so the indices are reproducible bit for bit.
+ * Logits are fp32 in a fixed summation order (H in chunks of 8 elements;
+ * partial j takes the j-th run of q = ceil((H/8)/64) consecutive chunks,
+ * element by element; the 64 partials combined by an xor butterfly
+ * 32,16,8,4,2,1), so the indices are reproducible bit for bit.
  * T = 0 is a no-op.
  */
 size_t moe_route_workspace_bytes(int T, int E);
@@ -378,6 +379,43 @@ int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *i
                       const float *topk_w, const float *shared_f32, const void *x_f16,
                       const void *shared_gate_w_f16, const void *residual_f16, int T, int H,
                       int k, void *out_f16, hipStream_t stream);
+
+/*
+ * Combine of one layer fused with route + permute of the next (Horizon
+ * RunMap "03 / Arquitetura": the experts' results return to the model, whose
+ * next layer's router then selects its experts; the pages run 16 such layers
+ * per token).  Exactly the two calls it stands for, bit for bit:
+ *   moe_combine (shared_gate_w_f16 NULL) or moe_combine_gated (non-NULL:
+ *     then shared_f32 and x_f16, the layer's input, are required) with y,
+ *     y_dtype, y_slices, inv_perm, topk_w, shared_f32, residual_f16, T, H, k,
+ *     writing out_f16;
+ *   then moe_route_permute(out_f16, w_router_f16, logit_bias, T, H, E, k_next,
+ *     flags, topk_idx, topk_w_next, counts, offsets, perm, inv_perm_next).
+ * One launch when T = 1, E <= 64 and y holds fp32 slices (y_slices > 1, the
+ * decode layout); otherwise the two calls run in turn on `stream`.
+ *   ws  device workspace of moe_combine_route_permute_workspace_bytes(T,
+ *       k_next, E) bytes, zero-filled before the first call
+ *       (moe_workspace_clear).  The fused launch leaves its first 256 bytes
+ *       alone and passes the next layer's logit partials from block to block
+ *       through tagged words after them (the selecting block polls them; no
+ *       other block waits), with a call counter at the end; so the same
+ *       workspace may also serve moe_route_permute, whose ticket lives in the
+ *       first 256 bytes.
+ * The layer's routing arrays (topk_w, inv_perm) and the next layer's
+ * (topk_w_next, inv_perm_next) may be the same arrays: every read of the
+ * former precedes every write of the latter.  out_f16 may alias residual_f16
+ * but not x_f16.  Errors: those of the two calls, checked before any launch;
+ * MOE_ENOMEM for a short workspace.
+ */
+size_t moe_combine_route_permute_workspace_bytes(int T, int k_next, int E);
+int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                              const float *topk_w, const float *shared_f32, const void *x_f16,
+                              const void *shared_gate_w_f16, const void *residual_f16, int T,
+                              int H, int k, void *out_f16, const void *w_router_f16,
+                              const float *logit_bias, int E, int k_next, unsigned flags,
+                              int32_t *topk_idx, float *topk_w_next, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv_perm_next, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------- expert slot pool */
 /*

@@ -19,7 +19,9 @@ __all__ = [
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "PoolConfig", "PoolStats", "PoolLayerArgs",
+    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
+    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "PoolConfig",
+    "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
     "moe_pool_destroy",
@@ -43,7 +45,8 @@ EXPORTS = [
     "moe_permute", "moe_route_permute_workspace_bytes", "moe_route_permute",
     "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
-    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated", "moe_pool_create",
+    "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
+    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "moe_pool_create",
     "moe_pool_prepare",
     "moe_pool_layer_forward", "moe_pool_pin",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
@@ -119,6 +122,10 @@ def _declare(L):
         "moe_combine": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "moe_combine_gated": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp,
                                     vp]),
+        "moe_combine_route_permute_workspace_bytes": (sz, [i32, i32, i32]),
+        "moe_combine_route_permute": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            vp, vp, vp, i32, i32, C.c_uint, vp, vp, vp, vp, vp,
+                                            vp, vp, sz, vp]),
         "moe_pool_create": (i32, [C.POINTER(PoolConfig), vp, C.POINTER(vp)]),
         "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
         "moe_pool_layer_forward": (i32, [vp, i32, C.POINTER(PoolLayerArgs), vp,
@@ -325,6 +332,21 @@ def moe_combine_gated(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,
     return _check(lib().moe_combine_gated(_p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w),
                                           _p(shared_f32), _p(x_f16), _p(gate_w_f16),
                                           _p(residual_f16), T, H, k, _p(out_f16), _s(stream)))
+
+
+def moe_combine_route_permute_workspace_bytes(T, k_next, E):
+    return lib().moe_combine_route_permute_workspace_bytes(T, k_next, E)
+
+
+def moe_combine_route_permute(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,
+                              gate_w_f16, residual_f16, T, H, k, out_f16, w_router, logit_bias,
+                              E, k_next, flags, topk_idx, topk_w_next, counts, offsets, perm,
+                              inv_perm_next, ws=None, ws_bytes=0, stream=None):
+    return _check(lib().moe_combine_route_permute(
+        _p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w), _p(shared_f32), _p(x_f16),
+        _p(gate_w_f16), _p(residual_f16), T, H, k, _p(out_f16), _p(w_router), _p(logit_bias),
+        E, k_next, flags, _p(topk_idx), _p(topk_w_next), _p(counts), _p(offsets), _p(perm),
+        _p(inv_perm_next), _p(ws), ws_bytes, _s(stream)))
 
 
 def moe_pool_create(cfg: PoolConfig, pinned_src_ptrs):

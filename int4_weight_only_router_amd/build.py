@@ -19,9 +19,10 @@ LIB = os.path.join(PKG, "libmoe_w4a16.so")
 POOL_HOST_LIB = os.path.join(PKG, "libmoe_pool_host.so")
 
 HIP_SOURCES = ["moe_api.cpp", "k_route.hip", "k_permute.hip", "k_ffn_decode.hip", "k_shared_gemv.hip",
-               "k_ffn_grouped.hip", "k_ffn_small.hip", "k_combine.hip", "k_quant.hip", "pool_hip.cpp",
+               "k_ffn_grouped.hip", "k_ffn_small.hip", "k_combine.hip", "k_combine_route.hip", "k_quant.hip", "pool_hip.cpp",
                "prepack_host.cpp"]
-HEADERS = ["moe_common.h", "k_w4_frag.h", "k_decode_frag.h", "k_sort_common.h", "pool_core.h"]
+HEADERS = ["moe_common.h", "k_w4_frag.h", "k_decode_frag.h", "k_sort_common.h", "k_combine_tile.h",
+           "pool_core.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [

@@ -11,7 +11,7 @@
 // Gated shared expert (the 60-expert top-4 model family of the Horizon RunMap
 // technical preview, results table): the shared term becomes G_t * s[t,c] with
 // G_t = sigmoid(x_t . wsg), the dot taken in fp32 by the block that needs it.
-#include "moe_common.h"
+#include "k_combine_tile.h"
 
 namespace moe {
 
@@ -39,109 +39,18 @@ __device__ inline float shared_gate_256(const f16 *__restrict__ xt, const f16 *_
     return 1.0f / (1.0f + expf(-a));
 }
 
-// Shared-expert gate of one token formed by one wave: fp32 dot of x_t with wsg
-// (8 columns per lane per pass), summed across the wave, then the sigmoid.
-// Every lane returns the same value.
-__device__ inline float shared_gate_wave(const f16 *__restrict__ xt, const f16 *__restrict__ wsg,
-                                         int H, int lane)
-{
-    float a = 0.0f;
-#pragma unroll 4
-    for (int c = lane * 8; c < H; c += 64 * 8) {
-        const half8_t xv = *reinterpret_cast<const half8_t *>(xt + c);
-        const half8_t wv = *reinterpret_cast<const half8_t *>(wsg + c);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            a = __builtin_fmaf((float)xv[m], (float)wv[m], a);
-    }
-    a = wave_sum_f32(a);
-    return 1.0f / (1.0f + expf(-a));
-}
-
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
-// Decode partials: fp32 y [S][T*k][H].  Block = CPB columns of one token, 256 threads as
-// NSG = 256 / (4 CPB) slice groups x 16 expert slots x CPB/4 column quads.
-// Thread (g, j, q) sums, in slice order, 4 columns of expert slot j over the
-// g-th contiguous share of the S slices with 16-byte loads; the first CPB
-// threads then form Y_j = share_0 + share_1 + ... (group order) and fold
-// w[t,j] Y_j in j order, then the shared and residual terms.  GATED: the
-// block's last wave forms the gate after its own loads (with CPB = 32 and
-// k <= 8 it has none, so the gate's loads overlap the slice loads).
-template <int CPB, bool GATED>
+// Decode partials: fp32 y [S][T*k][H].  Block = 32 consecutive columns of one
+// token (combine_tile).
+template <bool GATED>
 __global__ __launch_bounds__(256) void combine_slices_kernel(
     const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
     const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
     const f16 *__restrict__ wsg, const f16 *residual, int T, int H, int k, f16 *out)
 {
-    constexpr int QPB = CPB / 4;             // column quads per block
-    constexpr int NSG = 256 / (16 * QPB);    // slice groups
-    constexpr int SB = 16;                   // loads in flight per batch
-    __shared__ float part[NSG][16][CPB + 1];
-    __shared__ float gate_s;
-    const int q = threadIdx.x % QPB;
-    const int j = (threadIdx.x / QPB) & 15;
-    const int g = threadIdx.x / (16 * QPB);
-    const int t = blockIdx.y;
-    const int c0 = blockIdx.x * CPB + q * 4;
-    const size_t ntk = (size_t)T * k;
-    const int share = (S + NSG - 1) / NSG;
-    const int sb = g * share, se = min(S, sb + share);
-    if (j < k && c0 < H) {
-        const size_t f = (size_t)t * k + j;
-        const size_t p = inv_perm ? (size_t)inv_perm[f] : f;   // NULL: y in token order
-        const float *src = y + p * H + c0;
-        const size_t stride = ntk * H;
-        float4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s0 = sb; s0 < se; s0 += SB) {
-            float4_t vb[SB];
-#pragma unroll
-            for (int i = 0; i < SB; ++i)
-                vb[i] = (s0 + i < se) ? *reinterpret_cast<const float4_t *>(
-                                            src + (size_t)(s0 + i) * stride)
-                                      : float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < SB; ++i)
-                if (s0 + i < se) {
-                    v[0] += vb[i][0];
-                    v[1] += vb[i][1];
-                    v[2] += vb[i][2];
-                    v[3] += vb[i][3];
-                }
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            part[g][j][q * 4 + m] = v[m];
-    }
-    if constexpr (GATED) {
-        if (threadIdx.x >= 192) {
-            const float gv = shared_gate_wave(x + (size_t)t * H, wsg, H, threadIdx.x & 63);
-            if (threadIdx.x == 192)
-                gate_s = gv;
-        }
-    }
-    __syncthreads();
-    const int c = blockIdx.x * CPB + threadIdx.x;
-    if (threadIdx.x < CPB && c < H) {
-        float acc = 0.0f;
-        for (int jj = 0; jj < k; ++jj) {
-            float yj = part[0][jj][threadIdx.x];
-#pragma unroll
-            for (int gg = 1; gg < NSG; ++gg)
-                yj += part[gg][jj][threadIdx.x];
-            const float term = w[(size_t)t * k + jj] * yj;
-            acc += term;
-        }
-        if (shared) {
-            float gate = 1.0f;
-            if constexpr (GATED)
-                gate = gate_s;
-            acc += GATED ? gate * shared[(size_t)t * H + c] : shared[(size_t)t * H + c];
-        }
-        if (residual)
-            acc += (float)residual[(size_t)t * H + c];
-        out[(size_t)t * H + c] = (f16)acc;
-    }
+    __shared__ CombineTileSmem sm;
+    const int base = blockIdx.x * 32;
+    combine_tile<GATED>(y, S, inv_perm, w, shared, x, wsg, residual, T, blockIdx.y, H, k,
+                        min(32, H - base), ContigCols{base}, out, sm);
 }
 
 // 8 consecutive columns of one y row, loaded as one (fp16) or two (fp32)
@@ -309,14 +218,13 @@ int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, c
     const bool gated = gw != nullptr;
     f16 *o = static_cast<f16 *>(out);
     if (y_dtype == MOE_DTYPE_F32 && S > 1) {
-        constexpr int CPB = 32;
-        dim3 grid((H + CPB - 1) / CPB, T);
+        dim3 grid((H + 31) / 32, T);
         if (gated)
-            hipLaunchKernelGGL((combine_slices_kernel<CPB, true>), grid, dim3(256), 0, s,
+            hipLaunchKernelGGL((combine_slices_kernel<true>), grid, dim3(256), 0, s,
                                static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
                                T, H, k, o);
         else
-            hipLaunchKernelGGL((combine_slices_kernel<CPB, false>), grid, dim3(256), 0, s,
+            hipLaunchKernelGGL((combine_slices_kernel<false>), grid, dim3(256), 0, s,
                                static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
                                T, H, k, o);
         MOE_LAUNCH_CHECK("combine_slices_kernel");

@@ -1,0 +1,176 @@
+// k_combine_route.hip -- the combine of one decode layer fused with the
+// router, top-k and sort of the next layer (one token, at most 64 experts).
+//
+// Two stacked layers meet at x_{l+1} = combine_l(...): the next layer's
+// router needs every column of it, and the combine of a decode token is a
+// few microseconds of latency-bound reads of the fp32 partials.  One launch
+// does both.  Block j (64 blocks, or H/8 when fewer) owns the 8 q consecutive
+// columns of the q-chunk run j (q = ceil((H/8)/64)) -- exactly the chunks
+// that make up partial number j of every logit in the pinned order (Horizon
+// RunMap "08 / Comportamento do modelo": routing in FP32 with explicit
+// roundings; the order itself is this library's reading).  At H = 2048 that
+// is 32 columns, whole 128-byte lines of every partial row.  It
+//  1. combines its columns of x_{l+1} (combine_tile: the plain combine's
+//     arithmetic, so the bits equal moe_combine's) and stores them;
+//  2. with wave 0, lane e = expert e, accumulates partial j of every logit
+//     from the fp16 x_{l+1} columns it just rounded, element by element in
+//     chunk order, as the one-launch router does, and publishes the 64
+//     partials as tagged words: one 64-bit store each, the value in the low
+//     half and this call's tag in the high half, so a reader that sees the
+//     tag sees the value (no acknowledgement, fence or ticket needed);
+//  3. block 0 then polls the 64 x 64 tagged words until every tag is this
+//     call's, folds each logit's 64 partials in the butterfly order of the
+//     pinned logit sum (pinned_fold64), adds the bias, selects, weights and
+//     sorts as moe_route_permute does for one token (one_token_select), and
+//     advances the call counter.
+// Only block 0 waits, and only for blocks that never wait, so the wait ends
+// whenever one more block can run beside it; a poll limit bounds it anyway.
+// The tag is a quiet-NaN pattern carrying (call counter + 1) in its low 22
+// bits: no finite value left in the region by another call can match it.
+// The result is bit-identical to moe_combine followed by moe_route_permute.
+#include "k_combine_tile.h"
+#include "k_sort_common.h"
+
+namespace moe {
+
+constexpr int CR_MAX_POLLS = 1 << 20;   // far beyond any wait for co-running blocks
+
+template <int H, bool GATED>
+__global__ __launch_bounds__(256) void combine_route_kernel(
+    const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
+    const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
+    const f16 *__restrict__ wsg, const f16 *residual, int k, f16 *out,
+    const f16 *__restrict__ wr, const float *__restrict__ bias, int E, int kn, unsigned flags,
+    uint64_t *xchg, unsigned *calls, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv_perm_out)
+{
+    constexpr int NCH = H / 8;               // 8-column chunks
+    constexpr int NCL = (NCH + 63) / 64;     // chunks per partial (all present: H % 512 == 0
+                                             // or H = 256, where blocks j < 32 hold one)
+    __shared__ CombineTileSmem sm;
+    __shared__ __align__(16) f16 xs[32];
+    __shared__ __align__(16) uint64_t keys[64];
+
+    const int j = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+
+    // the call counter, and the router chunks j q + m of expert `lane` (lanes
+    // past E read row E - 1; block 0 ignores them), requested first.  Every
+    // wave issues them (only wave 0 uses them): a branch here would make the
+    // compiler wait for them before the slice loads.
+    const unsigned c = __hip_atomic_load(calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint4_t wv[NCL];
+    {
+        const uint4_t *row =
+            reinterpret_cast<const uint4_t *>(wr + (size_t)min(lane, E - 1) * H);
+#pragma unroll
+        for (int m = 0; m < NCL; ++m)
+            wv[m] = row[j * NCL + m];
+    }
+    const ContigCols cols{8 * NCL * j};
+    const f16 o = combine_tile<GATED>(y, S, inv_perm, w, shared, x, wsg, residual, 1, 0, H, k,
+                                      8 * NCL, cols, nullptr, sm);
+    if (wave != 0)
+        return;
+    if (lane < 8 * NCL) {
+        xs[lane] = o;
+        out[cols(lane)] = o;
+    }
+    __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+    const unsigned tag = 0x7FC00000u | ((c + 1u) & 0x3FFFFFu);
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCL; ++m) {
+        const half8_t xh = *reinterpret_cast<const half8_t *>(xs + 8 * m);
+        const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc = __builtin_fmaf((float)xh[i], (float)wh[i], acc);
+    }
+    __hip_atomic_store(xchg + j * 64 + lane,
+                       ((uint64_t)tag << 32) | __builtin_bit_cast(unsigned, acc),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (j != 0)
+        return;
+
+    // block 0: lane e gathers the 64 partials of expert e's logit (partial
+    // jj >= gridDim.x has no chunk and is zero, as in the one-launch router)
+    const int nb = gridDim.x;
+    float p[64];
+    for (int it = 0; it < CR_MAX_POLLS; ++it) {
+        bool mine = true;
+#pragma unroll
+        for (int jj = 0; jj < 64; ++jj) {
+            const uint64_t q = __hip_atomic_load(xchg + min(jj, nb - 1) * 64 + lane,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            p[jj] = jj < nb ? __builtin_bit_cast(float, (unsigned)q) : 0.0f;
+            mine = mine && (unsigned)(q >> 32) == tag;
+        }
+        if (__ballot(!mine) == 0)
+            break;
+    }
+    float l = pinned_fold64(p);
+    if (bias)
+        l = l + (lane < E ? bias[lane] : 0.0f);
+    one_token_select(l, E, kn, flags, keys, idx_out, w_out, counts, offsets, perm, inv_perm_out,
+                     lane);
+    if (lane == 0)
+        __hip_atomic_store(calls, tag & 0x3FFFFFu, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ws: [0, 256) the routers' ticket (not touched here), then 64 x 64 tagged
+// words, then the call counter.
+constexpr size_t CR_XCHG_OFF = 256;
+constexpr size_t CR_CALLS_OFF = CR_XCHG_OFF + (size_t)64 * 64 * sizeof(uint64_t);
+size_t combine_route_ws_bytes() { return CR_CALLS_OFF + 256; }
+
+template <int H, bool GATED>
+static void launch_cr(const float *y, int S, const int32_t *inv_perm, const float *w,
+                      const float *shared, const f16 *x, const f16 *wsg, const f16 *residual,
+                      int k, f16 *out, const f16 *wr, const float *bias, int E, int kn,
+                      unsigned flags, void *ws, int32_t *idx, float *wo, int32_t *counts,
+                      int32_t *offsets, int32_t *perm, int32_t *inv_perm_out, hipStream_t s)
+{
+    char *base = static_cast<char *>(ws);
+    uint64_t *xchg = reinterpret_cast<uint64_t *>(base + CR_XCHG_OFF);
+    unsigned *calls = reinterpret_cast<unsigned *>(base + CR_CALLS_OFF);
+    const int blocks = H / 8 < 64 ? H / 8 : 64;
+    hipLaunchKernelGGL((combine_route_kernel<H, GATED>), dim3(blocks), dim3(256), 0, s, y, S,
+                       inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E, kn, flags,
+                       xchg, calls, idx, wo, counts, offsets, perm, inv_perm_out);
+}
+
+// T = 1, E <= 64, fp32 decode partials; the caller has checked the shapes.
+int launch_combine_route(const float *y, int S, const int32_t *inv_perm, const float *w,
+                         const float *shared, const void *x, const void *gate_w,
+                         const void *residual, int H, int k, void *out, const void *wr,
+                         const float *bias, int E, int kn, unsigned flags, void *ws, int32_t *idx,
+                         float *wo, int32_t *counts, int32_t *offsets, int32_t *perm,
+                         int32_t *inv_perm_out, hipStream_t s)
+{
+    const f16 *xh = static_cast<const f16 *>(x), *gh = static_cast<const f16 *>(gate_w);
+    const f16 *rh = static_cast<const f16 *>(residual), *wh = static_cast<const f16 *>(wr);
+    f16 *oh = static_cast<f16 *>(out);
+#define MOE_CR(HH)                                                                              \
+    if (gh)                                                                                     \
+        launch_cr<HH, true>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn,      \
+                            flags, ws, idx, wo, counts, offsets, perm, inv_perm_out, s);        \
+    else                                                                                        \
+        launch_cr<HH, false>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn,     \
+                             flags, ws, idx, wo, counts, offsets, perm, inv_perm_out, s);
+    switch (H) {
+    case 256: MOE_CR(256) break;
+    case 512: MOE_CR(512) break;
+    case 1024: MOE_CR(1024) break;
+    case 2048: MOE_CR(2048) break;
+    default: return set_error(MOE_EUNSUPPORTED, "combine_route: H=%d not instantiated", H);
+    }
+#undef MOE_CR
+    MOE_LAUNCH_CHECK("combine_route_kernel");
+    return MOE_OK;
+}
+
+}  // namespace moe

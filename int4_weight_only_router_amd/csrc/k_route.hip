@@ -5,9 +5,10 @@
 // work on each token; "08 / Comportamento do modelo": routing stays outside
 // INT4 and accumulation is FP32 with explicit roundings.  The pages leave the
 // rest open; this kernel fixes it as follows.
-//  * Logit l[t,e] = sum_h x[t,h] Wr[e,h] in fp32 in a pinned order: chunk c
-//    (8 consecutive h) is accumulated, element by element, into partial
-//    number (c mod 64), chunks in increasing c; the 64 partials are combined
+//  * Logit l[t,e] = sum_h x[t,h] Wr[e,h] in fp32 in a pinned order: H is cut
+//    into chunks of 8 and the chunks into 64 runs of q = ceil((H/8)/64)
+//    consecutive chunks (NCL below); run j is accumulated, element by
+//    element, into partial number j; the 64 partials are combined
 //    by an xor butterfly with strides 32,16,8,4,2,1.  Partial j lives in lane
 //    j of the wave that owns (t, e), so the butterfly is a lane shuffle.
 //    fp16 x fp16 products are exact in fp32, hence fma and mul+add agree and
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
         const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane + 64 * m;
+            const int c = lane * NCL + m;
             dst[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
         }
     };
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
             acc[tt] = 0.0f;
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane + 64 * m;
+            const int c = lane * NCL + m;
             if (c < NCH) {
                 const half8_t wh = __builtin_bit_cast(half8_t, cur[m]);
 #pragma unroll
@@ -137,10 +138,10 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
 // Batches above 8 tokens: logits and top-k in two launches.
 //
 // route_logits_kernel: each wave computes an 8-token x 8-expert tile of
-// logits.  Lane j owns partial j of all 64 logits (chunks c = j, j+64, ...,
+// logits.  Lane j owns partial j of all 64 logits (chunks c = jq .. jq+q-1,
 // elements in order, acc = fma(x, w, acc) with exact fp16 products), reading
 // its 16-byte slices of the 8 activation rows and the 8 router rows straight
-// from memory (consecutive lanes read consecutive 16-byte slices of a row).
+// from memory (a wave's loads of one chunk step cover a row's 64 runs).
 // The 64 x 64 partials then go through LDS so that lane l holds the 64
 // partials of logit l and folds them in registers in the butterfly's order
 // (a_j + a_(j+32), then +16, ... +1): the same additions, operand for operand,
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(RL_WAVES * 64) void route_logits_kernel(
             acc[t][i] = 0.0f;
 #pragma unroll
     for (int m = 0; m < NCL; ++m) {
-        const int c = lane + 64 * m;
+        const int c = lane * NCL + m;
         if (c < NCH) {
             half8_t xv[8], wv[8];
 #pragma unroll
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
         const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane + 64 * m;
+            const int c = lane * NCL + m;
             wv[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
         }
         const uint4_t *src = reinterpret_cast<const uint4_t *>(x);
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
             acc[tt] = 0.0f;
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane + 64 * m;
+            const int c = lane * NCL + m;
             if (c < NCH) {
                 const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
 #pragma unroll
@@ -393,58 +394,13 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
             // ranks and softmax terms as the general path below).
             if (wave != 0)
                 return;
-            const int e = lane;
-            const bool valid = e < E;
-            const float l = valid ? __hip_atomic_load(ws_logits + e, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0.0f;
+            const float l = lane < E ? __hip_atomic_load(ws_logits + lane, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.0f;
             if (lane == 0)
                 __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t key = valid ? topk_key(l, e) : 0ull;
-            uint64_t *bkey = reinterpret_cast<uint64_t *>(smem);   // the 64 keys
-            bkey[lane] = key;
-            __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
-            int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-#pragma unroll
-            for (int j = 0; j < 64; j += 4) {
-                const uint4_t q = *reinterpret_cast<const uint4_t *>(bkey + j);
-                const uint4_t p = *reinterpret_cast<const uint4_t *>(bkey + j + 2);
-                r0 += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
-                r1 += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
-                r2 += (((uint64_t)p.y << 32) | p.x) > key ? 1 : 0;
-                r3 += (((uint64_t)p.w << 32) | p.z) > key ? 1 : 0;
-            }
-            const int rank = (r0 + r1) + (r2 + r3);
-            const bool sel = valid && rank < k;
-            // softmax over all E: the maximum is the logit ranked first
-            const int top = __ffsll((long long)__ballot(valid && rank == 0)) - 1;
-            const float m = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), top));
-            const float pe = valid ? expf(l - m) : 0.0f;
-            const float den = wave_sum_f32(pe);   // softmax denominator (order fixed, not pinned)
-            float p = pe / den;
-            if (flags & MOE_RENORM) {
-                const float ws = wave_sum_f32(sel ? p : 0.0f);
-                p = p / ws;
-            }
-            if (sel) {
-                idx_out[rank] = e;
-                w_out[rank] = p;
-            }
-            // the stable sort of k distinct experts of one token: position =
-            // selected experts of lower id, flat index = rank
-            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-            const int off = __popcll(__ballot(sel) & below);
-            if (valid) {
-                counts[e] = sel ? 1 : 0;
-                offsets[e] = off;
-            }
-            if (lane == E - 1)
-                offsets[E] = k;
-            if (sel) {
-                perm[off] = rank;
-                inv_perm[rank] = off;
-            }
+            one_token_select(l, E, k, flags, reinterpret_cast<uint64_t *>(smem), idx_out, w_out,
+                             counts, offsets, perm, inv_perm, lane);
             return;
         }
     }

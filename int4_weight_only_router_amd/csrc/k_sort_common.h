@@ -134,6 +134,21 @@ __device__ __forceinline__ float pinned_xor_sum(float a, int lane)
     return a;
 }
 
+// The same butterfly with all 64 partials held by one lane: after the step
+// of stride `off`, partial j (j < off) holds p_j + p_(j+off), exactly what
+// lane j (and lane j xor off) holds after that step of pinned_xor_sum, so
+// the result has the same bits.
+__device__ __forceinline__ float pinned_fold64(float (&p)[64])
+{
+#pragma unroll
+    for (int off = 32; off; off >>= 1) {
+#pragma unroll
+        for (int j = 0; j < off; ++j)
+            p[j] = p[j] + p[j + off];
+    }
+    return p[0];
+}
+
 struct Cand {
     float v;
     int e;   // -1: empty slot
@@ -150,6 +165,69 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e)
     const int u = __builtin_bit_cast(int, v + 0.0f);
     const uint32_t o = (uint32_t)(u ^ ((u >> 31) | (int)0x80000000));
     return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
+}
+
+// Selection, softmax and sort of one token over at most 64 experts by one
+// wave, lane e holding expert e's logit l (ignored for e >= E); `bkey` is 64
+// keys of LDS.  Ranks come from counting the keys that beat each lane's key;
+// the softmax maximum is the logit ranked first; the denominators use the
+// fixed-order wave sum.  Writes the k selected (idx, weight) pairs in rank
+// order and the stable sort of one token's k distinct experts: counts 0/1,
+// offsets = selected experts of lower id (offsets[E] = k), perm[off] = rank,
+// inv_perm[rank] = off.
+__device__ __forceinline__ void one_token_select(float l, int E, int k, unsigned flags,
+                                                 uint64_t *bkey, int32_t *__restrict__ idx_out,
+                                                 float *__restrict__ w_out,
+                                                 int32_t *__restrict__ counts,
+                                                 int32_t *__restrict__ offsets,
+                                                 int32_t *__restrict__ perm,
+                                                 int32_t *__restrict__ inv_perm, int lane)
+{
+    const int e = lane;
+    const bool valid = e < E;
+    const uint64_t key = valid ? topk_key(l, e) : 0ull;
+    bkey[lane] = key;
+    __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll
+    for (int j = 0; j < 64; j += 4) {
+        const uint4_t q = *reinterpret_cast<const uint4_t *>(bkey + j);
+        const uint4_t p = *reinterpret_cast<const uint4_t *>(bkey + j + 2);
+        r0 += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
+        r1 += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
+        r2 += (((uint64_t)p.y << 32) | p.x) > key ? 1 : 0;
+        r3 += (((uint64_t)p.w << 32) | p.z) > key ? 1 : 0;
+    }
+    const int rank = (r0 + r1) + (r2 + r3);
+    const bool sel = valid && rank < k;
+    // softmax over all E: the maximum is the logit ranked first
+    const int top = __ffsll((long long)__ballot(valid && rank == 0)) - 1;
+    const float m =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), top));
+    const float pe = valid ? expf(l - m) : 0.0f;
+    const float den = wave_sum_f32(pe);   // softmax denominator (order fixed, not pinned)
+    float p = pe / den;
+    if (flags & MOE_RENORM) {
+        const float ws = wave_sum_f32(sel ? p : 0.0f);
+        p = p / ws;
+    }
+    if (sel) {
+        idx_out[rank] = e;
+        w_out[rank] = p;
+    }
+    // position = selected experts of lower id, flat index = rank
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int off = __popcll(__ballot(sel) & below);
+    if (valid) {
+        counts[e] = sel ? 1 : 0;
+        offsets[e] = off;
+    }
+    if (lane == E - 1)
+        offsets[E] = k;
+    if (sel) {
+        perm[off] = rank;
+        inv_perm[rank] = off;
+    }
 }
 
 // One step of a wave-wide maximum of 64-bit keys: each lane takes the larger

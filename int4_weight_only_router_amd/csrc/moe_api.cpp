@@ -51,6 +51,11 @@ int launch_shared_gemv(const void *, const void *, const void *, const void *, i
                        float *, void *, hipStream_t);
 int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
                           float *, void *, hipStream_t);
+int launch_combine_route(const float *, int, const int32_t *, const float *, const float *,
+                         const void *, const void *, const void *, int, int, void *,
+                         const void *, const float *, int, int, unsigned, void *, int32_t *,
+                         float *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
+size_t combine_route_ws_bytes();
 int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
                    const void *, const void *, const void *, int, int, int, void *,
                    hipStream_t);
@@ -549,6 +554,67 @@ int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *i
         return set_error(MOE_EINVAL, "moe_combine_gated: x and gate vector need 16-byte alignment");
     return launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,
                           shared_gate_w_f16, residual_f16, T, H, k, out_f16, stream);
+}
+
+// One decode token of at most 64 experts, fp32 slice partials: the fused
+// launch; anything else runs the two calls it stands for.
+static bool combine_route_fused(int T, int E, int y_dtype, int y_slices)
+{
+    return T == 1 && E <= 64 && y_dtype == MOE_DTYPE_F32 && y_slices > 1;
+}
+
+size_t moe_combine_route_permute_workspace_bytes(int T, int k_next, int E)
+{
+    const size_t rp = moe_route_permute_workspace_bytes(T, k_next, E);
+    const size_t cr = combine_route_ws_bytes();
+    return (T == 1 && E > 0 && E <= 64 && cr > rp) ? cr : rp;
+}
+
+int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                              const float *topk_w, const float *shared_f32, const void *x_f16,
+                              const void *shared_gate_w_f16, const void *residual_f16, int T,
+                              int H, int k, void *out_f16, const void *w_router_f16,
+                              const float *logit_bias, int E, int k_next, unsigned flags,
+                              int32_t *topk_idx, float *topk_w_next, int32_t *counts,
+                              int32_t *offsets, int32_t *perm, int32_t *inv_perm_next, void *ws,
+                              size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    const char *fn = "moe_combine_route_permute";
+    int rc = check_combine_args(fn, y, y_dtype, y_slices, inv_perm, topk_w, T, H, k, out_f16);
+    if (rc)
+        return rc;
+    if (shared_gate_w_f16) {
+        if (!shared_f32 || !x_f16)
+            return set_error(MOE_EINVAL, "%s: a gate needs the shared output and x", fn);
+        if (((uintptr_t)x_f16 | (uintptr_t)shared_gate_w_f16) & 15)
+            return set_error(MOE_EINVAL, "%s: x and gate vector need 16-byte alignment", fn);
+    }
+    rc = check_route_args(fn, out_f16, w_router_f16, T, H, E, k_next, flags, topk_idx,
+                          topk_w_next);
+    if (rc)
+        return rc;
+    if (!counts || !offsets || (T > 0 && (!perm || !inv_perm_next)))
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    const size_t need = moe_combine_route_permute_workspace_bytes(T, k_next, E);
+    if (need && (!ws || ws_bytes < need))
+        return set_error(MOE_ENOMEM, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    if (combine_route_fused(T, E, y_dtype, y_slices))
+        return launch_combine_route(static_cast<const float *>(y), y_slices, inv_perm, topk_w,
+                                    shared_f32, x_f16, shared_gate_w_f16, residual_f16, H, k,
+                                    out_f16, w_router_f16, logit_bias, E, k_next, flags, ws,
+                                    topk_idx, topk_w_next, counts, offsets, perm, inv_perm_next,
+                                    stream);
+    if (T > 0) {
+        rc = launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32,
+                            shared_gate_w_f16 ? x_f16 : nullptr, shared_gate_w_f16, residual_f16,
+                            T, H, k, out_f16, stream);
+        if (rc)
+            return rc;
+    }
+    return moe_route_permute(out_f16, w_router_f16, logit_bias, T, H, E, k_next, flags, topk_idx,
+                             topk_w_next, counts, offsets, perm, inv_perm_next, ws, ws_bytes,
+                             stream);
 }
 
 }  // extern "C"

@@ -98,7 +98,8 @@ class MoELayer:
         # route/permute scratch; zero-filled once (the fused router keeps an
         # atomic ticket in it)
         pws = max(A.moe_permute_workspace_bytes(T, self.k, self.E),
-                  A.moe_route_permute_workspace_bytes(T, self.k, self.E))
+                  A.moe_route_permute_workspace_bytes(T, self.k, self.E),
+                  A.moe_combine_route_permute_workspace_bytes(T, self.k, self.E))
         n = T * self.k
         ytype = torch.float32 if ydt == A.MOE_DTYPE_F32 else torch.float16
         sh_out = sh_ws = None
@@ -164,6 +165,27 @@ class MoELayer:
                       b.T, self.H, self.k, out, stream)
         return out
 
+    def combine_route_next(self, b: LayerBuffers, nxt: "MoELayer", b_next: LayerBuffers,
+                           residual=None, out=None, stream=None, x=None):
+        """This layer's combine into `out` fused with the next layer's route +
+        permute of `out` into b_next (moe_combine_route_permute: one launch for a
+        decode token of at most 64 experts, else the two calls)."""
+        if nxt.H != self.H or b_next.T != b.T:
+            raise ValueError("the next layer must have the same H and batch")
+        out = b.out if out is None else out
+        inv = None if b.regime & A.MOE_Y_TOKEN_ORDER else b.inv_perm
+        gate = self.shared_gate
+        if gate is not None and x is None:
+            raise ValueError("the gated shared expert needs the layer input x")
+        nws = 0 if b_next.perm_ws is None else b_next.perm_ws.numel()
+        A.moe_combine_route_permute(b.y, b.y_dtype, b.y_slices, inv, b.topk_w, b.shared_out,
+                                    x if gate is not None else None, gate, residual, b.T,
+                                    self.H, self.k, out, nxt.router, nxt.bias, nxt.E, nxt.k,
+                                    nxt.flags, b_next.topk_idx, b_next.topk_w, b_next.counts,
+                                    b_next.offsets, b_next.perm, b_next.inv_perm, b_next.perm_ws,
+                                    nws, stream)
+        return out
+
     def pool_args(self, b: LayerBuffers, host_ids):
         """PoolLayerArgs for moe_pool_layer_forward with this layer's weights and
         b's buffers; x_f16 / residual_f16 / out_f16 are set per call."""
@@ -216,3 +238,22 @@ class MoELayer:
         self.experts(x, b, stream=main, shared=False)
         main.wait_event(join)
         return self.combine(b, residual, out, main, x=x)
+
+
+def stack_forward(layers, bufs, acts, stream=None, fuse=True):
+    """Stacked layers with residual connections, x_{l+1} = fp16(x_l + MoE_l(x_l)):
+    acts[l] is layer l's input and residual, acts[l + 1] its output.  With
+    `fuse`, each layer's combine runs together with the next layer's route +
+    permute (MoELayer.combine_route_next); the results are the same bits."""
+    L = len(layers)
+    layers[0].route_permute(acts[0], bufs[0], stream)
+    for l, lay in enumerate(layers):
+        if l > 0 and not fuse:
+            lay.route_permute(acts[l], bufs[l], stream)
+        lay.experts(acts[l], bufs[l], stream=stream)
+        if fuse and l + 1 < L:
+            lay.combine_route_next(bufs[l], layers[l + 1], bufs[l + 1], residual=acts[l],
+                                   out=acts[l + 1], stream=stream, x=acts[l])
+        else:
+            lay.combine(bufs[l], residual=acts[l], out=acts[l + 1], stream=stream, x=acts[l])
+    return acts[L]

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import int4_weight_only_router_amd as M
-from int4_weight_only_router_amd.layer import MoELayer, blob_table
+from int4_weight_only_router_amd.layer import MoELayer, blob_table, stack_forward
 import moe_inputs as MI
 import oracle as O
 from tests.gpu_util import (DEV, WTOL, OracleBlobs, check_close, device_experts, f16, make_layer,
@@ -91,10 +91,13 @@ def _free_running(cfg, L, x0, obls):
     return x, sets
 
 
-def test_decode_chain_16_layers_teacher_forced():
+@pytest.mark.parametrize("fuse", [False, True], ids=["three_calls", "combine_route_fused"])
+def test_decode_chain_16_layers_teacher_forced(fuse):
     """The benchmark's workload and launch configuration: 16 stacked decode
     layers captured in one graph, replayed once per step (fresh x0 each
-    step); every layer of every step against the oracle."""
+    step); every layer of every step against the oracle.  fuse: each layer's
+    combine runs with the next layer's route + permute in one launch, as the
+    benchmark runs it."""
     cfg = MI.OLMOE_DECODE
     L = cfg.layers
     lays = _layers(cfg, L)
@@ -103,6 +106,9 @@ def test_decode_chain_16_layers_teacher_forced():
     acts = [torch.empty((1, cfg.H), dtype=torch.float16, device=DEV) for _ in range(L + 1)]
 
     def step():
+        if fuse:
+            stack_forward(lays, bufs, acts)
+            return
         for l, lay in enumerate(lays):
             lay.forward(acts[l], bufs[l], residual=acts[l], out=acts[l + 1])
 

@@ -1,0 +1,206 @@
+"""moe_combine_route_permute on the GPU: one layer's combine fused with the
+next layer's route + permute must give exactly the bits of moe_combine (or
+moe_combine_gated) followed by moe_route_permute, in the fused launch (one
+decode token, at most 64 experts, fp32 slice partials) and in the cases that
+run the two calls; and the routing it produces must equal the oracle's on the
+combined activations.  Sources: Horizon RunMap "03 / Arquitetura" (combine,
+then the next layer's router) and "08 / Comportamento do modelo" (FP32
+routing with explicit roundings)."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_router_amd as M
+from int4_weight_only_router_amd.layer import MoELayer, stack_forward
+import moe_inputs as MI
+import oracle as O
+from tests.gpu_util import DEV, WTOL, f16, make_layer, say
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm")
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _next_layer(cfg, E=None, k=None, renorm=False, bias=False):
+    """A router-only stand-in for layer 1 of cfg (its experts are never run)."""
+    E = cfg.E if E is None else E
+    k = cfg.k if k is None else k
+    c = MI.MoEConfig(cfg.cid, cfg.name, H=cfg.H, E=E, k=k, I=cfg.I, g=cfg.g)
+    router = f16(MI.gen_router(c, 1))
+    b = None
+    if bias:
+        b = torch.from_numpy(np.random.default_rng(5).standard_normal(E).astype(np.float32)
+                             * np.float32(0.05)).to(DEV)
+    table = torch.zeros(E, dtype=torch.int64, device=DEV)
+    return MoELayer(cfg.H, cfg.I, E, k, cfg.g, router, table, b, renorm=renorm, device=DEV)
+
+
+def _run_layer(lay, T, x):
+    b = lay.buffers(T)
+    lay.route_permute(x, b)
+    lay.experts(x, b)
+    return b
+
+
+def _snapshot(b, out):
+    n = b.T * b.topk_idx.shape[1]
+    d = {key: _np(getattr(b, key)).copy() for key in KEYS}
+    d["perm"], d["inv_perm"] = d["perm"][:n], d["inv_perm"][:n]
+    d["out"] = _np(out).copy()
+    return d
+
+
+def _both(lay, nxt, b, T, x, residual=True):
+    """(separate calls, fused call) snapshots for the same layer state."""
+    res = x if residual else None
+    out_a = torch.empty((T, lay.H), dtype=torch.float16, device=DEV)
+    out_b = torch.empty_like(out_a)
+    ba, bb = nxt.buffers(T), nxt.buffers(T)
+    lay.combine(b, residual=res, out=out_a, x=x)
+    nxt.route_permute(out_a, ba)
+    lay.combine_route_next(b, nxt, bb, residual=res, out=out_b, x=x)
+    torch.cuda.synchronize()
+    return _snapshot(ba, out_a), _snapshot(bb, out_b), bb
+
+
+def _assert_same(a, b, what):
+    for key in ("out",) + KEYS:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), \
+            "%s: %s differs" % (what, key)
+
+
+def _assert_oracle_routing(nxt, snap, cfg_next):
+    wr = _np(nxt.router).astype(np.float16)
+    bias = None if nxt.bias is None else _np(nxt.bias)
+    idx, w, _ = O.route(snap["out"], wr, bias, nxt.k, renorm=bool(nxt.flags & M.MOE_RENORM))
+    assert np.array_equal(snap["topk_idx"], idx), "routing differs from the oracle"
+    assert np.max(np.abs(snap["topk_w"] - w)) <= WTOL
+    counts, offsets, perm, inv = O.permute(idx, nxt.E)
+    assert np.array_equal(snap["counts"], counts) and np.array_equal(snap["offsets"], offsets)
+    assert np.array_equal(snap["perm"], perm) and np.array_equal(snap["inv_perm"], inv)
+
+
+CASES = [
+    # (config, next E, next k, renorm, bias, residual)
+    ("olmoe", None, None, False, False, True),
+    ("olmoe", 48, 6, True, True, True),
+    ("olmoe", 64, 1, False, True, False),
+    ("tiny", None, None, False, False, True),
+    ("tiny", 64, 16, True, False, True),
+    ("qwen", None, None, False, False, True),       # gated shared expert
+    ("h512", 33, 5, False, True, True),
+    ("h1024", 64, 8, True, True, True),
+]
+
+
+def _cfg(name):
+    if name == "olmoe":
+        return MI.OLMOE_DECODE
+    if name == "tiny":
+        return MI.TINY
+    if name == "qwen":
+        return MI.QWEN
+    if name == "h512":
+        return MI.MoEConfig(90, "h512", H=512, E=16, k=4, I=256, g=64)
+    return MI.MoEConfig(91, "h1024", H=1024, E=32, k=8, I=512, g=128)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-E%s-k%s-r%d-b%d-res%d" % c)
+def test_fused_equals_separate_calls(case):
+    name, En, kn, renorm, bias, residual = case
+    cfg = _cfg(name)
+    say("combine+route %s" % (case,))
+    lay = make_layer(cfg, 0)
+    nxt = _next_layer(cfg, En, kn, renorm, bias)
+    for s in range(3):
+        x = f16(MI.gen_x(cfg, 1, step=s))
+        b = _run_layer(lay, 1, x)
+        assert b.y_dtype == M.MOE_DTYPE_F32 and b.y_slices > 1
+        a, f, _ = _both(lay, nxt, b, 1, x, residual)
+        _assert_same(a, f, "%s step %d" % (name, s))
+        _assert_oracle_routing(nxt, f, cfg)
+
+
+@pytest.mark.parametrize("T,En", [(2, None), (4, None), (1, 128), (1, 512), (16, None)])
+def test_two_call_cases_equal_separate_calls(T, En):
+    """Batches above one token, more than 64 experts in the next layer or
+    fp16 batched y: the entry point runs the two calls; same bits."""
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0)
+    nxt = _next_layer(cfg, En, 8 if En else None)
+    x = f16(MI.gen_x(cfg, T, step=7))
+    b = _run_layer(lay, T, x)
+    a, f, _ = _both(lay, nxt, b, T, x)
+    _assert_same(a, f, "T=%d E=%s" % (T, En))
+
+
+def test_routing_arrays_may_be_shared_and_ticket_returns_to_zero():
+    """The next layer's routing written into the same arrays the combine reads
+    (every read precedes every write), the residual updated in place, and the
+    workspace's ticket back at zero after each call."""
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0)
+    nxt = _next_layer(cfg)
+    for s in range(3):
+        x = f16(MI.gen_x(cfg, 1, step=20 + s))
+        b = _run_layer(lay, 1, x)
+        a, _, _ = _both(lay, nxt, b, 1, x)
+        xin = x.clone()
+        lay.combine_route_next(b, nxt, b, residual=xin, out=xin, x=x)
+        torch.cuda.synchronize()
+        got = _snapshot(b, xin)
+        _assert_same(a, got, "shared arrays step %d" % s)
+        assert int(_np(b.perm_ws[:4]).view(np.uint32)[0]) == 0
+
+
+def test_stack_forward_fused_equals_unfused():
+    """Four stacked decode layers: the fused chain (combine + next route in
+    one launch) and the plain one give the same bits at every layer."""
+    cfg = MI.OLMOE_DECODE
+    lays = [make_layer(cfg, l) for l in range(4)]
+    outs = {}
+    for fuse in (False, True):
+        bufs = [lay.buffers(1) for lay in lays]
+        acts = [torch.empty((1, cfg.H), dtype=torch.float16, device=DEV) for _ in range(5)]
+        acts[0].copy_(f16(MI.gen_x(cfg, 1, step=3)))
+        stack_forward(lays, bufs, acts, fuse=fuse)
+        torch.cuda.synchronize()
+        outs[fuse] = [(_np(a).copy(), _np(bf.topk_idx).copy(), _np(bf.perm).copy())
+                      for a, bf in zip(acts[1:], bufs)]
+    for l, (u, f) in enumerate(zip(outs[False], outs[True])):
+        for i in range(3):
+            assert np.array_equal(u[i].view(np.uint8), f[i].view(np.uint8)), (l, i)
+
+
+def test_rejects_bad_arguments():
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0)
+    nxt = _next_layer(cfg)
+    x = f16(MI.gen_x(cfg, 1, step=0))
+    b = _run_layer(lay, 1, x)
+    bn = nxt.buffers(1)
+    out = torch.empty_like(x)
+    with pytest.raises(M.MoEError) as e:   # workspace too small
+        M.moe_combine_route_permute(b.y, b.y_dtype, b.y_slices, None, b.topk_w, None, None,
+                                    None, x, 1, cfg.H, cfg.k, out, nxt.router, None, nxt.E,
+                                    nxt.k, 0, bn.topk_idx, bn.topk_w, bn.counts, bn.offsets,
+                                    bn.perm, bn.inv_perm, bn.perm_ws, 256)
+    assert e.value.code == M.MOE_ENOMEM
+    with pytest.raises(M.MoEError) as e:   # k_next > E
+        M.moe_combine_route_permute(b.y, b.y_dtype, b.y_slices, None, b.topk_w, None, None,
+                                    None, x, 1, cfg.H, cfg.k, out, nxt.router, None, nxt.E,
+                                    nxt.E + 1, 0, bn.topk_idx, bn.topk_w, bn.counts,
+                                    bn.offsets, bn.perm, bn.inv_perm, bn.perm_ws,
+                                    bn.perm_ws.numel())
+    assert e.value.code == M.MOE_EINVAL
+    with pytest.raises(M.MoEError) as e:   # a gate without the shared output
+        M.moe_combine_route_permute(b.y, b.y_dtype, b.y_slices, None, b.topk_w, None, x,
+                                    nxt.router, x, 1, cfg.H, cfg.k, out, nxt.router, None,
+                                    nxt.E, nxt.k, 0, bn.topk_idx, bn.topk_w, bn.counts,
+                                    bn.offsets, bn.perm, bn.inv_perm, bn.perm_ws,
+                                    bn.perm_ws.numel())
+    assert e.value.code == M.MOE_EINVAL

@@ -170,7 +170,8 @@ H1024 = MI.MoEConfig(88, "h1024_e64", H=1024, E=64, k=6, I=128, g=64)
 def test_router_logits_pinned_order(cfg, T):
     """The logits the router kernels leave in their workspace equal the
     oracle's pinned-order fp32 logits bit for bit (chunk c of 8 elements into
-    partial c mod 64 by single-rounding FMAs, xor butterfly, then the bias)."""
+    partial c // q, q = ceil(chunks / 64), by single-rounding FMAs, xor
+    butterfly, then the bias)."""
     say("logits %s T=%d" % (cfg.name, T))
     x = MI.gen_x(cfg, T, step=11)
     wr = MI.gen_router(cfg)
