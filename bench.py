@@ -230,7 +230,8 @@ def run_decode(args, torch, M):
     K, W = args.steps, args.warmup
     xs = torch.from_numpy(np.concatenate([MI.gen_x(cfg, 1, step=s) for s in range(K + W)])).to(dev)
     bufs = [lay.buffers(1) for lay in lays]
-    assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_W4_ZERO_POINT) == M.MOE_REGIME_DECODE
+    assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_Y_PARTIAL_ORDER
+                              | M.MOE_W4_ZERO_POINT) == M.MOE_REGIME_DECODE
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
 
     fuse = not getattr(args, "no_fuse", False)
@@ -448,7 +449,7 @@ def run_batched(args, torch, M, cfg):
                  + 2 * T * cfg.H * 2 + (cfg.H * 2 if cfg.shared_gate else 0))
         tf = f_routed / (us["expert_ffn"] * 1e-6) / 1e12
         ffn_bytes = touched * blob_bytes
-        reg = b.regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_W4_ZERO_POINT)
+        reg = b.regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_Y_PARTIAL_ORDER | M.MOE_W4_ZERO_POINT)
         line = {"T": T, "regime": {1: "decode", 2: "batched", 3: "small"}.get(reg, reg),
                 "experts_touched": touched, "max_rows_per_expert": int(counts.max()),
                 "us": {k: round(v, 1) for k, v in us.items()},

@@ -69,7 +69,15 @@ enum { MOE_REGIME_AUTO = 0, MOE_REGIME_DECODE = 1, MOE_REGIME_BATCHED = 2, MOE_R
 /* OR'd into the regime of moe_expert_ffn_plan / moe_expert_ffn_w4a16: y rows
  * in token order (row t*k + j) instead of sorted order; see below. */
 enum { MOE_Y_TOKEN_ORDER = 0x100 };
-enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1 };
+/* OR'd into the same regime: the DECODE partials' columns in partial-major
+ * order (the plan then reports MOE_DTYPE_F32_PM).  With C = H/8 chunks of 8
+ * columns and q = ceil(C/64), column c of chunk u = 64m + j (j < 64) is stored
+ * at column 8(jq + m) + c mod 8: the chunks j, j+64, ... that form partial j
+ * of the router's pinned logit sum lie side by side, so a reader that owns
+ * partial j reads whole lines.  Needs C <= 64 or C a multiple of 64. */
+enum { MOE_Y_PARTIAL_ORDER = 0x400 };
+/* y dtypes: fp16, fp32 (decode slices), fp32 in partial-major column order. */
+enum { MOE_DTYPE_F16 = 0, MOE_DTYPE_F32 = 1, MOE_DTYPE_F32_PM = 2 };
 /* Expert blob formats: symmetric codes, or codes with a zero point per group
  * (lucashiago.com.br explainer, step 1: each block carries a scale and a zero
  * point).  MOE_W4_ZERO_POINT is OR'd into the regime of moe_expert_ffn_plan /
@@ -190,10 +198,9 @@ int moe_unpack_expert_host(const void *src, int H, int I, int group, int fmt, vo
  *                 (0 for T <= 8, where ws may be NULL; above that it holds the
  *                 T x E fp32 logits between the logit and top-k launches;
  *                 contents need no initialisation); MOE_ENOMEM if too small
- * Logits are fp32 in a fixed summation order (H in chunks of 8 elements;
- * partial j takes the j-th run of q = ceil((H/8)/64) consecutive chunks,
- * element by element; the 64 partials combined by an xor butterfly
- * 32,16,8,4,2,1), so the indices are reproducible bit for bit.
+ * Logits are fp32 in a fixed summation order (chunks of 8 elements of H go
+ * to partial (chunk mod 64) in increasing order, partials combined by an xor
+ * butterfly 32,16,8,4,2,1), so the indices are reproducible bit for bit.
  * T = 0 is a no-op.
  */
 size_t moe_route_workspace_bytes(int T, int E);
@@ -274,9 +281,10 @@ int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,
  *            multiplied on the matrix cores; gate/up then down, h in ws.
  *            T > 32 is MOE_EUNSUPPORTED.  y is fp16 [1][T*k][H].
  *   BATCHED: tiled grouped GEMM, any T.  y is fp16 [1][T*k][H].
- * regime may carry MOE_Y_TOKEN_ORDER (DECODE only: MOE_EUNSUPPORTED when the
- * resolved regime is another) and MOE_W4_ZERO_POINT (any regime: the blobs
- * are MOE_FMT_ZP); resolved_regime is returned without them.
+ * regime may carry MOE_Y_TOKEN_ORDER and MOE_Y_PARTIAL_ORDER (DECODE only:
+ * MOE_EUNSUPPORTED when the resolved regime is another; with the second, y_dtype
+ * is MOE_DTYPE_F32_PM) and MOE_W4_ZERO_POINT (any regime: the blobs are
+ * MOE_FMT_ZP); resolved_regime is returned without them.
  */
 int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime,
                         int *resolved_regime, int *y_dtype, int *y_slices,
@@ -301,7 +309,9 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
  *                  Row p holds sorted row p; with MOE_Y_TOKEN_ORDER in regime
  *                  (DECODE only) the result of sorted row p goes to row
  *                  perm[p] = t*k + j instead, so that moe_combine needs no
- *                  inv_perm (one dependent memory round trip less)
+ *                  inv_perm (one dependent memory round trip less); with
+ *                  MOE_Y_PARTIAL_ORDER each row's columns are stored in
+ *                  partial-major order (MOE_DTYPE_F32_PM)
  *   ws             device scratch of the plan's size (may be NULL if 0)
  * Rounding: DECODE converts h to fp16 before the down projection; SMALL and
  * BATCHED convert the weights to fp16(q * s) and store h and y as fp16.
@@ -342,7 +352,8 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
  *   out[t,c] = fp16_rne( r + sum_j w[t,j] * Y(inv_perm[t*k+j], c) + s[t,c] )
  * where Y(p,c) is y[p,c] (y_dtype F16, y_slices 1) or the sum over slices of
  * y[slice][p][c] (F32; the slices summed in two contiguous halves, each in
- * slice order, then the halves added), r = residual[t,c] or 0, s the
+ * slice order, then the halves added; F32_PM: the same with column c read
+ * from its partial-major position), r = residual[t,c] or 0, s the
  * shared-expert output or 0.  fp32 sum in the order: experts j = 0..k-1
  * (each the slice sum), shared, residual; one final rounding.
  *   y            device, from moe_expert_ffn_w4a16; 16-byte aligned
@@ -353,8 +364,9 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
  *   residual_f16 device fp16 [T][H] or NULL (may alias out_f16)
  *   out_f16      device fp16 [T][H]
  * Errors: MOE_EINVAL for bad sizes or dtype (k outside 1..16, F16 y with
- * more than one slice), a null y/topk_w/out pointer or a misaligned y;
- * MOE_EUNSUPPORTED when H is not a multiple of 8.
+ * more than one slice, F32_PM with an H that has no partial-major order), a
+ * null y/topk_w/out pointer or a misaligned y; MOE_EUNSUPPORTED when H is
+ * not a multiple of 8.
  */
 int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
                 const float *topk_w, const float *shared_f32, const void *residual_f16,
@@ -392,7 +404,8 @@ int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *i
  *   then moe_route_permute(out_f16, w_router_f16, logit_bias, T, H, E, k_next,
  *     flags, topk_idx, topk_w_next, counts, offsets, perm, inv_perm_next).
  * One launch when T = 1, E <= 64 and y holds fp32 slices (y_slices > 1, the
- * decode layout); otherwise the two calls run in turn on `stream`.
+ * decode layout; with MOE_DTYPE_F32_PM every block of that launch reads whole
+ * lines); otherwise the two calls run in turn on `stream`.
  *   ws  device workspace of moe_combine_route_permute_workspace_bytes(T,
  *       k_next, E) bytes, zero-filled before the first call
  *       (moe_workspace_clear).  The fused launch leaves its first 256 bytes

@@ -9,8 +9,8 @@ from . import build as _build
 __all__ = [
     "MoEError", "lib", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_ENOMEM", "MOE_EHIP",
     "MOE_ECAPACITY", "MOE_ESTATE", "MOE_RENORM", "MOE_REGIME_AUTO", "MOE_REGIME_DECODE",
-    "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_DTYPE_F16",
-    "MOE_DTYPE_F32", "MOE_FMT_SYM", "MOE_FMT_ZP", "MOE_W4_ZERO_POINT", "EXPORTS",
+    "MOE_REGIME_BATCHED", "MOE_REGIME_SMALL", "MOE_Y_TOKEN_ORDER", "MOE_Y_PARTIAL_ORDER",
+    "MOE_DTYPE_F16", "MOE_DTYPE_F32", "MOE_DTYPE_F32_PM", "MOE_FMT_SYM", "MOE_FMT_ZP", "MOE_W4_ZERO_POINT", "EXPORTS",
     "moe_blob_layout_fmt", "moe_quantize_experts_fmt", "moe_prepack_experts_fmt",
     "moe_unpack_experts_fmt", "moe_prepack_expert_host", "moe_unpack_expert_host",
     "moe_last_error", "moe_workspace_clear", "moe_blob_layout", "moe_quantize_experts",
@@ -32,7 +32,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP, MOE_ECAPACITY, MOE_E
 MOE_RENORM = 1
 MOE_REGIME_AUTO, MOE_REGIME_DECODE, MOE_REGIME_BATCHED, MOE_REGIME_SMALL = 0, 1, 2, 3
 MOE_Y_TOKEN_ORDER = 0x100   # OR'd into a regime: decode y rows in token order
-MOE_DTYPE_F16, MOE_DTYPE_F32 = 0, 1
+MOE_Y_PARTIAL_ORDER = 0x400  # OR'd into a regime: decode y columns in partial-major order
+MOE_DTYPE_F16, MOE_DTYPE_F32, MOE_DTYPE_F32_PM = 0, 1, 2
 MOE_FMT_SYM, MOE_FMT_ZP = 0, 1   # expert blob formats (zero point per group)
 MOE_W4_ZERO_POINT = 0x200        # OR'd into a regime: the blobs are MOE_FMT_ZP
 

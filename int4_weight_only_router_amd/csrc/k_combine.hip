@@ -39,18 +39,23 @@ __device__ inline float shared_gate_256(const f16 *__restrict__ xt, const f16 *_
     return 1.0f / (1.0f + expf(-a));
 }
 
-// Decode partials: fp32 y [S][T*k][H].  Block = 32 consecutive columns of one
-// token (combine_tile).
-template <bool GATED>
+// Decode partials: fp32 y [S][T*k][H], columns in plain or (PM)
+// partial-major order.  Block = 32 consecutive y positions of one token
+// (combine_tile); with PM the output columns are the positions' originals.
+template <bool GATED, bool PM>
 __global__ __launch_bounds__(256) void combine_slices_kernel(
     const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
     const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
     const f16 *__restrict__ wsg, const f16 *residual, int T, int H, int k, f16 *out)
 {
-    __shared__ CombineTileSmem sm;
+    __shared__ CombineTileSmem sm[1];
     const int base = blockIdx.x * 32;
-    combine_tile<GATED>(y, S, inv_perm, w, shared, x, wsg, residual, T, blockIdx.y, H, k,
-                        min(32, H - base), ContigCols{base}, out, sm);
+    if constexpr (PM)
+        combine_tile<GATED, 1>(y, S, inv_perm, w, shared, x, wsg, residual, T, blockIdx.y, H, k,
+                               min(32, H - base), PmCols{base, H}, out, sm, threadIdx.x);
+    else
+        combine_tile<GATED, 1>(y, S, inv_perm, w, shared, x, wsg, residual, T, blockIdx.y, H, k,
+                               min(32, H - base), ContigCols{base}, out, sm, threadIdx.x);
 }
 
 // 8 consecutive columns of one y row, loaded as one (fp16) or two (fp32)
@@ -217,16 +222,21 @@ int launch_combine(const void *y, int y_dtype, int S, const int32_t *inv_perm, c
     const f16 *gw = static_cast<const f16 *>(gate_w_f16);
     const bool gated = gw != nullptr;
     f16 *o = static_cast<f16 *>(out);
-    if (y_dtype == MOE_DTYPE_F32 && S > 1) {
+    if ((y_dtype == MOE_DTYPE_F32 && S > 1) || y_dtype == MOE_DTYPE_F32_PM) {
         dim3 grid((H + 31) / 32, T);
-        if (gated)
-            hipLaunchKernelGGL((combine_slices_kernel<true>), grid, dim3(256), 0, s,
-                               static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
-                               T, H, k, o);
-        else
-            hipLaunchKernelGGL((combine_slices_kernel<false>), grid, dim3(256), 0, s,
-                               static_cast<const float *>(y), S, inv_perm, w, shared, xh, gw, res,
-                               T, H, k, o);
+        const float *yf = static_cast<const float *>(y);
+#define MOE_SLICES(G, P)                                                                         \
+    hipLaunchKernelGGL((combine_slices_kernel<G, P>), grid, dim3(256), 0, s, yf, S, inv_perm, w, \
+                       shared, xh, gw, res, T, H, k, o)
+        const bool pm = y_dtype == MOE_DTYPE_F32_PM;
+        if (gated) {
+            if (pm) MOE_SLICES(true, true);
+            else MOE_SLICES(true, false);
+        } else {
+            if (pm) MOE_SLICES(false, true);
+            else MOE_SLICES(false, false);
+        }
+#undef MOE_SLICES
         MOE_LAUNCH_CHECK("combine_slices_kernel");
         return MOE_OK;
     }

@@ -4,12 +4,14 @@
 // Two stacked layers meet at x_{l+1} = combine_l(...): the next layer's
 // router needs every column of it, and the combine of a decode token is a
 // few microseconds of latency-bound reads of the fp32 partials.  One launch
-// does both.  Block j (64 blocks, or H/8 when fewer) owns the 8 q consecutive
-// columns of the q-chunk run j (q = ceil((H/8)/64)) -- exactly the chunks
-// that make up partial number j of every logit in the pinned order (Horizon
-// RunMap "08 / Comportamento do modelo": routing in FP32 with explicit
-// roundings; the order itself is this library's reading).  At H = 2048 that
-// is 32 columns, whole 128-byte lines of every partial row.  It
+// does both.  In the pinned logit order (Horizon RunMap "08 / Comportamento
+// do modelo": routing in FP32 with explicit roundings; the order itself is
+// this library's reading) partial j of a logit accumulates the 8-column
+// chunks j, j+64, j+128, ...  Block j (64 blocks, or H/8 when fewer) owns
+// exactly those columns.  With the decode partials in partial-major column
+// order (MOE_DTYPE_F32_PM) they lie side by side, so the block reads whole
+// 128-byte lines of every partial row; in plain order it reads 32-byte
+// pieces (correct, slower: four blocks share each line).  The block
 //  1. combines its columns of x_{l+1} (combine_tile: the plain combine's
 //     arithmetic, so the bits equal moe_combine's) and stores them;
 //  2. with wave 0, lane e = expert e, accumulates partial j of every logit
@@ -35,7 +37,16 @@ namespace moe {
 
 constexpr int CR_MAX_POLLS = 1 << 20;   // far beyond any wait for co-running blocks
 
-template <int H, bool GATED>
+// Block j's i-th column: element i % 8 of chunk j + 64 (i / 8); in y at the
+// same column (plain) or at its partial-major position 8 j q + i (PM).
+template <bool PM>
+struct PartialCols {
+    int j, q;
+    __device__ int col(int, int i) const { return 8 * (j + 64 * (i >> 3)) + (i & 7); }
+    __device__ int y(int, int i) const { return PM ? 8 * j * q + i : col(0, i); }
+};
+
+template <int H, bool GATED, bool PM>
 __global__ __launch_bounds__(256) void combine_route_kernel(
     const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
     const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
@@ -48,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     constexpr int NCH = H / 8;               // 8-column chunks
     constexpr int NCL = (NCH + 63) / 64;     // chunks per partial (all present: H % 512 == 0
                                              // or H = 256, where blocks j < 32 hold one)
-    __shared__ CombineTileSmem sm;
+    __shared__ CombineTileSmem sm[1];
     __shared__ __align__(16) f16 xs[32];
     __shared__ __align__(16) uint64_t keys[64];
 
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
-    // the call counter, and the router chunks j q + m of expert `lane` (lanes
+    // the call counter, and the router chunks j + 64m of expert `lane` (lanes
     // past E read row E - 1; block 0 ignores them), requested first.  Every
     // wave issues them (only wave 0 uses them): a branch here would make the
     // compiler wait for them before the slice loads.
@@ -67,16 +78,16 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
             reinterpret_cast<const uint4_t *>(wr + (size_t)min(lane, E - 1) * H);
 #pragma unroll
         for (int m = 0; m < NCL; ++m)
-            wv[m] = row[j * NCL + m];
+            wv[m] = row[j + 64 * m];
     }
-    const ContigCols cols{8 * NCL * j};
-    const f16 o = combine_tile<GATED>(y, S, inv_perm, w, shared, x, wsg, residual, 1, 0, H, k,
-                                      8 * NCL, cols, nullptr, sm);
+    const PartialCols<PM> cols{j, NCL};
+    const f16 o = combine_tile<GATED, 1>(y, S, inv_perm, w, shared, x, wsg, residual, 1, 0, H,
+                                         k, 8 * NCL, cols, nullptr, sm, threadIdx.x);
     if (wave != 0)
         return;
     if (lane < 8 * NCL) {
         xs[lane] = o;
-        out[cols(lane)] = o;
+        out[cols.col(0, lane)] = o;
     }
     __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
     const unsigned tag = 0x7FC00000u | ((c + 1u) & 0x3FFFFFu);
@@ -97,6 +108,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
 
     // block 0: lane e gathers the 64 partials of expert e's logit (partial
     // jj >= gridDim.x has no chunk and is zero, as in the one-launch router)
+    // with agent-scope loads until every tag is this call's.
     const int nb = gridDim.x;
     float p[64];
     for (int it = 0; it < CR_MAX_POLLS; ++it) {
@@ -127,7 +139,7 @@ constexpr size_t CR_XCHG_OFF = 256;
 constexpr size_t CR_CALLS_OFF = CR_XCHG_OFF + (size_t)64 * 64 * sizeof(uint64_t);
 size_t combine_route_ws_bytes() { return CR_CALLS_OFF + 256; }
 
-template <int H, bool GATED>
+template <int H, bool GATED, bool PM>
 static void launch_cr(const float *y, int S, const int32_t *inv_perm, const float *w,
                       const float *shared, const f16 *x, const f16 *wsg, const f16 *residual,
                       int k, f16 *out, const f16 *wr, const float *bias, int E, int kn,
@@ -138,13 +150,14 @@ static void launch_cr(const float *y, int S, const int32_t *inv_perm, const floa
     uint64_t *xchg = reinterpret_cast<uint64_t *>(base + CR_XCHG_OFF);
     unsigned *calls = reinterpret_cast<unsigned *>(base + CR_CALLS_OFF);
     const int blocks = H / 8 < 64 ? H / 8 : 64;
-    hipLaunchKernelGGL((combine_route_kernel<H, GATED>), dim3(blocks), dim3(256), 0, s, y, S,
-                       inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E, kn, flags,
+    hipLaunchKernelGGL((combine_route_kernel<H, GATED, PM>), dim3(blocks), dim3(256), 0, s, y,
+                       S, inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E, kn, flags,
                        xchg, calls, idx, wo, counts, offsets, perm, inv_perm_out);
 }
 
-// T = 1, E <= 64, fp32 decode partials; the caller has checked the shapes.
-int launch_combine_route(const float *y, int S, const int32_t *inv_perm, const float *w,
+// T = 1, E <= 64, fp32 decode partials (pm: partial-major columns); the
+// caller has checked the shapes.
+int launch_combine_route(const float *y, bool pm, int S, const int32_t *inv_perm, const float *w,
                          const float *shared, const void *x, const void *gate_w,
                          const void *residual, int H, int k, void *out, const void *wr,
                          const float *bias, int E, int kn, unsigned flags, void *ws, int32_t *idx,
@@ -154,13 +167,17 @@ int launch_combine_route(const float *y, int S, const int32_t *inv_perm, const f
     const f16 *xh = static_cast<const f16 *>(x), *gh = static_cast<const f16 *>(gate_w);
     const f16 *rh = static_cast<const f16 *>(residual), *wh = static_cast<const f16 *>(wr);
     f16 *oh = static_cast<f16 *>(out);
+#define MOE_CR3(HH, G, P)                                                                       \
+    launch_cr<HH, G, P>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn, flags,   \
+                        ws, idx, wo, counts, offsets, perm, inv_perm_out, s)
 #define MOE_CR(HH)                                                                              \
-    if (gh)                                                                                     \
-        launch_cr<HH, true>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn,      \
-                            flags, ws, idx, wo, counts, offsets, perm, inv_perm_out, s);        \
-    else                                                                                        \
-        launch_cr<HH, false>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn,     \
-                             flags, ws, idx, wo, counts, offsets, perm, inv_perm_out, s);
+    if (gh) {                                                                                   \
+        if (pm) MOE_CR3(HH, true, true);                                                        \
+        else MOE_CR3(HH, true, false);                                                          \
+    } else {                                                                                    \
+        if (pm) MOE_CR3(HH, false, true);                                                       \
+        else MOE_CR3(HH, false, false);                                                         \
+    }
     switch (H) {
     case 256: MOE_CR(256) break;
     case 512: MOE_CR(512) break;
@@ -169,6 +186,7 @@ int launch_combine_route(const float *y, int S, const int32_t *inv_perm, const f
     default: return set_error(MOE_EUNSUPPORTED, "combine_route: H=%d not instantiated", H);
     }
 #undef MOE_CR
+#undef MOE_CR3
     MOE_LAUNCH_CHECK("combine_route_kernel");
     return MOE_OK;
 }

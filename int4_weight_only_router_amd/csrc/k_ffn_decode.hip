@@ -17,7 +17,8 @@
 // is applied, and the 32 fp16 h values then multiply the slice's 32-column
 // strip of the down projection (one 1 KB run per 64 output rows).  Each
 // workgroup writes an fp32 partial y for its slice (at the row's sorted
-// position, or at t*k + j with MOE_Y_TOKEN_ORDER); moe_combine adds the
+// position, or at t*k + j with MOE_Y_TOKEN_ORDER; each column at its
+// partial-major position with MOE_Y_PARTIAL_ORDER); moe_combine adds the
 // slices in order.  Each wave keeps a few weight chunks in flight and
 // computes each chunk as it lands (schedule notes at the kernel).
 #include "k_decode_frag.h"
@@ -92,7 +93,7 @@ template <int H, int G, int NW, int PD, bool ZP>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
-    const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk, int tok_order,
+    const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk, int yflags,
     int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, int64_t off_guz,
     int64_t off_dz, float *__restrict__ y)
 {
@@ -159,6 +160,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
     // flat indices t*k + j of the expert's first 64 rows (decode: at most 4
     // rows); needed for the token of a row (T > 1) and for a token-order y
+    const bool tok_order = (yflags & YF_TOKEN_ORDER) != 0;
     const int prow = ((T > 1 || tok_order) && lane < nrows) ? ldg(perm + p0 + lane) : 0;
 
     // scales: one per scale group among this wave's gate/up chunks, one per
@@ -355,12 +357,16 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
                 opaque(w[CPW + j]);
                 unpack_chunk(w[CPW + j], mj);
             }
+            // column rb * 64 + lane, stored at its partial-major position
+            // when asked (a uniform choice)
+            const int col = rb * 64 + lane;
+            const int ycol = (yflags & YF_PARTIAL_ORDER) ? pm_col(col, H) : col;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float c0 = hc[r];
                 if constexpr (ZP)
                     c0 = fmaf(-(float)zd[j], hs[r], c0);
-                y[((size_t)slice * ntk + yrow[r]) * H + rb * 64 + lane] =
+                y[((size_t)slice * ntk + yrow[r]) * H + ycol] =
                         dot_unpacked(PRE ? md[j] : mj, hp[r], c0) * s;
             }
         }
@@ -389,12 +395,12 @@ template <int H, bool ZP>
 static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
                            const int32_t *offsets, const uint8_t *const *blobs,
                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
-                           bool tok_order, const DevLayout &L, float *y)
+                           int yflags, const DevLayout &L, float *y)
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
 #define MOE_DECODE_LAUNCH(G)                                                                  \
     hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD, ZP>), grid, dim3(NW * 64), 0, s, \
-                       x, perm, offsets, blobs, skip, I, E, k, ntk, tok_order ? 1 : 0, L.gu_q,    \
+                       x, perm, offsets, blobs, skip, I, E, k, ntk, yflags, L.gu_q,               \
                        L.d_q, L.gu_s, L.d_s, L.gu_z, L.d_z, y)
     switch (g) {
     case 32: MOE_DECODE_LAUNCH(32); break;
@@ -411,7 +417,7 @@ static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t
 // null entry in `blobs` are not computed either.
 int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
                       const void *const *blobs, const void *const *skip, int T, int H, int I,
-                      int E, int k, int g, int fmt, bool tok_order, float *y, hipStream_t s)
+                      int E, int k, int g, int fmt, int yflags, float *y, hipStream_t s)
 {
     const int ntk = T * k;
     if (ntk == 0)
@@ -425,9 +431,9 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
 #define MOE_DECODE_H(HH)                                                                       \
     rc = fmt == FMT_ZP                                                                         \
              ? launch_decode_h<HH, true>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,    \
-                                         tok_order, L, y)                                      \
+                                         yflags, L, y)                                         \
              : launch_decode_h<HH, false>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,   \
-                                          tok_order, L, y)
+                                          yflags, L, y)
     switch (H) {
     case 256: MOE_DECODE_H(256); break;
     case 512: MOE_DECODE_H(512); break;

@@ -5,10 +5,9 @@
 // work on each token; "08 / Comportamento do modelo": routing stays outside
 // INT4 and accumulation is FP32 with explicit roundings.  The pages leave the
 // rest open; this kernel fixes it as follows.
-//  * Logit l[t,e] = sum_h x[t,h] Wr[e,h] in fp32 in a pinned order: H is cut
-//    into chunks of 8 and the chunks into 64 runs of q = ceil((H/8)/64)
-//    consecutive chunks (NCL below); run j is accumulated, element by
-//    element, into partial number j; the 64 partials are combined
+//  * Logit l[t,e] = sum_h x[t,h] Wr[e,h] in fp32 in a pinned order: chunk c
+//    (8 consecutive h) is accumulated, element by element, into partial
+//    number (c mod 64), chunks in increasing c; the 64 partials are combined
 //    by an xor butterfly with strides 32,16,8,4,2,1.  Partial j lives in lane
 //    j of the wave that owns (t, e), so the butterfly is a lane shuffle.
 //    fp16 x fp16 products are exact in fp32, hence fma and mul+add agree and
@@ -63,7 +62,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
         const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane * NCL + m;
+            const int c = lane + 64 * m;
             dst[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
         }
     };
@@ -78,7 +77,7 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
             acc[tt] = 0.0f;
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane * NCL + m;
+            const int c = lane + 64 * m;
             if (c < NCH) {
                 const half8_t wh = __builtin_bit_cast(half8_t, cur[m]);
 #pragma unroll
@@ -138,10 +137,10 @@ __global__ __launch_bounds__(NW * 64) void route_kernel(
 // Batches above 8 tokens: logits and top-k in two launches.
 //
 // route_logits_kernel: each wave computes an 8-token x 8-expert tile of
-// logits.  Lane j owns partial j of all 64 logits (chunks c = jq .. jq+q-1,
+// logits.  Lane j owns partial j of all 64 logits (chunks c = j, j+64, ...,
 // elements in order, acc = fma(x, w, acc) with exact fp16 products), reading
 // its 16-byte slices of the 8 activation rows and the 8 router rows straight
-// from memory (a wave's loads of one chunk step cover a row's 64 runs).
+// from memory (consecutive lanes read consecutive 16-byte slices of a row).
 // The 64 x 64 partials then go through LDS so that lane l holds the 64
 // partials of logit l and folds them in registers in the butterfly's order
 // (a_j + a_(j+32), then +16, ... +1): the same additions, operand for operand,
@@ -171,7 +170,7 @@ __global__ __launch_bounds__(RL_WAVES * 64) void route_logits_kernel(
             acc[t][i] = 0.0f;
 #pragma unroll
     for (int m = 0; m < NCL; ++m) {
-        const int c = lane * NCL + m;
+        const int c = lane + 64 * m;
         if (c < NCH) {
             half8_t xv[8], wv[8];
 #pragma unroll
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
         const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(e, E - 1) * H);
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane * NCL + m;
+            const int c = lane + 64 * m;
             wv[m] = (e < E && c < NCH) ? row[c] : uint4_t{0u, 0u, 0u, 0u};
         }
         const uint4_t *src = reinterpret_cast<const uint4_t *>(x);
@@ -345,7 +344,7 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
             acc[tt] = 0.0f;
 #pragma unroll
         for (int m = 0; m < NCL; ++m) {
-            const int c = lane * NCL + m;
+            const int c = lane + 64 * m;
             if (c < NCH) {
                 const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
 #pragma unroll

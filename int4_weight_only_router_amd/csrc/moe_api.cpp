@@ -39,7 +39,7 @@ int launch_route_split(const void *, const void *, const float *, int, int, int,
 int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, int32_t *,
                    void *, hipStream_t);
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
-                      const void *const *, int, int, int, int, int, int, int, bool, float *,
+                      const void *const *, int, int, int, int, int, int, int, int, float *,
                       hipStream_t);
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
@@ -51,7 +51,7 @@ int launch_shared_gemv(const void *, const void *, const void *, const void *, i
                        float *, void *, hipStream_t);
 int launch_shared_batched(const void *, const void *, const void *, const void *, int, int, int,
                           float *, void *, hipStream_t);
-int launch_combine_route(const float *, int, const int32_t *, const float *, const float *,
+int launch_combine_route(const float *, bool, int, const int32_t *, const float *, const float *,
                          const void *, const void *, const void *, int, int, void *,
                          const void *, const float *, int, int, unsigned, void *, int32_t *,
                          float *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
@@ -421,21 +421,26 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
     if (rc)
         return rc;
     const bool tok = (regime & MOE_Y_TOKEN_ORDER) != 0;
-    regime &= ~(MOE_Y_TOKEN_ORDER | MOE_W4_ZERO_POINT);
+    const bool pm = (regime & MOE_Y_PARTIAL_ORDER) != 0;
+    regime &= ~(MOE_Y_TOKEN_ORDER | MOE_Y_PARTIAL_ORDER | MOE_W4_ZERO_POINT);
     if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_SMALL)
         return set_error(MOE_EINVAL, "moe_expert_ffn_plan: bad regime %d", regime);
     const int r = resolve_regime(T, H, I, regime);
-    if (tok && r != MOE_REGIME_DECODE)
+    if ((tok || pm) && r != MOE_REGIME_DECODE)
         return set_error(MOE_EUNSUPPORTED,
-                         "moe_expert_ffn_plan: token-order y is a DECODE-regime option "
-                         "(resolved regime %d)", r);
+                         "moe_expert_ffn_plan: token-order and partial-major y are "
+                         "DECODE-regime options (resolved regime %d)", r);
+    if (pm && !partial_order_ok(H))
+        return set_error(MOE_EUNSUPPORTED,
+                         "moe_expert_ffn_plan: H=%d has no partial-major column order", H);
     if (r == MOE_REGIME_SMALL && !ffn_small_fits(T, H, I))
         return set_error(MOE_EUNSUPPORTED,
                          "moe_expert_ffn_plan: small-batch regime takes T <= 32 (T=%d)", T);
     if (resolved_regime)
         *resolved_regime = r;
     if (y_dtype)
-        *y_dtype = (r == MOE_REGIME_DECODE) ? MOE_DTYPE_F32 : MOE_DTYPE_F16;
+        *y_dtype = (r == MOE_REGIME_DECODE) ? (pm ? MOE_DTYPE_F32_PM : MOE_DTYPE_F32)
+                                            : MOE_DTYPE_F16;
     if (y_slices)
         *y_slices = (r == MOE_REGIME_DECODE) ? I / 32 : 1;
     if (ws_bytes)
@@ -468,8 +473,8 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
     const int fmt = (regime & MOE_W4_ZERO_POINT) ? MOE_FMT_ZP : MOE_FMT_SYM;
     if (r == MOE_REGIME_DECODE)
         return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
-                                 group, fmt, (regime & MOE_Y_TOKEN_ORDER) != 0,
-                                 static_cast<float *>(y), stream);
+                                 group, fmt, decode_yflags(regime), static_cast<float *>(y),
+                                 stream);
     if (r == MOE_REGIME_SMALL)
         return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, fmt, y,
                                 ws, stream);
@@ -512,8 +517,10 @@ static int check_combine_args(const char *fn, const void *y, int y_dtype, int y_
     if (T < 0 || H <= 0 || k <= 0 || k > 16 || y_slices <= 0)
         return set_error(MOE_EINVAL, "%s: bad sizes T=%d H=%d k=%d slices=%d", fn, T, H, k,
                          y_slices);
-    if (y_dtype != MOE_DTYPE_F16 && y_dtype != MOE_DTYPE_F32)
+    if (y_dtype != MOE_DTYPE_F16 && y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_F32_PM)
         return set_error(MOE_EINVAL, "%s: bad y dtype %d", fn, y_dtype);
+    if (y_dtype == MOE_DTYPE_F32_PM && H > 0 && H % 8 == 0 && !partial_order_ok(H))
+        return set_error(MOE_EINVAL, "%s: H=%d has no partial-major column order", fn, H);
     if (y_dtype == MOE_DTYPE_F16 && y_slices != 1)
         return set_error(MOE_EINVAL, "%s: fp16 y has exactly one slice", fn);
     if (H % 8)
@@ -560,7 +567,8 @@ int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *i
 // launch; anything else runs the two calls it stands for.
 static bool combine_route_fused(int T, int E, int y_dtype, int y_slices)
 {
-    return T == 1 && E <= 64 && y_dtype == MOE_DTYPE_F32 && y_slices > 1;
+    return T == 1 && E <= 64 && (y_dtype == MOE_DTYPE_F32 || y_dtype == MOE_DTYPE_F32_PM) &&
+           y_slices > 1;
 }
 
 size_t moe_combine_route_permute_workspace_bytes(int T, int k_next, int E)
@@ -600,7 +608,8 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
     if (need && (!ws || ws_bytes < need))
         return set_error(MOE_ENOMEM, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     if (combine_route_fused(T, E, y_dtype, y_slices))
-        return launch_combine_route(static_cast<const float *>(y), y_slices, inv_perm, topk_w,
+        return launch_combine_route(static_cast<const float *>(y), y_dtype == MOE_DTYPE_F32_PM,
+                                    y_slices, inv_perm, topk_w,
                                     shared_f32, x_f16, shared_gate_w_f16, residual_f16, H, k,
                                     out_f16, w_router_f16, logit_bias, E, k_next, flags, ws,
                                     topk_idx, topk_w_next, counts, offsets, perm, inv_perm_next,

@@ -13,6 +13,31 @@
 
 namespace moe {
 
+// Layout flags of the decode partials passed to the decode kernel: rows in
+// token order, columns in partial-major order (MOE_Y_PARTIAL_ORDER).
+constexpr int YF_TOKEN_ORDER = 1, YF_PARTIAL_ORDER = 2;
+inline int decode_yflags(int regime)
+{
+    return ((regime & MOE_Y_TOKEN_ORDER) ? YF_TOKEN_ORDER : 0) |
+           ((regime & MOE_Y_PARTIAL_ORDER) ? YF_PARTIAL_ORDER : 0);
+}
+
+// Partial-major column order: with C = H/8 chunks of 8 columns and
+// q = ceil(C/64), column c of chunk u = 64m + j (j < 64) is stored at column
+// 8(jq + m) + c mod 8.  A bijection when C <= 64 (then the identity) or C is
+// a multiple of 64.
+inline bool partial_order_ok(int H)
+{
+    const int C = H / 8;
+    return H > 0 && H % 8 == 0 && (C <= 64 || C % 64 == 0);
+}
+__host__ __device__ inline int pm_col(int c, int H)
+{
+    const int q = (H / 8 + 63) / 64;
+    const int u = c >> 3;
+    return (((u & 63) * q + (u >> 6)) << 3) | (c & 7);
+}
+
 // ------------------------------------------------------------ errors (host)
 
 int set_error(int code, const char *fmt, ...);   // stores a thread-local message

@@ -125,7 +125,7 @@ struct HipPoolBackend {
 
 namespace moe {
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
-                      const void *const *, int, int, int, int, int, int, int, bool, float *,
+                      const void *const *, int, int, int, int, int, int, int, int, float *,
                       hipStream_t);
 }
 
@@ -221,7 +221,8 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
                                         a->H, a->I, E, a->k, a->group,
                                         (a->regime & MOE_W4_ZERO_POINT) ? moe::FMT_ZP
                                                                         : moe::FMT_SYM,
-                                        tok, static_cast<float *>(a->y), stream);
+                                        moe::decode_yflags(a->regime),
+                                        static_cast<float *>(a->y), stream);
     } else if (!rc) {
         rc = P.publish(layer, stream);
         if (!rc)

@@ -85,7 +85,9 @@ class MoELayer:
         self.flags = A.MOE_RENORM if renorm else 0
         self.device = device
 
-    def buffers(self, T, regime=A.MOE_REGIME_AUTO) -> LayerBuffers:
+    def buffers(self, T, regime=A.MOE_REGIME_AUTO, partial_order=True) -> LayerBuffers:
+        """partial_order: decode partials in partial-major column order, which
+        the fused combine + next route reads in whole lines."""
         d = self.device
         r, ydt, ysl, ffn_ws = A.moe_expert_ffn_plan(T, self.H, self.I, self.E, self.k, self.g,
                                                     regime)
@@ -93,6 +95,9 @@ class MoELayer:
             # decode partials straight in token order: the combine then reads
             # them without inv_perm (one dependent round trip less)
             r |= A.MOE_Y_TOKEN_ORDER
+            if partial_order and (self.H // 8 <= 64 or (self.H // 8) % 64 == 0):
+                r |= A.MOE_Y_PARTIAL_ORDER
+                ydt = A.moe_expert_ffn_plan(T, self.H, self.I, self.E, self.k, self.g, r)[1]
         if self.fmt == A.MOE_FMT_ZP:
             r |= A.MOE_W4_ZERO_POINT
         # route/permute scratch; zero-filled once (the fused router keeps an
@@ -101,7 +106,7 @@ class MoELayer:
                   A.moe_route_permute_workspace_bytes(T, self.k, self.E),
                   A.moe_combine_route_permute_workspace_bytes(T, self.k, self.E))
         n = T * self.k
-        ytype = torch.float32 if ydt == A.MOE_DTYPE_F32 else torch.float16
+        ytype = torch.float16 if ydt == A.MOE_DTYPE_F16 else torch.float32
         sh_out = sh_ws = None
         if self.shared is not None:
             Is = self.shared[0].shape[0]

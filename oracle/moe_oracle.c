@@ -396,11 +396,10 @@ int oracle_dequant_rows_zp(const uint8_t *q, const uint16_t *s, const uint8_t *z
 /*
  * Router logit l[t,e] = sum_h x[t,h] * Wr[e,h] in fp32, in a pinned order
  * (READING; the pages only say accumulation is FP32 with explicit roundings,
- * [HR] "08"): H is cut into chunks of 8 elements and the chunks into 64 runs
- * of q = ceil((H/8)/64) consecutive chunks; run j (chunks jq .. jq+q-1, fewer
- * or none at the end) is added, element by element in increasing h, into
- * partial number j; the 64 partials are then combined by an xor butterfly
- * with strides 32, 16, 8, 4, 2, 1 (a_j <- a_j + a_{j xor s}).  fp16 x fp16
+ * [HR] "08"): H is cut into chunks of 8 elements; chunk c is added, element
+ * by element in increasing h, into partial number (c mod 64), chunks taken in
+ * increasing c; the 64 partials are then combined by an xor butterfly with
+ * strides 32, 16, 8, 4, 2, 1 (a_j <- a_j + a_{j xor s}).  fp16 x fp16
  * products are exact in fp32, so this order fixes every rounding.
  */
 static float logit_pinned(const float *x, const float *w, int H)
@@ -408,9 +407,8 @@ static float logit_pinned(const float *x, const float *w, int H)
     float part[64], nxt[64];
     for (int j = 0; j < 64; j++)
         part[j] = 0.0f;
-    const int q = (H / 8 + 63) / 64;
     for (int c = 0; c < H / 8; c++) {
-        int lane = c / q;
+        int lane = c % 64;
         for (int i = 0; i < 8; i++) {
             int h = c * 8 + i;
             float prod = x[h] * w[h];

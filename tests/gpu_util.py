@@ -133,3 +133,21 @@ def sample_rows(offsets, n_per_expert=2, max_extra=64, seed=0):
     if len(extra) > max_extra:
         extra = rng.choice(extra, max_extra, replace=False).tolist()
     return np.array(sorted(edges | set(extra)), np.int32)
+
+
+def pm_positions(H):
+    """Stored column of each column in the decode partials' partial-major
+    order (the header's rule: column c of chunk u = 64 m + j, j < 64, goes to
+    8 (j q + m) + c mod 8 with q = ceil(H / 8 / 64))."""
+    q = (H // 8 + 63) // 64
+    c = np.arange(H)
+    u = c // 8
+    return ((u % 64) * q + u // 64) * 8 + c % 8
+
+
+def y_plain(b):
+    """A layer's y as numpy, decode partial columns back in plain order."""
+    y = b.y.detach().cpu().numpy()
+    if b.y_dtype == M.MOE_DTYPE_F32_PM:
+        y = y[..., pm_positions(y.shape[-1])]
+    return y

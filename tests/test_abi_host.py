@@ -62,6 +62,11 @@ def test_plan_regimes():
                                                                      M.MOE_DTYPE_F32, 32, 0)
     assert M.moe_expert_ffn_plan(3, 2048, 1024, 64, 8, 128, M.MOE_REGIME_DECODE | tok)[0] == \
         M.MOE_REGIME_DECODE
+    # partial-major decode columns: reported as their own y dtype
+    pm = M.MOE_Y_PARTIAL_ORDER
+    for H in (256, 512, 1024, 2048):
+        assert M.moe_expert_ffn_plan(1, H, 1024, 64, 8, 64, tok | pm) == (
+            M.MOE_REGIME_DECODE, M.MOE_DTYPE_F32_PM, 32, 0)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -78,6 +83,7 @@ def test_plan_regimes():
     ((64, 2048, 1024, 64, 8, 128, M.MOE_Y_TOKEN_ORDER), M.MOE_EUNSUPPORTED),  # token order
     ((1, 2048, 1024, 64, 8, 128, M.MOE_REGIME_BATCHED | M.MOE_Y_TOKEN_ORDER),
      M.MOE_EUNSUPPORTED),                                                     # off decode
+    ((64, 2048, 1024, 64, 8, 128, M.MOE_Y_PARTIAL_ORDER), M.MOE_EUNSUPPORTED),  # off decode
 ])
 def test_plan_rejections(args, code):
     with pytest.raises(M.MoEError) as ei:

@@ -102,7 +102,8 @@ def test_decode_chain_16_layers_teacher_forced(fuse):
     L = cfg.layers
     lays = _layers(cfg, L)
     bufs = [lay.buffers(1) for lay in lays]
-    assert bufs[0].regime & ~M.MOE_Y_TOKEN_ORDER == M.MOE_REGIME_DECODE
+    assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_Y_PARTIAL_ORDER) == \
+        M.MOE_REGIME_DECODE
     acts = [torch.empty((1, cfg.H), dtype=torch.float16, device=DEV) for _ in range(L + 1)]
 
     def step():

@@ -2,8 +2,9 @@
 next layer's route + permute must give exactly the bits of moe_combine (or
 moe_combine_gated) followed by moe_route_permute, in the fused launch (one
 decode token, at most 64 experts, fp32 slice partials) and in the cases that
-run the two calls; and the routing it produces must equal the oracle's on the
-combined activations.  Sources: Horizon RunMap "03 / Arquitetura" (combine,
+run the two calls, with the decode partials in plain or partial-major column
+order; and the routing it produces must equal the oracle's on the combined
+activations.  Sources: Horizon RunMap "03 / Arquitetura" (combine,
 then the next layer's router) and "08 / Comportamento do modelo" (FP32
 routing with explicit roundings)."""
 import numpy as np
@@ -39,8 +40,8 @@ def _next_layer(cfg, E=None, k=None, renorm=False, bias=False):
     return MoELayer(cfg.H, cfg.I, E, k, cfg.g, router, table, b, renorm=renorm, device=DEV)
 
 
-def _run_layer(lay, T, x):
-    b = lay.buffers(T)
+def _run_layer(lay, T, x, partial_order=True):
+    b = lay.buffers(T, partial_order=partial_order)
     lay.route_permute(x, b)
     lay.experts(x, b)
     return b
@@ -109,8 +110,9 @@ def _cfg(name):
     return MI.MoEConfig(91, "h1024", H=1024, E=32, k=8, I=512, g=128)
 
 
+@pytest.mark.parametrize("po", [True, False], ids=["partial_major_y", "plain_y"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-E%s-k%s-r%d-b%d-res%d" % c)
-def test_fused_equals_separate_calls(case):
+def test_fused_equals_separate_calls(case, po):
     name, En, kn, renorm, bias, residual = case
     cfg = _cfg(name)
     say("combine+route %s" % (case,))
@@ -118,8 +120,8 @@ def test_fused_equals_separate_calls(case):
     nxt = _next_layer(cfg, En, kn, renorm, bias)
     for s in range(3):
         x = f16(MI.gen_x(cfg, 1, step=s))
-        b = _run_layer(lay, 1, x)
-        assert b.y_dtype == M.MOE_DTYPE_F32 and b.y_slices > 1
+        b = _run_layer(lay, 1, x, po)
+        assert b.y_dtype == (M.MOE_DTYPE_F32_PM if po else M.MOE_DTYPE_F32) and b.y_slices > 1
         a, f, _ = _both(lay, nxt, b, 1, x, residual)
         _assert_same(a, f, "%s step %d" % (name, s))
         _assert_oracle_routing(nxt, f, cfg)

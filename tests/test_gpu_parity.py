@@ -15,7 +15,7 @@ from int4_weight_only_router_amd.layer import MoELayer, blob_table
 import moe_inputs as MI
 import oracle as O
 from tests.gpu_util import (DEV, WTOL, OracleBlobs, check_close, device_experts, f16,
-                            make_layer, sample_rows, say)
+                            make_layer, pm_positions, sample_rows, say, y_plain)
 from tests.layout_util import numpy_prepack as _numpy_prepack
 
 pytestmark = pytest.mark.gpu
@@ -170,8 +170,7 @@ H1024 = MI.MoEConfig(88, "h1024_e64", H=1024, E=64, k=6, I=128, g=64)
 def test_router_logits_pinned_order(cfg, T):
     """The logits the router kernels leave in their workspace equal the
     oracle's pinned-order fp32 logits bit for bit (chunk c of 8 elements into
-    partial c // q, q = ceil(chunks / 64), by single-rounding FMAs, xor
-    butterfly, then the bias)."""
+    partial c mod 64 by single-rounding FMAs, xor butterfly, then the bias)."""
     say("logits %s T=%d" % (cfg.name, T))
     x = MI.gen_x(cfg, T, step=11)
     wr = MI.gen_router(cfg)
@@ -323,10 +322,10 @@ def _ffn_case(cfg, T, regime, layer=0, fmt=M.MOE_FMT_SYM):
     blobs = OracleBlobs(cfg, layer, fmt).get(used)
     y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows,
                          fmt=fmt)
-    y = _np(b.y).astype(np.float64)
+    y = y_plain(b).astype(np.float64)
     # decode partials are in token order: sorted row p sits at row perm[p]
     yr = perm[rows] if b.regime & M.MOE_Y_TOKEN_ORDER else rows
-    y_rows = y.sum(axis=0)[yr] if b.y_dtype == M.MOE_DTYPE_F32 else y[0][yr]
+    y_rows = y.sum(axis=0)[yr] if b.y_dtype != M.MOE_DTYPE_F16 else y[0][yr]
     return check_close(y_rows, y_ref, "y %s T=%d" % (cfg.name, T))
 
 
@@ -340,7 +339,7 @@ def test_decode_token_order_y(cfg, T):
     say("decode token order %s T=%d" % (cfg.name, T))
     lay = make_layer(cfg, 0, shared=False)
     xd = f16(MI.gen_x(cfg, T))
-    b = lay.buffers(T, M.MOE_REGIME_DECODE)
+    b = lay.buffers(T, M.MOE_REGIME_DECODE, partial_order=False)
     assert b.regime == M.MOE_REGIME_DECODE | M.MOE_Y_TOKEN_ORDER
     lay.route_permute(xd, b)
     lay.experts(xd, b)
@@ -356,6 +355,34 @@ def test_decode_token_order_y(cfg, T):
     perm = _np(b.perm)
     assert np.array_equal(_np(y_tok)[:, perm, :].view(np.int32), _np(b.y).view(np.int32))
     assert np.array_equal(_np(out_tok).view(np.int16), _np(out_sorted).view(np.int16))
+
+
+@pytest.mark.parametrize("cfg,T", [(MI.OLMOE_DECODE, 1), (MI.OLMOE_DECODE, 4), (MI.TINY, 2),
+                                   (MI.QWEN, 1), (MI.E512, 3)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_decode_partial_order_y(cfg, T):
+    """Decode partials with MOE_Y_PARTIAL_ORDER (dtype MOE_DTYPE_F32_PM) are
+    the plain partials with every column moved to its partial-major position
+    (the header's rule, rendered independently in pm_positions), bit for bit,
+    and the combine of either layout gives the same output bits (the gated
+    combine of the 60-expert layer included)."""
+    say("decode partial order %s T=%d" % (cfg.name, T))
+    lay = make_layer(cfg, 0)
+    xd = f16(MI.gen_x(cfg, T, step=5))
+    bp = lay.buffers(T, M.MOE_REGIME_DECODE, partial_order=False)
+    bm = lay.buffers(T, M.MOE_REGIME_DECODE)
+    assert bp.y_dtype == M.MOE_DTYPE_F32
+    assert bm.y_dtype == M.MOE_DTYPE_F32_PM and bm.regime & M.MOE_Y_PARTIAL_ORDER
+    outs = []
+    for b in (bp, bm):
+        lay.route_permute(xd, b)
+        lay.experts(xd, b)
+        outs.append(lay.combine(b, residual=xd, x=xd).clone())
+    torch.cuda.synchronize()
+    pos = pm_positions(cfg.H)
+    assert np.array_equal(np.sort(pos), np.arange(cfg.H))
+    assert np.array_equal(_np(bm.y)[..., pos].view(np.int32), _np(bp.y).view(np.int32))
+    assert np.array_equal(_np(outs[0]).view(np.int16), _np(outs[1]).view(np.int16))
 
 
 @pytest.mark.parametrize("cfg,T,regime", [
@@ -685,7 +712,7 @@ def test_decode_row_groups_and_shapes(H, I, g, E, k, T):
     lay.bias = torch.from_numpy(bias).to(DEV)
     x = MI.gen_x(cfg, T)
     b = lay.buffers(T, M.MOE_REGIME_DECODE)
-    assert b.regime == M.MOE_REGIME_DECODE | M.MOE_Y_TOKEN_ORDER
+    assert b.regime & ~M.MOE_Y_PARTIAL_ORDER == M.MOE_REGIME_DECODE | M.MOE_Y_TOKEN_ORDER
     xd = f16(x)
     lay.route_permute(xd, b)
     lay.experts(xd, b)
@@ -698,7 +725,7 @@ def test_decode_row_groups_and_shapes(H, I, g, E, k, T):
     rows = np.arange(T * cfg.k, dtype=np.int32)
     blobs = OracleBlobs(cfg, 0).get(range(3, 3 + cfg.k))
     y_ref = O.expert_ffn(x, perm, offsets, blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g, rows=rows)
-    check_close(_np(b.y).astype(np.float64).sum(axis=0)[perm[rows]], y_ref, "y %s" % cfg.name)
+    check_close(y_plain(b).astype(np.float64).sum(axis=0)[perm[rows]], y_ref, "y %s" % cfg.name)
     ref = O.moe_layer(x, MI.gen_router(cfg), blobs, cfg.H, cfg.I, cfg.E, cfg.k, cfg.g,
                       bias=bias)   # only the routed experts' blobs are packed
     check_close(_np(out).astype(np.float64), ref["out_f64"], "out %s" % cfg.name)

@@ -140,8 +140,8 @@ def test_blob_bytes_closed_form(cfg, expect):
 # ---------------------------------------------------------------- router
 
 def _pinned_logits_numpy(x16, w16):
-    """Independent float32 rendering of the pinned order (chunk c of 8 into
-    partial c // q, q = ceil(chunks / 64), in order, then the xor butterfly)."""
+    """Independent float32 rendering of the pinned order (chunks of 8 to
+    partial c mod 64, in order, then the xor butterfly)."""
     x = x16.astype(np.float32)
     w = w16.astype(np.float32)
     T, H = x.shape
@@ -151,10 +151,9 @@ def _pinned_logits_numpy(x16, w16):
         for e in range(E):
             part = np.zeros(64, np.float32)
             prod = x[t] * w[e]
-            q = (H // 8 + 63) // 64
             for c in range(H // 8):
                 for i in range(8):
-                    part[c // q] = np.float32(part[c // q] + prod[c * 8 + i])
+                    part[c % 64] = np.float32(part[c % 64] + prod[c * 8 + i])
             for st in (32, 16, 8, 4, 2, 1):
                 part = (part + part[np.arange(64) ^ st]).astype(np.float32)
             out[t, e] = part[0]
