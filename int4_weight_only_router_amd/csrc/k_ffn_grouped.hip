@@ -809,17 +809,20 @@ static int64_t tile_bound(int rows, int E, int BM)
 // top-10 (Zipf-skewed) and 60-expert top-4 layers from 64 to 4096 tokens: up
 // to 1024 rows 32-row tiles win (each workgroup has few, short items); above
 // that taller tiles win even when there are fewer items than CUs, because a
-// workgroup's per-item fill and epilogue dominate a short item: 64-row tiles
-// while experts hold at most 32 rows on average (at 2560 and 10240 rows of
-// the 512-expert layer they beat 32-row tiles by 21-23%; 128-row tiles pad
-// its many small experts), 128-row tiles above (64 experts at 4096 rows:
-// 124 against 133 us).  Every case was within 1% of its best height.
+// workgroup's per-item fill and epilogue dominate a short item, as long as
+// they do not mostly pad: 64-row tiles while experts hold at most 40 rows on
+// average (the 512-expert layer at 2560 and 10240 rows: 21-23% faster than
+// 32-row tiles), 96-row tiles up to 160 (64 experts at 4096 rows: 110 us
+// against 122 with 128-row and 134 with 64-row tiles; at 8192 rows 193
+// against 199-200), 128-row tiles above (64 experts at 16384 and 32768 rows:
+// 299 and 505 us against 313 and 519).  The one measured case off its best
+// height: 60 experts at 16384 rows (128-row tiles, 6% slower than 96).
 static int pick_mf(int rows, int E)
 {
     if (rows <= 1024)
         return 1;
     const int64_t avg = rows / std::max(1, std::min(E, rows));
-    return avg <= 32 ? 2 : 4;
+    return avg <= 40 ? 2 : (avg <= 160 ? 3 : 4);
 }
 
 // Row-tile height of the FP16 shared-expert GEMM: the tallest that still
@@ -925,6 +928,7 @@ static int launch_mode(hipStream_t s, const GemmArgs &a)
     if constexpr (MODE == GM_GATEUP_W4 || MODE == GM_DOWN_W4) {
         switch (pick_mf(a.rows, a.E)) {
         case 4: return launch_w4<MODE, 4, ZP>(s, a);
+        case 3: return launch_w4<MODE, 3, ZP>(s, a);
         case 2: return launch_w4<MODE, 2, ZP>(s, a);
         default: return launch_w4<MODE, 1, ZP>(s, a);
         }
