@@ -725,6 +725,23 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
                     if (g + W4_NS < total)
                         issue_next();   // refills the stage of step g (read by no one now)
                 }
+                // issue order inside the sub-step: each of the first MF MFMAs
+                // followed by one LDS operand read and three VALU ops (the
+                // next sub-step's dequantisation), the rest by three VALU ops,
+                // so the reads start early and the VALU work sits under the
+                // matrix core (2-3% on the 64- and 512-expert layers at 4096
+                // tokens against the compiler's own order)
+#pragma unroll
+                for (int i = 0; i < MF; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+                }
+#pragma unroll
+                for (int i = 0; i < MF; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                }
             }
             if (next)
                 wc = wn;
