@@ -528,22 +528,32 @@ def run_partial(args, torch, M):
     step = M.PoolStats()
     trace_layers, trace_ids = [], []
     pinned = None
+    # access map of the measured tokens: per-(layer, expert) hits and misses
+    # (the pool's own counters) and a hit/miss log per (token, layer)
+    acc_hits = np.zeros((L, cfg.E), np.int64)
+    acc_misses = np.zeros((L, cfg.E), np.int64)
+    hm_log = []
 
-    def token(x0, record):
+    def token(x0, record, log_hm=False):
         # one native call per layer: route, ids to the host, prepare (misses
         # copied), expert FFN through the published table, retire, combine
         x = x0.data_ptr()
         misses = 0
+        row = []
         for l in range(L):
             a = largs[l]
             out = act[l & 1].data_ptr()
             a.x_f16, a.residual_f16, a.out_f16 = x, x, out
             M.moe_pool_layer_forward(pool, l, a, stream, step)
             misses += step.misses
+            if log_hm:
+                row.append((step.hits, step.misses))
             if record:
                 trace_layers.append(l)
                 trace_ids.append(host_ids.numpy().copy())
             x = out
+        if log_hm:
+            hm_log.append(row)
         return misses
 
     blocks = []
@@ -572,20 +582,24 @@ def run_partial(args, torch, M):
                 token(torch.from_numpy(MI.gen_prompt_token(cfg, -1, i)).to(dev), blk == 0)
             torch.cuda.synchronize()
             base = M.moe_pool_stats(pool)
+            h0, m0 = M.moe_pool_access_counts(pool, L, cfg.E)
             x0s = [[torch.from_numpy(MI.gen_prompt_token(cfg, p, i)).to(dev)
                     for i in range(args.tokens)] for p in range(args.prompts)]
             busy = 0.0
             ntok = 0
             for p in range(args.prompts):
-                token(x0s[p][0], blk == 0)            # first token: outside the rate
+                token(x0s[p][0], blk == 0, True)      # first token: outside the rate
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 for i in range(1, args.tokens):
-                    token(x0s[p][i], blk == 0)
+                    token(x0s[p][i], blk == 0, True)
                 torch.cuda.synchronize()
                 busy += time.perf_counter() - t0
                 ntok += args.tokens - 1
             st = M.moe_pool_stats(pool)
+            h1, m1 = M.moe_pool_access_counts(pool, L, cfg.E)
+            acc_hits += h1 - h0
+            acc_misses += m1 - m0
             blocks.append({"tokens_per_s": ntok / busy,
                            "h2d_bytes": st.h2d_bytes - base.h2d_bytes,
                            "hits": st.hits - base.hits, "misses": st.misses - base.misses})
@@ -622,6 +636,14 @@ def run_partial(args, torch, M):
              "frac": round((t_calc + mpt * blob_bytes / (h2d_gbs * 1e9)) / t_meas, 4),
              "t_token_bound_pcie5_ms": round((t_calc + mpt * blob_bytes / 64e9) * 1e3, 4),
              "frac_pcie5": round((t_calc + mpt * blob_bytes / 64e9) / t_meas, 4)}
+    access = access_summary(acc_hits, acc_misses, cfg.capacity, hm_log)
+    if args.access_out:
+        with open(args.access_out, "w") as f:
+            json.dump({"layers": L, "experts": cfg.E, "capacity": cfg.capacity,
+                       "policy": args.policy, "hits": acc_hits.tolist(),
+                       "misses": acc_misses.tolist(),
+                       "hit_miss_log": [[list(hm) for hm in row] for row in hm_log]}, f)
+        access["file"] = args.access_out
     return {
         "workload": "olmoe_partial: 16 layers, %d of 64 experts resident + %d spares per layer, "
                     "Zipf(1.0) router bias, %d blocks x (64 warmup + %d prompts x %d tokens)"
@@ -638,7 +660,36 @@ def run_partial(args, torch, M):
         "decay_shift": args.decay_shift if pinned is None else None,
         "profile_tokens": args.profile_prompts * args.tokens if pinned is not None else 0,
         "t_token_model": bound,
+        "access": access,
     }
+
+
+def access_summary(hits, misses, C, hm_log):
+    """A few figures of the per-(layer, expert) access map of the measured
+    tokens (all blocks): how many experts each layer touched, the share of a
+    layer's uses taken by its C most used experts (the static hit ceiling of
+    the whole run), how concentrated the misses are, the hottest (layer,
+    expert) pairs, and from the per-(token, layer) log the share of layer
+    calls that missed at all."""
+    import numpy as np
+    uses = hits + misses
+    tot = max(1, int(uses.sum()))
+    per_layer = np.maximum(1, uses.sum(axis=1))
+    topc = np.sort(uses, axis=1)[:, ::-1][:, :C].sum(axis=1) / per_layer
+    ms = np.sort(misses, axis=1)[:, ::-1]
+    miss8 = ms[:, :8].sum() / max(1, int(misses.sum()))
+    flat = np.argsort(-uses, axis=None, kind="stable")[:5]
+    hottest = [[int(i // uses.shape[1]), int(i % uses.shape[1]),
+                int(uses.flat[i]), int(misses.flat[i])] for i in flat]
+    calls = [hm for row in hm_log for hm in row]
+    missed_calls = sum(1 for h, m in calls if m > 0)
+    return {"uses": tot,
+            "touched_per_layer": [int(v) for v in (uses > 0).sum(axis=1)],
+            "top_C_use_share_per_layer": [round(float(v), 4) for v in topc],
+            "miss_share_8_most_missed_per_layer": round(float(miss8), 4),
+            "hottest_layer_expert_uses_misses": hottest,
+            "layer_calls": len(calls),
+            "layer_calls_with_a_miss": round(missed_calls / max(1, len(calls)), 4)}
 
 
 def batched_leg(torch, M, T=4096):
@@ -661,7 +712,7 @@ def partial_leg(torch, M, prompts=2, tokens=64):
     """A short partial-residency run (one block: 64 warmup tokens, then
     `prompts` x `tokens` tokens) with the explainer's t_token bound."""
     a = argparse.Namespace(blocks=1, prompts=prompts, tokens=tokens, decay_shift=3,
-                           policy="decay", profile_prompts=0)
+                           policy="decay", profile_prompts=0, access_out="")
     r = run_partial(a, torch, M)
     keep = ("workload", "decode_tokens_per_s_pooled", "h2d_GiB_measured", "hit_rate",
             "misses_per_token", "pool_misses_block0", "t_token_model")
@@ -710,6 +761,9 @@ def main():
     ap.add_argument("--decay-shift", type=int, default=3)
     ap.add_argument("--policy", choices=["decay", "pinned"], default="decay",
                     help="partial: decayed-counter eviction, or a profile-pinned resident set")
+    ap.add_argument("--access-out", default="",
+                    help="partial: write the per-(layer, expert) access map and the "
+                         "per-(token, layer) hit/miss log to this JSON file")
     ap.add_argument("--profile-prompts", type=int, default=4,
                     help="partial --policy pinned: prompts of the profile pass")
     ap.add_argument("--no-fuse", dest="no_fuse", action="store_true", default=False,

@@ -562,6 +562,18 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
 /* Cumulative counters since creation or the last reset. */
 int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out);
 
+/*
+ * Per-(layer, expert) access counts since creation or the last reset: the
+ * uses of each expert that found it resident and those that copied it in.
+ * Their sum over a layer is that layer's routed distinct experts over all
+ * its generations.  This is the data a live map of expert traffic is drawn
+ * from (Strata, "Tracking MoE expert residency": aggregate hit rates did not
+ * explain the behaviour; the per-layer, per-expert distribution did).
+ * hits, misses: host int64 arrays of layers*experts, index l*E + e, written.
+ * MOE_EINVAL on a null argument.  Host only: nothing waits for the device.
+ */
+int moe_pool_access_counts(moe_pool_t pool, int64_t *hits, int64_t *misses);
+
 /* Waits for all pool work, restores the initial placement, clears counters. */
 int moe_pool_reset(moe_pool_t pool);
 

@@ -23,7 +23,7 @@ __all__ = [
     "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "PoolConfig",
     "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
-    "moe_pool_retire", "moe_pool_stats", "moe_pool_reset",
+    "moe_pool_retire", "moe_pool_stats", "moe_pool_access_counts", "moe_pool_reset",
     "moe_pool_destroy",
 ]
 
@@ -50,7 +50,8 @@ EXPORTS = [
     "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "moe_pool_create",
     "moe_pool_prepare",
     "moe_pool_layer_forward", "moe_pool_pin",
-    "moe_pool_retire", "moe_pool_stats", "moe_pool_reset", "moe_pool_destroy",
+    "moe_pool_retire", "moe_pool_stats", "moe_pool_access_counts", "moe_pool_reset",
+    "moe_pool_destroy",
 ]
 
 
@@ -134,6 +135,7 @@ def _declare(L):
         "moe_pool_pin": (i32, [vp, i32, vp, i32]),
         "moe_pool_retire": (i32, [vp, i32, vp]),
         "moe_pool_stats": (i32, [vp, C.POINTER(PoolStats)]),
+        "moe_pool_access_counts": (i32, [vp, vp, vp]),
         "moe_pool_reset": (i32, [vp]),
         "moe_pool_destroy": (i32, [vp]),
     }
@@ -393,6 +395,16 @@ def moe_pool_stats(pool):
     st = PoolStats()
     _check(lib().moe_pool_stats(pool, C.byref(st)))
     return st
+
+
+def moe_pool_access_counts(pool, layers, experts):
+    """Per-(layer, expert) (hits, misses) since creation or the last reset, as
+    two int64 numpy arrays of shape (layers, experts)."""
+    import numpy as np
+    h = np.zeros((layers, experts), np.int64)
+    m = np.zeros((layers, experts), np.int64)
+    _check(lib().moe_pool_access_counts(pool, h.ctypes.data, m.ctypes.data))
+    return h, m
 
 
 def moe_pool_reset(pool):

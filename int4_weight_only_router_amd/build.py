@@ -22,9 +22,10 @@ HIP_SOURCES = ["moe_api.cpp", "k_route.hip", "k_permute.hip", "k_ffn_decode.hip"
                "k_ffn_grouped.hip", "k_ffn_small.hip", "k_combine.hip", "k_combine_route.hip", "k_quant.hip", "pool_hip.cpp",
                "prepack_host.cpp"]
 HEADERS = ["moe_common.h", "k_w4_frag.h", "k_decode_frag.h", "k_sort_common.h", "k_combine_tile.h",
-           "pool_core.h"]
+           "pool_core.h", "trace.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_LIB = "/opt/rocm/lib"
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
     # no packed-fp32 instructions are generated (scalar fp32 only)
@@ -70,7 +71,9 @@ def build(force: bool = True, jobs: int = 8) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(compile_one, HIP_SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    # roctx ranges (trace.h) come from the ROCm profiler SDK's roctx library
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs +
+         ["-L", ROCM_LIB, "-Wl,-rpath," + ROCM_LIB, "-lrocprofiler-sdk-roctx"])
     os.replace(tmp, LIB)
     tmp = POOL_HOST_LIB + ".tmp%d" % os.getpid()
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-D__HIP_PLATFORM_AMD__",

@@ -7,6 +7,7 @@
 #include <string>
 
 #include "moe_common.h"
+#include "trace.h"
 
 namespace moe {
 
@@ -166,6 +167,7 @@ const char *moe_last_error(void) { return g_err.c_str(); }
 
 int moe_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     if (ws_bytes == 0)
         return MOE_OK;
@@ -214,6 +216,7 @@ static int check_fmt(const char *fn, int fmt)
 int moe_quantize_experts_fmt(const float *wg, const float *wu, const float *wd, int n, int H,
                              int I, int group, int fmt, void *blobs, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     if (!wg || !wu || !wd || !blobs || n < 0)
         return set_error(MOE_EINVAL, "moe_quantize_experts: null pointer or n < 0");
@@ -228,6 +231,7 @@ int moe_quantize_experts_fmt(const float *wg, const float *wu, const float *wd, 
 int moe_quantize_experts(const float *wg, const float *wu, const float *wd, int n, int H, int I,
                          int group, void *blobs, hipStream_t stream)
 {
+    MOE_API_RANGE();
     return moe_quantize_experts_fmt(wg, wu, wd, n, H, I, group, MOE_FMT_SYM, blobs, stream);
 }
 
@@ -252,6 +256,7 @@ static int prepack_common(const char *fn, const void *src, int n, int H, int I, 
 int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *dst,
                         hipStream_t stream)
 {
+    MOE_API_RANGE();
     return prepack_common("moe_prepack_experts", src, n, H, I, group, MOE_FMT_SYM, dst, 0,
                           stream);
 }
@@ -259,18 +264,21 @@ int moe_prepack_experts(const void *src, int n, int H, int I, int group, void *d
 int moe_unpack_experts(const void *src, int n, int H, int I, int group, void *dst,
                        hipStream_t stream)
 {
+    MOE_API_RANGE();
     return prepack_common("moe_unpack_experts", src, n, H, I, group, MOE_FMT_SYM, dst, 1, stream);
 }
 
 int moe_prepack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
                             hipStream_t stream)
 {
+    MOE_API_RANGE();
     return prepack_common("moe_prepack_experts_fmt", src, n, H, I, group, fmt, dst, 0, stream);
 }
 
 int moe_unpack_experts_fmt(const void *src, int n, int H, int I, int group, int fmt, void *dst,
                            hipStream_t stream)
 {
+    MOE_API_RANGE();
     return prepack_common("moe_unpack_experts_fmt", src, n, H, I, group, fmt, dst, 1, stream);
 }
 
@@ -303,6 +311,7 @@ int moe_route(const void *x_f16, const void *w_router_f16, const float *logit_bi
               int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w, void *ws,
               size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     int rc = check_route_args("moe_route", x_f16, w_router_f16, T, H, E, k, flags, topk_idx,
                               topk_w);
@@ -334,6 +343,7 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
                       int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                       void *ws, size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     int rc = check_route_args("moe_route_permute", x_f16, w_router_f16, T, H, E, k, flags,
                               topk_idx, topk_w);
@@ -367,6 +377,7 @@ int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,
                               int32_t *topk_idx, float *topk_w, int32_t *counts, int32_t *offsets,
                               int32_t *perm, int32_t *inv_perm, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     int rc = check_route_args("moe_route_permute_noalloc", x_f16, w_router_f16, T, H, E, k,
                               flags, topk_idx, topk_w);
@@ -398,6 +409,7 @@ size_t moe_permute_workspace_bytes(int T, int k, int E)
 int moe_permute(const int32_t *topk_idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
                 int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     int rc = check_route_shape("moe_permute", T, E, k);
     if (rc)
@@ -453,6 +465,7 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
                          int group, int regime, void *y, int y_dtype, int y_slices, void *ws,
                          size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     int r = 0, dt = 0, sl = 0;
     size_t need = 0;
     int rc = moe_expert_ffn_plan(T, H, I, E, k, group, regime, &r, &dt, &sl, &need);
@@ -491,6 +504,7 @@ int moe_shared_ffn_f16(const void *x_f16, const void *wg, const void *wu, const 
                        int H, int Is, float *out_f32, void *ws, size_t ws_bytes,
                        hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     if (T < 0 || H <= 0 || Is <= 0)
         return set_error(MOE_EINVAL, "moe_shared_ffn_f16: bad sizes T=%d H=%d Is=%d", T, H, Is);
@@ -536,6 +550,7 @@ int moe_combine(const void *y, int y_dtype, int y_slices, const int32_t *inv_per
                 const float *topk_w, const float *shared_f32, const void *residual_f16, int T,
                 int H, int k, void *out_f16, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     const int rc = check_combine_args("moe_combine", y, y_dtype, y_slices, inv_perm, topk_w, T,
                                       H, k, out_f16);
@@ -550,6 +565,7 @@ int moe_combine_gated(const void *y, int y_dtype, int y_slices, const int32_t *i
                       const void *shared_gate_w_f16, const void *residual_f16, int T, int H,
                       int k, void *out_f16, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     const int rc = check_combine_args("moe_combine_gated", y, y_dtype, y_slices, inv_perm,
                                       topk_w, T, H, k, out_f16);
@@ -587,6 +603,7 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
                               int32_t *offsets, int32_t *perm, int32_t *inv_perm_next, void *ws,
                               size_t ws_bytes, hipStream_t stream)
 {
+    MOE_API_RANGE();
     clear_error();
     const char *fn = "moe_combine_route_permute";
     int rc = check_combine_args(fn, y, y_dtype, y_slices, inv_perm, topk_w, T, H, k, out_f16);

@@ -57,8 +57,30 @@ class SlotPool {
     std::vector<Layer> layers;
     int64_t clock = 0;
     moe_pool_stats_t tot{};
+    // per (layer, expert), index l*E + e: routed uses that hit a resident
+    // slot and uses that missed, since creation or the last reset
+    std::vector<int64_t> use_hits, use_misses;
 
     int nslots() const { return cfg.capacity + cfg.spares; }
+
+    // a committed generation: every routed expert is a use, a hit unless it
+    // is among the misses
+    void count_uses(int l, const std::vector<char> &inR, const std::vector<int> &misses)
+    {
+        const size_t b = (size_t)l * cfg.experts;
+        for (int e = 0; e < cfg.experts; ++e)
+            use_hits[b + e] += inR[e] ? 1 : 0;
+        for (int m : misses) {
+            use_hits[b + m] -= 1;
+            use_misses[b + m] += 1;
+        }
+    }
+
+    void access_counts(int64_t *hits, int64_t *misses) const
+    {
+        std::copy(use_hits.begin(), use_hits.end(), hits);
+        std::copy(use_misses.begin(), use_misses.end(), misses);
+    }
 
     int create(const moe_pool_config &c, const void *const *pinned_src)
     {
@@ -87,6 +109,8 @@ class SlotPool {
         layers.assign(cfg.layers, Layer{});
         clock = 0;
         tot = moe_pool_stats_t{};
+        use_hits.assign((size_t)cfg.layers * cfg.experts, 0);
+        use_misses.assign((size_t)cfg.layers * cfg.experts, 0);
         for (int l = 0; l < cfg.layers; ++l) {
             Layer &L = layers[l];
             L.cnt.assign(cfg.experts, 0);
@@ -236,6 +260,7 @@ class SlotPool {
         st.misses = (int64_t)misses.size();
         st.evictions = (int64_t)victims.size();
         st.h2d_bytes = st.misses * cfg.expert_bytes;
+        count_uses(l, inR, misses);
         tot.hits += st.hits;
         tot.misses += st.misses;
         tot.evictions += st.evictions;
@@ -381,6 +406,7 @@ class SlotPool {
         st.misses = (int64_t)misses.size();
         st.evictions = 0;
         st.h2d_bytes = st.misses * cfg.expert_bytes;
+        count_uses(l, inR, misses);
         tot.hits += st.hits;
         tot.misses += st.misses;
         tot.h2d_bytes += st.h2d_bytes;

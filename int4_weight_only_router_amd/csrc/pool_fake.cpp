@@ -155,6 +155,14 @@ int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out)
     return MOE_OK;
 }
 
+int moe_pool_access_counts(moe_pool_t pool, int64_t *hits, int64_t *misses)
+{
+    if (!pool || !hits || !misses)
+        return moe::set_error(MOE_EINVAL, "null argument");
+    pool->p.access_counts(hits, misses);
+    return MOE_OK;
+}
+
 int moe_pool_reset(moe_pool_t pool)
 {
     return pool ? pool->p.reset() : moe::set_error(MOE_EINVAL, "null pool");

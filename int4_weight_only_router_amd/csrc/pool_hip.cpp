@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_common.h"
+#include "trace.h"
 #include "pool_core.h"
 
 namespace moe {
@@ -137,6 +138,7 @@ extern "C" {
 
 int moe_pool_create(const moe_pool_config *cfg, const void *const *pinned_src, moe_pool_t *out)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!cfg || !out)
         return moe::set_error(MOE_EINVAL, "moe_pool_create: null argument");
@@ -156,6 +158,7 @@ int moe_pool_create(const moe_pool_config *cfg, const void *const *pinned_src, m
 int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
                      hipStream_t compute, const void *const **d_table_out, moe_pool_stats_t *step)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool)
         return moe::set_error(MOE_EINVAL, "moe_pool_prepare: null pool");
@@ -165,6 +168,7 @@ int moe_pool_prepare(moe_pool_t pool, int layer, const int32_t *host_ids, int n,
 int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args *a,
                            hipStream_t stream, moe_pool_stats_t *step)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool || !a || !a->host_ids)
         return moe::set_error(MOE_EINVAL, "moe_pool_layer_forward: null argument");
@@ -242,6 +246,7 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
 
 int moe_pool_pin(moe_pool_t pool, int layer, const int32_t *experts, int n)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool)
         return moe::set_error(MOE_EINVAL, "moe_pool_pin: null pool");
@@ -250,6 +255,7 @@ int moe_pool_pin(moe_pool_t pool, int layer, const int32_t *experts, int n)
 
 int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool)
         return moe::set_error(MOE_EINVAL, "moe_pool_retire: null pool");
@@ -265,8 +271,18 @@ int moe_pool_stats(moe_pool_t pool, moe_pool_stats_t *out)
     return MOE_OK;
 }
 
+int moe_pool_access_counts(moe_pool_t pool, int64_t *hits, int64_t *misses)
+{
+    moe::clear_error();
+    if (!pool || !hits || !misses)
+        return moe::set_error(MOE_EINVAL, "moe_pool_access_counts: null argument");
+    pool->p.access_counts(hits, misses);
+    return MOE_OK;
+}
+
 int moe_pool_reset(moe_pool_t pool)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool)
         return moe::set_error(MOE_EINVAL, "moe_pool_reset: null pool");
@@ -275,6 +291,7 @@ int moe_pool_reset(moe_pool_t pool)
 
 int moe_pool_destroy(moe_pool_t pool)
 {
+    MOE_API_RANGE();
     moe::clear_error();
     if (!pool)
         return MOE_OK;

@@ -28,6 +28,7 @@ def L():
                                      C.POINTER(M.PoolStats)]
     lib.moe_pool_retire.argtypes = [vp, C.c_int, vp]
     lib.moe_pool_stats.argtypes = [vp, C.POINTER(M.PoolStats)]
+    lib.moe_pool_access_counts.argtypes = [vp, vp, vp]
     lib.moe_pool_reset.argtypes = [vp]
     lib.moe_pool_destroy.argtypes = [vp]
     lib.moe_pool_fake_fail_after.argtypes = [vp, C.c_long]
@@ -77,6 +78,12 @@ class FakePool:
         st = M.PoolStats()
         assert self.lib.moe_pool_stats(self.h, C.byref(st)) == 0
         return st
+
+    def access(self):
+        h = np.full((self.L, self.E), -1, np.int64)
+        m = np.full((self.L, self.E), -1, np.int64)
+        assert self.lib.moe_pool_access_counts(self.h, h.ctypes.data, m.ctypes.data) == 0
+        return h, m
 
     def close(self):
         self.lib.moe_pool_destroy(self.h)
@@ -130,6 +137,22 @@ def test_pool_matches_simulator_and_tables_are_complete(L, shift):
     assert tot.h2d_bytes == misses.sum() * P.nbytes
     assert tot.generation == len(ids)
     assert np.array_equal(P.src, P.src_copy)   # the source is never written
+    # per-(layer, expert) access counts: every routed expert of an event is a
+    # use; the simulator's miss list of the event names the misses
+    uses = np.zeros((Lyr, E), np.int64)
+    miss = np.zeros((Lyr, E), np.int64)
+    for l, R, m in zip(layers, ids, ml):
+        uses[l, R] += 1
+        for e in m:
+            if e >= 0:
+                miss[l, e] += 1
+    ah, am = P.access()
+    assert np.array_equal(am, miss)
+    assert np.array_equal(ah, uses - miss)
+    assert L.moe_pool_reset(P.h) == 0
+    ah, am = P.access()
+    assert not ah.any() and not am.any()
+    assert L.moe_pool_access_counts(P.h, None, am.ctypes.data) == M.MOE_EINVAL
     P.close()
 
 
