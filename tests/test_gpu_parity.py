@@ -426,6 +426,26 @@ def test_shared_ffn(T):
     check_close(_np(out)[toks], ref, "shared T=%d" % T)
 
 
+@pytest.mark.parametrize("T", [2048, 4000, 4096, 8192])
+def test_shared_ffn_wide_tiles(T):
+    """The 60-expert layer's shared expert (I_s = 5632) at large batches: the
+    eight-wave 256 x 256 / 128 x 256 tiles of the FP16 GEMM, with a ragged
+    last row tile at 4000 tokens; 24 sampled tokens against the oracle."""
+    cfg = MI.QWEN
+    say("shared wide T=%d" % T)
+    wg, wu, wd = MI.gen_shared(cfg)
+    x = MI.gen_x(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.float32, device=DEV)
+    wsb = M.moe_shared_ffn_workspace_bytes(T, cfg.H, cfg.Is)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    M.moe_shared_ffn_f16(f16(x), f16(wg), f16(wu), f16(wd), T, cfg.H, cfg.Is, out, ws, wsb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(T)
+    toks = np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 22, replace=False)]))
+    ref = O.shared_ffn(x, wg, wu, wd, toks=toks)
+    check_close(_np(out)[toks], ref, "shared wide T=%d" % T)
+
+
 # --------------------------------------------------------------- combine
 
 def _assert_combine_close(got, ref16, ref64, absum, nterms, extra=0.0):
