@@ -21,9 +21,12 @@
 //     half and this call's tag in the high half, so a reader that sees the
 //     tag sees the value (no acknowledgement, fence or ticket needed);
 //  3. block 0 then polls the 64 x 64 tagged words until every tag is this
-//     call's, folds each logit's 64 partials in the butterfly order of the
-//     pinned logit sum (pinned_fold64), adds the bias, selects, weights and
-//     sorts as moe_route_permute does for one token (one_token_select), and
+//     call's -- each of its four waves 16 partials of every logit, which
+//     meet in LDS (one wave issuing all 64 loads per lane took 1.8 us from
+//     the last store to the last tag seen, four waves 1.1 us) -- and wave 0
+//     folds each logit's 64 partials in the butterfly order of the pinned
+//     logit sum (pinned_fold64), adds the bias, selects, weights and sorts
+//     as moe_route_permute does for one token (one_token_select), and
 //     advances the call counter.
 // Only block 0 waits, and only for blocks that never wait, so the wait ends
 // whenever one more block can run beside it; a poll limit bounds it anyway.
@@ -62,6 +65,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     __shared__ CombineTileSmem sm[1];
     __shared__ __align__(16) f16 xs[32];
     __shared__ __align__(16) uint64_t keys[64];
+    __shared__ float pl[64][64];   // block 0: the gathered logit partials
 
     const int j = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -83,46 +87,60 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     const PartialCols<PM> cols{j, NCL};
     const f16 o = combine_tile<GATED, 1>(y, S, inv_perm, w, shared, x, wsg, residual, 1, 0, H,
                                          k, 8 * NCL, cols, nullptr, sm, threadIdx.x);
-    if (wave != 0)
+    if (wave != 0 && j != 0)
         return;
-    if (lane < 8 * NCL) {
-        xs[lane] = o;
-        out[cols.col(0, lane)] = o;
-    }
-    __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
     const unsigned tag = 0x7FC00000u | ((c + 1u) & 0x3FFFFFu);
-    float acc = 0.0f;
+    if (wave == 0) {
+        if (lane < 8 * NCL) {
+            xs[lane] = o;
+            out[cols.col(0, lane)] = o;
+        }
+        __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+        float acc = 0.0f;
 #pragma unroll
-    for (int m = 0; m < NCL; ++m) {
-        const half8_t xh = *reinterpret_cast<const half8_t *>(xs + 8 * m);
-        const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
+        for (int m = 0; m < NCL; ++m) {
+            const half8_t xh = *reinterpret_cast<const half8_t *>(xs + 8 * m);
+            const half8_t wh = __builtin_bit_cast(half8_t, wv[m]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc = __builtin_fmaf((float)xh[i], (float)wh[i], acc);
+            for (int i = 0; i < 8; ++i)
+                acc = __builtin_fmaf((float)xh[i], (float)wh[i], acc);
+        }
+        __hip_atomic_store(xchg + j * 64 + lane,
+                           ((uint64_t)tag << 32) | __builtin_bit_cast(unsigned, acc),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __hip_atomic_store(xchg + j * 64 + lane,
-                       ((uint64_t)tag << 32) | __builtin_bit_cast(unsigned, acc),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (j != 0)
         return;
 
-    // block 0: lane e gathers the 64 partials of expert e's logit (partial
-    // jj >= gridDim.x has no chunk and is zero, as in the one-launch router)
-    // with agent-scope loads until every tag is this call's.
+    // block 0: wave w gathers partials 16w .. 16w+15 of every expert's logit
+    // (lane e: expert e; partial jj >= gridDim.x has no chunk and is zero, as
+    // in the one-launch router) with agent-scope loads until every tag is
+    // this call's, and leaves them in LDS for wave 0
     const int nb = gridDim.x;
-    float p[64];
+    float pv[16];
     for (int it = 0; it < CR_MAX_POLLS; ++it) {
         bool mine = true;
 #pragma unroll
-        for (int jj = 0; jj < 64; ++jj) {
+        for (int i = 0; i < 16; ++i) {
+            const int jj = 16 * wave + i;
             const uint64_t q = __hip_atomic_load(xchg + min(jj, nb - 1) * 64 + lane,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            p[jj] = jj < nb ? __builtin_bit_cast(float, (unsigned)q) : 0.0f;
+            pv[i] = jj < nb ? __builtin_bit_cast(float, (unsigned)q) : 0.0f;
             mine = mine && (unsigned)(q >> 32) == tag;
         }
         if (__ballot(!mine) == 0)
             break;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        pl[16 * wave + i][lane] = pv[i];
+    __syncthreads();
+    if (wave != 0)
+        return;
+    float p[64];
+#pragma unroll
+    for (int jj = 0; jj < 64; ++jj)
+        p[jj] = pl[jj][lane];
     float l = pinned_fold64(p);
     if (bias)
         l = l + (lane < E ? bias[lane] : 0.0f);
