@@ -521,7 +521,11 @@ int moe_pool_retire(moe_pool_t pool, int layer, hipStream_t compute);
  * resident model -- in one host call, with the same readings as the calls it
  * chains: moe_route_permute on `stream`; the T*k routed ids copied into
  * host_ids (pinned host memory) and waited for (this call blocks the calling
- * thread until they arrive); moe_pool_prepare on this layer; the routed
+ * thread until they arrive; for one token of at most 64 experts the routing
+ * kernel itself writes them, then a sequence flag, into the pool's own
+ * coherent pinned buffer and the thread spins on the flag, MOE_EHIP after
+ * 10 s, instead of a device-to-host copy and an event wait); moe_pool_prepare
+ * on this layer; the routed
  * expert FFN (moe_expert_ffn_w4a16 with the published table and `regime`);
  * moe_pool_retire; moe_combine into out_f16.  E is the pool's expert count.
  * When the routed set has both hits and misses and the decode kernel runs,

@@ -310,7 +310,8 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
     const f16 *__restrict__ x, const f16 *__restrict__ wr, const float *__restrict__ bias,
     int T, int E, int k, unsigned flags, unsigned *ticket, float *ws_logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
+    HostMirror hm)
 {
     constexpr int RSPLIT_EPW = rsplit_epw(BIGE);
     constexpr int NCH = H / 8;
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
             if (lane == 0)
                 __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             one_token_select(l, E, k, flags, reinterpret_cast<uint64_t *>(smem), idx_out, w_out,
-                             counts, offsets, perm, inv_perm, lane);
+                             counts, offsets, perm, inv_perm, lane, hm);
             return;
         }
     }
@@ -463,7 +464,7 @@ template <int H>
 static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, int T, int E,
                                 int k, unsigned flags, int32_t *idx, float *w, int32_t *counts,
                                 int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
-                                hipStream_t s)
+                                hipStream_t s, HostMirror hm = HostMirror{nullptr, nullptr, 0u})
 {
     unsigned *ticket = static_cast<unsigned *>(ws);
     float *lg = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
@@ -477,11 +478,11 @@ static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, 
     if (E > 128)                                                                                \
         hipLaunchKernelGGL((route_split_kernel<H, TT, true, true>), grid, block, lds, s, x, wr,  \
                            bias, T, E, k, flags, ticket, lg, idx, w, counts, offsets, perm,      \
-                           inv_perm);                                                            \
+                           inv_perm, hm);                                                        \
     else                                                                                        \
         hipLaunchKernelGGL((route_split_kernel<H, TT, true, false>), grid, block, lds, s, x, wr, \
                            bias, T, E, k, flags, ticket, lg, idx, w, counts, offsets, perm,      \
-                           inv_perm)
+                           inv_perm, hm)
     if (T <= 1) MOE_RSPLIT(1);
     else if (T <= 2) MOE_RSPLIT(2);
     else if (T <= 4) MOE_RSPLIT(4);
@@ -506,6 +507,30 @@ int launch_route_split(const void *x, const void *wr, const float *bias, int T, 
                                                  offsets, perm, inv_perm, ws, s);
     case 2048: return launch_route_split_h<2048>(xh, wh, bias, T, E, k, flags, idx, w, counts,
                                                  offsets, perm, inv_perm, ws, s);
+    default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
+    }
+}
+
+// One token of at most 64 experts with the routed ids also mirrored into
+// host memory (the slot pool's wait for them): the fused route + permute of
+// launch_route_split, bit for bit.  ws as for launch_route_split.
+int launch_route_split_mirrored(const void *x, const void *wr, const float *bias, int H, int E,
+                                int k, unsigned flags, int32_t *idx, float *w, int32_t *counts,
+                                int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
+                                HostMirror hm, hipStream_t s)
+{
+    if (E > 64 || !hm.ids || !hm.flag)
+        return set_error(MOE_EINVAL, "route: host mirror needs one token of at most 64 experts");
+    const f16 *xh = static_cast<const f16 *>(x), *wh = static_cast<const f16 *>(wr);
+    switch (H) {
+    case 256: return launch_route_split_h<256>(xh, wh, bias, 1, E, k, flags, idx, w, counts,
+                                               offsets, perm, inv_perm, ws, s, hm);
+    case 512: return launch_route_split_h<512>(xh, wh, bias, 1, E, k, flags, idx, w, counts,
+                                               offsets, perm, inv_perm, ws, s, hm);
+    case 1024: return launch_route_split_h<1024>(xh, wh, bias, 1, E, k, flags, idx, w, counts,
+                                                 offsets, perm, inv_perm, ws, s, hm);
+    case 2048: return launch_route_split_h<2048>(xh, wh, bias, 1, E, k, flags, idx, w, counts,
+                                                 offsets, perm, inv_perm, ws, s, hm);
     default: return set_error(MOE_EUNSUPPORTED, "route: H=%d not instantiated", H);
     }
 }

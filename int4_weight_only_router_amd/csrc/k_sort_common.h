@@ -174,14 +174,16 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e)
 // fixed-order wave sum.  Writes the k selected (idx, weight) pairs in rank
 // order and the stable sort of one token's k distinct experts: counts 0/1,
 // offsets = selected experts of lower id (offsets[E] = k), perm[off] = rank,
-// inv_perm[rank] = off.
+// inv_perm[rank] = off.  With a host mirror (HostMirror) the selected ids
+// are also written there, then the mirror's flag.
 __device__ __forceinline__ void one_token_select(float l, int E, int k, unsigned flags,
                                                  uint64_t *bkey, int32_t *__restrict__ idx_out,
                                                  float *__restrict__ w_out,
                                                  int32_t *__restrict__ counts,
                                                  int32_t *__restrict__ offsets,
                                                  int32_t *__restrict__ perm,
-                                                 int32_t *__restrict__ inv_perm, int lane)
+                                                 int32_t *__restrict__ inv_perm, int lane,
+                                                 HostMirror hm = HostMirror{nullptr, nullptr, 0u})
 {
     const int e = lane;
     const bool valid = e < E;
@@ -214,6 +216,14 @@ __device__ __forceinline__ void one_token_select(float l, int E, int k, unsigned
     if (sel) {
         idx_out[rank] = e;
         w_out[rank] = p;
+        if (hm.ids)
+            __hip_atomic_store(hm.ids + rank, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (hm.ids) {
+        // the fence's wait covers the id stores of every lane of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        if (lane == 0)
+            __hip_atomic_store(hm.flag, hm.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     // position = selected experts of lower id, flat index = rank
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -34,6 +34,9 @@ size_t route_split_ws_bytes(int T, int E);
 size_t route_batched_ws_bytes(int T, int E);
 int launch_route_batched(const void *, const void *, const float *, int, int, int, int, unsigned,
                          int32_t *, float *, void *, hipStream_t);
+int launch_route_split_mirrored(const void *, const void *, const float *, int, int, int, unsigned,
+                                int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *,
+                                void *, HostMirror, hipStream_t);
 int launch_route_split(const void *, const void *, const float *, int, int, int, int, unsigned,
                        int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *, void *,
                        hipStream_t);
@@ -338,13 +341,19 @@ size_t moe_route_permute_workspace_bytes(int T, int k, int E)
     return ROUTE_TICKET_BYTES + route_batched_ws_bytes(T, E) + permute_ws_bytes(T, k, E);
 }
 
-int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T,
-                      int H, int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w,
-                      int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
-                      void *ws, size_t ws_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace moe {
+// moe_route_permute; with a host mirror (hm.ids set) and one token of at most
+// 64 experts, the fused launch also writes the routed ids and the mirror's
+// flag into host memory (*mirrored = true).
+int route_permute_mirror(const void *x_f16, const void *w_router_f16, const float *logit_bias,
+                         int T, int H, int E, int k, unsigned flags, int32_t *topk_idx,
+                         float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                         int32_t *inv_perm, void *ws, size_t ws_bytes, HostMirror hm,
+                         bool *mirrored, hipStream_t stream)
 {
-    MOE_API_RANGE();
-    clear_error();
+    *mirrored = false;
     int rc = check_route_args("moe_route_permute", x_f16, w_router_f16, T, H, E, k, flags,
                               topk_idx, topk_w);
     if (rc)
@@ -355,6 +364,12 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
     if (need && (!ws || ws_bytes < need))
         return set_error(MOE_ENOMEM, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes,
                          need);
+    if (hm.ids && T == 1 && E <= 64 && k <= 64 && route_fused(T, E)) {
+        *mirrored = true;
+        return launch_route_split_mirrored(x_f16, w_router_f16, logit_bias, H, E, k, flags,
+                                           topk_idx, topk_w, counts, offsets, perm, inv_perm, ws,
+                                           hm, stream);
+    }
     if (route_fused(T, E))
         return launch_route_split(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
                                   topk_w, counts, offsets, perm, inv_perm, ws, stream);
@@ -370,6 +385,22 @@ int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *
         pws = lws + route_batched_ws_bytes(T, E);
     }
     return launch_permute(topk_idx, T, k, E, counts, offsets, perm, inv_perm, pws, stream);
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_route_permute(const void *x_f16, const void *w_router_f16, const float *logit_bias, int T,
+                      int H, int E, int k, unsigned flags, int32_t *topk_idx, float *topk_w,
+                      int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_API_RANGE();
+    clear_error();
+    bool mirrored = false;
+    return route_permute_mirror(x_f16, w_router_f16, logit_bias, T, H, E, k, flags, topk_idx,
+                                topk_w, counts, offsets, perm, inv_perm, ws, ws_bytes,
+                                HostMirror{nullptr, nullptr, 0u}, &mirrored, stream);
 }
 
 int moe_route_permute_noalloc(const void *x_f16, const void *w_router_f16,

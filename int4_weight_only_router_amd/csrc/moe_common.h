@@ -16,6 +16,16 @@ namespace moe {
 // Layout flags of the decode partials passed to the decode kernel: rows in
 // token order, columns in partial-major order (MOE_Y_PARTIAL_ORDER).
 constexpr int YF_TOKEN_ORDER = 1, YF_PARTIAL_ORDER = 2;
+
+// Routed ids of one token mirrored into coherent pinned host memory by the
+// routing kernel: ids[0..k) in rank order, then -- after a system-scope
+// release -- *flag = seq, so a host thread that sees the flag sees the ids
+// (no device-to-host copy, no event).  ids == nullptr: no mirror.
+struct HostMirror {
+    int32_t *ids;
+    unsigned *flag;
+    unsigned seq;
+};
 inline int decode_yflags(int regime)
 {
     return ((regime & MOE_Y_TOKEN_ORDER) ? YF_TOKEN_ORDER : 0) |

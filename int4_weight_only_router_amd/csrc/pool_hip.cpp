@@ -3,6 +3,11 @@
 // a side stream; the compute stream waits on an event recorded after the
 // copies and the table upload; a per-layer retirement event recorded on the
 // compute stream guards reuse of evicted slots and of the older table buffer.
+// A pooled layer of one token gets its routed ids from the routing kernel
+// itself, written into coherent pinned host memory with a sequence flag.
+#include <chrono>
+#include <cstring>
+
 #include <hip/hip_runtime.h>
 
 #include "moe_common.h"
@@ -20,6 +25,12 @@ struct HipPoolBackend {
     hipStream_t side = nullptr;
     std::vector<hipEvent_t> retire_ev, copies_ev, upload_ev;
     hipEvent_t ids_ev = nullptr;         // routed ids on the host (moe_pool_layer_forward)
+    // one token's routed ids written into host memory by the routing kernel
+    // (coherent pinned memory: 64 ids, then the flag at byte 256)
+    void *mirror = nullptr;
+    int32_t *mirror_ids_dev = nullptr;
+    unsigned *mirror_flag_dev = nullptr;
+    unsigned mirror_seq = 0;
     std::vector<char> retired, uploaded;
 
     int init(const moe_pool_config &c)
@@ -47,7 +58,18 @@ struct HipPoolBackend {
             for (auto &ev : *v)
                 MOE_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
         MOE_HIP_TRY(hipEventCreateWithFlags(&ids_ev, hipEventDisableTiming));
+        MOE_HIP_TRY(hipHostMalloc(&mirror, 512, hipHostMallocCoherent));
+        std::memset(mirror, 0, 512);
+        void *dev = nullptr;
+        MOE_HIP_TRY(hipHostGetDevicePointer(&dev, mirror, 0));
+        mirror_ids_dev = static_cast<int32_t *>(dev);
+        mirror_flag_dev = reinterpret_cast<unsigned *>(static_cast<char *>(dev) + 256);
         return MOE_OK;
+    }
+    const int32_t *mirror_ids() const { return static_cast<const int32_t *>(mirror); }
+    const unsigned *mirror_flag() const
+    {
+        return reinterpret_cast<const unsigned *>(static_cast<const char *>(mirror) + 256);
     }
     void *slot_ptr(int l, int s) { return slots + ((size_t)l * nslots + s) * cfg.expert_bytes; }
     int wait_retired(int l)
@@ -111,6 +133,9 @@ struct HipPoolBackend {
             (void)hipStreamDestroy(side);
         if (staging)
             (void)hipHostFree(staging);
+        if (mirror)
+            (void)hipHostFree(mirror);
+        mirror = nullptr;
         if (tables)
             (void)hipFree(tables);
         if (slots)
@@ -128,6 +153,10 @@ namespace moe {
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
                       const void *const *, int, int, int, int, int, int, int, int, float *,
                       hipStream_t);
+int route_permute_mirror(const void *, const void *, const float *, int, int, int, int, unsigned,
+                         int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *, void *,
+                         size_t, HostMirror, bool *, hipStream_t);
+constexpr double MIRROR_WAIT_S = 10.0;   // far beyond any routing launch
 }
 
 struct moe_pool {
@@ -177,12 +206,35 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
         return moe::set_error(MOE_EINVAL, "moe_pool_layer_forward: bad layer %d", layer);
     const int E = P.cfg.experts;
     const int n = a->T * a->k;
-    int rc = moe_route_permute(a->x_f16, a->w_router_f16, a->logit_bias, a->T, a->H, E, a->k,
-                               a->flags, a->topk_idx, a->topk_w, a->counts, a->offsets, a->perm,
-                               a->inv_perm, a->route_ws, a->route_ws_bytes, stream);
+    // one token: the routing kernel writes the routed ids and then a fresh
+    // sequence number into host memory, and this thread spins on it (no
+    // device-to-host copy, no event); other shapes copy the ids and wait on
+    // an event
+    unsigned seq = ++P.be.mirror_seq;
+    if (seq == 0)
+        seq = ++P.be.mirror_seq;
+    bool mirrored = false;
+    int rc = moe::route_permute_mirror(
+        a->x_f16, a->w_router_f16, a->logit_bias, a->T, a->H, E, a->k, a->flags, a->topk_idx,
+        a->topk_w, a->counts, a->offsets, a->perm, a->inv_perm, a->route_ws, a->route_ws_bytes,
+        moe::HostMirror{P.be.mirror_ids_dev, P.be.mirror_flag_dev, seq}, &mirrored, stream);
     if (rc)
         return rc;
-    if (n > 0) {
+    if (mirrored) {
+        const auto t0 = std::chrono::steady_clock::now();
+        for (unsigned it = 0; __atomic_load_n(P.be.mirror_flag(), __ATOMIC_ACQUIRE) != seq; ++it) {
+            if ((it & 4095) == 4095 &&
+                std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() >
+                    moe::MIRROR_WAIT_S) {
+                const hipError_t e = hipStreamQuery(stream);
+                return moe::set_error(MOE_EHIP,
+                                      "moe_pool_layer_forward: routed ids not in host memory "
+                                      "after %.0f s (stream: %s)",
+                                      moe::MIRROR_WAIT_S, hipGetErrorString(e));
+            }
+        }
+        std::memcpy(a->host_ids, P.be.mirror_ids(), (size_t)n * sizeof(int32_t));
+    } else if (n > 0) {
         hipError_t err = hipMemcpyAsync(a->host_ids, a->topk_idx, (size_t)n * sizeof(int32_t),
                                         hipMemcpyDeviceToHost, stream);
         if (err == hipSuccess)
