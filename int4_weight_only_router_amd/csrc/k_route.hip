@@ -387,6 +387,128 @@ __global__ __launch_bounds__(rsplit_epw(BIGE) * 64) void route_split_kernel(
     if (!s_last)
         return;
 
+    if constexpr (FUSE && BIGE && TT == 1) {
+        if (E <= RSPLIT_EPW * 64 && k <= 64) {
+            // One token of 129..1024 experts: every wave of the workgroup,
+            // thread e holding expert e.  A radix select over the unique
+            // 64-bit selection keys (topk_key: the logit's order code, then
+            // 0xFFFF - e; bits 16..31 are zero and skipped) finds the k-th
+            // largest key four bits per round: each wave counts its
+            // candidates per digit with 16 ballots, the counts meet in LDS
+            // (double-buffered: one barrier per round), and every wave
+            // derives the same bucket; the rounds stop once the bucket holds
+            // exactly the keys still wanted.  The selected experts in id
+            // order are the sort (position = selected experts of lower id);
+            // wave 0 ranks the k selected keys and forms the softmax exactly
+            // as the general path does (same terms, same order).
+            int *hist = reinterpret_cast<int *>(smem);                           // [2][16][16]
+            float *lgs = reinterpret_cast<float *>(smem + 2048);                 // [E <= 1024]
+            int *wcnt = reinterpret_cast<int *>(smem + 2048 + 4096);             // [16]
+            uint64_t *lkey = reinterpret_cast<uint64_t *>(smem + 2048 + 4096 + 64);   // [64]
+            int *lidx = reinterpret_cast<int *>(lkey + 64);                      // [64]
+            int *rke = lidx + 64;                                                // [64]
+            const int e = threadIdx.x;
+            const bool valid = e < E;
+            const float lv = valid ? __hip_atomic_load(ws_logits + e, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0.0f;
+            if (valid)
+                lgs[e] = lv;
+            if (threadIdx.x == 0)
+                __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t key = valid ? topk_key(lv, e) : 0ull;
+            uint64_t prefix = 0, pmask = 0;
+            int r = k;
+            for (int round = 0; round < 12; ++round) {
+                const int sh = round < 8 ? 60 - 4 * round : 44 - 4 * round;   // 60..32, 12..0
+                const bool cand = valid && (key & pmask) == prefix;
+                const int dig = (int)((key >> sh) & 15u);
+                int mycnt = 0;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int c = __popcll(__ballot(cand && dig == v));
+                    mycnt = lane == v ? c : mycnt;
+                }
+                int *h = hist + (round & 1) * 256;
+                if (lane < 16)
+                    h[wave * 16 + lane] = mycnt;
+                __syncthreads();
+                int tot = 0;
+                if (lane < 16)
+                    for (int w = 0; w < RSPLIT_EPW; ++w)
+                        tot += h[w * 16 + lane];
+                int S = tot;   // lane v < 16: candidates with digit >= v
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    const int o = __shfl_down(S, off, 16);
+                    S += lane + off < 16 ? o : 0;
+                }
+                const uint64_t bal = __ballot(lane < 16 && S >= r);
+                const int d = 63 - __clzll((long long)bal);   // S_0 >= r: bal is never empty
+                const int above = d < 15 ? __shfl(S, d + 1, 64) : 0;
+                const int totd = __shfl(tot, d, 64);
+                r -= above;
+                prefix |= (uint64_t)d << sh;
+                pmask |= (uint64_t)15 << sh;
+                if (totd == r)
+                    break;   // the same round in every wave
+            }
+            const bool sel = valid && key >= prefix;
+            const uint64_t sb = __ballot(sel);
+            const int below = __popcll(sb & ((1ull << lane) - 1ull));
+            if (lane == 0)
+                wcnt[wave] = __popcll(sb);
+            __syncthreads();
+            int pos = below;
+            for (int w = 0; w < wave; ++w)
+                pos += wcnt[w];
+            if (valid) {
+                counts[e] = sel ? 1 : 0;
+                offsets[e] = pos;
+            }
+            if (e == E - 1)
+                offsets[E] = k;
+            if (sel) {
+                lkey[pos] = key;
+                lidx[pos] = e;
+            }
+            __syncthreads();
+            if (wave != 0)
+                return;
+            // lane j < k: the selected expert at position j (id order), its rank
+            const uint64_t mk = lane < k ? lkey[lane] : 0ull;
+            int rank = 0;
+            for (int j = 0; j < k; ++j)
+                rank += lkey[j] > mk ? 1 : 0;
+            if (lane < k) {
+                rke[rank] = lidx[lane];
+                perm[lane] = rank;
+                inv_perm[rank] = lane;
+            }
+            __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+            const int er = lane < k ? rke[lane] : 0;   // lane j: the expert ranked j
+            const float m = lgs[rke[0]];
+            float part = 0.0f;
+            for (int ee = lane; ee < E; ee += 64)
+                part += expf(lgs[ee] - m);
+            part = wave_sum_f32(part);   // softmax denominator (order fixed, not pinned)
+            const float den = part;
+            float pw = 0.0f;
+            if (lane < k)
+                pw = expf(lgs[er] - m) / den;
+            if (flags & MOE_RENORM) {
+                float ws = pw;
+                ws = wave_sum_f32(ws);
+                pw = pw / ws;
+            }
+            if (lane < k) {
+                idx_out[lane] = er;
+                w_out[lane] = pw;
+            }
+            return;
+        }
+    }
+
     if constexpr (FUSE && !BIGE && TT == 1) {
         if (E <= 64) {
             // One token of at most 64 experts: wave 0 alone, lane e holding
@@ -473,7 +595,9 @@ static int launch_route_split_h(const f16 *x, const f16 *wr, const float *bias, 
     const size_t xb = (size_t)8 * H * sizeof(f16);
     const size_t lb = (size_t)8 * E * sizeof(float) + 16 + (size_t)8 * topk_scratch_bytes(E) +
                       (size_t)8 * 16 * sizeof(Cand) + (size_t)(8 * 16 + E) * sizeof(int);
-    const size_t lds = xb > lb ? xb : lb;
+    size_t lds = xb > lb ? xb : lb;
+    if (lds < 8192)   // the one-token selection of more than 128 experts
+        lds = 8192;
 #define MOE_RSPLIT(TT)                                                                          \
     if (E > 128)                                                                                \
         hipLaunchKernelGGL((route_split_kernel<H, TT, true, true>), grid, block, lds, s, x, wr,  \
