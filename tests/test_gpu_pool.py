@@ -163,6 +163,8 @@ def test_native_pooled_layer_equals_resident_decode():
     args = [lay.pool_args(b, host_ids) for lay, b in zip(lays, bpool)]
     stream = torch.cuda.current_stream()
     misses = 0
+    uses = np.zeros((L, cfg.E), np.int64)
+    miss_map = np.zeros((L, cfg.E), np.int64)
     try:
         for s in range(steps):
             x0 = f16(MI.gen_prompt_token(cfg, 1, s))
@@ -172,9 +174,18 @@ def test_native_pooled_layer_equals_resident_decode():
                 outp = torch.empty_like(xp)
                 a = args[l]
                 a.x_f16, a.residual_f16, a.out_f16 = xp.data_ptr(), xp.data_ptr(), outp.data_ptr()
+                h0, m0 = M.moe_pool_access_counts(pool, L, cfg.E)
                 st = M.moe_pool_layer_forward(pool, l, a, stream)
                 misses += st.misses
+                # the routed ids the host got (one token: written by the
+                # routing kernel into pinned memory) are the device's
                 assert np.array_equal(host_ids.numpy(), bpool[l].topk_idx.cpu().numpy().ravel())
+                h1, m1 = M.moe_pool_access_counts(pool, L, cfg.E)
+                dh, dm = h1 - h0, m1 - m0
+                assert dh.sum() == st.hits and dm.sum() == st.misses
+                assert np.array_equal(np.flatnonzero(dh[l] + dm[l]), np.sort(host_ids.numpy()))
+                uses[l, host_ids.numpy()] += 1
+                miss_map += dm
                 torch.cuda.synchronize()
                 assert torch.equal(bpool[l].topk_idx, bref[l].topk_idx)
                 assert torch.equal(outp.view(torch.int16), outr.view(torch.int16)), (s, l)
@@ -182,6 +193,13 @@ def test_native_pooled_layer_equals_resident_decode():
         assert misses > 0
         tot = M.moe_pool_stats(pool)
         assert tot.misses == misses and tot.h2d_bytes == misses * total
+        # per-(layer, expert) access counts: every routed expert once per call
+        h, m = M.moe_pool_access_counts(pool, L, cfg.E)
+        assert np.array_equal(h + m, uses) and np.array_equal(m, miss_map)
+        assert m.sum() == misses
+        M.moe_pool_reset(pool)
+        h, m = M.moe_pool_access_counts(pool, L, cfg.E)
+        assert not h.any() and not m.any()
     finally:
         M.moe_pool_destroy(pool)
 
