@@ -45,10 +45,7 @@ constexpr int SB_D = 8;          // 32-K chunks in flight per wave
 constexpr int SB_MAXR = 32;      // rows of one expert (one MFMA column operand)
 constexpr int SB_XB = 4;         // 16-byte activation pieces per thread per staging round
 constexpr size_t SB_LDS_MAX = 156 * 1024;   // dynamic LDS of one workgroup (static part aside)
-#ifndef SB_XBUDGET_KB
-#define SB_XBUDGET_KB 40
-#endif
-constexpr size_t SB_XBUDGET = SB_XBUDGET_KB * 1024;   // staged rows per workgroup: four share a CU
+constexpr size_t SB_XBUDGET = 40 * 1024;   // staged rows per workgroup: four share a CU
 
 struct SmallArgs {
     const _Float16 *A;             // x [T][K] (gate/up) or h [T*k][K] (down)
