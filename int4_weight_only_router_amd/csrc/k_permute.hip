@@ -18,6 +18,8 @@ namespace moe {
 
 constexpr int PERM_CH = 512;     // elements per chunk in the multi-block path
 constexpr int PERM_SMALL = 512;  // up to this many elements: one wave does everything
+constexpr int PERM_BLOCK = 16384;   // up to this many (and E <= 1024): one workgroup
+constexpr int PERM_BW = 16;         // its waves
 
 // Whole sort in one wave (small T*k).
 __global__ __launch_bounds__(64) void permute_small_kernel(
@@ -27,6 +29,78 @@ __global__ __launch_bounds__(64) void permute_small_kernel(
     extern __shared__ int cnt[];   // [E]
     wave_count_scan(idx, n, E, cnt, counts, offsets, threadIdx.x);
     wave_scatter(idx, 0, n, E, cnt, perm, inv_perm, threadIdx.x);
+}
+
+// Whole sort in one workgroup of 16 waves (moderate T*k, E <= 1024): the
+// flat range is cut into 16 consecutive segments, one per wave.  Each wave
+// counts its segment into its own LDS histogram; thread e then adds expert
+// e's 16 counts, the workgroup scans them into offsets, and thread e turns
+// its column of histograms into the running positions of expert e in each
+// segment (offsets[e] + the segments before); each wave then scatters its
+// segment in order -- the multi-block path's chunks, inside one launch.
+__global__ __launch_bounds__(PERM_BW * 64) void permute_block_kernel(
+    const int32_t *__restrict__ idx, int n, int E, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm)
+{
+    extern __shared__ int hw[];   // [PERM_BW][E]
+    __shared__ int wsum[PERM_BW];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < PERM_BW * E; i += PERM_BW * 64)
+        hw[i] = 0;
+    __syncthreads();
+    const int seg = ((n + PERM_BW - 1) / PERM_BW + 63) / 64 * 64;   // elements per wave
+    const int f0 = min(n, w * seg), f1 = min(n, f0 + seg);
+    int *h = hw + w * E;
+    for (int b = f0; b < f1; b += 64 * WS_GROUPS) {   // keys loaded a batch at a time
+        int keys[WS_GROUPS];
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g) {
+            const int f = b + 64 * g + lane;
+            keys[g] = (f < f1) ? idx[f] : -1;
+        }
+#pragma unroll
+        for (int g = 0; g < WS_GROUPS; ++g)
+            if ((unsigned)keys[g] < (unsigned)E)
+                atomicAdd(&h[keys[g]], 1);
+    }
+    __syncthreads();
+    const int e = threadIdx.x;
+    int hv[PERM_BW];
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < PERM_BW; ++ww) {
+        hv[ww] = e < E ? hw[ww * E + e] : 0;
+        c += hv[ww];
+    }
+    int incl = c;   // workgroup exclusive scan of c over e
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+        const int o = __shfl_up(incl, st, 64);
+        if (lane >= st)
+            incl += o;
+    }
+    if (lane == 63)
+        wsum[w] = incl;
+    __syncthreads();
+    int pre = 0;
+    for (int i = 0; i < w; ++i)
+        pre += wsum[i];
+    const int off = pre + incl - c;
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+        int run = off;
+#pragma unroll
+        for (int ww = 0; ww < PERM_BW; ++ww) {
+            hw[ww * E + e] = run;
+            run += hv[ww];
+        }
+    }
+    if (e == 0)
+        offsets[E] = n;
+    __syncthreads();
+    wave_scatter(idx, f0, f1, E, h, perm, inv_perm, lane);
 }
 
 // Phase 1: per-chunk histograms hist[b][E].
@@ -132,10 +206,12 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
     wave_scatter(idx, f0, f1, E, cnt, perm, inv_perm, threadIdx.x);
 }
 
+static bool permute_one_block(int64_t n, int E) { return n <= PERM_BLOCK && E <= 1024; }
+
 size_t permute_ws_bytes(int T, int k, int E)
 {
     const int64_t n = (int64_t)T * k;
-    if (n <= PERM_SMALL)
+    if (n <= PERM_SMALL || permute_one_block(n, E))
         return 0;
     const int64_t nb = (n + PERM_CH - 1) / PERM_CH;
     return (size_t)(2 * nb * E * sizeof(int32_t));
@@ -149,6 +225,13 @@ int launch_permute(const int32_t *idx, int T, int k, int E, int32_t *counts, int
         hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), E * sizeof(int), s, idx, n,
                            E, counts, offsets, perm, inv_perm);
         MOE_LAUNCH_CHECK("permute_small_kernel");
+        return MOE_OK;
+    }
+    if (permute_one_block(n, E)) {
+        hipLaunchKernelGGL(permute_block_kernel, dim3(1), dim3(PERM_BW * 64),
+                           (size_t)PERM_BW * E * sizeof(int), s, idx, n, E, counts, offsets, perm,
+                           inv_perm);
+        MOE_LAUNCH_CHECK("permute_block_kernel");
         return MOE_OK;
     }
     const int nb = (n + PERM_CH - 1) / PERM_CH;
