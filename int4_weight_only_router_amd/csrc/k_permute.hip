@@ -18,7 +18,7 @@ namespace moe {
 
 constexpr int PERM_CH = 512;     // elements per chunk in the multi-block path
 constexpr int PERM_SMALL = 512;  // up to this many elements: one wave does everything
-constexpr int PERM_BLOCK = 16384;   // up to this many (and E <= 1024): one workgroup
+constexpr int PERM_BLOCK = 10240;   // up to this many (and E <= 1024): one workgroup
 constexpr int PERM_BW = 16;         // its waves
 
 // Whole sort in one wave (small T*k).
