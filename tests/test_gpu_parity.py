@@ -271,8 +271,12 @@ def _permute_gpu(idx_np, E):
 @pytest.mark.parametrize("T,k,E,skew", [(1, 8, 64, 0), (16, 2, 8, 0), (64, 8, 64, 0),
                                         (512, 8, 64, 0), (513, 8, 64, 0), (4096, 8, 64, 0),
                                         (4096, 10, 512, 1.1), (300, 16, 1024, 1.0),
-                                        (1, 1, 1, 0), (0, 8, 64, 0)])
+                                        (1024, 10, 512, 1.1), (1025, 10, 512, 1.1),
+                                        (640, 16, 1024, 0), (1, 1, 1, 0), (0, 8, 64, 0)])
 def test_permute_bit_exact(T, k, E, skew):
+    """Every sort path: one wave (T*k <= 512), one workgroup (up to 10240
+    elements, E <= 1024; 10240 itself and 10250 either side of the limit, and
+    E = 1024 with its 64 KB of per-wave histograms), chunked launches above."""
     say("permute T=%d k=%d E=%d" % (T, k, E))
     rng = np.random.default_rng(T * 7 + E)
     p = None
