@@ -297,15 +297,16 @@ int moe_expert_ffn_plan(int T, int H, int I, int E, int k, int group, int regime
  * uses FP16 activations and FP32 accumulation, and never keeps an expanded
  * expert).  For each sorted row p of expert e and token t = perm[p] / k:
  *   h = silu(Wg[e] x_t) * (Wu[e] x_t),   y_p = Wd[e] h,   W = q * s.
- *   x_f16          device fp16 [T][H]
+ *   x_f16          device fp16 [T][H]; 16-byte aligned
  *   perm, offsets  device, from moe_permute
  *   d_expert_blobs device array of E device pointers to prepacked blobs
  *                  (moe_prepack_experts); an entry may be NULL only for an
  *                  expert no token routes to, except in the DECODE regime,
  *                  where a routed expert with a NULL entry is skipped (its y
  *                  rows are left unwritten for another launch to fill)
- *   y              device output, layout from moe_expert_ffn_plan; y_dtype
- *                  and y_slices must equal the plan's (MOE_EINVAL otherwise).
+ *   y              device output, layout from moe_expert_ffn_plan, 16-byte
+ *                  aligned; y_dtype and y_slices must equal the plan's
+ *                  (MOE_EINVAL otherwise).
  *                  Row p holds sorted row p; with MOE_Y_TOKEN_ORDER in regime
  *                  (DECODE only) the result of sorted row p goes to row
  *                  perm[p] = t*k + j instead, so that moe_combine needs no

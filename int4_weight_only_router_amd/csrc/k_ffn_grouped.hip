@@ -789,8 +789,9 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
             // ---- epilogue of item cq (the next item's first steps are already
             // loading).  acc[m][n] = (weight rows) x (tokens): value r of lane l
             // is output column 8*(r/4) + 4*(l/32) + (r%4) of fragment n and
-            // token row m*32 + l%32, so r = 4j..4j+3 are 4 consecutive columns
-            // (one 8-byte store).
+            // token row m*32 + l%32, so r = 4j..4j+3 are 4 consecutive columns;
+            // a swap between the half-waves makes them 8 (one 16-byte store;
+            // 2-4% faster at 4096 tokens than 8-byte stores).
             const W4Item itm = items[cq];
             const int blk = itm.nt * W4_WAVES + wave;
             if (blk < a.nblk) {
@@ -798,29 +799,54 @@ __global__ __launch_bounds__(W4_T) void w4_gemm_kernel(GemmArgs a)
 #pragma unroll
                 for (int m = 0; m < MF; ++m) {
                     const int row = m * 32 + col;
-                    if (row >= mrows)
+                    // wave-uniform (the cross-lane swap below needs the
+                    // whole wave): skip fragments with no row in the tile
+                    if (__ballot(row < mrows) == 0ull)
                         continue;
-                    const size_t p = (size_t)(itm.p0 + row);
+                    // this lane's outputs of fragment f as fp16 pairs: group j
+                    // (4 columns) at 8 j + 4 half.  Swapping groups 2q+1 of
+                    // the lower half-wave with groups 2q of the upper one
+                    // (v_permlane32_swap: lanes 32-63 of the first operand
+                    // trade places with lanes 0-31 of the second) leaves each
+                    // lane 8 consecutive columns at 16 q + 8 half: one
+                    // 16-byte store per q instead of two 8-byte ones
+                    const size_t p = (size_t)(itm.p0 + min(row, mrows - 1));
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int c0 = 8 * j + 4 * half;
-                        half4_t v;
-                        if constexpr (GATEUP) {
+                    for (int f = 0; f < (GATEUP ? 1 : 2); ++f) {
+                        uint32_t d[4][2];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                v[i] = (_Float16)swiglu_fast(acc[m][0][4 * j + i],
-                                                             acc[m][1][4 * j + i]);
-                            *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) +
-                                                         p * a.ldo + blk * 32 + c0) = v;
-                        } else {
+                        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                            for (int f = 0; f < 2; ++f) {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    v[i] = (_Float16)acc[m][f][4 * j + i];
-                                *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(a.out) +
-                                                             p * a.ldo + blk * 64 + f * 32 + c0) = v;
+                            for (int i2 = 0; i2 < 2; ++i2) {
+                                half2_t v;
+                                if constexpr (GATEUP) {
+                                    v[0] = (_Float16)swiglu_fast(acc[m][0][4 * j + 2 * i2],
+                                                                 acc[m][1][4 * j + 2 * i2]);
+                                    v[1] = (_Float16)swiglu_fast(acc[m][0][4 * j + 2 * i2 + 1],
+                                                                 acc[m][1][4 * j + 2 * i2 + 1]);
+                                } else {
+                                    v[0] = (_Float16)acc[m][f][4 * j + 2 * i2];
+                                    v[1] = (_Float16)acc[m][f][4 * j + 2 * i2 + 1];
+                                }
+                                d[j][i2] = __builtin_bit_cast(uint32_t, v);
                             }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q)
+#pragma unroll
+                            for (int i2 = 0; i2 < 2; ++i2) {
+                                const auto r = __builtin_amdgcn_permlane32_swap(
+                                    d[2 * q][i2], d[2 * q + 1][i2], false, false);
+                                d[2 * q][i2] = r[0];
+                                d[2 * q + 1][i2] = r[1];
+                            }
+                        if (row < mrows) {
+                            _Float16 *o = static_cast<_Float16 *>(a.out) + p * a.ldo +
+                                          (GATEUP ? blk * 32 : blk * 64 + f * 32) + 8 * half;
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+                                *reinterpret_cast<uint4_t *>(o + 16 * q) =
+                                    uint4_t{d[2 * q][0], d[2 * q][1], d[2 * q + 1][0],
+                                            d[2 * q + 1][1]};
                         }
                     }
                 }

@@ -511,6 +511,8 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
         return MOE_OK;
     if (!x_f16 || !perm || !offsets || !d_expert_blobs || !y)
         return set_error(MOE_EINVAL, "moe_expert_ffn_w4a16: null pointer");
+    if (((uintptr_t)x_f16 | (uintptr_t)y) & 15u)
+        return set_error(MOE_EINVAL, "moe_expert_ffn_w4a16: x and y must be 16-byte aligned");
     if (need && (!ws || ws_bytes < need))
         return set_error(MOE_ENOMEM, "moe_expert_ffn_w4a16: workspace %zu < %zu bytes", ws_bytes,
                          need);

@@ -110,6 +110,14 @@ def test_compute_calls_reject_before_launch():
         M.moe_expert_ffn_w4a16(1, 1, 1, 1, 1, 2048, 1024, 64, 8, 128, M.MOE_REGIME_DECODE, 1,
                                M.MOE_DTYPE_F16, 1, stream=0)
     assert ei.value.code == M.MOE_EINVAL
+    with pytest.raises(M.MoEError) as ei:   # x or y not 16-byte aligned
+        M.moe_expert_ffn_w4a16(4096, 1, 1, 1, 1, 2048, 1024, 64, 8, 128, M.MOE_REGIME_DECODE,
+                               4096 + 8, M.MOE_DTYPE_F32, 32, stream=0)
+    assert ei.value.code == M.MOE_EINVAL and "aligned" in str(ei.value)
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_expert_ffn_w4a16(4096 + 8, 1, 1, 1, 1, 2048, 1024, 64, 8, 128,
+                               M.MOE_REGIME_DECODE, 4096, M.MOE_DTYPE_F32, 32, stream=0)
+    assert ei.value.code == M.MOE_EINVAL and "aligned" in str(ei.value)
     with pytest.raises(M.MoEError) as ei:
         M.moe_combine(1, M.MOE_DTYPE_F16, 4, 1, 1, None, None, 1, 2048, 8, 1, stream=0)
     assert ei.value.code == M.MOE_EINVAL
