@@ -74,8 +74,15 @@ static size_t sb_lds_bytes(int rmax, int K, int P)
     return std::max(xs, red);
 }
 
+// Workgroups per CU the register budget is sized for: four (128 VGPRs) for
+// symmetric blobs; three (170) with zero points, whose per-chunk offsets
+// spilled about 50 registers at four (T = 8: 72 -> 46 us, T = 32: 100 -> 71
+// us for the 64-expert layer; the symmetric kernel measures the same or
+// slower at three).
+constexpr int sb_occupancy(bool zp) { return zp ? 3 : 16 / SB_WAVES; }
+
 template <int MODE, int KS, bool ZP>
-__global__ __launch_bounds__(SB_T, 16 / SB_WAVES) void w4_small_kernel(SmallArgs a)
+__global__ __launch_bounds__(SB_T, sb_occupancy(ZP)) void w4_small_kernel(SmallArgs a)
 {
     constexpr bool GATEUP = MODE == SB_GATEUP;
     constexpr int BPW = SB_WAVES / KS;   // weight blocks per workgroup
