@@ -235,17 +235,33 @@ def run_decode(args, torch, M):
     act = [torch.empty((1, cfg.H), dtype=torch.float16, device=dev) for _ in range(2)]
 
     fuse = not getattr(args, "no_fuse", False)
+    split = fuse and not getattr(args, "route_in_combine", False)
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=dev)
 
     def step_from(x):
         # with fuse, layer l's combine and layer l+1's route + permute are
-        # one launch (moe_combine_route_permute); the same bits either way
+        # one launch (moe_combine_route_permute); with split (the default),
+        # layer l's combine hands on only layer l+1's logit partials and
+        # layer l+1's expert launch routes from them
+        # (moe_combine_route_partials + moe_expert_ffn_w4a16_routed); the
+        # same bits in every form
+        routed = False
         for l, lay in enumerate(lays):
             out = act[l & 1]
             if l == 0 or not fuse:
                 lay.route_permute(x, bufs[l])
-            lay.experts(x, bufs[l])
+            if routed:
+                lay.experts_routed(x, bufs[l], parts)
+            else:
+                lay.experts(x, bufs[l])
+            routed = False
             if fuse and l + 1 < L:
-                lay.combine_route_next(bufs[l], lays[l + 1], bufs[l + 1], residual=x, out=out)
+                if split:
+                    lay.combine_partials_next(bufs[l], lays[l + 1], parts, residual=x, out=out)
+                    routed = True
+                else:
+                    lay.combine_route_next(bufs[l], lays[l + 1], bufs[l + 1], residual=x,
+                                           out=out)
             else:
                 lay.combine(bufs[l], residual=x, out=out)
             x = out
@@ -302,8 +318,16 @@ def run_decode(args, torch, M):
                                                                   bufs[l + 1], residual=x0,
                                                                   out=act[0])
                                        for l in range(L - 1)], reps) / (L - 1)
+    t_cp = _graph_time(torch, lambda: [lays[l].combine_partials_next(bufs[l], lays[l + 1], parts,
+                                                                     residual=x0, out=act[0])
+                                       for l in range(L - 1)], reps) / (L - 1)
+    t_ffn_r = _graph_time(torch, lambda: [lays[l].experts_routed(x0, bufs[l], parts)
+                                          for l in range(1, L)], reps) / (L - 1)
     ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
-    achieved = ffn_bytes / (t_ffn * 1e-3) / 1e9
+    # the decode kernel as the step runs it: with split, layers 1..15 route
+    # inside it from the logit partials
+    t_dom = t_ffn_r if split else t_ffn
+    achieved = ffn_bytes / (t_dom * 1e-3) / 1e9
     ms_step = elapsed * 1e3 / K
     prof = _profile_record(DECODE_KERNEL_SOURCES, "ffn_decode_kernel olmoe_decode") or {}
     traffic = prof.get("hbm_bytes_per_launch")
@@ -322,18 +346,22 @@ def run_decode(args, torch, M):
         "config": {"workload": "olmoe_decode: 16 MoE layers H=2048 E=64 top-8 I=1024 g=128, "
                                "1 token/step, all experts resident",
                    "layers": L, "tokens_per_step": 1, "graph": bool(graph),
-                   "format": "sym" if fmt == 0 else "zp", "combine_route_fused": fuse},
+                   "format": "sym" if fmt == 0 else "zp", "combine_route_fused": fuse,
+                   "route_in_ffn": split},
         "layer_tokens_per_s": round(K * L / elapsed, 1),
         "per_layer_us": {"route+permute": round(t_route * 1e3, 2),
                          "expert_ffn": round(t_ffn * 1e3, 2),
                          "combine": round(t_comb * 1e3, 2),
-                         "combine+next_route": round(t_cr * 1e3, 2)},
-        "roofline": {"kernel": "ffn_decode_kernel (moe_expert_ffn_w4a16, DECODE)",
+                         "combine+next_route": round(t_cr * 1e3, 2),
+                         "combine+next_logit_partials": round(t_cp * 1e3, 2),
+                         "route_from_partials+expert_ffn": round(t_ffn_r * 1e3, 2)},
+        "roofline": {"kernel": "ffn_decode_kernel (%s, DECODE)" % (
+                         "moe_expert_ffn_w4a16_routed" if split else "moe_expert_ffn_w4a16"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "alg_bytes_per_launch": ffn_bytes,
-                     "avg_launch_us": round(t_ffn * 1e3, 3),
+                     "avg_launch_us": round(t_dom * 1e3, 3),
                      "timing": "HIP events around a graph of the kernel's 16 layer launches "
                                "on its launch stream, averaged per launch",
                      # the same kernel's average duration in the committed
@@ -768,6 +796,10 @@ def main():
                     help="partial --policy pinned: prompts of the profile pass")
     ap.add_argument("--no-fuse", dest="no_fuse", action="store_true", default=False,
                     help="decode: separate combine and next-layer route launches")
+    ap.add_argument("--route-in-combine", dest="route_in_combine", action="store_true",
+                    default=False,
+                    help="decode: route each next layer inside the fused combine launch "
+                         "(moe_combine_route_permute) instead of inside its expert launch")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True)
     ap.add_argument("--no-graph", dest="graph", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false", default=True)

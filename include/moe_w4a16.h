@@ -431,6 +431,48 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
                               int32_t *offsets, int32_t *perm, int32_t *inv_perm_next, void *ws,
                               size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The same two stacked decode layers split differently: the combine of
+ * layer l and only the next layer's logit partials in one launch, then the
+ * next layer's routing done inside its expert FFN.  Every workgroup of the
+ * FFN folds the partials in the pinned order and selects for itself, so no
+ * workgroup waits for another and the combine's launch ends once its
+ * partials are stored.  Together the two calls give, bit for bit, what
+ * moe_combine_route_permute followed by moe_expert_ffn_w4a16 give (the same
+ * out_f16, routing arrays and y).  For one decode token of at most 64 experts
+ * (T = 1, E <= 64, y of the decode regime: MOE_DTYPE_F32 or MOE_DTYPE_F32_PM
+ * with y_slices > 1); other shapes are MOE_EUNSUPPORTED (use the calls above).
+ *
+ * moe_combine_route_partials: arguments as moe_combine_route_permute up to
+ * logit_bias-less w_router_f16 and E; writes out_f16 and
+ *   logit_partials  device fp32 [64][64] (moe_logit_partials_bytes()):
+ *                   partial j of expert e's logit at j * 64 + e, partial j
+ *                   summing the 8-column chunks j, j + 64, ... of out_f16 in
+ *                   the pinned order (Horizon RunMap "08": routing in FP32
+ *                   with explicit roundings); rows j >= min(64, H / 8) are not
+ *                   written and count as zero.
+ * moe_expert_ffn_w4a16_routed: x_f16 (the combine's out_f16), the partials,
+ * logit_bias (may be NULL), E, k, flags as moe_route; writes the routing
+ * arrays of moe_route_permute (topk_idx, topk_w, counts, offsets, perm,
+ * inv_perm) and y as moe_expert_ffn_w4a16 in the DECODE regime (regime may
+ * carry MOE_Y_TOKEN_ORDER, MOE_Y_PARTIAL_ORDER and MOE_W4_ZERO_POINT;
+ * d_expert_blobs must hold every expert).  Errors: MOE_EINVAL / ENOMEM /
+ * EUNSUPPORTED as the calls they replace, checked before any launch.
+ */
+size_t moe_logit_partials_bytes(void);
+int moe_combine_route_partials(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                               const float *topk_w, const float *shared_f32, const void *x_f16,
+                               const void *shared_gate_w_f16, const void *residual_f16, int T,
+                               int H, int k, void *out_f16, const void *w_router_f16, int E,
+                               float *logit_partials, hipStream_t stream);
+int moe_expert_ffn_w4a16_routed(const void *x_f16, const float *logit_partials,
+                                const float *logit_bias, int E, int k, unsigned flags,
+                                int32_t *topk_idx, float *topk_w, int32_t *counts,
+                                int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                                const void *const *d_expert_blobs, int T, int H, int I,
+                                int group, int regime, void *y, int y_dtype, int y_slices,
+                                hipStream_t stream);
+
 /* ------------------------------------------------- expert slot pool */
 /*
  * Partial residency (Horizon RunMap "03 / Arquitetura",

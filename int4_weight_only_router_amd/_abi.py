@@ -20,7 +20,9 @@ __all__ = [
     "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
-    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "PoolConfig",
+    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute",
+    "moe_logit_partials_bytes", "moe_combine_route_partials", "moe_expert_ffn_w4a16_routed",
+    "PoolConfig",
     "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_access_counts", "moe_pool_reset",
@@ -47,7 +49,9 @@ EXPORTS = [
     "moe_route_permute_noalloc",
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
-    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute", "moe_pool_create",
+    "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute",
+    "moe_logit_partials_bytes", "moe_combine_route_partials", "moe_expert_ffn_w4a16_routed",
+    "moe_pool_create",
     "moe_pool_prepare",
     "moe_pool_layer_forward", "moe_pool_pin",
     "moe_pool_retire", "moe_pool_stats", "moe_pool_access_counts", "moe_pool_reset",
@@ -128,6 +132,12 @@ def _declare(L):
         "moe_combine_route_permute": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                             vp, vp, vp, i32, i32, C.c_uint, vp, vp, vp, vp, vp,
                                             vp, vp, sz, vp]),
+        "moe_logit_partials_bytes": (sz, []),
+        "moe_combine_route_partials": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32,
+                                             i32, vp, vp, i32, vp, vp]),
+        "moe_expert_ffn_w4a16_routed": (i32, [vp, vp, vp, i32, i32, C.c_uint, vp, vp, vp, vp,
+                                              vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32,
+                                              vp]),
         "moe_pool_create": (i32, [C.POINTER(PoolConfig), vp, C.POINTER(vp)]),
         "moe_pool_prepare": (i32, [vp, i32, vp, i32, vp, C.POINTER(vp), C.POINTER(PoolStats)]),
         "moe_pool_layer_forward": (i32, [vp, i32, C.POINTER(PoolLayerArgs), vp,
@@ -350,6 +360,28 @@ def moe_combine_route_permute(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32
         _p(gate_w_f16), _p(residual_f16), T, H, k, _p(out_f16), _p(w_router), _p(logit_bias),
         E, k_next, flags, _p(topk_idx), _p(topk_w_next), _p(counts), _p(offsets), _p(perm),
         _p(inv_perm_next), _p(ws), ws_bytes, _s(stream)))
+
+
+def moe_logit_partials_bytes():
+    return lib().moe_logit_partials_bytes()
+
+
+def moe_combine_route_partials(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,
+                               gate_w_f16, residual_f16, T, H, k, out_f16, w_router, E,
+                               logit_partials, stream=None):
+    return _check(lib().moe_combine_route_partials(
+        _p(y), y_dtype, y_slices, _p(inv_perm), _p(topk_w), _p(shared_f32), _p(x_f16),
+        _p(gate_w_f16), _p(residual_f16), T, H, k, _p(out_f16), _p(w_router), E,
+        _p(logit_partials), _s(stream)))
+
+
+def moe_expert_ffn_w4a16_routed(x, logit_partials, logit_bias, E, k, flags, topk_idx, topk_w,
+                                counts, offsets, perm, inv_perm, d_expert_blobs, T, H, I, group,
+                                regime, y, y_dtype, y_slices, stream=None):
+    return _check(lib().moe_expert_ffn_w4a16_routed(
+        _p(x), _p(logit_partials), _p(logit_bias), E, k, flags, _p(topk_idx), _p(topk_w),
+        _p(counts), _p(offsets), _p(perm), _p(inv_perm), _p(d_expert_blobs), T, H, I, group,
+        regime, _p(y), y_dtype, y_slices, _s(stream)))
 
 
 def moe_pool_create(cfg: PoolConfig, pinned_src_ptrs):

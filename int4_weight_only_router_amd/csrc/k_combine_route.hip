@@ -49,7 +49,11 @@ struct PartialCols {
     __device__ int y(int, int i) const { return PM ? 8 * j * q + i : col(0, i); }
 };
 
-template <int H, bool GATED, bool PM>
+// SEL = false: the partials are stored as plain fp32 into `part` ([64][64],
+// partial j of expert e at j * 64 + e) and the launch ends there; the next
+// layer's decode FFN folds and selects from them itself (ffn_decode_kernel
+// with ROUTE), so no workgroup waits for another.
+template <int H, bool GATED, bool PM, bool SEL>
 __global__ __launch_bounds__(256) void combine_route_kernel(
     const float *__restrict__ y, int S, const int32_t *__restrict__ inv_perm,
     const float *__restrict__ w, const float *__restrict__ shared, const f16 *__restrict__ x,
@@ -57,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     const f16 *__restrict__ wr, const float *__restrict__ bias, int E, int kn, unsigned flags,
     uint64_t *xchg, unsigned *calls, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-    int32_t *__restrict__ inv_perm_out)
+    int32_t *__restrict__ inv_perm_out, float *__restrict__ part)
 {
     constexpr int NCH = H / 8;               // 8-column chunks
     constexpr int NCL = (NCH + 63) / 64;     // chunks per partial (all present: H % 512 == 0
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     __shared__ CombineTileSmem sm[1];
     __shared__ __align__(16) f16 xs[32];
     __shared__ __align__(16) uint64_t keys[64];
-    __shared__ float pl[64][64];   // block 0: the gathered logit partials
+    __shared__ float pl[SEL ? 64 : 1][64];   // block 0: the gathered logit partials
 
     const int j = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -75,7 +79,8 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
     // past E read row E - 1; block 0 ignores them), requested first.  Every
     // wave issues them (only wave 0 uses them): a branch here would make the
     // compiler wait for them before the slice loads.
-    const unsigned c = __hip_atomic_load(calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned c = SEL ? __hip_atomic_load(calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0u;
     uint4_t wv[NCL];
     {
         const uint4_t *row =
@@ -105,11 +110,14 @@ __global__ __launch_bounds__(256) void combine_route_kernel(
             for (int i = 0; i < 8; ++i)
                 acc = __builtin_fmaf((float)xh[i], (float)wh[i], acc);
         }
-        __hip_atomic_store(xchg + j * 64 + lane,
-                           ((uint64_t)tag << 32) | __builtin_bit_cast(unsigned, acc),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (SEL)
+            __hip_atomic_store(xchg + j * 64 + lane,
+                               ((uint64_t)tag << 32) | __builtin_bit_cast(unsigned, acc),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            part[j * 64 + lane] = acc;
     }
-    if (j != 0)
+    if (!SEL || j != 0)
         return;
 
     // block 0: wave w gathers partials 16w .. 16w+15 of every expert's logit
@@ -162,32 +170,41 @@ static void launch_cr(const float *y, int S, const int32_t *inv_perm, const floa
                       const float *shared, const f16 *x, const f16 *wsg, const f16 *residual,
                       int k, f16 *out, const f16 *wr, const float *bias, int E, int kn,
                       unsigned flags, void *ws, int32_t *idx, float *wo, int32_t *counts,
-                      int32_t *offsets, int32_t *perm, int32_t *inv_perm_out, hipStream_t s)
+                      int32_t *offsets, int32_t *perm, int32_t *inv_perm_out, float *part,
+                      hipStream_t s)
 {
+    const int blocks = H / 8 < 64 ? H / 8 : 64;
+    if (part) {
+        hipLaunchKernelGGL((combine_route_kernel<H, GATED, PM, false>), dim3(blocks), dim3(256), 0,
+                           s, y, S, inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E,
+                           kn, flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, part);
+        return;
+    }
     char *base = static_cast<char *>(ws);
     uint64_t *xchg = reinterpret_cast<uint64_t *>(base + CR_XCHG_OFF);
     unsigned *calls = reinterpret_cast<unsigned *>(base + CR_CALLS_OFF);
-    const int blocks = H / 8 < 64 ? H / 8 : 64;
-    hipLaunchKernelGGL((combine_route_kernel<H, GATED, PM>), dim3(blocks), dim3(256), 0, s, y,
-                       S, inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E, kn, flags,
-                       xchg, calls, idx, wo, counts, offsets, perm, inv_perm_out);
+    hipLaunchKernelGGL((combine_route_kernel<H, GATED, PM, true>), dim3(blocks), dim3(256), 0, s,
+                       y, S, inv_perm, w, shared, x, wsg, residual, k, out, wr, bias, E, kn,
+                       flags, xchg, calls, idx, wo, counts, offsets, perm, inv_perm_out, nullptr);
 }
 
 // T = 1, E <= 64, fp32 decode partials (pm: partial-major columns); the
-// caller has checked the shapes.
+// caller has checked the shapes.  part != null: store the next layer's logit
+// partials there instead of routing (ws and the routing outputs unused).
 int launch_combine_route(const float *y, bool pm, int S, const int32_t *inv_perm, const float *w,
                          const float *shared, const void *x, const void *gate_w,
                          const void *residual, int H, int k, void *out, const void *wr,
                          const float *bias, int E, int kn, unsigned flags, void *ws, int32_t *idx,
                          float *wo, int32_t *counts, int32_t *offsets, int32_t *perm,
-                         int32_t *inv_perm_out, hipStream_t s)
+                         int32_t *inv_perm_out, float *part, hipStream_t s)
 {
     const f16 *xh = static_cast<const f16 *>(x), *gh = static_cast<const f16 *>(gate_w);
     const f16 *rh = static_cast<const f16 *>(residual), *wh = static_cast<const f16 *>(wr);
     f16 *oh = static_cast<f16 *>(out);
 #define MOE_CR3(HH, G, P)                                                                       \
     launch_cr<HH, G, P>(y, S, inv_perm, w, shared, xh, gh, rh, k, oh, wh, bias, E, kn, flags,   \
-                        ws, idx, wo, counts, offsets, perm, inv_perm_out, s)
+                        ws, idx, wo, counts, offsets, perm, inv_perm_out, part, s)
 #define MOE_CR(HH)                                                                              \
     if (gh) {                                                                                   \
         if (pm) MOE_CR3(HH, true, true);                                                        \

@@ -22,6 +22,7 @@
 // slices in order.  Each wave keeps a few weight chunks in flight and
 // computes each chunk as it lands (schedule notes at the kernel).
 #include "k_decode_frag.h"
+#include "k_sort_common.h"
 
 #include <type_traits>
 
@@ -72,6 +73,13 @@ __device__ __forceinline__ int nth_active_expert(const int32_t *__restrict__ off
 // (a hoisted unpack waits for every load issued before it).
 __device__ __forceinline__ void opaque(uint4_t &w) { asm volatile("" : "+v"(w)); }
 
+// ROUTE: one token whose routing is still to be formed from the next-layer
+// logit partials that the fused combine stored (DecodeRoute, moe_common.h).
+// Every workgroup folds the partials in the pinned order, selects as the
+// one-token router does and takes the blockIdx.y-th selected expert in id
+// order (its sorted row); wave 0 of the first workgroup also writes the
+// routing outputs, once its first weight loads are in flight.
+
 constexpr int DECODE_XPRE = 4;   // up to this many tokens, all x rows are staged at entry
 constexpr int DECODE_RG = 4;     // routed rows computed together from one weight unpack
 
@@ -89,13 +97,13 @@ constexpr int DECODE_RG = 4;     // routed rows computed together from one weigh
 // ZP: zero-point blobs (W = (u - z) s, z one byte per row and group in the
 // scales' order); the correction constant of a chunk becomes per row:
 // corr - z * sum (k_decode_frag.h).
-template <int H, int G, int NW, int PD, bool ZP>
+template <int H, int G, int NW, int PD, bool ZP, bool ROUTE>
 __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     const f16 *__restrict__ x, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ offsets, const uint8_t *const *__restrict__ blobs,
     const uint8_t *const *__restrict__ skip, int I, int E, int k, int ntk, int yflags,
     int64_t off_guq, int64_t off_dq, int64_t off_gus, int64_t off_ds, int64_t off_guz,
-    int64_t off_dz, float *__restrict__ y)
+    int64_t off_dz, float *__restrict__ y, DecodeRoute rt)
 {
     constexpr int NK = H / 32;                 // input chunks of gate/up rows
     constexpr int CPW = NK / NW;               // gate/up chunks per wave
@@ -115,6 +123,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     __shared__ float red[NW][RG][64];
     __shared__ __align__(16) half2_t hp[RG][16];              // prepared h chunks
     __shared__ int s_tok[RG];
+    __shared__ float s_part[ROUTE ? 8 : 1][64];          // ROUTE: folded logit partials
+    __shared__ uint64_t s_key[ROUTE ? NW : 1][64];      // ROUTE: each wave's selection keys
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -145,8 +155,83 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     }
 
     const uint8_t *blob = nullptr;
-    int p0 = 0, p1 = 0;
-    int e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &blob, &p0, &p1);
+    int p0 = 0, p1 = 0, route_rank = 0;
+    float l_route = 0.0f;
+    int e;
+    if constexpr (ROUTE) {
+        // The pinned fold of 64 partials is a butterfly (strides 32, 16, 8,
+        // 4, 2, 1); after its first three levels, value r < 8 depends only on
+        // partials r, r + 8, ..., r + 56.  So wave w loads those eight rows
+        // for r = w (and w + 4 with four waves) and folds them in registers;
+        // the eight values meet in LDS and every wave finishes the last
+        // three levels.  The same additions as pinned_fold64.  Rows past nb
+        // were never written and are zero.  The bias and the blob table are
+        // requested at the same time.
+        constexpr int NB = H / 8 < 64 ? H / 8 : 64;
+        constexpr int CPV = 8 / NW;
+        const bool ev = lane < E;
+        float v[CPV][8];
+#pragma unroll
+        for (int q = 0; q < CPV; ++q)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int jj = wave + NW * q + 8 * m;
+                v[q][m] = jj < NB ? ldg(rt.part + jj * 64 + lane) : 0.0f;
+            }
+        const float bv = rt.bias != nullptr && ev ? ldg(rt.bias + lane) : 0.0f;
+        const uint8_t *bp = ev ? ldg(blobs + lane) : nullptr;
+#pragma unroll
+        for (int q = 0; q < CPV; ++q) {
+            // v[q][m] is partial r + 8 m, r = wave + NW q
+            const float a0 = v[q][0] + v[q][4], a1 = v[q][1] + v[q][5];   // stride 32
+            const float a2 = v[q][2] + v[q][6], a3 = v[q][3] + v[q][7];
+            const float b0 = a0 + a2, b1 = a1 + a3;                      // stride 16
+            s_part[wave + NW * q][lane] = b0 + b1;                       // stride 8
+        }
+        __syncthreads();
+        float c[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            c[r] = s_part[r][lane];
+        const float d0 = c[0] + c[4], d1 = c[1] + c[5], d2 = c[2] + c[6], d3 = c[3] + c[7];
+        const float e0 = d0 + d2, e1 = d1 + d3;
+        float l = e0 + e1;
+        if (rt.bias != nullptr)
+            l = l + bv;
+        // the one-token router's ranks: count the keys that beat this lane's
+        const uint64_t key = ev ? topk_key(l, lane) : 0ull;
+        s_key[wave][lane] = key;
+        __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
+        int r0c = 0, r1c = 0, r2c = 0, r3c = 0;
+#pragma unroll
+        for (int j = 0; j < 64; j += 4) {
+            const uint4_t q = *reinterpret_cast<const uint4_t *>(&s_key[wave][j]);
+            const uint4_t u = *reinterpret_cast<const uint4_t *>(&s_key[wave][j + 2]);
+            r0c += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
+            r1c += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
+            r2c += (((uint64_t)u.y << 32) | u.x) > key ? 1 : 0;
+            r3c += (((uint64_t)u.w << 32) | u.z) > key ? 1 : 0;
+        }
+        const int rank = (r0c + r1c) + (r2c + r3c);
+        const bool sel = ev && rank < k;
+        const uint64_t smask = __ballot(sel);
+        const int a = blockIdx.y;
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const uint64_t hit = __ballot(sel && __popcll(smask & below) == a);
+        e = hit ? __ffsll((long long)hit) - 1 : -1;   // the same in every wave
+        if (e >= 0) {
+            const uint64_t b = reinterpret_cast<uint64_t>(bp);
+            const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, e);
+            const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), e);
+            blob = reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+            route_rank = __builtin_amdgcn_readlane(rank, e);
+            p0 = a;
+            p1 = a + 1;
+        }
+        l_route = l;
+    } else {
+        e = nth_active_expert(offsets, blobs, E, blockIdx.y, lane, &blob, &p0, &p1);
+    }
     // an expert without weights in the table, or one that `skip` lists (done
     // by an earlier launch), is left to another launch
     if (e >= 0 && (blob == nullptr || (skip != nullptr && ldg(skip + e) != nullptr)))
@@ -161,7 +246,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     // flat indices t*k + j of the expert's first 64 rows (decode: at most 4
     // rows); needed for the token of a row (T > 1) and for a token-order y
     const bool tok_order = (yflags & YF_TOKEN_ORDER) != 0;
-    const int prow = ((T > 1 || tok_order) && lane < nrows) ? ldg(perm + p0 + lane) : 0;
+    const int prow = ROUTE ? (lane == 0 ? route_rank : 0)
+                           : ((T > 1 || tok_order) && lane < nrows) ? ldg(perm + p0 + lane) : 0;
 
     // scales: one per scale group among this wave's gate/up chunks, one per
     // down block (2 bytes per lane each)
@@ -206,6 +292,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 #pragma unroll
     for (int i = 0; i < PD && i < NCH; ++i)
         issue(i);
+    // ROUTE: the routing outputs, by one wave while the first weight chunks
+    // are on their way (before them, they would delay this workgroup's
+    // stream and so the whole launch)
+    if constexpr (ROUTE) {
+        if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0)
+            one_token_select(l_route, E, k, rt.flags, s_key[0], rt.idx, rt.w, rt.counts,
+                             rt.offsets, rt.perm, rt.inv_perm, lane);
+    }
 
     // pinned here: prepared any earlier, the wait for x would come before
     // the expert lookup is even issued
@@ -391,17 +485,17 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
 
 constexpr int DECODE_PD = 4;   // weight chunks each wave keeps in flight
 
-template <int H, bool ZP>
+template <int H, bool ZP, bool ROUTE>
 static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t *perm,
                            const int32_t *offsets, const uint8_t *const *blobs,
                            const uint8_t *const *skip, int I, int E, int k, int g, int ntk,
-                           int yflags, const DevLayout &L, float *y)
+                           int yflags, const DevLayout &L, float *y, const DecodeRoute &rt)
 {
     constexpr int NW = (H >= 1024) ? 8 : 4;
 #define MOE_DECODE_LAUNCH(G)                                                                  \
-    hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD, ZP>), grid, dim3(NW * 64), 0, s, \
-                       x, perm, offsets, blobs, skip, I, E, k, ntk, yflags, L.gu_q,               \
-                       L.d_q, L.gu_s, L.d_s, L.gu_z, L.d_z, y)
+    hipLaunchKernelGGL((ffn_decode_kernel<H, G, NW, DECODE_PD, ZP, ROUTE>), grid,              \
+                       dim3(NW * 64), 0, s, x, perm, offsets, blobs, skip, I, E, k, ntk, yflags, \
+                       L.gu_q, L.d_q, L.gu_s, L.d_s, L.gu_z, L.d_z, y, rt)
     switch (g) {
     case 32: MOE_DECODE_LAUNCH(32); break;
     case 64: MOE_DECODE_LAUNCH(64); break;
@@ -414,10 +508,13 @@ static int launch_decode_h(dim3 grid, hipStream_t s, const f16 *x, const int32_t
 
 // skip (may be null): a device table of E pointers; experts with a non-null
 // entry there are not computed (an earlier launch did them).  Experts with a
-// null entry in `blobs` are not computed either.
+// null entry in `blobs` are not computed either.  rt (may be null): route one
+// token (E <= 64) from logit partials first (perm and offsets unused; the
+// caller has checked the shape).
 int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets,
                       const void *const *blobs, const void *const *skip, int T, int H, int I,
-                      int E, int k, int g, int fmt, int yflags, float *y, hipStream_t s)
+                      int E, int k, int g, int fmt, int yflags, float *y, hipStream_t s,
+                      const DecodeRoute *rt)
 {
     const int ntk = T * k;
     if (ntk == 0)
@@ -428,20 +525,28 @@ int launch_ffn_decode(const void *x, const int32_t *perm, const int32_t *offsets
     const uint8_t *const *b = reinterpret_cast<const uint8_t *const *>(blobs);
     const uint8_t *const *sk = reinterpret_cast<const uint8_t *const *>(skip);
     int rc;
-#define MOE_DECODE_H(HH)                                                                       \
+    const DecodeRoute rr = rt ? *rt : DecodeRoute{};
+#define MOE_DECODE_H2(HH, R)                                                                   \
     rc = fmt == FMT_ZP                                                                         \
-             ? launch_decode_h<HH, true>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,    \
-                                         yflags, L, y)                                         \
-             : launch_decode_h<HH, false>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk,   \
-                                          yflags, L, y)
+             ? launch_decode_h<HH, true, R>(grid, s, xh, perm, offsets, b, sk, I, E, k, g, ntk, \
+                                            yflags, L, y, rr)                                  \
+             : launch_decode_h<HH, false, R>(grid, s, xh, perm, offsets, b, sk, I, E, k, g,    \
+                                             ntk, yflags, L, y, rr)
+#define MOE_DECODE_H(HH)                                                                       \
+    if (rt) {                                                                                  \
+        MOE_DECODE_H2(HH, true);                                                               \
+    } else {                                                                                   \
+        MOE_DECODE_H2(HH, false);                                                              \
+    }
     switch (H) {
-    case 256: MOE_DECODE_H(256); break;
-    case 512: MOE_DECODE_H(512); break;
-    case 1024: MOE_DECODE_H(1024); break;
-    case 2048: MOE_DECODE_H(2048); break;
+    case 256: MOE_DECODE_H(256) break;
+    case 512: MOE_DECODE_H(512) break;
+    case 1024: MOE_DECODE_H(1024) break;
+    case 2048: MOE_DECODE_H(2048) break;
     default: return set_error(MOE_EUNSUPPORTED, "decode kernel: H=%d not instantiated", H);
     }
 #undef MOE_DECODE_H
+#undef MOE_DECODE_H2
     if (rc != MOE_OK)
         return rc;
     MOE_LAUNCH_CHECK("ffn_decode_kernel");

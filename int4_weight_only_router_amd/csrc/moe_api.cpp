@@ -44,7 +44,7 @@ int launch_permute(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t
                    void *, hipStream_t);
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
                       const void *const *, int, int, int, int, int, int, int, int, float *,
-                      hipStream_t);
+                      hipStream_t, const DecodeRoute *);
 size_t ffn_batched_ws_bytes(int T, int I, int k);
 int launch_ffn_batched(const void *, const int32_t *, const int32_t *, const void *const *, int,
                        int, int, int, int, int, int, void *, void *, hipStream_t);
@@ -58,7 +58,8 @@ int launch_shared_batched(const void *, const void *, const void *, const void *
 int launch_combine_route(const float *, bool, int, const int32_t *, const float *, const float *,
                          const void *, const void *, const void *, int, int, void *,
                          const void *, const float *, int, int, unsigned, void *, int32_t *,
-                         float *, int32_t *, int32_t *, int32_t *, int32_t *, hipStream_t);
+                         float *, int32_t *, int32_t *, int32_t *, int32_t *, float *,
+                         hipStream_t);
 size_t combine_route_ws_bytes();
 int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
                    const void *, const void *, const void *, int, int, int, void *,
@@ -520,7 +521,7 @@ int moe_expert_ffn_w4a16(const void *x_f16, const int32_t *perm, const int32_t *
     if (r == MOE_REGIME_DECODE)
         return launch_ffn_decode(x_f16, perm, offsets, d_expert_blobs, nullptr, T, H, I, E, k,
                                  group, fmt, decode_yflags(regime), static_cast<float *>(y),
-                                 stream);
+                                 stream, nullptr);
     if (r == MOE_REGIME_SMALL)
         return launch_ffn_small(x_f16, perm, offsets, d_expert_blobs, T, H, I, E, k, group, fmt, y,
                                 ws, stream);
@@ -663,7 +664,7 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
                                     shared_f32, x_f16, shared_gate_w_f16, residual_f16, H, k,
                                     out_f16, w_router_f16, logit_bias, E, k_next, flags, ws,
                                     topk_idx, topk_w_next, counts, offsets, perm, inv_perm_next,
-                                    stream);
+                                    nullptr, stream);
     if (T > 0) {
         rc = launch_combine(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32,
                             shared_gate_w_f16 ? x_f16 : nullptr, shared_gate_w_f16, residual_f16,
@@ -674,6 +675,79 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
     return moe_route_permute(out_f16, w_router_f16, logit_bias, T, H, E, k_next, flags, topk_idx,
                              topk_w_next, counts, offsets, perm, inv_perm_next, ws, ws_bytes,
                              stream);
+}
+
+size_t moe_logit_partials_bytes(void) { return (size_t)64 * 64 * sizeof(float); }
+
+int moe_combine_route_partials(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
+                               const float *topk_w, const float *shared_f32, const void *x_f16,
+                               const void *shared_gate_w_f16, const void *residual_f16, int T,
+                               int H, int k, void *out_f16, const void *w_router_f16, int E,
+                               float *logit_partials, hipStream_t stream)
+{
+    MOE_API_RANGE();
+    clear_error();
+    const char *fn = "moe_combine_route_partials";
+    int rc = check_combine_args(fn, y, y_dtype, y_slices, inv_perm, topk_w, T, H, k, out_f16);
+    if (rc)
+        return rc;
+    if (shared_gate_w_f16) {
+        if (!shared_f32 || !x_f16)
+            return set_error(MOE_EINVAL, "%s: a gate needs the shared output and x", fn);
+        if (((uintptr_t)x_f16 | (uintptr_t)shared_gate_w_f16) & 15)
+            return set_error(MOE_EINVAL, "%s: x and gate vector need 16-byte alignment", fn);
+    }
+    if (!w_router_f16 || !logit_partials)
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    if (E <= 0 || E > 64 || T != 1 || !combine_route_fused(T, E, y_dtype, y_slices))
+        return set_error(MOE_EUNSUPPORTED,
+                         "%s: one decode token of at most 64 experts only (T=%d, E=%d)", fn, T,
+                         E);
+    return launch_combine_route(static_cast<const float *>(y), y_dtype == MOE_DTYPE_F32_PM,
+                                y_slices, inv_perm, topk_w, shared_f32, x_f16, shared_gate_w_f16,
+                                residual_f16, H, k, out_f16, w_router_f16, nullptr, E, k, 0u,
+                                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                logit_partials, stream);
+}
+
+int moe_expert_ffn_w4a16_routed(const void *x_f16, const float *logit_partials,
+                                const float *logit_bias, int E, int k, unsigned flags,
+                                int32_t *topk_idx, float *topk_w, int32_t *counts,
+                                int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                                const void *const *d_expert_blobs, int T, int H, int I,
+                                int group, int regime, void *y, int y_dtype, int y_slices,
+                                hipStream_t stream)
+{
+    MOE_API_RANGE();
+    clear_error();
+    const char *fn = "moe_expert_ffn_w4a16_routed";
+    if (flags & ~(unsigned)MOE_RENORM)
+        return set_error(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+    int r = 0, dt = 0, sl = 0;
+    size_t need = 0;
+    int rc = moe_expert_ffn_plan(T, H, I, E, k, group, regime, &r, &dt, &sl, &need);
+    if (rc)
+        return rc;
+    if (T != 1 || E > 64 || r != MOE_REGIME_DECODE || need != 0)
+        return set_error(MOE_EUNSUPPORTED,
+                         "%s: one decode token of at most 64 experts only (T=%d, E=%d)", fn, T,
+                         E);
+    if (y_dtype != dt || y_slices != sl)
+        return set_error(MOE_EINVAL,
+                         "%s: y must be dtype %d with %d slices for this regime (got dtype %d, "
+                         "%d slices)",
+                         fn, dt, sl, y_dtype, y_slices);
+    if (!x_f16 || !logit_partials || !topk_idx || !topk_w || !counts || !offsets || !perm ||
+        !inv_perm || !d_expert_blobs || !y)
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    if (((uintptr_t)x_f16 | (uintptr_t)y) & 15u)
+        return set_error(MOE_EINVAL, "%s: x and y must be 16-byte aligned", fn);
+    const DecodeRoute rt{logit_partials, logit_bias, flags, topk_idx, counts, offsets, perm,
+                         inv_perm, topk_w};
+    const int fmt = (regime & MOE_W4_ZERO_POINT) ? MOE_FMT_ZP : MOE_FMT_SYM;
+    return launch_ffn_decode(x_f16, nullptr, nullptr, d_expert_blobs, nullptr, T, H, I, E, k,
+                             group, fmt, decode_yflags(regime), static_cast<float *>(y), stream,
+                             &rt);
 }
 
 }  // extern "C"

@@ -26,6 +26,19 @@ struct HostMirror {
     unsigned *flag;
     unsigned seq;
 };
+
+// Routing of one decode token formed inside the expert FFN from the logit
+// partials of the fused combine (partial j of expert e at part[j * 64 + e];
+// rows j >= min(64, H / 8) absent, taken as zero), plus the router's bias,
+// flags and the routing outputs it writes.
+struct DecodeRoute {
+    const float *part;
+    const float *bias;
+    unsigned flags;
+    int32_t *idx, *counts, *offsets, *perm, *inv_perm;
+    float *w;
+};
+
 inline int decode_yflags(int regime)
 {
     return ((regime & MOE_Y_TOKEN_ORDER) ? YF_TOKEN_ORDER : 0) |

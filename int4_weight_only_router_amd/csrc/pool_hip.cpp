@@ -152,7 +152,7 @@ struct HipPoolBackend {
 namespace moe {
 int launch_ffn_decode(const void *, const int32_t *, const int32_t *, const void *const *,
                       const void *const *, int, int, int, int, int, int, int, int, float *,
-                      hipStream_t);
+                      hipStream_t, const DecodeRoute *);
 int route_permute_mirror(const void *, const void *, const float *, int, int, int, int, unsigned,
                          int32_t *, float *, int32_t *, int32_t *, int32_t *, int32_t *, void *,
                          size_t, HostMirror, bool *, hipStream_t);
@@ -278,7 +278,7 @@ int moe_pool_layer_forward(moe_pool_t pool, int layer, const moe_pool_layer_args
                                         (a->regime & MOE_W4_ZERO_POINT) ? moe::FMT_ZP
                                                                         : moe::FMT_SYM,
                                         moe::decode_yflags(a->regime),
-                                        static_cast<float *>(a->y), stream);
+                                        static_cast<float *>(a->y), stream, nullptr);
     } else if (!rc) {
         rc = P.publish(layer, stream);
         if (!rc)

@@ -191,6 +191,39 @@ class MoELayer:
                                     nws, stream)
         return out
 
+    def split_route_ok(self, b: LayerBuffers, nxt: "MoELayer") -> bool:
+        """Whether this layer's combine can hand the next layer only its logit
+        partials (moe_combine_route_partials): one decode token, at most 64
+        experts in the next layer, fp32 slice partials here."""
+        return (b.T == 1 and nxt.E <= 64 and nxt.H == self.H and b.y_slices > 1 and
+                b.y_dtype in (A.MOE_DTYPE_F32, A.MOE_DTYPE_F32_PM))
+
+    def combine_partials_next(self, b: LayerBuffers, nxt: "MoELayer", parts,
+                              residual=None, out=None, stream=None, x=None):
+        """This layer's combine into `out` plus the next layer's logit partials
+        of `out` into `parts` (fp32, moe_logit_partials_bytes()), which
+        nxt.experts_routed then routes from."""
+        out = b.out if out is None else out
+        inv = None if b.regime & A.MOE_Y_TOKEN_ORDER else b.inv_perm
+        gate = self.shared_gate
+        if gate is not None and x is None:
+            raise ValueError("the gated shared expert needs the layer input x")
+        A.moe_combine_route_partials(b.y, b.y_dtype, b.y_slices, inv, b.topk_w, b.shared_out,
+                                     x if gate is not None else None, gate, residual, b.T,
+                                     self.H, self.k, out, nxt.router, nxt.E, parts, stream)
+        return out
+
+    def experts_routed(self, x, b: LayerBuffers, parts, stream=None, shared=True):
+        """Routing from the logit partials of the previous layer's combine and
+        the routed experts in one launch (moe_expert_ffn_w4a16_routed): fills
+        b's routing arrays and y as route_permute + experts would."""
+        A.moe_expert_ffn_w4a16_routed(x, parts, self.bias, self.E, self.k, self.flags,
+                                      b.topk_idx, b.topk_w, b.counts, b.offsets, b.perm,
+                                      b.inv_perm, self.table, b.T, self.H, self.I, self.g,
+                                      b.regime, b.y, b.y_dtype, b.y_slices, stream)
+        if shared and self.shared is not None:
+            self.shared_ffn(x, b, stream)
+
     def pool_args(self, b: LayerBuffers, host_ids):
         """PoolLayerArgs for moe_pool_layer_forward with this layer's weights and
         b's buffers; x_f16 / residual_f16 / out_f16 are set per call."""
@@ -245,20 +278,36 @@ class MoELayer:
         return self.combine(b, residual, out, main, x=x)
 
 
-def stack_forward(layers, bufs, acts, stream=None, fuse=True):
+def stack_forward(layers, bufs, acts, stream=None, fuse=True, parts=None):
     """Stacked layers with residual connections, x_{l+1} = fp16(x_l + MoE_l(x_l)):
     acts[l] is layer l's input and residual, acts[l + 1] its output.  With
     `fuse`, each layer's combine runs together with the next layer's route +
-    permute (MoELayer.combine_route_next); the results are the same bits."""
+    permute (MoELayer.combine_route_next); with `parts` as well (fp32 device
+    buffer of moe_logit_partials_bytes()), a decode token's combine hands the
+    next layer only its logit partials and that layer's expert launch routes
+    from them (combine_partials_next + experts_routed).  Every form gives the
+    same bits."""
     L = len(layers)
     layers[0].route_permute(acts[0], bufs[0], stream)
+    routed = False   # this layer's routing is still to be formed from `parts`
     for l, lay in enumerate(layers):
         if l > 0 and not fuse:
             lay.route_permute(acts[l], bufs[l], stream)
-        lay.experts(acts[l], bufs[l], stream=stream)
+        if routed:
+            lay.experts_routed(acts[l], bufs[l], parts, stream=stream)
+        else:
+            lay.experts(acts[l], bufs[l], stream=stream)
+        routed = False
         if fuse and l + 1 < L:
-            lay.combine_route_next(bufs[l], layers[l + 1], bufs[l + 1], residual=acts[l],
-                                   out=acts[l + 1], stream=stream, x=acts[l])
+            nxt = layers[l + 1]
+            if parts is not None and lay.split_route_ok(bufs[l], nxt) and \
+                    bufs[l + 1].regime & 0xFF == A.MOE_REGIME_DECODE:
+                lay.combine_partials_next(bufs[l], nxt, parts, residual=acts[l],
+                                          out=acts[l + 1], stream=stream, x=acts[l])
+                routed = True
+            else:
+                lay.combine_route_next(bufs[l], nxt, bufs[l + 1], residual=acts[l],
+                                       out=acts[l + 1], stream=stream, x=acts[l])
         else:
             lay.combine(bufs[l], residual=acts[l], out=acts[l + 1], stream=stream, x=acts[l])
     return acts[L]

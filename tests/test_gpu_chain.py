@@ -91,13 +91,14 @@ def _free_running(cfg, L, x0, obls):
     return x, sets
 
 
-@pytest.mark.parametrize("fuse", [False, True], ids=["three_calls", "combine_route_fused"])
+@pytest.mark.parametrize("fuse", ["three_calls", "combine_route_fused", "route_in_ffn"])
 def test_decode_chain_16_layers_teacher_forced(fuse):
     """The benchmark's workload and launch configuration: 16 stacked decode
     layers captured in one graph, replayed once per step (fresh x0 each
-    step); every layer of every step against the oracle.  fuse: each layer's
-    combine runs with the next layer's route + permute in one launch, as the
-    benchmark runs it."""
+    step); every layer of every step against the oracle.  combine_route_fused:
+    each layer's combine runs with the next layer's route + permute in one
+    launch; route_in_ffn: the combine hands on only the next layer's logit
+    partials and that layer's expert launch routes from them."""
     cfg = MI.OLMOE_DECODE
     L = cfg.layers
     lays = _layers(cfg, L)
@@ -105,10 +106,11 @@ def test_decode_chain_16_layers_teacher_forced(fuse):
     assert bufs[0].regime & ~(M.MOE_Y_TOKEN_ORDER | M.MOE_Y_PARTIAL_ORDER) == \
         M.MOE_REGIME_DECODE
     acts = [torch.empty((1, cfg.H), dtype=torch.float16, device=DEV) for _ in range(L + 1)]
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=DEV)
 
     def step():
-        if fuse:
-            stack_forward(lays, bufs, acts)
+        if fuse != "three_calls":
+            stack_forward(lays, bufs, acts, parts=parts if fuse == "route_in_ffn" else None)
             return
         for l, lay in enumerate(lays):
             lay.forward(acts[l], bufs[l], residual=acts[l], out=acts[l + 1])

@@ -206,3 +206,75 @@ def test_rejects_bad_arguments():
                                     bn.offsets, bn.perm, bn.inv_perm, bn.perm_ws,
                                     bn.perm_ws.numel())
     assert e.value.code == M.MOE_EINVAL
+
+
+SPLIT_CASES = [
+    # (config, next-layer renorm, next-layer bias, residual)
+    ("olmoe", False, False, True),
+    ("olmoe", True, True, True),
+    ("tiny", False, True, True),
+    ("qwen", False, False, True),       # gated shared expert, 60 experts, top-4
+    ("h512", True, False, True),
+    ("h1024", False, True, False),
+]
+
+
+@pytest.mark.parametrize("zp", [False, True], ids=["sym", "zero_point"])
+@pytest.mark.parametrize("po", [True, False], ids=["partial_major_y", "plain_y"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "%s-r%d-b%d-res%d" % c)
+def test_route_in_ffn_equals_fused(case, po, zp):
+    """moe_combine_route_partials + moe_expert_ffn_w4a16_routed against
+    moe_combine_route_permute + moe_expert_ffn_w4a16: the same out, routing
+    arrays and y, bit for bit, over three steps."""
+    name, renorm, bias, residual = case
+    cfg = _cfg(name)
+    fmt = M.MOE_FMT_ZP if zp else M.MOE_FMT_SYM
+    say("route in ffn %s po=%d zp=%d" % (case, po, zp))
+    lay = make_layer(cfg, 0, fmt=fmt)
+    nxt = make_layer(cfg, 1, fmt=fmt)
+    if renorm:
+        nxt.flags = M.MOE_RENORM
+    if bias:
+        nxt.bias = torch.from_numpy(np.random.default_rng(6).standard_normal(cfg.E)
+                                    .astype(np.float32) * np.float32(0.05)).to(DEV)
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=DEV)
+    for s in range(3):
+        x = f16(MI.gen_x(cfg, 1, step=20 + s))
+        b = _run_layer(lay, 1, x, po)
+        assert lay.split_route_ok(b, nxt)
+        res = x if residual else None
+        out_a = torch.empty((1, cfg.H), dtype=torch.float16, device=DEV)
+        out_b = torch.empty_like(out_a)
+        ba, bb = nxt.buffers(1, partial_order=po), nxt.buffers(1, partial_order=po)
+        bb.y.fill_(-7.0)
+        lay.combine_route_next(b, nxt, ba, residual=res, out=out_a, x=x)
+        nxt.experts(out_a, ba)
+        lay.combine_partials_next(b, nxt, parts, residual=res, out=out_b, x=x)
+        nxt.experts_routed(out_b, bb, parts)
+        torch.cuda.synchronize()
+        a, f = _snapshot(ba, out_a), _snapshot(bb, out_b)
+        _assert_same(a, f, "%s step %d" % (name, s))
+        assert np.array_equal(_np(ba.y).view(np.uint8), _np(bb.y).view(np.uint8)), \
+            "%s step %d: y differs" % (name, s)
+        _assert_oracle_routing(nxt, f, cfg)
+
+
+def test_route_in_ffn_rejects_other_shapes():
+    """Two tokens, more than 64 experts or a batched y: MOE_EUNSUPPORTED before
+    any launch."""
+    cfg = MI.OLMOE_DECODE
+    lay = make_layer(cfg, 0)
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=DEV)
+    b2 = lay.buffers(2)
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_expert_ffn_w4a16_routed(b2.out, parts, None, cfg.E, cfg.k, 0, b2.topk_idx,
+                                      b2.topk_w, b2.counts, b2.offsets, b2.perm, b2.inv_perm,
+                                      lay.table, 2, cfg.H, cfg.I, cfg.g, b2.regime, b2.y,
+                                      b2.y_dtype, b2.y_slices)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
+    nxt = _next_layer(cfg, 128, 8)
+    b = lay.buffers(1)
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_combine_route_partials(b.y, b.y_dtype, b.y_slices, None, b.topk_w, None, None,
+                                     None, None, 1, cfg.H, cfg.k, b.out, nxt.router, 128, parts)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
