@@ -171,6 +171,7 @@ def _graph_time(torch, fn, reps):
 
 DECODE_KERNEL_SOURCES = ("int4_weight_only_router_amd/csrc/k_ffn_decode.hip",
                          "int4_weight_only_router_amd/csrc/k_decode_frag.h",
+                         "int4_weight_only_router_amd/csrc/k_sort_common.h",
                          "int4_weight_only_router_amd/csrc/moe_common.h")
 
 
