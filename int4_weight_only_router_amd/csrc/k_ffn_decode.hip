@@ -125,6 +125,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
     __shared__ int s_tok[RG];
     __shared__ float s_part[ROUTE ? 8 : 1][64];          // ROUTE: folded logit partials
     __shared__ uint64_t s_key[ROUTE ? NW : 1][64];      // ROUTE: each wave's selection keys
+    __shared__ int s_cnt[ROUTE ? NW : 1][64];            // ROUTE: each wave's share of the ranks
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -198,21 +199,28 @@ __global__ __launch_bounds__(NW * 64) void ffn_decode_kernel(
         float l = e0 + e1;
         if (rt.bias != nullptr)
             l = l + bv;
-        // the one-token router's ranks: count the keys that beat this lane's
+        // the one-token router's ranks: the number of keys that beat this
+        // lane's.  Every wave holds all 64 keys; wave w counts only those of
+        // lanes 64/NW w .. 64/NW (w + 1) - 1 (two waves share a SIMD, so 64
+        // comparisons in every wave would be paid twice over), and the
+        // counts meet in LDS.
+        constexpr int KPW = 64 / NW;
         const uint64_t key = ev ? topk_key(l, lane) : 0ull;
         s_key[wave][lane] = key;
         __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order
-        int r0c = 0, r1c = 0, r2c = 0, r3c = 0;
+        int r0c = 0, r1c = 0;
 #pragma unroll
-        for (int j = 0; j < 64; j += 4) {
-            const uint4_t q = *reinterpret_cast<const uint4_t *>(&s_key[wave][j]);
-            const uint4_t u = *reinterpret_cast<const uint4_t *>(&s_key[wave][j + 2]);
+        for (int jj = 0; jj < KPW; jj += 2) {
+            const uint4_t q = *reinterpret_cast<const uint4_t *>(&s_key[wave][KPW * wave + jj]);
             r0c += (((uint64_t)q.y << 32) | q.x) > key ? 1 : 0;
             r1c += (((uint64_t)q.w << 32) | q.z) > key ? 1 : 0;
-            r2c += (((uint64_t)u.y << 32) | u.x) > key ? 1 : 0;
-            r3c += (((uint64_t)u.w << 32) | u.z) > key ? 1 : 0;
         }
-        const int rank = (r0c + r1c) + (r2c + r3c);
+        s_cnt[wave][lane] = r0c + r1c;
+        __syncthreads();
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            rank += s_cnt[w][lane];
         const bool sel = ev && rank < k;
         const uint64_t smask = __ballot(sel);
         const int a = blockIdx.y;
