@@ -275,17 +275,19 @@ def run_decode(args, torch, M):
 
     graph = None
     if args.graph:
-        # one captured step reading x0 from a fixed buffer, refreshed by a
-        # device copy inside the same graph
+        # one captured step: gather this step's token into a fixed buffer,
+        # run the 16 layers on it, advance the token index (all on the GPU,
+        # so a step is one replay)
         xin = torch.empty((1, cfg.H), dtype=torch.float16, device=dev)
         sel = torch.zeros(1, dtype=torch.int64, device=dev)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            xin.copy_(xs.index_select(0, sel))
+            torch.index_select(xs, 0, sel, out=xin)
             step_from(xin)
+            sel.add_(1)
         graph = (g, sel)
         for s in range(3):
-            sel.fill_(s)
+            sel.fill_(s % (K + W))   # every replay reads a row of xs
             g.replay()
         torch.cuda.synchronize()
 
@@ -294,8 +296,10 @@ def run_decode(args, torch, M):
     t0 = time.perf_counter()
     if graph:
         g, sel = graph
+        sel.fill_(W)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for s in range(W, W + K):
-            sel.fill_(s)
             g.replay()
     else:
         for s in range(W, W + K):
