@@ -259,6 +259,54 @@ def test_route_in_ffn_equals_fused(case, po, zp):
         _assert_oracle_routing(nxt, f, cfg)
 
 
+SPLIT_NEXT = [
+    # (config, next E, next k, renorm, bias): next layers of other expert counts
+    ("olmoe", 37, 5, False, True),
+    ("olmoe", 64, 16, True, False),
+    ("olmoe", 48, 1, False, False),
+    ("h512", 33, 5, True, True),
+    ("h1024", 9, 8, False, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_NEXT, ids=lambda c: "%s-E%d-k%d-r%d-b%d" % c)
+def test_route_in_ffn_other_expert_counts(case):
+    """The split form against the fused one when the next layer has another
+    expert count and top-k (E not a multiple of 8, k = 1 and 16, k close to
+    E): out, routing arrays and y bit for bit, routing against the oracle."""
+    name, En, kn, renorm, bias = case
+    cfg = _cfg(name)
+    cn = MI.MoEConfig(cfg.cid + 40 + En, "%s-next-E%d" % (name, En), H=cfg.H, E=En, k=kn,
+                      I=cfg.I, g=cfg.g)
+    say("route in ffn, next layer %s" % (case,))
+    lay = make_layer(cfg, 0)
+    nxt = make_layer(cn, 1)
+    if renorm:
+        nxt.flags = M.MOE_RENORM
+    if bias:
+        nxt.bias = torch.from_numpy(np.random.default_rng(7).standard_normal(En)
+                                    .astype(np.float32) * np.float32(0.05)).to(DEV)
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=DEV)
+    for s in range(2):
+        x = f16(MI.gen_x(cfg, 1, step=40 + s))
+        b = _run_layer(lay, 1, x)
+        assert lay.split_route_ok(b, nxt)
+        out_a = torch.empty((1, cfg.H), dtype=torch.float16, device=DEV)
+        out_b = torch.empty_like(out_a)
+        ba, bb = nxt.buffers(1), nxt.buffers(1)
+        bb.y.fill_(-7.0)
+        lay.combine_route_next(b, nxt, ba, residual=x, out=out_a, x=x)
+        nxt.experts(out_a, ba)
+        lay.combine_partials_next(b, nxt, parts, residual=x, out=out_b, x=x)
+        nxt.experts_routed(out_b, bb, parts)
+        torch.cuda.synchronize()
+        a, f = _snapshot(ba, out_a), _snapshot(bb, out_b)
+        _assert_same(a, f, "%s step %d" % (case, s))
+        assert np.array_equal(_np(ba.y).view(np.uint8), _np(bb.y).view(np.uint8)), \
+            "%s step %d: y differs" % (case, s)
+        _assert_oracle_routing(nxt, f, cn)
+
+
 def test_route_in_ffn_rejects_other_shapes():
     """Two tokens, more than 64 experts or a batched y: MOE_EUNSUPPORTED before
     any launch."""
