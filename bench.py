@@ -244,12 +244,16 @@ def run_decode(args, torch, M):
         # one launch (moe_combine_route_permute); with split (the default),
         # layer l's combine hands on only layer l+1's logit partials and
         # layer l+1's expert launch routes from them
-        # (moe_combine_route_partials + moe_expert_ffn_w4a16_routed); the
-        # same bits in every form
+        # (moe_combine_route_partials + moe_expert_ffn_w4a16_routed), and
+        # layer 0's from the partials of its input (moe_logit_partials);
+        # the same bits in every form
         routed = False
         for l, lay in enumerate(lays):
             out = act[l & 1]
-            if l == 0 or not fuse:
+            if l == 0 and split:
+                lay.logit_partials(x, parts)
+                routed = True
+            elif l == 0 or not fuse:
                 lay.route_permute(x, bufs[l])
             if routed:
                 lay.experts_routed(x, bufs[l], parts)
@@ -328,6 +332,7 @@ def run_decode(args, torch, M):
                                        for l in range(L - 1)], reps) / (L - 1)
     t_ffn_r = _graph_time(torch, lambda: [lays[l].experts_routed(x0, bufs[l], parts)
                                           for l in range(1, L)], reps) / (L - 1)
+    t_lp = _graph_time(torch, lambda: [lay.logit_partials(x0, parts) for lay in lays], reps) / L
     ffn_bytes = int(np.mean(touched)) * blob_bytes + cfg.H * 2   # INT4 + scales of routed experts, x
     # the decode kernel as the step runs it: with split, layers 1..15 route
     # inside it from the logit partials
@@ -359,7 +364,8 @@ def run_decode(args, torch, M):
                          "combine": round(t_comb * 1e3, 2),
                          "combine+next_route": round(t_cr * 1e3, 2),
                          "combine+next_logit_partials": round(t_cp * 1e3, 2),
-                         "route_from_partials+expert_ffn": round(t_ffn_r * 1e3, 2)},
+                         "route_from_partials+expert_ffn": round(t_ffn_r * 1e3, 2),
+                         "first_layer_logit_partials": round(t_lp * 1e3, 2)},
         "roofline": {"kernel": "ffn_decode_kernel (%s, DECODE)" % (
                          "moe_expert_ffn_w4a16_routed" if split else "moe_expert_ffn_w4a16"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -458,8 +458,17 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
  * carry MOE_Y_TOKEN_ORDER, MOE_Y_PARTIAL_ORDER and MOE_W4_ZERO_POINT;
  * d_expert_blobs must hold every expert).  Errors: MOE_EINVAL / ENOMEM /
  * EUNSUPPORTED as the calls they replace, checked before any launch.
+ * moe_logit_partials: the same partials straight from an fp16 input row
+ * that no combine forms (the first layer of a stack): x_f16 device fp16 [H]
+ * (T = 1), w_router_f16 device fp16 [E][H] (both 16-byte aligned), into
+ * logit_partials as above; routing from them equals moe_route_permute of
+ * x_f16 bit for bit.  One launch of min(64, H / 8) one-wave workgroups.
+ * Errors: MOE_EINVAL (shape, null, alignment), MOE_EUNSUPPORTED (T != 1,
+ * E > 64, H not instantiated), before any launch.
  */
 size_t moe_logit_partials_bytes(void);
+int moe_logit_partials(const void *x_f16, const void *w_router_f16, int T, int H, int E,
+                       float *logit_partials, hipStream_t stream);
 int moe_combine_route_partials(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
                                const float *topk_w, const float *shared_f32, const void *x_f16,
                                const void *shared_gate_w_f16, const void *residual_f16, int T,

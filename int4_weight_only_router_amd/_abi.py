@@ -21,7 +21,8 @@ __all__ = [
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
     "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute",
-    "moe_logit_partials_bytes", "moe_combine_route_partials", "moe_expert_ffn_w4a16_routed",
+    "moe_logit_partials_bytes", "moe_logit_partials", "moe_combine_route_partials",
+    "moe_expert_ffn_w4a16_routed",
     "PoolConfig",
     "PoolStats", "PoolLayerArgs",
     "moe_pool_create", "moe_pool_prepare", "moe_pool_layer_forward", "moe_pool_pin",
@@ -50,7 +51,8 @@ EXPORTS = [
     "moe_expert_ffn_plan", "moe_expert_ffn_w4a16", "moe_shared_ffn_workspace_bytes",
     "moe_shared_ffn_f16", "moe_combine", "moe_combine_gated",
     "moe_combine_route_permute_workspace_bytes", "moe_combine_route_permute",
-    "moe_logit_partials_bytes", "moe_combine_route_partials", "moe_expert_ffn_w4a16_routed",
+    "moe_logit_partials_bytes", "moe_logit_partials", "moe_combine_route_partials",
+    "moe_expert_ffn_w4a16_routed",
     "moe_pool_create",
     "moe_pool_prepare",
     "moe_pool_layer_forward", "moe_pool_pin",
@@ -133,6 +135,7 @@ def _declare(L):
                                             vp, vp, vp, i32, i32, C.c_uint, vp, vp, vp, vp, vp,
                                             vp, vp, sz, vp]),
         "moe_logit_partials_bytes": (sz, []),
+        "moe_logit_partials": (i32, [vp, vp, i32, i32, i32, vp, vp]),
         "moe_combine_route_partials": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32,
                                              i32, vp, vp, i32, vp, vp]),
         "moe_expert_ffn_w4a16_routed": (i32, [vp, vp, vp, i32, i32, C.c_uint, vp, vp, vp, vp,
@@ -364,6 +367,11 @@ def moe_combine_route_permute(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32
 
 def moe_logit_partials_bytes():
     return lib().moe_logit_partials_bytes()
+
+
+def moe_logit_partials(x_f16, w_router, T, H, E, logit_partials, stream=None):
+    return _check(lib().moe_logit_partials(_p(x_f16), _p(w_router), T, H, E,
+                                           _p(logit_partials), _s(stream)))
 
 
 def moe_combine_route_partials(y, y_dtype, y_slices, inv_perm, topk_w, shared_f32, x_f16,

@@ -226,4 +226,58 @@ int launch_combine_route(const float *y, bool pm, int S, const int32_t *inv_perm
     return MOE_OK;
 }
 
+// The 64 pinned-order partials of one token's router logits straight from
+// an fp16 input row (the first layer of a stack, whose input no combine
+// forms): block j, one wave, lane e = expert e, accumulates chunks j + 64 m
+// of x against router row e element by element, as the combine above does
+// from the columns it rounds, and stores partial j of every expert's logit
+// at part[j * 64 + e].  Lanes past E repeat row E - 1 (never read back).
+template <int H>
+__global__ __launch_bounds__(64) void logit_partials_kernel(const f16 *__restrict__ x,
+                                                            const f16 *__restrict__ wr, int E,
+                                                            float *__restrict__ part)
+{
+    constexpr int NCH = H / 8;
+    constexpr int NCL = (NCH + 63) / 64;
+    const int j = blockIdx.x;
+    const int lane = threadIdx.x;
+    const uint4_t *row = reinterpret_cast<const uint4_t *>(wr + (size_t)min(lane, E - 1) * H);
+    const uint4_t *xv = reinterpret_cast<const uint4_t *>(x);
+    uint4_t wq[NCL], xq[NCL];
+#pragma unroll
+    for (int m = 0; m < NCL; ++m) {
+        wq[m] = row[j + 64 * m];   // j + 64 m < NCH: the grid has min(64, NCH) blocks
+        xq[m] = xv[j + 64 * m];
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCL; ++m) {
+        const half8_t xh = __builtin_bit_cast(half8_t, xq[m]);
+        const half8_t wh = __builtin_bit_cast(half8_t, wq[m]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc = __builtin_fmaf((float)xh[i], (float)wh[i], acc);
+    }
+    part[j * 64 + lane] = acc;
+}
+
+// T = 1, E <= 64; the caller has checked the shapes and x's alignment.
+int launch_logit_partials(const void *x, const void *wr, int H, int E, float *part, hipStream_t s)
+{
+    const f16 *xh = static_cast<const f16 *>(x), *wh = static_cast<const f16 *>(wr);
+#define MOE_LP(HH)                                                                              \
+    hipLaunchKernelGGL((logit_partials_kernel<HH>), dim3(HH / 8 < 64 ? HH / 8 : 64), dim3(64), \
+                       0, s, xh, wh, E, part)
+    switch (H) {
+    case 256: MOE_LP(256); break;
+    case 512: MOE_LP(512); break;
+    case 1024: MOE_LP(1024); break;
+    case 2048: MOE_LP(2048); break;
+    default: return set_error(MOE_EUNSUPPORTED, "logit_partials: H=%d not instantiated", H);
+    }
+#undef MOE_LP
+    MOE_LAUNCH_CHECK("logit_partials_kernel");
+    return MOE_OK;
+}
+
 }  // namespace moe

@@ -61,6 +61,7 @@ int launch_combine_route(const float *, bool, int, const int32_t *, const float 
                          float *, int32_t *, int32_t *, int32_t *, int32_t *, float *,
                          hipStream_t);
 size_t combine_route_ws_bytes();
+int launch_logit_partials(const void *, const void *, int, int, float *, hipStream_t);
 int launch_combine(const void *, int, int, const int32_t *, const float *, const float *,
                    const void *, const void *, const void *, int, int, int, void *,
                    hipStream_t);
@@ -678,6 +679,24 @@ int moe_combine_route_permute(const void *y, int y_dtype, int y_slices, const in
 }
 
 size_t moe_logit_partials_bytes(void) { return (size_t)64 * 64 * sizeof(float); }
+
+int moe_logit_partials(const void *x_f16, const void *w_router_f16, int T, int H, int E,
+                       float *logit_partials, hipStream_t stream)
+{
+    MOE_API_RANGE();
+    clear_error();
+    const char *fn = "moe_logit_partials";
+    if (T < 0 || H <= 0 || E <= 0)
+        return set_error(MOE_EINVAL, "%s: bad shape T=%d H=%d E=%d", fn, T, H, E);
+    if (T != 1 || E > 64)
+        return set_error(MOE_EUNSUPPORTED, "%s: one token of at most 64 experts only (T=%d, E=%d)",
+                         fn, T, E);
+    if (!x_f16 || !w_router_f16 || !logit_partials)
+        return set_error(MOE_EINVAL, "%s: null pointer", fn);
+    if (((uintptr_t)x_f16 | (uintptr_t)w_router_f16) & 15u)
+        return set_error(MOE_EINVAL, "%s: x and the router must be 16-byte aligned", fn);
+    return launch_logit_partials(x_f16, w_router_f16, H, E, logit_partials, stream);
+}
 
 int moe_combine_route_partials(const void *y, int y_dtype, int y_slices, const int32_t *inv_perm,
                                const float *topk_w, const float *shared_f32, const void *x_f16,

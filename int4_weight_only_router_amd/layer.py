@@ -213,6 +213,16 @@ class MoELayer:
                                      self.H, self.k, out, nxt.router, nxt.E, parts, stream)
         return out
 
+    def route_from_partials_ok(self, b: LayerBuffers) -> bool:
+        """Whether this layer's expert launch can route from logit partials
+        (moe_expert_ffn_w4a16_routed): one decode token, at most 64 experts."""
+        return b.T == 1 and self.E <= 64 and b.regime & 0xFF == A.MOE_REGIME_DECODE
+
+    def logit_partials(self, x, parts, stream=None):
+        """This layer's logit partials of an input row in hand (the first
+        layer of a stack) into `parts`, for experts_routed."""
+        A.moe_logit_partials(x, self.router, 1, self.H, self.E, parts, stream)
+
     def experts_routed(self, x, b: LayerBuffers, parts, stream=None, shared=True):
         """Routing from the logit partials of the previous layer's combine and
         the routed experts in one launch (moe_expert_ffn_w4a16_routed): fills
@@ -285,11 +295,15 @@ def stack_forward(layers, bufs, acts, stream=None, fuse=True, parts=None):
     permute (MoELayer.combine_route_next); with `parts` as well (fp32 device
     buffer of moe_logit_partials_bytes()), a decode token's combine hands the
     next layer only its logit partials and that layer's expert launch routes
-    from them (combine_partials_next + experts_routed).  Every form gives the
-    same bits."""
+    from them (combine_partials_next + experts_routed), the first layer's
+    from moe_logit_partials of its input.  Every form gives the same bits."""
     L = len(layers)
-    layers[0].route_permute(acts[0], bufs[0], stream)
-    routed = False   # this layer's routing is still to be formed from `parts`
+    # routed: this layer's routing is still to be formed from `parts`
+    routed = fuse and parts is not None and layers[0].route_from_partials_ok(bufs[0])
+    if routed:
+        layers[0].logit_partials(acts[0], parts, stream)
+    else:
+        layers[0].route_permute(acts[0], bufs[0], stream)
     for l, lay in enumerate(layers):
         if l > 0 and not fuse:
             lay.route_permute(acts[l], bufs[l], stream)

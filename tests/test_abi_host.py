@@ -128,6 +128,18 @@ def test_compute_calls_reject_before_launch():
     with pytest.raises(M.MoEError) as ei:   # overlapping prepack buffers
         M.moe_prepack_experts(4096, 2, 256, 512, 64, 4096 + 256, stream=0)
     assert ei.value.code == M.MOE_EINVAL
+    with pytest.raises(M.MoEError) as ei:   # logit partials: two tokens
+        M.moe_logit_partials(4096, 8192, 2, 2048, 64, 4096, stream=0)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoEError) as ei:   # more than 64 experts
+        M.moe_logit_partials(4096, 8192, 1, 2048, 65, 4096, stream=0)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
+    with pytest.raises(M.MoEError) as ei:   # x not 16-byte aligned
+        M.moe_logit_partials(4096 + 2, 8192, 1, 2048, 64, 4096, stream=0)
+    assert ei.value.code == M.MOE_EINVAL and "aligned" in str(ei.value)
+    with pytest.raises(M.MoEError) as ei:   # H not instantiated
+        M.moe_logit_partials(4096, 8192, 1, 768, 64, 4096, stream=0)
+    assert ei.value.code == M.MOE_EUNSUPPORTED
     # T = 0 is a valid no-op for the routed FFN and combine
     M.moe_expert_ffn_w4a16(None, None, None, None, 0, 2048, 1024, 64, 8, 128,
                            M.MOE_REGIME_DECODE, None, M.MOE_DTYPE_F32, 32, stream=0)

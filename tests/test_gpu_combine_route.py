@@ -307,6 +307,40 @@ def test_route_in_ffn_other_expert_counts(case):
         _assert_oracle_routing(nxt, f, cn)
 
 
+@pytest.mark.parametrize("zp", [False, True], ids=["sym", "zero_point"])
+@pytest.mark.parametrize("name,renorm,bias", [("olmoe", False, False), ("olmoe", True, True),
+                                              ("tiny", False, True), ("qwen", False, False),
+                                              ("h512", True, True), ("h1024", False, True)])
+def test_first_layer_partials_equal_route_permute(name, renorm, bias, zp):
+    """moe_logit_partials + moe_expert_ffn_w4a16_routed against
+    moe_route_permute + moe_expert_ffn_w4a16 on one input row: routing arrays
+    and y bit for bit, routing against the oracle."""
+    cfg = _cfg(name)
+    say("first-layer partials %s renorm=%d bias=%d zp=%d" % (name, renorm, bias, zp))
+    lay = make_layer(cfg, 1, fmt=M.MOE_FMT_ZP if zp else M.MOE_FMT_SYM)
+    if renorm:
+        lay.flags = M.MOE_RENORM
+    if bias:
+        lay.bias = torch.from_numpy(np.random.default_rng(8).standard_normal(cfg.E)
+                                    .astype(np.float32) * np.float32(0.05)).to(DEV)
+    parts = torch.empty(M.moe_logit_partials_bytes() // 4, dtype=torch.float32, device=DEV)
+    for s in range(3):
+        x = f16(MI.gen_x(cfg, 1, step=60 + s))
+        ba, bb = lay.buffers(1), lay.buffers(1)
+        assert lay.route_from_partials_ok(bb)
+        bb.y.fill_(-7.0)
+        lay.route_permute(x, ba)
+        lay.experts(x, ba)
+        lay.logit_partials(x, parts)
+        lay.experts_routed(x, bb, parts)
+        torch.cuda.synchronize()
+        a, f = _snapshot(ba, x), _snapshot(bb, x)
+        _assert_same(a, f, "%s step %d" % (name, s))
+        assert np.array_equal(_np(ba.y).view(np.uint8), _np(bb.y).view(np.uint8)), \
+            "%s step %d: y differs" % (name, s)
+        _assert_oracle_routing(lay, f, cfg)
+
+
 def test_route_in_ffn_rejects_other_shapes():
     """Two tokens, more than 64 experts or a batched y: MOE_EUNSUPPORTED before
     any launch."""
